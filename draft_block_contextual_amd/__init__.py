@@ -1,0 +1,277 @@
+"""Python binding of libdcoco, the MI355X (gfx950) DCOCO corrector hot path.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/dcoco.h.  torch supplies device memory and the current
+HIP stream.  Importing this package does not need a GPU; the first call that
+launches work does.  If libdcoco.so has not been built, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdcoco.so")
+
+DCOCO_OK = 0
+DCOCO_ERR_INVALID_ARG = -1
+DCOCO_ERR_UNSUPPORTED = -2
+DCOCO_ERR_WORKSPACE = -3
+DCOCO_ERR_HIP = -4
+DTYPE_CODE = {"f32": 0, "bf16": 1}
+
+# every entry point include/dcoco.h declares
+EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select",
+           "dcoco_correct_block", "dcoco_status_string", "dcoco_abi_version"]
+
+
+class DcocoError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+class CDims(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int32), ("B", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("V", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_embed", ctypes.c_int32),
+                ("d_proj", ctypes.c_int32), ("d_z", ctypes.c_int32), ("d_pair", ctypes.c_int32),
+                ("d_mlp", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [("P_e", ctypes.c_void_p), ("P_h", ctypes.c_void_p), ("W_f", ctypes.c_void_p),
+                ("W_pair", ctypes.c_void_p), ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("b2", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdcoco.so (built by draft_block_contextual_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m draft_block_contextual_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+    pd, pw = ctypes.POINTER(CDims), ctypes.POINTER(CWeights)
+    lib.dcoco_topk.argtypes = [pd, vp, vp, vp, vp, sz, vp]
+    lib.dcoco_represent.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dcoco_score.argtypes = [pd, pw, vp, vp, vp, vp, vp, sz, vp]
+    lib.dcoco_select.argtypes = [pd, vp, vp, vp, vp, vp, vp]
+    lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
+    for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_correct_block"]:
+        getattr(lib, f).restype = ctypes.c_int
+    lib.dcoco_status_string.argtypes = [ctypes.c_int]
+    lib.dcoco_status_string.restype = ctypes.c_char_p
+    lib.dcoco_abi_version.argtypes = []
+    lib.dcoco_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().dcoco_status_string(status).decode()
+
+
+@dataclasses.dataclass
+class Dims:
+    n_blocks: int
+    B: int
+    K: int
+    V: int
+    d_hidden: int
+    d_embed: int
+    d_proj: int
+    d_z: int
+    d_pair: int
+    d_mlp: int
+    dtype: str = "bf16"
+    ln_eps: float = 1e-5
+
+    def c(self) -> CDims:
+        return CDims(self.n_blocks, self.B, self.K, self.V, self.d_hidden, self.d_embed, self.d_proj,
+                     self.d_z, self.d_pair, self.d_mlp, DTYPE_CODE[self.dtype], self.ln_eps)
+
+    @classmethod
+    def from_synth(cls, D) -> "Dims":
+        return cls(D.n_blocks, D.B, D.K, D.V, D.d, D.e, D.r, D.r_z, D.r_s, D.H, D.dtype, D.ln_eps)
+
+
+@dataclasses.dataclass
+class Weights:
+    P_e: object
+    P_h: object
+    W_f: object
+    W_pair: object
+    W1: object
+    b1: object
+    w2: object
+    b2: float
+
+    def c(self) -> CWeights:
+        return CWeights(_ptr(self.P_e), _ptr(self.P_h), _ptr(self.W_f), _ptr(self.W_pair),
+                        _ptr(self.W1), _ptr(self.b1), _ptr(self.w2), float(self.b2))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != DCOCO_OK:
+        raise DcocoError(fn, rc, status_string(rc))
+
+
+def _torch_dtype(dtype: str):
+    import torch
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    import torch
+    if workspace is not None:
+        return workspace
+    key = (str(device), nbytes)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        _ws_cache.clear()
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _query(fn, *args) -> int:
+    n = ctypes.c_size_t(0)
+    _check(fn.__name__, fn(*args, None, ctypes.byref(n), None))
+    return n.value
+
+
+def topk(dims: Dims, logits, cand_ids=None, cand_logits=None, workspace=None, stream=None):
+    """dcoco_topk: logits [N*B, V] -> (cand_ids [N*B, K] int32, cand_logits [N*B, K] fp32)."""
+    import torch
+    lib = load()
+    cd = dims.c()
+    R = dims.n_blocks * dims.B
+    dev = logits.device
+    if cand_ids is None:
+        cand_ids = torch.empty((R, dims.K), dtype=torch.int32, device=dev)
+    if cand_logits is None:
+        cand_logits = torch.empty((R, dims.K), dtype=torch.float32, device=dev)
+    need = _query(lib.dcoco_topk, ctypes.byref(cd), _ptr(logits), _ptr(cand_ids), _ptr(cand_logits))
+    ws = _workspace(need, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_topk", lib.dcoco_topk(ctypes.byref(cd), _ptr(logits), _ptr(cand_ids), _ptr(cand_logits),
+                                        _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return cand_ids, cand_logits
+
+
+def represent(dims: Dims, w: Weights, h, E, cand_ids, z=None, s=None, workspace=None, stream=None):
+    """dcoco_represent -> (z [N,B,K,d_z] dtype, s [N,B-1,d_pair] fp32)."""
+    import torch
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    dev = h.device
+    if z is None:
+        z = torch.empty((dims.n_blocks, dims.B, dims.K, dims.d_z), dtype=_torch_dtype(dims.dtype), device=dev)
+    if s is None:
+        s = torch.empty((dims.n_blocks, max(dims.B - 1, 1), dims.d_pair), dtype=torch.float32, device=dev)
+    args = (ctypes.byref(cd), ctypes.byref(cw), _ptr(h), _ptr(E), _ptr(cand_ids), _ptr(z), _ptr(s))
+    need = _query(lib.dcoco_represent, *args)
+    ws = _workspace(need, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_represent", lib.dcoco_represent(*args, _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return z, s[:, :dims.B - 1]
+
+
+def score(dims: Dims, w: Weights, z, s, cand_logits, S=None, workspace=None, stream=None):
+    """dcoco_score -> S [N, B-1, K, K] fp32."""
+    import torch
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    dev = z.device
+    if S is None:
+        S = torch.empty((dims.n_blocks, max(dims.B - 1, 1), dims.K, dims.K), dtype=torch.float32, device=dev)
+    args = (ctypes.byref(cd), ctypes.byref(cw), _ptr(z), _ptr(s), _ptr(cand_logits), _ptr(S))
+    need = _query(lib.dcoco_score, *args)
+    ws = _workspace(need, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_score", lib.dcoco_score(*args, _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return S[:, :dims.B - 1]
+
+
+def select(dims: Dims, S, cand_logits, cand_ids, sel_idx=None, sel_tok=None, stream=None):
+    """dcoco_select -> (sel_idx [N, B] int32, sel_tok [N, B] int32)."""
+    import torch
+    lib = load()
+    cd = dims.c()
+    dev = cand_logits.device
+    if sel_idx is None:
+        sel_idx = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+    if sel_tok is None:
+        sel_tok = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+    _check("dcoco_select", lib.dcoco_select(ctypes.byref(cd), _ptr(S), _ptr(cand_logits), _ptr(cand_ids),
+                                            _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
+    return sel_idx, sel_tok
+
+
+def correct_block_workspace_bytes(dims: Dims, w: Weights) -> int:
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    n = ctypes.c_size_t(0)
+    _check("dcoco_correct_block", lib.dcoco_correct_block(
+        ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, ctypes.byref(n),
+        None, None, None, None, None, None))
+    return n.value
+
+
+def correct_block(dims: Dims, w: Weights, logits, h, E, sel_tok=None, sel_idx=None, S=None,
+                  cand_ids=None, cand_logits=None, want_all: bool = False, workspace=None, stream=None):
+    """dcoco_correct_block.  Returns a dict with sel_tok (and, when asked for or
+    passed in, sel_idx, S, cand_ids, cand_logits)."""
+    import torch
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    dev = logits.device
+    N, B, K = dims.n_blocks, dims.B, dims.K
+    if sel_tok is None:
+        sel_tok = torch.empty((N, B), dtype=torch.int32, device=dev)
+    if want_all:
+        if sel_idx is None:
+            sel_idx = torch.empty((N, B), dtype=torch.int32, device=dev)
+        if S is None:
+            S = torch.empty((N, max(B - 1, 1), K, K), dtype=torch.float32, device=dev)
+        if cand_ids is None:
+            cand_ids = torch.empty((N, B, K), dtype=torch.int32, device=dev)
+        if cand_logits is None:
+            cand_logits = torch.empty((N, B, K), dtype=torch.float32, device=dev)
+    need = correct_block_workspace_bytes(dims, w)
+    ws = _workspace(need, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_correct_block", lib.dcoco_correct_block(
+        ctypes.byref(cd), ctypes.byref(cw), _ptr(logits), _ptr(h), _ptr(E), _ptr(ws), ctypes.byref(n),
+        _ptr(sel_tok), _ptr(sel_idx), _ptr(S), _ptr(cand_ids), _ptr(cand_logits), _stream(stream)))
+    out = {"sel_tok": sel_tok}
+    if sel_idx is not None:
+        out["sel_idx"] = sel_idx
+    if S is not None:
+        out["S"] = S[:, :B - 1]
+    if cand_ids is not None:
+        out["cand_ids"] = cand_ids
+    if cand_logits is not None:
+        out["cand_logits"] = cand_logits
+    return out

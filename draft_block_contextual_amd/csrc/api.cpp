@@ -1,0 +1,332 @@
+// C ABI of libdcoco: argument checks, workspace layout and the launch sequence
+// of each entry point on the caller's stream.  The operations themselves are
+// specified in include/dcoco.h.
+#include "../../include/dcoco.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+
+using namespace dcoco;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == DCOCO_BF16 ? 2 : 4; }
+
+int check_width(int32_t w, int32_t maxw) {
+  if (w <= 0) return DCOCO_ERR_INVALID_ARG;
+  if (w % 32 != 0 || w > maxw) return DCOCO_ERR_UNSUPPORTED;
+  return DCOCO_OK;
+}
+
+int check_dims(const dcoco_dims* d, bool need_widths) {
+  if (!d) return DCOCO_ERR_INVALID_ARG;
+  if (d->dtype != DCOCO_F32 && d->dtype != DCOCO_BF16) return DCOCO_ERR_INVALID_ARG;
+  if (d->n_blocks < 1 || d->B < 1 || d->K < 1 || d->V < 1 || d->K > d->V) return DCOCO_ERR_INVALID_ARG;
+  if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps)) return DCOCO_ERR_INVALID_ARG;
+  if (d->K > 64) return DCOCO_ERR_UNSUPPORTED;
+  const long long rows = static_cast<long long>(d->n_blocks) * d->B;
+  if (rows * d->K > (1ll << 30) || rows > 65535) return DCOCO_ERR_UNSUPPORTED;
+  if (need_widths) {
+    int rc;
+    if ((rc = check_width(d->d_hidden, 1 << 16)) != DCOCO_OK) return rc;
+    if ((rc = check_width(d->d_embed, 1 << 16)) != DCOCO_OK) return rc;
+    if ((rc = check_width(d->d_proj, 2048)) != DCOCO_OK) return rc;
+    if ((rc = check_width(d->d_z, 2048)) != DCOCO_OK) return rc;
+    if ((rc = check_width(d->d_pair, 8192)) != DCOCO_OK) return rc;
+    if ((rc = check_width(d->d_mlp, 1 << 16)) != DCOCO_OK) return rc;
+  }
+  return DCOCO_OK;
+}
+
+int check_weights(const dcoco_weights* w, bool rep, bool score) {
+  if (!w) return DCOCO_ERR_INVALID_ARG;
+  if (rep) {
+    if (!w->P_e || !w->P_h || !w->W_f || !w->W_pair) return DCOCO_ERR_INVALID_ARG;
+    if (!aligned16(w->P_e) || !aligned16(w->P_h) || !aligned16(w->W_f) || !aligned16(w->W_pair))
+      return DCOCO_ERR_INVALID_ARG;
+  }
+  if (score) {
+    if (!w->W1 || !w->w2) return DCOCO_ERR_INVALID_ARG;
+    if (!aligned16(w->W1) || !aligned16(w->w2) || (w->b1 && !aligned16(w->b1))) return DCOCO_ERR_INVALID_ARG;
+    if (!std::isfinite(w->b2)) return DCOCO_ERR_INVALID_ARG;
+  }
+  return DCOCO_OK;
+}
+
+bool ptr_ok(const void* p) { return p && aligned16(p); }
+bool opt_ok(const void* p) { return !p || aligned16(p); }
+
+// Sequential carve-up of a caller workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+struct RepLayout {
+  int split_slot, split_cand;
+  float* Y;       // [split_slot][R][r + 2 rs]
+  float* U;       // [split_cand][R K][r]
+  void* g;        // [R][r]
+  float* gf;      // [R][rz]
+  void* b;        // [R K][r]
+};
+
+RepLayout carve_rep(Carve& c, const dcoco_dims* d) {
+  RepLayout L;
+  const int R = d->n_blocks * d->B;
+  const int RK = R * d->K;
+  const int ns = d->d_proj + 2 * d->d_pair;
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  L.split_slot = gemm_pick_split(R, ns, d->d_hidden, dt, dt);
+  L.split_cand = gemm_pick_split(RK, d->d_proj, d->d_embed, dt, dt);
+  L.Y = static_cast<float*>(c.take(sizeof(float) * L.split_slot * static_cast<size_t>(R) * ns));
+  L.U = static_cast<float*>(c.take(sizeof(float) * L.split_cand * static_cast<size_t>(RK) * d->d_proj));
+  L.g = c.take(esize(d->dtype) * static_cast<size_t>(R) * d->d_proj);
+  L.gf = static_cast<float*>(c.take(sizeof(float) * static_cast<size_t>(R) * d->d_z));
+  L.b = c.take(esize(d->dtype) * static_cast<size_t>(RK) * d->d_proj);
+  return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DCOCO_OK : DCOCO_ERR_HIP; }
+
+// representation stage: g, s, b, z (see dcoco_represent)
+hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
+                         const int32_t* ids, void* z, float* s, const RepLayout& L, hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int R = d->n_blocks * d->B;
+  const int RK = R * d->K;
+  const int r = d->d_proj, rs = d->d_pair, rz = d->d_z, dh = d->d_hidden;
+  const int ns = r + 2 * rs;
+  hipError_t e;
+  // slot projections: [P_h; W_L; W_R] h, fp32 partial sums
+  {
+    GemmProblem q{};
+    q.M = R; q.N = ns; q.Kd = dh;
+    q.A = h; q.lda = dh; q.a_rows = nullptr; q.a_dtype = dt;
+    q.w[0] = w->P_h; q.ldw[0] = dh; q.col0[0] = 0; q.seg_end[0] = r;
+    q.w[1] = w->W_pair; q.ldw[1] = 2ll * dh; q.col0[1] = 0; q.seg_end[1] = r + rs;
+    q.w[2] = w->W_pair; q.ldw[2] = 2ll * dh; q.col0[2] = dh; q.seg_end[2] = ns;
+    q.w_dtype = dt;
+    q.split = L.split_slot; q.out_f32 = L.Y; q.ldo = ns; q.out = nullptr;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
+  if ((e = launch_ln_rows(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
+  if ((e = launch_pair_state(L.Y, L.split_slot, d->n_blocks, d->B, ns, r, r + rs, rs, s, st)) != hipSuccess)
+    return e;
+  // gf = W_fg g (the slot half of the fusion), once per slot
+  {
+    GemmProblem q{};
+    q.M = R; q.N = rz; q.Kd = r;
+    q.A = L.g; q.lda = r; q.a_dtype = dt;
+    q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = r; q.seg_end[0] = rz;
+    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = rz;
+    q.w_dtype = dt;
+    q.split = 1; q.out_f32 = L.gf; q.ldo = rz; q.out = nullptr;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
+  // candidate projections P_e E[c], gathered rows
+  {
+    GemmProblem q{};
+    q.M = RK; q.N = r; q.Kd = d->d_embed;
+    q.A = E; q.lda = d->d_embed; q.a_rows = ids; q.a_rows_max = d->V - 1; q.a_dtype = dt;
+    q.w[0] = w->P_e; q.ldw[0] = d->d_embed; q.col0[0] = 0; q.seg_end[0] = r;
+    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = r;
+    q.w_dtype = dt;
+    q.split = L.split_cand; q.out_f32 = L.U; q.ldo = r; q.out = nullptr;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
+  if ((e = launch_ln_rows(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, L.b, dt, st)) != hipSuccess) return e;
+  // z = W_fb b + gf[slot]
+  {
+    GemmProblem q{};
+    q.M = RK; q.N = rz; q.Kd = r;
+    q.A = L.b; q.lda = r; q.a_dtype = dt;
+    q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = 0; q.seg_end[0] = rz;
+    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = rz;
+    q.w_dtype = dt;
+    q.split = 1; q.out = z; q.out_dtype = dt; q.ldo = rz;
+    q.row_bias = L.gf; q.row_bias_div = d->K; q.col_bias = nullptr;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// scoring stage: C = W1s s + b1, then the grid
+hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
+                     const float* cl, float* S, float* C, hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int P = d->n_blocks * (d->B - 1);
+  if (P == 0) return hipSuccess;
+  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
+  const long long ldw1 = 2ll * rz + rs;
+  hipError_t e;
+  {
+    GemmProblem q{};
+    q.M = P; q.N = H; q.Kd = rs;
+    q.A = s; q.lda = rs; q.a_dtype = kDtypeF32;
+    q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 2 * rz; q.seg_end[0] = H;
+    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = H;
+    q.w_dtype = dt;
+    q.split = 1; q.out = C; q.out_dtype = kDtypeF32; q.ldo = H;
+    q.row_bias = nullptr; q.row_bias_div = 1; q.col_bias = w->b1;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
+  GridProblem g{};
+  g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.rz = rz; g.H = H;
+  g.z = z; g.dtype = dt; g.W1 = w->W1; g.ldw1 = ldw1; g.C = C; g.w2 = w->w2; g.b2 = w->b2;
+  g.cand_logits = cl; g.S = S;
+  return launch_grid(g, st);
+}
+
+int check_ws(void* ws, size_t* bytes, size_t need) {
+  if (!bytes) return DCOCO_ERR_INVALID_ARG;
+  if (!ws) {
+    *bytes = need;
+    return 1;   // size query answered
+  }
+  if ((reinterpret_cast<uintptr_t>(ws) % kAlign) != 0 || *bytes < need) return DCOCO_ERR_WORKSPACE;
+  return DCOCO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dcoco_abi_version(void) { return 100; }
+
+const char* dcoco_status_string(int status) {
+  switch (status) {
+    case DCOCO_OK: return "ok";
+    case DCOCO_ERR_INVALID_ARG: return "invalid argument";
+    case DCOCO_ERR_UNSUPPORTED: return "unsupported shape";
+    case DCOCO_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case DCOCO_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dcoco_topk(const dcoco_dims* d, const void* logits, int32_t* cand_ids, float* cand_logits,
+               void* workspace, size_t* workspace_bytes, void* stream) {
+  int rc = check_dims(d, false);
+  if (rc != DCOCO_OK) return rc;
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  if (!topk_supported(dt, d->V, d->K)) return DCOCO_ERR_UNSUPPORTED;
+  const int R = d->n_blocks * d->B;
+  Carve c(nullptr);
+  c.take(topk_workspace_bytes(dt, R, d->V, d->K));
+  rc = check_ws(workspace, workspace_bytes, c.off);
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if (!ptr_ok(logits) || !ptr_ok(cand_ids) || !ptr_ok(cand_logits)) return DCOCO_ERR_INVALID_ARG;
+  return hip_status(launch_topk(dt, logits, R, d->V, d->K, workspace, cand_ids, cand_logits,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_represent(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
+                    const int32_t* cand_ids, void* z, float* s, void* workspace,
+                    size_t* workspace_bytes, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  Carve c(nullptr);
+  carve_rep(c, d);
+  rc = check_ws(workspace, workspace_bytes, c.off);
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if ((rc = check_weights(w, true, false)) != DCOCO_OK) return rc;
+  if (!ptr_ok(h) || !ptr_ok(E) || !ptr_ok(cand_ids) || !ptr_ok(z)) return DCOCO_ERR_INVALID_ARG;
+  if (d->B > 1 && !ptr_ok(s)) return DCOCO_ERR_INVALID_ARG;
+  Carve cw(workspace);
+  const RepLayout L = carve_rep(cw, d);
+  return hip_status(run_represent(d, w, h, E, cand_ids, z, s, L, static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
+                const float* cand_logits, float* S, void* workspace, size_t* workspace_bytes,
+                void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
+  Carve c(nullptr);
+  c.take(sizeof(float) * P * d->d_mlp);
+  rc = check_ws(workspace, workspace_bytes, c.off);
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if ((rc = check_weights(w, false, true)) != DCOCO_OK) return rc;
+  if (P == 0) return DCOCO_OK;
+  if (!ptr_ok(z) || !ptr_ok(s) || !ptr_ok(cand_logits) || !ptr_ok(S)) return DCOCO_ERR_INVALID_ARG;
+  Carve cw(workspace);
+  float* C = static_cast<float*>(cw.take(sizeof(float) * P * d->d_mlp));
+  return hip_status(run_score(d, w, z, s, cand_logits, S, C, static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_select(const dcoco_dims* d, const float* S, const float* cand_logits, const int32_t* cand_ids,
+                 int32_t* sel_idx, int32_t* sel_tok, void* stream) {
+  int rc = check_dims(d, false);
+  if (rc != DCOCO_OK) return rc;
+  if (!ptr_ok(cand_logits) || !ptr_ok(cand_ids) || !ptr_ok(sel_tok) || !opt_ok(sel_idx))
+    return DCOCO_ERR_INVALID_ARG;
+  if (d->B > 1 && !ptr_ok(S)) return DCOCO_ERR_INVALID_ARG;
+  return hip_status(launch_walk(S, cand_logits, cand_ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h,
+                        const void* E, void* workspace, size_t* workspace_bytes, int32_t* sel_tok,
+                        int32_t* sel_idx, float* S_out, int32_t* cand_ids_out, float* cand_logits_out,
+                        void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  if (!topk_supported(dt, d->V, d->K)) return DCOCO_ERR_UNSUPPORTED;
+  const int R = d->n_blocks * d->B;
+  const size_t RK = static_cast<size_t>(R) * d->K;
+  const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
+  auto layout = [&](Carve& c, void** topk_ws, int32_t** ids, float** cl, RepLayout* L, void** z,
+                    float** s, float** C, float** S) {
+    *topk_ws = c.take(topk_workspace_bytes(dt, R, d->V, d->K));
+    *ids = static_cast<int32_t*>(c.take(sizeof(int32_t) * RK));
+    *cl = static_cast<float*>(c.take(sizeof(float) * RK));
+    *L = carve_rep(c, d);
+    *z = c.take(esize(d->dtype) * RK * d->d_z);
+    *s = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_pair));
+    *C = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_mlp));
+    *S = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->K * d->K));
+  };
+  void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* C; float* S;
+  {
+    Carve c(nullptr);
+    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &C, &S);
+    rc = check_ws(workspace, workspace_bytes, c.off);
+    if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  }
+  if ((rc = check_weights(w, true, true)) != DCOCO_OK) return rc;
+  if (!ptr_ok(logits) || !ptr_ok(h) || !ptr_ok(E) || !ptr_ok(sel_tok)) return DCOCO_ERR_INVALID_ARG;
+  if (!opt_ok(sel_idx) || !opt_ok(S_out) || !opt_ok(cand_ids_out) || !opt_ok(cand_logits_out))
+    return DCOCO_ERR_INVALID_ARG;
+  Carve cw(workspace);
+  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &C, &S);
+  if (cand_ids_out) ids = cand_ids_out;
+  if (cand_logits_out) cl = cand_logits_out;
+  if (S_out) S = S_out;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
+  if (e == hipSuccess) e = run_represent(d, w, h, E, ids, z, s, L, st);
+  if (e == hipSuccess) e = run_score(d, w, z, s, cl, S, C, st);
+  if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Host-side launchers of the DCOCO kernels (internal to libdcoco).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dcoco {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBf16 = 1;
+
+// ---------------------------------------------------------------- top-K
+size_t topk_workspace_bytes(int dtype, int rows, int V, int K);
+bool topk_supported(int dtype, int V, int K);
+hipError_t launch_topk(int dtype, const void* logits, int rows, int V, int K, void* partial,
+                       int32_t* ids, float* vals, hipStream_t st);
+
+// ----------------------------------------------------------------- GEMM
+// out = A (M x Kd) * W^T, W being the row-wise concatenation of up to three
+// segments (rows [0,end0) from w[0], [end0,end1) from w[1], [end1,N) from w[2];
+// segment s reads W row j as w[s] + (j - start_s) * ldw[s] + col0[s]).
+// A row m is A + m * lda, or A + a_rows[m] * lda when a_rows is given.
+struct GemmProblem {
+  int M, N, Kd;
+  const void* A;
+  long long lda;
+  const int32_t* a_rows;
+  int a_rows_max;              // gathered ids are clamped into [0, a_rows_max]
+  int a_dtype;                 // kDtypeBf16 / kDtypeF32
+  const void* w[3];
+  long long ldw[3];
+  int col0[3];
+  int seg_end[3];              // seg_end[2] == N
+  int w_dtype;
+  // epilogue
+  int split;                   // > 1: fp32 partial sums out_f32[split][M][ldo]
+  float* out_f32;
+  int ldo;
+  void* out;                   // split == 1 and out != nullptr: converted store
+  int out_dtype;
+  const float* row_bias;       // optional fp32 bias [M / row_bias_div][N]
+  int row_bias_div;
+  const void* col_bias;        // optional bias [N] of type w_dtype
+};
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
+// number of K-splits and partial-buffer bytes chosen for a problem size
+int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype);
+
+// ------------------------------------------------------ row LayerNorm
+// y[m, :] = LN(sum_s x[s][m][col0 : col0 + r]) (non-affine), stored as out_dtype.
+hipError_t launch_ln_rows(const float* x, int split, int M, int ldx, int col0, int r, float eps,
+                          void* y, int out_dtype, hipStream_t st);
+
+// s[n, p, :] = sum_s Y[s][n*B+p][cl : cl+rs] + sum_s Y[s][n*B+p+1][cr : cr+rs]
+hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
+                             int rs, float* s, hipStream_t st);
+
+// ----------------------------------------------------- scoring and walk
+struct GridProblem {
+  int N, B, K, rz, H;
+  const void* z;               // [N, B, K, rz] (dtype)
+  int dtype;
+  const void* W1;              // [H, 2 rz + rs]
+  long long ldw1;
+  const float* C;              // [N, B-1, H] = W1s s + b1 (fp32)
+  const void* w2;              // [H] (dtype)
+  float b2;
+  const float* cand_logits;    // [N, B, K]
+  float* S;                    // [N, B-1, K, K]
+};
+hipError_t launch_grid(const GridProblem& p, hipStream_t st);
+
+hipError_t launch_walk(const float* S, const float* cand_logits, const int32_t* cand_ids, int N,
+                       int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
+
+}  // namespace dcoco

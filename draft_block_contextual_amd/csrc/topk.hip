@@ -1,0 +1,362 @@
+// Top-K candidate extraction over logit rows ([P1] "Keep the leading
+// candidates"; [P2] part 1, paper Sec. 3.2).  P1 = Two Delta, "Two Delta
+// makes NVIDIA Nemotron 3.5 Super even faster with DCOCO"; P2 = review of
+// arXiv 2610.12570, "Contextual Correction of Parallel Drafts for Speculative
+// Decoding".
+//
+// Order: value descending under order_key() (-0 == +0, NaN below -inf), equal
+// values to the lower id.  Every element carries a 64-bit composite
+// (key << 32) | (0xffffffff - id); composites are unique, so "the K largest
+// composites" is exactly the wanted set, whatever the ties.
+//
+// Design (HBM-bound scan; each logit is read once):
+//   * a row is split into chunks of 4 wave segments; one workgroup (4 waves)
+//     per (row, chunk).  A wave segment is 64 lanes x 8 x 16-byte vectors, read
+//     with coalesced 16-byte loads and kept in registers as keys;
+//   * each lane keeps the maximum key of G groups of its vectors.  The K-th
+//     largest of those 64*G group maxima is a lower bound T0 of the segment's
+//     K-th largest key (K distinct elements reach it), so only elements with
+//     key >= T0 can be in the segment's top-K.  On random rows that leaves about
+//     K + a few candidates, appended to LDS;
+//   * an exact radix selection (bit by bit, ballot counts) over the few
+//     candidates picks the segment's top-K; the 4 waves' results are merged the
+//     same way and the workgroup writes K composites per chunk;
+//   * if a segment has more than kCandCap candidates (long runs of equal
+//     values), the wave selects exactly from its registers instead;
+//   * a second kernel merges the chunks of a row, sorts the K winners and
+//     writes ids and the original logit values.
+#include "common.h"
+#include "kernels.h"
+
+namespace dcoco {
+
+namespace {
+
+constexpr int kTopkWaves = 4;
+constexpr int kTopkThreads = kTopkWaves * kWave;
+constexpr int kVecPerLane = 8;
+constexpr int kCandCap = 256;   // candidates a wave may append before it falls back
+
+template <typename T>
+struct TopkShape {
+  static constexpr int kVec = Elem<T>::kPer16B;
+  static constexpr int kEPL = kVecPerLane * kVec;
+  static constexpr int kSeg = kWave * kEPL;
+  static constexpr int kChunk = kTopkWaves * kSeg;
+  static constexpr int kKeyBits = sizeof(T) * 8;
+};
+
+__device__ __forceinline__ uint32_t comp_key(uint64_t c) { return static_cast<uint32_t>(c >> 32); }
+__device__ __forceinline__ uint32_t comp_inv(uint64_t c) { return static_cast<uint32_t>(c); }
+__device__ __forceinline__ uint64_t make_comp(uint32_t key, uint32_t id) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint64_t>(0xffffffffu - id);
+}
+
+// Exact top-K of the composites c[0..Q) held by the lanes of one wave (0 =
+// empty slot).  Marks the min(K, #non-empty) largest in sel[].
+template <int Q, int KEYBITS>
+__device__ void select_topk(const uint64_t (&c)[Q], int K, bool (&sel)[Q]) {
+  uint32_t tk = 0;
+  for (int bit = KEYBITS - 1; bit >= 0; --bit) {
+    const uint32_t cand = tk | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) cnt += __popcll(ballot(c[q] != 0 && comp_key(c[q]) >= cand));
+    if (cnt >= K) tk = cand;
+  }
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const bool v = c[q] != 0;
+    ngt += __popcll(ballot(v && comp_key(c[q]) > tk));
+    neq += __popcll(ballot(v && comp_key(c[q]) == tk));
+  }
+  const int need = K - ngt;
+  uint32_t ti = 0;
+  if (neq > need) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = ti | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        cnt += __popcll(ballot(c[q] != 0 && comp_key(c[q]) == tk && comp_inv(c[q]) >= cand));
+      if (cnt >= need) ti = cand;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint32_t k = comp_key(c[q]);
+    sel[q] = c[q] != 0 && (k > tk || (k == tk && comp_inv(c[q]) >= ti));
+  }
+}
+
+// Select the top-K of src[0..count) (count <= 64*Q) and write them, in any
+// order, to dst[0..K) padded with zeros.  Executed by one whole wave.
+template <int Q, int KEYBITS>
+__device__ void select_to(const uint64_t* src, int count, int K, uint64_t* dst) {
+  const int l = lane_id();
+  uint64_t c[Q];
+  bool sel[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = q * kWave + l;
+    c[q] = i < count ? src[i] : 0ull;
+  }
+  select_topk<Q, KEYBITS>(c, K, sel);
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t m = ballot(sel[q]);
+    if (sel[q]) dst[base + lanes_below(m)] = c[q];
+    base += __popcll(m);
+  }
+  for (int i = base + l; i < K; i += kWave) dst[i] = 0ull;
+}
+
+template <int KEYBITS>
+__device__ void select_small(const uint64_t* src, int count, int K, uint64_t* dst) {
+  if (count <= kWave)
+    select_to<1, KEYBITS>(src, count, K, dst);
+  else if (count <= 2 * kWave)
+    select_to<2, KEYBITS>(src, count, K, dst);
+  else
+    select_to<4, KEYBITS>(src, count, K, dst);
+}
+
+template <typename T, bool kVecLoad>
+__global__ void __launch_bounds__(kTopkThreads)
+topk_partial_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
+                    uint64_t* __restrict__ partial) {
+  using S = TopkShape<T>;
+  constexpr int kVec = S::kVec;
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const T* rowp = logits + static_cast<size_t>(row) * V;
+
+  __shared__ uint64_t s_cand[kTopkWaves][kCandCap];
+  __shared__ uint64_t s_best[kTopkWaves * 64];
+  __shared__ int s_cnt[kTopkWaves];
+
+  const int seg0 = chunk * S::kChunk + w * S::kSeg;
+  if (l == 0) s_cnt[w] = 0;
+
+  uint64_t* wave_out = s_best + w * K;
+  if (seg0 < V) {
+    // ---- load the segment and turn it into keys (padding -> key 0, skipped)
+    uint32_t key[kVecPerLane][kVec];
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i) {
+      const int e0 = seg0 + (i * kWave + l) * kVec;
+      if (kVecLoad && e0 + kVec <= V) {
+        union { uint4 u; T t[kVec]; } v;
+        v.u = *reinterpret_cast<const uint4*>(rowp + e0);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) key[i][j] = order_key(v.t[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) key[i][j] = (e0 + j < V) ? order_key(rowp[e0 + j]) : 0u;
+      }
+    }
+    // ---- group maxima: G groups of kVecPerLane/G vectors per lane
+    const int G = K <= 16 ? 1 : (K <= 32 ? 2 : 4);
+    uint32_t gmax[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) m = max(m, key[i][j]);
+      const int gi = (i * G) / kVecPerLane;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (g == gi) gmax[g] = max(gmax[g], m);
+    }
+    // ---- T0 = K-th largest group maximum
+    uint32_t t0 = 0;
+    for (int bit = S::kKeyBits - 1; bit >= 0; --bit) {
+      const uint32_t cand = t0 | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (g < G) cnt += __popcll(ballot(gmax[g] >= cand));
+      if (cnt >= K) t0 = cand;
+    }
+    // ---- append every real element with key >= T0 (LDS operations of one
+    //      wave complete in order, so s_cnt[w] is already 0 here)
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i) {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int e = seg0 + (i * kWave + l) * kVec + j;
+        if (key[i][j] >= t0 && e < V) {
+          const int pos = atomicAdd(&s_cnt[w], 1);
+          if (pos < kCandCap) s_cand[w][pos] = make_comp(key[i][j], static_cast<uint32_t>(e));
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const int count = s_cnt[w];
+    if (count <= kCandCap) {
+      select_small<S::kKeyBits + 32>(s_cand[w], count, K, wave_out);
+    } else {
+      // ---- exact fallback over the registers: key threshold, then the
+      //      lowest ids among keys equal to it.
+      uint32_t tk = 0;
+      for (int bit = S::kKeyBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = tk | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kVecPerLane; ++i)
+#pragma unroll
+          for (int j = 0; j < kVec; ++j) {
+            const int e = seg0 + (i * kWave + l) * kVec + j;
+            cnt += (key[i][j] >= cand && e < V) ? 1 : 0;
+          }
+        if (wave_sum_i(cnt) >= K) tk = cand;
+      }
+      // keys above tk: fewer than K of them, appended in any order
+      if (l == 0) s_cnt[w] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < kVecPerLane; ++i)
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+          const int e = seg0 + (i * kWave + l) * kVec + j;
+          if (key[i][j] > tk && e < V) {
+            const int pos = atomicAdd(&s_cnt[w], 1);
+            wave_out[pos] = make_comp(key[i][j], static_cast<uint32_t>(e));
+          }
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      int have = s_cnt[w];
+      // keys equal to tk, lowest ids first: vectors in index order
+#pragma unroll
+      for (int i = 0; i < kVecPerLane; ++i) {
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+          const int e = seg0 + (i * kWave + l) * kVec + j;
+          mine += (key[i][j] == tk && e < V) ? 1 : 0;
+        }
+        const int incl = wave_prefix_incl(mine);
+        int pos = have + incl - mine;
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) {
+          const int e = seg0 + (i * kWave + l) * kVec + j;
+          if (key[i][j] == tk && e < V) {
+            if (pos < K) wave_out[pos] = make_comp(tk, static_cast<uint32_t>(e));
+            ++pos;
+          }
+        }
+        have += __shfl(incl, kWave - 1, kWave);
+      }
+      for (int i = min(have, K) + l; i < K; i += kWave) wave_out[i] = 0ull;
+    }
+  } else {
+    for (int i = l; i < K; i += kWave) wave_out[i] = 0ull;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint64_t* dst = partial + (static_cast<size_t>(row) * nchunks + chunk) * K;
+    __shared__ uint64_t s_out[64];
+    select_small<S::kKeyBits + 32>(s_best, kTopkWaves * K, K, s_out);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    for (int i = l; i < K; i += kWave) dst[i] = s_out[i];
+  }
+}
+
+template <typename T, int Q>
+__global__ void __launch_bounds__(kWave)
+topk_merge_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
+                  const uint64_t* __restrict__ partial, int32_t* __restrict__ ids,
+                  float* __restrict__ vals) {
+  constexpr int kKeyBits = sizeof(T) * 8;
+  const int row = blockIdx.x;
+  const int l = lane_id();
+  const int count = nchunks * K;
+  const uint64_t* src = partial + static_cast<size_t>(row) * count;
+  __shared__ uint64_t s_sel[64];
+  uint64_t c[Q];
+  bool sel[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = q * kWave + l;
+    c[q] = i < count ? src[i] : 0ull;
+  }
+  select_topk<Q, kKeyBits + 32>(c, K, sel);
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t m = ballot(sel[q]);
+    if (sel[q]) s_sel[base + lanes_below(m)] = c[q];
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  if (l < base) {
+    const uint64_t mine = s_sel[l];
+    int rank = 0;
+    for (int j = 0; j < base; ++j) rank += s_sel[j] > mine ? 1 : 0;
+    const uint32_t id = 0xffffffffu - comp_inv(mine);
+    ids[static_cast<size_t>(row) * K + rank] = static_cast<int32_t>(id);
+    vals[static_cast<size_t>(row) * K + rank] =
+        Elem<T>::to_f32(logits[static_cast<size_t>(row) * V + id]);
+  }
+}
+
+template <typename T>
+int topk_nchunks(int V) {
+  return (V + TopkShape<T>::kChunk - 1) / TopkShape<T>::kChunk;
+}
+
+template <typename T>
+hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* partial,
+                         int32_t* ids, float* vals, hipStream_t st) {
+  const int nch = topk_nchunks<T>(V);
+  const T* lg = static_cast<const T*>(logits);
+  const bool vec = (static_cast<size_t>(V) * sizeof(T)) % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(logits) % 16) == 0;
+  dim3 g1(nch, rows);
+  if (vec)
+    hipLaunchKernelGGL((topk_partial_kernel<T, true>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
+  else
+    hipLaunchKernelGGL((topk_partial_kernel<T, false>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
+  const int count = nch * K;
+  const int q = (count + kWave - 1) / kWave;
+#define DCOCO_MERGE(QQ)                                                                     \
+  hipLaunchKernelGGL((topk_merge_kernel<T, QQ>), dim3(rows), dim3(kWave), 0, st, lg, V, K, nch, \
+                     partial, ids, vals)
+  if (q <= 1) DCOCO_MERGE(1);
+  else if (q <= 2) DCOCO_MERGE(2);
+  else if (q <= 4) DCOCO_MERGE(4);
+  else if (q <= 8) DCOCO_MERGE(8);
+  else if (q <= 16) DCOCO_MERGE(16);
+  else DCOCO_MERGE(32);
+#undef DCOCO_MERGE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int dtype, int rows, int V, int K) {
+  const int nch = dtype == kDtypeBf16 ? topk_nchunks<bf16>(V) : topk_nchunks<float>(V);
+  return static_cast<size_t>(rows) * nch * K * sizeof(uint64_t);
+}
+
+bool topk_supported(int dtype, int V, int K) {
+  const int nch = dtype == kDtypeBf16 ? topk_nchunks<bf16>(V) : topk_nchunks<float>(V);
+  return static_cast<long long>(nch) * K <= 32 * kWave;
+}
+
+hipError_t launch_topk(int dtype, const void* logits, int rows, int V, int K, void* partial,
+                       int32_t* ids, float* vals, hipStream_t st) {
+  if (dtype == kDtypeBf16)
+    return launch_topk_t<bf16>(logits, rows, V, K, static_cast<uint64_t*>(partial), ids, vals, st);
+  return launch_topk_t<float>(logits, rows, V, K, static_cast<uint64_t*>(partial), ids, vals, st);
+}
+
+}  // namespace dcoco

@@ -1,0 +1,171 @@
+/*
+ * dcoco.h - C ABI of the DCOCO contextual-corrector hot path for AMD MI355X
+ * (gfx950).
+ *
+ * DCOCO re-selects the tokens of a parallel draft block.  For every block of
+ * B slots it keeps each slot's top-K draft candidates, builds a representation
+ * of every candidate and of every pair of neighbouring slots, scores all
+ * (B-1)K^2 transitions between neighbouring candidates with one shared
+ * two-layer MLP added to the later candidate's draft logit, and walks the
+ * scored grid left to right, each slot taking the best successor of the token
+ * actually chosen before it.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] Two Delta, "Two Delta makes NVIDIA Nemotron 3.5 Super even faster
+ *        with DCOCO" (twodelta.com/blog/dcoco), section "How DCOCO works".
+ *   [P2] review of arXiv 2610.12570, "Contextual Correction of Parallel Drafts
+ *        for Speculative Decoding" (jaehun.me/posts/paper-2610-12570), section
+ *        "New approach: DCOCO", parts 1 (paper Sec. 3.2) and 2 (paper
+ *        Sec. 3.3).
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device,
+ *     16-byte aligned, row-major, owned by the caller.  The library never
+ *     allocates or frees device memory and keeps no pointer after returning.
+ *   - Matrices use the [out, in] layout of a linear layer: y = W x reads row o
+ *     of W for output o.
+ *   - dims->dtype selects the storage type of logits, h, E, the weight
+ *     matrices, b1, w2 and of the representation z: DCOCO_BF16 (bf16 values,
+ *     fp32 accumulation) or DCOCO_F32.  Candidate logits, pair states s and
+ *     scores S are always fp32; ids and indices int32.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without waiting.  Buffers must stay valid until the
+ *     stream has finished the work.  Calls on different streams with separate
+ *     workspaces may run concurrently.
+ *   - Entry points that take `workspace`: with workspace == NULL the call
+ *     stores the number of bytes it needs in *workspace_bytes and returns
+ *     DCOCO_OK without launching anything.  Otherwise *workspace_bytes must
+ *     hold the size of the caller's buffer (256-byte aligned), which must be
+ *     at least that number.  The workspace holds no state between calls.
+ *   - Arguments are checked before anything is launched; a failed check
+ *     returns a negative dcoco_status and enqueues nothing.  No C++ exception
+ *     crosses this interface.  A launch failure returns DCOCO_ERR_HIP.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     run after run.
+ *
+ * Supported shapes: n_blocks >= 1, B >= 1, 1 <= K <= min(V, 64); d_hidden,
+ * d_embed, d_proj, d_z, d_pair and d_mlp positive multiples of 32, with
+ * d_proj, d_z <= 2048 and d_pair <= 8192; ln_eps > 0.  Valid shapes outside
+ * this set return DCOCO_ERR_UNSUPPORTED.
+ */
+#ifndef DCOCO_H
+#define DCOCO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DCOCO_OK = 0,
+  DCOCO_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, bad eps */
+  DCOCO_ERR_UNSUPPORTED = -2,   /* valid but outside the supported shape set */
+  DCOCO_ERR_WORKSPACE = -3,     /* workspace too small or misaligned */
+  DCOCO_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} dcoco_status;
+
+typedef enum { DCOCO_F32 = 0, DCOCO_BF16 = 1 } dcoco_dtype;
+
+/* Problem shape.  Notation: B slots per draft block, K candidates per slot,
+ * V vocabulary size, d_hidden = d (h_i in R^d), d_embed = e (rows of E),
+ * d_proj = r (width of b_{i,k} and g_i), d_z = width of z_{i,k},
+ * d_pair = width of s_p, d_mlp = H (hidden width of Delta_theta). */
+typedef struct {
+  int32_t n_blocks;   /* N: independent draft blocks (decoding streams) per call */
+  int32_t B, K, V;
+  int32_t d_hidden, d_embed, d_proj, d_z, d_pair, d_mlp;
+  int32_t dtype;      /* dcoco_dtype */
+  float ln_eps;       /* LayerNorm epsilon (> 0) */
+} dcoco_dims;
+
+/* Corrector parameters, shared by every slot and transition ([P2] part 1,
+ * paper Sec. 3.2).  Storage type = dims.dtype; b2 is passed by value.
+ *   P_e    [d_proj, d_embed]        candidate embedding projection
+ *   P_h    [d_proj, d_hidden]       slot hidden-state projection
+ *   W_f    [d_z, 2*d_proj]          fusion f; columns [b | g]
+ *   W_pair [d_pair, 2*d_hidden]     pair state; columns [h_p | h_{p+1}]
+ *   W1     [d_mlp, 2*d_z + d_pair]  MLP layer 1; columns [z_a | z_b | s]
+ *   b1     [d_mlp]                  MLP layer-1 bias (NULL means zeros)
+ *   w2     [d_mlp]                  MLP output layer (scalar output)
+ *   b2                              MLP output bias */
+typedef struct {
+  const void *P_e, *P_h, *W_f, *W_pair, *W1, *b1, *w2;
+  float b2;
+} dcoco_weights;
+
+/* Top-K candidate extraction ([P1] "Keep the leading candidates"; [P2]
+ * part 1, paper Sec. 3.2).
+ *   logits      [n_blocks*B, V] dtype    the drafter's raw logits
+ *   cand_ids    [n_blocks*B, K] int32    out: c_{i,k}
+ *   cand_logits [n_blocks*B, K] fp32     out: l_i(k), the logit value widened
+ * Each row's K largest logits, sorted by value descending; equal values go to
+ * the lower id; -0 equals +0; NaN ranks below every number. */
+int dcoco_topk(const dcoco_dims* dims, const void* logits, int32_t* cand_ids,
+               float* cand_logits, void* workspace, size_t* workspace_bytes,
+               void* stream);
+
+/* Candidate and slot representations and pair states ([P1] "Score
+ * neighboring candidates in parallel"; [P2] part 1, paper Sec. 3.2).
+ *   h        [n_blocks, B, d_hidden] dtype   drafter hidden states h_i
+ *   E        [V, d_embed] dtype              frozen token-embedding table
+ *   cand_ids [n_blocks, B, K] int32          candidates (ids must be < V)
+ *   z        [n_blocks, B, K, d_z] dtype     out: z_{i,k} = W_f [b_{i,k}; g_i]
+ *   s        [n_blocks, B-1, d_pair] fp32    out: s_p = W_pair [h_p; h_{p+1}]
+ * with g_i = LN(P_h h_i), b_{i,k} = LN(P_e E[c_{i,k}]), LN non-affine.  In
+ * bf16 mode g, b and z are rounded to bf16 (nearest-even); s is not. */
+int dcoco_represent(const dcoco_dims* dims, const dcoco_weights* w, const void* h,
+                    const void* E, const int32_t* cand_ids, void* z, float* s,
+                    void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Transition scores ([P1] "Score neighboring candidates in parallel"; [P2]
+ * part 1, paper Sec. 3.2):
+ *   S[n,p,a,b] = l_{p+1}(b) + w2 . SiLU(W1 [z_{p,a}; z_{p+1,b}; s_p] + b1) + b2
+ *   z           [n_blocks, B, K, d_z] dtype
+ *   s           [n_blocks, B-1, d_pair] fp32
+ *   cand_logits [n_blocks, B, K] fp32
+ *   S           [n_blocks, B-1, K, K] fp32   out (unnormalised) */
+int dcoco_score(const dcoco_dims* dims, const dcoco_weights* w, const void* z,
+                const float* s, const float* cand_logits, float* S,
+                void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Prefix-first greedy walk ([P1] "Select using the realized token
+ * identities"; [P2] part 2, paper Sec. 3.3): k_1 = argmax_k l_1(k);
+ * k_{p+1} = argmax_b S_p(k_p, b); y_p = c_{p, k_p}.  argmax takes the lowest
+ * index among equal maxima and never picks NaN (index 0 if a row is all NaN).
+ *   S        [n_blocks, B-1, K, K] fp32
+ *   cand_logits [n_blocks, B, K] fp32
+ *   cand_ids [n_blocks, B, K] int32
+ *   sel_idx  [n_blocks, B] int32   out: k_p (may be NULL)
+ *   sel_tok  [n_blocks, B] int32   out: y_p */
+int dcoco_select(const dcoco_dims* dims, const float* S, const float* cand_logits,
+                 const int32_t* cand_ids, int32_t* sel_idx, int32_t* sel_tok,
+                 void* stream);
+
+/* The whole path for n_blocks draft blocks: top-K, representations, pair
+ * states, transition scores and the greedy walk, on one stream.
+ *   logits [n_blocks*B, V], h [n_blocks, B, d_hidden], E [V, d_embed]: dtype
+ *   sel_tok         [n_blocks, B] int32           out: the corrected block
+ *   sel_idx         [n_blocks, B] int32           out, may be NULL
+ *   S_out           [n_blocks, B-1, K, K] fp32    out, may be NULL
+ *   cand_ids_out    [n_blocks, B, K] int32        out, may be NULL
+ *   cand_logits_out [n_blocks, B, K] fp32         out, may be NULL */
+int dcoco_correct_block(const dcoco_dims* dims, const dcoco_weights* w,
+                        const void* logits, const void* h, const void* E,
+                        void* workspace, size_t* workspace_bytes,
+                        int32_t* sel_tok, int32_t* sel_idx, float* S_out,
+                        int32_t* cand_ids_out, float* cand_logits_out,
+                        void* stream);
+
+/* Static description of a status code. */
+const char* dcoco_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int dcoco_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCOCO_H */

@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/dcoco.h declares, answers workspace queries and rejects bad arguments
+before launching anything.  No GPU needed: every call here returns before the
+library touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "dcoco.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcoco_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    import draft_block_contextual_amd as dc
+    names = _declared_functions()
+    assert set(names) == set(dc.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    import draft_block_contextual_amd as dc
+    assert lib.dcoco_abi_version() == 100
+    assert dc.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert dc.status_string(code) not in ("ok", "unknown status")
+    assert dc.status_string(7) == "unknown status"
+
+
+def _dims(**kw):
+    import draft_block_contextual_amd as dc
+    base = dict(n_blocks=32, B=16, K=16, V=151936, d_hidden=4096, d_embed=4096, d_proj=256,
+                d_z=256, d_pair=256, d_mlp=512, dtype="bf16", ln_eps=1e-5)
+    base.update(kw)
+    return dc.Dims(**base)
+
+
+def _query_topk(lib, dims):
+    cd = dims.c()
+    n = ctypes.c_size_t(0)
+    rc = lib.dcoco_topk(ctypes.byref(cd), None, None, None, None, ctypes.byref(n), None)
+    return rc, n.value
+
+
+def _query_block(lib, dims):
+    import draft_block_contextual_amd as dc
+    cd = dims.c()
+    cw = dc.CWeights()
+    n = ctypes.c_size_t(0)
+    rc = lib.dcoco_correct_block(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None,
+                                 ctypes.byref(n), None, None, None, None, None, None)
+    return rc, n.value
+
+
+def test_workspace_queries(lib):
+    rc, n = _query_topk(lib, _dims())
+    assert rc == 0 and n > 0
+    rc, n = _query_block(lib, _dims())
+    assert rc == 0 and n >= 16 * 2 ** 20
+    rc, n2 = _query_block(lib, _dims(n_blocks=4))
+    assert rc == 0 and 0 < n2 < n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_blocks=0), -1), (dict(B=0), -1), (dict(K=0), -1), (dict(K=20, V=10), -1),
+    (dict(ln_eps=0.0), -1), (dict(ln_eps=float("nan")), -1), (dict(ln_eps=-1.0), -1),
+    (dict(K=65), -2), (dict(d_proj=48), -2), (dict(d_proj=0), -1), (dict(d_mlp=-32), -1),
+    (dict(d_z=4096), -2), (dict(d_hidden=100), -2),
+])
+def test_invalid_dims_rejected(lib, kw, code):
+    rc, _ = _query_block(lib, _dims(**kw))
+    assert rc == code
+
+
+def test_bad_dtype_rejected(lib):
+    d = _dims()
+    cd = d.c()
+    cd.dtype = 7
+    n = ctypes.c_size_t(0)
+    assert lib.dcoco_topk(ctypes.byref(cd), None, None, None, None, ctypes.byref(n), None) == -1
+
+
+def test_workspace_and_pointer_checks(lib):
+    import draft_block_contextual_amd as dc
+    d = _dims()
+    cd = d.c()
+    rc, need = _query_topk(lib, d)
+    fake = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced: checks fail first
+    small = ctypes.c_size_t(need - 256)
+    assert lib.dcoco_topk(ctypes.byref(cd), fake, fake, fake, fake, ctypes.byref(small), None) == -3
+    ok = ctypes.c_size_t(need)
+    mis = ctypes.c_void_p((1 << 20) + 128)
+    assert lib.dcoco_topk(ctypes.byref(cd), fake, fake, fake, mis, ctypes.byref(ok), None) == -3
+    # null or misaligned data pointers
+    assert lib.dcoco_topk(ctypes.byref(cd), None, fake, fake, fake, ctypes.byref(ok), None) == -1
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.dcoco_topk(ctypes.byref(cd), odd, fake, fake, fake, ctypes.byref(ok), None) == -1
+    # a missing workspace_bytes pointer
+    assert lib.dcoco_topk(ctypes.byref(cd), fake, fake, fake, None, None, None) == -1
+    # missing weights in the full path
+    rc, need_b = _query_block(lib, d)
+    cw = dc.CWeights()
+    nb = ctypes.c_size_t(need_b)
+    assert lib.dcoco_correct_block(ctypes.byref(cd), ctypes.byref(cw), fake, fake, fake, fake,
+                                   ctypes.byref(nb), fake, None, None, None, None, None) == -1
+    # select: null outputs
+    assert lib.dcoco_select(ctypes.byref(cd), fake, fake, fake, None, None, None) == -1
+
+
+def test_unsupported_vocab_for_topk(lib):
+    # the row merge holds at most 2048 chunk candidates
+    rc, _ = _query_topk(lib, _dims(K=64, V=600000))
+    assert rc == -2

@@ -1,0 +1,345 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: top-K ids and selected paths bit-exact; S within 3e-2 absolute on the
+bf16 path and 1e-4 relative on the fp32 path; end-to-end tokens identical
+wherever the oracle's best-vs-second margin exceeds 0.1.  Full-size shapes are
+run in the same launch configuration the benchmark times and compared on
+sampled blocks (blocks are independent).
+"""
+import functools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from helpers import (device_inputs, ensure_built, lockstep_path_check, s_tolerance_ok, to_dev,
+                     PATH_MARGIN)
+from oracle import dcoco_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    ensure_built()
+    print(f"device: {torch.cuda.get_device_name(0)}", flush=True)
+
+
+def _np(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return (t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=4)
+def _inputs(name, n_blocks=None):
+    return synth.make_inputs(name, n_blocks=n_blocks)
+
+
+@functools.lru_cache(maxsize=8)
+def _oracle(name, blocks=None):
+    inp = _inputs(name)
+    return O.correct_block(inp, blocks=None if blocks is None else list(blocks))
+
+
+SMALL = ["tiny", "tiny_zero", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "mid_f32",
+         "k64_small", "k32_small"]
+
+
+def _run_block(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    inp = _inputs(name)
+    dims, w, logits, h, E = device_inputs(inp)
+    out = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    torch.cuda.synchronize()
+    return inp, {k: _np(v) for k, v in out.items()}
+
+
+# ------------------------------------------------------------------ top-K
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_f32", "mid_bf16", "k64_small", "k32_small"])
+def test_topk_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case topk {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    dims = dc.Dims.from_synth(D)
+    logits = to_dev(inp["logits"].reshape(-1, D.V), D.dtype)
+    ids, vals = dc.topk(dims, logits)
+    torch.cuda.synchronize()
+    ref = _oracle(name)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref["cand_ids"].reshape(-1, D.K))
+    np.testing.assert_array_equal(vals.cpu().numpy().astype(np.float64), ref["cand_vals"].reshape(-1, D.K))
+
+
+def _special_rows(V, dtype, seed):
+    g = np.random.default_rng(seed)
+    rows = [
+        np.full(V, 1.5),                                    # all equal
+        g.choice([-1.0, 0.0, 2.0, 2.5], size=V),            # few distinct values
+        g.choice([0.0, -0.0, 1.0, -np.inf], size=V),        # signed zeros, -inf
+        np.arange(V, dtype=np.float64) * (8.0 / V),         # ascending ramp
+        np.arange(V, 0, -1, dtype=np.float64) * (8.0 / V),  # descending ramp
+        np.round(g.standard_normal(V) * 2) / 2,             # many ties
+        g.standard_normal(V),
+    ]
+    r = g.standard_normal(V)
+    r[g.integers(0, V, 40)] = np.nan
+    rows.append(r)
+    rows.append(g.choice([np.inf, -np.inf, np.nan, 0.0], size=V))
+    r = np.full(V, np.nan)
+    r[g.integers(0, V, 3)] = -5.0
+    rows.append(r)                                          # almost all NaN
+    a = np.array(rows)
+    if dtype == "bf16":
+        return synth.f32_to_bf16_bits(a.astype(np.float32))
+    return a.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V,K", [(5003, 1), (5003, 7), (40000, 16), (40000, 64), (151936, 16), (70, 64)])
+def test_topk_ties_and_special_values(dtype, V, K):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case topk special {dtype} V={V} K={K}", flush=True)
+    rows = _special_rows(V, dtype, seed=V + K)
+    R = rows.shape[0]
+    dims = dc.Dims(R, 1, K, V, 32, 32, 32, 32, 32, 32, dtype)
+    ids, vals = dc.topk(dims, to_dev(rows, dtype))
+    torch.cuda.synchronize()
+    ref_ids, ref_vals = O.top_k(O.to_f64(rows, dtype), K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    got = vals.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref_vals))
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref_vals[~np.isnan(ref_vals)])
+
+
+# ------------------------------------------------------------------- walk
+
+def _select(S, vals, ids):
+    import draft_block_contextual_amd as dc
+    import torch
+    N, B, K = vals.shape
+    dims = dc.Dims(N, B, K, max(K, 1), 32, 32, 32, 32, 32, 32, "f32")
+    Sd = torch.from_numpy(np.ascontiguousarray(S, dtype=np.float32)).cuda() if B > 1 else None
+    if Sd is None:
+        Sd = torch.zeros(1, dtype=torch.float32, device="cuda")
+    si, st = dc.select(dims, Sd, torch.from_numpy(vals.astype(np.float32)).cuda(),
+                       torch.from_numpy(ids.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    return si.cpu().numpy(), st.cpu().numpy()
+
+
+def test_select_matches_oracle_walk():
+    g = np.random.default_rng(3)
+    for N, B, K in [(5, 16, 16), (3, 7, 64), (4, 16, 3), (2, 1, 5), (6, 40, 32)]:
+        print(f"case select N={N} B={B} K={K}", flush=True)
+        S = (np.round(g.standard_normal((N, max(B - 1, 0), K, K)) * 4) / 4).astype(np.float32)
+        S[S > 1.7] = np.nan
+        vals = np.sort(g.standard_normal((N, B, K)))[..., ::-1].astype(np.float32)
+        ids = g.integers(0, 100000, (N, B, K)).astype(np.int32)
+        si, st = _select(S, vals, ids)
+        ri, rt, _ = O.greedy_walk(S.astype(np.float64), vals.astype(np.float64), ids)
+        np.testing.assert_array_equal(si, ri)
+        np.testing.assert_array_equal(st, rt)
+
+
+def test_select_worked_example():
+    with open(os.path.join(GOLD, "worked_example.json")) as f:
+        W = json.load(f)
+    B, K = W["B"], W["K"]
+    for name, rd in W["readings"].items():
+        for case in rd["cases"]:
+            ell = np.array(rd["logits"], np.float32)
+            S = np.zeros((1, B - 1, K, K), np.float32)
+            for p in range(B - 1):
+                S[0, p] = ell[p + 1][None, :]
+            for p, a, b, v in case.get("plants", []):
+                S[0, p, a, b] += np.float32(v)
+            ids = np.arange(B * K, dtype=np.int32).reshape(1, B, K)
+            si, st = _select(S, ell[None], ids)
+            assert list(si[0]) == case["path"], (name, case)
+
+
+# ------------------------------------------------------ representation
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_f32", "mid_bf16", "k32_small"])
+def test_represent_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case represent {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    dims, w, logits, h, E = device_inputs(inp)
+    ids = torch.from_numpy(ref["cand_ids"].astype(np.int32)).cuda()
+    z, s = dc.represent(dims, w, h, E, ids)
+    torch.cuda.synchronize()
+    z = _np(z).astype(np.float64)
+    s = _np(s).astype(np.float64)
+    if D.dtype == "bf16":
+        # one bf16 step of |z| where fp32 and fp64 sums round differently
+        assert np.all(np.abs(z - ref["z"]) <= 2.0 ** -7 * np.abs(ref["z"]) + 1e-3)
+        assert np.mean(z == ref["z"]) > 0.98
+        np.testing.assert_allclose(s, ref["s"], rtol=0, atol=2e-2)
+    else:
+        np.testing.assert_allclose(z, ref["z"], rtol=1e-4, atol=1e-4)
+        np.testing.assert_allclose(s, ref["s"], rtol=1e-4, atol=1e-3)
+
+
+@pytest.mark.parametrize("name", ["tiny_bias", "small_bf16", "small_f32", "mid_bf16", "k64_small"])
+def test_score_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case score {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    dims, w, logits, h, E = device_inputs(inp)
+    zst = ref["z"].astype(np.float32)
+    if D.dtype == "bf16":
+        zst = synth.f32_to_bf16_bits(zst)      # the oracle's z is bf16-valued: exact
+    z = to_dev(zst, D.dtype)
+    s = torch.from_numpy(ref["s"].astype(np.float32)).cuda()
+    cl = torch.from_numpy(ref["cand_vals"].astype(np.float32)).cuda()
+    S = dc.score(dims, w, z, s, cl)
+    torch.cuda.synchronize()
+    # reference S from the same fp32-stored s
+    Sref = O.transition_scores(ref["z"], ref["s"].astype(np.float32).astype(np.float64), ref["cand_vals"],
+                               O.to_f64(inp["W1"], D.dtype), O.to_f64(inp["b1"], D.dtype),
+                               O.to_f64(inp["w2"], D.dtype), inp["b2"])
+    ok, worst, nbad = s_tolerance_ok(_np(S), Sref, D.dtype)
+    assert ok, f"{nbad} scores out of tolerance, worst |dS| = {worst}"
+
+
+# ---------------------------------------------------------- whole path
+
+@pytest.mark.parametrize("name", SMALL)
+def test_correct_block_matches_oracle(name):
+    print(f"case correct_block {name}", flush=True)
+    inp, out = _run_block(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    np.testing.assert_array_equal(out["cand_ids"], ref["cand_ids"])
+    np.testing.assert_array_equal(out["cand_logits"].astype(np.float64), ref["cand_vals"])
+    ok, worst, nbad = s_tolerance_ok(out["S"], ref["S"], D.dtype)
+    assert ok, f"{nbad} scores out of tolerance, worst |dS| = {worst}"
+    ok, cmp, tot, fail = lockstep_path_check(out["S"], ref["S"], ref["cand_vals"], out["sel_idx"], ref["sel_idx"])
+    assert ok, f"path differs at a step with margin > {PATH_MARGIN}: {fail}"
+    # tokens are the selected candidates' ids
+    N, B, K = ref["cand_ids"].shape
+    np.testing.assert_array_equal(out["sel_tok"], out["cand_ids"][np.arange(N)[:, None], np.arange(B)[None], out["sel_idx"]])
+    # the walk on the GPU's own scores is exact
+    ri, rt, _ = O.greedy_walk(out["S"].astype(np.float64), out["cand_logits"].astype(np.float64), out["cand_ids"])
+    np.testing.assert_array_equal(out["sel_idx"], ri)
+
+
+@pytest.mark.parametrize("name", ["tiny_zero", "small_bf16", "mid_bf16", "k64_small"])
+def test_zero_output_layer_reproduces_drafter(name):
+    import dataclasses
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case zero output layer {name}", flush=True)
+    inp = dict(_inputs(name))
+    D = inp["dims"]
+    inp["w2"] = np.zeros_like(inp["w2"])
+    inp["b2"] = 0.0
+    dims, w, logits, h, E = device_inputs(inp)
+    out = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    torch.cuda.synchronize()
+    S = out["S"].cpu().numpy()
+    cl = out["cand_logits"].cpu().numpy()
+    for p in range(D.B - 1):
+        for a in range(D.K):
+            np.testing.assert_array_equal(S[:, p, a, :], cl[:, p + 1, :])   # bit-exact
+    np.testing.assert_array_equal(out["sel_idx"].cpu().numpy(), 0)
+    lg = O.to_f64(inp["logits"], D.dtype)
+    np.testing.assert_array_equal(out["sel_tok"].cpu().numpy(), np.argmax(lg, axis=-1))
+
+
+def test_deterministic_bitwise():
+    import draft_block_contextual_amd as dc
+    import torch
+    print("case determinism mid_bf16", flush=True)
+    inp = _inputs("mid_bf16")
+    dims, w, logits, h, E = device_inputs(inp)
+    a = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    a = {k: v.clone() for k, v in a.items()}
+    b = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
+
+
+def test_worked_example_end_to_end():
+    import draft_block_contextual_amd as dc
+    import torch
+    with open(os.path.join(GOLD, "worked_example.json")) as f:
+        W = json.load(f)
+    B, K = W["B"], W["K"]
+    V, d, r, H = 12, 32, 32, 32
+    g = np.random.default_rng(16)
+    for name in ["W-lit", "W-rank"]:
+        rd = W["readings"][name]
+        lg = np.full((B, V), -10.0, np.float32)
+        for p in range(B):
+            for j in range(K):
+                lg[p, 3 * p + j] = rd["logits"][p][j]
+        dims = dc.Dims(1, B, K, V, d, d, r, r, r, H, "f32")
+        f = lambda *s: torch.from_numpy((g.standard_normal(s) * 0.1).astype(np.float32)).cuda()
+        w = dc.Weights(P_e=f(r, d), P_h=f(r, d), W_f=f(r, 2 * r), W_pair=f(r, 2 * d), W1=f(H, 3 * r),
+                       b1=None, w2=torch.zeros(H, device="cuda"), b2=0.0)
+        out = dc.correct_block(dims, w, torch.from_numpy(lg).cuda(), f(1, B, d) * 300, f(V, d) * 0.2)
+        torch.cuda.synchronize()
+        toks = out["sel_tok"].cpu().numpy()[0]
+        words = [W["tokens"][p][int(t) - 3 * p] for p, t in enumerate(toks)]
+        case = [c for c in rd["cases"] if c["delta"] == "zero"][0]
+        assert " ".join(words) == case["text"]
+
+
+# ------------------------------------------------- full-size workloads
+
+def _full_size(name, blocks):
+    print(f"case full size {name} blocks={blocks}", flush=True)
+    inp, out = _run_block(name)
+    D = inp["dims"]
+    ref = O.correct_block(inp, blocks=list(blocks))
+    sl = list(blocks)
+    np.testing.assert_array_equal(out["cand_ids"][sl], ref["cand_ids"])
+    ok, worst, nbad = s_tolerance_ok(out["S"][sl], ref["S"], D.dtype)
+    assert ok, f"{nbad} scores out of tolerance, worst |dS| = {worst}"
+    ok, cmp, tot, fail = lockstep_path_check(out["S"][sl], ref["S"], ref["cand_vals"], out["sel_idx"][sl],
+                                             ref["sel_idx"])
+    assert ok, f"path differs at a step with margin > {PATH_MARGIN}: {fail}"
+    print(f"  worst |dS| = {worst:.3g}; path steps compared {cmp}/{tot}", flush=True)
+    # the planted peaks are each row's known top-K
+    cfg = inp["cfg"]
+    for n in sl:
+        pid, _ = synth.planted_peaks(cfg, n)
+        np.testing.assert_array_equal(out["cand_ids"][n], pid[:, :D.K])
+    return inp, out
+
+
+def test_full_q8b_1():
+    _full_size("q8b_1", (0,))
+
+
+def test_full_q8b_32_sampled():
+    _full_size("q8b_32", (0, 13, 31))
+
+
+def test_full_kstress_sampled():
+    _full_size("kstress", (5,))
+
+
+def test_full_large_sampled():
+    _full_size("large", (0, 63))
