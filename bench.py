@@ -1,0 +1,256 @@
+"""Benchmark of the DCOCO corrector hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--workload q8b_32]
+
+A step is one dcoco_correct_block call: top-K, representations, pair states,
+transition scores and the greedy walk for N draft blocks.  The default
+workload is 32 streams of B = 16 slots, K = 16 candidates, d = 4096,
+V = 151936 (bf16 storage, fp32 accumulation).  Inputs are seeded synthetic
+tensors resident in HBM before timing starts; R >= 4 independently seeded
+input sets (logits and hidden states; the embedding table and the weights are
+shared) rotate from step to step so that one step's logits are not still in
+the 256 MB Infinity Cache from the step before.
+
+Prints one JSON line: blocks/s over the timed steps, plus per-stage times
+from HIP events on the stream the stages run on, the roofline of the dominant
+kernel and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+# fp32 vector issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-ops/s
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="q8b_32")
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=2)
+    ap.add_argument("--sweep", action="store_true", help="also time 4/8/16 streams")
+    return ap.parse_args()
+
+
+def algorithmic_work(D):
+    """Bytes and flops the method itself must move / compute per call."""
+    e = 2 if D.dtype == "bf16" else 4
+    R = D.n_blocks * D.B
+    RK = R * D.K
+    P = D.n_blocks * (D.B - 1)
+    w_params = (D.r * D.e + D.r * D.d + D.r_z * 2 * D.r + D.r_s * 2 * D.d
+                + D.H * (2 * D.r_z + D.r_s) + 2 * D.H)
+    return {
+        "logit_bytes": R * D.V * e,
+        "gather_bytes": RK * D.e * e,
+        "h_bytes": R * D.d * e,
+        "weight_bytes": w_params * e,
+        "mfma_flops": 2.0 * (RK * D.e * D.r + R * D.d * (D.r + 2 * D.r_s) + R * D.r * D.r_z
+                             + RK * D.r * D.r_z + 2 * RK * D.r_z * D.H),
+        "grid_elems": P * D.K * D.K * D.H,
+        "transitions": P * D.K * D.K,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(blocks are independent; sharding would split the streams).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import draft_block_contextual_amd as dc
+    import synth
+
+    def to_dev(a, dtype, device):
+        if dtype == "bf16":
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return t.to(device)
+
+    if not os.path.exists(dc.LIB_PATH):
+        from draft_block_contextual_amd import build as _b
+        _b.build()
+    dc.load()
+    cfg = synth.get_config(args.workload)
+    D = cfg.dims
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"# generating inputs for {cfg.name}: {cfg.desc}", file=sys.stderr, flush=True)
+    base = synth.make_inputs(cfg)
+    sets = [{"logits": base["logits"], "h": base["h"]}]
+    for j in range(1, args.sets):
+        sets.append(synth.make_stream_inputs(cfg, cfg.seed + 100 * j))
+    dims = dc.Dims.from_synth(D)
+    dt = D.dtype
+    w = dc.Weights(P_e=to_dev(base["P_e"], dt, dev), P_h=to_dev(base["P_h"], dt, dev),
+                   W_f=to_dev(base["W_f"], dt, dev), W_pair=to_dev(base["W_pair"], dt, dev),
+                   W1=to_dev(base["W1"], dt, dev), b1=to_dev(base["b1"], dt, dev),
+                   w2=to_dev(base["w2"], dt, dev), b2=base["b2"])
+    E = to_dev(base["E"], dt, dev)
+    dsets = [(to_dev(s["logits"].reshape(D.n_blocks * D.B, D.V), dt, dev), to_dev(s["h"], dt, dev))
+             for s in sets]
+    N, B, K = D.n_blocks, D.B, D.K
+    sel_tok = torch.empty((N, B), dtype=torch.int32, device=dev)
+    ws = torch.empty(dc.correct_block_workspace_bytes(dims, w), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    print("# inputs resident; warming up", file=sys.stderr, flush=True)
+
+    def step(i):
+        lg, h = dsets[i % len(dsets)]
+        dc.correct_block(dims, w, lg, h, E, sel_tok=sel_tok, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    blocks_per_s = N * args.steps / (gpu_ms / 1e3)
+    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})",
+          file=sys.stderr, flush=True)
+
+    # ---- per-stage times: each entry point alone, between events on the same stream
+    R = N * B
+    ids = torch.empty((R, K), dtype=torch.int32, device=dev)
+    cl = torch.empty((R, K), dtype=torch.float32, device=dev)
+    z = torch.empty((N, B, K, D.r_z), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=dev)
+    s = torch.empty((N, max(B - 1, 1), D.r_s), dtype=torch.float32, device=dev)
+    S = torch.empty((N, max(B - 1, 1), K, K), dtype=torch.float32, device=dev)
+    si = torch.empty((N, B), dtype=torch.int32, device=dev)
+    stages = {
+        "topk": lambda i: dc.topk(dims, dsets[i % len(dsets)][0], ids, cl, workspace=ws, stream=stream),
+        "represent": lambda i: dc.represent(dims, w, dsets[i % len(dsets)][1], E, ids, z, s, workspace=ws,
+                                            stream=stream),
+        "score": lambda i: dc.score(dims, w, z, s, cl, S, workspace=ws, stream=stream),
+        "select": lambda i: dc.select(dims, S, cl, ids, si, sel_tok, stream=stream),
+    }
+    stage_us = {}
+    for name, fn in stages.items():
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.stage_reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        stage_us[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    print(f"# stage us: {stage_us}", file=sys.stderr, flush=True)
+
+    work = algorithmic_work(D)
+    # dominant stage and its roofline
+    topk_gbs = work["logit_bytes"] / (stage_us["topk"] * 1e-6) / 1e9
+    grid_rate = work["grid_elems"] * 6 / (stage_us["score"] * 1e-6)
+    dominant = max(stage_us, key=stage_us.get)
+    if dominant == "topk":
+        roof = {"bound": "hbm", "kernel": "topk (partial scan + row merge)", "achieved": round(topk_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(topk_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": work["logit_bytes"],
+                "launch_us": round(stage_us["topk"], 2)}
+    elif dominant == "represent":
+        tf = work["mfma_flops"] / (stage_us["represent"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": "represent (projection GEMMs)", "achieved": round(tf, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "launch_us": round(stage_us["represent"], 2)}
+    else:
+        peak = VALU_LANE_OPS / 1e12
+        ach = grid_rate / 1e12
+        roof = {"bound": "alu", "kernel": "score (transition grid)", "achieved": round(ach, 2),
+                "peak": round(peak, 2), "unit": "Tlane-op/s", "frac": round(ach / peak, 4), "traffic": None,
+                "launch_us": round(stage_us["score"], 2)}
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import dcoco_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        nb = max(1, min(args.cpu_blocks, N))
+        blocks = list(range(nb))
+        t = time.perf_counter()
+        O.correct_block(base, blocks=blocks)
+        el = time.perf_counter() - t
+        cpu = {"value": round(nb / el, 4), "unit": "blocks/s", "cores": threads, "kind": "oracle",
+               "sample": f"{nb} of the {N} blocks of one input set (same shapes), NumPy float64, "
+                         f"{el:.1f} s"}
+
+    out = {
+        "metric": "corrected draft blocks/sec @B=16,K=16,d=4096,32 streams; % HBM/MFMA peak",
+        "value": round(blocks_per_s, 1),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == "bf16" else "f32",
+        "data": f"synthetic, seeded; {len(dsets)} rotating input sets",
+        "config": {"workload": f"{cfg.name}: {cfg.desc}", "streams": N, "B": B, "K": K, "d": D.d,
+                   "V": D.V, "embed": D.e, "proj": D.r, "mlp_hidden": D.H},
+        "transitions_per_s": round(work["transitions"] * args.steps / (gpu_ms / 1e3), 1),
+        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "hbm_frac_topk": round(topk_gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac_represent": round(work["mfma_flops"] / (stage_us["represent"] * 1e-6) / 1e12
+                                     / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if args.sweep:
+        sweep = {}
+        for n in (4, 8, 16):
+            dn = dc.Dims.from_synth(D)
+            dn.n_blocks = n
+            lg_n = dsets[0][0][: n * B]
+            h_n = dsets[0][1][:n]
+            st_n = torch.empty((n, B), dtype=torch.int32, device=dev)
+            for i in range(5):
+                dc.correct_block(dn, w, lg_n, h_n, E, sel_tok=st_n, workspace=ws, stream=stream)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(20):
+                dc.correct_block(dn, w, lg_n, h_n, E, sel_tok=st_n, workspace=ws, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / 20
+            sweep[str(n)] = {"us_per_call": round(us, 2), "blocks_per_s": round(n / (us * 1e-6), 1)}
+        out["stream_sweep"] = sweep
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

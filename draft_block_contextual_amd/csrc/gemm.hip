@@ -241,6 +241,197 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmDev p) {
       }
 }
 
+// bf16 x bf16 with a multi-stage ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4: each wave instruction writes 64 lanes x 16 bytes
+// = 1 KB of LDS, so staging costs no VGPRs and several k stages stay in
+// flight per workgroup).  A stage holds 64 k values: 128-byte tile rows.  Row
+// r's 16-byte chunk c is stored at position c ^ ((r >> 1) & 7), so the 16
+// rows a fragment read touches hit 16 distinct 4-bank groups.
+constexpr int kDmaRow = 128;
+
+__device__ __forceinline__ int dma_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// The ring's loads and barriers are issued as inline asm: the compiler then
+// neither counts the loads nor guards LDS reads with blanket waits, and the
+// explicit vmcnt(N) below is the only synchronisation (loads complete in
+// order, so vmcnt <= N means all but the N most recent have landed).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+// wait until at most N of this wave's ring loads are in flight, then barrier
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <int BM, int BN, int STAGES, int MODE>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
+  constexpr int kABytes = BM * kDmaRow;
+  constexpr int kWBytes = BN * kDmaRow;
+  constexpr int kStage = kABytes + kWBytes;
+  constexpr int AJ = kABytes / 1024 / 4;   // A load instructions per wave per stage
+  constexpr int WJ = kWBytes / 1024 / 4;
+  constexpr int IPS = AJ + WJ;
+  constexpr int TM = BM / 32;
+  constexpr int TN = BN / 32;
+  static_assert(AJ >= 1 && WJ >= 1, "tile too small for 4 waves");
+  static_assert(STAGES == 3 || STAGES == 4, "ring depth");
+  // one LDS object per ring slot: the compiler tracks direct-to-LDS loads per
+  // object, so reads of one slot need not wait for loads into the others
+  __shared__ __align__(1024) char sm0[kStage];
+  __shared__ __align__(1024) char sm1[kStage];
+  __shared__ __align__(1024) char sm2[kStage];
+  __shared__ __align__(1024) char sm3[STAGES == 4 ? kStage : 16];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv >> 1;
+  const int wn = wv & 1;
+  int bid = blockIdx.x;
+  if (remap) bid = (bid % 8) * (static_cast<int>(gridDim.x) / 8) + bid / 8;
+  const int tn = bid % tiles_n;
+  bid /= tiles_n;
+  const int tm = bid % tiles_m;
+  const int zs = bid / tiles_m;
+  const int n0 = tn * BN;
+  const int m0 = tm * BM;
+  const int kbeg = zs * p.ksplit;
+  const int kend = min(p.Kd, kbeg + p.ksplit);
+  const int nk = kend > kbeg ? (kend - kbeg) / 64 : 0;
+
+  // every lane always issues its loads (rows past the edge re-read a valid
+  // row and are never stored), so vmcnt counts are exact
+  const char* srcA[AJ];
+#pragma unroll
+  for (int j = 0; j < AJ; ++j) {
+    const int r = 8 * (wv + 4 * j) + (l >> 3);
+    const int c = dma_swz(r, l & 7);
+    const int m = min(m0 + r, p.M - 1);
+    long long row = m;
+    if (p.a_rows) {
+      int id = p.a_rows[m];
+      id = id < 0 ? 0 : (id > p.a_rows_max ? p.a_rows_max : id);
+      row = id;
+    }
+    srcA[j] = p.A + row * p.lda * 2 + c * 16;
+  }
+  const char* srcW[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int r = 8 * (wv + 4 * j) + (l >> 3);
+    const int c = dma_swz(r, l & 7);
+    const int jn = min(n0 + r, p.N - 1);
+    const char* base;
+    long long ld;
+    int col0, j0;
+    if (jn < p.end0) { base = p.w0; ld = p.ldw0; col0 = p.col00; j0 = 0; }
+    else if (jn < p.end1) { base = p.w1; ld = p.ldw1; col0 = p.col01; j0 = p.end0; }
+    else { base = p.w2; ld = p.ldw2; col0 = p.col02; j0 = p.end1; }
+    srcW[j] = base + (static_cast<long long>(jn - j0) * ld + col0) * 2 + c * 16;
+  }
+  auto issue = [&](char* base, int k0) {
+    const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_offset(base) + wv * 1024);
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) dma16(srcA[j] + static_cast<long long>(k0) * 2, b0 + j * 4096);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+      dma16(srcW[j] + static_cast<long long>(k0) * 2, b0 + kABytes + j * 4096);
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto slot = [&](auto S) -> char* {
+    constexpr int kS = decltype(S)::value;
+    if constexpr (kS == 0) return sm0;
+    else if constexpr (kS == 1) return sm1;
+    else if constexpr (kS == 2) return sm2;
+    else return sm3;
+  };
+  const int frow = l & 15;
+  auto compute = [&](const char* sa) {
+    const char* sw = sa + kABytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + (l >> 4);
+      bf16x8_t fa[TM], fw[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int row = wm * (BM / 2) + a * 16 + frow;
+        fa[a] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + row * kDmaRow + dma_swz(row, c) * 16));
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int row = wn * (BN / 2) + b * 16 + frow;
+        fw[b] = as_bf16x8(*reinterpret_cast<const uint4*>(sw + row * kDmaRow + dma_swz(row, c) * 16));
+      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fw[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  // one pipeline step on ring slot S: wait for its loads, barrier, refill the
+  // slot consumed in the previous step, then compute on slot S
+  auto step = [&](auto S, int it) {
+    constexpr int kS = decltype(S)::value;
+    if (it + STAGES - 2 < nk) wait_vmcnt_barrier<(STAGES - 2) * IPS>();
+    else wait_vmcnt_barrier<0>();
+    if (it + STAGES - 1 < nk)
+      issue(slot(std::integral_constant<int, (kS + STAGES - 1) % STAGES>{}),
+            kbeg + (it + STAGES - 1) * 64);
+    compute(slot(S));
+  };
+  if (0 < nk) issue(sm0, kbeg);
+  if (1 < nk) issue(sm1, kbeg + 64);
+  if constexpr (STAGES == 4) {
+    if (2 < nk) issue(sm2, kbeg + 128);
+  }
+  for (int it = 0; it < nk; it += STAGES) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nk) step(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 < nk) step(std::integral_constant<int, 2>{}, it + 2);
+    if constexpr (STAGES == 4) {
+      if (it + 3 < nk) step(std::integral_constant<int, 3>{}, it + 3);
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v;
+        const int n = n0 + wn * (BN / 2) + b * 16 + (l & 15);
+        if (m < p.M && n < p.N) {
+          if constexpr (MODE == 0) {
+            p.out_f32[(static_cast<long long>(zs) * p.M + m) * p.ldo + n] = acc[a][b][v];
+          } else {
+            float x = acc[a][b][v];
+            if (p.row_bias) x += p.row_bias[static_cast<long long>(m / p.row_bias_div) * p.N + n];
+            if (p.col_bias) x += bf16_to_f32(static_cast<const bf16*>(p.col_bias)[n].bits);
+            static_cast<bf16*>(p.out)[static_cast<long long>(m) * p.ldo + n] = bf16{f32_to_bf16(x)};
+          }
+        }
+      }
+}
+
 struct Tile {
   int bm, bn;
 };
@@ -284,6 +475,24 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
   p.col_bias = q.col_bias;
   const Tile t = pick_tile(q.M, q.N);
   const bool partial = q.out == nullptr;
+  if constexpr (kBF) {
+    if (q.Kd % 64 == 0) {
+      const int tiles_m = (q.M + t.bm - 1) / t.bm;
+      const int tiles_n = (q.N + t.bn - 1) / t.bn;
+      const int total = tiles_m * tiles_n * split;
+      const int remap = (total % 8 == 0) ? 1 : 0;
+#define DCOCO_DMA(BMV, BNV, ST, MODEV)                                                         \
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BMV, BNV, ST, MODEV>), dim3(total), dim3(kGemmThreads), 0, st, \
+                     p, tiles_m, tiles_n, remap)
+      if (t.bm == 128) {
+        if (partial) DCOCO_DMA(128, 128, 4, 0); else DCOCO_DMA(128, 128, 4, 1);
+      } else {
+        if (partial) DCOCO_DMA(64, 64, 4, 0); else DCOCO_DMA(64, 64, 4, 1);
+      }
+#undef DCOCO_DMA
+      return hipGetLastError();
+    }
+  }
   dim3 grid((q.N + t.bn - 1) / t.bn, (q.M + t.bm - 1) / t.bm, split);
 #define DCOCO_GEMM(BMV, BNV, MODEV)                                                       \
   hipLaunchKernelGGL((gemm_kernel<TA, TW, TO, BMV, BNV, MODEV>), grid, dim3(kGemmThreads), 0, st, p)

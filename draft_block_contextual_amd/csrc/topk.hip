@@ -25,6 +25,8 @@
 //     values), the wave selects exactly from its registers instead;
 //   * a second kernel merges the chunks of a row, sorts the K winners and
 //     writes ids and the original logit values.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -269,6 +271,211 @@ topk_partial_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 rows: the scan works on pairs of keys packed in 32-bit words.  The key
+// of a bf16 pattern x is 0x8000 + |x| for x >= 0 and 0x8000 - |x| for x < 0
+// (so -0 and +0 share 0x8000 and -inf maps to 0x0080); per 16-bit half that
+// is  m = x >> 15 (arithmetic),  k = (x ^ (m | 0x8000)) - m,  three packed
+// instructions per pair.  NaN patterns land above 0xff80 or below 0x0080; a
+// wave that meets one re-derives exact keys (NaN -> 0, below -inf) and
+// selects without the threshold shortcut.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_keys(uint32_t w) {
+  const i16x2 x = __builtin_bit_cast(i16x2, w);
+  const uint32_t m = __builtin_bit_cast(uint32_t, x >> (i16x2){15, 15});
+  const u16x2 t = __builtin_bit_cast(u16x2, w ^ (m | 0x80008000u));
+  return __builtin_bit_cast(uint32_t, t - __builtin_bit_cast(u16x2, m));
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+// per half: saturate(a - b); nonzero iff the half of a exceeds that of b
+__device__ __forceinline__ uint32_t pk_sub_sat(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, a),
+                                                                    __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t canon_half(uint32_t k) { return (k > 0xff80u || k < 0x0080u) ? 0u : k; }
+
+constexpr int kWords = kVecPerLane * 4;   // 32 words = 64 bf16 per lane
+
+// exact key of one bf16 pattern (NaN -> 0), elements past the row -> none
+__device__ __forceinline__ uint32_t exact_key16(uint32_t bits) {
+  return canon_half((pack_keys(bits) & 0xffffu));
+}
+
+// Exact top-K of one wave segment, re-reading it from memory (cached): used
+// when the segment holds a NaN or too many keys tie near the threshold.
+// Writes min(K, #elements) composites to out[0..K), zero padded.
+__device__ __attribute__((noinline)) void exact_segment_bf16(const uint16_t* rowp, int V, int K, int seg0,
+                                                             int* cnt_slot, uint64_t* out) {
+  const int l = lane_id();
+  auto key_at = [&](int e) -> int { return e < V ? static_cast<int>(exact_key16(rowp[e])) : -1; };
+  uint32_t tk = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const int cand = static_cast<int>(tk | (1u << bit));
+    int cnt = 0;
+#pragma unroll 1
+    for (int i = 0; i < kVecPerLane; ++i)
+#pragma unroll 1
+      for (int j = 0; j < 8; ++j) cnt += key_at(seg0 + (i * kWave + l) * 8 + j) >= cand ? 1 : 0;
+    if (wave_sum_i(cnt) >= K) tk = static_cast<uint32_t>(cand);
+  }
+  if (l == 0) *cnt_slot = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+  for (int i = 0; i < kVecPerLane; ++i)
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) {
+      const int e = seg0 + (i * kWave + l) * 8 + j;
+      const int k = key_at(e);
+      if (k > static_cast<int>(tk)) {
+        const int pos = atomicAdd(cnt_slot, 1);
+        out[pos] = make_comp(static_cast<uint32_t>(k), static_cast<uint32_t>(e));
+      }
+    }
+  __builtin_amdgcn_wave_barrier();
+  int have = *cnt_slot;
+  // keys equal to tk, lowest ids first (vector by vector, lane order, then j)
+#pragma unroll 1
+  for (int i = 0; i < kVecPerLane; ++i) {
+    int mine = 0;
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) mine += key_at(seg0 + (i * kWave + l) * 8 + j) == static_cast<int>(tk) ? 1 : 0;
+    const int incl = wave_prefix_incl(mine);
+    int pos = have + incl - mine;
+#pragma unroll 1
+    for (int j = 0; j < 8; ++j) {
+      const int e = seg0 + (i * kWave + l) * 8 + j;
+      if (key_at(e) == static_cast<int>(tk)) {
+        if (pos < K) out[pos] = make_comp(tk, static_cast<uint32_t>(e));
+        ++pos;
+      }
+    }
+    have += __shfl(incl, kWave - 1, kWave);
+  }
+  for (int i = min(have, K) + l; i < K; i += kWave) out[i] = 0ull;
+}
+
+template <int G, bool kVecLoad>
+__global__ void __launch_bounds__(kTopkThreads)
+topk_bf16_partial_kernel(const uint16_t* __restrict__ logits, int V, int K, int nchunks,
+                         uint64_t* __restrict__ partial) {
+  constexpr int kSeg = kWave * kWords * 2;
+  constexpr int kChunk = kTopkWaves * kSeg;
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
+
+  __shared__ uint64_t s_cand[kTopkWaves][kCandCap];
+  __shared__ uint64_t s_best[kTopkWaves * 64];
+  __shared__ uint64_t s_out[64];
+  __shared__ int s_cnt[kTopkWaves];
+
+  const int seg0 = chunk * kChunk + w * kSeg;
+  if (l == 0) s_cnt[w] = 0;
+  uint64_t* wave_out = s_best + w * K;
+  // element index of half h of word j of this lane
+  auto elem = [&](int j, int h) { return seg0 + ((j >> 2) * kWave + l) * 8 + (j & 3) * 2 + h; };
+
+  if (seg0 < V) {
+    uint32_t kw[kWords];
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i) {
+      const int e0 = seg0 + (i * kWave + l) * 8;
+      if (kVecLoad && e0 + 8 <= V) {
+        const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);
+        kw[4 * i] = v.x; kw[4 * i + 1] = v.y; kw[4 * i + 2] = v.z; kw[4 * i + 3] = v.w;
+      } else {
+        // past the row end: -inf patterns (never appended: their ids are >= V)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = e0 + 2 * q < V ? rowp[e0 + 2 * q] : 0xff80u;
+          const uint32_t hi = e0 + 2 * q + 1 < V ? rowp[e0 + 2 * q + 1] : 0xff80u;
+          kw[4 * i + q] = lo | (hi << 16);
+        }
+      }
+    }
+    uint32_t gmx[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) gmx[g] = 0u;
+    uint32_t mn = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < kWords; ++j) {
+      kw[j] = pack_keys(kw[j]);
+      const int g = (j * G) / kWords;
+      gmx[g] = pk_max(gmx[g], kw[j]);
+      mn = pk_min(mn, kw[j]);
+    }
+    uint32_t top = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      gmx[g] = max(gmx[g] & 0xffffu, gmx[g] >> 16);
+      top = max(top, gmx[g]);
+    }
+    const bool lane_nan = top > 0xff80u || min(mn & 0xffffu, mn >> 16) < 0x0080u;
+    const bool wave_nan = ballot(lane_nan) != 0;
+    int count = kCandCap + 1;
+    uint32_t t0 = 0;
+    if (!wave_nan) {
+      // T0 = K-th largest group maximum; every key here is >= 0x0080
+      for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t cand = t0 | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) cnt += __popcll(ballot(gmx[g] >= cand));
+        if (cnt >= K) t0 = cand;
+      }
+      const uint32_t thr = (t0 - 1u) * 0x00010001u;
+      // words holding a key >= T0 (rare), then append their elements
+      uint32_t mask = 0;
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) mask |= (pk_sub_sat(kw[j], thr) != 0u ? 1u : 0u) << j;
+      while (mask) {
+        const int j = __builtin_ctz(mask);
+        mask &= mask - 1u;
+        const int e = elem(j, 0);
+        if (e >= V) continue;   // padding only
+        const uint32_t lo = rowp[e];
+        const uint32_t hi = e + 1 < V ? rowp[e + 1] : 0xff80u;
+        const uint32_t kk = pack_keys(lo | (hi << 16));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t k = (kk >> (16 * h)) & 0xffffu;
+          if (k >= t0 && e + h < V) {
+            const int pos = atomicAdd(&s_cnt[w], 1);
+            if (pos < kCandCap) s_cand[w][pos] = make_comp(k, static_cast<uint32_t>(e + h));
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      count = s_cnt[w];
+    }
+    if (count <= kCandCap) {
+      select_small<16 + 32>(s_cand[w], count, K, wave_out);
+    } else {
+      exact_segment_bf16(rowp, V, K, seg0, s_cnt + w, wave_out);
+    }
+  } else {
+    for (int i = l; i < K; i += kWave) wave_out[i] = 0ull;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint64_t* dst = partial + (static_cast<size_t>(row) * nchunks + chunk) * K;
+    select_small<16 + 32>(s_best, kTopkWaves * K, K, s_out);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = l; i < K; i += kWave) dst[i] = s_out[i];
+  }
+}
+
 template <typename T, int Q>
 __global__ void __launch_bounds__(kWave)
 topk_merge_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
@@ -321,10 +528,23 @@ hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* p
   const bool vec = (static_cast<size_t>(V) * sizeof(T)) % 16 == 0 &&
                    (reinterpret_cast<uintptr_t>(logits) % 16) == 0;
   dim3 g1(nch, rows);
-  if (vec)
-    hipLaunchKernelGGL((topk_partial_kernel<T, true>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
-  else
-    hipLaunchKernelGGL((topk_partial_kernel<T, false>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
+  if constexpr (std::is_same<T, bf16>::value) {
+    const uint16_t* lb = reinterpret_cast<const uint16_t*>(logits);
+    const int G = K <= 16 ? 1 : (K <= 32 ? 2 : 4);
+#define DCOCO_TOPK16(GG, VV) \
+  hipLaunchKernelGGL((topk_bf16_partial_kernel<GG, VV>), g1, dim3(kTopkThreads), 0, st, lb, V, K, nch, partial)
+    if (vec) {
+      if (G == 1) DCOCO_TOPK16(1, true); else if (G == 2) DCOCO_TOPK16(2, true); else DCOCO_TOPK16(4, true);
+    } else {
+      if (G == 1) DCOCO_TOPK16(1, false); else if (G == 2) DCOCO_TOPK16(2, false); else DCOCO_TOPK16(4, false);
+    }
+#undef DCOCO_TOPK16
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((topk_partial_kernel<T, true>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
+    else
+      hipLaunchKernelGGL((topk_partial_kernel<T, false>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
+  }
   const int count = nch * K;
   const int q = (count + kWave - 1) / kWave;
 #define DCOCO_MERGE(QQ)                                                                     \

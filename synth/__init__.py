@@ -297,6 +297,22 @@ def make_inputs(cfg: Config | str, seed: int | None = None, n_blocks: int | None
     return out
 
 
+def make_stream_inputs(cfg: Config | str, seed: int, n_blocks: int | None = None) -> dict:
+    """Only the per-stream tensors (logits [N,B,V] and h [N,B,d]) of an input
+    set drawn with ``seed``; weights and E are shared across rotating sets."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    D = cfg.dims if n_blocks is None else dataclasses.replace(cfg.dims, n_blocks=n_blocks)
+    dt = D.dtype
+    h = np.empty((D.n_blocks, D.B, D.d), np.uint16 if dt == "bf16" else np.float32)
+    logits = np.empty((D.n_blocks, D.B, D.V), np.uint16 if dt == "bf16" else np.float32)
+    for n in range(D.n_blocks):
+        gh = _rng(seed, ROLE["stream"], n, STREAM_ROLE["h"])
+        h[n] = _store(gh.standard_normal((D.B, D.d), dtype=np.float32) * np.float32(cfg.h_scale), dt)
+        logits[n] = _store(_logit_row_block(cfg, n, seed), dt)
+    return {"h": h, "logits": logits, "dims": D, "seed": seed}
+
+
 def to_float(a: np.ndarray, dtype: str) -> np.ndarray:
     """View stored values as float32 (bf16 bits are widened exactly)."""
     if dtype == "bf16":

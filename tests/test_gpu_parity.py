@@ -187,9 +187,16 @@ def test_represent_matches_oracle(name):
     z = _np(z).astype(np.float64)
     s = _np(s).astype(np.float64)
     if D.dtype == "bf16":
-        # one bf16 step of |z| where fp32 and fp64 sums round differently
-        assert np.all(np.abs(z - ref["z"]) <= 2.0 ** -7 * np.abs(ref["z"]) + 1e-3)
-        assert np.mean(z == ref["z"]) > 0.98
+        # z, b and g are rounded to bf16 where they are produced; an fp32 and
+        # an fp64 sum that straddle a rounding midpoint round one bf16 step
+        # apart, in z itself or in a b/g element that feeds it (one step there
+        # moves z by |W_f| * 2^-7 ~ 1e-3).
+        zr = ref["z"]
+        ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(zr), 2.0 ** -126))).astype(int) - 7)
+        dz = np.abs(z - zr)
+        print(f"  z: max |dz| = {dz.max():.3g}, exact fraction {np.mean(dz == 0):.4f}", flush=True)
+        assert np.all(dz <= ulp + 4e-3)
+        assert np.mean(dz == 0) > 0.98
         np.testing.assert_allclose(s, ref["s"], rtol=0, atol=2e-2)
     else:
         np.testing.assert_allclose(z, ref["z"], rtol=1e-4, atol=1e-4)
