@@ -42,7 +42,7 @@ int check_dims(const dcoco_dims* d, bool need_widths) {
     if ((rc = check_width(d->d_embed, 1 << 16)) != DCOCO_OK) return rc;
     if ((rc = check_width(d->d_proj, 2048)) != DCOCO_OK) return rc;
     if ((rc = check_width(d->d_z, 2048)) != DCOCO_OK) return rc;
-    if ((rc = check_width(d->d_pair, 8192)) != DCOCO_OK) return rc;
+    if ((rc = check_width(d->d_pair, 2048)) != DCOCO_OK) return rc;
     if ((rc = check_width(d->d_mlp, 1 << 16)) != DCOCO_OK) return rc;
   }
   return DCOCO_OK;
@@ -126,11 +126,16 @@ hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void
     q.split = L.split_slot; q.out_f32 = L.Y; q.ldo = ns; q.out = nullptr;
     if ((e = launch_gemm(q, st)) != hipSuccess) return e;
   }
-  if ((e = launch_ln_rows(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
   if ((e = launch_pair_state(L.Y, L.split_slot, d->n_blocks, d->B, ns, r, r + rs, rs, s, st)) != hipSuccess)
     return e;
-  // gf = W_fg g (the slot half of the fusion), once per slot
-  {
+  const bool fused = dt == kDtypeBf16;
+  // gf = W_fg g with g = LN(P_h h) (the slot half of the fusion), once per slot
+  if (fused) {
+    if ((e = launch_ln_gemm(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, nullptr,
+                            nullptr, 1, st)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = launch_ln_rows(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
     GemmProblem q{};
     q.M = R; q.N = rz; q.Kd = r;
     q.A = L.g; q.lda = r; q.a_dtype = dt;
@@ -151,9 +156,13 @@ hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void
     q.split = L.split_cand; q.out_f32 = L.U; q.ldo = r; q.out = nullptr;
     if ((e = launch_gemm(q, st)) != hipSuccess) return e;
   }
-  if ((e = launch_ln_rows(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, L.b, dt, st)) != hipSuccess) return e;
-  // z = W_fb b + gf[slot]
-  {
+  // z = W_fb b + gf[slot] with b = LN(P_e E[c])
+  if (fused) {
+    if ((e = launch_ln_gemm(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, w->W_f, 2ll * r, 0, rz, nullptr, z, L.gf,
+                            d->K, st)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = launch_ln_rows(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, L.b, dt, st)) != hipSuccess) return e;
     GemmProblem q{};
     q.M = RK; q.N = rz; q.Kd = r;
     q.A = L.b; q.lda = r; q.a_dtype = dt;
@@ -167,30 +176,16 @@ hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void
   return hipSuccess;
 }
 
-// scoring stage: C = W1s s + b1, then the grid
+// scoring stage: the grid kernel forms C_p = W1s s_p + b1 itself
 hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
-                     const float* cl, float* S, float* C, hipStream_t st) {
+                     const float* cl, float* S, hipStream_t st) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int P = d->n_blocks * (d->B - 1);
   if (P == 0) return hipSuccess;
-  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
-  const long long ldw1 = 2ll * rz + rs;
-  hipError_t e;
-  {
-    GemmProblem q{};
-    q.M = P; q.N = H; q.Kd = rs;
-    q.A = s; q.lda = rs; q.a_dtype = kDtypeF32;
-    q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 2 * rz; q.seg_end[0] = H;
-    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = H;
-    q.w_dtype = dt;
-    q.split = 1; q.out = C; q.out_dtype = kDtypeF32; q.ldo = H;
-    q.row_bias = nullptr; q.row_bias_div = 1; q.col_bias = w->b1;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
   GridProblem g{};
-  g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.rz = rz; g.H = H;
-  g.z = z; g.dtype = dt; g.W1 = w->W1; g.ldw1 = ldw1; g.C = C; g.w2 = w->w2; g.b2 = w->b2;
-  g.cand_logits = cl; g.S = S;
+  g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.rz = d->d_z; g.rs = d->d_pair; g.H = d->d_mlp;
+  g.z = z; g.dtype = dt; g.s = s; g.W1 = w->W1; g.ldw1 = 2ll * d->d_z + d->d_pair; g.b1 = w->b1;
+  g.w2 = w->w2; g.b2 = w->b2; g.cand_logits = cl; g.S = S;
   return launch_grid(g, st);
 }
 
@@ -260,16 +255,12 @@ int dcoco_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, cons
   int rc = check_dims(d, true);
   if (rc != DCOCO_OK) return rc;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
-  Carve c(nullptr);
-  c.take(sizeof(float) * P * d->d_mlp);
-  rc = check_ws(workspace, workspace_bytes, c.off);
+  rc = check_ws(workspace, workspace_bytes, 0);
   if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
   if ((rc = check_weights(w, false, true)) != DCOCO_OK) return rc;
   if (P == 0) return DCOCO_OK;
   if (!ptr_ok(z) || !ptr_ok(s) || !ptr_ok(cand_logits) || !ptr_ok(S)) return DCOCO_ERR_INVALID_ARG;
-  Carve cw(workspace);
-  float* C = static_cast<float*>(cw.take(sizeof(float) * P * d->d_mlp));
-  return hip_status(run_score(d, w, z, s, cand_logits, S, C, static_cast<hipStream_t>(stream)));
+  return hip_status(run_score(d, w, z, s, cand_logits, S, static_cast<hipStream_t>(stream)));
 }
 
 int dcoco_select(const dcoco_dims* d, const float* S, const float* cand_logits, const int32_t* cand_ids,
@@ -295,20 +286,19 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   const size_t RK = static_cast<size_t>(R) * d->K;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
   auto layout = [&](Carve& c, void** topk_ws, int32_t** ids, float** cl, RepLayout* L, void** z,
-                    float** s, float** C, float** S) {
+                    float** s, float** S) {
     *topk_ws = c.take(topk_workspace_bytes(dt, R, d->V, d->K));
     *ids = static_cast<int32_t*>(c.take(sizeof(int32_t) * RK));
     *cl = static_cast<float*>(c.take(sizeof(float) * RK));
     *L = carve_rep(c, d);
     *z = c.take(esize(d->dtype) * RK * d->d_z);
     *s = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_pair));
-    *C = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_mlp));
     *S = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->K * d->K));
   };
-  void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* C; float* S;
+  void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* S;
   {
     Carve c(nullptr);
-    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &C, &S);
+    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S);
     rc = check_ws(workspace, workspace_bytes, c.off);
     if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
   }
@@ -317,14 +307,14 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (!opt_ok(sel_idx) || !opt_ok(S_out) || !opt_ok(cand_ids_out) || !opt_ok(cand_logits_out))
     return DCOCO_ERR_INVALID_ARG;
   Carve cw(workspace);
-  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &C, &S);
+  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S);
   if (cand_ids_out) ids = cand_ids_out;
   if (cand_logits_out) cl = cand_logits_out;
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = run_represent(d, w, h, E, ids, z, s, L, st);
-  if (e == hipSuccess) e = run_score(d, w, z, s, cl, S, C, st);
+  if (e == hipSuccess) e = run_score(d, w, z, s, cl, S, st);
   if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
   return hip_status(e);
 }

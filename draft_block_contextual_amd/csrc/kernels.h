@@ -51,18 +51,26 @@ int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype);
 hipError_t launch_ln_rows(const float* x, int split, int M, int ldx, int col0, int r, float eps,
                           void* y, int out_dtype, hipStream_t st);
 
+// bf16 only: out[m, :] = W[:, wcol0 : wcol0 + r] LN(sum_s x[s][m][col0 : col0 + r]) with the
+// LN output rounded to bf16; fp32 out (out_bf == nullptr) or bf16 out with
+// + row_bias[m / row_div][n] (out_bf != nullptr).
+hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, int r, float eps,
+                          const void* W, long long ldw, int wcol0, int N, float* out_f32, void* out_bf,
+                          const float* row_bias, int row_div, hipStream_t st);
+
 // s[n, p, :] = sum_s Y[s][n*B+p][cl : cl+rs] + sum_s Y[s][n*B+p+1][cr : cr+rs]
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
                              int rs, float* s, hipStream_t st);
 
 // ----------------------------------------------------- scoring and walk
 struct GridProblem {
-  int N, B, K, rz, H;
+  int N, B, K, rz, rs, H;
   const void* z;               // [N, B, K, rz] (dtype)
   int dtype;
+  const float* s;              // [N, B-1, rs] (fp32)
   const void* W1;              // [H, 2 rz + rs]
   long long ldw1;
-  const float* C;              // [N, B-1, H] = W1s s + b1 (fp32)
+  const void* b1;              // [H] (dtype) or null
   const void* w2;              // [H] (dtype)
   float b2;
   const float* cand_logits;    // [N, B, K]

@@ -70,6 +70,112 @@ pair_state_kernel(const float* __restrict__ Y, int split, int N, int B, int ldy,
   }
 }
 
+// bf16 path: LayerNorm of BM rows straight into an LDS operand tile, then
+// y = W x for those rows on MFMA (W rows streamed from L2 as 16-byte
+// fragments).  Used for gf = W_fg g (fp32 out) and z = W_fb b + gf[slot]
+// (bf16 out), so the normalised g and b never leave the chip.
+template <int BM, int RMAX, int MODE>
+__global__ void __launch_bounds__(256)
+ln_gemm_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0, int r, float eps,
+               const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
+               bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div) {
+  constexpr int kStr = RMAX * 2 + 16;              // LDS bytes per tile row
+  constexpr int VPL = RMAX / kWave;
+  constexpr int WM = BM == 64 ? 2 : 1;             // wave grid: WM x (4 / WM)
+  constexpr int WN = 4 / WM;
+  constexpr int TM = BM / (16 * WM);
+  constexpr int TN = 8;                            // 128 columns per wave pass
+  __shared__ __align__(16) char tile[BM * kStr];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int m0 = blockIdx.x * BM;
+
+  // ---- LayerNorm, one wave per row
+  for (int rr = wv; rr < BM; rr += 4) {
+    const int m = m0 + rr;
+    uint16_t* trow = reinterpret_cast<uint16_t*>(tile + rr * kStr);
+    if (m >= M) {
+      for (int c = l; c < r; c += kWave) trow[c] = 0;
+      continue;
+    }
+    float v[VPL];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = l + i * kWave;
+      float a = 0.f;
+      if (c < r)
+        for (int s2 = 0; s2 < split; ++s2) a += x[(static_cast<long long>(s2) * M + m) * ldx + col0 + c];
+      v[i] = a;
+      sum += a;
+    }
+    const float mean = wave_sum(sum) / static_cast<float>(r);
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = l + i * kWave;
+      v[i] = c < r ? v[i] - mean : 0.f;
+      sq += v[i] * v[i];
+    }
+    const float inv = 1.0f / sqrtf(wave_sum(sq) / static_cast<float>(r) + eps);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = l + i * kWave;
+      if (c < r) trow[c] = f32_to_bf16(v[i] * inv);
+    }
+  }
+  __syncthreads();
+
+  // ---- y = W x on MFMA
+  const int wm = wv / WN;
+  const int wn = wv % WN;
+  const int frow = l & 15;
+  const int fk = (l >> 4) * 8;
+  for (int n0 = wn * 128; n0 < N; n0 += WN * 128) {
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < r; k += 32) {
+      bf16x8_t fa[TM];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+        fa[a] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                    tile + (wm * (BM / WM) + a * 16 + frow) * kStr + (k + fk) * 2));
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int n = min(n0 + b * 16 + frow, N - 1);
+        const uint4 u = *reinterpret_cast<const uint4*>(W + static_cast<long long>(n) * ldw + wcol0 + k + fk);
+        const bf16x8_t fw = __builtin_bit_cast(bf16x8_t, u);
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fw, acc[a][b], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * (BM / WM) + a * 16 + (l >> 4) * 4 + v;
+        if (m >= M) continue;
+        const float* rb = MODE == 1 ? row_bias + static_cast<long long>(m / row_div) * N : nullptr;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int n = n0 + b * 16 + (l & 15);
+          if (n >= N) continue;
+          if constexpr (MODE == 0) {
+            out_f32[static_cast<long long>(m) * N + n] = acc[a][b][v];
+          } else {
+            out_bf[static_cast<long long>(m) * N + n] = bf16{f32_to_bf16(acc[a][b][v] + rb[n])};
+          }
+        }
+      }
+  }
+}
+
 template <typename TO>
 hipError_t launch_ln_t(const float* x, int split, int M, int ldx, int col0, int r, float eps, void* y,
                        hipStream_t st) {
@@ -93,6 +199,24 @@ hipError_t launch_ln_rows(const float* x, int split, int M, int ldx, int col0, i
                           void* y, int out_dtype, hipStream_t st) {
   if (out_dtype == kDtypeBf16) return launch_ln_t<bf16>(x, split, M, ldx, col0, r, eps, y, st);
   return launch_ln_t<float>(x, split, M, ldx, col0, r, eps, y, st);
+}
+
+hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, int r, float eps,
+                          const void* W, long long ldw, int wcol0, int N, float* out_f32, void* out_bf,
+                          const float* row_bias, int row_div, hipStream_t st) {
+  const bf16* Wb = static_cast<const bf16*>(W);
+  bf16* ob = static_cast<bf16*>(out_bf);
+  const bool bias = out_bf != nullptr;
+#define DCOCO_LNG(BMV, RM, MD)                                                                        \
+  hipLaunchKernelGGL((ln_gemm_kernel<BMV, RM, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, split, \
+                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div)
+  if (r <= 512) {
+    if (bias) DCOCO_LNG(64, 512, 1); else DCOCO_LNG(64, 512, 0);
+  } else {
+    if (bias) DCOCO_LNG(16, 2048, 1); else DCOCO_LNG(16, 2048, 0);
+  }
+#undef DCOCO_LNG
+  return hipGetLastError();
 }
 
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,

@@ -55,7 +55,8 @@ __device__ __forceinline__ uint64_t make_comp(uint32_t key, uint32_t id) {
 }
 
 // Exact top-K of the composites c[0..Q) held by the lanes of one wave (0 =
-// empty slot).  Marks the min(K, #non-empty) largest in sel[].
+// empty slot); KEYBITS is the width of the key half.  Marks the
+// min(K, #non-empty) largest in sel[].
 template <int Q, int KEYBITS>
 __device__ void select_topk(const uint64_t (&c)[Q], int K, bool (&sel)[Q]) {
   uint32_t tk = 0;
@@ -201,7 +202,7 @@ topk_partial_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
     __builtin_amdgcn_wave_barrier();
     const int count = s_cnt[w];
     if (count <= kCandCap) {
-      select_small<S::kKeyBits + 32>(s_cand[w], count, K, wave_out);
+      select_small<S::kKeyBits>(s_cand[w], count, K, wave_out);
     } else {
       // ---- exact fallback over the registers: key threshold, then the
       //      lowest ids among keys equal to it.
@@ -264,7 +265,7 @@ topk_partial_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
   if (w == 0) {
     uint64_t* dst = partial + (static_cast<size_t>(row) * nchunks + chunk) * K;
     __shared__ uint64_t s_out[64];
-    select_small<S::kKeyBits + 32>(s_best, kTopkWaves * K, K, s_out);
+    select_small<S::kKeyBits>(s_best, kTopkWaves * K, K, s_out);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     for (int i = l; i < K; i += kWave) dst[i] = s_out[i];
@@ -460,7 +461,7 @@ topk_bf16_partial_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
       count = s_cnt[w];
     }
     if (count <= kCandCap) {
-      select_small<16 + 32>(s_cand[w], count, K, wave_out);
+      select_small<16>(s_cand[w], count, K, wave_out);
     } else {
       exact_segment_bf16(rowp, V, K, seg0, s_cnt + w, wave_out);
     }
@@ -470,7 +471,7 @@ topk_bf16_partial_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
   __syncthreads();
   if (w == 0) {
     uint64_t* dst = partial + (static_cast<size_t>(row) * nchunks + chunk) * K;
-    select_small<16 + 32>(s_best, kTopkWaves * K, K, s_out);
+    select_small<16>(s_best, kTopkWaves * K, K, s_out);
     __builtin_amdgcn_wave_barrier();
     for (int i = l; i < K; i += kWave) dst[i] = s_out[i];
   }
@@ -494,7 +495,7 @@ topk_merge_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
     const int i = q * kWave + l;
     c[q] = i < count ? src[i] : 0ull;
   }
-  select_topk<Q, kKeyBits + 32>(c, K, sel);
+  select_topk<Q, kKeyBits>(c, K, sel);
   int base = 0;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {

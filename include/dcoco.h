@@ -45,7 +45,7 @@
  *
  * Supported shapes: n_blocks >= 1, B >= 1, 1 <= K <= min(V, 64); d_hidden,
  * d_embed, d_proj, d_z, d_pair and d_mlp positive multiples of 32, with
- * d_proj, d_z <= 2048 and d_pair <= 8192; ln_eps > 0.  Valid shapes outside
+ * d_proj, d_z, d_pair <= 2048; ln_eps > 0.  Valid shapes outside
  * this set return DCOCO_ERR_UNSUPPORTED.
  */
 #ifndef DCOCO_H
