@@ -176,16 +176,62 @@ hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void
   return hipSuccess;
 }
 
-// scoring stage: the grid kernel forms C_p = W1s s_p + b1 itself
+// scoring stage buffers
+struct ScoreLayout {
+  void* s3;       // bf16 [3, P, rs] (bf16 path only)
+  float* C;       // fp32 [nq, P, H]
+  float* AB;      // fp32 [N*B*K, 2H]
+};
+
+ScoreLayout carve_score(Carve& c, const dcoco_dims* d) {
+  ScoreLayout L;
+  const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
+  const size_t RK = static_cast<size_t>(d->n_blocks) * d->B * d->K;
+  const int nq = d->dtype == DCOCO_BF16 ? 3 : 1;
+  L.s3 = c.take(d->dtype == DCOCO_BF16 ? 3 * P * d->d_pair * 2 : 0);
+  L.C = static_cast<float*>(c.take(sizeof(float) * nq * P * d->d_mlp));
+  L.AB = static_cast<float*>(c.take(sizeof(float) * RK * 2 * d->d_mlp));
+  return L;
+}
+
+// scoring stage: C_p parts = W1s s_p (s split into bf16 hi/mid/lo rows on the
+// bf16 path), AB = z [W1a; W1b]^T, then the grid
 hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
-                     const float* cl, float* S, hipStream_t st) {
+                     const float* cl, float* S, const ScoreLayout& L, hipStream_t st) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int P = d->n_blocks * (d->B - 1);
   if (P == 0) return hipSuccess;
+  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
+  const int RK = d->n_blocks * d->B * d->K;
+  const long long ldw1 = 2ll * rz + rs;
+  const int nq = dt == kDtypeBf16 ? 3 : 1;
+  hipError_t e;
+  if (dt == kDtypeBf16 && (e = launch_split3(s, static_cast<long long>(P) * rs, L.s3, st)) != hipSuccess) return e;
+  {
+    GemmProblem q{};
+    q.M = nq * P; q.N = H; q.Kd = rs;
+    q.A = dt == kDtypeBf16 ? L.s3 : static_cast<const void*>(s); q.lda = rs; q.a_dtype = dt;
+    q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 2 * rz; q.seg_end[0] = H;
+    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = H;
+    q.w_dtype = dt;
+    q.split = 1; q.out_f32 = L.C; q.ldo = H; q.out = nullptr;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
+  {
+    GemmProblem q{};
+    q.M = RK; q.N = 2 * H; q.Kd = rz;
+    q.A = z; q.lda = rz; q.a_dtype = dt;
+    q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 0; q.seg_end[0] = H;
+    q.w[1] = w->W1; q.ldw[1] = ldw1; q.col0[1] = rz; q.seg_end[1] = 2 * H;
+    q.w[2] = w->W1; q.ldw[2] = ldw1; q.col0[2] = rz; q.seg_end[2] = 2 * H;
+    q.w_dtype = dt;
+    q.split = 1; q.out_f32 = L.AB; q.ldo = 2 * H; q.out = nullptr;
+    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
+  }
   GridProblem g{};
-  g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.rz = d->d_z; g.rs = d->d_pair; g.H = d->d_mlp;
-  g.z = z; g.dtype = dt; g.s = s; g.W1 = w->W1; g.ldw1 = 2ll * d->d_z + d->d_pair; g.b1 = w->b1;
-  g.w2 = w->w2; g.b2 = w->b2; g.cand_logits = cl; g.S = S;
+  g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.H = H; g.dtype = dt;
+  g.AB = L.AB; g.C = L.C; g.nq = nq; g.b1 = w->b1; g.w2 = w->w2; g.b2 = w->b2;
+  g.cand_logits = cl; g.S = S;
   return launch_grid(g, st);
 }
 
@@ -255,12 +301,16 @@ int dcoco_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, cons
   int rc = check_dims(d, true);
   if (rc != DCOCO_OK) return rc;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
-  rc = check_ws(workspace, workspace_bytes, 0);
+  Carve c(nullptr);
+  carve_score(c, d);
+  rc = check_ws(workspace, workspace_bytes, c.off);
   if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
   if ((rc = check_weights(w, false, true)) != DCOCO_OK) return rc;
   if (P == 0) return DCOCO_OK;
   if (!ptr_ok(z) || !ptr_ok(s) || !ptr_ok(cand_logits) || !ptr_ok(S)) return DCOCO_ERR_INVALID_ARG;
-  return hip_status(run_score(d, w, z, s, cand_logits, S, static_cast<hipStream_t>(stream)));
+  Carve cw(workspace);
+  const ScoreLayout SL = carve_score(cw, d);
+  return hip_status(run_score(d, w, z, s, cand_logits, S, SL, static_cast<hipStream_t>(stream)));
 }
 
 int dcoco_select(const dcoco_dims* d, const float* S, const float* cand_logits, const int32_t* cand_ids,
@@ -286,7 +336,7 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   const size_t RK = static_cast<size_t>(R) * d->K;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
   auto layout = [&](Carve& c, void** topk_ws, int32_t** ids, float** cl, RepLayout* L, void** z,
-                    float** s, float** S) {
+                    float** s, float** S, ScoreLayout* SL) {
     *topk_ws = c.take(topk_workspace_bytes(dt, R, d->V, d->K));
     *ids = static_cast<int32_t*>(c.take(sizeof(int32_t) * RK));
     *cl = static_cast<float*>(c.take(sizeof(float) * RK));
@@ -294,11 +344,12 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
     *z = c.take(esize(d->dtype) * RK * d->d_z);
     *s = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_pair));
     *S = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->K * d->K));
+    *SL = carve_score(c, d);
   };
-  void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* S;
+  void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* S; ScoreLayout SL;
   {
     Carve c(nullptr);
-    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S);
+    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
     rc = check_ws(workspace, workspace_bytes, c.off);
     if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
   }
@@ -307,14 +358,14 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (!opt_ok(sel_idx) || !opt_ok(S_out) || !opt_ok(cand_ids_out) || !opt_ok(cand_logits_out))
     return DCOCO_ERR_INVALID_ARG;
   Carve cw(workspace);
-  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S);
+  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
   if (cand_ids_out) ids = cand_ids_out;
   if (cand_logits_out) cl = cand_logits_out;
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = run_represent(d, w, h, E, ids, z, s, L, st);
-  if (e == hipSuccess) e = run_score(d, w, z, s, cl, S, st);
+  if (e == hipSuccess) e = run_score(d, w, z, s, cl, S, SL, st);
   if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
   return hip_status(e);
 }

@@ -446,7 +446,7 @@ int pick_split(int M, int N, int Kd, int bk) {
   const Tile t = pick_tile(M, N);
   const long long tiles = static_cast<long long>((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
   int split = 1;
-  while (tiles * split < 256 && Kd / (split * 2) >= 4 * bk) split *= 2;
+  while (tiles * split < 256 && split < 4 && Kd / (split * 2) >= 4 * bk) split *= 2;
   return split;
 }
 

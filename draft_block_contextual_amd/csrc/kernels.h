@@ -64,12 +64,11 @@ hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, i
 
 // ----------------------------------------------------- scoring and walk
 struct GridProblem {
-  int N, B, K, rz, rs, H;
-  const void* z;               // [N, B, K, rz] (dtype)
-  int dtype;
-  const float* s;              // [N, B-1, rs] (fp32)
-  const void* W1;              // [H, 2 rz + rs]
-  long long ldw1;
+  int N, B, K, H;
+  int dtype;                   // storage type of b1 and w2
+  const float* AB;             // [N*B*K, 2H] fp32: W1a z | W1b z
+  const float* C;              // [nq, N*(B-1), H] fp32: parts of W1s s_p (summed)
+  int nq;
   const void* b1;              // [H] (dtype) or null
   const void* w2;              // [H] (dtype)
   float b2;
@@ -77,6 +76,9 @@ struct GridProblem {
   float* S;                    // [N, B-1, K, K]
 };
 hipError_t launch_grid(const GridProblem& p, hipStream_t st);
+
+// s3 = three bf16 rows per value of s (hi, mid, lo), s3[q * n + i]
+hipError_t launch_split3(const float* s, long long n, void* s3, hipStream_t st);
 
 hipError_t launch_walk(const float* S, const float* cand_logits, const int32_t* cand_ids, int N,
                        int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);

@@ -72,15 +72,19 @@ pair_state_kernel(const float* __restrict__ Y, int split, int N, int B, int ldy,
 
 // bf16 path: LayerNorm of BM rows straight into an LDS operand tile, then
 // y = W x for those rows on MFMA (W rows streamed from L2 as 16-byte
-// fragments).  Used for gf = W_fg g (fp32 out) and z = W_fb b + gf[slot]
-// (bf16 out), so the normalised g and b never leave the chip.
-template <int BM, int RMAX, int MODE>
+// fragments, one k step prefetched).  Used for gf = W_fg g (fp32 out) and
+// z = W_fb b + gf[slot] (bf16 out), so the normalised g and b never leave the
+// chip.  The LN phase keeps several rows' loads (all SPLIT partial sums of
+// each) in flight at once: a wave normalises RP rows per pass.
+template <int BM, int RMAX, int SPLIT, int MODE>
 __global__ void __launch_bounds__(256)
-ln_gemm_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0, int r, float eps,
+ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, float eps,
                const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
                bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div) {
   constexpr int kStr = RMAX * 2 + 16;              // LDS bytes per tile row
   constexpr int VPL = RMAX / kWave;
+  constexpr int RP0 = 64 / (VPL * SPLIT);
+  constexpr int RP = RP0 < 1 ? 1 : (RP0 > BM / 4 ? BM / 4 : RP0);
   constexpr int WM = BM == 64 ? 2 : 1;             // wave grid: WM x (4 / WM)
   constexpr int WN = 4 / WM;
   constexpr int TM = BM / (16 * WM);
@@ -92,38 +96,49 @@ ln_gemm_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0,
   const int wv = tid >> 6;
   const int m0 = blockIdx.x * BM;
 
-  // ---- LayerNorm, one wave per row
-  for (int rr = wv; rr < BM; rr += 4) {
-    const int m = m0 + rr;
-    uint16_t* trow = reinterpret_cast<uint16_t*>(tile + rr * kStr);
-    if (m >= M) {
-      for (int c = l; c < r; c += kWave) trow[c] = 0;
-      continue;
-    }
-    float v[VPL];
-    float sum = 0.f;
+  // ---- LayerNorm: wave wv owns rows wv*RP + 4*RP*j + q, q < RP
+  for (int rb = wv * RP; rb < BM; rb += 4 * RP) {
+    float v[RP][VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int c = l + i * kWave;
-      float a = 0.f;
-      if (c < r)
-        for (int s2 = 0; s2 < split; ++s2) a += x[(static_cast<long long>(s2) * M + m) * ldx + col0 + c];
-      v[i] = a;
-      sum += a;
-    }
-    const float mean = wave_sum(sum) / static_cast<float>(r);
-    float sq = 0.f;
+    for (int q = 0; q < RP; ++q) {
+      const int m = min(m0 + rb + q, M - 1);
+      float part[SPLIT][VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int c = l + i * kWave;
-      v[i] = c < r ? v[i] - mean : 0.f;
-      sq += v[i] * v[i];
-    }
-    const float inv = 1.0f / sqrtf(wave_sum(sq) / static_cast<float>(r) + eps);
+      for (int s2 = 0; s2 < SPLIT; ++s2)
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int c = l + i * kWave;
-      if (c < r) trow[c] = f32_to_bf16(v[i] * inv);
+        for (int i = 0; i < VPL; ++i) {
+          const int c = l + i * kWave;
+          part[s2][i] = c < r ? x[(static_cast<long long>(s2) * M + m) * ldx + col0 + c] : 0.f;
+        }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        float a = part[0][i];
+#pragma unroll
+        for (int s2 = 1; s2 < SPLIT; ++s2) a += part[s2][i];
+        v[q][i] = a;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RP; ++q) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) sum += v[q][i];
+      const float mean = wave_sum(sum) / static_cast<float>(r);
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int c = l + i * kWave;
+        v[q][i] = c < r ? v[q][i] - mean : 0.f;
+        sq += v[q][i] * v[q][i];
+      }
+      const float inv = 1.0f / sqrtf(wave_sum(sq) / static_cast<float>(r) + eps);
+      const bool live = m0 + rb + q < M;
+      uint16_t* trow = reinterpret_cast<uint16_t*>(tile + (rb + q) * kStr);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int c = l + i * kWave;
+        if (c < r) trow[c] = live ? f32_to_bf16(v[q][i] * inv) : 0;
+      }
     }
   }
   __syncthreads();
@@ -139,7 +154,19 @@ ln_gemm_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0,
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const bf16* wrow[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+      wrow[b] = W + static_cast<long long>(min(n0 + b * 16 + frow, N - 1)) * ldw + wcol0 + fk;
+    uint4 wf[TN];
+#pragma unroll
+    for (int b = 0; b < TN; ++b) wf[b] = *reinterpret_cast<const uint4*>(wrow[b]);
     for (int k = 0; k < r; k += 32) {
+      uint4 wn_[TN];
+      const bool more = k + 32 < r;
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        wn_[b] = more ? *reinterpret_cast<const uint4*>(wrow[b] + k + 32) : wf[b];
       bf16x8_t fa[TM];
 #pragma unroll
       for (int a = 0; a < TM; ++a)
@@ -147,13 +174,13 @@ ln_gemm_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0,
                     tile + (wm * (BM / WM) + a * 16 + frow) * kStr + (k + fk) * 2));
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
-        const int n = min(n0 + b * 16 + frow, N - 1);
-        const uint4 u = *reinterpret_cast<const uint4*>(W + static_cast<long long>(n) * ldw + wcol0 + k + fk);
-        const bf16x8_t fw = __builtin_bit_cast(bf16x8_t, u);
+        const bf16x8_t fw = __builtin_bit_cast(bf16x8_t, wf[b]);
 #pragma unroll
         for (int a = 0; a < TM; ++a)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fw, acc[a][b], 0, 0, 0);
       }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) wf[b] = wn_[b];
     }
 #pragma unroll
     for (int a = 0; a < TM; ++a)
@@ -207,14 +234,24 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   const bf16* Wb = static_cast<const bf16*>(W);
   bf16* ob = static_cast<bf16*>(out_bf);
   const bool bias = out_bf != nullptr;
-#define DCOCO_LNG(BMV, RM, MD)                                                                        \
-  hipLaunchKernelGGL((ln_gemm_kernel<BMV, RM, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, split, \
-                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div)
-  if (r <= 512) {
-    if (bias) DCOCO_LNG(64, 512, 1); else DCOCO_LNG(64, 512, 0);
+  if (split != 1 && split != 2 && split != 4) return hipErrorInvalidValue;
+  // small row counts: 16-row tiles for more workgroups
+  const bool small = r > 512 || M < 4096;
+#define DCOCO_LNG(BMV, RM, SP, MD)                                                                      \
+  hipLaunchKernelGGL((ln_gemm_kernel<BMV, RM, SP, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, M, \
+                     ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div)
+#define DCOCO_LNG_SPLIT(BMV, RM, MD)                 \
+  if (split == 1) DCOCO_LNG(BMV, RM, 1, MD);         \
+  else if (split == 2) DCOCO_LNG(BMV, RM, 2, MD);    \
+  else DCOCO_LNG(BMV, RM, 4, MD)
+  if (!small) {
+    if (bias) { DCOCO_LNG_SPLIT(64, 512, 1); } else { DCOCO_LNG_SPLIT(64, 512, 0); }
+  } else if (r <= 512) {
+    if (bias) { DCOCO_LNG_SPLIT(16, 512, 1); } else { DCOCO_LNG_SPLIT(16, 512, 0); }
   } else {
-    if (bias) DCOCO_LNG(16, 2048, 1); else DCOCO_LNG(16, 2048, 0);
+    if (bias) { DCOCO_LNG_SPLIT(16, 2048, 1); } else { DCOCO_LNG_SPLIT(16, 2048, 0); }
   }
+#undef DCOCO_LNG_SPLIT
 #undef DCOCO_LNG
   return hipGetLastError();
 }

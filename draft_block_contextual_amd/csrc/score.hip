@@ -36,135 +36,90 @@ constexpr float kNegLog2e = -1.4426950408889634f;
 constexpr float kNegLn2 = -0.6931471805599453f;
 
 struct GridDev {
-  int N, B, K, rz, rs, H;
-  const void* z;
-  const float* s;        // [N, B-1, rs] pair states (fp32)
-  const void* W1;        // [H, 2 rz + rs]
-  long long ldw1;
+  int N, B, K, H, P, nq;
+  const float* AB;       // [N*B*K, 2H]: W1a z | W1b z
+  const float* C;        // [nq, P, H]: parts of W1s s_p
   const void* b1;        // [H] or null
-  const void* w2;
+  const void* w2;        // [H]
   float b2;
   const float* cand_logits;
   float* S;
 };
 
-__device__ __forceinline__ void load8_f32(const bf16* p, float (&f)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+// s -> three bf16 rows per pair (hi, mid, lo with s = hi + mid + lo exactly
+// for normal values: each part takes the next 8 significand bits), the MFMA
+// operand that keeps W1s s_p at fp32 accuracy on bf16 matrix cores.
+__global__ void __launch_bounds__(256)
+split3_kernel(const float* __restrict__ s, long long n, uint16_t* __restrict__ s3) {
+  for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
+    const float x = s[i];
+    const uint16_t hi = f32_to_bf16(x);
+    const float r1 = x - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    s3[i] = hi;
+    s3[n + i] = mid;
+    s3[2 * n + i] = lo;
   }
 }
-__device__ __forceinline__ void load8_f32(const float* p, float (&f)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
 
-// MFMA operand fragment: 8 consecutive k values of one row.
-template <typename T> struct FragT;
-template <> struct FragT<bf16> {
-  bf16x8_t v;
-  __device__ void load(const bf16* p, bool ok) {
-    const uint4 u = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
-    v = __builtin_bit_cast(bf16x8_t, u);
-  }
-};
-template <> struct FragT<float> {
-  float v[8];
-  __device__ void load(const float* p, bool ok) {
-    if (ok) {
-      load8_f32(p, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
-  }
-};
-
-__device__ __forceinline__ f32x4_t mma(const FragT<bf16>& a, const FragT<bf16>& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma(const FragT<float>& a, const FragT<float>& b, f32x4_t c) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[t], b.v[t], c, 0, 0, 0);
-  return c;
-}
-
-// One workgroup (4 waves) per (block n, pair p).  The hidden units are cut
-// into chunks of 32; wave w takes chunks w, w+4, ...  For a chunk, the wave
-// forms A = -log2(e) W1a z_{p,a} and B = -log2(e) (W1b z_{p+1,b} + C_p) for
-// its 32 units on MFMA into its own LDS tile, then runs the K x K x 32 grid
-// from LDS.  Lane (la, lb) of the 8 x 8 lane grid owns the TA x TA outputs
-// a = TA la + i, b = TA lb + j (K <= 8 TA).  The four waves' partial sums are
-// added in a fixed order at the end.
-constexpr int kChunkH = 32;
-constexpr int kChunkStr = kChunkH + 4;     // LDS row stride (floats)
-constexpr int kMaxPair = 2048;             // largest supported pair width
-
+// The K x K x H grid.  Inputs per pair (n, p): A = W1a z_{p,a} and
+// B = W1b z_{p+1,b} (rows of the fp32 product AB = z [W1a; W1b]^T), and
+// C_p = sum of nq rows of the fp32 product of the s operand with W1s.  With
+// A' = -log2(e) A, B' = -log2(e) (B + C_p + b1) and w' = -ln2 w2, the term
+// is  w2 SiLU(u) = w' (A' + B') / (1 + 2^A' 2^B').  The hidden units are
+// processed in slabs staged in LDS as 2^A', w'A' (per candidate a) and
+// 2^B', w'B' (per candidate b), so one grid element costs an fma, a rcp, an
+// add and an fma.  If some |A'| in a slab exceeds 64 the factors could
+// over/underflow where their product does not; that slab stages A', B' and
+// w' instead and evaluates 2^(A'+B') directly.
+//
+// One workgroup (4 waves) per pair; each wave takes a quarter of every slab's
+// units for all K x K outputs: lane (la, lb) of the 8 x 8 lane grid owns
+// a = TA la + i, b = TA lb + j (i, j < TA, K <= 8 TA).  The four waves'
+// partial sums are added in a fixed order at the end.
 template <int TA>
-struct GridSmem {
+struct GridShape {
   static constexpr int KR = 8 * TA;
-  static constexpr int KRM = ((KR + 15) / 16) * 16;
-  static constexpr int kTile = KRM * kChunkStr;
-  static constexpr int kRed = KR * KR;
-  static constexpr int kWork = 2 * kTile + 2 * kChunkH;   // A, B tiles, w2', C
-  static constexpr int kPerWave = kWork > kRed ? kWork : kRed;
+  static constexpr int HS = 4096 / KR;           // hidden units per slab
+  static constexpr int STR = HS + 4;             // LDS row stride (floats)
+  static constexpr int ARR = KR * STR;
+  static constexpr int kRed = 4 * KR * KR;
+  static constexpr int kSmem = (4 * ARR > kRed ? 4 * ARR : kRed) + 2 * HS;
 };
 
 template <typename T, int TA>
 __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
-  using SM = GridSmem<TA>;
-  constexpr int KR = SM::KR;
-  constexpr int MT = SM::KRM / 16;
-  __shared__ __align__(16) float smem[4 * SM::kPerWave];
+  using GS = GridShape<TA>;
+  constexpr int KR = GS::KR;
+  constexpr int HS = GS::HS;
+  constexpr int STR = GS::STR;
+  __shared__ __align__(16) float smem[GS::kSmem];
+  __shared__ int s_slow;
+  float* arr0 = smem;                 // 2^A'  (or A')
+  float* arr1 = smem + GS::ARR;       // w'A'
+  float* arr2 = smem + 2 * GS::ARR;   // 2^B'  (or B')
+  float* arr3 = smem + 3 * GS::ARR;   // w'B'
+  float* sCp = smem + 4 * GS::ARR;    // per unit: -log2(e) (C_p + b1)
+  float* sWp = sCp + HS;              // per unit: w'
 
   const int np = blockIdx.x;
   const int Bm1 = g.B - 1;
   const int n = np / Bm1;
   const int p = np % Bm1;
   const int K = g.K;
-  const int rz = g.rz;
-  const T* za = static_cast<const T*>(g.z) + (static_cast<long long>(n) * g.B + p) * K * rz;
-  const T* zb = za + static_cast<long long>(K) * rz;
-  const T* W1 = static_cast<const T*>(g.W1);
+  const int H = g.H;
+  const long long ldab = 2ll * H;
+  const float* Arow = g.AB + (static_cast<long long>(n) * g.B + p) * K * ldab;
+  const float* Brow = g.AB + (static_cast<long long>(n) * g.B + p + 1) * K * ldab + H;
   const T* w2 = static_cast<const T*>(g.w2);
+  const T* b1 = static_cast<const T*>(g.b1);
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wv = tid >> 6;
-  const int frow = l & 15;
-  const int fk = (l >> 4) * 8;
   const int la = l >> 3;
   const int lb = l & 7;
-  float* sA = smem + wv * SM::kPerWave;
-  float* sB = sA + SM::kTile;
-  float* sW = sB + SM::kTile;
-  float* sC = sW + kChunkH;
-  // s_p as MFMA operand rows: bf16 path hi/mid/lo parts in rows 0..2, fp32
-  // path s_p itself in row 0
-  constexpr int kSRows = std::is_same<T, bf16>::value ? 3 : 1;
-  __shared__ __align__(16) T sS[kSRows * kMaxPair];
-  const int rs = g.rs;
-  const float* sp = g.s + static_cast<long long>(np) * rs;
-  for (int k = tid; k < rs; k += 256) {
-    const float x = sp[k];
-    if constexpr (std::is_same<T, bf16>::value) {
-      const uint16_t hi = f32_to_bf16(x);
-      const float r1 = x - bf16_to_f32(hi);
-      const uint16_t mid = f32_to_bf16(r1);
-      const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-      sS[k] = bf16{hi};
-      sS[kMaxPair + k] = bf16{mid};
-      sS[2 * kMaxPair + k] = bf16{lo};
-    } else {
-      sS[k] = x;
-    }
-  }
-  __syncthreads();
 
   float acc[TA][TA];
 #pragma unroll
@@ -172,117 +127,111 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
 #pragma unroll
     for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
 
-  const int nchunks = g.H / kChunkH;
-  for (int c = wv; c < nchunks; c += 4) {
-    const int h0 = c * kChunkH;
-    // ---- per-candidate products for 32 hidden units on MFMA
-    f32x4_t accA[MT][2], accB[MT][2];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        accA[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        accB[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    for (int k = 0; k < rz; k += 32) {
-      FragT<T> fa[MT], fb[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int row = m * 16 + frow;
-        fa[m].load(za + static_cast<long long>(row) * rz + k + fk, row < K);
-        fb[m].load(zb + static_cast<long long>(row) * rz + k + fk, row < K);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const T* wrow = W1 + static_cast<long long>(h0 + t * 16 + frow) * g.ldw1 + k + fk;
-        FragT<T> wa, wb;
-        wa.load(wrow, true);
-        wb.load(wrow + rz, true);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          accA[m][t] = mma(fa[m], wa, accA[m][t]);
-          accB[m][t] = mma(fb[m], wb, accB[m][t]);
-        }
-      }
+  for (int hs0 = 0; hs0 < H; hs0 += HS) {
+    const int hlen = min(HS, H - hs0);
+    // ---- stage the slab
+    if (tid == 0) s_slow = 0;
+    for (int h = tid; h < hlen; h += 256) {
+      float c = 0.f;
+      for (int q = 0; q < g.nq; ++q) c += g.C[(static_cast<long long>(q) * g.P + np) * H + hs0 + h];
+      if (b1) c += Elem<T>::to_f32(b1[hs0 + h]);
+      sCp[h] = kNegLog2e * c;
+      sWp[h] = kNegLn2 * Elem<T>::to_f32(w2[hs0 + h]);
     }
-    // ---- C_p = W1s s_p + b1 for the chunk's 32 units
-    {
-      f32x4_t accC[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-      for (int k = 0; k < rs; k += 32) {
-        FragT<T> fs;
-        fs.load(&sS[(frow < kSRows ? frow : 0) * kMaxPair + k + fk], frow < kSRows);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          FragT<T> ws;
-          ws.load(W1 + static_cast<long long>(h0 + t * 16 + frow) * g.ldw1 + 2 * rz + k + fk, true);
-          accC[t] = mma(fs, ws, accC[t]);
-        }
+    __syncthreads();
+    bool big = false;
+    const int q4 = hlen / 4;
+    for (int idx = tid; idx < KR * q4; idx += 256) {
+      const int row = idx / q4;
+      const int h = (idx - row * q4) * 4;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (row < K) {
+        a = *reinterpret_cast<const float4*>(Arow + row * ldab + hs0 + h);
+        b = *reinterpret_cast<const float4*>(Brow + row * ldab + hs0 + h);
       }
-      // rows 0..kSRows-1 of the product live in lanes 0..15
-      if (l < 16) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float cv = accC[t][0];
-          if constexpr (kSRows == 3) cv = (cv + accC[t][1]) + accC[t][2];
-          if (g.b1) cv += Elem<T>::to_f32(static_cast<const T*>(g.b1)[h0 + t * 16 + l]);
-          sC[t * 16 + l] = cv;
-        }
+      const float4 cp = *reinterpret_cast<const float4*>(sCp + h);
+      a.x *= kNegLog2e; a.y *= kNegLog2e; a.z *= kNegLog2e; a.w *= kNegLog2e;
+      b.x = fmaf(kNegLog2e, b.x, cp.x); b.y = fmaf(kNegLog2e, b.y, cp.y);
+      b.z = fmaf(kNegLog2e, b.z, cp.z); b.w = fmaf(kNegLog2e, b.w, cp.w);
+      big |= fabsf(a.x) > 64.f || fabsf(a.y) > 64.f || fabsf(a.z) > 64.f || fabsf(a.w) > 64.f;
+      *reinterpret_cast<float4*>(arr0 + row * STR + h) = a;
+      *reinterpret_cast<float4*>(arr2 + row * STR + h) = b;
+    }
+    if (big) s_slow = 1;
+    __syncthreads();
+    const bool slow = s_slow != 0;
+    if (!slow) {
+      for (int idx = tid; idx < KR * q4; idx += 256) {
+        const int row = idx / q4;
+        const int h = (idx - row * q4) * 4;
+        const float4 wq = *reinterpret_cast<const float4*>(sWp + h);
+        float4 a = *reinterpret_cast<const float4*>(arr0 + row * STR + h);
+        float4 b = *reinterpret_cast<const float4*>(arr2 + row * STR + h);
+        *reinterpret_cast<float4*>(arr1 + row * STR + h) = make_float4(wq.x * a.x, wq.y * a.y, wq.z * a.z, wq.w * a.w);
+        *reinterpret_cast<float4*>(arr3 + row * STR + h) = make_float4(wq.x * b.x, wq.y * b.y, wq.z * b.z, wq.w * b.w);
+        a.x = __builtin_amdgcn_exp2f(a.x); a.y = __builtin_amdgcn_exp2f(a.y);
+        a.z = __builtin_amdgcn_exp2f(a.z); a.w = __builtin_amdgcn_exp2f(a.w);
+        b.x = __builtin_amdgcn_exp2f(b.x); b.y = __builtin_amdgcn_exp2f(b.y);
+        b.z = __builtin_amdgcn_exp2f(b.z); b.w = __builtin_amdgcn_exp2f(b.w);
+        *reinterpret_cast<float4*>(arr0 + row * STR + h) = a;
+        *reinterpret_cast<float4*>(arr2 + row * STR + h) = b;
       }
-      __builtin_amdgcn_wave_barrier();
+      __syncthreads();
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = t * 16 + (l & 15);
-      const float cb = sC[col];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = m * 16 + (l >> 4) * 4 + v;
-          sA[row * kChunkStr + col] = kNegLog2e * accA[m][t][v];
-          sB[row * kChunkStr + col] = kNegLog2e * (accB[m][t][v] + cb);
-        }
-    }
-    if (l < kChunkH) sW[l] = kNegLn2 * Elem<T>::to_f32(w2[h0 + l]);
-    // LDS operations of one wave complete in order: the reads below see the
-    // writes above without a barrier
-    __builtin_amdgcn_wave_barrier();
-    // ---- the K x K x 32 grid
+    // ---- this wave's quarter of the slab
+    const int h_beg = wv * q4;
+    const int h_end = h_beg + q4;
+    if (!slow) {
 #pragma unroll 2
-    for (int h = 0; h < kChunkH; h += 4) {
-      float4 av[TA], bv[TA];
-#pragma unroll
-      for (int i = 0; i < TA; ++i) {
-        av[i] = *reinterpret_cast<const float4*>(&sA[(la * TA + i) * kChunkStr + h]);
-        bv[i] = *reinterpret_cast<const float4*>(&sB[(lb * TA + i) * kChunkStr + h]);
-      }
-      const float4 wq = *reinterpret_cast<const float4*>(&sW[h]);
-      const float w4[4] = {wq.x, wq.y, wq.z, wq.w};
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int h = h_beg; h < h_end; h += 4) {
+        float4 ea[TA], wa[TA], eb[TA], wb[TA];
 #pragma unroll
         for (int i = 0; i < TA; ++i) {
-          const float a4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-#pragma unroll
-          for (int j = 0; j < TA; ++j) {
-            const float b4[4] = {bv[j].x, bv[j].y, bv[j].z, bv[j].w};
-            const float t = a4[cc] + b4[cc];
-            const float e = __builtin_amdgcn_exp2f(t);
-            const float r = __builtin_amdgcn_rcpf(1.0f + e);
-            acc[i][j] = fmaf(w4[cc], t * r, acc[i][j]);
-          }
+          ea[i] = *reinterpret_cast<const float4*>(arr0 + (la * TA + i) * STR + h);
+          wa[i] = *reinterpret_cast<const float4*>(arr1 + (la * TA + i) * STR + h);
+          eb[i] = *reinterpret_cast<const float4*>(arr2 + (lb * TA + i) * STR + h);
+          wb[i] = *reinterpret_cast<const float4*>(arr3 + (lb * TA + i) * STR + h);
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < TA; ++i)
+#pragma unroll
+            for (int j = 0; j < TA; ++j) {
+              const float den = fmaf(ea[i][c], eb[j][c], 1.0f);
+              const float r = __builtin_amdgcn_rcpf(den);
+              acc[i][j] = fmaf(wa[i][c] + wb[j][c], r, acc[i][j]);
+            }
+      }
+    } else {
+      for (int h = h_beg; h < h_end; h += 4) {
+        float4 av[TA], bv[TA];
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+          av[i] = *reinterpret_cast<const float4*>(arr0 + (la * TA + i) * STR + h);
+          bv[i] = *reinterpret_cast<const float4*>(arr2 + (lb * TA + i) * STR + h);
+        }
+        const float4 wq = *reinterpret_cast<const float4*>(sWp + h);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int i = 0; i < TA; ++i)
+#pragma unroll
+            for (int j = 0; j < TA; ++j) {
+              const float t = av[i][c] + bv[j][c];
+              const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+              acc[i][j] = fmaf(wq[c], t * r, acc[i][j]);
+            }
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
   }
   // ---- add the four waves' partial sums in a fixed order
-  __syncthreads();
-  float* red = smem + wv * SM::kPerWave;
+  float* red = smem;
 #pragma unroll
   for (int i = 0; i < TA; ++i)
 #pragma unroll
-    for (int j = 0; j < TA; ++j) red[(la * TA + i) * KR + lb * TA + j] = acc[i][j];
+    for (int j = 0; j < TA; ++j) red[(wv * KR + la * TA + i) * KR + lb * TA + j] = acc[i][j];
   __syncthreads();
   const float* lnext = g.cand_logits + (static_cast<long long>(n) * g.B + p + 1) * K;
   float* Sp = g.S + static_cast<long long>(np) * K * K;
@@ -290,8 +239,7 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
     const int a = idx / K;
     const int b = idx - a * K;
     const int o = a * KR + b;
-    const float sum = ((smem[o] + smem[SM::kPerWave + o]) + smem[2 * SM::kPerWave + o]) +
-                      smem[3 * SM::kPerWave + o];
+    const float sum = ((red[o] + red[KR * KR + o]) + red[2 * KR * KR + o]) + red[3 * KR * KR + o];
     Sp[idx] = lnext[b] + (sum + g.b2);
   }
 }
@@ -349,8 +297,8 @@ walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int
 template <typename T>
 hipError_t launch_grid_t(const GridProblem& q, hipStream_t st) {
   GridDev g;
-  g.N = q.N; g.B = q.B; g.K = q.K; g.rz = q.rz; g.rs = q.rs; g.H = q.H;
-  g.z = q.z; g.s = q.s; g.W1 = q.W1; g.ldw1 = q.ldw1; g.b1 = q.b1; g.w2 = q.w2; g.b2 = q.b2;
+  g.N = q.N; g.B = q.B; g.K = q.K; g.H = q.H; g.P = q.N * (q.B - 1); g.nq = q.nq;
+  g.AB = q.AB; g.C = q.C; g.b1 = q.b1; g.w2 = q.w2; g.b2 = q.b2;
   g.cand_logits = q.cand_logits; g.S = q.S;
   const int blocks = q.N * (q.B - 1);
   if (blocks <= 0) return hipSuccess;
@@ -368,6 +316,14 @@ hipError_t launch_grid_t(const GridProblem& q, hipStream_t st) {
 hipError_t launch_grid(const GridProblem& q, hipStream_t st) {
   if (q.dtype == kDtypeBf16) return launch_grid_t<bf16>(q, st);
   return launch_grid_t<float>(q, st);
+}
+
+hipError_t launch_split3(const float* s, long long n, void* s3, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(split3_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st, s, n,
+                     static_cast<uint16_t*>(s3));
+  return hipGetLastError();
 }
 
 hipError_t launch_walk(const float* S, const float* cand_logits, const int32_t* cand_ids, int N,
