@@ -411,25 +411,48 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
     }
   }
 
+  // epilogue; with a bias, all bias values are fetched (clamped, branch-free)
+  // before any store so the loads overlap
+  if constexpr (MODE == 1) {
+    float bias[TM][TN][4];
 #pragma unroll
-  for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < TN; ++b)
+      for (int b = 0; b < TN; ++b)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v;
-        const int n = n0 + wn * (BN / 2) + b * 16 + (l & 15);
-        if (m < p.M && n < p.N) {
-          if constexpr (MODE == 0) {
-            p.out_f32[(static_cast<long long>(zs) * p.M + m) * p.ldo + n] = acc[a][b][v];
-          } else {
-            float x = acc[a][b][v];
-            if (p.row_bias) x += p.row_bias[static_cast<long long>(m / p.row_bias_div) * p.N + n];
-            if (p.col_bias) x += bf16_to_f32(static_cast<const bf16*>(p.col_bias)[n].bits);
-            static_cast<bf16*>(p.out)[static_cast<long long>(m) * p.ldo + n] = bf16{f32_to_bf16(x)};
-          }
+        for (int v = 0; v < 4; ++v) {
+          const int m = min(m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v, p.M - 1);
+          const int n = min(n0 + wn * (BN / 2) + b * 16 + (l & 15), p.N - 1);
+          float x = 0.f;
+          if (p.row_bias) x += p.row_bias[static_cast<long long>(m / p.row_bias_div) * p.N + n];
+          if (p.col_bias) x += bf16_to_f32(static_cast<const bf16*>(p.col_bias)[n].bits);
+          bias[a][b][v] = x;
         }
-      }
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v;
+          const int n = n0 + wn * (BN / 2) + b * 16 + (l & 15);
+          if (m < p.M && n < p.N)
+            static_cast<bf16*>(p.out)[static_cast<long long>(m) * p.ldo + n] =
+                bf16{f32_to_bf16(acc[a][b][v] + bias[a][b][v])};
+        }
+  } else {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v;
+          const int n = n0 + wn * (BN / 2) + b * 16 + (l & 15);
+          if (m < p.M && n < p.N)
+            p.out_f32[(static_cast<long long>(zs) * p.M + m) * p.ldo + n] = acc[a][b][v];
+        }
+  }
 }
 
 struct Tile {

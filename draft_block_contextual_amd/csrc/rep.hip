@@ -158,15 +158,7 @@ ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, flo
 #pragma unroll
     for (int b = 0; b < TN; ++b)
       wrow[b] = W + static_cast<long long>(min(n0 + b * 16 + frow, N - 1)) * ldw + wcol0 + fk;
-    uint4 wf[TN];
-#pragma unroll
-    for (int b = 0; b < TN; ++b) wf[b] = *reinterpret_cast<const uint4*>(wrow[b]);
-    for (int k = 0; k < r; k += 32) {
-      uint4 wn_[TN];
-      const bool more = k + 32 < r;
-#pragma unroll
-      for (int b = 0; b < TN; ++b)
-        wn_[b] = more ? *reinterpret_cast<const uint4*>(wrow[b] + k + 32) : wf[b];
+    auto kstep = [&](int k, const uint4 (&wf)[TN]) {
       bf16x8_t fa[TM];
 #pragma unroll
       for (int a = 0; a < TM; ++a)
@@ -179,27 +171,62 @@ ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, flo
         for (int a = 0; a < TM; ++a)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fw, acc[a][b], 0, 0, 0);
       }
+    };
+    // two fragment buffers, one k step in flight ahead of the MFMAs
+    uint4 w0[TN], w1[TN];
 #pragma unroll
-      for (int b = 0; b < TN; ++b) wf[b] = wn_[b];
+    for (int b = 0; b < TN; ++b) w0[b] = *reinterpret_cast<const uint4*>(wrow[b]);
+    for (int k = 0; k < r; k += 64) {
+      const bool two = k + 32 < r;
+      if (two) {
+#pragma unroll
+        for (int b = 0; b < TN; ++b) w1[b] = *reinterpret_cast<const uint4*>(wrow[b] + k + 32);
+      }
+      kstep(k, w0);
+      if (k + 64 < r) {
+#pragma unroll
+        for (int b = 0; b < TN; ++b) w0[b] = *reinterpret_cast<const uint4*>(wrow[b] + k + 64);
+      }
+      if (two) kstep(k + 32, w1);
     }
+    // epilogue: every bias value is fetched (clamped, branch-free) before
+    // any store, so the loads overlap
+    int mrow[TM][4];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * (BM / WM) + a * 16 + (l >> 4) * 4 + v;
-        if (m >= M) continue;
-        const float* rb = MODE == 1 ? row_bias + static_cast<long long>(m / row_div) * N : nullptr;
+      for (int v = 0; v < 4; ++v) mrow[a][v] = m0 + wm * (BM / WM) + a * 16 + (l >> 4) * 4 + v;
+    if constexpr (MODE == 1) {
+      float bias[TM][4][TN];
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int n = n0 + b * 16 + (l & 15);
-          if (n >= N) continue;
-          if constexpr (MODE == 0) {
-            out_f32[static_cast<long long>(m) * N + n] = acc[a][b][v];
-          } else {
-            out_bf[static_cast<long long>(m) * N + n] = bf16{f32_to_bf16(acc[a][b][v] + rb[n])};
-          }
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float* rb = row_bias + static_cast<long long>(min(mrow[a][v], M - 1) / row_div) * N;
+#pragma unroll
+          for (int b = 0; b < TN; ++b) bias[a][v][b] = rb[min(n0 + b * 16 + (l & 15), N - 1)];
         }
-      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            const int n = n0 + b * 16 + (l & 15);
+            if (mrow[a][v] < M && n < N)
+              out_bf[static_cast<long long>(mrow[a][v]) * N + n] = bf16{f32_to_bf16(acc[a][b][v] + bias[a][v][b])};
+          }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            const int n = n0 + b * 16 + (l & 15);
+            if (mrow[a][v] < M && n < N) out_f32[static_cast<long long>(mrow[a][v]) * N + n] = acc[a][b][v];
+          }
+    }
   }
 }
 
