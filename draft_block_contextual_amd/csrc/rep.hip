@@ -85,7 +85,7 @@ ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, flo
   constexpr int VPL = RMAX / kWave;
   constexpr int RP0 = 64 / (VPL * SPLIT);
   constexpr int RP = RP0 < 1 ? 1 : (RP0 > BM / 4 ? BM / 4 : RP0);
-  constexpr int WM = BM == 64 ? 2 : 1;             // wave grid: WM x (4 / WM)
+  constexpr int WM = BM >= 32 ? 2 : 1;             // wave grid: WM x (4 / WM)
   constexpr int WN = 4 / WM;
   constexpr int TM = BM / (16 * WM);
   constexpr int TN = 8;                            // 128 columns per wave pass
@@ -262,8 +262,7 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   bf16* ob = static_cast<bf16*>(out_bf);
   const bool bias = out_bf != nullptr;
   if (split != 1 && split != 2 && split != 4) return hipErrorInvalidValue;
-  // small row counts: 16-row tiles for more workgroups
-  const bool small = r > 512 || M < 4096;
+  // tile rows: enough workgroups to cover the chip, LN width in registers
 #define DCOCO_LNG(BMV, RM, SP, MD)                                                                      \
   hipLaunchKernelGGL((ln_gemm_kernel<BMV, RM, SP, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, M, \
                      ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div)
@@ -271,8 +270,12 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   if (split == 1) DCOCO_LNG(BMV, RM, 1, MD);         \
   else if (split == 2) DCOCO_LNG(BMV, RM, 2, MD);    \
   else DCOCO_LNG(BMV, RM, 4, MD)
-  if (!small) {
-    if (bias) { DCOCO_LNG_SPLIT(64, 512, 1); } else { DCOCO_LNG_SPLIT(64, 512, 0); }
+  if (r <= 256) {
+    if (M >= 4096) {
+      if (bias) { DCOCO_LNG_SPLIT(32, 256, 1); } else { DCOCO_LNG_SPLIT(32, 256, 0); }
+    } else {
+      if (bias) { DCOCO_LNG_SPLIT(16, 256, 1); } else { DCOCO_LNG_SPLIT(16, 256, 0); }
+    }
   } else if (r <= 512) {
     if (bias) { DCOCO_LNG_SPLIT(16, 512, 1); } else { DCOCO_LNG_SPLIT(16, 512, 0); }
   } else {

@@ -246,8 +246,15 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
 
 constexpr int kWalkLds = 8192;   // floats of scores staged per batch
 
-__device__ __forceinline__ uint64_t arg_comp(float v, int idx) {
-  return (static_cast<uint64_t>(order_key(v)) << 32) | static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(idx));
+// argmax over lanes 0..K-1 of one wave: the largest order key, the lowest lane
+// among equal keys (lanes >= K carry key 0, the NaN key, and sit above every
+// valid lane, so they never win)
+__device__ __forceinline__ int wave_argmax(float v, bool valid) {
+  const uint32_t key = valid ? order_key(v) : 0u;
+  uint32_t m = key;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o, kWave)));
+  return __builtin_ctzll(ballot(key == m));
 }
 
 __global__ void __launch_bounds__(256)
@@ -265,26 +272,29 @@ walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int
   const int32_t* idn = ids + static_cast<long long>(n) * B * K;
   int k = 0;
   if (tid < kWave) {
-    const uint64_t c = l < K ? arg_comp(cln[l], l) : 0ull;
-    const uint64_t best = wave_max_u64(c);
-    k = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+    k = wave_argmax(l < K ? cln[l] : 0.f, l < K);
     if (l == 0) {
       if (sel_idx) sel_idx[static_cast<long long>(n) * B] = k;
       sel_tok[static_cast<long long>(n) * B] = idn[k];
     }
   }
+  const bool vec = ((reinterpret_cast<uintptr_t>(Sn) & 15) == 0) && (per % 4 == 0);
   for (int p0 = 0; p0 < Bm1; p0 += batch) {
     const int cnt = min(batch, Bm1 - p0);
     const int nval = cnt * per;
+    const float* src = Sn + static_cast<long long>(p0) * per;
     __syncthreads();
-    for (int i = tid; i < nval; i += 256) sS[i] = Sn[static_cast<long long>(p0) * per + i];
+    if (vec) {
+      for (int i = tid * 4; i < nval; i += 1024)
+        *reinterpret_cast<float4*>(&sS[i]) = *reinterpret_cast<const float4*>(src + i);
+    } else {
+      for (int i = tid; i < nval; i += 256) sS[i] = src[i];
+    }
     __syncthreads();
     if (tid < kWave) {
       for (int q = 0; q < cnt; ++q) {
         const int p = p0 + q;
-        const uint64_t c = l < K ? arg_comp(sS[q * per + k * K + l], l) : 0ull;
-        const uint64_t best = wave_max_u64(c);
-        k = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+        k = wave_argmax(l < K ? sS[q * per + k * K + l] : 0.f, l < K);
         if (l == 0) {
           if (sel_idx) sel_idx[static_cast<long long>(n) * B + p + 1] = k;
           sel_tok[static_cast<long long>(n) * B + p + 1] = idn[(p + 1) * K + k];
