@@ -33,7 +33,7 @@ int check_dims(const dcoco_dims* d, bool need_widths) {
   if (d->dtype != DCOCO_F32 && d->dtype != DCOCO_BF16) return DCOCO_ERR_INVALID_ARG;
   if (d->n_blocks < 1 || d->B < 1 || d->K < 1 || d->V < 1 || d->K > d->V) return DCOCO_ERR_INVALID_ARG;
   if (!(d->ln_eps > 0.0f) || !std::isfinite(d->ln_eps)) return DCOCO_ERR_INVALID_ARG;
-  if (d->K > 64) return DCOCO_ERR_UNSUPPORTED;
+  if (d->K > 64 || d->V > (1 << 30)) return DCOCO_ERR_UNSUPPORTED;
   const long long rows = static_cast<long long>(d->n_blocks) * d->B;
   if (rows * d->K > (1ll << 30) || rows > 65535) return DCOCO_ERR_UNSUPPORTED;
   if (need_widths) {
@@ -237,6 +237,7 @@ hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z,
 
 int check_ws(void* ws, size_t* bytes, size_t need) {
   if (!bytes) return DCOCO_ERR_INVALID_ARG;
+  need = need < kAlign ? kAlign : need;   // never 0: NULL always means "size query"
   if (!ws) {
     *bytes = need;
     return 1;   // size query answered

@@ -304,93 +304,127 @@ __device__ __forceinline__ uint32_t pk_sub_sat(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t canon_half(uint32_t k) { return (k > 0xff80u || k < 0x0080u) ? 0u : k; }
 
-constexpr int kWords = kVecPerLane * 4;   // 32 words = 64 bf16 per lane
-
-// exact key of one bf16 pattern (NaN -> 0), elements past the row -> none
+// Exact key of one bf16 pattern (NaN -> 0).
 __device__ __forceinline__ uint32_t exact_key16(uint32_t bits) {
   return canon_half((pack_keys(bits) & 0xffffu));
 }
 
-// Exact top-K of one wave segment, re-reading it from memory (cached): used
-// when the segment holds a NaN or too many keys tie near the threshold.
-// Writes min(K, #elements) composites to out[0..K), zero padded.
-__device__ __attribute__((noinline)) void exact_segment_bf16(const uint16_t* rowp, int V, int K, int seg0,
-                                                             int* cnt_slot, uint64_t* out) {
+// Final step of a row: top-K of src[0..count) (count <= 64 * Q), sorted by
+// composite (value desc, id asc); writes ids and the original logit values.
+// Executed by one wave.
+template <int Q, int KEYBITS, typename T>
+__device__ void finish_row(const uint64_t* src, int count, int K, uint64_t* s_fin, const T* rowp,
+                           int32_t* ids_row, float* vals_row) {
   const int l = lane_id();
+  select_to<Q, KEYBITS>(src, count, K, s_fin);
+  __builtin_amdgcn_wave_barrier();
+  if (l < K) {
+    const uint64_t mine = s_fin[l];
+    int rank = 0;
+    for (int j = 0; j < K; ++j) rank += s_fin[j] > mine ? 1 : 0;
+    const uint32_t id = 0xffffffffu - comp_inv(mine);
+    ids_row[rank] = static_cast<int32_t>(id);
+    if constexpr (std::is_same<T, uint16_t>::value) vals_row[rank] = bf16_to_f32(rowp[id]);
+    else vals_row[rank] = Elem<T>::to_f32(rowp[id]);
+  }
+}
+
+// Exact top-K of the elements a wave owns (segments first_seg + r * seg_stride,
+// r < rounds, each 64 lanes x nv vectors of 8), re-read from memory: the path
+// for a wave that met a NaN or too many near-threshold keys.  Writes
+// min(K, #elements) composites to out[0..K), zero padded.
+__device__ __attribute__((noinline)) void exact_wave_bf16(const uint16_t* rowp, int V, int K, int first_seg,
+                                                          int seg_stride, int rounds, int nv, int* cnt_slot,
+                                                          uint64_t* out) {
+  const int l = lane_id();
+  const int seg_len = kWave * nv * 8;
   auto key_at = [&](int e) -> int { return e < V ? static_cast<int>(exact_key16(rowp[e])) : -1; };
   uint32_t tk = 0;
   for (int bit = 15; bit >= 0; --bit) {
     const int cand = static_cast<int>(tk | (1u << bit));
     int cnt = 0;
-#pragma unroll 1
-    for (int i = 0; i < kVecPerLane; ++i)
-#pragma unroll 1
-      for (int j = 0; j < 8; ++j) cnt += key_at(seg0 + (i * kWave + l) * 8 + j) >= cand ? 1 : 0;
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int seg0 = (first_seg + rd * seg_stride) * seg_len;
+      for (int i = 0; i < nv; ++i)
+        for (int j = 0; j < 8; ++j) cnt += key_at(seg0 + (i * kWave + l) * 8 + j) >= cand ? 1 : 0;
+    }
     if (wave_sum_i(cnt) >= K) tk = static_cast<uint32_t>(cand);
   }
   if (l == 0) *cnt_slot = 0;
   __builtin_amdgcn_wave_barrier();
-#pragma unroll 1
-  for (int i = 0; i < kVecPerLane; ++i)
-#pragma unroll 1
-    for (int j = 0; j < 8; ++j) {
-      const int e = seg0 + (i * kWave + l) * 8 + j;
-      const int k = key_at(e);
-      if (k > static_cast<int>(tk)) {
-        const int pos = atomicAdd(cnt_slot, 1);
-        out[pos] = make_comp(static_cast<uint32_t>(k), static_cast<uint32_t>(e));
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int seg0 = (first_seg + rd * seg_stride) * seg_len;
+    for (int i = 0; i < nv; ++i)
+      for (int j = 0; j < 8; ++j) {
+        const int e = seg0 + (i * kWave + l) * 8 + j;
+        const int k = key_at(e);
+        if (k > static_cast<int>(tk)) {
+          const int pos = atomicAdd(cnt_slot, 1);
+          out[pos] = make_comp(static_cast<uint32_t>(k), static_cast<uint32_t>(e));
+        }
       }
-    }
+  }
   __builtin_amdgcn_wave_barrier();
   int have = *cnt_slot;
-  // keys equal to tk, lowest ids first (vector by vector, lane order, then j)
-#pragma unroll 1
-  for (int i = 0; i < kVecPerLane; ++i) {
-    int mine = 0;
-#pragma unroll 1
-    for (int j = 0; j < 8; ++j) mine += key_at(seg0 + (i * kWave + l) * 8 + j) == static_cast<int>(tk) ? 1 : 0;
-    const int incl = wave_prefix_incl(mine);
-    int pos = have + incl - mine;
-#pragma unroll 1
-    for (int j = 0; j < 8; ++j) {
-      const int e = seg0 + (i * kWave + l) * 8 + j;
-      if (key_at(e) == static_cast<int>(tk)) {
-        if (pos < K) out[pos] = make_comp(tk, static_cast<uint32_t>(e));
-        ++pos;
+  // keys equal to tk, lowest ids first: segments, vectors, lanes, then j
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int seg0 = (first_seg + rd * seg_stride) * seg_len;
+    for (int i = 0; i < nv; ++i) {
+      int mine = 0;
+      for (int j = 0; j < 8; ++j) mine += key_at(seg0 + (i * kWave + l) * 8 + j) == static_cast<int>(tk) ? 1 : 0;
+      const int incl = wave_prefix_incl(mine);
+      int pos = have + incl - mine;
+      for (int j = 0; j < 8; ++j) {
+        const int e = seg0 + (i * kWave + l) * 8 + j;
+        if (key_at(e) == static_cast<int>(tk)) {
+          if (pos < K) out[pos] = make_comp(tk, static_cast<uint32_t>(e));
+          ++pos;
+        }
       }
+      have += __shfl(incl, kWave - 1, kWave);
     }
-    have += __shfl(incl, kWave - 1, kWave);
   }
   for (int i = min(have, K) + l; i < K; i += kWave) out[i] = 0ull;
 }
 
-template <int G, bool kVecLoad>
-__global__ void __launch_bounds__(kTopkThreads)
-topk_bf16_partial_kernel(const uint16_t* __restrict__ logits, int V, int K, int nchunks,
-                         uint64_t* __restrict__ partial) {
-  constexpr int kSeg = kWave * kWords * 2;
-  constexpr int kChunk = kTopkWaves * kSeg;
-  const int chunk = blockIdx.x;
-  const int row = blockIdx.y;
+// One workgroup (8 waves) per bf16 row; no cross-workgroup merge.  Wave w
+// scans segments w, w+8, ... of 64 lanes x NV 16-byte vectors (8 bf16 each),
+// all NV loads of a segment in flight at once, and keeps a running lower bound
+// on its own K-th largest key: the K-th largest of a segment's 64*G group
+// maxima.  Keys at or above it (about K + a few per segment on random rows)
+// are appended to LDS.  Each wave then selects its top-K exactly and wave 0
+// merges the 8 lists, sorts the K winners and writes ids and values.
+constexpr int kRowWaves = 8;
+
+template <int NV, int G, bool kVecLoad>
+__global__ void __launch_bounds__(kRowWaves * kWave)
+topk_bf16_row_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
+                     float* __restrict__ vals) {
+  constexpr int kWordsL = NV * 4;           // 32-bit words (bf16 pairs) per lane
+  constexpr int kSegLen = kWave * NV * 8;
+  static_assert(kWordsL <= 128, "candidate bitmask holds 128 words");
+  const int row = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int l = lane_id();
   const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
 
-  __shared__ uint64_t s_cand[kTopkWaves][kCandCap];
-  __shared__ uint64_t s_best[kTopkWaves * 64];
-  __shared__ uint64_t s_out[64];
-  __shared__ int s_cnt[kTopkWaves];
+  __shared__ uint64_t s_cand[kRowWaves][kCandCap];
+  __shared__ uint64_t s_best[kRowWaves * 64];
+  __shared__ uint64_t s_fin[64];
+  __shared__ int s_cnt[kRowWaves];
 
-  const int seg0 = chunk * kChunk + w * kSeg;
   if (l == 0) s_cnt[w] = 0;
-  uint64_t* wave_out = s_best + w * K;
-  // element index of half h of word j of this lane
-  auto elem = [&](int j, int h) { return seg0 + ((j >> 2) * kWave + l) * 8 + (j & 3) * 2 + h; };
-
-  if (seg0 < V) {
-    uint32_t kw[kWords];
+  __builtin_amdgcn_wave_barrier();
+  uint32_t t_run = 0;       // running lower bound on this wave's K-th largest key
+  bool exact = false;
+  int nseg = 0;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int seg0 = (rd * kRowWaves + w) * kSegLen;
+    if (seg0 >= V) break;
+    ++nseg;
+    uint32_t kw[kWordsL];
 #pragma unroll
-    for (int i = 0; i < kVecPerLane; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int e0 = seg0 + (i * kWave + l) * 8;
       if (kVecLoad && e0 + 8 <= V) {
         const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);
@@ -410,9 +444,9 @@ topk_bf16_partial_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
     for (int g = 0; g < G; ++g) gmx[g] = 0u;
     uint32_t mn = 0xffffffffu;
 #pragma unroll
-    for (int j = 0; j < kWords; ++j) {
+    for (int j = 0; j < kWordsL; ++j) {
       kw[j] = pack_keys(kw[j]);
-      const int g = (j * G) / kWords;
+      const int g = (j * G) / kWordsL;
       gmx[g] = pk_max(gmx[g], kw[j]);
       mn = pk_min(mn, kw[j]);
     }
@@ -423,57 +457,76 @@ topk_bf16_partial_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
       top = max(top, gmx[g]);
     }
     const bool lane_nan = top > 0xff80u || min(mn & 0xffffu, mn >> 16) < 0x0080u;
-    const bool wave_nan = ballot(lane_nan) != 0;
-    int count = kCandCap + 1;
+    if (ballot(lane_nan) != 0) {
+      exact = true;
+      break;
+    }
+    // this segment's bound: the K-th largest group maximum (all keys >= 0x0080)
     uint32_t t0 = 0;
-    if (!wave_nan) {
-      // T0 = K-th largest group maximum; every key here is >= 0x0080
-      for (int bit = 15; bit >= 0; --bit) {
-        const uint32_t cand = t0 | (1u << bit);
-        int cnt = 0;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = t0 | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-        for (int g = 0; g < G; ++g) cnt += __popcll(ballot(gmx[g] >= cand));
-        if (cnt >= K) t0 = cand;
+      for (int g = 0; g < G; ++g) cnt += __popcll(ballot(gmx[g] >= cand));
+      if (cnt >= K) t0 = cand;
+    }
+    t_run = max(t_run, t0);
+    const uint32_t thr = (t_run - 1u) * 0x00010001u;
+    // one bit per word holding a key >= t_run (words 0..63 and 64..)
+    uint64_t mlo = 0, mhi = 0;
+#pragma unroll
+    for (int j = 0; j < kWordsL; ++j) {
+      const uint64_t bit = pk_sub_sat(kw[j], thr) != 0u ? 1ull : 0ull;
+      if (j < 64) mlo |= bit << j;
+      else mhi |= bit << (j - 64);
+    }
+    while (mlo | mhi) {
+      int j;
+      if (mlo) {
+        j = __builtin_ctzll(mlo);
+        mlo &= mlo - 1ull;
+      } else {
+        j = 64 + __builtin_ctzll(mhi);
+        mhi &= mhi - 1ull;
       }
-      const uint32_t thr = (t0 - 1u) * 0x00010001u;
-      // words holding a key >= T0 (rare), then append their elements
-      uint32_t mask = 0;
+      const int e = seg0 + ((j >> 2) * kWave + l) * 8 + (j & 3) * 2;
+      if (e >= V) continue;   // padding only
+      const uint32_t lo = rowp[e];
+      const uint32_t hi = e + 1 < V ? rowp[e + 1] : 0xff80u;
+      const uint32_t kk = pack_keys(lo | (hi << 16));
 #pragma unroll
-      for (int j = 0; j < kWords; ++j) mask |= (pk_sub_sat(kw[j], thr) != 0u ? 1u : 0u) << j;
-      while (mask) {
-        const int j = __builtin_ctz(mask);
-        mask &= mask - 1u;
-        const int e = elem(j, 0);
-        if (e >= V) continue;   // padding only
-        const uint32_t lo = rowp[e];
-        const uint32_t hi = e + 1 < V ? rowp[e + 1] : 0xff80u;
-        const uint32_t kk = pack_keys(lo | (hi << 16));
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t k = (kk >> (16 * h)) & 0xffffu;
-          if (k >= t0 && e + h < V) {
-            const int pos = atomicAdd(&s_cnt[w], 1);
-            if (pos < kCandCap) s_cand[w][pos] = make_comp(k, static_cast<uint32_t>(e + h));
-          }
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t k = (kk >> (16 * h)) & 0xffffu;
+        if (k >= t_run && e + h < V) {
+          const int pos = atomicAdd(&s_cnt[w], 1);
+          if (pos < kCandCap) s_cand[w][pos] = make_comp(k, static_cast<uint32_t>(e + h));
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      count = s_cnt[w];
     }
-    if (count <= kCandCap) {
-      select_small<16>(s_cand[w], count, K, wave_out);
-    } else {
-      exact_segment_bf16(rowp, V, K, seg0, s_cnt + w, wave_out);
+    __builtin_amdgcn_wave_barrier();
+    if (s_cnt[w] > kCandCap) {
+      exact = true;
+      break;
     }
-  } else {
+  }
+  uint64_t* wave_out = s_best + w * K;
+  if (nseg == 0) {
     for (int i = l; i < K; i += kWave) wave_out[i] = 0ull;
+  } else if (!exact) {
+    select_small<16>(s_cand[w], s_cnt[w], K, wave_out);
+  } else {
+    int segs = 0;
+    for (int rd = 0; rd < rounds; ++rd) segs += (rd * kRowWaves + w) * kSegLen < V ? 1 : 0;
+    exact_wave_bf16(rowp, V, K, w, kRowWaves, segs, NV, &s_cnt[w], wave_out);
   }
   __syncthreads();
   if (w == 0) {
-    uint64_t* dst = partial + (static_cast<size_t>(row) * nchunks + chunk) * K;
-    select_small<16>(s_best, kTopkWaves * K, K, s_out);
-    __builtin_amdgcn_wave_barrier();
-    for (int i = l; i < K; i += kWave) dst[i] = s_out[i];
+    const int count = kRowWaves * K;
+    int32_t* ids_row = ids + static_cast<size_t>(row) * K;
+    float* vals_row = vals + static_cast<size_t>(row) * K;
+    if (count <= 2 * kWave) finish_row<2, 16>(s_best, count, K, s_fin, rowp, ids_row, vals_row);
+    else if (count <= 4 * kWave) finish_row<4, 16>(s_best, count, K, s_fin, rowp, ids_row, vals_row);
+    else finish_row<8, 16>(s_best, count, K, s_fin, rowp, ids_row, vals_row);
   }
 }
 
@@ -532,14 +585,30 @@ hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* p
   if constexpr (std::is_same<T, bf16>::value) {
     const uint16_t* lb = reinterpret_cast<const uint16_t*>(logits);
     const int G = K <= 16 ? 1 : (K <= 32 ? 2 : 4);
-#define DCOCO_TOPK16(GG, VV) \
-  hipLaunchKernelGGL((topk_bf16_partial_kernel<GG, VV>), g1, dim3(kTopkThreads), 0, st, lb, V, K, nch, partial)
-    if (vec) {
-      if (G == 1) DCOCO_TOPK16(1, true); else if (G == 2) DCOCO_TOPK16(2, true); else DCOCO_TOPK16(4, true);
-    } else {
-      if (G == 1) DCOCO_TOPK16(1, false); else if (G == 2) DCOCO_TOPK16(2, false); else DCOCO_TOPK16(4, false);
-    }
-#undef DCOCO_TOPK16
+    // vectors per lane: the fewest rounds of 8 waves x 20 vectors, then the
+    // smallest vector count (from 4, 8, 12, 16, 20) that covers the row
+    const int per_round_max = kRowWaves * kWave * 20 * 8;
+    const int rounds = (V + per_round_max - 1) / per_round_max;
+    const int need = (V + rounds * kRowWaves * kWave * 8 - 1) / (rounds * kRowWaves * kWave * 8);
+    const int nv = need <= 4 ? 4 : (need <= 8 ? 8 : (need <= 12 ? 12 : (need <= 16 ? 16 : 20)));
+#define DCOCO_ROW(NVV, GG, VV)                                                                       \
+  hipLaunchKernelGGL((topk_bf16_row_kernel<NVV, GG, VV>), dim3(rows), dim3(kRowWaves * kWave), 0, st, lb, V, \
+                     K, rounds, ids, vals)
+#define DCOCO_ROW_G(NVV, VV)                          \
+  if (G == 1) DCOCO_ROW(NVV, 1, VV);                  \
+  else if (G == 2) DCOCO_ROW(NVV, 2, VV);             \
+  else DCOCO_ROW(NVV, 4, VV)
+#define DCOCO_ROW_NV(VV)                              \
+  if (nv == 4) { DCOCO_ROW_G(4, VV); }                \
+  else if (nv == 8) { DCOCO_ROW_G(8, VV); }           \
+  else if (nv == 12) { DCOCO_ROW_G(12, VV); }         \
+  else if (nv == 16) { DCOCO_ROW_G(16, VV); }         \
+  else { DCOCO_ROW_G(20, VV); }
+    if (vec) { DCOCO_ROW_NV(true) } else { DCOCO_ROW_NV(false) }
+#undef DCOCO_ROW_NV
+#undef DCOCO_ROW_G
+#undef DCOCO_ROW
+    return hipGetLastError();
   } else {
     if (vec)
       hipLaunchKernelGGL((topk_partial_kernel<T, true>), g1, dim3(kTopkThreads), 0, st, lg, V, K, nch, partial);
@@ -564,13 +633,13 @@ hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* p
 }  // namespace
 
 size_t topk_workspace_bytes(int dtype, int rows, int V, int K) {
-  const int nch = dtype == kDtypeBf16 ? topk_nchunks<bf16>(V) : topk_nchunks<float>(V);
-  return static_cast<size_t>(rows) * nch * K * sizeof(uint64_t);
+  if (dtype == kDtypeBf16) return 0;   // one workgroup per row, no partials
+  return static_cast<size_t>(rows) * topk_nchunks<float>(V) * K * sizeof(uint64_t);
 }
 
 bool topk_supported(int dtype, int V, int K) {
-  const int nch = dtype == kDtypeBf16 ? topk_nchunks<bf16>(V) : topk_nchunks<float>(V);
-  return static_cast<long long>(nch) * K <= 32 * kWave;
+  if (dtype == kDtypeBf16) return true;
+  return static_cast<long long>(topk_nchunks<float>(V)) * K <= 32 * kWave;
 }
 
 hipError_t launch_topk(int dtype, const void* logits, int rows, int V, int K, void* partial,

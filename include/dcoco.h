@@ -36,7 +36,8 @@
  *     stores the number of bytes it needs in *workspace_bytes and returns
  *     DCOCO_OK without launching anything.  Otherwise *workspace_bytes must
  *     hold the size of the caller's buffer (256-byte aligned), which must be
- *     at least that number.  The workspace holds no state between calls.
+ *     at least that number (never less than 256).  The workspace holds no
+ *     state between calls.
  *   - Arguments are checked before anything is launched; a failed check
  *     returns a negative dcoco_status and enqueues nothing.  No C++ exception
  *     crosses this interface.  A launch failure returns DCOCO_ERR_HIP.

@@ -121,7 +121,11 @@ def test_workspace_and_pointer_checks(lib):
     assert lib.dcoco_select(ctypes.byref(cd), fake, fake, fake, None, None, None) == -1
 
 
-def test_unsupported_vocab_for_topk(lib):
-    # the row merge holds at most 2048 chunk candidates
-    rc, _ = _query_topk(lib, _dims(K=64, V=600000))
+def test_vocab_limits_for_topk(lib):
+    # bf16 rows: one workgroup per row, any vocabulary up to 2^30
+    rc, n = _query_topk(lib, _dims(K=64, V=600000))
+    assert rc == 0 and n >= 256
+    assert _query_topk(lib, _dims(K=64, V=(1 << 30) + 1))[0] == -2
+    # fp32 rows: the chunk merge holds at most 2048 candidates
+    rc, _ = _query_topk(lib, _dims(K=64, V=600000, dtype="f32"))
     assert rc == -2

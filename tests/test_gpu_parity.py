@@ -106,7 +106,7 @@ def _special_rows(V, dtype, seed):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("V,K", [(5003, 1), (5003, 7), (40000, 16), (40000, 64), (151936, 16), (70, 64)])
+@pytest.mark.parametrize("V,K", [(5003, 1), (5003, 7), (40000, 16), (40000, 64), (151936, 16), (70, 64), (200000, 32), (262144, 64)])
 def test_topk_ties_and_special_values(dtype, V, K):
     import draft_block_contextual_amd as dc
     import torch
