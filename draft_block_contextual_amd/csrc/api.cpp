@@ -7,6 +7,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -105,16 +107,17 @@ RepLayout carve_rep(Carve& c, const dcoco_dims* d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DCOCO_OK : DCOCO_ERR_HIP; }
 
-// representation stage: g, s, b, z (see dcoco_represent)
-hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
-                         const int32_t* ids, void* z, float* s, const RepLayout& L, hipStream_t st) {
+// ---- representation stage, in parts that can run on two streams
+
+// slot side: [P_h; W_L; W_R] h (split-K partials), s_p (+ its bf16 split when
+// s3 is given), gf = W_fg LN(P_h h)
+hipError_t slot_part(const dcoco_dims* d, const dcoco_weights* w, const void* h, float* s, void* s3,
+                     const RepLayout& L, hipStream_t st) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int R = d->n_blocks * d->B;
-  const int RK = R * d->K;
   const int r = d->d_proj, rs = d->d_pair, rz = d->d_z, dh = d->d_hidden;
   const int ns = r + 2 * rs;
   hipError_t e;
-  // slot projections: [P_h; W_L; W_R] h, fp32 partial sums
   {
     GemmProblem q{};
     q.M = R; q.N = ns; q.Kd = dh;
@@ -126,54 +129,67 @@ hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void
     q.split = L.split_slot; q.out_f32 = L.Y; q.ldo = ns; q.out = nullptr;
     if ((e = launch_gemm(q, st)) != hipSuccess) return e;
   }
-  if ((e = launch_pair_state(L.Y, L.split_slot, d->n_blocks, d->B, ns, r, r + rs, rs, s, st)) != hipSuccess)
+  if ((e = launch_pair_state(L.Y, L.split_slot, d->n_blocks, d->B, ns, r, r + rs, rs, s, s3, st)) != hipSuccess)
     return e;
-  const bool fused = dt == kDtypeBf16;
-  // gf = W_fg g with g = LN(P_h h) (the slot half of the fusion), once per slot
-  if (fused) {
-    if ((e = launch_ln_gemm(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, nullptr,
-                            nullptr, 1, st)) != hipSuccess)
-      return e;
-  } else {
-    if ((e = launch_ln_rows(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
-    GemmProblem q{};
-    q.M = R; q.N = rz; q.Kd = r;
-    q.A = L.g; q.lda = r; q.a_dtype = dt;
-    q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = r; q.seg_end[0] = rz;
-    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = rz;
-    q.w_dtype = dt;
-    q.split = 1; q.out_f32 = L.gf; q.ldo = rz; q.out = nullptr;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
-  // candidate projections P_e E[c], gathered rows
-  {
-    GemmProblem q{};
-    q.M = RK; q.N = r; q.Kd = d->d_embed;
-    q.A = E; q.lda = d->d_embed; q.a_rows = ids; q.a_rows_max = d->V - 1; q.a_dtype = dt;
-    q.w[0] = w->P_e; q.ldw[0] = d->d_embed; q.col0[0] = 0; q.seg_end[0] = r;
-    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = r;
-    q.w_dtype = dt;
-    q.split = L.split_cand; q.out_f32 = L.U; q.ldo = r; q.out = nullptr;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
-  // z = W_fb b + gf[slot] with b = LN(P_e E[c])
-  if (fused) {
-    if ((e = launch_ln_gemm(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, w->W_f, 2ll * r, 0, rz, nullptr, z, L.gf,
-                            d->K, st)) != hipSuccess)
-      return e;
-  } else {
-    if ((e = launch_ln_rows(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, L.b, dt, st)) != hipSuccess) return e;
-    GemmProblem q{};
-    q.M = RK; q.N = rz; q.Kd = r;
-    q.A = L.b; q.lda = r; q.a_dtype = dt;
-    q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = 0; q.seg_end[0] = rz;
-    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = rz;
-    q.w_dtype = dt;
-    q.split = 1; q.out = z; q.out_dtype = dt; q.ldo = rz;
-    q.row_bias = L.gf; q.row_bias_div = d->K; q.col_bias = nullptr;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (dt == kDtypeBf16)
+    return launch_ln_gemm(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, nullptr,
+                          nullptr, 1, st);
+  if ((e = launch_ln_rows(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
+  GemmProblem q{};
+  q.M = R; q.N = rz; q.Kd = r;
+  q.A = L.g; q.lda = r; q.a_dtype = dt;
+  q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = r; q.seg_end[0] = rz;
+  q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = rz;
+  q.w_dtype = dt;
+  q.split = 1; q.out_f32 = L.gf; q.ldo = rz; q.out = nullptr;
+  return launch_gemm(q, st);
+}
+
+// candidate side, first half: P_e E[c] over gathered rows (split-K partials)
+hipError_t cand_gemm(const dcoco_dims* d, const dcoco_weights* w, const void* E, const int32_t* ids,
+                     const RepLayout& L, hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int RK = d->n_blocks * d->B * d->K;
+  const int r = d->d_proj;
+  GemmProblem q{};
+  q.M = RK; q.N = r; q.Kd = d->d_embed;
+  q.A = E; q.lda = d->d_embed; q.a_rows = ids; q.a_rows_max = d->V - 1; q.a_dtype = dt;
+  q.w[0] = w->P_e; q.ldw[0] = d->d_embed; q.col0[0] = 0; q.seg_end[0] = r;
+  q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = r;
+  q.w_dtype = dt;
+  q.split = L.split_cand; q.out_f32 = L.U; q.ldo = r; q.out = nullptr;
+  return launch_gemm(q, st);
+}
+
+// candidate side, second half (needs gf): z = W_fb LN(P_e E[c]) + gf[slot]
+hipError_t cand_finish(const dcoco_dims* d, const dcoco_weights* w, void* z, const RepLayout& L,
+                       hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int RK = d->n_blocks * d->B * d->K;
+  const int r = d->d_proj, rz = d->d_z;
+  if (dt == kDtypeBf16)
+    return launch_ln_gemm(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, w->W_f, 2ll * r, 0, rz, nullptr, z, L.gf,
+                          d->K, st);
+  hipError_t e;
+  if ((e = launch_ln_rows(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, L.b, dt, st)) != hipSuccess) return e;
+  GemmProblem q{};
+  q.M = RK; q.N = rz; q.Kd = r;
+  q.A = L.b; q.lda = r; q.a_dtype = dt;
+  q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = 0; q.seg_end[0] = rz;
+  q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = rz;
+  q.w_dtype = dt;
+  q.split = 1; q.out = z; q.out_dtype = dt; q.ldo = rz;
+  q.row_bias = L.gf; q.row_bias_div = d->K; q.col_bias = nullptr;
+  return launch_gemm(q, st);
+}
+
+// representation stage on one stream (see dcoco_represent)
+hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
+                         const int32_t* ids, void* z, float* s, const RepLayout& L, hipStream_t st) {
+  hipError_t e;
+  if ((e = slot_part(d, w, h, s, nullptr, L, st)) != hipSuccess) return e;
+  if ((e = cand_gemm(d, w, E, ids, L, st)) != hipSuccess) return e;
+  return cand_finish(d, w, z, L, st);
 }
 
 // scoring stage buffers
@@ -194,29 +210,39 @@ ScoreLayout carve_score(Carve& c, const dcoco_dims* d) {
   return L;
 }
 
-// scoring stage: C_p parts = W1s s_p (s split into bf16 hi/mid/lo rows on the
-// bf16 path), AB = z [W1a; W1b]^T, then the grid
-hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
-                     const float* cl, float* S, const ScoreLayout& L, hipStream_t st) {
+// pair term: C_p parts = W1s s_p (bf16 path: s split into hi/mid/lo rows; the
+// split is made here unless s3_ready)
+hipError_t pair_term(const dcoco_dims* d, const dcoco_weights* w, const float* s, const ScoreLayout& L,
+                     bool s3_ready, hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int P = d->n_blocks * (d->B - 1);
+  if (P == 0) return hipSuccess;
+  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
+  const int nq = dt == kDtypeBf16 ? 3 : 1;
+  hipError_t e;
+  if (dt == kDtypeBf16 && !s3_ready &&
+      (e = launch_split3(s, static_cast<long long>(P) * rs, L.s3, st)) != hipSuccess)
+    return e;
+  GemmProblem q{};
+  q.M = nq * P; q.N = H; q.Kd = rs;
+  q.A = dt == kDtypeBf16 ? L.s3 : static_cast<const void*>(s); q.lda = rs; q.a_dtype = dt;
+  q.w[0] = w->W1; q.ldw[0] = 2ll * rz + rs; q.col0[0] = 2 * rz; q.seg_end[0] = H;
+  q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = H;
+  q.w_dtype = dt;
+  q.split = 1; q.out_f32 = L.C; q.ldo = H; q.out = nullptr;
+  return launch_gemm(q, st);
+}
+
+// AB = z [W1a; W1b]^T, then the grid (needs the pair term)
+hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* cl, float* S,
+                      const ScoreLayout& L, hipStream_t st) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int P = d->n_blocks * (d->B - 1);
   if (P == 0) return hipSuccess;
   const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
   const int RK = d->n_blocks * d->B * d->K;
   const long long ldw1 = 2ll * rz + rs;
-  const int nq = dt == kDtypeBf16 ? 3 : 1;
   hipError_t e;
-  if (dt == kDtypeBf16 && (e = launch_split3(s, static_cast<long long>(P) * rs, L.s3, st)) != hipSuccess) return e;
-  {
-    GemmProblem q{};
-    q.M = nq * P; q.N = H; q.Kd = rs;
-    q.A = dt == kDtypeBf16 ? L.s3 : static_cast<const void*>(s); q.lda = rs; q.a_dtype = dt;
-    q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 2 * rz; q.seg_end[0] = H;
-    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = H;
-    q.w_dtype = dt;
-    q.split = 1; q.out_f32 = L.C; q.ldo = H; q.out = nullptr;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
   {
     GemmProblem q{};
     q.M = RK; q.N = 2 * H; q.Kd = rz;
@@ -230,9 +256,61 @@ hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z,
   }
   GridProblem g{};
   g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.H = H; g.dtype = dt;
-  g.AB = L.AB; g.C = L.C; g.nq = nq; g.b1 = w->b1; g.w2 = w->w2; g.b2 = w->b2;
+  g.AB = L.AB; g.C = L.C; g.nq = dt == kDtypeBf16 ? 3 : 1; g.b1 = w->b1; g.w2 = w->w2; g.b2 = w->b2;
   g.cand_logits = cl; g.S = S;
   return launch_grid(g, st);
+}
+
+hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
+                     const float* cl, float* S, const ScoreLayout& L, hipStream_t st) {
+  hipError_t e;
+  if ((e = pair_term(d, w, s, L, false, st)) != hipSuccess) return e;
+  return score_tail(d, w, z, cl, S, L, st);
+}
+
+// ---- a second stream per device for the slot side of dcoco_correct_block
+// (default priority), joined to the caller's stream with events
+constexpr int kEventRing = 32;
+struct SideCtx {
+  bool tried = false;
+  bool ok = false;
+  hipStream_t stream = nullptr;
+  hipEvent_t ev[kEventRing][2];
+  unsigned next = 0;
+};
+std::mutex g_side_mu;
+SideCtx g_side[64];
+
+bool single_stream_forced() {
+  static const bool forced = [] {
+    const char* v = std::getenv("DCOCO_SINGLE_STREAM");
+    return v && v[0] == '1';
+  }();
+  return forced;
+}
+
+// a side stream and a (fork, join) event pair for this call; false: run on
+// the caller's stream only
+bool side_stream(hipStream_t* side, hipEvent_t* fork, hipEvent_t* join) {
+  if (single_stream_forced()) return false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideCtx& c = g_side[dev];
+  if (!c.tried) {
+    c.tried = true;
+    bool ok = hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; ok && i < kEventRing; ++i)
+      ok = hipEventCreateWithFlags(&c.ev[i][0], hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&c.ev[i][1], hipEventDisableTiming) == hipSuccess;
+    c.ok = ok;
+  }
+  if (!c.ok) return false;
+  const unsigned i = c.next++ % kEventRing;
+  *side = c.stream;
+  *fork = c.ev[i][0];
+  *join = c.ev[i][1];
+  return true;
 }
 
 int check_ws(void* ws, size_t* bytes, size_t need) {
@@ -364,9 +442,26 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (cand_logits_out) cl = cand_logits_out;
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
-  if (e == hipSuccess) e = run_represent(d, w, h, E, ids, z, s, L, st);
-  if (e == hipSuccess) e = run_score(d, w, z, s, cl, S, SL, st);
+  // The slot side (slot projections, pair states, gf, the pair term) needs
+  // only h; it runs on a second stream while top-K and the gathered
+  // projection run on the caller's stream, and joins before z.
+  const bool bf = dt == kDtypeBf16;
+  hipStream_t side = st;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  const bool two = side_stream(&side, &ev_fork, &ev_join);
+  hipError_t e = hipSuccess;
+  if (two) {
+    e = hipEventRecord(ev_fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+  }
+  if (e == hipSuccess) e = slot_part(d, w, h, s, bf ? SL.s3 : nullptr, L, side);
+  if (e == hipSuccess) e = pair_term(d, w, s, SL, bf, side);
+  if (two && e == hipSuccess) e = hipEventRecord(ev_join, side);
+  if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
+  if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
+  if (two && e == hipSuccess) e = hipStreamWaitEvent(st, ev_join, 0);
+  if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
+  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st);
   if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
   return hip_status(e);
 }

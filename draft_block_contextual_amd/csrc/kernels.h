@@ -59,8 +59,9 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
                           const float* row_bias, int row_div, hipStream_t st);
 
 // s[n, p, :] = sum_s Y[s][n*B+p][cl : cl+rs] + sum_s Y[s][n*B+p+1][cr : cr+rs]
+// s3 (optional): the same values as three bf16 rows hi, mid, lo (s3[q * n + i])
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
-                             int rs, float* s, hipStream_t st);
+                             int rs, float* s, void* s3, hipStream_t st);
 
 // ----------------------------------------------------- scoring and walk
 struct GridProblem {

@@ -52,7 +52,7 @@ ln_rows_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0,
 
 __global__ void __launch_bounds__(256)
 pair_state_kernel(const float* __restrict__ Y, int split, int N, int B, int ldy, int cl, int cr,
-                  int rs, float* __restrict__ s) {
+                  int rs, float* __restrict__ s, uint16_t* __restrict__ s3) {
   const long long total = static_cast<long long>(N) * (B - 1) * rs;
   const long long M = static_cast<long long>(N) * B;
   for (long long t = blockIdx.x * 256ll + threadIdx.x; t < total; t += 256ll * gridDim.x) {
@@ -66,7 +66,17 @@ pair_state_kernel(const float* __restrict__ Y, int split, int N, int B, int ldy,
       left += Y[(q * M + rl) * ldy + cl + j];
       right += Y[(q * M + rl + 1) * ldy + cr + j];
     }
-    s[t] = left + right;
+    const float x = left + right;
+    s[t] = x;
+    if (s3) {
+      // x = hi + mid + lo exactly (three bf16 parts of 8 significand bits)
+      const uint16_t hi = f32_to_bf16(x);
+      const float r1 = x - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16(r1);
+      s3[t] = hi;
+      s3[total + t] = mid;
+      s3[2 * total + t] = f32_to_bf16(r1 - bf16_to_f32(mid));
+    }
   }
 }
 
@@ -287,12 +297,13 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
 }
 
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
-                             int rs, float* s, hipStream_t st) {
+                             int rs, float* s, void* s3, hipStream_t st) {
   const long long total = static_cast<long long>(N) * (B - 1) * rs;
   if (total <= 0) return hipSuccess;
   const long long blocks = (total + 255) / 256;
   dim3 grid(static_cast<unsigned>(blocks < 65535 ? blocks : 65535));
-  hipLaunchKernelGGL(pair_state_kernel, grid, dim3(256), 0, st, Y, split, N, B, ldy, cl, cr, rs, s);
+  hipLaunchKernelGGL(pair_state_kernel, grid, dim3(256), 0, st, Y, split, N, B, ldy, cl, cr, rs, s,
+                     static_cast<uint16_t*>(s3));
   return hipGetLastError();
 }
 
