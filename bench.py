@@ -18,8 +18,10 @@ kernel and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,6 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2)
     ap.add_argument("--sweep", action="store_true", help="also time 4/8/16 streams")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for scaling HBM counters)")
+    ap.add_argument("--null-stream", action="store_true",
+                    help="launch on the null stream instead of a stream of our own")
     return ap.parse_args()
 
 
@@ -67,6 +73,45 @@ def algorithmic_work(D):
     }
 
 
+def copy_calibration():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+    factor between what those counters read and the bytes actually moved."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+
+
+def source_digest(paths):
+    """Digest of kernel sources; a stored counter figure is used only while it matches."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, digest):
+    """HBM bytes per launch read from a committed counter summary, or None when
+    the summary is missing or was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"^- (\w+): (\S+)$", line.strip())
+        if m:
+            vals[m.group(1)] = m.group(2)
+    if vals.get("source_digest") != digest or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -76,6 +121,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import draft_block_contextual_amd as dc
     import synth
 
@@ -111,7 +159,8 @@ def main():
     N, B, K = D.n_blocks, D.B, D.K
     sel_tok = torch.empty((N, B), dtype=torch.int32, device=dev)
     ws = torch.empty(dc.correct_block_workspace_bytes(dims, w), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    # a stream of our own (default priority), as a serving loop would use
+    stream = torch.cuda.current_stream() if args.null_stream else torch.cuda.Stream()
     print("# inputs resident; warming up", file=sys.stderr, flush=True)
 
     def step(i):
@@ -167,26 +216,22 @@ def main():
     print(f"# stage us: {stage_us}", file=sys.stderr, flush=True)
 
     work = algorithmic_work(D)
-    # dominant stage and its roofline
-    topk_gbs = work["logit_bytes"] / (stage_us["topk"] * 1e-6) / 1e9
-    grid_rate = work["grid_elems"] * 6 / (stage_us["score"] * 1e-6)
-    dominant = max(stage_us, key=stage_us.get)
-    if dominant == "topk":
-        roof = {"bound": "hbm", "kernel": "topk (partial scan + row merge)", "achieved": round(topk_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(topk_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": work["logit_bytes"],
-                "launch_us": round(stage_us["topk"], 2)}
-    elif dominant == "represent":
-        tf = work["mfma_flops"] / (stage_us["represent"] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": "represent (projection GEMMs)", "achieved": round(tf, 1),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "launch_us": round(stage_us["represent"], 2)}
-    else:
-        peak = VALU_LANE_OPS / 1e12
-        ach = grid_rate / 1e12
-        roof = {"bound": "alu", "kernel": "score (transition grid)", "achieved": round(ach, 2),
-                "peak": round(peak, 2), "unit": "Tlane-op/s", "frac": round(ach / peak, 4), "traffic": None,
-                "launch_us": round(stage_us["score"], 2)}
+    # Dominant kernel: top-K, one launch per dcoco_topk call, so the events
+    # around that call time exactly that kernel.  It is bound by reading the
+    # logits once from HBM.
+    kname = "topk_bf16_row_kernel" if dt == "bf16" else "topk_partial_kernel+topk_merge_kernel"
+    topk_us = stage_us["topk"]
+    ach = work["logit_bytes"] / (topk_us * 1e-6) / 1e9
+    digest = source_digest(["draft_block_contextual_amd/csrc/topk.hip", "draft_block_contextual_amd/csrc/common.h"])
+    traffic = stored_traffic(f"topk_{cfg.name}", digest)
+    roof = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic / (topk_us * 1e-6) / 1e9, 1),
+            "traffic_bytes_per_launch": traffic,
+            "algorithmic_bytes_per_launch": work["logit_bytes"], "launch_us": round(topk_us, 2),
+            "source_digest": digest}
+    # a grid element issues fma, rcp (quarter rate: 4 slots), add, fma
+    grid_rate = work["grid_elems"] * 7 / (stage_us["score"] * 1e-6)
 
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -223,9 +268,9 @@ def main():
                    "V": D.V, "embed": D.e, "proj": D.r, "mlp_hidden": D.H},
         "transitions_per_s": round(work["transitions"] * args.steps / (gpu_ms / 1e3), 1),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "hbm_frac_topk": round(topk_gbs / HBM_PEAK_GBS, 4),
         "mfma_frac_represent": round(work["mfma_flops"] / (stage_us["represent"] * 1e-6) / 1e12
                                      / MFMA_BF16_PEAK_TFLOPS, 4),
+        "alu_frac_score": round(grid_rate / VALU_LANE_OPS, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

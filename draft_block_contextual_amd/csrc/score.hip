@@ -245,6 +245,7 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
 }
 
 constexpr int kWalkLds = 8192;   // floats of scores staged per batch
+constexpr int kWalkIds = 1088;   // candidate ids staged per batch: (16 + 1) rows of 64
 
 // argmax over lanes 0..K-1 of one wave: the largest order key, the lowest lane
 // among equal keys (lanes >= K carry key 0, the NaN key, and sit above every
@@ -257,50 +258,75 @@ __device__ __forceinline__ int wave_argmax(float v, bool valid) {
   return __builtin_ctzll(ballot(key == m));
 }
 
+// copy n 4-byte words global -> LDS with 256 threads; each thread issues up to
+// four loads before it waits, so one batch costs about one memory latency
+template <typename W, typename V>
+__device__ __forceinline__ void walk_stage(W* dst, const W* src, int n, int tid) {
+  constexpr int kPer = sizeof(V) / sizeof(W);
+  const int nv = n / kPer;
+  for (int b = tid; b < nv; b += 1024) {
+    V v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (b + 256 * j < nv) v[j] = reinterpret_cast<const V*>(src)[b + 256 * j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (b + 256 * j < nv) reinterpret_cast<V*>(dst)[b + 256 * j] = v[j];
+  }
+  for (int i = nv * kPer + tid; i < n; i += 256) dst[i] = src[i];
+}
+
+// One workgroup per block.  Each batch of pairs stages its scores and the
+// candidate ids of the slots it selects into LDS with one round of loads;
+// wave 0 then walks the batch from LDS only, so the chain of dependent
+// argmaxes never waits on global memory.
 __global__ void __launch_bounds__(256)
 walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int32_t* __restrict__ ids,
             int B, int K, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_tok) {
   __shared__ __align__(16) float sS[kWalkLds];
+  __shared__ __align__(16) int32_t sI[kWalkIds];
+  __shared__ __align__(16) float sC[kWave];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int per = K * K;
-  const int batch = max(1, kWalkLds / per);
   const int Bm1 = B - 1;
+  const int batch = max(1, min(kWalkLds / per, kWalkIds / K - 1));
   const float* Sn = S + static_cast<long long>(n) * Bm1 * per;
-  const float* cln = cl + static_cast<long long>(n) * B * K;
   const int32_t* idn = ids + static_cast<long long>(n) * B * K;
-  int k = 0;
-  if (tid < kWave) {
-    k = wave_argmax(l < K ? cln[l] : 0.f, l < K);
-    if (l == 0) {
-      if (sel_idx) sel_idx[static_cast<long long>(n) * B] = k;
-      sel_tok[static_cast<long long>(n) * B] = idn[k];
-    }
-  }
+  int32_t* si = sel_idx ? sel_idx + static_cast<long long>(n) * B : nullptr;
+  int32_t* stok = sel_tok + static_cast<long long>(n) * B;
   const bool vec = ((reinterpret_cast<uintptr_t>(Sn) & 15) == 0) && (per % 4 == 0);
-  for (int p0 = 0; p0 < Bm1; p0 += batch) {
-    const int cnt = min(batch, Bm1 - p0);
-    const int nval = cnt * per;
-    const float* src = Sn + static_cast<long long>(p0) * per;
+  const bool vec_id = ((reinterpret_cast<uintptr_t>(idn) & 15) == 0) && (K % 4 == 0);
+  int k = 0;
+  for (int p0 = 0;; p0 += batch) {
+    const int cnt = max(0, min(batch, Bm1 - p0));
     __syncthreads();
-    if (vec) {
-      for (int i = tid * 4; i < nval; i += 1024)
-        *reinterpret_cast<float4*>(&sS[i]) = *reinterpret_cast<const float4*>(src + i);
-    } else {
-      for (int i = tid; i < nval; i += 256) sS[i] = src[i];
-    }
+    const float* src = Sn + static_cast<long long>(p0) * per;
+    if (vec) walk_stage<float, float4>(sS, src, cnt * per, tid);
+    else walk_stage<float, float>(sS, src, cnt * per, tid);
+    // ids of slots p0 .. p0 + cnt
+    if (vec_id) walk_stage<int32_t, int4>(sI, idn + static_cast<long long>(p0) * K, (cnt + 1) * K, tid);
+    else walk_stage<int32_t, int32_t>(sI, idn + static_cast<long long>(p0) * K, (cnt + 1) * K, tid);
+    if (p0 == 0 && tid < K) sC[tid] = cl[static_cast<long long>(n) * B * K + tid];
     __syncthreads();
     if (tid < kWave) {
+      if (p0 == 0) {
+        k = wave_argmax(l < K ? sC[l] : 0.f, l < K);
+        if (l == 0) {
+          if (si) si[0] = k;
+          stok[0] = sI[k];
+        }
+      }
       for (int q = 0; q < cnt; ++q) {
-        const int p = p0 + q;
         k = wave_argmax(l < K ? sS[q * per + k * K + l] : 0.f, l < K);
         if (l == 0) {
-          if (sel_idx) sel_idx[static_cast<long long>(n) * B + p + 1] = k;
-          sel_tok[static_cast<long long>(n) * B + p + 1] = idn[(p + 1) * K + k];
+          if (si) si[p0 + q + 1] = k;
+          stok[p0 + q + 1] = sI[(q + 1) * K + k];
         }
       }
     }
+    if (p0 + batch >= Bm1) break;
   }
 }
 
