@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace dcoco {
@@ -250,28 +251,6 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_kernel(GemmDev p) {
 constexpr int kDmaRow = 128;
 
 __device__ __forceinline__ int dma_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
-
-// The ring's loads and barriers are issued as inline asm: the compiler then
-// neither counts the loads nor guards LDS reads with blanket waits, and the
-// explicit vmcnt(N) below is the only synchronisation (loads complete in
-// order, so vmcnt <= N means all but the N most recent have landed).
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds)
-               : "memory", "m0");
-}
-
-// wait until at most N of this wave's ring loads are in flight, then barrier
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
-}
 
 template <int BM, int BN, int STAGES, int MODE>
 __global__ void __launch_bounds__(kGemmThreads)

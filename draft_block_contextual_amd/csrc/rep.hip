@@ -7,7 +7,9 @@
 // order.  LN statistics are two-pass in fp32 (mean, then mean of squared
 // deviations), one wave64 per row.
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
+#include "wave.h"
 
 namespace dcoco {
 
@@ -240,6 +242,175 @@ ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, flo
   }
 }
 
+// bf16 path for r <= 256, with the weight slice resident in LDS: a chunk of
+// 256 output columns of W (256 rows x r k values) is copied into LDS with
+// direct global->LDS loads issued before the LayerNorm phase, so the copy
+// overlaps the LN loads and arithmetic and the MFMA phase then reads both
+// operands from LDS only.  W rows are 512 bytes apart; row n's 16-byte k chunk
+// c sits in slot c ^ (n & 15), so the 16 rows one fragment read touches fall
+// on distinct banks.  LN: each wave normalises BM / 4 rows, one float4 of
+// every split partial per lane and row, all loads in flight together.
+constexpr int kLgCols = 256;                 // W rows (output columns) per LDS chunk
+constexpr int kLgRowBytes = 512;             // LDS bytes per W row (k <= 256)
+
+template <int BM, int SPLIT, int MODE>
+__global__ void __launch_bounds__(256)
+ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, float eps,
+                 const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
+                 bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div) {
+  constexpr int kStr = 256 * 2 + 16;         // LDS bytes per normalised row
+  constexpr int RPW = BM / 4;                // LN rows per wave
+  constexpr int TM = BM / 16;
+  constexpr int TN = 4;                      // 64 columns per wave
+  __shared__ __align__(1024) char wl[kLgCols * kLgRowBytes];
+  __shared__ __align__(16) char tile[BM * kStr];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int m0 = blockIdx.x * BM;
+  const int cr = r >> 3;                     // 16-byte k chunks per W row
+
+  // 128 one-KB copies per chunk (two W rows each); wave wv issues copies
+  // wv, wv + 4, ...; slots whose logical chunk is past r copy the row's first
+  // chunk and are never read
+  auto issue_w = [&](int n0) {
+    const int p = l & 31;
+#pragma unroll 8
+    for (int i = 0; i < kLgCols / 8; ++i) {
+      const int j = wv + 4 * i;
+      const int row = 2 * j + (l >> 5);
+      const int c = p ^ (row & 15);
+      const long long n = min(n0 + row, N - 1);
+      const char* g = reinterpret_cast<const char*>(W + n * ldw + wcol0) + (c < cr ? c : 0) * 16;
+      dma16(g, __builtin_amdgcn_readfirstlane(lds_offset(wl) + j * 1024));
+    }
+  };
+  issue_w(0);
+
+  // z mode: the row bias of every output this lane stores, fetched before the
+  // LN phase so its latency hides behind the LN and MFMA work
+  const int frow = l & 15;
+  const int fq = l >> 4;
+  float bias[TM][4][TN];
+  auto load_bias = [&](int n0) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float* rb = row_bias + static_cast<long long>(min(m0 + a * 16 + fq * 4 + v, M - 1) / row_div) * N;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) bias[a][v][b] = rb[min(n0 + wv * 64 + b * 16 + frow, N - 1)];
+      }
+  };
+  if constexpr (MODE == 1) load_bias(0);
+
+  // ---- LayerNorm of rows m0 + wv * RPW + q into the tile (bf16).  Loads are
+  // unconditional (lanes past r re-read column 0 and are zeroed), so all of
+  // them are in flight before the first wait.
+  {
+    const int c4 = 4 * l;
+    const bool on = c4 < r;
+    const int cc = on ? c4 : 0;
+    const float inv_r = 1.0f / static_cast<float>(r);
+    float4 v[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const long long m = min(m0 + wv * RPW + q, M - 1);
+      v[q] = *reinterpret_cast<const float4*>(x + m * ldx + col0 + cc);
+    }
+#pragma unroll
+    for (int s2 = 1; s2 < SPLIT; ++s2)
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) {
+        const long long m = min(m0 + wv * RPW + q, M - 1);
+        const float4 b = *reinterpret_cast<const float4*>(x + (s2 * static_cast<long long>(M) + m) * ldx + col0 + cc);
+        v[q].x += b.x; v[q].y += b.y; v[q].z += b.z; v[q].w += b.w;
+      }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      if (!on) v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float mean = wave_sum_dpp((v[q].x + v[q].y) + (v[q].z + v[q].w)) * inv_r;
+      float4 d = make_float4(v[q].x - mean, v[q].y - mean, v[q].z - mean, v[q].w - mean);
+      if (!on) d = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float sq = (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
+      const float inv = rsqrtf(wave_sum_dpp(sq) * inv_r + eps);
+      const bool live = m0 + wv * RPW + q < M;
+      if (on) {
+        uint2 pk;
+        pk.x = live ? (static_cast<uint32_t>(f32_to_bf16(d.x * inv)) |
+                       (static_cast<uint32_t>(f32_to_bf16(d.y * inv)) << 16)) : 0u;
+        pk.y = live ? (static_cast<uint32_t>(f32_to_bf16(d.z * inv)) |
+                       (static_cast<uint32_t>(f32_to_bf16(d.w * inv)) << 16)) : 0u;
+        *reinterpret_cast<uint2*>(tile + (wv * RPW + q) * kStr + c4 * 2) = pk;
+      }
+    }
+  }
+
+  for (int n0 = 0; n0 < N; n0 += kLgCols) {
+    if (n0 > 0) {
+      __syncthreads();                       // every wave is done with the last chunk
+      issue_w(n0);
+      if constexpr (MODE == 1) load_bias(n0);
+    }
+    wait_all_barrier();
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < r; k += 32) {
+      const int c = (k >> 3) + fq;
+      bf16x8_t fa[TM], fw[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+        fa[a] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                    tile + (a * 16 + frow) * kStr + c * 16));
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int row = wv * 64 + b * 16 + frow;
+        fw[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                    wl + row * kLgRowBytes + (c ^ (row & 15)) * 16));
+      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fw[b], acc[a][b], 0, 0, 0);
+    }
+
+    // epilogue: lane l holds column l & 15 and rows 4 (l >> 4) + v of each tile
+    int mrow[TM][4];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mrow[a][v] = m0 + a * 16 + fq * 4 + v;
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            const int n = n0 + wv * 64 + b * 16 + frow;
+            if (mrow[a][v] < M && n < N)
+              out_bf[static_cast<long long>(mrow[a][v]) * N + n] = bf16{f32_to_bf16(acc[a][b][v] + bias[a][v][b])};
+          }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            const int n = n0 + wv * 64 + b * 16 + frow;
+            if (mrow[a][v] < M && n < N) out_f32[static_cast<long long>(mrow[a][v]) * N + n] = acc[a][b][v];
+          }
+    }
+  }
+}
+
 template <typename TO>
 hipError_t launch_ln_t(const float* x, int split, int M, int ldx, int col0, int r, float eps, void* y,
                        hipStream_t st) {
@@ -280,17 +451,26 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   if (split == 1) DCOCO_LNG(BMV, RM, 1, MD);         \
   else if (split == 2) DCOCO_LNG(BMV, RM, 2, MD);    \
   else DCOCO_LNG(BMV, RM, 4, MD)
+#define DCOCO_LNW(BMV, SP, MD)                                                                      \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, M, \
+                     ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div)
+#define DCOCO_LNW_SPLIT(BMV, MD)                 \
+  if (split == 1) DCOCO_LNW(BMV, 1, MD);         \
+  else if (split == 2) DCOCO_LNW(BMV, 2, MD);    \
+  else DCOCO_LNW(BMV, 4, MD)
   if (r <= 256) {
     if (M >= 4096) {
-      if (bias) { DCOCO_LNG_SPLIT(32, 256, 1); } else { DCOCO_LNG_SPLIT(32, 256, 0); }
+      if (bias) { DCOCO_LNW_SPLIT(32, 1); } else { DCOCO_LNW_SPLIT(32, 0); }
     } else {
-      if (bias) { DCOCO_LNG_SPLIT(16, 256, 1); } else { DCOCO_LNG_SPLIT(16, 256, 0); }
+      if (bias) { DCOCO_LNW_SPLIT(16, 1); } else { DCOCO_LNW_SPLIT(16, 0); }
     }
   } else if (r <= 512) {
     if (bias) { DCOCO_LNG_SPLIT(16, 512, 1); } else { DCOCO_LNG_SPLIT(16, 512, 0); }
   } else {
     if (bias) { DCOCO_LNG_SPLIT(16, 2048, 1); } else { DCOCO_LNG_SPLIT(16, 2048, 0); }
   }
+#undef DCOCO_LNW_SPLIT
+#undef DCOCO_LNW
 #undef DCOCO_LNG_SPLIT
 #undef DCOCO_LNG
   return hipGetLastError();

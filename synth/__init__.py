@@ -140,6 +140,9 @@ CONFIGS = {
                         30.0, "peaks", 64, 2005, "random", "K = 64 on a small shape"),
     "k32_small": Config("k32_small", _d(2, 5, 32, 9000, 512, 256, 128, 128, 128, 320, "bf16"),
                         30.0, "peaks", 32, 2006, "random", "K = 32 on a small shape"),
+    "widez_bf16": Config("widez_bf16", _d(2, 6, 8, 7001, 256, 192, 160, 320, 96, 128, "bf16"),
+                         30.0, "peaks", 8, 2007, "random",
+                         "r = 160 (20 k chunks) and d_z = 320 (two column chunks, the second partial)"),
 }
 
 # tensor roles, in the fixed order their seeds are spawned
