@@ -7,8 +7,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <mutex>
 
 #include "kernels.h"
 
@@ -268,51 +266,6 @@ hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z,
   return score_tail(d, w, z, cl, S, L, st);
 }
 
-// ---- a second stream per device for the slot side of dcoco_correct_block
-// (default priority), joined to the caller's stream with events
-constexpr int kEventRing = 32;
-struct SideCtx {
-  bool tried = false;
-  bool ok = false;
-  hipStream_t stream = nullptr;
-  hipEvent_t ev[kEventRing][2];
-  unsigned next = 0;
-};
-std::mutex g_side_mu;
-SideCtx g_side[64];
-
-bool single_stream_forced() {
-  static const bool forced = [] {
-    const char* v = std::getenv("DCOCO_SINGLE_STREAM");
-    return v && v[0] == '1';
-  }();
-  return forced;
-}
-
-// a side stream and a (fork, join) event pair for this call; false: run on
-// the caller's stream only
-bool side_stream(hipStream_t* side, hipEvent_t* fork, hipEvent_t* join) {
-  if (single_stream_forced()) return false;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  SideCtx& c = g_side[dev];
-  if (!c.tried) {
-    c.tried = true;
-    bool ok = hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; ok && i < kEventRing; ++i)
-      ok = hipEventCreateWithFlags(&c.ev[i][0], hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&c.ev[i][1], hipEventDisableTiming) == hipSuccess;
-    c.ok = ok;
-  }
-  if (!c.ok) return false;
-  const unsigned i = c.next++ % kEventRing;
-  *side = c.stream;
-  *fork = c.ev[i][0];
-  *join = c.ev[i][1];
-  return true;
-}
-
 int check_ws(void* ws, size_t* bytes, size_t need) {
   if (!bytes) return DCOCO_ERR_INVALID_ARG;
   need = need < kAlign ? kAlign : need;   // never 0: NULL always means "size query"
@@ -442,24 +395,12 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (cand_logits_out) cl = cand_logits_out;
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  // The slot side (slot projections, pair states, gf, the pair term) needs
-  // only h; it runs on a second stream while top-K and the gathered
-  // projection run on the caller's stream, and joins before z.
   const bool bf = dt == kDtypeBf16;
-  hipStream_t side = st;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  const bool two = side_stream(&side, &ev_fork, &ev_join);
-  hipError_t e = hipSuccess;
-  if (two) {
-    e = hipEventRecord(ev_fork, st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
-  }
-  if (e == hipSuccess) e = slot_part(d, w, h, s, bf ? SL.s3 : nullptr, L, side);
-  if (e == hipSuccess) e = pair_term(d, w, s, SL, bf, side);
-  if (two && e == hipSuccess) e = hipEventRecord(ev_join, side);
+  // the pair-state kernel also writes the bf16 split of s that the pair term reads
+  hipError_t e = slot_part(d, w, h, s, bf ? SL.s3 : nullptr, L, st);
+  if (e == hipSuccess) e = pair_term(d, w, s, SL, bf, st);
   if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
-  if (two && e == hipSuccess) e = hipStreamWaitEvent(st, ev_join, 0);
   if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
   if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st);
   if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);

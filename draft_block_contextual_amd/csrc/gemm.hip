@@ -252,31 +252,37 @@ constexpr int kDmaRow = 128;
 
 __device__ __forceinline__ int dma_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int BM, int BN, int STAGES, int MODE>
-__global__ void __launch_bounds__(kGemmThreads)
+// WM x WN waves, each owning a (BM / WM) x (BN / WN) block of the tile.
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
+__global__ void __launch_bounds__(64 * WM * WN)
 gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
+  constexpr int NW = WM * WN;
   constexpr int kABytes = BM * kDmaRow;
   constexpr int kWBytes = BN * kDmaRow;
   constexpr int kStage = kABytes + kWBytes;
-  constexpr int AJ = kABytes / 1024 / 4;   // A load instructions per wave per stage
-  constexpr int WJ = kWBytes / 1024 / 4;
+  constexpr int AJ = kABytes / 1024 / NW;  // A load instructions per wave per stage
+  constexpr int WJ = kWBytes / 1024 / NW;
   constexpr int IPS = AJ + WJ;
-  constexpr int TM = BM / 32;
-  constexpr int TN = BN / 32;
-  static_assert(AJ >= 1 && WJ >= 1, "tile too small for 4 waves");
-  static_assert(STAGES == 3 || STAGES == 4, "ring depth");
+  constexpr int MW = BM / WM;              // wave block
+  constexpr int NWB = BN / WN;
+  constexpr int TM = MW / 16;
+  constexpr int TN = NWB / 16;
+  static_assert(AJ >= 1 && WJ >= 1 && AJ * NW * 1024 == kABytes && WJ * NW * 1024 == kWBytes,
+                "tile does not split into whole 1 KB copies per wave");
+  static_assert(TM >= 1 && TN >= 1 && TM * 16 * WM == BM && TN * 16 * WN == BN, "wave grid");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
   // one LDS object per ring slot: the compiler tracks direct-to-LDS loads per
   // object, so reads of one slot need not wait for loads into the others
   __shared__ __align__(1024) char sm0[kStage];
   __shared__ __align__(1024) char sm1[kStage];
-  __shared__ __align__(1024) char sm2[kStage];
+  __shared__ __align__(1024) char sm2[STAGES >= 3 ? kStage : 16];
   __shared__ __align__(1024) char sm3[STAGES == 4 ? kStage : 16];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wv = tid >> 6;
-  const int wm = wv >> 1;
-  const int wn = wv & 1;
+  const int wm = wv / WN;
+  const int wn = wv % WN;
   int bid = blockIdx.x;
   if (remap) bid = (bid % 8) * (static_cast<int>(gridDim.x) / 8) + bid / 8;
   const int tn = bid % tiles_n;
@@ -294,7 +300,7 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
   const char* srcA[AJ];
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
-    const int r = 8 * (wv + 4 * j) + (l >> 3);
+    const int r = 8 * (wv + NW * j) + (l >> 3);
     const int c = dma_swz(r, l & 7);
     const int m = min(m0 + r, p.M - 1);
     long long row = m;
@@ -308,7 +314,7 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
   const char* srcW[WJ];
 #pragma unroll
   for (int j = 0; j < WJ; ++j) {
-    const int r = 8 * (wv + 4 * j) + (l >> 3);
+    const int r = 8 * (wv + NW * j) + (l >> 3);
     const int c = dma_swz(r, l & 7);
     const int jn = min(n0 + r, p.N - 1);
     const char* base;
@@ -322,10 +328,10 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
   auto issue = [&](char* base, int k0) {
     const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_offset(base) + wv * 1024);
 #pragma unroll
-    for (int j = 0; j < AJ; ++j) dma16(srcA[j] + static_cast<long long>(k0) * 2, b0 + j * 4096);
+    for (int j = 0; j < AJ; ++j) dma16(srcA[j] + static_cast<long long>(k0) * 2, b0 + j * NW * 1024);
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
-      dma16(srcW[j] + static_cast<long long>(k0) * 2, b0 + kABytes + j * 4096);
+      dma16(srcW[j] + static_cast<long long>(k0) * 2, b0 + kABytes + j * NW * 1024);
   };
 
   f32x4_t acc[TM][TN];
@@ -350,12 +356,12 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
       bf16x8_t fa[TM], fw[TN];
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
-        const int row = wm * (BM / 2) + a * 16 + frow;
+        const int row = wm * MW + a * 16 + frow;
         fa[a] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + row * kDmaRow + dma_swz(row, c) * 16));
       }
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
-        const int row = wn * (BN / 2) + b * 16 + frow;
+        const int row = wn * NWB + b * 16 + frow;
         fw[b] = as_bf16x8(*reinterpret_cast<const uint4*>(sw + row * kDmaRow + dma_swz(row, c) * 16));
       }
 #pragma unroll
@@ -377,14 +383,18 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
     compute(slot(S));
   };
   if (0 < nk) issue(sm0, kbeg);
-  if (1 < nk) issue(sm1, kbeg + 64);
+  if constexpr (STAGES >= 3) {
+    if (1 < nk) issue(sm1, kbeg + 64);
+  }
   if constexpr (STAGES == 4) {
     if (2 < nk) issue(sm2, kbeg + 128);
   }
   for (int it = 0; it < nk; it += STAGES) {
     step(std::integral_constant<int, 0>{}, it);
     if (it + 1 < nk) step(std::integral_constant<int, 1>{}, it + 1);
-    if (it + 2 < nk) step(std::integral_constant<int, 2>{}, it + 2);
+    if constexpr (STAGES >= 3) {
+      if (it + 2 < nk) step(std::integral_constant<int, 2>{}, it + 2);
+    }
     if constexpr (STAGES == 4) {
       if (it + 3 < nk) step(std::integral_constant<int, 3>{}, it + 3);
     }
@@ -400,8 +410,8 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
       for (int b = 0; b < TN; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = min(m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v, p.M - 1);
-          const int n = min(n0 + wn * (BN / 2) + b * 16 + (l & 15), p.N - 1);
+          const int m = min(m0 + wm * MW + a * 16 + (l >> 4) * 4 + v, p.M - 1);
+          const int n = min(n0 + wn * NWB + b * 16 + (l & 15), p.N - 1);
           float x = 0.f;
           if (p.row_bias) x += p.row_bias[static_cast<long long>(m / p.row_bias_div) * p.N + n];
           if (p.col_bias) x += bf16_to_f32(static_cast<const bf16*>(p.col_bias)[n].bits);
@@ -413,8 +423,8 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
       for (int b = 0; b < TN; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v;
-          const int n = n0 + wn * (BN / 2) + b * 16 + (l & 15);
+          const int m = m0 + wm * MW + a * 16 + (l >> 4) * 4 + v;
+          const int n = n0 + wn * NWB + b * 16 + (l & 15);
           if (m < p.M && n < p.N)
             static_cast<bf16*>(p.out)[static_cast<long long>(m) * p.ldo + n] =
                 bf16{f32_to_bf16(acc[a][b][v] + bias[a][b][v])};
@@ -426,8 +436,8 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
       for (int b = 0; b < TN; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = m0 + wm * (BM / 2) + a * 16 + (l >> 4) * 4 + v;
-          const int n = n0 + wn * (BN / 2) + b * 16 + (l & 15);
+          const int m = m0 + wm * MW + a * 16 + (l >> 4) * 4 + v;
+          const int n = n0 + wn * NWB + b * 16 + (l & 15);
           if (m < p.M && n < p.N)
             p.out_f32[(static_cast<long long>(zs) * p.M + m) * p.ldo + n] = acc[a][b][v];
         }
@@ -438,14 +448,18 @@ struct Tile {
   int bm, bn;
 };
 
-Tile pick_tile(int M, int N) {
+// bf16 x bf16 with Kd % 64 == 0 runs on the DMA kernel, which also has a
+// 128 x 256 tile (8 waves): tall products with N >= 256 read each A row once
+// per 256 columns
+Tile pick_tile(int M, int N, bool dma) {
   const long long t128 = static_cast<long long>((M + 127) / 128) * ((N + 127) / 128);
+  if (dma && M >= 2048 && N >= 256 && N % 256 == 0) return {128, 256};
   if (M >= 1024 && N >= 128 && t128 >= 64) return {128, 128};
   return {64, 64};
 }
 
-int pick_split(int M, int N, int Kd, int bk) {
-  const Tile t = pick_tile(M, N);
+int pick_split(int M, int N, int Kd, int bk, bool dma) {
+  const Tile t = pick_tile(M, N, dma);
   const long long tiles = static_cast<long long>((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
   int split = 1;
   while (tiles * split < 256 && split < 4 && Kd / (split * 2) >= 4 * bk) split *= 2;
@@ -475,21 +489,24 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
   p.out_f32 = q.out_f32; p.ldo = q.ldo; p.out = q.out;
   p.row_bias = q.row_bias; p.row_bias_div = q.row_bias_div > 0 ? q.row_bias_div : 1;
   p.col_bias = q.col_bias;
-  const Tile t = pick_tile(q.M, q.N);
+  const bool dma = kBF && q.Kd % 64 == 0;
+  const Tile t = pick_tile(q.M, q.N, dma);
   const bool partial = q.out == nullptr;
   if constexpr (kBF) {
-    if (q.Kd % 64 == 0) {
+    if (dma) {
       const int tiles_m = (q.M + t.bm - 1) / t.bm;
       const int tiles_n = (q.N + t.bn - 1) / t.bn;
       const int total = tiles_m * tiles_n * split;
       const int remap = (total % 8 == 0) ? 1 : 0;
-#define DCOCO_DMA(BMV, BNV, ST, MODEV)                                                         \
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BMV, BNV, ST, MODEV>), dim3(total), dim3(kGemmThreads), 0, st, \
-                     p, tiles_m, tiles_n, remap)
-      if (t.bm == 128) {
-        if (partial) DCOCO_DMA(128, 128, 4, 0); else DCOCO_DMA(128, 128, 4, 1);
+#define DCOCO_DMA(BMV, BNV, WMV, WNV, ST, MODEV)                                                  \
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BMV, BNV, WMV, WNV, ST, MODEV>), dim3(total),              \
+                     dim3(64 * WMV * WNV), 0, st, p, tiles_m, tiles_n, remap)
+      if (t.bn == 256) {
+        if (partial) DCOCO_DMA(128, 256, 2, 4, 3, 0); else DCOCO_DMA(128, 256, 2, 4, 3, 1);
+      } else if (t.bm == 128) {
+        if (partial) DCOCO_DMA(128, 128, 2, 2, 4, 0); else DCOCO_DMA(128, 128, 2, 2, 4, 1);
       } else {
-        if (partial) DCOCO_DMA(64, 64, 4, 0); else DCOCO_DMA(64, 64, 4, 1);
+        if (partial) DCOCO_DMA(64, 64, 2, 2, 4, 0); else DCOCO_DMA(64, 64, 2, 2, 4, 1);
       }
 #undef DCOCO_DMA
       return hipGetLastError();
@@ -511,7 +528,8 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
 
 int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype) {
   const int bk = (a_dtype == kDtypeBf16 && w_dtype == kDtypeBf16) ? 64 : 32;
-  return pick_split(M, N, Kd, bk);
+  const bool dma = a_dtype == kDtypeBf16 && w_dtype == kDtypeBf16 && Kd % 64 == 0;
+  return pick_split(M, N, Kd, bk, dma);
 }
 
 hipError_t launch_gemm(const GemmProblem& q, hipStream_t st) {

@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "wave.h"
 
 namespace dcoco {
 
@@ -252,9 +253,7 @@ constexpr int kWalkIds = 1088;   // candidate ids staged per batch: (16 + 1) row
 // valid lane, so they never win)
 __device__ __forceinline__ int wave_argmax(float v, bool valid) {
   const uint32_t key = valid ? order_key(v) : 0u;
-  uint32_t m = key;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o, kWave)));
+  const uint32_t m = wave_max_u32_dpp(key);
   return __builtin_ctzll(ballot(key == m));
 }
 

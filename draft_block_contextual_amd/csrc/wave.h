@@ -26,4 +26,22 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ uint32_t read_lane_u32(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Maximum over all 64 lanes, same lane moves as wave_sum_dpp.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, dpp_move_u32<0xB1>(v));
+  v = max(v, dpp_move_u32<0x4E>(v));
+  v = max(v, dpp_move_u32<0x141>(v));
+  v = max(v, dpp_move_u32<0x140>(v));
+  return max(max(read_lane_u32(v, 0), read_lane_u32(v, 16)), max(read_lane_u32(v, 32), read_lane_u32(v, 48)));
+}
+
 }  // namespace dcoco

@@ -145,13 +145,7 @@ int dcoco_select(const dcoco_dims* dims, const float* S, const float* cand_logit
                  void* stream);
 
 /* The whole path for n_blocks draft blocks: top-K, representations, pair
- * states, transition scores and the greedy walk.  The slot side (pair states
- * and the parts of z and of the scores that depend on h only) runs on a
- * second stream that the library creates once per device (default priority)
- * and that forks from and joins back into `stream` with events, so all work
- * is ordered on `stream` as if it ran there alone; concurrent calls on one
- * device share that second stream.  Setting DCOCO_SINGLE_STREAM=1 in the
- * environment keeps everything on `stream`.
+ * states, transition scores and the greedy walk, on one stream.
  *   logits [n_blocks*B, V], h [n_blocks, B, d_hidden], E [V, d_embed]: dtype
  *   sel_tok         [n_blocks, B] int32           out: the corrected block
  *   sel_idx         [n_blocks, B] int32           out, may be NULL

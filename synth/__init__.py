@@ -143,6 +143,9 @@ CONFIGS = {
     "widez_bf16": Config("widez_bf16", _d(2, 6, 8, 7001, 256, 192, 160, 320, 96, 128, "bf16"),
                          30.0, "peaks", 8, 2007, "random",
                          "r = 160 (20 k chunks) and d_z = 320 (two column chunks, the second partial)"),
+    "tall_bf16": Config("tall_bf16", _d(3, 15, 50, 6007, 256, 512, 256, 256, 64, 256, "bf16"),
+                        30.0, "peaks", 50, 2008, "random",
+                        "2250 candidate rows (ragged over 128-row tiles) with 256-wide projections"),
 }
 
 # tensor roles, in the fixed order their seeds are spawned

@@ -50,7 +50,7 @@ def _oracle(name, blocks=None):
 
 
 SMALL = ["tiny", "tiny_zero", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "mid_f32",
-         "k64_small", "k32_small", "widez_bf16"]
+         "k64_small", "k32_small", "widez_bf16", "tall_bf16"]
 
 
 def _run_block(name):
@@ -172,7 +172,8 @@ def test_select_worked_example():
 
 # ------------------------------------------------------ representation
 
-@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_f32", "mid_bf16", "k32_small", "widez_bf16"])
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_f32", "mid_bf16", "k32_small", "widez_bf16",
+                                  "tall_bf16"])
 def test_represent_matches_oracle(name):
     import draft_block_contextual_amd as dc
     import torch
