@@ -28,7 +28,9 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
+#include "wave.h"
 
 namespace dcoco {
 
@@ -297,6 +299,11 @@ __device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
                                                                 __builtin_bit_cast(u16x2, b)));
 }
+// per half: signed 16-bit maximum
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, a),
+                                                                __builtin_bit_cast(i16x2, b)));
+}
 // per half: saturate(a - b); nonzero iff the half of a exceeds that of b
 __device__ __forceinline__ uint32_t pk_sub_sat(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, a),
@@ -313,7 +320,7 @@ __device__ __forceinline__ uint32_t exact_key16(uint32_t bits) {
 // composite (value desc, id asc); writes ids and the original logit values.
 // Executed by one wave.
 template <int Q, int KEYBITS, typename T>
-__device__ void finish_row(const uint64_t* src, int count, int K, uint64_t* s_fin, const T* rowp,
+__device__ void finish_row(const uint64_t* src, int count, int K, uint64_t* s_fin, const T* rowp, int V,
                            int32_t* ids_row, float* vals_row) {
   const int l = lane_id();
   select_to<Q, KEYBITS>(src, count, K, s_fin);
@@ -324,8 +331,11 @@ __device__ void finish_row(const uint64_t* src, int count, int K, uint64_t* s_fi
     for (int j = 0; j < K; ++j) rank += s_fin[j] > mine ? 1 : 0;
     const uint32_t id = 0xffffffffu - comp_inv(mine);
     ids_row[rank] = static_cast<int32_t>(id);
-    if constexpr (std::is_same<T, uint16_t>::value) vals_row[rank] = bf16_to_f32(rowp[id]);
-    else vals_row[rank] = Elem<T>::to_f32(rowp[id]);
+    // every id here is < V (a row holds at least K elements); the guard keeps
+    // the value read inside the row regardless
+    const uint32_t rid = id < static_cast<uint32_t>(V) ? id : 0u;
+    if constexpr (std::is_same<T, uint16_t>::value) vals_row[rank] = bf16_to_f32(rowp[rid]);
+    else vals_row[rank] = Elem<T>::to_f32(rowp[rid]);
   }
 }
 
@@ -388,132 +398,160 @@ __device__ __attribute__((noinline)) void exact_wave_bf16(const uint16_t* rowp, 
 }
 
 // One workgroup (8 waves) per bf16 row; no cross-workgroup merge.  Wave w
-// scans segments w, w+8, ... of 64 lanes x NV 16-byte vectors (8 bf16 each),
-// all NV loads of a segment in flight at once, and keeps a running lower bound
-// on its own K-th largest key: the K-th largest of a segment's 64*G group
-// maxima.  Keys at or above it (about K + a few per segment on random rows)
-// are appended to LDS.  Each wave then selects its top-K exactly and wave 0
-// merges the 8 lists, sorts the K winners and writes ids and values.
+// scans segments w, w+8, ... of 64 lanes x NV 16-byte vectors (8 bf16 each).
+//   1. A row-wide bound T on the K-th largest key: the K-th largest of the
+//      maxima of G groups per lane over every wave's first segment (K
+//      distinct elements reach it).
+//   2. Streaming: every 16-byte vector is screened against T; the start of
+//      each vector holding an element at or above T is recorded in a
+//      per-wave LDS list.  On random rows that is about K times the ratio of
+//      the row to the sampled part, spread over 8 waves.  The screen is a few
+//      instructions per vector and never waits on memory, so the stream stays
+//      ahead.
+//   3. The flagged vectors are read again in one parallel round (the rows
+//      were just streamed) and their elements at or above T become
+//      candidates; each wave selects its top-K exactly and wave 0 merges the
+//      8 lists, sorts the K winners and writes ids and values.
+// A NaN among the candidates, or a list that overflows, sends the wave to the
+// exact path.
 constexpr int kRowWaves = 8;
+constexpr int kRowCap = 128;                // candidates per wave list
+constexpr int kFlagCap = 128;               // flagged vectors per wave list
 
-template <int NV, int G, bool kVecLoad>
-__global__ void __launch_bounds__(kRowWaves * kWave)
-topk_bf16_row_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
-                     float* __restrict__ vals) {
-  constexpr int kWordsL = NV * 4;           // 32-bit words (bf16 pairs) per lane
-  constexpr int kSegLen = kWave * NV * 8;
-  static_assert(kWordsL <= 128, "candidate bitmask holds 128 words");
-  const int row = blockIdx.x;
-  const int w = threadIdx.x / kWave;
-  const int l = lane_id();
-  const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
+// group maxima of one segment's packed keys (raw bf16 pairs in kw)
+template <int NV, int G>
+__device__ __forceinline__ void group_max(const uint32_t (&kw)[NV * 4], uint32_t (&gmx)[G]) {
+  constexpr int kWordsL = NV * 4;
+#pragma unroll
+  for (int g = 0; g < G; ++g) gmx[g] = 0u;
+#pragma unroll
+  for (int j = 0; j < kWordsL; ++j) {
+    const int g = (j * G) / kWordsL;
+    gmx[g] = pk_max(gmx[g], pack_keys(kw[j]));
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) gmx[g] = max(gmx[g] & 0xffffu, gmx[g] >> 16);
+}
 
-  __shared__ uint64_t s_cand[kRowWaves][kCandCap];
-  __shared__ uint64_t s_best[kRowWaves * 64];
-  __shared__ uint64_t s_fin[64];
-  __shared__ int s_cnt[kRowWaves];
+// Row-wide bound from every wave's group maxima (s_gm holds kRowWaves * G *
+// 64 keys); called by all waves after a barrier, each computes the same T.
+template <int G>
+__device__ __forceinline__ uint32_t row_bound(const uint32_t* s_gm, int K, int l) {
+  constexpr int Q = kRowWaves * G;
+  uint32_t v[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) v[q] = s_gm[q * kWave + l];
+  uint32_t t = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) n += __popcll(ballot(v[q] >= c));
+    if (n >= K) t = c;
+  }
+  return t;
+}
 
-  if (l == 0) s_cnt[w] = 0;
-  __builtin_amdgcn_wave_barrier();
-  uint32_t t_run = 0;       // running lower bound on this wave's K-th largest key
-  bool exact = false;
-  int nseg = 0;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int seg0 = (rd * kRowWaves + w) * kSegLen;
-    if (seg0 >= V) break;
-    ++nseg;
-    uint32_t kw[kWordsL];
+// Screens one segment (raw bf16 pairs in kw) against the bound t and records
+// the first element index of every vector holding an element at or above t.
+//
+// For a bound above the key of zero (t > 0x8000) the qualifying patterns are
+// exactly the non-negative ones at or above the raw pattern of t, and read as
+// signed 16-bit integers raw patterns order like their values on that side
+// (negative patterns, -0 included, read as negative integers and never
+// qualify), so a vector is screened with a packed signed max over its words
+// and one compare.  Otherwise its words are packed into keys and compared.
+// NaN patterns need no screening of their own: a positive NaN reads above
+// every number and is always flagged, and a NaN that is not flagged ranks
+// below at least K numbers of the row.
+template <int NV>
+__device__ __forceinline__ void row_screen(const uint32_t (&kw)[NV * 4], int seg0, int V, int l, uint32_t t,
+                                           int& nflag, int32_t* flags) {
+  uint32_t vflag = 0u;
+  if (t > 0x8000u) {
+    const uint32_t thr = ((t ^ 0x8000u) - 1u) * 0x00010001u;   // raw pattern of t, minus one
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e0 = seg0 + (i * kWave + l) * 8;
-      if (kVecLoad && e0 + 8 <= V) {
-        const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);
-        kw[4 * i] = v.x; kw[4 * i + 1] = v.y; kw[4 * i + 2] = v.z; kw[4 * i + 3] = v.w;
-      } else {
-        // past the row end: -inf patterns (never appended: their ids are >= V)
+      const uint32_t m = pk_max_i16(pk_max_i16(kw[4 * i], kw[4 * i + 1]), pk_max_i16(kw[4 * i + 2], kw[4 * i + 3]));
+      vflag |= (pk_max_i16(m, thr) != thr ? 1u : 0u) << i;
+    }
+  } else {
+    const uint32_t thr = (t - 1u) * 0x00010001u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = e0 + 2 * q < V ? rowp[e0 + 2 * q] : 0xff80u;
-          const uint32_t hi = e0 + 2 * q + 1 < V ? rowp[e0 + 2 * q + 1] : 0xff80u;
-          kw[4 * i + q] = lo | (hi << 16);
-        }
+    for (int i = 0; i < NV; ++i) {
+      uint32_t any = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) any |= pk_sub_sat(pack_keys(kw[4 * i + q]), thr);
+      vflag |= (any != 0u ? 1u : 0u) << i;
+    }
+  }
+  if (ballot(vflag != 0u) == 0ull) return;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e0 = seg0 + (i * kWave + l) * 8;
+    const bool f = ((vflag >> i) & 1u) && e0 < V;
+    const uint64_t m = ballot(f);
+    if (m == 0ull) continue;
+    const int pos = nflag + lanes_below(m);
+    if (f && pos < kFlagCap) flags[pos] = e0;
+    nflag += __popcll(m);
+  }
+}
+
+// Reads the flagged vectors again (each lane one vector per pass) and appends
+// their elements at or above t to cand, compacted with ballots.  Returns
+// false when the wave must take the exact path (a NaN candidate, or more
+// candidates than the list holds).
+template <bool kVec>
+__device__ __forceinline__ bool row_collect(const uint16_t* rowp, int V, uint32_t t, const int32_t* flags,
+                                            int nflag, int l, uint64_t* cand, int& cnt) {
+  bool bad = false;
+  for (int b = 0; b < nflag; b += kWave) {
+    const bool act = b + l < nflag;
+    const int e0 = act ? flags[b + l] : 0;
+    uint32_t w4[4];
+    if constexpr (kVec) {
+      const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);   // e0 + 8 <= V
+      w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = e0 + 2 * q < V ? rowp[e0 + 2 * q] : 0xffffu;
+        const uint32_t hi = e0 + 2 * q + 1 < V ? rowp[e0 + 2 * q + 1] : 0xffffu;
+        w4[q] = lo | (hi << 16);
       }
     }
-    uint32_t gmx[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) gmx[g] = 0u;
-    uint32_t mn = 0xffffffffu;
-#pragma unroll
-    for (int j = 0; j < kWordsL; ++j) {
-      kw[j] = pack_keys(kw[j]);
-      const int g = (j * G) / kWordsL;
-      gmx[g] = pk_max(gmx[g], kw[j]);
-      mn = pk_min(mn, kw[j]);
-    }
-    uint32_t top = 0;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      gmx[g] = max(gmx[g] & 0xffffu, gmx[g] >> 16);
-      top = max(top, gmx[g]);
-    }
-    const bool lane_nan = top > 0xff80u || min(mn & 0xffffu, mn >> 16) < 0x0080u;
-    if (ballot(lane_nan) != 0) {
-      exact = true;
-      break;
-    }
-    // this segment's bound: the K-th largest group maximum (all keys >= 0x0080)
-    uint32_t t0 = 0;
-    for (int bit = 15; bit >= 0; --bit) {
-      const uint32_t cand = t0 | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int g = 0; g < G; ++g) cnt += __popcll(ballot(gmx[g] >= cand));
-      if (cnt >= K) t0 = cand;
-    }
-    t_run = max(t_run, t0);
-    const uint32_t thr = (t_run - 1u) * 0x00010001u;
-    // one bit per word holding a key >= t_run (words 0..63 and 64..)
-    uint64_t mlo = 0, mhi = 0;
-#pragma unroll
-    for (int j = 0; j < kWordsL; ++j) {
-      const uint64_t bit = pk_sub_sat(kw[j], thr) != 0u ? 1ull : 0ull;
-      if (j < 64) mlo |= bit << j;
-      else mhi |= bit << (j - 64);
-    }
-    while (mlo | mhi) {
-      int j;
-      if (mlo) {
-        j = __builtin_ctzll(mlo);
-        mlo &= mlo - 1ull;
-      } else {
-        j = 64 + __builtin_ctzll(mhi);
-        mhi &= mhi - 1ull;
-      }
-      const int e = seg0 + ((j >> 2) * kWave + l) * 8 + (j & 3) * 2;
-      if (e >= V) continue;   // padding only
-      const uint32_t lo = rowp[e];
-      const uint32_t hi = e + 1 < V ? rowp[e + 1] : 0xff80u;
-      const uint32_t kk = pack_keys(lo | (hi << 16));
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t kk = pack_keys(w4[q]);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t k = (kk >> (16 * h)) & 0xffffu;
-        if (k >= t_run && e + h < V) {
-          const int pos = atomicAdd(&s_cnt[w], 1);
-          if (pos < kCandCap) s_cand[w][pos] = make_comp(k, static_cast<uint32_t>(e + h));
-        }
+        const int e = e0 + 2 * q + h;
+        const bool c = act && k >= t && e < V;
+        bad |= c && (k > 0xff80u || k < 0x0080u);
+        const uint64_t m = ballot(c);
+        const int pos = cnt + lanes_below(m);
+        if (c && pos < kRowCap) cand[pos] = make_comp(k, static_cast<uint32_t>(e));
+        cnt += __popcll(m);
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    if (s_cnt[w] > kCandCap) {
-      exact = true;
-      break;
-    }
   }
+  return ballot(bad) == 0ull && cnt <= kRowCap;
+}
+
+// After the scan: each wave's exact top-K into s_best, then wave 0 sorts the
+// row's K winners and writes ids and values.
+template <int NV>
+__device__ __forceinline__ void row_finish(const uint16_t* rowp, int V, int K, int rounds, int w, int l, int nseg,
+                                           bool exact, int cnt, uint64_t (*s_cand)[kRowCap], uint64_t* s_best,
+                                           uint64_t* s_fin, int* s_cnt, int32_t* ids_row, float* vals_row) {
+  constexpr int kSegLen = kWave * NV * 8;
   uint64_t* wave_out = s_best + w * K;
   if (nseg == 0) {
     for (int i = l; i < K; i += kWave) wave_out[i] = 0ull;
   } else if (!exact) {
-    select_small<16>(s_cand[w], s_cnt[w], K, wave_out);
+    select_small<16>(s_cand[w], cnt, K, wave_out);
   } else {
     int segs = 0;
     for (int rd = 0; rd < rounds; ++rd) segs += (rd * kRowWaves + w) * kSegLen < V ? 1 : 0;
@@ -522,12 +560,177 @@ topk_bf16_row_kernel(const uint16_t* __restrict__ logits, int V, int K, int roun
   __syncthreads();
   if (w == 0) {
     const int count = kRowWaves * K;
-    int32_t* ids_row = ids + static_cast<size_t>(row) * K;
-    float* vals_row = vals + static_cast<size_t>(row) * K;
-    if (count <= 2 * kWave) finish_row<2, 16>(s_best, count, K, s_fin, rowp, ids_row, vals_row);
-    else if (count <= 4 * kWave) finish_row<4, 16>(s_best, count, K, s_fin, rowp, ids_row, vals_row);
-    else finish_row<8, 16>(s_best, count, K, s_fin, rowp, ids_row, vals_row);
+    if (count <= 2 * kWave) finish_row<2, 16>(s_best, count, K, s_fin, rowp, V, ids_row, vals_row);
+    else if (count <= 4 * kWave) finish_row<4, 16>(s_best, count, K, s_fin, rowp, V, ids_row, vals_row);
+    else finish_row<8, 16>(s_best, count, K, s_fin, rowp, V, ids_row, vals_row);
   }
+}
+
+// Rows whose length is a multiple of 8 and that start 16-byte aligned.  Each
+// wave streams its segments through a private ring of S LDS slots filled by
+// direct global->LDS loads: S - 1 segments are in flight while the wave
+// screens the current one, and the waits are a fixed vmcnt.  Loads are
+// unconditional; a vector past the row end reads a clamped address inside the
+// row and is replaced when the segment is read.  Padding is the pattern
+// 0xffff (a NaN whose packed key is 1, below every real key but the NaNs
+// that also sit below -inf): groups of padding never lift the bound, and
+// padding is never appended (its ids are >= V).
+template <int NV, int G, int S>
+__global__ void __launch_bounds__(kRowWaves * kWave)
+topk_bf16_row_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
+                     float* __restrict__ vals) {
+  constexpr int kSegLen = kWave * NV * 8;
+  constexpr int kSlot = NV * 1024;           // LDS bytes per segment
+  static_assert(S >= 2 && (S - 1) * NV < 64, "ring depth");
+  const int row = blockIdx.x;
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
+
+  __shared__ __align__(1024) char s_ring[kRowWaves * S * kSlot];
+  // the group maxima of the first segments live in the (still empty) lists
+  static_assert(kRowWaves * G * kWave * 4 <= kRowWaves * kRowCap * 8, "group maxima fit the lists");
+  __shared__ uint64_t s_cand[kRowWaves][kRowCap];
+  __shared__ int32_t s_flag[kRowWaves][kFlagCap];
+  __shared__ uint64_t s_best[kRowWaves * 64];
+  __shared__ uint64_t s_fin[64];
+  __shared__ int s_cnt[kRowWaves];
+  uint32_t* s_gm = reinterpret_cast<uint32_t*>(&s_cand[0][0]);
+
+  char* ring = s_ring + w * S * kSlot;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
+  const uint16_t* lane_p = rowp + l * 8;
+  auto issue = [&](int rd) {
+    const int seg0 = (rd * kRowWaves + w) * kSegLen;
+    const uint32_t slot = ring_lds + static_cast<uint32_t>(rd % S) * kSlot;
+    if (seg0 + kSegLen <= V) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        dma16(lane_p + seg0 + i * (kWave * 8), __builtin_amdgcn_readfirstlane(slot + i * 1024));
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e0 = seg0 + (i * kWave + l) * 8;
+        dma16(rowp + min(e0, V - 8), __builtin_amdgcn_readfirstlane(slot + i * 1024));
+      }
+    }
+  };
+  auto read = [&](int rd, uint32_t (&kw)[NV * 4]) {
+    const int seg0 = (rd * kRowWaves + w) * kSegLen;
+    const char* slot = ring + (rd % S) * kSlot;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint4 v = *reinterpret_cast<const uint4*>(slot + i * 1024 + l * 16);
+      kw[4 * i] = v.x;
+      kw[4 * i + 1] = v.y;
+      kw[4 * i + 2] = v.z;
+      kw[4 * i + 3] = v.w;
+    }
+    if (seg0 + kSegLen > V) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const bool in = seg0 + (i * kWave + l) * 8 < V;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kw[4 * i + q] = in ? kw[4 * i + q] : 0xffffffffu;
+      }
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < S - 1; ++r) issue(r);
+
+  // row-wide bound from the first segments (all -inf for a wave past the end)
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"((S - 2) * NV) : "memory");
+  {
+    uint32_t kw[NV * 4];
+    read(0, kw);
+    uint32_t gmx[G];
+    group_max<NV, G>(kw, gmx);
+#pragma unroll
+    for (int g = 0; g < G; ++g) s_gm[(w * G + g) * kWave + l] = gmx[g];
+  }
+  __syncthreads();
+  const uint32_t t = row_bound<G>(s_gm, K, l);
+  __syncthreads();                          // the lists overwrite the maxima from here on
+
+  int nseg = 0;
+  int nflag = 0;
+  for (int rd = 0; rd < rounds; ++rd) {
+    issue(rd + S - 1);
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"((S - 1) * NV) : "memory");
+    const int seg0 = (rd * kRowWaves + w) * kSegLen;
+    if (seg0 >= V) continue;
+    ++nseg;
+    uint32_t kw[NV * 4];
+    read(rd, kw);
+    row_screen<NV>(kw, seg0, V, l, t, nflag, s_flag[w]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+  const bool exact = nflag > kFlagCap || !row_collect<true>(rowp, V, t, s_flag[w], nflag, l, s_cand[w], cnt);
+  row_finish<NV>(rowp, V, K, rounds, w, l, nseg, exact, cnt, s_cand, s_best, s_fin, s_cnt,
+                 ids + static_cast<size_t>(row) * K, vals + static_cast<size_t>(row) * K);
+}
+
+// Any other bf16 row: element loads, one segment at a time.
+template <int NV, int G>
+__global__ void __launch_bounds__(kRowWaves * kWave)
+topk_bf16_row_unaligned_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds,
+                               int32_t* __restrict__ ids, float* __restrict__ vals) {
+  constexpr int kSegLen = kWave * NV * 8;
+  const int row = blockIdx.x;
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
+
+  static_assert(kRowWaves * G * kWave * 4 <= kRowWaves * kRowCap * 8, "group maxima fit the lists");
+  __shared__ uint64_t s_cand[kRowWaves][kRowCap];
+  __shared__ int32_t s_flag[kRowWaves][kFlagCap];
+  __shared__ uint64_t s_best[kRowWaves * 64];
+  __shared__ uint64_t s_fin[64];
+  __shared__ int s_cnt[kRowWaves];
+  uint32_t* s_gm = reinterpret_cast<uint32_t*>(&s_cand[0][0]);
+
+  auto load = [&](int rd, uint32_t (&kw)[NV * 4]) {
+    const int seg0 = (rd * kRowWaves + w) * kSegLen;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e0 = seg0 + (i * kWave + l) * 8;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = e0 + 2 * q < V ? rowp[e0 + 2 * q] : 0xffffu;
+        const uint32_t hi = e0 + 2 * q + 1 < V ? rowp[e0 + 2 * q + 1] : 0xffffu;
+        kw[4 * i + q] = lo | (hi << 16);
+      }
+    }
+  };
+  {
+    uint32_t kw[NV * 4];
+    load(0, kw);
+    uint32_t gmx[G];
+    group_max<NV, G>(kw, gmx);
+#pragma unroll
+    for (int g = 0; g < G; ++g) s_gm[(w * G + g) * kWave + l] = gmx[g];
+  }
+  __syncthreads();
+  const uint32_t t = row_bound<G>(s_gm, K, l);
+  __syncthreads();
+
+  int nseg = 0;
+  int nflag = 0;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int seg0 = (rd * kRowWaves + w) * kSegLen;
+    if (seg0 >= V) break;
+    ++nseg;
+    uint32_t kw[NV * 4];
+    load(rd, kw);
+    row_screen<NV>(kw, seg0, V, l, t, nflag, s_flag[w]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+  const bool exact = nflag > kFlagCap || !row_collect<false>(rowp, V, t, s_flag[w], nflag, l, s_cand[w], cnt);
+  row_finish<NV>(rowp, V, K, rounds, w, l, nseg, exact, cnt, s_cand, s_best, s_fin, s_cnt,
+                 ids + static_cast<size_t>(row) * K, vals + static_cast<size_t>(row) * K);
 }
 
 template <typename T, int Q>
@@ -585,29 +788,28 @@ hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* p
   if constexpr (std::is_same<T, bf16>::value) {
     const uint16_t* lb = reinterpret_cast<const uint16_t*>(logits);
     const int G = K <= 16 ? 1 : (K <= 32 ? 2 : 4);
-    // vectors per lane: the fewest rounds of 8 waves x 20 vectors, then the
-    // smallest vector count (from 4, 8, 12, 16, 20) that covers the row
-    const int per_round_max = kRowWaves * kWave * 20 * 8;
-    const int rounds = (V + per_round_max - 1) / per_round_max;
-    const int need = (V + rounds * kRowWaves * kWave * 8 - 1) / (rounds * kRowWaves * kWave * 8);
-    const int nv = need <= 4 ? 4 : (need <= 8 ? 8 : (need <= 12 ? 12 : (need <= 16 ? 16 : 20)));
-#define DCOCO_ROW(NVV, GG, VV)                                                                       \
-  hipLaunchKernelGGL((topk_bf16_row_kernel<NVV, GG, VV>), dim3(rows), dim3(kRowWaves * kWave), 0, st, lb, V, \
-                     K, rounds, ids, vals)
-#define DCOCO_ROW_G(NVV, VV)                          \
-  if (G == 1) DCOCO_ROW(NVV, 1, VV);                  \
-  else if (G == 2) DCOCO_ROW(NVV, 2, VV);             \
-  else DCOCO_ROW(NVV, 4, VV)
-#define DCOCO_ROW_NV(VV)                              \
-  if (nv == 4) { DCOCO_ROW_G(4, VV); }                \
-  else if (nv == 8) { DCOCO_ROW_G(8, VV); }           \
-  else if (nv == 12) { DCOCO_ROW_G(12, VV); }         \
-  else if (nv == 16) { DCOCO_ROW_G(16, VV); }         \
-  else { DCOCO_ROW_G(20, VV); }
-    if (vec) { DCOCO_ROW_NV(true) } else { DCOCO_ROW_NV(false) }
-#undef DCOCO_ROW_NV
-#undef DCOCO_ROW_G
+    // aligned rows: 3 vectors per lane and segment, a 2-slot ring per wave
+    // (48 KB of LDS: two workgroups fit a compute unit); other rows: 8
+    // vectors per lane, element loads
+    if (vec) {
+      const int rounds = (V + kRowWaves * kWave * 3 * 8 - 1) / (kRowWaves * kWave * 3 * 8);
+#define DCOCO_ROW(GG)                                                                                   \
+  hipLaunchKernelGGL((topk_bf16_row_kernel<3, GG, 2>), dim3(rows), dim3(kRowWaves * kWave), 0, st, lb, V, K, \
+                     rounds, ids, vals)
+      if (G == 1) DCOCO_ROW(1);
+      else if (G == 2) DCOCO_ROW(2);
+      else DCOCO_ROW(4);
 #undef DCOCO_ROW
+    } else {
+      const int rounds = (V + kRowWaves * kWave * 8 * 8 - 1) / (kRowWaves * kWave * 8 * 8);
+#define DCOCO_ROW(GG)                                                                                 \
+  hipLaunchKernelGGL((topk_bf16_row_unaligned_kernel<8, GG>), dim3(rows), dim3(kRowWaves * kWave), 0, st, lb, \
+                     V, K, rounds, ids, vals)
+      if (G == 1) DCOCO_ROW(1);
+      else if (G == 2) DCOCO_ROW(2);
+      else DCOCO_ROW(4);
+#undef DCOCO_ROW
+    }
     return hipGetLastError();
   } else {
     if (vec)

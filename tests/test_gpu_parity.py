@@ -92,6 +92,9 @@ def _special_rows(V, dtype, seed):
         np.round(g.standard_normal(V) * 2) / 2,             # many ties
         g.standard_normal(V),
     ]
+    rows.append(g.standard_normal(V) - 20.0)                 # all negative (log-probability-like)
+    rows.append(-np.abs(g.standard_normal(V)))               # non-positive, top keys near -0
+    rows.append(np.where(g.random(V) < 0.002, 1.0, -1.0) * g.random(V))  # few positives
     r = g.standard_normal(V)
     r[g.integers(0, V, 40)] = np.nan
     rows.append(r)
