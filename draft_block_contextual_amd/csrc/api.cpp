@@ -127,6 +127,9 @@ hipError_t slot_part(const dcoco_dims* d, const dcoco_weights* w, const void* h,
     q.split = L.split_slot; q.out_f32 = L.Y; q.ldo = ns; q.out = nullptr;
     if ((e = launch_gemm(q, st)) != hipSuccess) return e;
   }
+  if (dt == kDtypeBf16 && ln_gemm_pair_supported(r, rs))
+    return launch_ln_gemm_pair(L.Y, L.split_slot, R, ns, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, d->B, r,
+                               r + rs, rs, s, s3, st);
   if ((e = launch_pair_state(L.Y, L.split_slot, d->n_blocks, d->B, ns, r, r + rs, rs, s, s3, st)) != hipSuccess)
     return e;
   if (dt == kDtypeBf16)

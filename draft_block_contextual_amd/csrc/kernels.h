@@ -60,6 +60,12 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
 
 // s[n, p, :] = sum_s Y[s][n*B+p][cl : cl+rs] + sum_s Y[s][n*B+p+1][cr : cr+rs]
 // s3 (optional): the same values as three bf16 rows hi, mid, lo (s3[q * n + i])
+// gf = W_fg LN(Y[:, 0:r]) plus, in the same launch, the pair states s and
+// their bf16 split (bf16 path; needs ln_gemm_pair_supported)
+bool ln_gemm_pair_supported(int r, int rs);
+hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r, float eps, const void* W,
+                               long long ldw, int wcol0, int N, float* gf, int B, int cl, int cr, int rs, float* s,
+                               void* s3, hipStream_t st);
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
                              int rs, float* s, void* s3, hipStream_t st);
 

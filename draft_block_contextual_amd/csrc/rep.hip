@@ -253,11 +253,21 @@ ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, flo
 constexpr int kLgCols = 256;                 // W rows (output columns) per LDS chunk
 constexpr int kLgRowBytes = 512;             // LDS bytes per W row (k <= 256)
 
-template <int BM, int SPLIT, int MODE>
+// Pair states assembled by the same launch (gf mode): for the workgroup's
+// slot rows m = n B + i with i < B - 1, s_p = Y_L[m] + Y_R[m + 1] (split
+// partials added in order) and its exact three-way bf16 split.
+struct PairArgs {
+  int B, cl, cr, rs;
+  float* s;
+  uint16_t* s3;
+  long long total;      // N (B - 1) rs
+};
+
+template <int BM, int SPLIT, int MODE, bool PAIR>
 __global__ void __launch_bounds__(256)
 ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, float eps,
                  const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
-                 bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div) {
+                 bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div, PairArgs pa) {
   constexpr int kStr = 256 * 2 + 16;         // LDS bytes per normalised row
   constexpr int RPW = BM / 4;                // LN rows per wave
   constexpr int TM = BM / 16;
@@ -343,6 +353,63 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
         pk.y = live ? (static_cast<uint32_t>(f32_to_bf16(d.z * inv)) |
                        (static_cast<uint32_t>(f32_to_bf16(d.w * inv)) << 16)) : 0u;
         *reinterpret_cast<uint2*>(tile + (wv * RPW + q) * kStr + c4 * 2) = pk;
+      }
+    }
+  }
+
+  // ---- pair states of this workgroup's rows (loads in flight with the
+  // weight copy; float4 items of (row, 4 columns), 1024 per batch)
+  if constexpr (PAIR) {
+    const int q4 = pa.rs / 4;
+    const int items = BM * q4;
+    for (int base = 0; base < items; base += 1024) {
+      float4 sum[4];
+      bool ok[4];
+      long long t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int item = base + k * 256 + tid;
+        const int row = item / q4;
+        const int j = (item - row * q4) * 4;
+        const int m = m0 + row;
+        const int i = m % pa.B;
+        ok[k] = item < items && m < M && i < pa.B - 1;
+        // rows past the block's last pair read row 0 (always present) and are not stored
+        const long long mm = ok[k] ? m : 0;
+        const long long mr = ok[k] ? m + 1 : 0;
+        const int jj = ok[k] ? j : 0;
+        float4 a = *reinterpret_cast<const float4*>(x + mm * ldx + pa.cl + jj);
+        float4 b = *reinterpret_cast<const float4*>(x + mr * ldx + pa.cr + jj);
+#pragma unroll
+        for (int s2 = 1; s2 < SPLIT; ++s2) {
+          const float4 a2 = *reinterpret_cast<const float4*>(x + (s2 * static_cast<long long>(M) + mm) * ldx + pa.cl + jj);
+          const float4 b2 = *reinterpret_cast<const float4*>(x + (s2 * static_cast<long long>(M) + mr) * ldx + pa.cr + jj);
+          a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+          b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+        }
+        sum[k] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        t[k] = (static_cast<long long>(m / pa.B) * (pa.B - 1) + i) * pa.rs + j;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (!ok[k]) continue;
+        *reinterpret_cast<float4*>(pa.s + t[k]) = sum[k];
+        if (pa.s3 == nullptr) continue;
+        const float v4[4] = {sum[k].x, sum[k].y, sum[k].z, sum[k].w};
+        uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          hi[c] = f32_to_bf16(v4[c]);
+          const float r1 = v4[c] - bf16_to_f32(hi[c]);
+          mid[c] = f32_to_bf16(r1);
+          lo[c] = f32_to_bf16(r1 - bf16_to_f32(mid[c]));
+        }
+        auto pack4 = [](const uint16_t (&h)[4]) {
+          return make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
+        };
+        *reinterpret_cast<uint2*>(pa.s3 + t[k]) = pack4(hi);
+        *reinterpret_cast<uint2*>(pa.s3 + pa.total + t[k]) = pack4(mid);
+        *reinterpret_cast<uint2*>(pa.s3 + 2 * pa.total + t[k]) = pack4(lo);
       }
     }
   }
@@ -452,8 +519,8 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   else if (split == 2) DCOCO_LNG(BMV, RM, 2, MD);    \
   else DCOCO_LNG(BMV, RM, 4, MD)
 #define DCOCO_LNW(BMV, SP, MD)                                                                      \
-  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, M, \
-                     ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div)
+  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD, false>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, \
+                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div, PairArgs{})
 #define DCOCO_LNW_SPLIT(BMV, MD)                 \
   if (split == 1) DCOCO_LNW(BMV, 1, MD);         \
   else if (split == 2) DCOCO_LNW(BMV, 2, MD);    \
@@ -473,6 +540,28 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
 #undef DCOCO_LNW
 #undef DCOCO_LNG_SPLIT
 #undef DCOCO_LNG
+  return hipGetLastError();
+}
+
+bool ln_gemm_pair_supported(int r, int rs) { return r <= 256 && rs % 4 == 0; }
+
+hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r, float eps, const void* W,
+                               long long ldw, int wcol0, int N, float* gf, int B, int cl, int cr, int rs, float* s,
+                               void* s3, hipStream_t st) {
+  if (!ln_gemm_pair_supported(r, rs) || (split != 1 && split != 2 && split != 4)) return hipErrorInvalidValue;
+  PairArgs pa;
+  pa.B = B; pa.cl = cl; pa.cr = cr; pa.rs = rs;
+  pa.s = s; pa.s3 = static_cast<uint16_t*>(s3);
+  pa.total = static_cast<long long>(M / B) * (B - 1) * rs;
+  const bf16* Wb = static_cast<const bf16*>(W);
+#define DCOCO_LNP(SP)                                                                                    \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, true>), dim3((M + 15) / 16), dim3(256), 0, st, Y, M, ldy, 0, \
+                     r, eps, Wb, ldw, wcol0, N, gf, static_cast<bf16*>(nullptr), static_cast<const float*>(nullptr), \
+                     1, pa)
+  if (split == 1) DCOCO_LNP(1);
+  else if (split == 2) DCOCO_LNP(2);
+  else DCOCO_LNP(4);
+#undef DCOCO_LNP
   return hipGetLastError();
 }
 
