@@ -72,37 +72,48 @@ split3_kernel(const float* __restrict__ s, long long n, uint16_t* __restrict__ s
 // processed in slabs staged in LDS as 2^A', w'A' (per candidate a) and
 // 2^B', w'B' (per candidate b), so one grid element costs an fma, a rcp, an
 // add and an fma.  If some |A'| in a slab exceeds 64 the factors could
-// over/underflow where their product does not; that slab stages A', B' and
-// w' instead and evaluates 2^(A'+B') directly.
+// over/underflow where their product does not; that slab is staged again as
+// A', B' and evaluated with 2^(A'+B') directly.
 //
 // One workgroup (4 waves) per pair; each wave takes a quarter of every slab's
-// units for all K x K outputs: lane (la, lb) of the 8 x 8 lane grid owns
-// a = TA la + i, b = TA lb + j (i, j < TA, K <= 8 TA).  The four waves'
-// partial sums are added in a fixed order at the end.
-template <int TA>
+// units.  A lane owns a TA x TA block of (a, b) outputs; the KR/TA x KR/TA
+// lanes covering all outputs form a group, and a wave holds UPS groups that
+// work on different runs of 4 units, so every 4 units a lane reads 4 TA
+// values per array for 4 TA^2 elements.  The next slab's A and B rows are
+// loaded into registers while the current slab is computed.  The partial
+// sums of the 4 UPS lane groups are added in a fixed order at the end.
+template <int KRV, int TAV>
 struct GridShape {
-  static constexpr int KR = 8 * TA;
+  static constexpr int KR = KRV;                 // candidates, padded
+  static constexpr int TA = TAV;                 // outputs per lane along a and b
+  static constexpr int LPU = (KR / TA) * (KR / TA);   // lanes per group
+  static constexpr int UPS = kWave / LPU;        // groups per wave
   static constexpr int HS = 4096 / KR;           // hidden units per slab
   static constexpr int STR = HS + 4;             // LDS row stride (floats)
   static constexpr int ARR = KR * STR;
-  static constexpr int kRed = 4 * KR * KR;
-  static constexpr int kSmem = (4 * ARR > kRed ? 4 * ARR : kRed) + 2 * HS;
+  static constexpr int NLD = KR * HS / 4 / 256;  // float4 per thread per operand and slab
+  static constexpr int kRed = 4 * UPS * KR * KR;
+  static constexpr int kSmem = (4 * ARR > kRed ? 4 * ARR : kRed) + 4 * HS;
+  static_assert(LPU * UPS == kWave && NLD * 1024 == KR * HS, "grid shape");
+  static_assert(kRed <= kSmem, "reduction fits");
 };
 
-template <typename T, int TA>
+template <typename T, typename GS>
 __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
-  using GS = GridShape<TA>;
   constexpr int KR = GS::KR;
+  constexpr int TA = GS::TA;
   constexpr int HS = GS::HS;
   constexpr int STR = GS::STR;
+  constexpr int NLD = GS::NLD;
+  constexpr int UPS = GS::UPS;
   __shared__ __align__(16) float smem[GS::kSmem];
-  __shared__ int s_slow;
+  __shared__ int s_slow[2];
   float* arr0 = smem;                 // 2^A'  (or A')
   float* arr1 = smem + GS::ARR;       // w'A'
   float* arr2 = smem + 2 * GS::ARR;   // 2^B'  (or B')
   float* arr3 = smem + 3 * GS::ARR;   // w'B'
-  float* sCp = smem + 4 * GS::ARR;    // per unit: -log2(e) (C_p + b1)
-  float* sWp = sCp + HS;              // per unit: w'
+  float* sCp = smem + 4 * GS::ARR;    // [2][HS] per unit: -log2(e) (C_p + b1)
+  float* sWp = sCp + 2 * HS;          // [2][HS] per unit: w'
 
   const int np = blockIdx.x;
   const int Bm1 = g.B - 1;
@@ -119,8 +130,37 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wv = tid >> 6;
-  const int la = l >> 3;
-  const int lb = l & 7;
+  const int grp = l / GS::LPU;
+  const int gi = l % GS::LPU;
+  const int la = gi / (KR / TA);
+  const int lb = gi % (KR / TA);
+
+  // slab rows in registers: item k of thread tid is (row, 4 units) of the
+  // slab's KR x HS block; rows >= K and units past H read as zero
+  float4 pa[NLD], pb[NLD];
+  auto fetch = [&](int hs0) {
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int idx = tid + 256 * k;
+      const int row = idx / (HS / 4);
+      const int h = hs0 + (idx % (HS / 4)) * 4;
+      const bool ok = row < K && h < H;
+      pa[k] = ok ? *reinterpret_cast<const float4*>(Arow + row * ldab + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+      pb[k] = ok ? *reinterpret_cast<const float4*>(Brow + row * ldab + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto stage_c = [&](int hs0, int cb) {
+    for (int h = tid; h < HS; h += 256) {
+      float c = 0.f, wq = 0.f;
+      if (hs0 + h < H) {
+        for (int q = 0; q < g.nq; ++q) c += g.C[(static_cast<long long>(q) * g.P + np) * H + hs0 + h];
+        if (b1) c += Elem<T>::to_f32(b1[hs0 + h]);
+        wq = kNegLn2 * Elem<T>::to_f32(w2[hs0 + h]);
+      }
+      sCp[cb * HS + h] = kNegLog2e * c;
+      sWp[cb * HS + h] = wq;
+    }
+  };
 
   float acc[TA][TA];
 #pragma unroll
@@ -128,63 +168,71 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
 #pragma unroll
     for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
 
-  for (int hs0 = 0; hs0 < H; hs0 += HS) {
+  fetch(0);
+  stage_c(0, 0);
+  if (tid == 0) s_slow[0] = 0;
+  __syncthreads();
+  int cb = 0;
+  for (int hs0 = 0; hs0 < H; hs0 += HS, cb ^= 1) {
     const int hlen = min(HS, H - hs0);
-    // ---- stage the slab
-    if (tid == 0) s_slow = 0;
-    for (int h = tid; h < hlen; h += 256) {
-      float c = 0.f;
-      for (int q = 0; q < g.nq; ++q) c += g.C[(static_cast<long long>(q) * g.P + np) * H + hs0 + h];
-      if (b1) c += Elem<T>::to_f32(b1[hs0 + h]);
-      sCp[h] = kNegLog2e * c;
-      sWp[h] = kNegLn2 * Elem<T>::to_f32(w2[hs0 + h]);
-    }
-    __syncthreads();
+    const float* cp = sCp + cb * HS;
+    const float* wp = sWp + cb * HS;
+    // ---- stage the slab (fast form) from registers
     bool big = false;
-    const int q4 = hlen / 4;
-    for (int idx = tid; idx < KR * q4; idx += 256) {
-      const int row = idx / q4;
-      const int h = (idx - row * q4) * 4;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (row < K) {
-        a = *reinterpret_cast<const float4*>(Arow + row * ldab + hs0 + h);
-        b = *reinterpret_cast<const float4*>(Brow + row * ldab + hs0 + h);
-      }
-      const float4 cp = *reinterpret_cast<const float4*>(sCp + h);
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int idx = tid + 256 * k;
+      const int row = idx / (HS / 4);
+      const int h = (idx % (HS / 4)) * 4;
+      const float4 c4 = *reinterpret_cast<const float4*>(cp + h);
+      const float4 w4 = *reinterpret_cast<const float4*>(wp + h);
+      float4 a = pa[k], b = pb[k];
       a.x *= kNegLog2e; a.y *= kNegLog2e; a.z *= kNegLog2e; a.w *= kNegLog2e;
-      b.x = fmaf(kNegLog2e, b.x, cp.x); b.y = fmaf(kNegLog2e, b.y, cp.y);
-      b.z = fmaf(kNegLog2e, b.z, cp.z); b.w = fmaf(kNegLog2e, b.w, cp.w);
+      b.x = fmaf(kNegLog2e, b.x, c4.x); b.y = fmaf(kNegLog2e, b.y, c4.y);
+      b.z = fmaf(kNegLog2e, b.z, c4.z); b.w = fmaf(kNegLog2e, b.w, c4.w);
       big |= fabsf(a.x) > 64.f || fabsf(a.y) > 64.f || fabsf(a.z) > 64.f || fabsf(a.w) > 64.f;
-      *reinterpret_cast<float4*>(arr0 + row * STR + h) = a;
-      *reinterpret_cast<float4*>(arr2 + row * STR + h) = b;
+      *reinterpret_cast<float4*>(arr1 + row * STR + h) = make_float4(w4.x * a.x, w4.y * a.y, w4.z * a.z, w4.w * a.w);
+      *reinterpret_cast<float4*>(arr3 + row * STR + h) = make_float4(w4.x * b.x, w4.y * b.y, w4.z * b.z, w4.w * b.w);
+      *reinterpret_cast<float4*>(arr0 + row * STR + h) =
+          make_float4(__builtin_amdgcn_exp2f(a.x), __builtin_amdgcn_exp2f(a.y), __builtin_amdgcn_exp2f(a.z),
+                      __builtin_amdgcn_exp2f(a.w));
+      *reinterpret_cast<float4*>(arr2 + row * STR + h) =
+          make_float4(__builtin_amdgcn_exp2f(b.x), __builtin_amdgcn_exp2f(b.y), __builtin_amdgcn_exp2f(b.z),
+                      __builtin_amdgcn_exp2f(b.w));
     }
-    if (big) s_slow = 1;
+    if (big) s_slow[cb] = 1;
+    // ---- next slab: rows into registers, per-unit terms into the other buffer
+    if (hs0 + HS < H) {
+      fetch(hs0 + HS);
+      stage_c(hs0 + HS, cb ^ 1);
+    }
+    if (tid == 0) s_slow[cb ^ 1] = 0;
     __syncthreads();
-    const bool slow = s_slow != 0;
-    if (!slow) {
-      for (int idx = tid; idx < KR * q4; idx += 256) {
-        const int row = idx / q4;
-        const int h = (idx - row * q4) * 4;
-        const float4 wq = *reinterpret_cast<const float4*>(sWp + h);
-        float4 a = *reinterpret_cast<const float4*>(arr0 + row * STR + h);
-        float4 b = *reinterpret_cast<const float4*>(arr2 + row * STR + h);
-        *reinterpret_cast<float4*>(arr1 + row * STR + h) = make_float4(wq.x * a.x, wq.y * a.y, wq.z * a.z, wq.w * a.w);
-        *reinterpret_cast<float4*>(arr3 + row * STR + h) = make_float4(wq.x * b.x, wq.y * b.y, wq.z * b.z, wq.w * b.w);
-        a.x = __builtin_amdgcn_exp2f(a.x); a.y = __builtin_amdgcn_exp2f(a.y);
-        a.z = __builtin_amdgcn_exp2f(a.z); a.w = __builtin_amdgcn_exp2f(a.w);
-        b.x = __builtin_amdgcn_exp2f(b.x); b.y = __builtin_amdgcn_exp2f(b.y);
-        b.z = __builtin_amdgcn_exp2f(b.z); b.w = __builtin_amdgcn_exp2f(b.w);
+    const bool slow = s_slow[cb] != 0;
+    if (slow) {
+      // rare: stage A' and B' themselves (read again from memory)
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) {
+        const int idx = tid + 256 * k;
+        const int row = idx / (HS / 4);
+        const int h = (idx % (HS / 4)) * 4;
+        const bool ok = row < K && hs0 + h < H;
+        float4 a = ok ? *reinterpret_cast<const float4*>(Arow + row * ldab + hs0 + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 b = ok ? *reinterpret_cast<const float4*>(Brow + row * ldab + hs0 + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 c4 = *reinterpret_cast<const float4*>(cp + h);
+        a.x *= kNegLog2e; a.y *= kNegLog2e; a.z *= kNegLog2e; a.w *= kNegLog2e;
+        b.x = fmaf(kNegLog2e, b.x, c4.x); b.y = fmaf(kNegLog2e, b.y, c4.y);
+        b.z = fmaf(kNegLog2e, b.z, c4.z); b.w = fmaf(kNegLog2e, b.w, c4.w);
         *reinterpret_cast<float4*>(arr0 + row * STR + h) = a;
         *reinterpret_cast<float4*>(arr2 + row * STR + h) = b;
       }
       __syncthreads();
     }
-    // ---- this wave's quarter of the slab
-    const int h_beg = wv * q4;
-    const int h_end = h_beg + q4;
+    // ---- this wave's quarter of the slab, runs of 4 units per lane group
+    const int q4 = hlen / 4;
+    const int h_end = wv * q4 + q4;
     if (!slow) {
-#pragma unroll 2
-      for (int h = h_beg; h < h_end; h += 4) {
+      for (int h = wv * q4 + 4 * grp; h < h_end; h += 4 * UPS) {
         float4 ea[TA], wa[TA], eb[TA], wb[TA];
 #pragma unroll
         for (int i = 0; i < TA; ++i) {
@@ -205,14 +253,14 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
             }
       }
     } else {
-      for (int h = h_beg; h < h_end; h += 4) {
+      for (int h = wv * q4 + 4 * grp; h < h_end; h += 4 * UPS) {
         float4 av[TA], bv[TA];
 #pragma unroll
         for (int i = 0; i < TA; ++i) {
           av[i] = *reinterpret_cast<const float4*>(arr0 + (la * TA + i) * STR + h);
           bv[i] = *reinterpret_cast<const float4*>(arr2 + (lb * TA + i) * STR + h);
         }
-        const float4 wq = *reinterpret_cast<const float4*>(sWp + h);
+        const float4 wq = *reinterpret_cast<const float4*>(wp + h);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -227,12 +275,13 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
     }
     __syncthreads();
   }
-  // ---- add the four waves' partial sums in a fixed order
+  // ---- add the 4 UPS partial sums per output in a fixed order
   float* red = smem;
+  const int slot = wv * UPS + grp;
 #pragma unroll
   for (int i = 0; i < TA; ++i)
 #pragma unroll
-    for (int j = 0; j < TA; ++j) red[(wv * KR + la * TA + i) * KR + lb * TA + j] = acc[i][j];
+    for (int j = 0; j < TA; ++j) red[(slot * KR + la * TA + i) * KR + lb * TA + j] = acc[i][j];
   __syncthreads();
   const float* lnext = g.cand_logits + (static_cast<long long>(n) * g.B + p + 1) * K;
   float* Sp = g.S + static_cast<long long>(np) * K * K;
@@ -240,7 +289,8 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
     const int a = idx / K;
     const int b = idx - a * K;
     const int o = a * KR + b;
-    const float sum = ((red[o] + red[KR * KR + o]) + red[2 * KR * KR + o]) + red[3 * KR * KR + o];
+    float sum = red[o];
+    for (int sl = 1; sl < 4 * UPS; ++sl) sum += red[sl * KR * KR + o];
     Sp[idx] = lnext[b] + (sum + g.b2);
   }
 }
@@ -337,11 +387,11 @@ hipError_t launch_grid_t(const GridProblem& q, hipStream_t st) {
   g.cand_logits = q.cand_logits; g.S = q.S;
   const int blocks = q.N * (q.B - 1);
   if (blocks <= 0) return hipSuccess;
-#define DCOCO_GRID(TAV) hipLaunchKernelGGL((grid_kernel<T, TAV>), dim3(blocks), dim3(256), 0, st, g)
-  if (q.K <= 8) DCOCO_GRID(1);
-  else if (q.K <= 16) DCOCO_GRID(2);
-  else if (q.K <= 32) DCOCO_GRID(4);
-  else DCOCO_GRID(8);
+#define DCOCO_GRID(KRV, TAV) hipLaunchKernelGGL((grid_kernel<T, GridShape<KRV, TAV>>), dim3(blocks), dim3(256), 0, st, g)
+  if (q.K <= 8) DCOCO_GRID(8, 2);
+  else if (q.K <= 16) DCOCO_GRID(16, 4);
+  else if (q.K <= 32) DCOCO_GRID(32, 4);
+  else DCOCO_GRID(64, 8);
 #undef DCOCO_GRID
   return hipGetLastError();
 }
