@@ -334,7 +334,7 @@ walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int
             int B, int K, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_tok) {
   __shared__ __align__(16) float sS[kWalkLds];
   __shared__ __align__(16) int32_t sI[kWalkIds];
-  __shared__ __align__(16) float sC[kWave];
+  __shared__ __align__(16) float sC[kWave + 4];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -345,19 +345,43 @@ walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int
   const int32_t* idn = ids + static_cast<long long>(n) * B * K;
   int32_t* si = sel_idx ? sel_idx + static_cast<long long>(n) * B : nullptr;
   int32_t* stok = sel_tok + static_cast<long long>(n) * B;
-  const bool vec = ((reinterpret_cast<uintptr_t>(Sn) & 15) == 0) && (per % 4 == 0);
-  const bool vec_id = ((reinterpret_cast<uintptr_t>(idn) & 15) == 0) && (K % 4 == 0);
+  const bool vec = ((reinterpret_cast<uintptr_t>(Sn) & 15) == 0) && (per % 4 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(idn) & 15) == 0) && (K % 4 == 0);
   int k = 0;
   for (int p0 = 0;; p0 += batch) {
     const int cnt = max(0, min(batch, Bm1 - p0));
     __syncthreads();
     const float* src = Sn + static_cast<long long>(p0) * per;
-    if (vec) walk_stage<float, float4>(sS, src, cnt * per, tid);
-    else walk_stage<float, float>(sS, src, cnt * per, tid);
-    // ids of slots p0 .. p0 + cnt
-    if (vec_id) walk_stage<int32_t, int4>(sI, idn + static_cast<long long>(p0) * K, (cnt + 1) * K, tid);
-    else walk_stage<int32_t, int32_t>(sI, idn + static_cast<long long>(p0) * K, (cnt + 1) * K, tid);
-    if (p0 == 0 && tid < K) sC[tid] = cl[static_cast<long long>(n) * B * K + tid];
+    const int32_t* isrc = idn + static_cast<long long>(p0) * K;
+    const int ns = cnt * per;
+    const int ni = (cnt + 1) * K;
+    if (vec && ns >= 4 && ns <= 4096 && ni <= 1024) {
+      // one round: up to 4 float4 of scores, one int4 of ids and one logit per
+      // thread.  The loads are unconditional (out-of-range threads re-read
+      // element 0) so they are all in flight before the first wait.
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;
+        v[j] = reinterpret_cast<const float4*>(src)[idx * 4 < ns ? idx : 0];
+      }
+      const int4 iv = reinterpret_cast<const int4*>(isrc)[tid * 4 < ni ? tid : 0];
+      const float c0 = cl[static_cast<long long>(n) * B * K + (tid < K ? tid : 0)];
+      // stores without branches: out-of-range threads write a spare slot
+      // past the staged data (float4 1023: ns <= 4092 whenever some thread is
+      // out of range; int4 271: ni <= 1024; sC[64])
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;
+        reinterpret_cast<float4*>(sS)[idx * 4 < ns ? idx : 1023] = v[j];
+      }
+      reinterpret_cast<int4*>(sI)[tid * 4 < ni ? tid : kWalkIds / 4 - 1] = iv;
+      sC[p0 == 0 && tid < K ? tid : kWave] = c0;
+    } else {
+      walk_stage<float, float>(sS, src, ns, tid);
+      walk_stage<int32_t, int32_t>(sI, isrc, ni, tid);
+      if (p0 == 0 && tid < K) sC[tid] = cl[static_cast<long long>(n) * B * K + tid];
+    }
     __syncthreads();
     if (tid < kWave) {
       if (p0 == 0) {
