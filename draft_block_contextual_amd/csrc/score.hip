@@ -136,29 +136,37 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
   const int lb = gi % (KR / TA);
 
   // slab rows in registers: item k of thread tid is (row, 4 units) of the
-  // slab's KR x HS block; rows >= K and units past H read as zero
+  // slab's KR x HS block.  The loads are unconditional (row and unit clamped
+  // into the pair's data) so none of them waits for another; rows >= K and
+  // units past H are zeroed when the slab is staged.
   float4 pa[NLD], pb[NLD];
   auto fetch = [&](int hs0) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int idx = tid + 256 * k;
-      const int row = idx / (HS / 4);
-      const int h = hs0 + (idx % (HS / 4)) * 4;
-      const bool ok = row < K && h < H;
-      pa[k] = ok ? *reinterpret_cast<const float4*>(Arow + row * ldab + h) : make_float4(0.f, 0.f, 0.f, 0.f);
-      pb[k] = ok ? *reinterpret_cast<const float4*>(Brow + row * ldab + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int row = min(idx / (HS / 4), K - 1);
+      const int h = min(hs0 + (idx % (HS / 4)) * 4, H - 4);
+      pa[k] = *reinterpret_cast<const float4*>(Arow + row * ldab + h);
+      pb[k] = *reinterpret_cast<const float4*>(Brow + row * ldab + h);
     }
   };
+  // per-unit terms of a slab; the loads are unconditional (clamped unit,
+  // clamped part index) so they are all in flight before the first wait
   auto stage_c = [&](int hs0, int cb) {
     for (int h = tid; h < HS; h += 256) {
-      float c = 0.f, wq = 0.f;
-      if (hs0 + h < H) {
-        for (int q = 0; q < g.nq; ++q) c += g.C[(static_cast<long long>(q) * g.P + np) * H + hs0 + h];
-        if (b1) c += Elem<T>::to_f32(b1[hs0 + h]);
-        wq = kNegLn2 * Elem<T>::to_f32(w2[hs0 + h]);
-      }
-      sCp[cb * HS + h] = kNegLog2e * c;
-      sWp[cb * HS + h] = wq;
+      const bool in = hs0 + h < H;
+      const int hh = in ? hs0 + h : H - 1;
+      float cq[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) cq[q] = g.C[(static_cast<long long>(min(q, g.nq - 1)) * g.P + np) * H + hh];
+      const float bb = b1 ? Elem<T>::to_f32(b1[hh]) : 0.f;
+      const float ww = Elem<T>::to_f32(w2[hh]);
+      float c = cq[0];
+      if (g.nq > 1) c += cq[1];
+      if (g.nq > 2) c += cq[2];
+      c += bb;
+      sCp[cb * HS + h] = in ? kNegLog2e * c : 0.f;
+      sWp[cb * HS + h] = in ? kNegLn2 * ww : 0.f;
     }
   };
 
@@ -168,8 +176,8 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
 #pragma unroll
     for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
 
-  fetch(0);
   stage_c(0, 0);
+  fetch(0);
   if (tid == 0) s_slow[0] = 0;
   __syncthreads();
   int cb = 0;
@@ -186,7 +194,9 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
       const int h = (idx % (HS / 4)) * 4;
       const float4 c4 = *reinterpret_cast<const float4*>(cp + h);
       const float4 w4 = *reinterpret_cast<const float4*>(wp + h);
-      float4 a = pa[k], b = pb[k];
+      const bool ok = row < K && hs0 + h < H;
+      float4 a = ok ? pa[k] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 b = ok ? pb[k] : make_float4(0.f, 0.f, 0.f, 0.f);
       a.x *= kNegLog2e; a.y *= kNegLog2e; a.z *= kNegLog2e; a.w *= kNegLog2e;
       b.x = fmaf(kNegLog2e, b.x, c4.x); b.y = fmaf(kNegLog2e, b.y, c4.y);
       b.z = fmaf(kNegLog2e, b.z, c4.z); b.w = fmaf(kNegLog2e, b.w, c4.w);
@@ -203,8 +213,9 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
     if (big) s_slow[cb] = 1;
     // ---- next slab: rows into registers, per-unit terms into the other buffer
     if (hs0 + HS < H) {
-      fetch(hs0 + HS);
+      // the per-unit terms first: waiting for them must not wait for the rows
       stage_c(hs0 + HS, cb ^ 1);
+      fetch(hs0 + HS);
     }
     if (tid == 0) s_slow[cb ^ 1] = 0;
     __syncthreads();
