@@ -23,7 +23,8 @@ DTYPE_CODE = {"f32": 0, "bf16": 1}
 
 # every entry point include/dcoco.h declares
 EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select",
-           "dcoco_correct_block", "dcoco_status_string", "dcoco_abi_version"]
+           "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
+           "dcoco_status_string", "dcoco_abi_version"]
 
 
 class DcocoError(RuntimeError):
@@ -64,7 +65,10 @@ def load() -> ctypes.CDLL:
     lib.dcoco_score.argtypes = [pd, pw, vp, vp, vp, vp, vp, sz, vp]
     lib.dcoco_select.argtypes = [pd, vp, vp, vp, vp, vp, vp]
     lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
-    for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_correct_block"]:
+    lib.dcoco_build_btable.argtypes = [pd, pw, vp, vp, vp, sz, vp]
+    lib.dcoco_correct_block_btable.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
+    for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_correct_block",
+              "dcoco_build_btable", "dcoco_correct_block_btable"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.dcoco_status_string.argtypes = [ctypes.c_int]
     lib.dcoco_status_string.restype = ctypes.c_char_p
@@ -229,20 +233,38 @@ def select(dims: Dims, S, cand_logits, cand_ids, sel_idx=None, sel_tok=None, str
     return sel_idx, sel_tok
 
 
-def correct_block_workspace_bytes(dims: Dims, w: Weights) -> int:
+def correct_block_workspace_bytes(dims: Dims, w: Weights, btable: bool = False) -> int:
     lib = load()
     cd, cw = dims.c(), w.c()
     n = ctypes.c_size_t(0)
-    _check("dcoco_correct_block", lib.dcoco_correct_block(
-        ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, ctypes.byref(n),
-        None, None, None, None, None, None))
+    fn = lib.dcoco_correct_block_btable if btable else lib.dcoco_correct_block
+    _check(fn.__name__, fn(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, ctypes.byref(n),
+                           None, None, None, None, None, None))
     return n.value
 
 
+def build_btable(dims: Dims, w: Weights, E, table=None, workspace=None, stream=None):
+    """dcoco_build_btable: the [V, d_proj] bf16 table of LN(P_e E_v)."""
+    import torch
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    dev = E.device
+    if table is None:
+        table = torch.empty((dims.V, dims.d_proj), dtype=torch.bfloat16, device=dev)
+    args = (ctypes.byref(cd), ctypes.byref(cw), _ptr(E), _ptr(table))
+    need = _query(lib.dcoco_build_btable, *args)
+    ws = _workspace(need, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_build_btable", lib.dcoco_build_btable(*args, _ptr(ws), ctypes.byref(n), _stream(stream)))
+    return table
+
+
 def correct_block(dims: Dims, w: Weights, logits, h, E, sel_tok=None, sel_idx=None, S=None,
-                  cand_ids=None, cand_logits=None, want_all: bool = False, workspace=None, stream=None):
-    """dcoco_correct_block.  Returns a dict with sel_tok (and, when asked for or
-    passed in, sel_idx, S, cand_ids, cand_logits)."""
+                  cand_ids=None, cand_logits=None, want_all: bool = False, workspace=None, stream=None,
+                  btable=None):
+    """dcoco_correct_block (dcoco_correct_block_btable when btable, a table from
+    build_btable, is given; E is then not used).  Returns a dict with sel_tok
+    (and, when asked for or passed in, sel_idx, S, cand_ids, cand_logits)."""
     import torch
     lib = load()
     cd, cw = dims.c(), w.c()
@@ -259,11 +281,13 @@ def correct_block(dims: Dims, w: Weights, logits, h, E, sel_tok=None, sel_idx=No
             cand_ids = torch.empty((N, B, K), dtype=torch.int32, device=dev)
         if cand_logits is None:
             cand_logits = torch.empty((N, B, K), dtype=torch.float32, device=dev)
-    need = correct_block_workspace_bytes(dims, w)
+    need = correct_block_workspace_bytes(dims, w, btable is not None)
     ws = _workspace(need, dev, workspace)
     n = ctypes.c_size_t(ws.numel())
-    _check("dcoco_correct_block", lib.dcoco_correct_block(
-        ctypes.byref(cd), ctypes.byref(cw), _ptr(logits), _ptr(h), _ptr(E), _ptr(ws), ctypes.byref(n),
+    fn = lib.dcoco_correct_block if btable is None else lib.dcoco_correct_block_btable
+    src = E if btable is None else btable
+    _check(fn.__name__, fn(
+        ctypes.byref(cd), ctypes.byref(cw), _ptr(logits), _ptr(h), _ptr(src), _ptr(ws), ctypes.byref(n),
         _ptr(sel_tok), _ptr(sel_idx), _ptr(S), _ptr(cand_ids), _ptr(cand_logits), _stream(stream)))
     out = {"sel_tok": sel_tok}
     if sel_idx is not None:

@@ -87,7 +87,8 @@ struct RepLayout {
   void* b;        // [R K][r]
 };
 
-RepLayout carve_rep(Carve& c, const dcoco_dims* d) {
+// cand = false: no buffers for the gathered projection (table path)
+RepLayout carve_rep(Carve& c, const dcoco_dims* d, bool cand = true) {
   RepLayout L;
   const int R = d->n_blocks * d->B;
   const int RK = R * d->K;
@@ -96,10 +97,11 @@ RepLayout carve_rep(Carve& c, const dcoco_dims* d) {
   L.split_slot = gemm_pick_split(R, ns, d->d_hidden, dt, dt);
   L.split_cand = gemm_pick_split(RK, d->d_proj, d->d_embed, dt, dt);
   L.Y = static_cast<float*>(c.take(sizeof(float) * L.split_slot * static_cast<size_t>(R) * ns));
-  L.U = static_cast<float*>(c.take(sizeof(float) * L.split_cand * static_cast<size_t>(RK) * d->d_proj));
+  L.U = cand ? static_cast<float*>(c.take(sizeof(float) * L.split_cand * static_cast<size_t>(RK) * d->d_proj))
+             : nullptr;
   L.g = c.take(esize(d->dtype) * static_cast<size_t>(R) * d->d_proj);
   L.gf = static_cast<float*>(c.take(sizeof(float) * static_cast<size_t>(R) * d->d_z));
-  L.b = c.take(esize(d->dtype) * static_cast<size_t>(RK) * d->d_proj);
+  L.b = cand ? c.take(esize(d->dtype) * static_cast<size_t>(RK) * d->d_proj) : nullptr;
   return L;
 }
 
@@ -269,6 +271,8 @@ hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z,
   return score_tail(d, w, z, cl, S, L, st);
 }
 
+constexpr int kTableChunk = 8192;   // table rows projected per launch pair
+
 int check_ws(void* ws, size_t* bytes, size_t need) {
   if (!bytes) return DCOCO_ERR_INVALID_ARG;
   need = need < kAlign ? kAlign : need;   // never 0: NULL always means "size query"
@@ -284,7 +288,7 @@ int check_ws(void* ws, size_t* bytes, size_t need) {
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 100; }
+int dcoco_abi_version(void) { return 101; }
 
 const char* dcoco_status_string(int status) {
   switch (status) {
@@ -405,6 +409,93 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
   if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
+  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st);
+  if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
+  return hip_status(e);
+}
+
+int dcoco_build_btable(const dcoco_dims* d, const dcoco_weights* w, const void* E, void* table,
+                       void* workspace, size_t* workspace_bytes, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  if (d->dtype != DCOCO_BF16 || !gather_gemm_supported(d->d_proj)) return DCOCO_ERR_UNSUPPORTED;
+  const int dt = kDtypeBf16;
+  const int r = d->d_proj;
+  const int chunk = d->V < kTableChunk ? d->V : kTableChunk;
+  // room for the largest split any chunk can pick (4)
+  const size_t need = sizeof(float) * 4 * static_cast<size_t>(chunk) * r;
+  rc = check_ws(workspace, workspace_bytes, need);
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if (!w || !ptr_ok(w->P_e) || !ptr_ok(E) || !ptr_ok(table)) return DCOCO_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  float* U = static_cast<float*>(workspace);
+  hipError_t e = hipSuccess;
+  for (int v0 = 0; v0 < d->V && e == hipSuccess; v0 += chunk) {
+    const int M = d->V - v0 < chunk ? d->V - v0 : chunk;
+    GemmProblem q{};
+    q.M = M; q.N = r; q.Kd = d->d_embed;
+    q.A = static_cast<const uint16_t*>(E) + static_cast<size_t>(v0) * d->d_embed; q.lda = d->d_embed;
+    q.a_rows = nullptr; q.a_dtype = dt;
+    q.w[0] = w->P_e; q.ldw[0] = d->d_embed; q.col0[0] = 0; q.seg_end[0] = r;
+    q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = r;
+    q.w_dtype = dt;
+    q.split = gemm_pick_split(M, r, d->d_embed, dt, dt); q.out_f32 = U; q.ldo = r; q.out = nullptr;
+    e = launch_gemm(q, st);
+    if (e == hipSuccess)
+      e = launch_ln_rows(U, q.split, M, r, 0, r, d->ln_eps, static_cast<uint16_t*>(table) + static_cast<size_t>(v0) * r,
+                         dt, st);
+  }
+  return hip_status(e);
+}
+
+int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h,
+                               const void* btable, void* workspace, size_t* workspace_bytes, int32_t* sel_tok,
+                               int32_t* sel_idx, float* S_out, int32_t* cand_ids_out, float* cand_logits_out,
+                               void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  if (d->dtype != DCOCO_BF16 || !gather_gemm_supported(d->d_proj)) return DCOCO_ERR_UNSUPPORTED;
+  const int dt = kDtypeBf16;
+  if (!topk_supported(dt, d->V, d->K)) return DCOCO_ERR_UNSUPPORTED;
+  const int R = d->n_blocks * d->B;
+  const size_t RK = static_cast<size_t>(R) * d->K;
+  const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
+  auto layout = [&](Carve& c, void** topk_ws, int32_t** ids, float** cl, RepLayout* L, void** z,
+                    float** s, float** S, ScoreLayout* SL) {
+    *topk_ws = c.take(topk_workspace_bytes(dt, R, d->V, d->K));
+    *ids = static_cast<int32_t*>(c.take(sizeof(int32_t) * RK));
+    *cl = static_cast<float*>(c.take(sizeof(float) * RK));
+    *L = carve_rep(c, d, false);
+    *z = c.take(esize(d->dtype) * RK * d->d_z);
+    *s = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_pair));
+    *S = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->K * d->K));
+    *SL = carve_score(c, d);
+  };
+  void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* S; ScoreLayout SL;
+  {
+    Carve c(nullptr);
+    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
+    rc = check_ws(workspace, workspace_bytes, c.off);
+    if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  }
+  if ((rc = check_weights(w, false, true)) != DCOCO_OK) return rc;
+  if (!ptr_ok(w->P_h) || !ptr_ok(w->W_f) || !ptr_ok(w->W_pair)) return DCOCO_ERR_INVALID_ARG;
+  if (!ptr_ok(logits) || !ptr_ok(h) || !ptr_ok(btable) || !ptr_ok(sel_tok)) return DCOCO_ERR_INVALID_ARG;
+  if (!opt_ok(sel_idx) || !opt_ok(S_out) || !opt_ok(cand_ids_out) || !opt_ok(cand_logits_out))
+    return DCOCO_ERR_INVALID_ARG;
+  Carve cw(workspace);
+  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
+  if (cand_ids_out) ids = cand_ids_out;
+  if (cand_logits_out) cl = cand_logits_out;
+  if (S_out) S = S_out;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int r = d->d_proj;
+  hipError_t e = slot_part(d, w, h, s, SL.s3, L, st);
+  if (e == hipSuccess) e = pair_term(d, w, s, SL, true, st);
+  if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
+  if (e == hipSuccess)
+    e = launch_gather_gemm(btable, ids, d->V - 1, static_cast<int>(RK), r, w->W_f, 2ll * r, 0, d->d_z, z, L.gf,
+                           d->K, st);
   if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st);
   if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
   return hip_status(e);

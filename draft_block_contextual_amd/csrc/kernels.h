@@ -66,6 +66,12 @@ bool ln_gemm_pair_supported(int r, int rs);
 hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r, float eps, const void* W,
                                long long ldw, int wcol0, int N, float* gf, int B, int cl, int cr, int rs, float* s,
                                void* s3, hipStream_t st);
+// z rows from a table of normalised projections (bf16): out = W[:, wcol0 .. +r]
+// tab[ids[m]] + row_bias[m / row_div], bf16 out [M][N]
+bool gather_gemm_supported(int r);
+hipError_t launch_gather_gemm(const void* tab, const int32_t* ids, int idmax, int M, int r, const void* W,
+                              long long ldw, int wcol0, int N, void* out_bf, const float* row_bias, int row_div,
+                              hipStream_t st);
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
                              int rs, float* s, void* s3, hipStream_t st);
 

@@ -10,6 +10,7 @@
 #include "dma.h"
 #include "kernels.h"
 #include "wave.h"
+#include "ln_tile.h"
 
 namespace dcoco {
 
@@ -263,11 +264,20 @@ struct PairArgs {
   long long total;      // N (B - 1) rs
 };
 
-template <int BM, int SPLIT, int MODE, bool PAIR>
+// Rows taken from a bf16 table instead of normalised here (GATHER mode): row
+// m of the operand is table row ids[m] (clamped into [0, idmax]), r values.
+struct GatherArgs {
+  const uint16_t* tab;
+  const int32_t* ids;
+  int idmax;
+};
+
+template <int BM, int SPLIT, int MODE, bool PAIR, bool GATHER = false>
 __global__ void __launch_bounds__(256)
 ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, float eps,
                  const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
-                 bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div, PairArgs pa) {
+                 bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div, PairArgs pa,
+                 GatherArgs ga) {
   constexpr int kStr = 256 * 2 + 16;         // LDS bytes per normalised row
   constexpr int RPW = BM / 4;                // LN rows per wave
   constexpr int TM = BM / 16;
@@ -315,46 +325,33 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
   };
   if constexpr (MODE == 1) load_bias(0);
 
-  // ---- LayerNorm of rows m0 + wv * RPW + q into the tile (bf16).  Loads are
-  // unconditional (lanes past r re-read column 0 and are zeroed), so all of
-  // them are in flight before the first wait.
-  {
-    const int c4 = 4 * l;
-    const bool on = c4 < r;
-    const int cc = on ? c4 : 0;
-    const float inv_r = 1.0f / static_cast<float>(r);
-    float4 v[RPW];
+  if constexpr (GATHER) {
+    // ---- table rows of this wave's RPW operand rows: lanes 0-31 and 32-63
+    // take two rows per load round, one 16-byte chunk each; every load is
+    // issued (clamped row, clamped chunk) before the stores
+    static_assert(RPW % 2 == 0, "two rows per round");
+    const int ch = l & 31;
+    const int ccl = ch < cr ? ch : 0;
+    uint4 v[RPW / 2];
+    bool keep[RPW / 2];
 #pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const long long m = min(m0 + wv * RPW + q, M - 1);
-      v[q] = *reinterpret_cast<const float4*>(x + m * ldx + col0 + cc);
+    for (int i = 0; i < RPW / 2; ++i) {
+      const int q = 2 * i + (l >> 5);
+      const int m = m0 + wv * RPW + q;
+      int id = ga.ids[min(m, M - 1)];
+      id = id < 0 ? 0 : (id > ga.idmax ? ga.idmax : id);
+      v[i] = *reinterpret_cast<const uint4*>(ga.tab + static_cast<long long>(id) * r + ccl * 8);
+      keep[i] = m < M;
     }
 #pragma unroll
-    for (int s2 = 1; s2 < SPLIT; ++s2)
-#pragma unroll
-      for (int q = 0; q < RPW; ++q) {
-        const long long m = min(m0 + wv * RPW + q, M - 1);
-        const float4 b = *reinterpret_cast<const float4*>(x + (s2 * static_cast<long long>(M) + m) * ldx + col0 + cc);
-        v[q].x += b.x; v[q].y += b.y; v[q].z += b.z; v[q].w += b.w;
-      }
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      if (!on) v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float mean = wave_sum_dpp((v[q].x + v[q].y) + (v[q].z + v[q].w)) * inv_r;
-      float4 d = make_float4(v[q].x - mean, v[q].y - mean, v[q].z - mean, v[q].w - mean);
-      if (!on) d = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float sq = (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
-      const float inv = rsqrtf(wave_sum_dpp(sq) * inv_r + eps);
-      const bool live = m0 + wv * RPW + q < M;
-      if (on) {
-        uint2 pk;
-        pk.x = live ? (static_cast<uint32_t>(f32_to_bf16(d.x * inv)) |
-                       (static_cast<uint32_t>(f32_to_bf16(d.y * inv)) << 16)) : 0u;
-        pk.y = live ? (static_cast<uint32_t>(f32_to_bf16(d.z * inv)) |
-                       (static_cast<uint32_t>(f32_to_bf16(d.w * inv)) << 16)) : 0u;
-        *reinterpret_cast<uint2*>(tile + (wv * RPW + q) * kStr + c4 * 2) = pk;
-      }
+    for (int i = 0; i < RPW / 2; ++i) {
+      const int q = 2 * i + (l >> 5);
+      if (ch < cr)
+        *reinterpret_cast<uint4*>(tile + (wv * RPW + q) * kStr + ch * 16) = keep[i] ? v[i] : make_uint4(0, 0, 0, 0);
     }
+  } else {
+    // ---- LayerNorm of rows m0 + wv * RPW + q into the tile (bf16)
+    ln_rows_tile<RPW, SPLIT>(x, M, ldx, col0, r, eps, m0 + wv * RPW, tile + wv * RPW * kStr, kStr, l);
   }
 
   // ---- pair states of this workgroup's rows (loads in flight with the
@@ -520,7 +517,8 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   else DCOCO_LNG(BMV, RM, 4, MD)
 #define DCOCO_LNW(BMV, SP, MD)                                                                      \
   hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD, false>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, \
-                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div, PairArgs{})
+                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div, PairArgs{},      \
+                     GatherArgs{})
 #define DCOCO_LNW_SPLIT(BMV, MD)                 \
   if (split == 1) DCOCO_LNW(BMV, 1, MD);         \
   else if (split == 2) DCOCO_LNW(BMV, 2, MD);    \
@@ -557,11 +555,33 @@ hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r,
 #define DCOCO_LNP(SP)                                                                                    \
   hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, true>), dim3((M + 15) / 16), dim3(256), 0, st, Y, M, ldy, 0, \
                      r, eps, Wb, ldw, wcol0, N, gf, static_cast<bf16*>(nullptr), static_cast<const float*>(nullptr), \
-                     1, pa)
+                     1, pa, GatherArgs{})
   if (split == 1) DCOCO_LNP(1);
   else if (split == 2) DCOCO_LNP(2);
   else DCOCO_LNP(4);
 #undef DCOCO_LNP
+  return hipGetLastError();
+}
+
+bool gather_gemm_supported(int r) { return r <= 256 && r % 8 == 0; }
+
+hipError_t launch_gather_gemm(const void* tab, const int32_t* ids, int idmax, int M, int r, const void* W,
+                              long long ldw, int wcol0, int N, void* out_bf, const float* row_bias, int row_div,
+                              hipStream_t st) {
+  if (!gather_gemm_supported(r)) return hipErrorInvalidValue;
+  GatherArgs ga;
+  ga.tab = static_cast<const uint16_t*>(tab);
+  ga.ids = ids;
+  ga.idmax = idmax;
+  const bf16* Wb = static_cast<const bf16*>(W);
+  bf16* ob = static_cast<bf16*>(out_bf);
+#define DCOCO_LNG_G(BMV)                                                                                  \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, 1, 1, false, true>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, \
+                     static_cast<const float*>(nullptr), M, r, 0, r, 1.0f, Wb, ldw, wcol0, N,                \
+                     static_cast<float*>(nullptr), ob, row_bias, row_div, PairArgs{}, ga)
+  if (M >= 4096) DCOCO_LNG_G(32);
+  else DCOCO_LNG_G(16);
+#undef DCOCO_LNG_G
   return hipGetLastError();
 }
 

@@ -159,10 +159,36 @@ int dcoco_correct_block(const dcoco_dims* dims, const dcoco_weights* w,
                         int32_t* cand_ids_out, float* cand_logits_out,
                         void* stream);
 
+/* Table of normalised candidate projections, a re-association of step a2
+ * beyond the per-call path: E is frozen and P_e fixed at inference ([P1]
+ * "Score neighboring candidates in parallel"; [P2] part 1), so
+ * b_v = LN(P_e E_v) can be formed once for every token v and gathered per
+ * call instead of gathering E rows and projecting them.  bf16 only, d_proj
+ * <= 256 (otherwise DCOCO_ERR_UNSUPPORTED).
+ *   E     [V, d_embed] bf16
+ *   table [V, d_proj] bf16   out: b_v rounded to bf16 (the per-call rounding
+ *                            point of b); uses only w->P_e.
+ * Workspace as for the other entry points (the fp32 partial sums of one
+ * chunk of 8192 rows).  Run once per weight set; the table is the caller's. */
+int dcoco_build_btable(const dcoco_dims* dims, const dcoco_weights* w, const void* E,
+                       void* table, void* workspace, size_t* workspace_bytes, void* stream);
+
+/* dcoco_correct_block with b_{i,k} read from a table made by
+ * dcoco_build_btable (table [V, d_proj] bf16) instead of projecting gathered
+ * E rows; w->P_e is not used.  Same outputs, ordering and errors; the result
+ * equals the per-call path up to the fp32 summation order of P_e E_v. */
+int dcoco_correct_block_btable(const dcoco_dims* dims, const dcoco_weights* w,
+                               const void* logits, const void* h, const void* btable,
+                               void* workspace, size_t* workspace_bytes,
+                               int32_t* sel_tok, int32_t* sel_idx, float* S_out,
+                               int32_t* cand_ids_out, float* cand_logits_out,
+                               void* stream);
+
 /* Static description of a status code. */
 const char* dcoco_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 101 adds the table
+ * entry points. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import draft_block_contextual_amd as dc
-    assert lib.dcoco_abi_version() == 100
+    assert lib.dcoco_abi_version() == 101
     assert dc.status_string(0) == "ok"
     for code in (-1, -2, -3, -4):
         assert dc.status_string(code) not in ("ok", "unknown status")
@@ -129,3 +129,23 @@ def test_vocab_limits_for_topk(lib):
     # fp32 rows: the chunk merge holds at most 2048 candidates
     rc, _ = _query_topk(lib, _dims(K=64, V=600000, dtype="f32"))
     assert rc == -2
+
+
+def test_btable_queries(lib):
+    import draft_block_contextual_amd as dc
+    d = _dims()
+    cd = d.c()
+    cw = dc.CWeights()
+    n = ctypes.c_size_t(0)
+    assert lib.dcoco_build_btable(ctypes.byref(cd), ctypes.byref(cw), None, None, None, ctypes.byref(n), None) == 0
+    assert n.value >= 4 * 8192 * 256 * 4
+    n2 = ctypes.c_size_t(0)
+    assert lib.dcoco_correct_block_btable(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None,
+                                          ctypes.byref(n2), None, None, None, None, None, None) == 0
+    rc, n_full = _query_block(lib, d)
+    assert rc == 0 and 0 < n2.value < n_full          # no buffers for the gathered projection
+    # fp32 storage and wide projections have no table path
+    for kw in (dict(dtype="f32"), dict(d_proj=512)):
+        cdx = _dims(**kw).c()
+        assert lib.dcoco_build_btable(ctypes.byref(cdx), ctypes.byref(cw), None, None, None,
+                                      ctypes.byref(n), None) == -2

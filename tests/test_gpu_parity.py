@@ -354,3 +354,81 @@ def test_full_kstress_sampled():
 
 def test_full_large_sampled():
     _full_size("large", (0, 63))
+
+
+# --------------------------------- table of normalised candidate projections
+
+def _bf16_ulp(x):
+    return np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))).astype(int) - 7)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "tall_bf16", "q8b_1"])
+def test_btable_rows_match_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case btable rows {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    dims, w, logits, h, E = device_inputs(inp)
+    tab = dc.build_btable(dims, w, E)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, D.V - 1], g.integers(0, D.V, 2000)]))
+    got = tab[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    E_rows = O.to_f64(np.asarray(inp["E"])[rows], D.dtype)
+    ref = O.candidate_embedding(E_rows, np.arange(len(rows)), O.to_f64(inp["P_e"], D.dtype), D.ln_eps, True)
+    d = np.abs(got - ref)
+    print(f"  max |db| = {d.max():.3g}, exact fraction {np.mean(d == 0):.4f}", flush=True)
+    # fp32 against fp64 before the bf16 rounding: at most one bf16 step apart,
+    # plus the fp32 accumulation error of P_e E_v scaled by 1/sigma, which only
+    # shows on values near zero (whose bf16 step is tiny)
+    assert np.all(d <= _bf16_ulp(ref) + 1e-4)
+    assert np.mean(d == 0) > 0.98
+
+
+def _check_block(inp, out, ref, sl=None):
+    D = inp["dims"]
+    sl = slice(None) if sl is None else list(sl)
+    np.testing.assert_array_equal(out["cand_ids"][sl], ref["cand_ids"])
+    ok, worst, nbad = s_tolerance_ok(out["S"][sl], ref["S"], D.dtype)
+    assert ok, f"{nbad} scores out of tolerance, worst |dS| = {worst}"
+    ok, cmp, tot, fail = lockstep_path_check(out["S"][sl], ref["S"], ref["cand_vals"], out["sel_idx"][sl],
+                                             ref["sel_idx"])
+    assert ok, f"path differs at a step with margin > {PATH_MARGIN}: {fail}"
+    return worst
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "k64_small", "k32_small", "widez_bf16", "tall_bf16"])
+def test_correct_block_btable_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case correct_block btable {name}", flush=True)
+    inp = _inputs(name)
+    dims, w, logits, h, E = device_inputs(inp)
+    tab = dc.build_btable(dims, w, E)
+    out = dc.correct_block(dims, w, logits, h, None, want_all=True, btable=tab)
+    torch.cuda.synchronize()
+    out = {k: _np(v) for k, v in out.items()}
+    _check_block(inp, out, _oracle(name))
+    ri, rt, _ = O.greedy_walk(out["S"].astype(np.float64), out["cand_logits"].astype(np.float64), out["cand_ids"])
+    np.testing.assert_array_equal(out["sel_idx"], ri)
+
+
+def test_full_q8b_32_btable_sampled():
+    import draft_block_contextual_amd as dc
+    import torch
+    print("case full size q8b_32 btable blocks=(0, 13, 31)", flush=True)
+    inp = _inputs("q8b_32")
+    dims, w, logits, h, E = device_inputs(inp)
+    tab = dc.build_btable(dims, w, E)
+    out_t = dc.correct_block(dims, w, logits, h, None, want_all=True, btable=tab)
+    out_p = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    torch.cuda.synchronize()
+    out_t = {k: _np(v) for k, v in out_t.items()}
+    out_p = {k: _np(v) for k, v in out_p.items()}
+    blocks = (0, 13, 31)
+    worst = _check_block(inp, out_t, O.correct_block(inp, blocks=list(blocks)), blocks)
+    print(f"  worst |dS| vs the oracle = {worst:.3g}", flush=True)
+    # the two device paths differ only in the fp32 summation order of P_e E_v
+    np.testing.assert_array_equal(out_t["cand_ids"], out_p["cand_ids"])
+    assert np.max(np.abs(out_t["S"] - out_p["S"])) < 3e-2
