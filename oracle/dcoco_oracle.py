@@ -19,7 +19,8 @@ section:
       for Speculative Decoding" (jaehun.me/posts/paper-2610-12570), section
       "New approach: DCOCO": part 1 "learned corrector on the block grid"
       (paper Sec. 3.2), part 2 "prefix-first greedy selection" (paper
-      Sec. 3.3), and section "How it works: a concrete example" (paper Fig. 2).
+      Sec. 3.3), section "How it works: a concrete example" (paper Fig. 2),
+      and section "Path selection and ablation" (paper Sec. 4.3, Tab. 3).
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes):
@@ -33,6 +34,10 @@ the design notes):
   * projections P_e, P_h, W_f and W_pair carry no bias; s_p is not normalised;
   * walk argmax: the lowest index among maxima, NaN never wins (index 0 if a
     whole row is NaN);
+  * whole-path rules: the path score is l_1(k_1) plus the transition scores
+    along the path, slot j weighted by lam^(j-1) (lam = 1: Global-Sum); the
+    first slot is free; NaN terms count as -inf; ties go to the
+    lexicographically smallest path;
   * bf16 contract: inputs and weights are bf16 values; g, b and z are rounded
     to bf16 (nearest, ties to even) where they are produced; s, the MLP and S
     stay unrounded.  In "f32" mode nothing is rounded.
@@ -49,7 +54,7 @@ import numpy as np
 __all__ = [
     "to_f64", "round_bf16", "top_k", "layer_norm", "slot_context",
     "candidate_embedding", "fuse", "pair_state", "silu", "transition_scores",
-    "greedy_walk", "correct_block",
+    "greedy_walk", "best_path", "correct_block",
 ]
 
 
@@ -255,6 +260,61 @@ def greedy_walk(S: np.ndarray, cand_vals: np.ndarray, cand_ids: np.ndarray):
             sel_idx[n, p + 1] = k
         sel_tok[n] = cand_ids[n, np.arange(B), sel_idx[n]]
     return sel_idx, sel_tok, reads
+
+
+# ---------------------------------------------------- whole-path rules ---
+
+def best_path(S: np.ndarray, cand_vals: np.ndarray, cand_ids: np.ndarray, lam: float):
+    """The two whole-path rules the P2 review compares with the greedy walk on
+    the same score grid ([P2] section "Path selection and ablation", paper
+    Sec. 4.3 and Tab. 3; the objective is the one [P2] part 2 sets the greedy
+    rule against): choose the candidate path k_1..k_B that maximises the
+    weighted total score
+
+        J(k) = sum_{j=1..B} lam^(j-1) * sigma_j,
+        sigma_1 = l_1(k_1),   sigma_j = S_{j-1}(k_{j-1}, k_j)  (j >= 2).
+
+    lam = 1 is Global-Sum (the plain total); 0 < lam < 1 is the geometric
+    discount (the pages evaluate lam = 0.75).  The first slot is free, as a
+    total over the path implies.  A NaN term counts as -inf; among paths of
+    equal J the lexicographically smallest (k_1, ..., k_B) wins.
+
+    The maximum over all K^B paths is taken by dynamic programming over the
+    chain: V_B = 0 and, from the back, V_j(a) = max_b [lam^j S_j(a,b) +
+    V_{j+1}(b)] is the best weighted score of the slots after j given
+    k_j = a.  Then k_1 = argmax_a [l_1(a) + V_1(a)] and k_{j+1} = argmax_b
+    [lam^j S_j(k_j, b) + V_{j+1}(b)], each the lowest index among maxima,
+    which walks the lexicographically smallest optimal path.
+
+    S [N, B-1, K, K], cand_vals [N, B, K], cand_ids [N, B, K] ->
+    sel_idx [N, B], sel_tok [N, B] (int64) and J of the chosen path [N].
+    """
+    if not lam > 0:
+        raise ValueError("lam must be positive")
+    N, B, K = cand_vals.shape
+    w = float(lam) ** np.arange(B, dtype=np.float64)     # weight of slot j (0-based)
+    sel_idx = np.zeros((N, B), np.int64)
+    sel_tok = np.zeros((N, B), np.int64)
+    best = np.zeros(N)
+
+    def no_nan(x):
+        return np.where(np.isnan(x), -np.inf, x)
+
+    for n in range(N):
+        V = [None] * B
+        V[B - 1] = np.zeros(K)
+        for p in range(B - 2, -1, -1):        # pair p joins slots p and p+1
+            V[p] = no_nan(w[p + 1] * S[n, p].astype(np.float64) + V[p + 1][None, :]).max(axis=1)
+        first = no_nan(w[0] * cand_vals[n, 0].astype(np.float64) + V[0])
+        k = int(np.argmax(first))            # first occurrence: the lowest index
+        best[n] = first[k]
+        sel_idx[n, 0] = k
+        for p in range(B - 1):
+            row = no_nan(w[p + 1] * S[n, p, k].astype(np.float64) + V[p + 1])
+            k = int(np.argmax(row))
+            sel_idx[n, p + 1] = k
+        sel_tok[n] = cand_ids[n, np.arange(B), sel_idx[n]]
+    return sel_idx, sel_tok, best
 
 
 # ------------------------------------------------------------- the block ---

@@ -449,3 +449,91 @@ def test_tiny_zero_config_reproduces_drafter_argmax():
     for p in range(D.B - 1):
         for a in range(D.K):
             np.testing.assert_array_equal(out["S"][:, p, a, :], out["cand_vals"][:, p + 1, :])
+
+
+# ------------------------------------------------------- whole-path rules
+
+def _brute_best_path(S, vals, lam):
+    """Every one of the K^B paths scored left to right; the first maximum in
+    itertools.product order is the lexicographically smallest one."""
+    B, K = vals.shape
+    best, arg = None, None
+    for path in itertools.product(range(K), repeat=B):
+        terms = [vals[0, path[0]]] + [S[p, path[p], path[p + 1]] for p in range(B - 1)]
+        J = 0.0
+        for j, t in enumerate(terms):
+            t = -math.inf if math.isnan(t) else float(t)
+            J = J + lam ** j * t
+        if math.isnan(J):
+            J = -math.inf
+        if best is None or J > best:
+            best, arg = J, path
+    return np.array(arg), best
+
+
+@pytest.mark.parametrize("lam", [1.0, 0.75, 0.5])
+def test_best_path_brute_force(lam):
+    # small integers and dyadic weights: every total is exact in float64, so
+    # ties are real ties and both orders of summation agree bit for bit
+    g = _rng(31)
+    for trial in range(60):
+        B = int(g.integers(1, 6))
+        K = int(g.integers(1, 5))
+        vals = g.integers(-3, 4, size=(1, B, K)).astype(np.float64)
+        S = g.integers(-3, 4, size=(1, max(B - 1, 0), K, K)).astype(np.float64)
+        if trial % 5 == 0 and B > 1:
+            S[0, 0, 0, :] = np.nan            # a NaN row
+        if trial % 7 == 0 and B > 1:
+            S[0, -1, :, 0] = -np.inf
+        ids = g.integers(0, 1000, size=(1, B, K))
+        sel, tok, J = O.best_path(S, vals, ids, lam)
+        ref, Jref = _brute_best_path(S[0], vals[0], lam)
+        assert sel[0].tolist() == ref.tolist(), (trial, B, K)
+        assert J[0] == Jref
+        assert tok[0].tolist() == ids[0, np.arange(B), ref].tolist()
+
+
+def test_best_path_departs_from_greedy_by_hand():
+    # l_1 = (1, 0); S_1 rows: from candidate 0 (0, 0), from candidate 1 (5, 4).
+    # Greedy keeps k_1 = 0 and takes the lower of the tied successors: (0, 0).
+    # Global-Sum: (1, 0) scores 0 + 5 = 5 against 1 + 0 = 1 for (0, 0).
+    # Discount 0.75: (1, 0) scores 0 + 0.75*5 = 3.75 > 1.  Discount 0.1:
+    # 0 + 0.1*5 = 0.5 < 1 + 0.1*0 = 1, so (0, 0) again.
+    vals = np.array([[[1.0, 0.0], [0.0, 0.0]]])
+    S = np.array([[[[0.0, 0.0], [5.0, 4.0]]]])
+    ids = np.array([[[10, 11], [20, 21]]])
+    gsel, _, _ = O.greedy_walk(S, vals, ids)
+    assert gsel[0].tolist() == [0, 0]
+    for lam, want, J in ((1.0, [1, 0], 5.0), (0.75, [1, 0], 3.75), (0.1, [0, 0], 1.0)):
+        sel, tok, best = O.best_path(S, vals, ids, lam)
+        assert sel[0].tolist() == want
+        assert best[0] == pytest.approx(J, abs=1e-15)
+        assert tok[0].tolist() == [ids[0, 0, want[0]], ids[0, 1, want[1]]]
+
+
+def test_best_path_tiny_discount_is_greedy():
+    # lam -> 0 orders paths lexicographically by (l_1(k_1), S_1(k_1, k_2), ...):
+    # exactly the prefix-first greedy walk when no step has a near-tie
+    g = _rng(32)
+    N, B, K = 6, 9, 7
+    vals = g.standard_normal((N, B, K))
+    S = g.standard_normal((N, B - 1, K, K)) * 3
+    ids = g.integers(0, 50000, size=(N, B, K))
+    gsel, gtok, _ = O.greedy_walk(S, vals, ids)
+    sel, tok, _ = O.best_path(S, vals, ids, 1e-9)
+    assert np.array_equal(sel, gsel) and np.array_equal(tok, gtok)
+
+
+@pytest.mark.parametrize("lam", [1.0, 0.75])
+def test_best_path_zero_correction_is_drafter_argmax(lam):
+    # with Delta = 0, S_p(a, b) = l_{p+1}(b): the weighted total splits into
+    # independent per-slot terms, so the best path is each slot's own argmax
+    g = _rng(33)
+    N, B, K = 4, 6, 5
+    vals = g.standard_normal((N, B, K))
+    S = np.broadcast_to(vals[:, 1:, None, :], (N, B - 1, K, K)).copy()
+    ids = g.integers(0, 50000, size=(N, B, K))
+    sel, _, J = O.best_path(S, vals, ids, lam)
+    assert np.array_equal(sel, vals.argmax(axis=2))
+    w = lam ** np.arange(B)
+    assert np.allclose(J, (vals.max(axis=2) * w).sum(axis=1), rtol=0, atol=1e-12)
