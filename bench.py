@@ -234,6 +234,11 @@ def main():
                                             stream=stream),
         "score": lambda i: dc.score(dims, w, z, s, cl, S, workspace=ws, stream=stream),
         "select": lambda i: dc.select(dims, S, cl, ids, si, sel_tok, stream=stream),
+        # the whole-path rules on the same grid (reported beside the stages)
+        "select_global_sum": lambda i: dc.select_path(dims, S, cl, ids, "global_sum", 1.0, si, sel_tok,
+                                                      stream=stream),
+        "select_discount": lambda i: dc.select_path(dims, S, cl, ids, "discount", 0.75, si, sel_tok,
+                                                    stream=stream),
     }
     stage_us = {}
     for name, fn in stages.items():

@@ -22,7 +22,7 @@ DCOCO_ERR_HIP = -4
 DTYPE_CODE = {"f32": 0, "bf16": 1}
 
 # every entry point include/dcoco.h declares
-EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select",
+EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
            "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
            "dcoco_status_string", "dcoco_abi_version"]
 
@@ -64,10 +64,12 @@ def load() -> ctypes.CDLL:
     lib.dcoco_represent.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dcoco_score.argtypes = [pd, pw, vp, vp, vp, vp, vp, sz, vp]
     lib.dcoco_select.argtypes = [pd, vp, vp, vp, vp, vp, vp]
+    lib.dcoco_select_path.argtypes = [pd, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp]
     lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     lib.dcoco_build_btable.argtypes = [pd, pw, vp, vp, vp, sz, vp]
     lib.dcoco_correct_block_btable.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
-    for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_correct_block",
+    for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
+              "dcoco_correct_block",
               "dcoco_build_btable", "dcoco_correct_block_btable"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.dcoco_status_string.argtypes = [ctypes.c_int]
@@ -230,6 +232,27 @@ def select(dims: Dims, S, cand_logits, cand_ids, sel_idx=None, sel_tok=None, str
         sel_tok = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
     _check("dcoco_select", lib.dcoco_select(ctypes.byref(cd), _ptr(S), _ptr(cand_logits), _ptr(cand_ids),
                                             _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
+    return sel_idx, sel_tok
+
+
+PATH_RULES = {"greedy": 0, "global_sum": 1, "discount": 2}
+
+
+def select_path(dims: Dims, S, cand_logits, cand_ids, rule: str = "greedy", lam: float = 1.0,
+                sel_idx=None, sel_tok=None, stream=None):
+    """dcoco_select_path -> (sel_idx [N, B] int32, sel_tok [N, B] int32).
+    rule: "greedy", "global_sum" or "discount" (weight lam^(j-1) on slot j)."""
+    import torch
+    lib = load()
+    cd = dims.c()
+    dev = cand_logits.device
+    if sel_idx is None:
+        sel_idx = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+    if sel_tok is None:
+        sel_tok = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+    _check("dcoco_select_path", lib.dcoco_select_path(ctypes.byref(cd), _ptr(S), _ptr(cand_logits),
+                                                      _ptr(cand_ids), PATH_RULES[rule], float(lam),
+                                                      _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
     return sel_idx, sel_tok
 
 

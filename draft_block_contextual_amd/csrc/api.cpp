@@ -288,7 +288,7 @@ int check_ws(void* ws, size_t* bytes, size_t need) {
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 101; }
+int dcoco_abi_version(void) { return 102; }
 
 const char* dcoco_status_string(int status) {
   switch (status) {
@@ -360,6 +360,22 @@ int dcoco_select(const dcoco_dims* d, const float* S, const float* cand_logits, 
     return DCOCO_ERR_INVALID_ARG;
   if (d->B > 1 && !ptr_ok(S)) return DCOCO_ERR_INVALID_ARG;
   return hip_status(launch_walk(S, cand_logits, cand_ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_select_path(const dcoco_dims* d, const float* S, const float* cand_logits, const int32_t* cand_ids,
+                      int rule, float lambda, int32_t* sel_idx, int32_t* sel_tok, void* stream) {
+  if (rule == DCOCO_PATH_GREEDY) return dcoco_select(d, S, cand_logits, cand_ids, sel_idx, sel_tok, stream);
+  if (rule != DCOCO_PATH_GLOBAL_SUM && rule != DCOCO_PATH_DISCOUNT) return DCOCO_ERR_INVALID_ARG;
+  const float lam = rule == DCOCO_PATH_GLOBAL_SUM ? 1.0f : lambda;
+  if (!(lam > 0.0f && lam <= 1.0f)) return DCOCO_ERR_INVALID_ARG;   // also rejects NaN
+  int rc = check_dims(d, false);
+  if (rc != DCOCO_OK) return rc;
+  if (!ptr_ok(cand_logits) || !ptr_ok(cand_ids) || !ptr_ok(sel_tok) || !opt_ok(sel_idx))
+    return DCOCO_ERR_INVALID_ARG;
+  if (d->B > 1 && !ptr_ok(S)) return DCOCO_ERR_INVALID_ARG;
+  if (!path_supported(d->B, d->K)) return DCOCO_ERR_UNSUPPORTED;
+  return hip_status(launch_path(S, cand_logits, cand_ids, d->n_blocks, d->B, d->K, lam, sel_idx, sel_tok,
                                 static_cast<hipStream_t>(stream)));
 }
 

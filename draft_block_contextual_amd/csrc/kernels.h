@@ -96,4 +96,10 @@ hipError_t launch_split3(const float* s, long long n, void* s3, hipStream_t st);
 hipError_t launch_walk(const float* S, const float* cand_logits, const int32_t* cand_ids, int N,
                        int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
 
+// Whole-path rules: maximise sum_j lam^j sigma_j over all K^B paths (slot j
+// 0-based; sigma_0 = l_0(k_0), sigma_j = S_{j-1}(k_{j-1}, k_j)).
+bool path_supported(int B, int K);
+hipError_t launch_path(const float* S, const float* cand_logits, const int32_t* cand_ids, int N, int B, int K,
+                       float lam, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
+
 }  // namespace dcoco

@@ -414,6 +414,124 @@ walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int
   }
 }
 
+constexpr int kPathLds = 12288;   // floats of scores staged per chunk of pairs
+constexpr int kPathBp = 16384;    // bytes of back-pointers, one per (pair, candidate)
+constexpr int kPathMaxB = 4096;   // slots per block: the chosen indices reuse the score buffer
+
+// Whole-path rules, one workgroup per block.  The path score weights slot j
+// (0-based) by lam^j; with U_{B-1} = 0 and, from the last pair back,
+//   U_p(a) = max_b [S_p(a, b) + lam * U_{p+1}(b)],
+// lam^(p+1) U_p(a) is the best weighted score of the slots after p given
+// k_p = a.  Lane a of wave 0 holds U(a) in a register and reads U(b) with
+// readlane; the lowest maximising b is kept as a back-pointer in LDS.  The
+// forward pass takes k_0 = argmax_a [l_0(a) + lam U_0(a)] and follows the
+// back-pointers, which walks the lexicographically smallest optimal path.
+// NaN never wins a comparison, so a NaN term acts as -inf.
+__global__ void __launch_bounds__(256)
+path_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int32_t* __restrict__ ids,
+            int B, int K, float lam, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_tok) {
+  __shared__ __align__(16) float sS[kPathLds];
+  __shared__ uint8_t sBp[kPathBp];
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int Bm1 = B - 1;
+  const int per = K * K;
+  const int KS = ((K + 3) & ~3) + 4;   // padded row stride in floats (16-byte rows)
+  const int pstr = K * KS;              // floats per staged pair
+  const int chunk = kPathLds / pstr;    // >= 2 for K <= 64
+  const float* Sn = S + static_cast<long long>(n) * Bm1 * per;
+  const bool vec = ((reinterpret_cast<uintptr_t>(Sn) & 15) == 0) && (K % 4 == 0);
+  float u = 0.f;
+  for (int hi = Bm1; hi > 0;) {
+    const int lo = max(0, hi - chunk);
+    const int ne = (hi - lo) * per;
+    const float* src = Sn + static_cast<long long>(lo) * per;
+    __syncthreads();   // the previous chunk has been consumed
+    if (vec) {
+      // 8 float4 per thread and round, loads unconditional (index clamped)
+      const int nv = ne / 4;
+      for (int e0 = 0; e0 < nv; e0 += 256 * 8) {
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const float4*>(src)[min(e0 + tid + 256 * j, nv - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = 4 * (e0 + tid + 256 * j);
+          if (e < ne) {
+            const int q = e / per;
+            const int r = e - q * per;
+            const int a = r / K;
+            *reinterpret_cast<float4*>(sS + q * pstr + a * KS + (r - a * K)) = v[j];
+          }
+        }
+      }
+    } else {
+      for (int e0 = 0; e0 < ne; e0 += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = src[min(e0 + tid + 256 * j, ne - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = e0 + tid + 256 * j;
+          if (e < ne) {
+            const int q = e / per;
+            const int r = e - q * per;
+            const int a = r / K;
+            sS[q * pstr + a * KS + (r - a * K)] = v[j];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      for (int p = hi - 1; p >= lo; --p) {
+        // lanes >= K work on row K-1 and their results are never read
+        const float* row = sS + (p - lo) * pstr + min(l, K - 1) * KS;
+        float best = -INFINITY;
+        int bi = 0;
+        for (int b4 = 0; b4 < K; b4 += 4) {
+          const float4 r4 = *reinterpret_cast<const float4*>(row + b4);
+          const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int b = b4 + t;
+            if (b < K) {
+              const float c = rv[t] + lam * read_lane(u, b);
+              if (c > best) {
+                best = c;
+                bi = b;
+              }
+            }
+          }
+        }
+        u = best;
+        if (l < K) sBp[p * K + l] = static_cast<uint8_t>(bi);
+      }
+    }
+    hi = lo;
+  }
+  __syncthreads();
+  int32_t* sK = reinterpret_cast<int32_t*>(sS);   // the chosen index per slot
+  if (tid < kWave) {
+    const float c0 = cl[static_cast<long long>(n) * B * K + min(l, K - 1)] + lam * u;
+    int k = wave_argmax(c0 == c0 ? c0 : -INFINITY, l < K);
+    if (l == 0) {
+      for (int j = 0; j < B; ++j) {
+        sK[j] = k;
+        if (j < Bm1) k = sBp[j * K + k];
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < B; j += 256) {
+    const int k = sK[j];
+    const long long o = static_cast<long long>(n) * B + j;
+    if (sel_idx) sel_idx[o] = k;
+    sel_tok[o] = ids[o * K + k];
+  }
+}
+
 template <typename T>
 hipError_t launch_grid_t(const GridProblem& q, hipStream_t st) {
   GridDev g;
@@ -432,6 +550,18 @@ hipError_t launch_grid_t(const GridProblem& q, hipStream_t st) {
 }
 
 }  // namespace
+
+bool path_supported(int B, int K) {
+  return B >= 1 && K >= 1 && K <= 64 && B <= kPathMaxB && static_cast<long long>(B) * K <= kPathBp;
+}
+
+hipError_t launch_path(const float* S, const float* cand_logits, const int32_t* cand_ids, int N, int B, int K,
+                       float lam, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st) {
+  if (!path_supported(B, K)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(path_kernel, dim3(N), dim3(256), 0, st, S, cand_logits, cand_ids, B, K, lam, sel_idx,
+                     sel_tok);
+  return hipGetLastError();
+}
 
 hipError_t launch_grid(const GridProblem& q, hipStream_t st) {
   if (q.dtype == kDtypeBf16) return launch_grid_t<bf16>(q, st);

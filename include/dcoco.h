@@ -16,7 +16,8 @@
  *   [P2] review of arXiv 2610.12570, "Contextual Correction of Parallel Drafts
  *        for Speculative Decoding" (jaehun.me/posts/paper-2610-12570), section
  *        "New approach: DCOCO", parts 1 (paper Sec. 3.2) and 2 (paper
- *        Sec. 3.3).
+ *        Sec. 3.3), and section "Path selection and ablation" (paper
+ *        Sec. 4.3).
  *
  * Conventions for every entry point
  *   - All array arguments are DEVICE pointers on the current HIP device,
@@ -144,6 +145,30 @@ int dcoco_select(const dcoco_dims* dims, const float* S, const float* cand_logit
                  const int32_t* cand_ids, int32_t* sel_idx, int32_t* sel_tok,
                  void* stream);
 
+/* Path-selection rules compared with the greedy walk on the same score grid
+ * ([P2] section "Path selection and ablation", paper Sec. 4.3 and Tab. 3).
+ *   DCOCO_PATH_GREEDY      the prefix-first walk of dcoco_select (lambda unused)
+ *   DCOCO_PATH_GLOBAL_SUM  maximise the total path score
+ *   DCOCO_PATH_DISCOUNT    maximise the geometrically discounted score
+ * The page gives no formula; the reading used: over all K^B paths k_1..k_B,
+ *   J(k) = sum_{j=1..B} lambda^(j-1) sigma_j,
+ *   sigma_1 = l_1(k_1), sigma_j = S_{j-1}(k_{j-1}, k_j) (j >= 2),
+ * with lambda = 1 for Global-Sum and 0 < lambda <= 1 for the discount (the
+ * page evaluates 0.75).  The first slot is free; a NaN term counts as -inf;
+ * among paths of equal J (in fp32 arithmetic) the lexicographically smallest
+ * index sequence wins.  Arguments as dcoco_select.  Errors: an unknown rule
+ * or, for DCOCO_PATH_DISCOUNT, lambda outside (0, 1] -> DCOCO_ERR_INVALID_ARG;
+ * for the two whole-path rules, B > 4096 or B*K > 16384 ->
+ * DCOCO_ERR_UNSUPPORTED.  One workgroup per block; O(B K^2) work. */
+typedef enum {
+  DCOCO_PATH_GREEDY = 0,
+  DCOCO_PATH_GLOBAL_SUM = 1,
+  DCOCO_PATH_DISCOUNT = 2
+} dcoco_path_rule;
+int dcoco_select_path(const dcoco_dims* dims, const float* S, const float* cand_logits,
+                      const int32_t* cand_ids, int rule, float lambda, int32_t* sel_idx,
+                      int32_t* sel_tok, void* stream);
+
 /* The whole path for n_blocks draft blocks: top-K, representations, pair
  * states, transition scores and the greedy walk, on one stream.
  *   logits [n_blocks*B, V], h [n_blocks, B, d_hidden], E [V, d_embed]: dtype
@@ -188,7 +213,7 @@ int dcoco_correct_block_btable(const dcoco_dims* dims, const dcoco_weights* w,
 const char* dcoco_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor): 101 adds the table
- * entry points. */
+ * entry points, 102 dcoco_select_path. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import draft_block_contextual_amd as dc
-    assert lib.dcoco_abi_version() == 101
+    assert lib.dcoco_abi_version() == 102
     assert dc.status_string(0) == "ok"
     for code in (-1, -2, -3, -4):
         assert dc.status_string(code) not in ("ok", "unknown status")
@@ -149,3 +149,24 @@ def test_btable_queries(lib):
         cdx = _dims(**kw).c()
         assert lib.dcoco_build_btable(ctypes.byref(cdx), ctypes.byref(cw), None, None, None,
                                       ctypes.byref(n), None) == -2
+
+
+def test_select_path_argument_checks(lib):
+    # every case returns before a launch: the rule, lambda and shape checks
+    # come first, and the fake pointers are never dereferenced
+    fake = ctypes.c_void_p(1 << 20)
+    cd = _dims(n_blocks=2, B=16, K=16).c()
+
+    def call(rule, lam, dims=cd, S=fake):
+        return lib.dcoco_select_path(ctypes.byref(dims), S, fake, fake, rule, lam, None, fake, None)
+
+    assert call(3, 1.0) == -1                    # unknown rule
+    assert call(-1, 1.0) == -1
+    for lam in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert call(2, lam) == -1, lam           # a discount lies in (0, 1]
+    assert call(2, 0.75, S=None) == -1           # B > 1 needs scores
+    big = _dims(n_blocks=2, B=4097, K=2).c()
+    assert call(1, 1.0, dims=big) == -2          # too many slots for the back-pointer buffer
+    wide = _dims(n_blocks=2, B=300, K=64).c()
+    assert call(2, 0.5, dims=wide) == -2         # B*K > 16384
+    assert call(1, 1.0, dims=_dims(n_blocks=2, B=16, K=65).c()) == -2   # K > 64

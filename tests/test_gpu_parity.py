@@ -173,6 +173,110 @@ def test_select_worked_example():
             assert list(si[0]) == case["path"], (name, case)
 
 
+# ---------------------------------------------------- whole-path rules
+
+def _select_path(S, vals, ids, rule, lam):
+    import draft_block_contextual_amd as dc
+    import torch
+    N, B, K = vals.shape
+    dims = dc.Dims(N, B, K, max(K, 1), 32, 32, 32, 32, 32, 32, "f32")
+    if B > 1:
+        Sd = torch.from_numpy(np.ascontiguousarray(S, dtype=np.float32)).cuda()
+    else:
+        Sd = torch.zeros(1, dtype=torch.float32, device="cuda")
+    si, st = dc.select_path(dims, Sd, torch.from_numpy(np.ascontiguousarray(vals, dtype=np.float32)).cuda(),
+                            torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda(), rule, lam)
+    torch.cuda.synchronize()
+    return si.cpu().numpy(), st.cpu().numpy()
+
+
+def _path_score(S, vals, path, lam):
+    """J of one path in float64 with the oracle's weights (NaN terms -inf)."""
+    B = len(path)
+    terms = [vals[0, path[0]]] + [S[p, path[p], path[p + 1]] for p in range(B - 1)]
+    terms = np.array([-np.inf if np.isnan(t) else t for t in terms], np.float64)
+    w = lam ** np.arange(B, dtype=np.float64)
+    with np.errstate(invalid="ignore"):
+        J = float((w * terms).sum())
+    return (-np.inf if np.isnan(J) else J), float(np.abs(terms[np.isfinite(terms)]).sum())
+
+
+@pytest.mark.parametrize("lam", [1.0, 0.5])
+def test_select_path_exact_on_integer_grids(lam):
+    # integer scores: with lam = 1 every fp32 total is exact at any length,
+    # with lam = 0.5 up to 16 slots, so exact ties are ties on both sides and
+    # the lexicographic tie rule must give the same path bit for bit
+    g = np.random.default_rng(41)
+    cases = [(5, 16, 16), (3, 7, 64), (4, 16, 3), (2, 1, 5), (6, 12, 32), (3, 16, 1), (4, 9, 17)]
+    if lam == 1.0:
+        cases += [(2, 300, 8), (1, 4096, 4), (1, 256, 64)]     # long blocks up to both limits
+    for N, B, K in cases:
+        print(f"case select_path lam={lam} N={N} B={B} K={K}", flush=True)
+        S = g.integers(-3, 4, size=(N, max(B - 1, 0), K, K)).astype(np.float32)
+        vals = g.integers(-3, 4, size=(N, B, K)).astype(np.float32)
+        if B > 2:
+            S[0, 1, :, 0] = np.nan               # NaN terms never win
+            S[-1, 0, 0, :] = -np.inf
+        ids = g.integers(0, 100000, (N, B, K)).astype(np.int32)
+        rule = "global_sum" if lam == 1.0 else "discount"
+        si, st = _select_path(S, vals, ids, rule, lam)
+        ri, rt, _ = O.best_path(S.astype(np.float64), vals.astype(np.float64), ids, lam)
+        np.testing.assert_array_equal(si, ri)
+        np.testing.assert_array_equal(st, rt)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "mid_bf16", "k32_small", "k64_small"])
+@pytest.mark.parametrize("lam", [1.0, 0.75])
+def test_select_path_on_oracle_scores(name, lam):
+    # the oracle's own S (rounded to fp32, the type the entry point takes):
+    # the GPU path must be the oracle's, unless the two are within the fp32
+    # summation error of each other (then the GPU path's J, in float64, must
+    # be within that bound of the optimum)
+    print(f"case select_path {name} lam={lam}", flush=True)
+    ref = _oracle(name)
+    S = ref["S"].astype(np.float32)
+    vals = ref["cand_vals"].astype(np.float32)
+    ids = ref["cand_ids"].astype(np.int32)
+    rule = "global_sum" if lam == 1.0 else "discount"
+    si, st = _select_path(S, vals, ids, rule, lam)
+    ri, rt, Jb = O.best_path(S.astype(np.float64), vals.astype(np.float64), ids, lam)
+    same = 0
+    for n in range(vals.shape[0]):
+        if np.array_equal(si[n], ri[n]):
+            same += 1
+            assert np.array_equal(st[n], rt[n])
+            continue
+        J, mag = _path_score(S[n].astype(np.float64), vals[n].astype(np.float64), si[n], lam)
+        assert J >= Jb[n] - 1e-4 * (1.0 + mag), (n, J, Jb[n])
+        assert np.array_equal(st[n], ids[n, np.arange(vals.shape[1]), si[n]])
+    assert same >= 0.9 * vals.shape[0]
+
+
+def test_select_path_rules_against_greedy():
+    g = np.random.default_rng(42)
+    N, B, K = 8, 16, 16
+    S = g.standard_normal((N, B - 1, K, K)).astype(np.float32) * 3
+    vals = np.sort(g.standard_normal((N, B, K)))[..., ::-1].astype(np.float32)
+    ids = g.integers(0, 100000, (N, B, K)).astype(np.int32)
+    gi, gt = _select(S, vals, ids)
+    # the greedy rule is dcoco_select itself
+    si, st = _select_path(S, vals, ids, "greedy", 0.0)
+    np.testing.assert_array_equal(si, gi)
+    np.testing.assert_array_equal(st, gt)
+    # a vanishing discount orders paths by (l_1, S_1, S_2, ...) lexicographically:
+    # the greedy walk, on scores with no near-ties
+    si, st = _select_path(S, vals, ids, "discount", 1e-6)
+    np.testing.assert_array_equal(si, gi)
+    # the hand-worked case where the total departs from the greedy walk
+    vals2 = np.array([[[1.0, 0.0], [0.0, 0.0]]], np.float32)
+    S2 = np.array([[[[0.0, 0.0], [5.0, 4.0]]]], np.float32)
+    ids2 = np.array([[[10, 11], [20, 21]]], np.int32)
+    for rule, lam, want in (("global_sum", 1.0, [1, 0]), ("discount", 0.75, [1, 0]), ("discount", 0.1, [0, 0])):
+        si, st = _select_path(S2, vals2, ids2, rule, lam)
+        assert si[0].tolist() == want, (rule, lam)
+        assert st[0].tolist() == [ids2[0, 0, want[0]], ids2[0, 1, want[1]]]
+
+
 # ------------------------------------------------------ representation
 
 @pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_f32", "mid_bf16", "k32_small", "widez_bf16",
