@@ -20,7 +20,9 @@ section:
       "New approach: DCOCO": part 1 "learned corrector on the block grid"
       (paper Sec. 3.2), part 2 "prefix-first greedy selection" (paper
       Sec. 3.3), section "How it works: a concrete example" (paper Fig. 2),
-      and section "Path selection and ablation" (paper Sec. 4.3, Tab. 3).
+      section "Path selection and ablation" (paper Sec. 4.3, Tab. 3), and
+      part 3 "training: supervised by the verifier's prefix only" (paper
+      Sec. 3.2, App. A).
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes):
@@ -34,6 +36,9 @@ the design notes):
   * projections P_e, P_h, W_f and W_pair carry no bias; s_p is not normalised;
   * walk argmax: the lowest index among maxima, NaN never wins (index 0 if a
     whole row is NaN);
+  * training loss: joint softmax over the K^2 scores of a pair, pair p
+    weighted by exp(-(p-1)/rho), masked unless both target tokens are among
+    the candidates, summed over pairs and averaged over blocks;
   * whole-path rules: the path score is l_1(k_1) plus the transition scores
     along the path, slot j weighted by lam^(j-1) (lam = 1: Global-Sum); the
     first slot is free; NaN terms count as -inf; ties go to the
@@ -54,7 +59,7 @@ import numpy as np
 __all__ = [
     "to_f64", "round_bf16", "top_k", "layer_norm", "slot_context",
     "candidate_embedding", "fuse", "pair_state", "silu", "transition_scores",
-    "greedy_walk", "best_path", "correct_block",
+    "greedy_walk", "best_path", "corrector_loss", "score_backward", "correct_block",
 ]
 
 
@@ -260,6 +265,110 @@ def greedy_walk(S: np.ndarray, cand_vals: np.ndarray, cand_ids: np.ndarray):
             sel_idx[n, p + 1] = k
         sel_tok[n] = cand_ids[n, np.arange(B), sel_idx[n]]
     return sel_idx, sel_tok, reads
+
+
+# ------------------------------------------------------------ training ---
+
+def corrector_loss(S: np.ndarray, cand_ids: np.ndarray, target_tok: np.ndarray, rho: float) -> dict:
+    """The corrector's training loss and its gradient with respect to the
+    scores ([P1] "How we train the corrector"; [P2] part 3, paper Sec. 3.2
+    and App. A).  The label of pair p is the pair of target tokens of slots
+    p and p+1, (a*_p, b*_p) = their positions in the two slots' candidate
+    lists; m_p = 1 only when both are present.  Each active pair contributes
+    the cross-entropy of a softmax taken jointly over its K^2 scores, weighted
+    by an exponential decay over the pair's position.  The pages lose the
+    formula; the reading taken:
+
+        L = (1/N) sum_n sum_{p=1..B-1} m_{n,p} exp(-(p-1)/rho) CE_{n,p},
+        CE = log sum_{a,b} exp(S_p(a, b)) - S_p(a*, b*),
+
+    and dL/dS_p(a, b) = (1/N) m w_p (softmax(S_p)(a, b) - [(a, b) = (a*, b*)]).
+
+    S [N, B-1, K, K], cand_ids [N, B, K], target_tok [N, B] -> dict with
+    loss (float), pair_loss [N, B-1] (m w CE / N), mask, a_star, b_star
+    [N, B-1] (-1 where absent) and dS [N, B-1, K, K] (float64).
+    """
+    S = np.asarray(S, np.float64)
+    N, Bm1, K, _ = S.shape
+    pos = np.full((N, Bm1 + 1), -1, np.int64)
+    for n in range(N):
+        for i in range(Bm1 + 1):
+            hit = np.nonzero(np.asarray(cand_ids[n, i]) == target_tok[n, i])[0]
+            if len(hit):
+                pos[n, i] = hit[0]
+    a_star, b_star = pos[:, :-1], pos[:, 1:]
+    mask = (a_star >= 0) & (b_star >= 0)
+    w = np.exp(-np.arange(Bm1, dtype=np.float64) / rho)
+    pair_loss = np.zeros((N, Bm1))
+    dS = np.zeros_like(S)
+    for n in range(N):
+        for p in range(Bm1):
+            if not mask[n, p]:
+                continue
+            flat = S[n, p].reshape(-1)
+            top = flat.max()
+            e = np.exp(flat - top)
+            lse = top + np.log(e.sum())
+            label = a_star[n, p] * K + b_star[n, p]
+            coef = w[p] / N
+            pair_loss[n, p] = coef * (lse - flat[label])
+            g = e / e.sum()
+            g[label] -= 1.0
+            dS[n, p] = (coef * g).reshape(K, K)
+    return {"loss": float(pair_loss.sum()), "pair_loss": pair_loss, "mask": mask,
+            "a_star": np.where(mask, a_star, -1), "b_star": np.where(mask, b_star, -1), "dS": dS}
+
+
+def score_backward(z: np.ndarray, s: np.ndarray, W1: np.ndarray, b1: np.ndarray, w2: np.ndarray,
+                   dS: np.ndarray) -> dict:
+    """Gradients of a loss through the transition scores, given G = dL/dS
+    (the backward of transition_scores; [P2] part 1, paper Sec. 3.2: one
+    shared MLP over x = [z_{p,a}; z_{p+1,b}; s_p]).  With u = W1 x + b1:
+
+        dL/dw2 = sum G SiLU(u),  dL/db2 = sum G,
+        dL/du = G w2 SiLU'(u),   SiLU'(u) = sig(u) (1 + u (1 - sig(u))),
+        dL/dW1 = sum dL/du x^T,  dL/db1 = sum dL/du,  dL/dx = W1^T dL/du,
+
+    dL/dx split back into its three parts and added into dz_{p,a},
+    dz_{p+1,b} and ds_p; the draft logit term gives dL/dl_{p+1}(b) =
+    sum_a G(a, b).  Sums run over every pair and candidate pair.  The bf16
+    rounding of z in the forward pass is taken as the identity.
+
+    z [N, B, K, r_z], s [N, B-1, r_s], dS [N, B-1, K, K] -> dict of float64
+    dz, ds, dW1, db1, dw2, db2, d_cand_vals.
+    """
+    z = np.asarray(z, np.float64)
+    s = np.asarray(s, np.float64)
+    W1 = np.asarray(W1, np.float64)
+    b1 = np.asarray(b1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    G = np.asarray(dS, np.float64)
+    N, B, K, rz = z.shape
+    rs = s.shape[-1]
+    out = {"dz": np.zeros_like(z), "ds": np.zeros((N, max(B - 1, 0), rs)), "dW1": np.zeros_like(W1),
+           "db1": np.zeros_like(b1), "dw2": np.zeros_like(w2), "db2": 0.0,
+           "d_cand_vals": np.zeros((N, B, K))}
+    for n in range(N):
+        for p in range(B - 1):
+            za = np.broadcast_to(z[n, p][:, None, :], (K, K, rz))
+            zb = np.broadcast_to(z[n, p + 1][None, :, :], (K, K, rz))
+            sp = np.broadcast_to(s[n, p][None, None, :], (K, K, rs))
+            x = np.concatenate([za, zb, sp], axis=-1).reshape(K * K, -1)
+            u = x @ W1.T + b1
+            with np.errstate(over="ignore"):
+                sig = 1.0 / (1.0 + np.exp(-u))
+            g = G[n, p].reshape(K * K)
+            out["dw2"] += (g[:, None] * (u * sig)).sum(axis=0)
+            out["db2"] += g.sum()
+            du = g[:, None] * w2[None, :] * sig * (1.0 + u * (1.0 - sig))
+            out["dW1"] += du.T @ x
+            out["db1"] += du.sum(axis=0)
+            dx = (du @ W1).reshape(K, K, -1)
+            out["dz"][n, p] += dx[:, :, :rz].sum(axis=1)
+            out["dz"][n, p + 1] += dx[:, :, rz:2 * rz].sum(axis=0)
+            out["ds"][n, p] += dx[:, :, 2 * rz:].sum(axis=(0, 1))
+            out["d_cand_vals"][n, p + 1] += G[n, p].sum(axis=0)
+    return out
 
 
 # ---------------------------------------------------- whole-path rules ---

@@ -537,3 +537,135 @@ def test_best_path_zero_correction_is_drafter_argmax(lam):
     assert np.array_equal(sel, vals.argmax(axis=2))
     w = lam ** np.arange(B)
     assert np.allclose(J, (vals.max(axis=2) * w).sum(axis=1), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------- training
+
+def _loss_case(seed, N=3, B=6, K=4, absent=True):
+    g = _rng(seed)
+    S = g.standard_normal((N, B - 1, K, K)) * 2
+    ids = np.stack([np.stack([g.permutation(1000)[:K] for _ in range(B)]) for _ in range(N)])
+    tgt = np.empty((N, B), np.int64)
+    for n in range(N):
+        for i in range(B):
+            tgt[n, i] = ids[n, i, g.integers(0, K)]
+    if absent:
+        tgt[0, 2] = 5000                       # not among slot 2's candidates
+    return S, ids, tgt
+
+
+def test_loss_against_torch_cross_entropy():
+    # torch's own cross-entropy and autograd, float64, as an independent route
+    S, ids, tgt = _loss_case(51)
+    rho = 4.0
+    out = O.corrector_loss(S, ids, tgt, rho)
+    N, Bm1, K, _ = S.shape
+    St = torch.tensor(S, dtype=torch.float64, requires_grad=True)
+    labels = torch.zeros((N, Bm1), dtype=torch.long)
+    coef = torch.zeros((N, Bm1), dtype=torch.float64)
+    for n in range(N):
+        for p in range(Bm1):
+            a = list(ids[n, p]).index(tgt[n, p]) if tgt[n, p] in ids[n, p] else None
+            b = list(ids[n, p + 1]).index(tgt[n, p + 1]) if tgt[n, p + 1] in ids[n, p + 1] else None
+            if a is not None and b is not None:
+                labels[n, p] = a * K + b
+                coef[n, p] = math.exp(-p / rho) / N
+    ce = torch.nn.functional.cross_entropy(St.reshape(N * Bm1, K * K), labels.reshape(-1), reduction="none")
+    L = (ce.reshape(N, Bm1) * coef).sum()
+    L.backward()
+    assert out["loss"] == pytest.approx(L.item(), rel=1e-13)
+    np.testing.assert_allclose(out["dS"], St.grad.numpy(), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(out["mask"], (coef > 0).numpy())
+    # slot 2 has no target among its candidates: pairs 1 and 2 are dropped
+    assert not out["mask"][0, 1] and not out["mask"][0, 2]
+    assert np.all(out["dS"][0, 1] == 0) and np.all(out["dS"][0, 2] == 0)
+
+
+def test_loss_closed_forms():
+    # equal scores: the joint softmax is uniform, CE = log K^2 for every pair
+    N, B, K = 2, 4, 3
+    ids = np.arange(N * B * K).reshape(N, B, K)
+    tgt = ids[:, :, 1]
+    out = O.corrector_loss(np.full((N, B - 1, K, K), 0.7), ids, tgt, 4.0)
+    w = np.exp(-np.arange(B - 1) / 4.0)
+    assert out["loss"] == pytest.approx(math.log(K * K) * w.sum(), rel=1e-14)
+    # each active pair's gradient sums to zero (softmax minus a one-hot)
+    S, ids, tgt = _loss_case(52)
+    out = O.corrector_loss(S, ids, tgt, 4.0)
+    np.testing.assert_allclose(out["dS"].sum(axis=(2, 3)), 0.0, atol=1e-15)
+    # one candidate per slot: the softmax is certain, no loss and no gradient
+    S1 = _rng(53).standard_normal((2, 3, 1, 1))
+    ids1 = np.arange(8).reshape(2, 4, 1)
+    out = O.corrector_loss(S1, ids1, ids1[:, :, 0], 4.0)
+    assert out["loss"] == 0.0 and np.all(out["dS"] == 0)
+    # a dominant label score: CE -> log(1 + (K^2 - 1) e^-D)
+    S2 = np.zeros((1, 1, 2, 2))
+    S2[0, 0, 1, 0] = 30.0
+    ids2 = np.array([[[7, 8], [9, 10]]])
+    out = O.corrector_loss(S2, ids2, np.array([[8, 9]]), 4.0)
+    assert out["loss"] == pytest.approx(math.log1p(3 * math.exp(-30.0)), rel=1e-12)
+
+
+def _bwd_case(seed):
+    g = _rng(seed)
+    N, B, K, rz, rs, H = 2, 3, 2, 3, 2, 4
+    z = g.standard_normal((N, B, K, rz))
+    s = g.standard_normal((N, B - 1, rs))
+    W1 = g.standard_normal((H, 2 * rz + rs)) * 0.7
+    b1 = g.standard_normal(H) * 0.3
+    w2 = g.standard_normal(H)
+    b2 = 0.2
+    vals = g.standard_normal((N, B, K))
+    G = g.standard_normal((N, B - 1, K, K))
+    return z, s, W1, b1, w2, b2, vals, G
+
+
+def test_score_backward_finite_differences():
+    # f(theta) = sum G * S(theta) with the (separately pinned) forward; every
+    # gradient entry against a central difference
+    z, s, W1, b1, w2, b2, vals, G = _bwd_case(54)
+    out = O.score_backward(z, s, W1, b1, w2, G)
+
+    def f(z=z, s=s, W1=W1, b1=b1, w2=w2, b2=b2, vals=vals):
+        return float((G * O.transition_scores(z, s, vals, W1, b1, w2, b2)).sum())
+
+    eps = 1e-6
+    for name, arr in (("dz", z), ("ds", s), ("dW1", W1), ("db1", b1), ("dw2", w2), ("d_cand_vals", vals)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            hi, lo = arr.copy(), arr.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            key = {"dz": "z", "ds": "s", "dW1": "W1", "db1": "b1", "dw2": "w2", "d_cand_vals": "vals"}[name]
+            num[idx] = (f(**{key: hi}) - f(**{key: lo})) / (2 * eps)
+        np.testing.assert_allclose(out[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+    num_b2 = (f(b2=b2 + eps) - f(b2=b2 - eps)) / (2 * eps)
+    assert out["db2"] == pytest.approx(num_b2, rel=1e-8)
+
+
+def test_score_backward_against_torch_autograd():
+    # a larger case through torch's autograd (float64, torch's own SiLU)
+    g = _rng(55)
+    N, B, K, rz, rs, H = 2, 5, 4, 8, 6, 16
+    z = g.standard_normal((N, B, K, rz))
+    s = g.standard_normal((N, B - 1, rs)) * 3
+    W1 = g.standard_normal((H, 2 * rz + rs)) * 0.4
+    b1 = g.standard_normal(H) * 0.3
+    w2 = g.standard_normal(H)
+    G = g.standard_normal((N, B - 1, K, K))
+    out = O.score_backward(z, s, W1, b1, w2, G)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in dict(z=z, s=s, W1=W1, b1=b1, w2=w2).items()}
+    b2 = torch.tensor(0.0, dtype=torch.float64, requires_grad=True)
+    vals = torch.zeros((N, B, K), dtype=torch.float64, requires_grad=True)
+    za = t["z"][:, :-1, :, None, :].expand(N, B - 1, K, K, rz)
+    zb = t["z"][:, 1:, None, :, :].expand(N, B - 1, K, K, rz)
+    sp = t["s"][:, :, None, None, :].expand(N, B - 1, K, K, rs)
+    x = torch.cat([za, zb, sp], dim=-1)
+    delta = torch.nn.functional.silu(x @ t["W1"].T + t["b1"]) @ t["w2"] + b2
+    S = vals[:, 1:, None, :] + delta
+    (torch.tensor(G) * S).sum().backward()
+    for name, key in (("dz", "z"), ("ds", "s"), ("dW1", "W1"), ("db1", "b1"), ("dw2", "w2")):
+        np.testing.assert_allclose(out[name], t[key].grad.numpy(), rtol=1e-12, atol=1e-12, err_msg=name)
+    assert out["db2"] == pytest.approx(b2.grad.item(), rel=1e-12)
+    np.testing.assert_allclose(out["d_cand_vals"], vals.grad.numpy(), rtol=1e-12, atol=1e-12)
