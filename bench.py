@@ -239,7 +239,18 @@ def main():
                                                       stream=stream),
         "select_discount": lambda i: dc.select_path(dims, S, cl, ids, "discount", 0.75, si, sel_tok,
                                                     stream=stream),
+        # the training side on the same grid: loss and dL/dS, then the MLP backward
+        "train_loss": lambda i: dc.loss(dims, S, ids, targets(), 4.0, stream=stream),
+        "train_backward": lambda i: dc.score_backward(dims, w, z, s, S, stream=stream),
     }
+    tgt_cache = []
+
+    def targets():
+        # one of each slot's candidates, drawn once (seeded) after top-K has run
+        if not tgt_cache:
+            pick = torch.from_numpy(np.random.default_rng(5).integers(0, K, (N, B, 1))).to(dev)
+            tgt_cache.append(torch.gather(ids.view(N, B, K), 2, pick).view(N, B).to(torch.int32).contiguous())
+        return tgt_cache[0]
     stage_us = {}
     for name, fn in stages.items():
         for i in range(3):

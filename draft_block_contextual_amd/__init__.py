@@ -23,7 +23,7 @@ DTYPE_CODE = {"f32": 0, "bf16": 1}
 
 # every entry point include/dcoco.h declares
 EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
-           "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
+           "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
            "dcoco_status_string", "dcoco_abi_version"]
 
 
@@ -38,6 +38,11 @@ class CDims(ctypes.Structure):
                 ("V", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_embed", ctypes.c_int32),
                 ("d_proj", ctypes.c_int32), ("d_z", ctypes.c_int32), ("d_pair", ctypes.c_int32),
                 ("d_mlp", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+class CMlpGrads(ctypes.Structure):
+    _fields_ = [("dW1", ctypes.c_void_p), ("db1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
+                ("db2", ctypes.c_void_p)]
 
 
 class CWeights(ctypes.Structure):
@@ -65,11 +70,13 @@ def load() -> ctypes.CDLL:
     lib.dcoco_score.argtypes = [pd, pw, vp, vp, vp, vp, vp, sz, vp]
     lib.dcoco_select.argtypes = [pd, vp, vp, vp, vp, vp, vp]
     lib.dcoco_select_path.argtypes = [pd, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+    lib.dcoco_loss.argtypes = [pd, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
+    lib.dcoco_score_backward.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, ctypes.POINTER(CMlpGrads), vp, sz, vp]
     lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     lib.dcoco_build_btable.argtypes = [pd, pw, vp, vp, vp, sz, vp]
     lib.dcoco_correct_block_btable.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
-              "dcoco_correct_block",
+              "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block",
               "dcoco_build_btable", "dcoco_correct_block_btable"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.dcoco_status_string.argtypes = [ctypes.c_int]
@@ -254,6 +261,51 @@ def select_path(dims: Dims, S, cand_logits, cand_ids, rule: str = "greedy", lam:
                                                       _ptr(cand_ids), PATH_RULES[rule], float(lam),
                                                       _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
     return sel_idx, sel_tok
+
+
+def loss(dims: Dims, S, cand_ids, target_tok, rho: float = 4.0, stream=None):
+    """dcoco_loss -> (loss [1], pair_loss [N, B-1], dS [N, B-1, K, K]), fp32."""
+    import torch
+    lib = load()
+    cd = dims.c()
+    dev = cand_ids.device
+    Bm1 = max(dims.B - 1, 1)
+    out = torch.empty(4, dtype=torch.float32, device=dev)   # a 16-byte slot for the scalar
+    pair = torch.empty((dims.n_blocks, Bm1), dtype=torch.float32, device=dev)
+    dS = torch.empty((dims.n_blocks, Bm1, dims.K, dims.K), dtype=torch.float32, device=dev)
+    _check("dcoco_loss", lib.dcoco_loss(ctypes.byref(cd), _ptr(S), _ptr(cand_ids), _ptr(target_tok),
+                                        float(rho), _ptr(out), _ptr(pair), _ptr(dS), _stream(stream)))
+    return out[:1], pair[:, :dims.B - 1], dS[:, :dims.B - 1]
+
+
+def score_backward(dims: Dims, w: Weights, z, s, dS, workspace=None, stream=None) -> dict:
+    """dcoco_score_backward -> dict of fp32 gradients: dz, ds, d_cand_logits,
+    dW1, db1, dw2, db2."""
+    import torch
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    dev = z.device
+    N, B, K = dims.n_blocks, dims.B, dims.K
+    H, rz, rs = dims.d_mlp, dims.d_z, dims.d_pair
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dz": torch.empty((N, B, K, rz), **f32), "ds": torch.empty((N, max(B - 1, 1), rs), **f32),
+           "d_cand_logits": torch.empty((N, B, K), **f32), "dW1": torch.empty((H, 2 * rz + rs), **f32),
+           "db1": torch.empty(H, **f32), "dw2": torch.empty(H, **f32), "db2": torch.empty(4, **f32)}
+    g = CMlpGrads(out["dW1"].data_ptr(), out["db1"].data_ptr(), out["dw2"].data_ptr(), out["db2"].data_ptr())
+    n = ctypes.c_size_t(0)
+    _check("dcoco_score_backward", lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), None, None, None,
+                                                            None, None, None, ctypes.byref(g), None,
+                                                            ctypes.byref(n), None))
+    ws = _workspace(n.value, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_score_backward",
+           lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), _ptr(z), _ptr(s), _ptr(dS),
+                                    _ptr(out["dz"]), _ptr(out["ds"]) if B > 1 else None,
+                                    _ptr(out["d_cand_logits"]), ctypes.byref(g), _ptr(ws), ctypes.byref(n),
+                                    _stream(stream)))
+    out["ds"] = out["ds"][:, :B - 1]
+    out["db2"] = out["db2"][:1]
+    return out
 
 
 def correct_block_workspace_bytes(dims: Dims, w: Weights, btable: bool = False) -> int:

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -236,27 +237,33 @@ hipError_t pair_term(const dcoco_dims* d, const dcoco_weights* w, const float* s
   return launch_gemm(q, st);
 }
 
-// AB = z [W1a; W1b]^T, then the grid (needs the pair term)
+// AB = z [W1a; W1b]^T (fp32)
+hipError_t ab_gemm(const dcoco_dims* d, const dcoco_weights* w, const void* z, const ScoreLayout& L,
+                   hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
+  const int RK = d->n_blocks * d->B * d->K;
+  const long long ldw1 = 2ll * rz + rs;
+  GemmProblem q{};
+  q.M = RK; q.N = 2 * H; q.Kd = rz;
+  q.A = z; q.lda = rz; q.a_dtype = dt;
+  q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 0; q.seg_end[0] = H;
+  q.w[1] = w->W1; q.ldw[1] = ldw1; q.col0[1] = rz; q.seg_end[1] = 2 * H;
+  q.w[2] = w->W1; q.ldw[2] = ldw1; q.col0[2] = rz; q.seg_end[2] = 2 * H;
+  q.w_dtype = dt;
+  q.split = 1; q.out_f32 = L.AB; q.ldo = 2 * H; q.out = nullptr;
+  return launch_gemm(q, st);
+}
+
+// AB, then the grid (needs the pair term)
 hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* cl, float* S,
                       const ScoreLayout& L, hipStream_t st) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int P = d->n_blocks * (d->B - 1);
   if (P == 0) return hipSuccess;
-  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
-  const int RK = d->n_blocks * d->B * d->K;
-  const long long ldw1 = 2ll * rz + rs;
+  const int H = d->d_mlp;
   hipError_t e;
-  {
-    GemmProblem q{};
-    q.M = RK; q.N = 2 * H; q.Kd = rz;
-    q.A = z; q.lda = rz; q.a_dtype = dt;
-    q.w[0] = w->W1; q.ldw[0] = ldw1; q.col0[0] = 0; q.seg_end[0] = H;
-    q.w[1] = w->W1; q.ldw[1] = ldw1; q.col0[1] = rz; q.seg_end[1] = 2 * H;
-    q.w[2] = w->W1; q.ldw[2] = ldw1; q.col0[2] = rz; q.seg_end[2] = 2 * H;
-    q.w_dtype = dt;
-    q.split = 1; q.out_f32 = L.AB; q.ldo = 2 * H; q.out = nullptr;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
+  if ((e = ab_gemm(d, w, z, L, st)) != hipSuccess) return e;
   GridProblem g{};
   g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.H = H; g.dtype = dt;
   g.AB = L.AB; g.C = L.C; g.nq = dt == kDtypeBf16 ? 3 : 1; g.b1 = w->b1; g.w2 = w->w2; g.b2 = w->b2;
@@ -284,11 +291,49 @@ int check_ws(void* ws, size_t* bytes, size_t need) {
   return DCOCO_OK;
 }
 
+constexpr int kMaxGradSplit = 16;
+
+struct BwdLayout {
+  ScoreLayout SL;
+  float* dAB;    // [N*B*K, 2H]
+  float* dC;     // [P, H]
+  float* dw2p;   // [P, H]
+  float* part;   // [kMaxGradSplit, H, max(d_z, d_pair)]
+};
+
+BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
+  BwdLayout L;
+  const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
+  const size_t RK = static_cast<size_t>(d->n_blocks) * d->B * d->K;
+  const size_t H = d->d_mlp;
+  L.SL = carve_score(c, d);
+  L.dAB = static_cast<float*>(c.take(sizeof(float) * RK * 2 * H));
+  L.dC = static_cast<float*>(c.take(sizeof(float) * P * H));
+  L.dw2p = static_cast<float*>(c.take(sizeof(float) * P * H));
+  L.part = static_cast<float*>(c.take(sizeof(float) * kMaxGradSplit * H * std::max(d->d_z, d->d_pair)));
+  return L;
+}
+
+// C[M, N] = sum over Kd of A(m, k) B(k, n), split over k so the launch has
+// about 256 workgroups, the splits added in order into out (row stride ldo)
+hipError_t grad_product(GemmF32Args q, int a_dt, int b_dt, float* part, float* out, long long ldo,
+                        hipStream_t st) {
+  const int tiles = ((q.M + 63) / 64) * ((q.N + 63) / 64);
+  int splits = std::max(1, std::min(kMaxGradSplit, 256 / std::max(tiles, 1)));
+  splits = std::min(splits, std::max(1, q.K / 64));
+  q.k_split = ((q.K + splits - 1) / splits + 15) / 16 * 16;
+  splits = (q.K + q.k_split - 1) / q.k_split;
+  q.C = part; q.ldc = q.N; q.c_split = static_cast<long long>(q.M) * q.N; q.accumulate = 0;
+  hipError_t e = launch_gemm_f32(q, a_dt, b_dt, st);
+  if (e != hipSuccess) return e;
+  return launch_sum_splits(part, splits, q.M, q.N, out, ldo, st);
+}
+
 }  // namespace
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 102; }
+int dcoco_abi_version(void) { return 103; }
 
 const char* dcoco_status_string(int status) {
   switch (status) {
@@ -377,6 +422,102 @@ int dcoco_select_path(const dcoco_dims* d, const float* S, const float* cand_log
   if (!path_supported(d->B, d->K)) return DCOCO_ERR_UNSUPPORTED;
   return hip_status(launch_path(S, cand_logits, cand_ids, d->n_blocks, d->B, d->K, lam, sel_idx, sel_tok,
                                 static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_loss(const dcoco_dims* d, const float* S, const int32_t* cand_ids, const int32_t* target_tok,
+               float rho, float* loss, float* pair_loss, float* dS, void* stream) {
+  int rc = check_dims(d, false);
+  if (rc != DCOCO_OK) return rc;
+  if (!(rho > 0.0f) || !std::isfinite(rho)) return DCOCO_ERR_INVALID_ARG;
+  if (!ptr_ok(cand_ids) || !ptr_ok(target_tok) || !ptr_ok(loss)) return DCOCO_ERR_INVALID_ARG;
+  if (d->B > 1 && (!ptr_ok(S) || !ptr_ok(pair_loss) || !ptr_ok(dS))) return DCOCO_ERR_INVALID_ARG;
+  return hip_status(launch_loss(S, cand_ids, target_tok, d->n_blocks, d->B, d->K, rho, pair_loss, loss, dS,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_score_backward(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
+                         const float* dS, float* dz, float* ds, float* d_cand_logits, const dcoco_mlp_grads* g,
+                         void* workspace, size_t* workspace_bytes, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  Carve c(nullptr);
+  carve_bwd(c, d);
+  rc = check_ws(workspace, workspace_bytes, c.off);
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if ((rc = check_weights(w, false, true)) != DCOCO_OK) return rc;
+  if (!g || !ptr_ok(g->dW1) || !ptr_ok(g->db1) || !ptr_ok(g->dw2) || !ptr_ok(g->db2) || !ptr_ok(dz) ||
+      !opt_ok(ds) || !opt_ok(d_cand_logits))
+    return DCOCO_ERR_INVALID_ARG;
+  const int P = d->n_blocks * (d->B - 1);
+  if (P > 0 && (!ptr_ok(z) || !ptr_ok(s) || !ptr_ok(dS))) return DCOCO_ERR_INVALID_ARG;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int rz = d->d_z, rs = d->d_pair, H = d->d_mlp;
+  const int RK = d->n_blocks * d->B * d->K;
+  const long long ldw1 = 2ll * rz + rs;
+  hipError_t e = hipSuccess;
+  if (P == 0) {
+    // no transitions: every gradient is zero
+    if (e == hipSuccess) e = launch_fill(dz, static_cast<long long>(RK) * rz, 0.f, st);
+    if (e == hipSuccess) e = launch_fill(g->dW1, H * ldw1, 0.f, st);
+    if (e == hipSuccess) e = launch_fill(g->db1, H, 0.f, st);
+    if (e == hipSuccess) e = launch_fill(g->dw2, H, 0.f, st);
+    if (e == hipSuccess) e = launch_fill(g->db2, 1, 0.f, st);
+    if (e == hipSuccess && d_cand_logits) e = launch_fill(d_cand_logits, RK, 0.f, st);
+    return hip_status(e);
+  }
+  Carve cw(workspace);
+  const BwdLayout L = carve_bwd(cw, d);
+  const char* W1 = static_cast<const char*>(w->W1);
+  const size_t es = esize(d->dtype);
+  // forward recompute: the pair term and A, B
+  if (e == hipSuccess) e = pair_term(d, w, s, L.SL, false, st);
+  if (e == hipSuccess) e = ab_gemm(d, w, z, L.SL, st);
+  if (e == hipSuccess) {
+    GridBwdArgs a{};
+    a.B = d->B; a.K = d->K; a.H = H; a.P = P; a.nq = dt == kDtypeBf16 ? 3 : 1;
+    a.AB = L.SL.AB; a.C = L.SL.C; a.b1 = w->b1; a.w2 = w->w2; a.dS = dS;
+    a.dAB = L.dAB; a.dC = L.dC; a.dw2p = L.dw2p;
+    e = launch_grid_bwd(a, dt, st);
+  }
+  if (e == hipSuccess) e = launch_colsum(L.dw2p, P, H, H, g->dw2, st);
+  if (e == hipSuccess) e = launch_colsum(L.dC, P, H, H, g->db1, st);
+  if (e == hipSuccess) e = launch_sum(dS, static_cast<long long>(P) * d->K * d->K, g->db2, st);
+  if (e == hipSuccess && d_cand_logits) e = launch_dlogit(dS, d->n_blocks, d->B, d->K, d_cand_logits, st);
+  // dW1 = [dA^T z | dB^T z | dC^T s]
+  for (int part = 0; part < 3 && e == hipSuccess; ++part) {
+    GemmF32Args q{};
+    q.M = H;
+    if (part < 2) {
+      q.N = rz; q.K = RK;
+      q.A = L.dAB + part * H; q.a_m = 1; q.a_k = 2ll * H;
+      q.B = z; q.b_k = rz; q.b_n = 1;
+      e = grad_product(q, kDtypeF32, dt, L.part, g->dW1 + part * rz, ldw1, st);
+    } else {
+      q.N = rs; q.K = P;
+      q.A = L.dC; q.a_m = 1; q.a_k = H;
+      q.B = s; q.b_k = rs; q.b_n = 1;
+      e = grad_product(q, kDtypeF32, kDtypeF32, L.part, g->dW1 + 2 * rz, ldw1, st);
+    }
+  }
+  // dz = dA W1a + dB W1b; ds = dC W1s
+  for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+    GemmF32Args q{};
+    q.M = RK; q.N = rz; q.K = H; q.k_split = H;
+    q.A = L.dAB + part * H; q.a_m = 2ll * H; q.a_k = 1;
+    q.B = W1 + es * part * rz; q.b_k = ldw1; q.b_n = 1;
+    q.C = dz; q.ldc = rz; q.c_split = 0; q.accumulate = part;
+    e = launch_gemm_f32(q, kDtypeF32, dt, st);
+  }
+  if (e == hipSuccess && ds) {
+    GemmF32Args q{};
+    q.M = P; q.N = rs; q.K = H; q.k_split = H;
+    q.A = L.dC; q.a_m = H; q.a_k = 1;
+    q.B = W1 + es * 2 * rz; q.b_k = ldw1; q.b_n = 1;
+    q.C = ds; q.ldc = rs; q.c_split = 0; q.accumulate = 0;
+    e = launch_gemm_f32(q, kDtypeF32, dt, st);
+  }
+  return hip_status(e);
 }
 
 int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h,

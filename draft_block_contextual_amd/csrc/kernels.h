@@ -102,4 +102,42 @@ bool path_supported(int B, int K);
 hipError_t launch_path(const float* S, const float* cand_logits, const int32_t* cand_ids, int N, int B, int K,
                        float lam, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
 
+// ------------------------------------------------------------ training side
+// loss per pair, its sum into loss[0], and dL/dS (see train.hip)
+hipError_t launch_loss(const float* S, const int32_t* cand_ids, const int32_t* target_tok, int N, int B, int K,
+                       float rho, float* pair_loss, float* loss, float* dS, hipStream_t st);
+
+struct GridBwdArgs {
+  int B, K, H, P, nq;
+  const float* AB;     // [N*B*K, 2H]: W1a z | W1b z
+  const float* C;      // [nq, P, H]: parts of W1s s_p
+  const void* b1;      // [H] (dtype) or null
+  const void* w2;      // [H] (dtype)
+  const float* dS;     // [P, K, K]
+  float* dAB;          // out [N*B*K, 2H]: dA | dB
+  float* dC;           // out [P, H]
+  float* dw2p;         // out [P, H]: per-pair parts of dw2
+};
+hipError_t launch_grid_bwd(const GridBwdArgs& g, int dtype, hipStream_t st);
+
+// C[m, n] (+)= sum_k A(m, k) B(k, n), A(m, k) = A[m a_m + k a_k],
+// B(k, n) = B[k b_k + n b_n]; split z writes C + z c_split
+struct GemmF32Args {
+  int M, N, K, k_split;
+  const void* A;
+  long long a_m, a_k;
+  const void* B;
+  long long b_k, b_n;
+  float* C;
+  long long ldc, c_split;
+  int accumulate;
+};
+hipError_t launch_gemm_f32(const GemmF32Args& g, int a_dtype, int b_dtype, hipStream_t st);
+hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, float* out, long long ld_out,
+                             hipStream_t st);
+hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* out, hipStream_t st);
+hipError_t launch_sum(const float* x, long long n, float* out, hipStream_t st);
+hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st);
+hipError_t launch_fill(float* x, long long n, float v, hipStream_t st);
+
 }  // namespace dcoco

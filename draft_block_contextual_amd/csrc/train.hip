@@ -1,0 +1,407 @@
+// Training side of the corrector on the same score grid: the masked,
+// decay-weighted joint-softmax loss and its gradient dL/dS, and the backward
+// of the shared scoring MLP (gradients of W1, b1, w2, b2, of z and s, and of
+// the draft logits).  Sources: Two Delta, "Two Delta makes NVIDIA Nemotron
+// 3.5 Super even faster with DCOCO", section "How we train the corrector";
+// review of arXiv 2610.12570, section "New approach: DCOCO", parts 1 and 3
+// (paper Sec. 3.2, App. A).
+#include "common.h"
+#include "kernels.h"
+
+namespace dcoco {
+namespace {
+
+constexpr int kThreads = 256;
+
+// fixed-order sum over the 256 threads of a workgroup (tree over LDS); every
+// thread gets the result
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per pair (n, p).  The label (a*, b*) is the position of the
+// target token of slot p among c_p and of slot p+1 among c_{p+1}; a pair
+// whose targets are not both present gets zero loss and zero gradient.
+// Otherwise, with the joint softmax over the pair's K^2 scores and the
+// weight w_p = exp(-p / rho) (p 0-based here):
+//   pair_loss = w_p / N * (logsumexp(S_p) - S_p(a*, b*)),
+//   dS_p      = w_p / N * (softmax(S_p) - onehot(a*, b*)).
+__global__ void __launch_bounds__(kThreads)
+loss_kernel(const float* __restrict__ S, const int32_t* __restrict__ ids, const int32_t* __restrict__ tgt,
+            int B, int K, float rho, float inv_n, float* __restrict__ pair_loss, float* __restrict__ dS) {
+  __shared__ float red[kThreads];
+  __shared__ int s_pos[2];
+  const int np = blockIdx.x;
+  const int Bm1 = B - 1;
+  const int n = np / Bm1;
+  const int p = np - n * Bm1;
+  const int tid = threadIdx.x;
+  const int l = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int per = K * K;
+  const float* Sp = S + static_cast<long long>(np) * per;
+  float* dSp = dS + static_cast<long long>(np) * per;
+  if (wv < 2) {
+    // wave 0 looks for slot p's target, wave 1 for slot p+1's
+    const long long slot = static_cast<long long>(n) * B + p + wv;
+    const int t = tgt[slot];
+    const bool hit = l < K && ids[slot * K + min(l, K - 1)] == t;
+    const uint64_t m = ballot(hit);
+    if (l == 0) s_pos[wv] = m ? __builtin_ctzll(m) : -1;
+  }
+  __syncthreads();
+  const int a = s_pos[0];
+  const int b = s_pos[1];
+  if (a < 0 || b < 0) {
+    for (int i = tid; i < per; i += kThreads) dSp[i] = 0.f;
+    if (tid == 0) pair_loss[np] = 0.f;
+    return;
+  }
+  float mx = -INFINITY;
+  for (int i = tid; i < per; i += kThreads) mx = fmaxf(mx, Sp[i]);
+  mx = block_max(mx, red);
+  float se = 0.f;
+  for (int i = tid; i < per; i += kThreads) se += expf(Sp[i] - mx);
+  se = block_sum(se, red);
+  const float coef = expf(-static_cast<float>(p) / rho) * inv_n;
+  const float inv_se = 1.0f / se;
+  const int label = a * K + b;
+  for (int i = tid; i < per; i += kThreads) {
+    const float sm = expf(Sp[i] - mx) * inv_se;
+    dSp[i] = coef * (i == label ? sm - 1.0f : sm);
+  }
+  if (tid == 0) pair_loss[np] = coef * ((mx + logf(se)) - Sp[label]);
+}
+
+// out[0] = sum of x[0..n) in a fixed order (one workgroup)
+__global__ void __launch_bounds__(kThreads) sum_kernel(const float* __restrict__ x, long long n,
+                                                       float* __restrict__ out) {
+  __shared__ float red[kThreads];
+  float v = 0.f;
+  for (long long i = threadIdx.x; i < n; i += kThreads) v += x[i];
+  v = block_sum(v, red);
+  if (threadIdx.x == 0) out[0] = v;
+}
+
+// out[c] = sum over rows r of x[r * ld + c], rows added in a fixed order:
+// 64 columns per workgroup, four row groups combined at the end
+__global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restrict__ x, int rows, int cols,
+                                                          long long ld, float* __restrict__ out) {
+  __shared__ float red[kThreads];
+  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int g = threadIdx.x >> 6;
+  const int cc = min(c, cols - 1);
+  float v = 0.f;
+  for (int r = g; r < rows; r += 4) v += x[static_cast<long long>(r) * ld + cc];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  if (g == 0 && c < cols)
+    out[c] = (red[threadIdx.x] + red[threadIdx.x + 64]) + (red[threadIdx.x + 128] + red[threadIdx.x + 192]);
+}
+
+// d l_i(b) = sum_a dS_{i-1}(a, b) for slots i >= 1, 0 for slot 0; one thread
+// per (n, i, b)
+__global__ void __launch_bounds__(kThreads) dlogit_kernel(const float* __restrict__ dS, int N, int B, int K,
+                                                          float* __restrict__ dcl) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx >= static_cast<long long>(N) * B * K) return;
+  const int b = static_cast<int>(idx % K);
+  const long long ni = idx / K;
+  const int i = static_cast<int>(ni % B);
+  const long long n = ni / B;
+  float v = 0.f;
+  if (i > 0) {
+    const float* g = dS + ((n * (B - 1) + i - 1) * K) * K + b;
+    for (int a = 0; a < K; ++a) v += g[static_cast<long long>(a) * K];
+  }
+  dcl[idx] = v;
+}
+
+__global__ void __launch_bounds__(kThreads) fill_kernel(float* __restrict__ x, long long n, float v) {
+  const long long i = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+
+// Backward of the scoring grid.  One thread per (pair, hidden unit h): with
+// A' = A_{p,a,h} + C_{p,h} (C already holds b1) and B_b = B_{p+1,b,h},
+//   u = A' + B_b, sig = 1 / (1 + e^-u), SiLU = u sig,
+//   SiLU' = sig (1 + u (1 - sig)), du = dS(a, b) w2_h SiLU',
+//   dA(a, h) = sum_b du, dB(b, h) = sum_a du, dC(h) = sum du,
+//   dw2 part(h) = sum dS(a, b) SiLU.
+// e^-u is formed as e^-A' e^-B when both exponents are within +-40 (no
+// overflow of the product), else per element.  No cross-thread reductions:
+// every sum above runs inside one thread.  The pair that ends at the last
+// slot also zeroes that slot's dA rows, and the pair that starts at slot 0
+// zeroes slot 0's dB rows, so dAB holds a full [N*B*K, 2H] gradient.
+template <int KR, typename T>
+__global__ void __launch_bounds__(kThreads) grid_bwd_kernel(GridBwdArgs g) {
+  __shared__ float sG[KR * KR];
+  const int np = blockIdx.x;
+  const int Bm1 = g.B - 1;
+  const int n = np / Bm1;
+  const int p = np - n * Bm1;
+  const int K = g.K;
+  const int H = g.H;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y * kThreads + tid;
+  const int hh = min(h, H - 1);
+  const long long ld = 2ll * H;
+  for (int i = tid; i < K * K; i += kThreads) sG[i] = g.dS[static_cast<long long>(np) * K * K + i];
+
+  float c = 0.f;
+  for (int q = 0; q < g.nq; ++q) c += g.C[(static_cast<long long>(q) * g.P + np) * H + hh];
+  if (g.b1) c += Elem<T>::to_f32(static_cast<const T*>(g.b1)[hh]);
+  const float w2h = Elem<T>::to_f32(static_cast<const T*>(g.w2)[hh]);
+  const float* Arow = g.AB + (static_cast<long long>(n) * g.B + p) * K * ld + hh;
+  const float* Brow = g.AB + (static_cast<long long>(n) * g.B + p + 1) * K * ld + H + hh;
+
+  float bv[KR], eb[KR], db[KR];
+  bool small = true;
+#pragma unroll
+  for (int b = 0; b < KR; ++b) {
+    bv[b] = b < K ? Brow[static_cast<long long>(b) * ld] : 0.f;
+    small = small && fabsf(bv[b]) <= 40.f;
+    eb[b] = expf(-bv[b]);
+    db[b] = 0.f;
+  }
+  __syncthreads();
+  float dw2 = 0.f, dc = 0.f;
+  float* dArow = g.dAB + (static_cast<long long>(n) * g.B + p) * K * ld + h;
+  for (int a = 0; a < K; ++a) {
+    const float ap = Arow[static_cast<long long>(a) * ld] + c;
+    const float* ga = sG + a * K;
+    float da = 0.f;
+    if (small && fabsf(ap) <= 40.f) {
+      const float ea = expf(-ap);
+#pragma unroll
+      for (int b = 0; b < KR; ++b) {
+        if (b < K) {
+          const float u = ap + bv[b];
+          const float sg = __builtin_amdgcn_rcpf(fmaf(ea, eb[b], 1.0f));
+          const float gab = ga[b];
+          const float du = gab * w2h * (sg * fmaf(u, 1.0f - sg, 1.0f));
+          dw2 = fmaf(gab, u * sg, dw2);
+          da += du;
+          db[b] += du;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < KR; ++b) {
+        if (b < K) {
+          const float u = ap + bv[b];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-u));
+          const float gab = ga[b];
+          const float du = gab * w2h * (sg * fmaf(u, 1.0f - sg, 1.0f));
+          dw2 = fmaf(gab, u * sg, dw2);
+          da += du;
+          db[b] += du;
+        }
+      }
+    }
+    dc += da;
+    if (h < H) dArow[static_cast<long long>(a) * ld] = da;
+  }
+  if (h >= H) return;
+  float* dBrow = g.dAB + (static_cast<long long>(n) * g.B + p + 1) * K * ld + H + h;
+#pragma unroll
+  for (int b = 0; b < KR; ++b)
+    if (b < K) dBrow[static_cast<long long>(b) * ld] = db[b];
+  g.dC[static_cast<long long>(np) * H + h] = dc;
+  g.dw2p[static_cast<long long>(np) * H + h] = dw2;
+  if (p == Bm1 - 1) {
+    float* z = g.dAB + (static_cast<long long>(n) * g.B + Bm1) * K * ld + h;
+    for (int a = 0; a < K; ++a) z[static_cast<long long>(a) * ld] = 0.f;
+  }
+  if (p == 0) {
+    float* z = g.dAB + static_cast<long long>(n) * g.B * K * ld + H + h;
+    for (int b = 0; b < K; ++b) z[static_cast<long long>(b) * ld] = 0.f;
+  }
+}
+
+// Plain fp32 tiled product C[m, n] (+)= sum_k A(m, k) B(k, n) with element
+// strides, for the gradient products (operands read as stored, bf16 or fp32,
+// and widened).  64 x 64 tile, 256 threads of 4 x 4 outputs, 16-deep k
+// stages through LDS; the load order follows whichever index of an operand is
+// contiguous.  Loads are unconditional (indices clamped) and masked to zero.
+// blockIdx.z takes one k range of a split; its partial goes to C + z * c_split.
+template <typename TA, typename TB>
+__global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmF32Args g) {
+  __shared__ __align__(16) float sA[16][68];
+  __shared__ __align__(16) float sB[16][68];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15;
+  const int ty = tid >> 4;
+  const int m0 = blockIdx.y * 64;
+  const int n0 = blockIdx.x * 64;
+  const int kb = blockIdx.z * g.k_split;
+  const int ke = min(g.K, kb + g.k_split);
+  const TA* A = static_cast<const TA*>(g.A);
+  const TB* Bm = static_cast<const TB*>(g.B);
+  const bool a_mc = g.a_m == 1;   // A contiguous along m
+  const bool b_nc = g.b_n == 1;   // B contiguous along n
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = kb; k0 < ke; k0 += 16) {
+    float av[4], bw[4];
+    int am[4], ak[4], bk[4], bn[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      am[r] = a_mc ? (tid & 63) : (tid >> 4) + 16 * r;
+      ak[r] = a_mc ? (tid >> 6) + 4 * r : (tid & 15);
+      bn[r] = b_nc ? (tid & 63) : (tid >> 4) + 16 * r;
+      bk[r] = b_nc ? (tid >> 6) + 4 * r : (tid & 15);
+      const int mm = min(m0 + am[r], g.M - 1);
+      const int ka = min(k0 + ak[r], ke - 1);
+      const int nn = min(n0 + bn[r], g.N - 1);
+      const int kk = min(k0 + bk[r], ke - 1);
+      av[r] = Elem<TA>::to_f32(A[mm * g.a_m + ka * g.a_k]);
+      bw[r] = Elem<TB>::to_f32(Bm[kk * g.b_k + nn * g.b_n]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sA[ak[r]][am[r]] = (m0 + am[r] < g.M && k0 + ak[r] < ke) ? av[r] : 0.f;
+      sB[bk[r]][bn[r]] = (n0 + bn[r] < g.N && k0 + bk[r] < ke) ? bw[r] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&sA[kk][ty * 4]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&sB[kk][tx * 4]);
+      const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float br[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* C = g.C + static_cast<long long>(blockIdx.z) * g.c_split;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nn = n0 + tx * 4 + j;
+      if (nn >= g.N) continue;
+      float* o = C + static_cast<long long>(m) * g.ldc + nn;
+      *o = g.accumulate ? *o + acc[i][j] : acc[i][j];
+    }
+  }
+}
+
+// out[r * ld_out + c] = sum over the splits s (in order) of part[s][r][c]
+__global__ void __launch_bounds__(kThreads) sum_splits_kernel(const float* __restrict__ part, int splits,
+                                                              int rows, int cols, float* __restrict__ out,
+                                                              long long ld_out) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  const long long total = static_cast<long long>(rows) * cols;
+  if (idx >= total) return;
+  float v = 0.f;
+  for (int s = 0; s < splits; ++s) v += part[s * total + idx];
+  out[(idx / cols) * ld_out + idx % cols] = v;
+}
+
+inline unsigned blocks_for(long long n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_loss(const float* S, const int32_t* cand_ids, const int32_t* target_tok, int N, int B, int K,
+                       float rho, float* pair_loss, float* loss, float* dS, hipStream_t st) {
+  const int P = N * (B - 1);
+  if (P > 0)
+    hipLaunchKernelGGL(loss_kernel, dim3(P), dim3(kThreads), 0, st, S, cand_ids, target_tok, B, K, rho,
+                       1.0f / static_cast<float>(N), pair_loss, dS);
+  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, pair_loss, static_cast<long long>(P), loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* x, long long n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, st, x, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_grid_bwd(const GridBwdArgs& g, int dtype, hipStream_t st) {
+  const dim3 grid(g.P, (g.H + kThreads - 1) / kThreads);
+#define DCOCO_BWD(KRV)                                                                           \
+  do {                                                                                           \
+    if (dtype == kDtypeBf16)                                                                     \
+      hipLaunchKernelGGL((grid_bwd_kernel<KRV, bf16>), grid, dim3(kThreads), 0, st, g);          \
+    else                                                                                         \
+      hipLaunchKernelGGL((grid_bwd_kernel<KRV, float>), grid, dim3(kThreads), 0, st, g);         \
+  } while (0)
+  if (g.K <= 8) DCOCO_BWD(8);
+  else if (g.K <= 16) DCOCO_BWD(16);
+  else if (g.K <= 32) DCOCO_BWD(32);
+  else DCOCO_BWD(64);
+#undef DCOCO_BWD
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmF32Args& g, int a_dtype, int b_dtype, hipStream_t st) {
+  const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, (g.K + g.k_split - 1) / g.k_split);
+  if (a_dtype == kDtypeBf16 && b_dtype == kDtypeBf16)
+    hipLaunchKernelGGL((gemm_f32_kernel<bf16, bf16>), grid, dim3(kThreads), 0, st, g);
+  else if (a_dtype == kDtypeBf16)
+    hipLaunchKernelGGL((gemm_f32_kernel<bf16, float>), grid, dim3(kThreads), 0, st, g);
+  else if (b_dtype == kDtypeBf16)
+    hipLaunchKernelGGL((gemm_f32_kernel<float, bf16>), grid, dim3(kThreads), 0, st, g);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<float, float>), grid, dim3(kThreads), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, float* out, long long ld_out,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(sum_splits_kernel, dim3(blocks_for(static_cast<long long>(rows) * cols)), dim3(kThreads), 0,
+                     st, part, splits, rows, cols, out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(colsum_kernel, dim3((cols + 63) / 64), dim3(kThreads), 0, st, x, rows, cols, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum(const float* x, long long n, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, x, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st) {
+  hipLaunchKernelGGL(dlogit_kernel, dim3(blocks_for(static_cast<long long>(N) * B * K)), dim3(kThreads), 0, st,
+                     dS, N, B, K, dcl);
+  return hipGetLastError();
+}
+
+}  // namespace dcoco

@@ -16,8 +16,8 @@
  *   [P2] review of arXiv 2610.12570, "Contextual Correction of Parallel Drafts
  *        for Speculative Decoding" (jaehun.me/posts/paper-2610-12570), section
  *        "New approach: DCOCO", parts 1 (paper Sec. 3.2) and 2 (paper
- *        Sec. 3.3), and section "Path selection and ablation" (paper
- *        Sec. 4.3).
+ *        Sec. 3.3), part 3 (training, paper Sec. 3.2 and App. A), and
+ *        section "Path selection and ablation" (paper Sec. 4.3).
  *
  * Conventions for every entry point
  *   - All array arguments are DEVICE pointers on the current HIP device,
@@ -169,6 +169,58 @@ int dcoco_select_path(const dcoco_dims* dims, const float* S, const float* cand_
                       const int32_t* cand_ids, int rule, float lambda, int32_t* sel_idx,
                       int32_t* sel_tok, void* stream);
 
+/* Training loss of the corrector ([P1] "How we train the corrector"; [P2]
+ * part 3, paper Sec. 3.2 and App. A).  The label of pair p is the pair of
+ * target tokens of slots p and p+1 (the target model's choices under the
+ * training context): a*_p and b*_p are their positions among the candidates
+ * of the two slots, and the pair counts (m_p = 1) only when both are
+ * present.  The pages lose the formula; the reading implemented:
+ *   L = (1/N) sum_n sum_{p=1..B-1} m_p exp(-(p-1)/rho) CE_p,
+ *   CE_p = log sum_{a,b} exp(S_p(a,b)) - S_p(a*_p, b*_p)  (joint softmax),
+ *   dL/dS_p(a,b) = (1/N) m_p exp(-(p-1)/rho) (softmax(S_p)(a,b) - [a=a*,b=b*]).
+ *   S          [n_blocks, B-1, K, K] fp32   scores (finite)
+ *   cand_ids   [n_blocks, B, K] int32       candidates
+ *   target_tok [n_blocks, B] int32          target token per slot
+ *   rho        > 0 (the pages train with 4)
+ *   loss       [1] fp32                     out: L
+ *   pair_loss  [n_blocks, B-1] fp32         out: each pair's term of L
+ *   dS         [n_blocks, B-1, K, K] fp32   out: dL/dS
+ * S, pair_loss and dS may be NULL when B == 1 (then L = 0).  Errors:
+ * rho <= 0 or not finite -> DCOCO_ERR_INVALID_ARG.  Deterministic. */
+int dcoco_loss(const dcoco_dims* dims, const float* S, const int32_t* cand_ids,
+               const int32_t* target_tok, float rho, float* loss, float* pair_loss,
+               float* dS, void* stream);
+
+/* Gradients of the shared scoring MLP, fp32, overwritten (not accumulated). */
+typedef struct {
+  float* dW1;   /* [d_mlp, 2 d_z + d_pair], columns as W1: [z_a | z_b | s] */
+  float* db1;   /* [d_mlp] (also when b1 is NULL) */
+  float* dw2;   /* [d_mlp] */
+  float* db2;   /* [1] */
+} dcoco_mlp_grads;
+
+/* Backward of the transition scores ([P2] part 1, paper Sec. 3.2): given
+ * G = dL/dS (e.g. from dcoco_loss), with x = [z_{p,a}; z_{p+1,b}; s_p] and
+ * u = W1 x + b1,
+ *   dw2 = sum G SiLU(u), db2 = sum G, du = G w2 SiLU'(u),
+ *   dW1 = sum du x^T, db1 = sum du, dx = W1^T du -> dz_{p,a}, dz_{p+1,b}, ds_p,
+ *   d l_{p+1}(b) = sum_a G(a, b)  (the draft logit term).
+ * Sums run over every pair and candidate pair; the forward's bf16 rounding of
+ * z counts as the identity.  A, B and the pair term are recomputed here.
+ *   z             [n_blocks, B, K, d_z] dtype   the forward's z
+ *   s             [n_blocks, B-1, d_pair] fp32  the forward's s
+ *   dS            [n_blocks, B-1, K, K] fp32    G
+ *   dz            [n_blocks, B, K, d_z] fp32    out
+ *   ds            [n_blocks, B-1, d_pair] fp32  out (may be NULL)
+ *   d_cand_logits [n_blocks, B, K] fp32         out (may be NULL; slot 1 gets 0)
+ *   grads                                       out (every pointer required)
+ * Workspace as for dcoco_score (query with workspace == NULL).  Deterministic:
+ * split sums are added in a fixed order. */
+int dcoco_score_backward(const dcoco_dims* dims, const dcoco_weights* w, const void* z,
+                         const float* s, const float* dS, float* dz, float* ds,
+                         float* d_cand_logits, const dcoco_mlp_grads* grads,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
 /* The whole path for n_blocks draft blocks: top-K, representations, pair
  * states, transition scores and the greedy walk, on one stream.
  *   logits [n_blocks*B, V], h [n_blocks, B, d_hidden], E [V, d_embed]: dtype
@@ -213,7 +265,8 @@ int dcoco_correct_block_btable(const dcoco_dims* dims, const dcoco_weights* w,
 const char* dcoco_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor): 101 adds the table
- * entry points, 102 dcoco_select_path. */
+ * entry points, 102 dcoco_select_path, 103 dcoco_loss and
+ * dcoco_score_backward. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import draft_block_contextual_amd as dc
-    assert lib.dcoco_abi_version() == 102
+    assert lib.dcoco_abi_version() == 103
     assert dc.status_string(0) == "ok"
     for code in (-1, -2, -3, -4):
         assert dc.status_string(code) not in ("ok", "unknown status")
@@ -170,3 +170,28 @@ def test_select_path_argument_checks(lib):
     wide = _dims(n_blocks=2, B=300, K=64).c()
     assert call(2, 0.5, dims=wide) == -2         # B*K > 16384
     assert call(1, 1.0, dims=_dims(n_blocks=2, B=16, K=65).c()) == -2   # K > 64
+
+
+def test_training_argument_checks(lib):
+    import draft_block_contextual_amd as dc
+    fake = ctypes.c_void_p(1 << 20)
+    cd = _dims(n_blocks=2).c()
+    for rho in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.dcoco_loss(ctypes.byref(cd), fake, fake, fake, rho, fake, fake, fake, None) == -1
+    assert lib.dcoco_loss(ctypes.byref(cd), fake, fake, fake, 4.0, None, fake, fake, None) == -1
+    assert lib.dcoco_loss(ctypes.byref(cd), None, fake, fake, 4.0, fake, fake, fake, None) == -1
+    # backward: size query, then missing gradient buffers
+    cw = dc.CWeights()
+    g = dc.CMlpGrads()
+    n = ctypes.c_size_t(0)
+    assert lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, None, None,
+                                    ctypes.byref(g), None, ctypes.byref(n), None) == 0
+    # A and B, their gradients, the pair term and the split partials
+    assert n.value >= 2 * 2 * 16 * 16 * 512 * 4 * 2
+    cw.W1 = cw.w2 = 1 << 20
+    nb = ctypes.c_size_t(n.value)
+    assert lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), fake, fake, fake, fake, None, None,
+                                    ctypes.byref(g), fake, ctypes.byref(nb), None) == -1
+    small = ctypes.c_size_t(n.value - 256)
+    assert lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), fake, fake, fake, fake, None, None,
+                                    ctypes.byref(g), fake, ctypes.byref(small), None) == -3

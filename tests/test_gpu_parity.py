@@ -536,3 +536,150 @@ def test_full_q8b_32_btable_sampled():
     # the two device paths differ only in the fp32 summation order of P_e E_v
     np.testing.assert_array_equal(out_t["cand_ids"], out_p["cand_ids"])
     assert np.max(np.abs(out_t["S"] - out_p["S"])) < 3e-2
+
+
+# ------------------------------------------------------------- training
+
+def _targets(ids, V, seed, absent=0.2):
+    """A target token per slot: one of the slot's candidates, or (with
+    probability `absent`) a token no candidate list holds."""
+    g = np.random.default_rng(seed)
+    N, B, K = ids.shape
+    pick = ids[np.arange(N)[:, None], np.arange(B)[None, :], g.integers(0, K, (N, B))]
+    return np.where(g.random((N, B)) < absent, V + 7, pick).astype(np.int32)
+
+
+def _dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _dev_i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _bf16_dev(x):
+    # values already representable in bf16: their top 16 bits
+    import torch
+    bits = (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_bf16", "small_f32", "mid_bf16", "k64_small"])
+def test_loss_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case loss {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    S = ref["S"].astype(np.float32)
+    ids = ref["cand_ids"].astype(np.int32)
+    tgt = _targets(ids, D.V, 61)
+    dims = dc.Dims.from_synth(D)
+    L, pair, dS = dc.loss(dims, _dev_f32(S), _dev_i32(ids), _dev_i32(tgt), rho=4.0)
+    torch.cuda.synchronize()
+    R = O.corrector_loss(S.astype(np.float64), ids, tgt, 4.0)
+    assert R["mask"].any()
+    if R["mask"].size >= 20:
+        assert not R["mask"].all()      # some pairs are dropped
+    # fp32 softmax: each term is within a few ulps of its own size
+    assert abs(float(L.cpu()[0]) - R["loss"]) <= 1e-5 * max(1.0, abs(R["loss"]))
+    np.testing.assert_allclose(_np(pair), R["pair_loss"], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(_np(dS), R["dS"], rtol=1e-4, atol=1e-7)
+    assert np.all(_np(dS)[~R["mask"]] == 0)
+
+
+def test_loss_degenerate_cases():
+    import draft_block_contextual_amd as dc
+    import torch
+    g = np.random.default_rng(62)
+    # every target absent: zero loss and zero gradient
+    N, B, K = 3, 5, 4
+    S = g.standard_normal((N, B - 1, K, K)).astype(np.float32)
+    ids = g.integers(0, 1000, (N, B, K)).astype(np.int32)
+    dims = dc.Dims(N, B, K, 2000, 32, 32, 32, 32, 32, 32, "f32")
+    L, pair, dS = dc.loss(dims, _dev_f32(S), _dev_i32(ids), _dev_i32(np.full((N, B), 5000)), 4.0)
+    torch.cuda.synchronize()
+    assert float(L.cpu()[0]) == 0.0 and np.all(_np(dS) == 0) and np.all(_np(pair) == 0)
+    # one candidate per slot: the softmax is certain
+    ids1 = np.arange(N * B).reshape(N, B, 1).astype(np.int32)
+    dims1 = dc.Dims(N, B, 1, 2000, 32, 32, 32, 32, 32, 32, "f32")
+    S1 = g.standard_normal((N, B - 1, 1, 1)).astype(np.float32)
+    L, pair, dS = dc.loss(dims1, _dev_f32(S1), _dev_i32(ids1), _dev_i32(ids1[:, :, 0]), 4.0)
+    torch.cuda.synchronize()
+    assert float(L.cpu()[0]) == 0.0 and np.all(_np(dS) == 0)
+    # equal scores: log K^2 per active pair, weighted
+    ids2 = np.arange(N * B * K).reshape(N, B, K).astype(np.int32)
+    L, pair, dS = dc.loss(dims, _dev_f32(np.full((N, B - 1, K, K), 0.25)), _dev_i32(ids2),
+                          _dev_i32(ids2[:, :, 2]), 4.0)
+    torch.cuda.synchronize()
+    want = np.log(K * K) * np.exp(-np.arange(B - 1) / 4.0).sum()
+    assert abs(float(L.cpu()[0]) - want) <= 1e-5 * want
+    # one slot: no pairs, zero loss
+    dimsb = dc.Dims(N, 1, K, 2000, 32, 32, 32, 32, 32, 32, "f32")
+    L, _, _ = dc.loss(dimsb, None, _dev_i32(ids[:, :1]), _dev_i32(ids[:, :1, 0]), 4.0)
+    torch.cuda.synchronize()
+    assert float(L.cpu()[0]) == 0.0
+
+
+def _grad_check(got, R, name, rel=2e-4):
+    """fp32 against float64: each gradient within rel of its largest entry
+    (the sums run over thousands of terms of both signs), and no element off by
+    more than 1e-3 of its own size beyond that floor."""
+    g = got.astype(np.float64)
+    r = np.asarray(R, np.float64)
+    scale = max(np.abs(r).max(), 1e-30)
+    err = np.abs(g - r)
+    assert err.max() <= rel * scale, (name, err.max(), scale)
+    assert np.all(err <= 1e-3 * np.abs(r) + rel * scale), name
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "k32_small",
+                                  "k64_small", "widez_bf16"])
+def test_score_backward_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case score_backward {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    dims, w, _, _, _ = device_inputs(inp)
+    g = np.random.default_rng(63)
+    G = g.standard_normal(ref["S"].shape) / D.n_blocks        # a dense upstream gradient
+    z = ref["z"]
+    s32 = ref["s"].astype(np.float32)
+    zd = _bf16_dev(z) if D.dtype == "bf16" else _dev_f32(z)
+    out = dc.score_backward(dims, w, zd, _dev_f32(s32), _dev_f32(G.astype(np.float32)))
+    torch.cuda.synchronize()
+    wt = {k: O.to_f64(inp[k], D.dtype) for k in ("W1", "b1", "w2")}
+    R = O.score_backward(z, s32.astype(np.float64), wt["W1"], wt["b1"], wt["w2"],
+                         G.astype(np.float32).astype(np.float64))
+    for key in ("dz", "ds", "dW1", "db1", "dw2", "d_cand_vals"):
+        got = _np(out["d_cand_logits" if key == "d_cand_vals" else key])
+        _grad_check(got, R[key], f"{name}:{key}")
+    assert abs(float(_np(out["db2"])[0]) - R["db2"]) <= 1e-5 * max(1.0, np.abs(G).sum())
+
+
+def test_training_step_end_to_end():
+    # loss then backward on one config, as a training step would chain them
+    import draft_block_contextual_amd as dc
+    import torch
+    name = "small_bf16"
+    inp = _inputs(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    dims, w, _, _, _ = device_inputs(inp)
+    ids = ref["cand_ids"].astype(np.int32)
+    tgt = _targets(ids, D.V, 64, absent=0.1)
+    S32 = ref["S"].astype(np.float32)
+    L, _, dS = dc.loss(dims, _dev_f32(S32), _dev_i32(ids), _dev_i32(tgt), 4.0)
+    out = dc.score_backward(dims, w, _bf16_dev(ref["z"]), _dev_f32(ref["s"].astype(np.float32)), dS)
+    torch.cuda.synchronize()
+    RL = O.corrector_loss(S32.astype(np.float64), ids, tgt, 4.0)
+    wt = {k: O.to_f64(inp[k], D.dtype) for k in ("W1", "b1", "w2")}
+    R = O.score_backward(ref["z"], ref["s"].astype(np.float32).astype(np.float64), wt["W1"], wt["b1"], wt["w2"],
+                         RL["dS"])
+    for key in ("dz", "dW1", "dw2", "db1"):
+        _grad_check(_np(out[key]), R[key], f"e2e:{key}", rel=5e-4)
