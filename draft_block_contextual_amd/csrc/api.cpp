@@ -293,12 +293,23 @@ int check_ws(void* ws, size_t* bytes, size_t need) {
 
 constexpr int kMaxGradSplit = 16;
 
+// bf16 storage with N*B*K a multiple of 32: the two large gradient products
+// run on bf16 MFMA over a two-part split of the fp32 gradients
+bool bwd_on_mfma(const dcoco_dims* d) {
+  return d->dtype == DCOCO_BF16 && (static_cast<long long>(d->n_blocks) * d->B * d->K) % 32 == 0;
+}
+
 struct BwdLayout {
   ScoreLayout SL;
-  float* dAB;    // [N*B*K, 2H]
-  float* dC;     // [P, H]
-  float* dw2p;   // [P, H]
-  float* part;   // [kMaxGradSplit, H, max(d_z, d_pair)]
+  float* dAB;      // [N*B*K, 2H]
+  float* dC;       // [P, H]
+  float* dw2p;     // [P, H]
+  float* part;     // [kMaxGradSplit, H, max(d_z, d_pair)]
+  float* red;      // partial sums of the reductions
+  void* A1;        // bf16 [N*B*K, 4H]: [dA | dB] hi, then lo
+  void* At;        // bf16 [2H, 2 N*B*K]: its transpose, parts side by side
+  void* Zt;        // bf16 [d_z, 2 N*B*K]: z transposed, twice
+  void* W1t;       // bf16 [d_z, 4H]
 };
 
 BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
@@ -311,6 +322,14 @@ BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
   L.dC = static_cast<float*>(c.take(sizeof(float) * P * H));
   L.dw2p = static_cast<float*>(c.take(sizeof(float) * P * H));
   L.part = static_cast<float*>(c.take(sizeof(float) * kMaxGradSplit * H * std::max(d->d_z, d->d_pair)));
+  const size_t red = 2 * (static_cast<size_t>(colsum_blocks(static_cast<int>(P))) + 1) * H +
+                     P * d->K * d->K / 8192 + 2;
+  L.red = static_cast<float*>(c.take(sizeof(float) * red));
+  const bool mf = bwd_on_mfma(d);
+  L.A1 = c.take(mf ? 2 * RK * 4 * H : 0);
+  L.At = c.take(mf ? 2 * 2 * H * 2 * RK : 0);
+  L.Zt = c.take(mf ? 2 * static_cast<size_t>(d->d_z) * 2 * RK : 0);
+  L.W1t = c.take(mf ? 2 * static_cast<size_t>(d->d_z) * 4 * H : 0);
   return L;
 }
 
@@ -480,34 +499,67 @@ int dcoco_score_backward(const dcoco_dims* d, const dcoco_weights* w, const void
     a.dAB = L.dAB; a.dC = L.dC; a.dw2p = L.dw2p;
     e = launch_grid_bwd(a, dt, st);
   }
-  if (e == hipSuccess) e = launch_colsum(L.dw2p, P, H, H, g->dw2, st);
-  if (e == hipSuccess) e = launch_colsum(L.dC, P, H, H, g->db1, st);
-  if (e == hipSuccess) e = launch_sum(dS, static_cast<long long>(P) * d->K * d->K, g->db2, st);
+  float* red2 = L.red + 2 * (colsum_blocks(P) + 1) * static_cast<long long>(H);
+  if (e == hipSuccess) e = launch_colsum(L.dw2p, P, H, H, L.red, g->dw2, st);
+  if (e == hipSuccess) e = launch_colsum(L.dC, P, H, H, L.red, g->db1, st);
+  if (e == hipSuccess) e = launch_sum(dS, static_cast<long long>(P) * d->K * d->K, red2, g->db2, st);
   if (e == hipSuccess && d_cand_logits) e = launch_dlogit(dS, d->n_blocks, d->B, d->K, d_cand_logits, st);
-  // dW1 = [dA^T z | dB^T z | dC^T s]
-  for (int part = 0; part < 3 && e == hipSuccess; ++part) {
-    GemmF32Args q{};
-    q.M = H;
-    if (part < 2) {
-      q.N = rz; q.K = RK;
+  if (bwd_on_mfma(d)) {
+    // [dA | dB] = hi + lo (two bf16 parts); z and W1 are bf16 already
+    if (e == hipSuccess) e = launch_split_t(L.dAB, true, RK, 2 * H, L.A1, L.At, st);
+    if (e == hipSuccess) e = launch_split_t(z, false, RK, rz, nullptr, L.Zt, st);
+    if (e == hipSuccess) e = launch_w1t(w->W1, H, rz, ldw1, L.W1t, st);
+    // dz = [dA | dB]_hi [W1a; W1b] + [dA | dB]_lo [W1a; W1b], one product over 4H
+    if (e == hipSuccess) {
+      GemmProblem q{};
+      q.M = RK; q.N = rz; q.Kd = 4 * H;
+      q.A = L.A1; q.lda = 4ll * H; q.a_dtype = kDtypeBf16;
+      q.w[0] = L.W1t; q.ldw[0] = 4ll * H; q.col0[0] = 0;
+      q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = rz;
+      q.w_dtype = kDtypeBf16;
+      q.split = 1; q.out_f32 = dz; q.ldo = rz; q.out = nullptr;
+      e = launch_gemm(q, st);
+    }
+    // dW1a, dW1b: (dA or dB)^T z over 2 N*B*K (both parts), split over k
+    for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+      GemmProblem q{};
+      q.M = H; q.N = rz; q.Kd = 2 * RK;
+      q.A = static_cast<const char*>(L.At) + 2ll * part * H * 2 * RK; q.lda = 2ll * RK; q.a_dtype = kDtypeBf16;
+      q.w[0] = L.Zt; q.ldw[0] = 2ll * RK; q.col0[0] = 0;
+      q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = rz;
+      q.w_dtype = kDtypeBf16;
+      int split = 1;
+      while (split < kMaxGradSplit && ((H + 63) / 64) * ((rz + 63) / 64) * split < 256 && q.Kd / (2 * split) >= 256)
+        split *= 2;
+      q.split = split; q.out_f32 = L.part; q.ldo = rz; q.out = nullptr;
+      e = launch_gemm(q, st);
+      if (e == hipSuccess) e = launch_sum_splits(L.part, split, H, rz, g->dW1 + part * rz, ldw1, st);
+    }
+  } else {
+    // fp32 products: dW1a, dW1b, then dz = dA W1a + dB W1b
+    for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+      GemmF32Args q{};
+      q.M = H; q.N = rz; q.K = RK;
       q.A = L.dAB + part * H; q.a_m = 1; q.a_k = 2ll * H;
       q.B = z; q.b_k = rz; q.b_n = 1;
       e = grad_product(q, kDtypeF32, dt, L.part, g->dW1 + part * rz, ldw1, st);
-    } else {
-      q.N = rs; q.K = P;
-      q.A = L.dC; q.a_m = 1; q.a_k = H;
-      q.B = s; q.b_k = rs; q.b_n = 1;
-      e = grad_product(q, kDtypeF32, kDtypeF32, L.part, g->dW1 + 2 * rz, ldw1, st);
+    }
+    for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+      GemmF32Args q{};
+      q.M = RK; q.N = rz; q.K = H; q.k_split = H;
+      q.A = L.dAB + part * H; q.a_m = 2ll * H; q.a_k = 1;
+      q.B = W1 + es * part * rz; q.b_k = ldw1; q.b_n = 1;
+      q.C = dz; q.ldc = rz; q.c_split = 0; q.accumulate = part;
+      e = launch_gemm_f32(q, kDtypeF32, dt, st);
     }
   }
-  // dz = dA W1a + dB W1b; ds = dC W1s
-  for (int part = 0; part < 2 && e == hipSuccess; ++part) {
+  // dW1s = dC^T s (fp32: s stays fp32)
+  if (e == hipSuccess) {
     GemmF32Args q{};
-    q.M = RK; q.N = rz; q.K = H; q.k_split = H;
-    q.A = L.dAB + part * H; q.a_m = 2ll * H; q.a_k = 1;
-    q.B = W1 + es * part * rz; q.b_k = ldw1; q.b_n = 1;
-    q.C = dz; q.ldc = rz; q.c_split = 0; q.accumulate = part;
-    e = launch_gemm_f32(q, kDtypeF32, dt, st);
+    q.M = H; q.N = rs; q.K = P;
+    q.A = L.dC; q.a_m = 1; q.a_k = H;
+    q.B = s; q.b_k = rs; q.b_n = 1;
+    e = grad_product(q, kDtypeF32, kDtypeF32, L.part, g->dW1 + 2 * rz, ldw1, st);
   }
   if (e == hipSuccess && ds) {
     GemmF32Args q{};

@@ -135,8 +135,17 @@ struct GemmF32Args {
 hipError_t launch_gemm_f32(const GemmF32Args& g, int a_dtype, int b_dtype, hipStream_t st);
 hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, float* out, long long ld_out,
                              hipStream_t st);
-hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* out, hipStream_t st);
-hipError_t launch_sum(const float* x, long long n, float* out, hipStream_t st);
+// column sums of x [rows, cols] (row stride ld) into out [cols]; tmp holds
+// the partial rows (colsum_tmp_floats of them)
+int colsum_blocks(int rows);
+hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* tmp, float* out, hipStream_t st);
+// out[0] = sum of x[0..n); tmp holds n / 8192 + 1 partial sums
+hipError_t launch_sum(const float* x, long long n, float* tmp, float* out, hipStream_t st);
+// two-part bf16 split of X [M, C] fp32 (or a bf16 copy): A1 [M, 2C] = [hi | lo]
+// (optional), At [C, 2M] = its transpose with the parts side by side
+hipError_t launch_split_t(const void* X, bool split, int M, int C, void* A1, void* At, hipStream_t st);
+// W1t [rz, 4H] bf16 from W1 [H, ldw] bf16 (see train.hip)
+hipError_t launch_w1t(const void* W1, int H, int rz, long long ldw, void* W1t, hipStream_t st);
 hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st);
 hipError_t launch_fill(float* x, long long n, float v, hipStream_t st);
 

@@ -97,30 +97,48 @@ loss_kernel(const float* __restrict__ S, const int32_t* __restrict__ ids, const 
   if (tid == 0) pair_loss[np] = coef * ((mx + logf(se)) - Sp[label]);
 }
 
-// out[0] = sum of x[0..n) in a fixed order (one workgroup)
-__global__ void __launch_bounds__(kThreads) sum_kernel(const float* __restrict__ x, long long n,
+// out[blockIdx.x] = sum of x[blockIdx.x * chunk, ...+chunk) in a fixed order;
+// eight independent loads per thread and round (indices clamped, masked)
+__global__ void __launch_bounds__(kThreads) sum_kernel(const float* __restrict__ x, long long n, long long chunk,
                                                        float* __restrict__ out) {
   __shared__ float red[kThreads];
+  const long long b0 = static_cast<long long>(blockIdx.x) * chunk;
+  const long long b1 = min(n, b0 + chunk);
   float v = 0.f;
-  for (long long i = threadIdx.x; i < n; i += kThreads) v += x[i];
+  for (long long i0 = b0 + threadIdx.x; i0 < b1; i0 += 8 * kThreads) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = x[min(i0 + j * kThreads, n - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += i0 + j * kThreads < b1 ? t[j] : 0.f;
+  }
   v = block_sum(v, red);
-  if (threadIdx.x == 0) out[0] = v;
+  if (threadIdx.x == 0) out[blockIdx.x] = v;
 }
 
-// out[c] = sum over rows r of x[r * ld + c], rows added in a fixed order:
-// 64 columns per workgroup, four row groups combined at the end
+// Column sums in a fixed order.  Workgroup (bx, by) takes 64 columns of the
+// rows [by * kColRows, +kColRows): four row groups of eight rows, loads all in
+// flight, combined through LDS into out[by * cols + c] (one partial row per
+// row block; a second launch with rows = number of blocks adds those).
+constexpr int kColRows = 32;
 __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restrict__ x, int rows, int cols,
                                                           long long ld, float* __restrict__ out) {
   __shared__ float red[kThreads];
   const int c = blockIdx.x * 64 + (threadIdx.x & 63);
   const int g = threadIdx.x >> 6;
   const int cc = min(c, cols - 1);
+  const int r0 = blockIdx.y * kColRows + g * (kColRows / 4);
+  float t[kColRows / 4];
+#pragma unroll
+  for (int j = 0; j < kColRows / 4; ++j) t[j] = x[static_cast<long long>(min(r0 + j, rows - 1)) * ld + cc];
   float v = 0.f;
-  for (int r = g; r < rows; r += 4) v += x[static_cast<long long>(r) * ld + cc];
+#pragma unroll
+  for (int j = 0; j < kColRows / 4; ++j) v += r0 + j < rows ? t[j] : 0.f;
   red[threadIdx.x] = v;
   __syncthreads();
   if (g == 0 && c < cols)
-    out[c] = (red[threadIdx.x] + red[threadIdx.x + 64]) + (red[threadIdx.x + 128] + red[threadIdx.x + 192]);
+    out[static_cast<long long>(blockIdx.y) * cols + c] =
+        (red[threadIdx.x] + red[threadIdx.x + 64]) + (red[threadIdx.x + 128] + red[threadIdx.x + 192]);
 }
 
 // d l_i(b) = sum_a dS_{i-1}(a, b) for slots i >= 1, 0 for slot 0; one thread
@@ -331,6 +349,66 @@ __global__ void __launch_bounds__(kThreads) sum_splits_kernel(const float* __res
   out[(idx / cols) * ld_out + idx % cols] = v;
 }
 
+// Two-part bf16 split of an fp32 matrix X [M, C]:
+// X = hi + lo + e with hi = bf16(X), lo = bf16(X - hi), |e| <= 2^-17 |X|.
+// Writes A1 [M, 2C] = [hi | lo] (row-major, when A1 is not null) and the
+// transpose At [C, 2M] with At[j][q M + m] = part q of X[m][j].  A bf16 input
+// (SPLIT false) is copied into both halves of At unchanged.  64 x 64 tiles
+// through LDS so both stores are coalesced.
+template <typename TI, bool SPLIT>
+__global__ void __launch_bounds__(kThreads) split_t_kernel(const TI* __restrict__ X, int M, int C,
+                                                           uint16_t* __restrict__ A1, uint16_t* __restrict__ At) {
+  __shared__ uint16_t sH[64][66];
+  __shared__ uint16_t sL[64][66];
+  const int m0 = blockIdx.y * 64;
+  const int j0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const int lj = tid & 63;
+  const int j = min(j0 + lj, C - 1);
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r) {
+    const int lm = r * 4 + (tid >> 6);
+    const int m = min(m0 + lm, M - 1);
+    uint16_t hi, lo;
+    if constexpr (SPLIT) {
+      const float x = X[static_cast<long long>(m) * C + j];
+      hi = f32_to_bf16(x);
+      lo = f32_to_bf16(x - bf16_to_f32(hi));
+    } else {
+      hi = lo = X[static_cast<long long>(m) * C + j].bits;
+    }
+    sH[lm][lj] = hi;
+    sL[lm][lj] = lo;
+    if (A1 && m0 + lm < M && j0 + lj < C) {
+      A1[static_cast<long long>(m) * 2 * C + j] = hi;
+      A1[static_cast<long long>(m) * 2 * C + C + j] = lo;
+    }
+  }
+  __syncthreads();
+  const int lm = tid & 63;
+  if (m0 + lm >= M) return;
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r) {
+    const int jj = r * 4 + (tid >> 6);
+    if (j0 + jj >= C) break;
+    const long long row = static_cast<long long>(j0 + jj) * 2 * M;
+    At[row + m0 + lm] = sH[lm][jj];
+    At[row + M + m0 + lm] = sL[lm][jj];
+  }
+}
+
+// W1t [rz, 4H] bf16: W1t[c][q 2H + j] = W1[j][c] (j < H) or W1[j - H][rz + c],
+// for q = 0, 1 (the two halves meet the hi and lo parts of [dA | dB])
+__global__ void __launch_bounds__(kThreads) w1t_kernel(const uint16_t* __restrict__ W1, int H, int rz,
+                                                       long long ldw, uint16_t* __restrict__ W1t) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx >= static_cast<long long>(rz) * 4 * H) return;
+  const int c = static_cast<int>(idx / (4 * H));
+  const int k = static_cast<int>(idx % (4 * H));
+  const int j = k % (2 * H);
+  W1t[idx] = j < H ? W1[static_cast<long long>(j) * ldw + c] : W1[static_cast<long long>(j - H) * ldw + rz + c];
+}
+
 inline unsigned blocks_for(long long n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -341,7 +419,25 @@ hipError_t launch_loss(const float* S, const int32_t* cand_ids, const int32_t* t
   if (P > 0)
     hipLaunchKernelGGL(loss_kernel, dim3(P), dim3(kThreads), 0, st, S, cand_ids, target_tok, B, K, rho,
                        1.0f / static_cast<float>(N), pair_loss, dS);
-  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, pair_loss, static_cast<long long>(P), loss);
+  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, pair_loss, static_cast<long long>(P),
+                     static_cast<long long>(P), loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_t(const void* X, bool split, int M, int C, void* A1, void* At, hipStream_t st) {
+  const dim3 grid((C + 63) / 64, (M + 63) / 64);
+  if (split)
+    hipLaunchKernelGGL((split_t_kernel<float, true>), grid, dim3(kThreads), 0, st, static_cast<const float*>(X), M,
+                       C, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At));
+  else
+    hipLaunchKernelGGL((split_t_kernel<bf16, false>), grid, dim3(kThreads), 0, st, static_cast<const bf16*>(X), M,
+                       C, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At));
+  return hipGetLastError();
+}
+
+hipError_t launch_w1t(const void* W1, int H, int rz, long long ldw, void* W1t, hipStream_t st) {
+  hipLaunchKernelGGL(w1t_kernel, dim3(blocks_for(static_cast<long long>(rz) * 4 * H)), dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(W1), H, rz, ldw, static_cast<uint16_t*>(W1t));
   return hipGetLastError();
 }
 
@@ -388,13 +484,27 @@ hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, 
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(colsum_kernel, dim3((cols + 63) / 64), dim3(kThreads), 0, st, x, rows, cols, ld, out);
-  return hipGetLastError();
+int colsum_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
+
+hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* tmp, float* out, hipStream_t st) {
+  const int rb = colsum_blocks(rows);
+  if (rb == 1) {
+    hipLaunchKernelGGL(colsum_kernel, dim3((cols + 63) / 64, 1), dim3(kThreads), 0, st, x, rows, cols, ld, out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(colsum_kernel, dim3((cols + 63) / 64, rb), dim3(kThreads), 0, st, x, rows, cols, ld, tmp);
+  return launch_colsum(tmp, rb, cols, cols, tmp + static_cast<long long>(rb) * cols, out, st);
 }
 
-hipError_t launch_sum(const float* x, long long n, float* out, hipStream_t st) {
-  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, x, n, out);
+hipError_t launch_sum(const float* x, long long n, float* tmp, float* out, hipStream_t st) {
+  const long long chunk = 8192;
+  const long long nb = (n + chunk - 1) / chunk;
+  if (nb <= 1) {
+    hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, x, n, n, out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(sum_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, x, n, chunk, tmp);
+  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, tmp, nb, nb, out);
   return hipGetLastError();
 }
 

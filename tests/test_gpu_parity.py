@@ -683,3 +683,41 @@ def test_training_step_end_to_end():
                          RL["dS"])
     for key in ("dz", "dW1", "dw2", "db1"):
         _grad_check(_np(out[key]), R[key], f"e2e:{key}", rel=5e-4)
+
+
+def test_score_backward_full_q8b_32_sampled():
+    # the full 32-block launch (two-part bf16 MFMA products, split sums) with
+    # the upstream gradient nonzero in two blocks only: the oracle computes
+    # those two blocks, every other block's dz must be exactly zero
+    import draft_block_contextual_amd as dc
+    import torch
+    D = synth.get_config("q8b_32").dims
+    N, B, K, rz, rs, H = D.n_blocks, D.B, D.K, D.r_z, D.r_s, D.H
+    print(f"case score_backward q8b_32 N={N} B={B} K={K}", flush=True)
+    g = np.random.default_rng(65)
+
+    def bf(x):
+        return (np.asarray(x, np.float32).view(np.uint32) + 0x8000 >> 16 << 16).view(np.float32).astype(np.float64)
+
+    z = bf(g.standard_normal((N, B, K, rz)))
+    s = (g.standard_normal((N, B - 1, rs)) * 30).astype(np.float32)
+    W1 = bf(g.standard_normal((H, 2 * rz + rs)) * np.sqrt(2.0 / (H + 2 * rz + rs)))
+    b1 = bf(g.standard_normal(H) * 0.1)
+    w2 = bf(g.standard_normal(H) * np.sqrt(2.0 / (H + 1)))
+    G = np.zeros((N, B - 1, K, K), np.float32)
+    blocks = [0, 17]
+    G[blocks] = g.standard_normal((len(blocks), B - 1, K, K)).astype(np.float32) / N
+    dims = dc.Dims.from_synth(D)
+    w = dc.Weights(P_e=None, P_h=None, W_f=None, W_pair=None, W1=_bf16_dev(W1), b1=_bf16_dev(b1), w2=_bf16_dev(w2),
+                   b2=0.0)
+    out = dc.score_backward(dims, w, _bf16_dev(z), _dev_f32(s), _dev_f32(G))
+    torch.cuda.synchronize()
+    R = O.score_backward(z[blocks], s[blocks].astype(np.float64), W1, b1, w2, G[blocks].astype(np.float64))
+    dz = _np(out["dz"])
+    others = np.setdiff1d(np.arange(N), blocks)
+    assert np.all(dz[others] == 0)
+    _grad_check(dz[blocks], R["dz"], "full:dz")
+    _grad_check(_np(out["ds"])[blocks], R["ds"], "full:ds")
+    for key in ("dW1", "db1", "dw2"):
+        _grad_check(_np(out[key]), R[key], f"full:{key}")
+    _grad_check(_np(out["d_cand_logits"])[blocks], R["d_cand_vals"], "full:dcl")
