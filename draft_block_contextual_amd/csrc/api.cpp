@@ -304,7 +304,7 @@ struct BwdLayout {
   float* dAB;      // [N*B*K, 2H]
   float* dC;       // [P, H]
   float* dw2p;     // [P, H]
-  float* part;     // [kMaxGradSplit, H, max(d_z, d_pair)]
+  float* part;     // [kMaxGradSplit, max(H, P), max(d_z, d_pair)]
   float* red;      // partial sums of the reductions
   void* A1;        // bf16 [N*B*K, 4H]: [dA | dB] hi, then lo
   void* At;        // bf16 [2H, 2 N*B*K]: its transpose, parts side by side
@@ -321,7 +321,8 @@ BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
   L.dAB = static_cast<float*>(c.take(sizeof(float) * RK * 2 * H));
   L.dC = static_cast<float*>(c.take(sizeof(float) * P * H));
   L.dw2p = static_cast<float*>(c.take(sizeof(float) * P * H));
-  L.part = static_cast<float*>(c.take(sizeof(float) * kMaxGradSplit * H * std::max(d->d_z, d->d_pair)));
+  L.part = static_cast<float*>(
+      c.take(sizeof(float) * kMaxGradSplit * std::max(H, P) * std::max(d->d_z, d->d_pair)));
   const size_t red = 2 * (static_cast<size_t>(colsum_blocks(static_cast<int>(P))) + 1) * H +
                      P * d->K * d->K / 8192 + 2;
   L.red = static_cast<float*>(c.take(sizeof(float) * red));
@@ -563,11 +564,10 @@ int dcoco_score_backward(const dcoco_dims* d, const dcoco_weights* w, const void
   }
   if (e == hipSuccess && ds) {
     GemmF32Args q{};
-    q.M = P; q.N = rs; q.K = H; q.k_split = H;
+    q.M = P; q.N = rs; q.K = H;
     q.A = L.dC; q.a_m = H; q.a_k = 1;
     q.B = W1 + es * 2 * rz; q.b_k = ldw1; q.b_n = 1;
-    q.C = ds; q.ldc = rs; q.c_split = 0; q.accumulate = 0;
-    e = launch_gemm_f32(q, kDtypeF32, dt, st);
+    e = grad_product(q, kDtypeF32, dt, L.part, ds, rs, st);
   }
   return hip_status(e);
 }

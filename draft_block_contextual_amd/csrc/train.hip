@@ -197,11 +197,19 @@ __global__ void __launch_bounds__(kThreads) grid_bwd_kernel(GridBwdArgs g) {
   const float* Arow = g.AB + (static_cast<long long>(n) * g.B + p) * K * ld + hh;
   const float* Brow = g.AB + (static_cast<long long>(n) * g.B + p + 1) * K * ld + H + hh;
 
-  float bv[KR], eb[KR], db[KR];
+  // every row of B (and, for KR <= 32, of A) is loaded before the first use:
+  // unconditional loads with the row clamped, so none waits for another
+  constexpr int KA = KR <= 32 ? KR : 1;
+  float bv[KR], eb[KR], db[KR], av[KA];
+#pragma unroll
+  for (int b = 0; b < KR; ++b) bv[b] = Brow[static_cast<long long>(min(b, K - 1)) * ld];
+  if constexpr (KR <= 32) {
+#pragma unroll
+    for (int a = 0; a < KR; ++a) av[a] = Arow[static_cast<long long>(min(a, K - 1)) * ld];
+  }
   bool small = true;
 #pragma unroll
   for (int b = 0; b < KR; ++b) {
-    bv[b] = b < K ? Brow[static_cast<long long>(b) * ld] : 0.f;
     small = small && fabsf(bv[b]) <= 40.f;
     eb[b] = expf(-bv[b]);
     db[b] = 0.f;
@@ -210,7 +218,15 @@ __global__ void __launch_bounds__(kThreads) grid_bwd_kernel(GridBwdArgs g) {
   float dw2 = 0.f, dc = 0.f;
   float* dArow = g.dAB + (static_cast<long long>(n) * g.B + p) * K * ld + h;
   for (int a = 0; a < K; ++a) {
-    const float ap = Arow[static_cast<long long>(a) * ld] + c;
+    float ar;
+    if constexpr (KR <= 32) {
+      ar = av[0];
+#pragma unroll
+      for (int t = 1; t < KR; ++t) ar = a == t ? av[t] : ar;
+    } else {
+      ar = Arow[static_cast<long long>(a) * ld];
+    }
+    const float ap = ar + c;
     const float* ga = sG + a * K;
     float da = 0.f;
     if (small && fabsf(ap) <= 40.f) {
