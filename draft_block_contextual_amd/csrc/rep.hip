@@ -272,17 +272,25 @@ struct GatherArgs {
   int idmax;
 };
 
-template <int BM, int SPLIT, int MODE, bool PAIR, bool GATHER = false>
+// NCOL W rows (output columns) per LDS chunk, NCOL / 4 per wave.  Workgroup
+// (x, y) takes rows [x BM, +BM) and output columns [y ncols_wg, +ncols_wg) in
+// chunks of NCOL; a launch with one column group per workgroup row has
+// gridDim.y == 1 and ncols_wg == N.  With several column groups each one
+// normalises the same rows (cheap next to the loads), and in gf mode
+// assembles its share of the pair-state columns.
+template <int BM, int SPLIT, int MODE, bool PAIR, bool GATHER = false, int NCOL = kLgCols>
 __global__ void __launch_bounds__(256)
 ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, float eps,
                  const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
                  bf16* __restrict__ out_bf, const float* __restrict__ row_bias, int row_div, PairArgs pa,
-                 GatherArgs ga) {
+                 GatherArgs ga, int ncols_wg) {
   constexpr int kStr = 256 * 2 + 16;         // LDS bytes per normalised row
   constexpr int RPW = BM / 4;                // LN rows per wave
   constexpr int TM = BM / 16;
-  constexpr int TN = 4;                      // 64 columns per wave
-  __shared__ __align__(1024) char wl[kLgCols * kLgRowBytes];
+  constexpr int TN = NCOL / 64;              // NCOL / 4 columns per wave
+  constexpr int CW = NCOL / 4;
+  static_assert(NCOL % 64 == 0 && NCOL <= kLgCols, "column chunk");
+  __shared__ __align__(1024) char wl[NCOL * kLgRowBytes];
   __shared__ __align__(16) char tile[BM * kStr];
 
   const int tid = threadIdx.x;
@@ -290,14 +298,16 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
   const int wv = tid >> 6;
   const int m0 = blockIdx.x * BM;
   const int cr = r >> 3;                     // 16-byte k chunks per W row
+  const int nb = blockIdx.y * ncols_wg;      // this workgroup's output columns
+  const int ne = min(N, nb + ncols_wg);
 
-  // 128 one-KB copies per chunk (two W rows each); wave wv issues copies
+  // NCOL / 2 one-KB copies per chunk (two W rows each); wave wv issues copies
   // wv, wv + 4, ...; slots whose logical chunk is past r copy the row's first
   // chunk and are never read
   auto issue_w = [&](int n0) {
     const int p = l & 31;
 #pragma unroll 8
-    for (int i = 0; i < kLgCols / 8; ++i) {
+    for (int i = 0; i < NCOL / 8; ++i) {
       const int j = wv + 4 * i;
       const int row = 2 * j + (l >> 5);
       const int c = p ^ (row & 15);
@@ -306,7 +316,7 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
       dma16(g, __builtin_amdgcn_readfirstlane(lds_offset(wl) + j * 1024));
     }
   };
-  issue_w(0);
+  issue_w(nb);
 
   // z mode: the row bias of every output this lane stores, fetched before the
   // LN phase so its latency hides behind the LN and MFMA work
@@ -320,10 +330,10 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
       for (int v = 0; v < 4; ++v) {
         const float* rb = row_bias + static_cast<long long>(min(m0 + a * 16 + fq * 4 + v, M - 1) / row_div) * N;
 #pragma unroll
-        for (int b = 0; b < TN; ++b) bias[a][v][b] = rb[min(n0 + wv * 64 + b * 16 + frow, N - 1)];
+        for (int b = 0; b < TN; ++b) bias[a][v][b] = rb[min(n0 + wv * CW + b * 16 + frow, N - 1)];
       }
   };
-  if constexpr (MODE == 1) load_bias(0);
+  if constexpr (MODE == 1) load_bias(nb);
 
   if constexpr (GATHER) {
     // ---- table rows of this wave's RPW operand rows: lanes 0-31 and 32-63
@@ -357,8 +367,13 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
   // ---- pair states of this workgroup's rows (loads in flight with the
   // weight copy; float4 items of (row, 4 columns), 1024 per batch)
   if constexpr (PAIR) {
-    const int q4 = pa.rs / 4;
-    const int items = BM * q4;
+    // this column group's share of the pair-state columns (all of them when
+    // the share would not be whole float4 items)
+    const int groups = gridDim.y;
+    const bool share = pa.rs % (4 * groups) == 0;
+    const int q4 = share ? pa.rs / (4 * groups) : pa.rs / 4;
+    const int jb = share ? static_cast<int>(blockIdx.y) * q4 * 4 : 0;
+    const int items = (share || blockIdx.y == 0) ? BM * q4 : 0;
     for (int base = 0; base < items; base += 1024) {
       float4 sum[4];
       bool ok[4];
@@ -367,7 +382,7 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
       for (int k = 0; k < 4; ++k) {
         const int item = base + k * 256 + tid;
         const int row = item / q4;
-        const int j = (item - row * q4) * 4;
+        const int j = jb + (item - row * q4) * 4;
         const int m = m0 + row;
         const int i = m % pa.B;
         ok[k] = item < items && m < M && i < pa.B - 1;
@@ -411,8 +426,8 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
     }
   }
 
-  for (int n0 = 0; n0 < N; n0 += kLgCols) {
-    if (n0 > 0) {
+  for (int n0 = nb; n0 < ne; n0 += NCOL) {
+    if (n0 > nb) {
       __syncthreads();                       // every wave is done with the last chunk
       issue_w(n0);
       if constexpr (MODE == 1) load_bias(n0);
@@ -433,7 +448,7 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
                     tile + (a * 16 + frow) * kStr + c * 16));
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
-        const int row = wv * 64 + b * 16 + frow;
+        const int row = wv * CW + b * 16 + frow;
         fw[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
                     wl + row * kLgRowBytes + (c ^ (row & 15)) * 16));
       }
@@ -457,8 +472,8 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
         for (int v = 0; v < 4; ++v)
 #pragma unroll
           for (int b = 0; b < TN; ++b) {
-            const int n = n0 + wv * 64 + b * 16 + frow;
-            if (mrow[a][v] < M && n < N)
+            const int n = n0 + wv * CW + b * 16 + frow;
+            if (mrow[a][v] < M && n < ne)
               out_bf[static_cast<long long>(mrow[a][v]) * N + n] = bf16{f32_to_bf16(acc[a][b][v] + bias[a][v][b])};
           }
     } else {
@@ -468,8 +483,8 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
         for (int v = 0; v < 4; ++v)
 #pragma unroll
           for (int b = 0; b < TN; ++b) {
-            const int n = n0 + wv * 64 + b * 16 + frow;
-            if (mrow[a][v] < M && n < N) out_f32[static_cast<long long>(mrow[a][v]) * N + n] = acc[a][b][v];
+            const int n = n0 + wv * CW + b * 16 + frow;
+            if (mrow[a][v] < M && n < ne) out_f32[static_cast<long long>(mrow[a][v]) * N + n] = acc[a][b][v];
           }
     }
   }
@@ -518,7 +533,7 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
 #define DCOCO_LNW(BMV, SP, MD)                                                                      \
   hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD, false>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, \
                      M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div, PairArgs{},      \
-                     GatherArgs{})
+                     GatherArgs{}, N)
 #define DCOCO_LNW_SPLIT(BMV, MD)                 \
   if (split == 1) DCOCO_LNW(BMV, 1, MD);         \
   else if (split == 2) DCOCO_LNW(BMV, 2, MD);    \
@@ -552,10 +567,11 @@ hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r,
   pa.s = s; pa.s3 = static_cast<uint16_t*>(s3);
   pa.total = static_cast<long long>(M / B) * (B - 1) * rs;
   const bf16* Wb = static_cast<const bf16*>(W);
-#define DCOCO_LNP(SP)                                                                                    \
-  hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, true>), dim3((M + 15) / 16), dim3(256), 0, st, Y, M, ldy, 0, \
-                     r, eps, Wb, ldw, wcol0, N, gf, static_cast<bf16*>(nullptr), static_cast<const float*>(nullptr), \
-                     1, pa, GatherArgs{})
+  // few rows: the output columns are spread over four workgroups of 64
+#define DCOCO_LNP(SP)                                                                                             \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, true, false, 64>), dim3((M + 15) / 16, (N + 63) / 64), dim3(256), \
+                     0, st, Y, M, ldy, 0, r, eps, Wb, ldw, wcol0, N, gf, static_cast<bf16*>(nullptr),               \
+                     static_cast<const float*>(nullptr), 1, pa, GatherArgs{}, 64)
   if (split == 1) DCOCO_LNP(1);
   else if (split == 2) DCOCO_LNP(2);
   else DCOCO_LNP(4);
@@ -578,7 +594,7 @@ hipError_t launch_gather_gemm(const void* tab, const int32_t* ids, int idmax, in
 #define DCOCO_LNG_G(BMV)                                                                                  \
   hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, 1, 1, false, true>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, \
                      static_cast<const float*>(nullptr), M, r, 0, r, 1.0f, Wb, ldw, wcol0, N,                \
-                     static_cast<float*>(nullptr), ob, row_bias, row_div, PairArgs{}, ga)
+                     static_cast<float*>(nullptr), ob, row_bias, row_div, PairArgs{}, ga, N)
   if (M >= 4096) DCOCO_LNG_G(32);
   else DCOCO_LNG_G(16);
 #undef DCOCO_LNG_G
