@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling HBM counters)")
     ap.add_argument("--no-btable", action="store_true", help="skip the table-path timing")
+    ap.add_argument("--no-lm-head", action="store_true", help="skip the fused LM-head top-K timing")
     ap.add_argument("--null-stream", action="store_true",
                     help="launch on the null stream instead of a stream of our own")
     return ap.parse_args()
@@ -268,6 +269,45 @@ def main():
         stage_us[name] = float(a.elapsed_time(b) * 1e3 / args.stage_reps)
     print(f"# stage us: {stage_us}", file=sys.stderr, flush=True)
 
+    # ---- next row: the drafter's LM head fused with top-K (head tied to E),
+    # beside the same product through the BLAS library followed by dcoco_topk
+    lm_head = None
+    if dt == "bf16" and D.d == D.e and not args.no_lm_head:
+        L = synth.make_lm_head_inputs(cfg, base["E"])
+        hd = to_dev(L["hd"], dt, dev)
+        for _ in range(3):
+            dc.lm_head_topk(dims, hd, E, ids, cl, stream=stream)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = 10
+        a.record(stream)
+        for _ in range(reps):
+            dc.lm_head_topk(dims, hd, E, ids, cl, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        fused_us = a.elapsed_time(b) * 1e3 / reps
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                lg = torch.matmul(hd, E.t())
+                dc.topk(dims, lg, ids, cl, stream=stream)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                lg = torch.matmul(hd, E.t())
+                dc.topk(dims, lg, ids, cl, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        unfused_us = a.elapsed_time(b) * 1e3 / reps
+        flops = 2.0 * N * B * D.V * D.d
+        lm_head = {"us": round(fused_us, 1), "tflops": round(flops / (fused_us * 1e-6) / 1e12, 1),
+                   "mfma_frac": round(flops / (fused_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "unfused_us": round(unfused_us, 1),
+                   "shape": f"[{N * B}, {D.d}] x [{D.V}, {D.d}]^T, top-{K}, bf16"}
+        print(f"# lm head + top-K: {fused_us:.1f} us fused, {unfused_us:.1f} us as library GEMM + dcoco_topk",
+              file=sys.stderr, flush=True)
+        del lg, hd
+
     work = algorithmic_work(D)
     # Dominant kernel: top-K, one launch per dcoco_topk call, so the events
     # around that call time exactly that kernel.  It is bound by reading the
@@ -334,6 +374,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "btable_path": btable,
+        "lm_head_topk": lm_head,
     }
     if args.sweep:
         sweep = {}

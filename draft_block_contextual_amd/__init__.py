@@ -23,7 +23,7 @@ DTYPE_CODE = {"f32": 0, "bf16": 1}
 
 # every entry point include/dcoco.h declares
 EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
-           "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
+           "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
            "dcoco_status_string", "dcoco_abi_version"]
 
 
@@ -71,12 +71,13 @@ def load() -> ctypes.CDLL:
     lib.dcoco_select.argtypes = [pd, vp, vp, vp, vp, vp, vp]
     lib.dcoco_select_path.argtypes = [pd, vp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp]
     lib.dcoco_loss.argtypes = [pd, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
+    lib.dcoco_lm_head_topk.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
     lib.dcoco_score_backward.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, ctypes.POINTER(CMlpGrads), vp, sz, vp]
     lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     lib.dcoco_build_btable.argtypes = [pd, pw, vp, vp, vp, sz, vp]
     lib.dcoco_correct_block_btable.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
-              "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block",
+              "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block",
               "dcoco_build_btable", "dcoco_correct_block_btable"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.dcoco_status_string.argtypes = [ctypes.c_int]
@@ -261,6 +262,28 @@ def select_path(dims: Dims, S, cand_logits, cand_ids, rule: str = "greedy", lam:
                                                       _ptr(cand_ids), PATH_RULES[rule], float(lam),
                                                       _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
     return sel_idx, sel_tok
+
+
+def lm_head_topk(dims: Dims, hd, W_lm, cand_ids=None, cand_logits=None, workspace=None, stream=None):
+    """dcoco_lm_head_topk -> (cand_ids [N*B, K] int32, cand_logits [N*B, K] fp32)."""
+    import torch
+    lib = load()
+    cd = dims.c()
+    dev = hd.device
+    R = dims.n_blocks * dims.B
+    if cand_ids is None:
+        cand_ids = torch.empty((R, dims.K), dtype=torch.int32, device=dev)
+    if cand_logits is None:
+        cand_logits = torch.empty((R, dims.K), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t(0)
+    _check("dcoco_lm_head_topk", lib.dcoco_lm_head_topk(ctypes.byref(cd), None, None, None, None, None,
+                                                        ctypes.byref(n), None))
+    ws = _workspace(n.value, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_lm_head_topk", lib.dcoco_lm_head_topk(ctypes.byref(cd), _ptr(hd), _ptr(W_lm), _ptr(cand_ids),
+                                                        _ptr(cand_logits), _ptr(ws), ctypes.byref(n),
+                                                        _stream(stream)))
+    return cand_ids, cand_logits
 
 
 def loss(dims: Dims, S, cand_ids, target_tok, rho: float = 4.0, stream=None):

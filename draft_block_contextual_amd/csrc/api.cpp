@@ -353,7 +353,7 @@ hipError_t grad_product(GemmF32Args q, int a_dt, int b_dt, float* part, float* o
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 103; }
+int dcoco_abi_version(void) { return 104; }
 
 const char* dcoco_status_string(int status) {
   switch (status) {
@@ -442,6 +442,19 @@ int dcoco_select_path(const dcoco_dims* d, const float* S, const float* cand_log
   if (!path_supported(d->B, d->K)) return DCOCO_ERR_UNSUPPORTED;
   return hip_status(launch_path(S, cand_logits, cand_ids, d->n_blocks, d->B, d->K, lam, sel_idx, sel_tok,
                                 static_cast<hipStream_t>(stream)));
+}
+
+int dcoco_lm_head_topk(const dcoco_dims* d, const void* hd, const void* W_lm, int32_t* cand_ids,
+                       float* cand_logits, void* workspace, size_t* workspace_bytes, void* stream) {
+  int rc = check_dims(d, false);
+  if (rc != DCOCO_OK) return rc;
+  const int M = d->n_blocks * d->B;
+  if (d->dtype != DCOCO_BF16 || !lm_head_topk_supported(M, d->V, d->d_hidden, d->K)) return DCOCO_ERR_UNSUPPORTED;
+  rc = check_ws(workspace, workspace_bytes, lm_head_workspace_bytes(M, d->V, d->K));
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if (!ptr_ok(hd) || !ptr_ok(W_lm) || !ptr_ok(cand_ids) || !ptr_ok(cand_logits)) return DCOCO_ERR_INVALID_ARG;
+  return hip_status(launch_lm_head_topk(hd, W_lm, M, d->V, d->d_hidden, d->K, workspace, cand_ids, cand_logits,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int dcoco_loss(const dcoco_dims* d, const float* S, const int32_t* cand_ids, const int32_t* target_tok,

@@ -15,11 +15,13 @@
 // both operands, so any k order the instruction uses pairs them correctly.
 // Large reductions are split over grid.z into fp32 partial sums that the
 // consumer adds in a fixed order (deterministic, no atomics).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
 #include "dma.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace dcoco {
 
@@ -252,51 +254,49 @@ constexpr int kDmaRow = 128;
 
 __device__ __forceinline__ int dma_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// WM x WN waves, each owning a (BM / WM) x (BN / WN) block of the tile.
-template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
-__global__ void __launch_bounds__(64 * WM * WN)
-gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
-  constexpr int NW = WM * WN;
-  constexpr int kABytes = BM * kDmaRow;
-  constexpr int kWBytes = BN * kDmaRow;
-  constexpr int kStage = kABytes + kWBytes;
-  constexpr int AJ = kABytes / 1024 / NW;  // A load instructions per wave per stage
-  constexpr int WJ = kWBytes / 1024 / NW;
-  constexpr int IPS = AJ + WJ;
-  constexpr int MW = BM / WM;              // wave block
-  constexpr int NWB = BN / WN;
-  constexpr int TM = MW / 16;
-  constexpr int TN = NWB / 16;
+// Geometry of a BM x BN tile computed by WM x WN waves, each owning a
+// (BM / WM) x (BN / WN) block of 16 x 16 MFMA tiles, with a ring of STAGES
+// 64-deep k stages.
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct DmaTile {
+  static constexpr int NW = WM * WN;
+  static constexpr int kABytes = BM * kDmaRow;
+  static constexpr int kWBytes = BN * kDmaRow;
+  static constexpr int kStage = kABytes + kWBytes;
+  static constexpr int AJ = kABytes / 1024 / NW;  // A load instructions per wave per stage
+  static constexpr int WJ = kWBytes / 1024 / NW;
+  static constexpr int IPS = AJ + WJ;
+  static constexpr int MW = BM / WM;              // wave block
+  static constexpr int NWB = BN / WN;
+  static constexpr int TM = MW / 16;
+  static constexpr int TN = NWB / 16;
   static_assert(AJ >= 1 && WJ >= 1 && AJ * NW * 1024 == kABytes && WJ * NW * 1024 == kWBytes,
                 "tile does not split into whole 1 KB copies per wave");
   static_assert(TM >= 1 && TN >= 1 && TM * 16 * WM == BM && TN * 16 * WN == BN, "wave grid");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
-  // one LDS object per ring slot: the compiler tracks direct-to-LDS loads per
-  // object, so reads of one slot need not wait for loads into the others
-  __shared__ __align__(1024) char sm0[kStage];
-  __shared__ __align__(1024) char sm1[kStage];
-  __shared__ __align__(1024) char sm2[STAGES >= 3 ? kStage : 16];
-  __shared__ __align__(1024) char sm3[STAGES == 4 ? kStage : 16];
+};
 
+// The k loop of one tile: acc = A[m0 : m0 + BM, kbeg : kend] W[n0 : n0 + BN,
+// kbeg : kend]^T (kend - kbeg a multiple of 64) through the LDS ring sm0..sm3
+// (one LDS object per slot: the compiler tracks direct-to-LDS loads per
+// object, so reads of one slot need not wait for loads into the others).
+// Every lane always issues its loads (rows past the edge re-read a valid row
+// and are never stored), so vmcnt counts are exact.  Leaves every load
+// complete; the caller synchronises before it reuses the ring.
+template <int BM, int BN, int WM, int WN, int STAGES>
+__device__ __forceinline__ void dma_tile_mainloop(
+    const GemmDev& p, int m0, int n0, int kbeg, int kend, char* sm0, char* sm1, char* sm2, char* sm3,
+    f32x4_t (&acc)[DmaTile<BM, BN, WM, WN, STAGES>::TM][DmaTile<BM, BN, WM, WN, STAGES>::TN]) {
+  using G = DmaTile<BM, BN, WM, WN, STAGES>;
+  constexpr int NW = G::NW, AJ = G::AJ, WJ = G::WJ, IPS = G::IPS, MW = G::MW, NWB = G::NWB;
+  constexpr int TM = G::TM, TN = G::TN, kABytes = G::kABytes;
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wv = tid >> 6;
   const int wm = wv / WN;
   const int wn = wv % WN;
-  int bid = blockIdx.x;
-  if (remap) bid = (bid % 8) * (static_cast<int>(gridDim.x) / 8) + bid / 8;
-  const int tn = bid % tiles_n;
-  bid /= tiles_n;
-  const int tm = bid % tiles_m;
-  const int zs = bid / tiles_m;
-  const int n0 = tn * BN;
-  const int m0 = tm * BM;
-  const int kbeg = zs * p.ksplit;
-  const int kend = min(p.Kd, kbeg + p.ksplit);
   const int nk = kend > kbeg ? (kend - kbeg) / 64 : 0;
 
-  // every lane always issues its loads (rows past the edge re-read a valid
-  // row and are never stored), so vmcnt counts are exact
   const char* srcA[AJ];
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
@@ -334,7 +334,6 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
       dma16(srcW[j] + static_cast<long long>(k0) * 2, b0 + kABytes + j * NW * 1024);
   };
 
-  f32x4_t acc[TM][TN];
 #pragma unroll
   for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -399,6 +398,37 @@ gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
       if (it + 3 < nk) step(std::integral_constant<int, 3>{}, it + 3);
     }
   }
+}
+
+// One output tile (or one k split of it) per workgroup.
+template <int BM, int BN, int WM, int WN, int STAGES, int MODE>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_bf16_dma_kernel(GemmDev p, int tiles_m, int tiles_n, int remap) {
+  using G = DmaTile<BM, BN, WM, WN, STAGES>;
+  constexpr int MW = G::MW, NWB = G::NWB, TM = G::TM, TN = G::TN, kStage = G::kStage;
+  __shared__ __align__(1024) char sm0[kStage];
+  __shared__ __align__(1024) char sm1[kStage];
+  __shared__ __align__(1024) char sm2[STAGES >= 3 ? kStage : 16];
+  __shared__ __align__(1024) char sm3[STAGES == 4 ? kStage : 16];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv / WN;
+  const int wn = wv % WN;
+  int bid = blockIdx.x;
+  if (remap) bid = (bid % 8) * (static_cast<int>(gridDim.x) / 8) + bid / 8;
+  const int tn = bid % tiles_n;
+  bid /= tiles_n;
+  const int tm = bid % tiles_m;
+  const int zs = bid / tiles_m;
+  const int n0 = tn * BN;
+  const int m0 = tm * BM;
+  const int kbeg = zs * p.ksplit;
+  const int kend = min(p.Kd, kbeg + p.ksplit);
+
+  f32x4_t acc[TM][TN];
+  dma_tile_mainloop<BM, BN, WM, WN, STAGES>(p, m0, n0, kbeg, kend, sm0, sm1, sm2, sm3, acc);
 
   // epilogue; with a bias, all bias values are fetched (clamped, branch-free)
   // before any store so the loads overlap
@@ -524,7 +554,231 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Drafter LM head fused with top-K: logits l_i(v) = W_lm[v] . hd_i are formed
+// tile by tile on MFMA, rounded to bf16 (the drafter's stored logit), and
+// each workgroup keeps, per row, the top K of every vocabulary tile it has
+// seen; the logits never reach memory.  Workgroup (tm, g) takes rows
+// [128 tm, +128) and vocabulary tiles g, g + groups, ...  Per tile, after the
+// k loop, the 128 x 256 keys are staged in the (now idle) LDS ring; each wave
+// then takes 16 rows: the tile's composites above the row's current K-th best
+// are merged into its sorted list (a few per tile: inserted one by one; many,
+// as on the first tile: an exact selection over list + tile).  The lists of
+// all groups are merged by lm_head_merge_kernel.
+constexpr int kLmBM = 128;
+constexpr int kLmBN = 256;
+constexpr int kLmMaxK = 16;
+using LmTile = DmaTile<kLmBM, kLmBN, 2, 4, 2>;
+
+__device__ __forceinline__ uint32_t key16_of(float x) { return order_key(bf16{f32_to_bf16(x)}); }
+
+__global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int tiles_m, int tiles_n, int groups,
+                                                           int xcd_map, uint64_t* __restrict__ part) {
+  constexpr int TM = LmTile::TM, TN = LmTile::TN, MW = LmTile::MW, NWB = LmTile::NWB;
+  __shared__ __align__(1024) char sm0[LmTile::kStage];
+  __shared__ __align__(1024) char sm1[LmTile::kStage];
+  __shared__ uint64_t s_top[kLmBM][kLmMaxK];
+  __shared__ uint64_t s_kth[kLmBM];
+  constexpr int kRowBytes = kLmBN * 2;                   // staged keys of one row
+  constexpr int kRows0 = LmTile::kStage / kRowBytes;     // rows that fit in sm0
+  static_assert(kLmBM - kRows0 <= LmTile::kStage / kRowBytes, "keys fit the ring");
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv / 4;
+  const int wn = wv % 4;
+  const int b = blockIdx.x;
+  int tm, g;
+  if (xcd_map) {
+    // the row tiles of one vocabulary group share an XCD (and its L2)
+    const int idx = b / 8;
+    tm = idx % tiles_m;
+    g = (idx / tiles_m) * 8 + b % 8;
+  } else {
+    tm = b % tiles_m;
+    g = b / tiles_m;
+  }
+  const int m0 = tm * kLmBM;
+  auto keyrow = [&](int r) -> uint16_t* {
+    return reinterpret_cast<uint16_t*>(r < kRows0 ? sm0 + r * kRowBytes : sm1 + (r - kRows0) * kRowBytes);
+  };
+  for (int i = tid; i < kLmBM * kLmMaxK; i += 512) (&s_top[0][0])[i] = 0ull;
+  for (int i = tid; i < kLmBM; i += 512) s_kth[i] = 0ull;
+
+  for (int tn = g; tn < tiles_n; tn += groups) {
+    const int n0 = tn * kLmBN;
+    f32x4_t acc[TM][TN];
+    dma_tile_mainloop<kLmBM, kLmBN, 2, 4, 2>(p, m0, n0, 0, p.Kd, sm0, sm1, sm0, sm0, acc);
+    __syncthreads();                         // every wave is done with the ring
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int bb = 0; bb < TN; ++bb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = wm * MW + a * 16 + (l >> 4) * 4 + v;
+          const int c = wn * NWB + bb * 16 + (l & 15);
+          keyrow(r)[c] = n0 + c < p.N ? static_cast<uint16_t>(key16_of(acc[a][bb][v])) : 0;
+        }
+    __syncthreads();
+    for (int i = 0; i < kLmBM / 8; ++i) {
+      const int r = wv + 8 * i;
+      const uint64_t thr = s_kth[r];
+      const uint16_t* kr = keyrow(r);
+      uint64_t c[5];
+      c[0] = l < K ? s_top[r][l] : 0ull;     // the current list, sorted
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = q * 64 + l;
+        const uint32_t key = kr[col];
+        const uint64_t cc = key ? make_comp(key, static_cast<uint32_t>(n0 + col)) : 0ull;
+        c[q + 1] = cc > thr ? cc : 0ull;
+        n += __popcll(ballot(c[q + 1] != 0ull));
+      }
+      if (n == 0) continue;
+      uint64_t cur = c[0];
+      if (n <= 8 && thr != 0ull) {
+        // insert each newcomer into the sorted list (lanes 0..K-1)
+#pragma unroll
+        for (int q = 1; q < 5; ++q) {
+          uint64_t m = ballot(c[q] != 0ull);
+          while (m) {
+            const int src = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint64_t x = __shfl(c[q], src, kWave);
+            const int pos = __popcll(ballot(l < K && cur > x));
+            const uint64_t up = __shfl_up(cur, 1, kWave);
+            cur = l < pos ? cur : (l == pos ? x : up);
+          }
+        }
+      } else {
+        bool sel[5];
+        select_topk<5, 16>(c, K, sel);
+        // compact the selection into lanes 0..K-1, then sort it
+        uint64_t* scratch = &s_top[r][0];
+        int base = 0;
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+          const uint64_t m = ballot(sel[q]);
+          __builtin_amdgcn_wave_barrier();
+          if (sel[q]) scratch[base + lanes_below(m)] = c[q];
+          base += __popcll(m);
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t mine = l < base ? scratch[l] : 0ull;
+        int rank = 0;
+        for (int j = 0; j < base; ++j) rank += __shfl(mine, j, kWave) > mine ? 1 : 0;
+        cur = 0ull;
+        for (int j = 0; j < base; ++j) {
+          const uint64_t xj = __shfl(mine, j, kWave);
+          const int rj = __shfl(rank, j, kWave);
+          cur = l == rj ? xj : cur;
+        }
+      }
+      if (l < K) s_top[r][l] = cur;
+      const uint64_t last = __shfl(cur, K - 1, kWave);
+      if (l == 0) s_kth[r] = last;           // 0 while the list is not full
+    }
+    __syncthreads();                         // the next tile's loads reuse the ring
+  }
+  for (int i = tid; i < kLmBM * K; i += 512) {
+    const int r = i / K;
+    const int j = i - r * K;
+    if (m0 + r < p.M) part[(static_cast<long long>(g) * p.M + m0 + r) * K + j] = s_top[r][j];
+  }
+}
+
+// bf16 pattern of an order key (keys of -0 and +0 coincide: +0 comes back)
+__device__ __forceinline__ float value_of_key16(uint32_t k) {
+  const uint32_t bits = k >= 0x8000u ? k - 0x8000u : ((0x8000u - k) | 0x8000u);
+  return bf16_to_f32(static_cast<uint16_t>(bits));
+}
+
+// One wave per row: the top K of the groups' lists, sorted (value desc, id
+// asc), ids and bf16 values out.
+template <int Q>
+__global__ void __launch_bounds__(64) lm_head_merge_kernel(const uint64_t* __restrict__ part, int groups, int M,
+                                                           int K, int32_t* __restrict__ ids, float* __restrict__ vals) {
+  __shared__ uint64_t s_fin[64];
+  const int row = blockIdx.x;
+  const int l = threadIdx.x;
+  uint64_t c[Q];
+  bool sel[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = q * kWave + l;
+    const int gq = i / K;
+    c[q] = gq < groups ? part[(static_cast<long long>(gq) * M + row) * K + (i - gq * K)] : 0ull;
+  }
+  select_topk<Q, 16>(c, K, sel);
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t m = ballot(sel[q]);
+    if (sel[q]) s_fin[base + lanes_below(m)] = c[q];
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (l < K) {
+    const uint64_t mine = l < base ? s_fin[l] : 0ull;
+    int rank = 0;
+    for (int j = 0; j < base; ++j) rank += s_fin[j] > mine ? 1 : 0;
+    if (l < base) {
+      ids[static_cast<long long>(row) * K + rank] = static_cast<int32_t>(0xffffffffu - comp_inv(mine));
+      vals[static_cast<long long>(row) * K + rank] = value_of_key16(comp_key(mine));
+    }
+  }
+}
+
 }  // namespace
+
+bool lm_head_topk_supported(int M, int V, int d, int K) {
+  return M >= 1 && V >= K && K >= 1 && K <= kLmMaxK && d >= 64 && d % 64 == 0;
+}
+
+int lm_head_groups(int M, int V, int K) {
+  const int tiles_m = (M + kLmBM - 1) / kLmBM;
+  const int tiles_n = (V + kLmBN - 1) / kLmBN;
+  int groups = std::max(1, 256 / tiles_m);
+  groups = std::min(groups, 1024 / K);         // the merge holds 1024 composites per row
+  groups = std::min(groups, tiles_n);
+  if (groups >= 8) groups -= groups % 8;
+  return groups;
+}
+
+size_t lm_head_workspace_bytes(int M, int V, int K) {
+  return sizeof(uint64_t) * static_cast<size_t>(lm_head_groups(M, V, K)) * M * K;
+}
+
+hipError_t launch_lm_head_topk(const void* hd, const void* W_lm, int M, int V, int d, int K, void* workspace,
+                               int32_t* ids, float* vals, hipStream_t st) {
+  if (!lm_head_topk_supported(M, V, d, K)) return hipErrorInvalidValue;
+  GemmDev p{};
+  p.M = M; p.N = V; p.Kd = d; p.ksplit = d;
+  p.A = static_cast<const char*>(hd); p.lda = d;
+  p.w0 = p.w1 = p.w2 = static_cast<const char*>(W_lm);
+  p.ldw0 = p.ldw1 = p.ldw2 = d;
+  p.end0 = p.end1 = V;
+  p.row_bias_div = 1;
+  const int tiles_m = (M + kLmBM - 1) / kLmBM;
+  const int tiles_n = (V + kLmBN - 1) / kLmBN;
+  const int groups = lm_head_groups(M, V, K);
+  const int xcd_map = groups % 8 == 0 ? 1 : 0;
+  uint64_t* part = static_cast<uint64_t*>(workspace);
+  hipLaunchKernelGGL(lm_head_topk_kernel, dim3(tiles_m * groups), dim3(512), 0, st, p, K, tiles_m, tiles_n, groups,
+                     xcd_map, part);
+  const int count = groups * K;
+#define DCOCO_LMM(QV) \
+  hipLaunchKernelGGL((lm_head_merge_kernel<QV>), dim3(M), dim3(64), 0, st, part, groups, M, K, ids, vals)
+  if (count <= 64) DCOCO_LMM(1);
+  else if (count <= 256) DCOCO_LMM(4);
+  else if (count <= 512) DCOCO_LMM(8);
+  else DCOCO_LMM(16);
+#undef DCOCO_LMM
+  return hipGetLastError();
+}
 
 int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype) {
   const int bk = (a_dtype == kDtypeBf16 && w_dtype == kDtypeBf16) ? 64 : 32;

@@ -102,6 +102,13 @@ bool path_supported(int B, int K);
 hipError_t launch_path(const float* S, const float* cand_logits, const int32_t* cand_ids, int N, int B, int K,
                        float lam, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
 
+// ----------------------------------------------- LM head fused with top-K
+// top-K of bf16(hd W_lm^T) per row without storing the logits (gemm.hip)
+bool lm_head_topk_supported(int M, int V, int d, int K);
+size_t lm_head_workspace_bytes(int M, int V, int K);
+hipError_t launch_lm_head_topk(const void* hd, const void* W_lm, int M, int V, int d, int K, void* workspace,
+                               int32_t* ids, float* vals, hipStream_t st);
+
 // ------------------------------------------------------------ training side
 // loss per pair, its sum into loss[0], and dL/dS (see train.hip)
 hipError_t launch_loss(const float* S, const int32_t* cand_ids, const int32_t* target_tok, int N, int B, int K,

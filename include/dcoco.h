@@ -169,6 +169,26 @@ int dcoco_select_path(const dcoco_dims* dims, const float* S, const float* cand_
                       const int32_t* cand_ids, int rule, float lambda, int32_t* sel_idx,
                       int32_t* sel_tok, void* stream);
 
+/* The drafter's LM head fused with top-K ([P1] "Keep the leading
+ * candidates": the candidates are the drafter's own top-K; [P1] "Score
+ * neighboring candidates in parallel": the corrector reuses what the drafter
+ * pass already computed).  For every row i (one slot of one block),
+ *   l_i(v) = bf16( sum_k hd[i,k] W_lm[v,k] )   (fp32 accumulation, rounded
+ *            to nearest-even bf16: the logit the drafter would store),
+ * and the K largest are selected exactly as dcoco_topk does (value
+ * descending, equal values to the lower id), without writing the
+ * [n_blocks*B, V] logits anywhere.
+ *   hd          [n_blocks*B, d_hidden] bf16   the drafter's final hidden states
+ *   W_lm        [V, d_hidden] bf16            LM head (rows = vocabulary)
+ *   cand_ids    [n_blocks*B, K] int32         out
+ *   cand_logits [n_blocks*B, K] fp32          out: the bf16 logits, widened
+ * bf16 storage only; K <= 16 and d_hidden a multiple of 64, else
+ * DCOCO_ERR_UNSUPPORTED.  Workspace: query with workspace == NULL (a few MB:
+ * per-workgroup candidate lists).  Deterministic. */
+int dcoco_lm_head_topk(const dcoco_dims* dims, const void* hd, const void* W_lm,
+                       int32_t* cand_ids, float* cand_logits, void* workspace,
+                       size_t* workspace_bytes, void* stream);
+
 /* Training loss of the corrector ([P1] "How we train the corrector"; [P2]
  * part 3, paper Sec. 3.2 and App. A).  The label of pair p is the pair of
  * target tokens of slots p and p+1 (the target model's choices under the
@@ -266,7 +286,7 @@ const char* dcoco_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor): 101 adds the table
  * entry points, 102 dcoco_select_path, 103 dcoco_loss and
- * dcoco_score_backward. */
+ * dcoco_score_backward, 104 dcoco_lm_head_topk. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

@@ -36,6 +36,8 @@ the design notes):
   * projections P_e, P_h, W_f and W_pair carry no bias; s_p is not normalised;
   * walk argmax: the lowest index among maxima, NaN never wins (index 0 if a
     whole row is NaN);
+  * LM head: logits rounded to bf16 (the stored drafter logit) before the
+    top-K, which follows the top-K order above;
   * training loss: joint softmax over the K^2 scores of a pair, pair p
     weighted by exp(-(p-1)/rho), masked unless both target tokens are among
     the candidates, summed over pairs and averaged over blocks;
@@ -59,7 +61,8 @@ import numpy as np
 __all__ = [
     "to_f64", "round_bf16", "top_k", "layer_norm", "slot_context",
     "candidate_embedding", "fuse", "pair_state", "silu", "transition_scores",
-    "greedy_walk", "best_path", "corrector_loss", "score_backward", "correct_block",
+    "greedy_walk", "best_path", "corrector_loss", "score_backward", "lm_head_logits", "lm_head_topk",
+    "correct_block",
 ]
 
 
@@ -265,6 +268,33 @@ def greedy_walk(S: np.ndarray, cand_vals: np.ndarray, cand_ids: np.ndarray):
             sel_idx[n, p + 1] = k
         sel_tok[n] = cand_ids[n, np.arange(B), sel_idx[n]]
     return sel_idx, sel_tok, reads
+
+
+# ---------------------------------------------------- drafter LM head ---
+
+def lm_head_logits(hd: np.ndarray, W_lm: np.ndarray, dtype: str, rows=None, v_chunk: int = 16384) -> np.ndarray:
+    """The drafter's logits from its LM head: l_i(v) = W_lm[v] . hd_i, stored
+    as the drafter stores logits (rounded to bf16 in the bf16 contract).
+
+    hd [R, d], W_lm [V, d] (stored values) -> [R or len(rows), V] float64.
+    The vocabulary is processed in chunks only to bound memory; each logit is
+    one plain dot product.
+    """
+    h = to_f64(hd if rows is None else hd[np.asarray(rows)], dtype)
+    V = W_lm.shape[0]
+    logits = np.empty((h.shape[0], V), np.float64)
+    for v0 in range(0, V, v_chunk):
+        v1 = min(V, v0 + v_chunk)
+        logits[:, v0:v1] = h @ to_f64(W_lm[v0:v1], dtype).T
+    if dtype == "bf16":
+        logits = round_bf16(logits)
+    return logits
+
+
+def lm_head_topk(hd: np.ndarray, W_lm: np.ndarray, K: int, dtype: str, rows=None, v_chunk: int = 16384):
+    """The drafter's candidates straight from its LM head ([P1] "Keep the
+    leading candidates"): top_k of lm_head_logits.  -> ids, vals."""
+    return top_k(lm_head_logits(hd, W_lm, dtype, rows, v_chunk), K)
 
 
 # ------------------------------------------------------------ training ---

@@ -38,7 +38,7 @@ from __future__ import annotations
 import dataclasses
 import numpy as np
 
-__all__ = ["Dims", "CONFIGS", "get_config", "make_inputs", "f32_to_bf16_bits",
+__all__ = ["Dims", "CONFIGS", "get_config", "make_inputs", "make_lm_head_inputs", "f32_to_bf16_bits",
            "bf16_bits_to_f32", "ROLE"]
 
 
@@ -146,6 +146,16 @@ CONFIGS = {
     "tall_bf16": Config("tall_bf16", _d(3, 15, 50, 6007, 256, 512, 256, 256, 64, 256, "bf16"),
                         30.0, "peaks", 50, 2008, "random",
                         "2250 candidate rows (ragged over 128-row tiles) with 256-wide projections"),
+    # LM-head shapes (head tied to E, so d == e): ragged vocabulary tiles,
+    # ragged row tiles, rows without planted peaks (bf16 ties at the K-th)
+    "lmh_small": Config("lmh_small", _d(2, 8, 16, 5003, 256, 256, 64, 64, 64, 64, "bf16"),
+                        30.0, "peaks", 16, 2101, "random", "LM head: 16 rows, V = 5003, d = 256"),
+    "lmh_rows": Config("lmh_rows", _d(25, 8, 16, 9001, 320, 320, 64, 64, 64, 64, "bf16"),
+                       30.0, "peaks", 16, 2102, "random", "LM head: 200 rows (two row tiles), d = 320"),
+    "lmh_flat": Config("lmh_flat", _d(3, 16, 12, 20011, 512, 512, 64, 64, 64, 64, "bf16"),
+                       30.0, "peaks", 0, 2103, "random", "LM head: background only, K = 12, V = 20011"),
+    "lmh_k1": Config("lmh_k1", _d(2, 4, 1, 3001, 128, 128, 64, 64, 64, 64, "bf16"),
+                     30.0, "peaks", 1, 2104, "random", "LM head: K = 1"),
 }
 
 # tensor roles, in the fixed order their seeds are spawned
@@ -317,6 +327,50 @@ def make_stream_inputs(cfg: Config | str, seed: int, n_blocks: int | None = None
         h[n] = _store(gh.standard_normal((D.B, D.d), dtype=np.float32) * np.float32(cfg.h_scale), dt)
         logits[n] = _store(_logit_row_block(cfg, n, seed), dt)
     return {"h": h, "logits": logits, "dims": D, "seed": seed}
+
+
+def make_lm_head_inputs(cfg: Config | str, E: np.ndarray, seed: int | None = None,
+                        n_blocks: int | None = None) -> dict:
+    """Inputs of the drafter's LM head for one call, with the head tied to the
+    token-embedding table (W_lm = E, rows = vocabulary; needs d == e).
+
+    hd [N*B, d]: the final hidden state of each slot, N(0, s^2) with
+    s = 100 / sqrt(d) (so the background logits hd . E[v] have a standard
+    deviation near 2, as the logit rows above), plus, per row, P planted
+    directions that lift P distinct random ids to 20 + 0.5 j: the row gains
+    the combination of those P rows of E that brings their dot products to
+    the targets (a P x P solve), so after rounding to bf16 the planted logits
+    land close to their targets.  At d = 4096 they stand clear of the
+    background; at small widths the added direction also lifts other ids,
+    which is just another logit row to select from.
+    Returns {"hd": bits or float32, "W_lm": E, "planted": [N*B, P] ids,
+    "dims": Dims}.
+    """
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    seed = cfg.seed if seed is None else seed
+    D = cfg.dims if n_blocks is None else dataclasses.replace(cfg.dims, n_blocks=n_blocks)
+    assert D.d == D.e, "a tied head needs d == e"
+    dt = D.dtype
+    P = cfg.n_peaks
+    R = D.n_blocks * D.B
+    hd = np.empty((R, D.d), np.uint16 if dt == "bf16" else np.float32)
+    planted = np.empty((R, P), np.int64)
+    s = np.float32(100.0 / np.sqrt(D.d))
+    targets = (20.0 + 0.5 * np.arange(P)).astype(np.float64)
+    for n in range(D.n_blocks):
+        g = _rng(seed, ROLE["stream"], n, STREAM_ROLE["h"] + 16)
+        gp = _rng(seed, ROLE["stream"], n, STREAM_ROLE["peak_pos"] + 16)
+        for i in range(D.B):
+            x = g.standard_normal(D.d, dtype=np.float32).astype(np.float64) * s
+            ids = gp.choice(D.V, size=P, replace=False)
+            if P:
+                t = targets[gp.permutation(P)]
+                rows = to_float(E[ids], dt).astype(np.float64)
+                x = x + np.linalg.solve(rows @ rows.T, t - rows @ x) @ rows
+            hd[n * D.B + i] = _store(x.astype(np.float32)[None, :], dt)[0]
+            planted[n * D.B + i] = ids
+    return {"hd": hd, "W_lm": E, "planted": planted, "dims": D}
 
 
 def to_float(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -721,3 +721,83 @@ def test_score_backward_full_q8b_32_sampled():
     for key in ("dW1", "db1", "dw2"):
         _grad_check(_np(out[key]), R[key], f"full:{key}")
     _grad_check(_np(out["d_cand_logits"])[blocks], R["d_cand_vals"], "full:dcl")
+
+
+# ---------------------------------------------------------- drafter LM head
+
+def _lm_check(ids, vals, logits, K):
+    """GPU (ids, vals) per row against the oracle's bf16 logits of that row.
+    The GPU rounds an fp32 sum and the oracle an fp64 one, so a logit may sit
+    one bf16 step away; within that, the selection must be a valid top-K in
+    the pages' order, and it must equal the oracle's exactly in most rows."""
+    R, V = logits.shape
+    ref_ids, ref_vals = O.top_k(logits, K)
+    exact = 0
+    for i in range(R):
+        g, gv, lg = ids[i].astype(np.int64), vals[i].astype(np.float64), logits[i]
+        assert len(set(g.tolist())) == K and g.min() >= 0 and g.max() < V, i
+        ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(lg[g]), 2.0 ** -126))).astype(int) - 7)
+        assert np.all(np.abs(gv - lg[g]) <= ulp), (i, gv, lg[g])
+        # sorted by value, equal values by id
+        assert np.all((gv[:-1] > gv[1:]) | ((gv[:-1] == gv[1:]) & (g[:-1] < g[1:]))), i
+        # nothing left out beats anything taken by more than one step
+        rest = np.delete(lg, g)
+        kth = lg[g].min()
+        assert rest.max() <= kth + 2 * ulp.max(), (i, rest.max(), kth)
+        if np.array_equal(g, ref_ids[i]) and np.array_equal(gv, ref_vals[i]):
+            exact += 1
+    return exact / R
+
+
+@pytest.mark.parametrize("name", ["lmh_small", "lmh_rows", "lmh_flat", "lmh_k1"])
+def test_lm_head_topk_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case lm_head_topk {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    L = synth.make_lm_head_inputs(name, inp["E"])
+    dims = dc.Dims.from_synth(D)
+    ids, vals = dc.lm_head_topk(dims, to_dev(L["hd"], "bf16"), to_dev(L["W_lm"], "bf16"))
+    torch.cuda.synchronize()
+    logits = O.lm_head_logits(L["hd"], L["W_lm"], "bf16")
+    frac = _lm_check(_np(ids), _np(vals), logits, D.K)
+    assert frac >= 0.95, frac
+
+
+def test_lm_head_topk_matches_dcoco_topk_on_stored_logits():
+    # the fused path selects what the two-step path selects from the same
+    # logits once they are stored (rows where no rounding straddles)
+    import draft_block_contextual_amd as dc
+    import torch
+    name = "lmh_rows"
+    inp = _inputs(name)
+    D = inp["dims"]
+    L = synth.make_lm_head_inputs(name, inp["E"])
+    dims = dc.Dims.from_synth(D)
+    ids, vals = dc.lm_head_topk(dims, to_dev(L["hd"], "bf16"), to_dev(L["W_lm"], "bf16"))
+    stored = synth.f32_to_bf16_bits(O.lm_head_logits(L["hd"], L["W_lm"], "bf16").astype(np.float32))
+    ids2, vals2 = dc.topk(dims, to_dev(stored, "bf16"))
+    torch.cuda.synchronize()
+    same = np.mean([np.array_equal(a, b) for a, b in zip(_np(ids), _np(ids2))])
+    assert same >= 0.95, same
+
+
+def test_full_q8b_32_lm_head_sampled():
+    # the full 512 x 151936 x 4096 launch; the oracle computes sampled rows
+    import draft_block_contextual_amd as dc
+    import torch
+    name = "q8b_32"
+    print("case lm_head_topk q8b_32", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    L = synth.make_lm_head_inputs(name, inp["E"])
+    dims = dc.Dims.from_synth(D)
+    ids, vals = dc.lm_head_topk(dims, to_dev(L["hd"], "bf16"), to_dev(L["W_lm"], "bf16"))
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 255, 300, 384, 511]
+    logits = O.lm_head_logits(L["hd"], L["W_lm"], "bf16", rows=rows)
+    frac = _lm_check(_np(ids)[rows], _np(vals)[rows], logits, D.K)
+    assert frac >= 0.75, frac
+    # every row: the planted peaks are the top 16 (they stand 12+ above the background)
+    np.testing.assert_array_equal(np.sort(_np(ids), axis=1), np.sort(L["planted"], axis=1))

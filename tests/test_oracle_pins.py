@@ -669,3 +669,42 @@ def test_score_backward_against_torch_autograd():
         np.testing.assert_allclose(out[name], t[key].grad.numpy(), rtol=1e-12, atol=1e-12, err_msg=name)
     assert out["db2"] == pytest.approx(b2.grad.item(), rel=1e-12)
     np.testing.assert_allclose(out["d_cand_vals"], vals.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------- drafter LM head
+
+def test_lm_head_one_hot_rows_closed_form():
+    # a head whose row v is c_v times a unit vector e_{j(v)}: the logit is
+    # bf16(c_v * hd_i[j(v)]) element by element, so the head's orientation
+    # (rows = vocabulary) and the bf16 rounding of the logits are both pinned
+    g = _rng(71)
+    R, d, V, K = 5, 24, 300, 9
+    hd = synth.f32_to_bf16_bits(g.standard_normal((R, d)).astype(np.float32) * 3)
+    j = g.integers(0, d, V)
+    c = synth.f32_to_bf16_bits(g.standard_normal(V).astype(np.float32))
+    W = np.zeros((V, d), np.uint16)
+    W[np.arange(V), j] = c
+    h = synth.bf16_bits_to_f32(hd).astype(np.float64)
+    want = O.round_bf16(h[:, j] * synth.bf16_bits_to_f32(c).astype(np.float64)[None, :])
+    np.testing.assert_array_equal(O.lm_head_logits(hd, W, "bf16"), want)
+    ids, vals = O.lm_head_topk(hd, W, K, "bf16")
+    rids, rvals = O.top_k(want, K)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_array_equal(vals, rvals)
+    # a head stored transposed would not even have the right shape here: V != d
+    assert O.lm_head_logits(hd, W, "bf16").shape == (R, V)
+
+
+def test_lm_head_chunking_and_row_subsets():
+    g = _rng(72)
+    R, d, V = 6, 32, 1001
+    hd = synth.f32_to_bf16_bits(g.standard_normal((R, d)).astype(np.float32))
+    W = synth.f32_to_bf16_bits(g.standard_normal((V, d)).astype(np.float32) * 0.3)
+    full = O.lm_head_logits(hd, W, "bf16")
+    np.testing.assert_array_equal(O.lm_head_logits(hd, W, "bf16", v_chunk=7), full)
+    np.testing.assert_array_equal(O.lm_head_logits(hd, W, "bf16", rows=[4, 1]), full[[4, 1]])
+    # rounding only in the bf16 contract: fp32 storage keeps the exact sums
+    hf = synth.bf16_bits_to_f32(hd)
+    Wf = synth.bf16_bits_to_f32(W)
+    np.testing.assert_allclose(O.lm_head_logits(hf, Wf, "f32"), hf.astype(np.float64) @ Wf.T.astype(np.float64),
+                               rtol=1e-15, atol=0)
