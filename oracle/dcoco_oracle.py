@@ -61,7 +61,7 @@ import numpy as np
 __all__ = [
     "to_f64", "round_bf16", "top_k", "layer_norm", "slot_context",
     "candidate_embedding", "fuse", "pair_state", "silu", "transition_scores",
-    "greedy_walk", "best_path", "corrector_loss", "score_backward", "lm_head_logits", "lm_head_topk",
+    "greedy_walk", "best_path", "corrector_loss", "score_backward", "represent_backward", "lm_head_logits", "lm_head_topk",
     "correct_block",
 ]
 
@@ -399,6 +399,72 @@ def score_backward(z: np.ndarray, s: np.ndarray, W1: np.ndarray, b1: np.ndarray,
             out["ds"][n, p] += dx[:, :, 2 * rz:].sum(axis=(0, 1))
             out["d_cand_vals"][n, p + 1] += G[n, p].sum(axis=0)
     return out
+
+
+def represent_backward(h: np.ndarray, E_rows: np.ndarray, P_e: np.ndarray, P_h: np.ndarray, W_f: np.ndarray,
+                       W_pair: np.ndarray, dz: np.ndarray, ds: np.ndarray, eps: float, bf16: bool) -> dict:
+    """Gradients of a loss through the representations, given dL/dz and
+    dL/ds (the backward of slot_context, candidate_embedding, fuse and
+    pair_state; [P2] part 1, paper Sec. 3.2).  Step by step, in the forward's
+    notation:
+
+        z = W_f [b; g]        dW_f = sum dz [b; g]^T,  db = W_fb^T dz,
+                              dg_i = W_fg^T sum_k dz_{i,k}
+        b = LN(x_e), g = LN(x_h), y = LN(x) with sigma = sqrt(var + eps):
+                              dx = (dy - mean(dy) - y mean(dy y)) / sigma
+        x_e = P_e E[c]        dP_e = sum dx_e E[c]^T
+        x_h = P_h h           dP_h = sum dx_h h^T,  dh += P_h^T dx_h
+        s_p = W_pair [h_p; h_{p+1}]
+                              dW_pair = sum ds_p [h_p; h_{p+1}]^T,
+                              dh_p += W_L^T ds_p,  dh_{p+1} += W_R^T ds_p
+
+    The bf16 roundings of b and g count as the identity; dW_f takes the
+    rounded b and g the forward multiplied by.  E is frozen (no gradient).
+    h [N, B, d], E_rows [N, B, K, e] (the gathered rows), dz [N, B, K, r_z],
+    ds [N, B-1, r_s] -> dict of float64 dP_e, dP_h, dW_f, dW_pair, dh.
+    """
+    h = np.asarray(h, np.float64)
+    Er = np.asarray(E_rows, np.float64)
+    P_e = np.asarray(P_e, np.float64)
+    P_h = np.asarray(P_h, np.float64)
+    W_f = np.asarray(W_f, np.float64)
+    W_pair = np.asarray(W_pair, np.float64)
+    dz = np.asarray(dz, np.float64)
+    ds = np.asarray(ds, np.float64)
+    N, B, K, e = Er.shape
+    d = h.shape[-1]
+    r = P_e.shape[0]
+
+    def ln_fwd(x):
+        mu = x.mean(axis=-1, keepdims=True)
+        sig = np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+        return (x - mu) / sig, sig
+
+    def ln_bwd(dy, y, sig):
+        return (dy - dy.mean(axis=-1, keepdims=True) - y * (dy * y).mean(axis=-1, keepdims=True)) / sig
+
+    x_e = Er @ P_e.T                              # [N, B, K, r]
+    y_e, sig_e = ln_fwd(x_e)
+    x_h = h @ P_h.T                               # [N, B, r]
+    y_h, sig_h = ln_fwd(x_h)
+    b = round_bf16(y_e) if bf16 else y_e
+    g = round_bf16(y_h) if bf16 else y_h
+    W_fb, W_fg = W_f[:, :r], W_f[:, r:]
+    dzs = dz.sum(axis=2)                          # [N, B, r_z]
+    dW_f = np.concatenate([np.einsum("nbkz,nbkr->zr", dz, b), np.einsum("nbz,nbr->zr", dzs, g)], axis=1)
+    db = dz @ W_fb                                # [N, B, K, r]
+    dg = dzs @ W_fg                               # [N, B, r]
+    dx_e = ln_bwd(db, y_e, sig_e)
+    dx_h = ln_bwd(dg, y_h, sig_h)
+    dP_e = np.einsum("nbkr,nbke->re", dx_e, Er)
+    dP_h = np.einsum("nbr,nbd->rd", dx_h, h)
+    dh = dx_h @ P_h
+    W_L, W_R = W_pair[:, :d], W_pair[:, d:]
+    dW_pair = np.concatenate([np.einsum("nps,npd->sd", ds, h[:, :-1]), np.einsum("nps,npd->sd", ds, h[:, 1:])],
+                             axis=1)
+    dh[:, :-1] += ds @ W_L
+    dh[:, 1:] += ds @ W_R
+    return {"dP_e": dP_e, "dP_h": dP_h, "dW_f": dW_f, "dW_pair": dW_pair, "dh": dh}
 
 
 # ---------------------------------------------------- whole-path rules ---

@@ -708,3 +708,72 @@ def test_lm_head_chunking_and_row_subsets():
     Wf = synth.bf16_bits_to_f32(W)
     np.testing.assert_allclose(O.lm_head_logits(hf, Wf, "f32"), hf.astype(np.float64) @ Wf.T.astype(np.float64),
                                rtol=1e-15, atol=0)
+
+
+def _rep_case(seed, N=2, B=3, K=2, d=6, e=5, r=4, rz=3, rs=3):
+    g = _rng(seed)
+    h = g.standard_normal((N, B, d)) * 2
+    Er = g.standard_normal((N, B, K, e)) * 0.5
+    P_e = g.standard_normal((r, e))
+    P_h = g.standard_normal((r, d)) * 0.5
+    W_f = g.standard_normal((rz, 2 * r))
+    W_pair = g.standard_normal((rs, 2 * d))
+    dz = g.standard_normal((N, B, K, rz))
+    ds = g.standard_normal((N, B - 1, rs))
+    return h, Er, P_e, P_h, W_f, W_pair, dz, ds
+
+
+def test_represent_backward_finite_differences():
+    # f = sum dz * z + sum ds * s through the (separately pinned) forward
+    # functions in fp32 storage mode; every gradient entry against a central
+    # difference
+    h, Er, P_e, P_h, W_f, W_pair, dz, ds = _rep_case(81)
+    eps = 1e-5
+    out = O.represent_backward(h, Er, P_e, P_h, W_f, W_pair, dz, ds, eps, bf16=False)
+    N, B, K, e = Er.shape
+    ids = np.arange(N * B * K).reshape(N, B, K)
+    Etab = Er.reshape(N * B * K, e)
+
+    def f(h=h, P_e=P_e, P_h=P_h, W_f=W_f, W_pair=W_pair):
+        b = O.candidate_embedding(Etab, ids, P_e, eps, bf16=False)
+        g = O.slot_context(h, P_h, eps, bf16=False)
+        z = O.fuse(b, g, W_f, bf16=False)
+        s = O.pair_state(h, W_pair)
+        return float((dz * z).sum() + (ds * s).sum())
+
+    step = 1e-6
+    for name, key, arr in (("dP_e", "P_e", P_e), ("dP_h", "P_h", P_h), ("dW_f", "W_f", W_f),
+                           ("dW_pair", "W_pair", W_pair), ("dh", "h", h)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            hi, lo = arr.copy(), arr.copy()
+            hi[idx] += step
+            lo[idx] -= step
+            num[idx] = (f(**{key: hi}) - f(**{key: lo})) / (2 * step)
+        np.testing.assert_allclose(out[name], num, rtol=1e-5, atol=1e-7, err_msg=name)
+
+
+def test_represent_backward_torch_autograd_straight_through():
+    # bf16 mode: torch's own layer_norm and autograd, with each bf16 rounding
+    # written as x + (round(x) - x).detach() (identity in the backward)
+    h, Er, P_e, P_h, W_f, W_pair, dz, ds = _rep_case(82, N=2, B=4, K=3, d=16, e=12, r=8, rz=6, rs=5)
+    eps = 1e-5
+    out = O.represent_backward(h, Er, P_e, P_h, W_f, W_pair, dz, ds, eps, bf16=True)
+    T = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in dict(h=h, P_e=P_e, P_h=P_h, W_f=W_f, W_pair=W_pair).items()}
+
+    def rnd(x):
+        q = x.detach().to(torch.float32).to(torch.bfloat16).to(torch.float64)
+        return x + (q - x).detach()
+
+    r = P_e.shape[0]
+    d = h.shape[-1]
+    Ert = torch.tensor(Er, dtype=torch.float64)
+    b = rnd(torch.nn.functional.layer_norm(Ert @ T["P_e"].T, (r,), eps=eps))
+    g = rnd(torch.nn.functional.layer_norm(T["h"] @ T["P_h"].T, (r,), eps=eps))
+    z = torch.cat([b, g[:, :, None, :].expand_as(b)], dim=-1) @ T["W_f"].T
+    s = torch.cat([T["h"][:, :-1], T["h"][:, 1:]], dim=-1) @ T["W_pair"].T
+    ((torch.tensor(dz) * z).sum() + (torch.tensor(ds) * s).sum()).backward()
+    for name, key in (("dP_e", "P_e"), ("dP_h", "P_h"), ("dW_f", "W_f"), ("dW_pair", "W_pair"), ("dh", "h")):
+        np.testing.assert_allclose(out[name], T[key].grad.numpy(), rtol=1e-9, atol=1e-10, err_msg=name)
+    assert d > 0
