@@ -23,7 +23,8 @@ DTYPE_CODE = {"f32": 0, "bf16": 1}
 
 # every entry point include/dcoco.h declares
 EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
-           "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
+           "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_represent_backward",
+           "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
            "dcoco_status_string", "dcoco_abi_version"]
 
 
@@ -43,6 +44,11 @@ class CDims(ctypes.Structure):
 class CMlpGrads(ctypes.Structure):
     _fields_ = [("dW1", ctypes.c_void_p), ("db1", ctypes.c_void_p), ("dw2", ctypes.c_void_p),
                 ("db2", ctypes.c_void_p)]
+
+
+class CRepGrads(ctypes.Structure):
+    _fields_ = [("dP_e", ctypes.c_void_p), ("dP_h", ctypes.c_void_p), ("dW_f", ctypes.c_void_p),
+                ("dW_pair", ctypes.c_void_p)]
 
 
 class CWeights(ctypes.Structure):
@@ -73,12 +79,13 @@ def load() -> ctypes.CDLL:
     lib.dcoco_loss.argtypes = [pd, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
     lib.dcoco_lm_head_topk.argtypes = [pd, vp, vp, vp, vp, vp, sz, vp]
     lib.dcoco_score_backward.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, ctypes.POINTER(CMlpGrads), vp, sz, vp]
+    lib.dcoco_represent_backward.argtypes = [pd, pw, vp, vp, vp, vp, vp, ctypes.POINTER(CRepGrads), vp, vp, sz, vp]
     lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     lib.dcoco_build_btable.argtypes = [pd, pw, vp, vp, vp, sz, vp]
     lib.dcoco_correct_block_btable.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
-              "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_correct_block",
-              "dcoco_build_btable", "dcoco_correct_block_btable"]:
+              "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_represent_backward",
+              "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.dcoco_status_string.argtypes = [ctypes.c_int]
     lib.dcoco_status_string.restype = ctypes.c_char_p
@@ -328,6 +335,36 @@ def score_backward(dims: Dims, w: Weights, z, s, dS, workspace=None, stream=None
                                     _stream(stream)))
     out["ds"] = out["ds"][:, :B - 1]
     out["db2"] = out["db2"][:1]
+    return out
+
+
+def represent_backward(dims: Dims, w: Weights, h, E, cand_ids, dz, ds, want_dh: bool = True, workspace=None,
+                       stream=None) -> dict:
+    """dcoco_represent_backward -> dict of fp32 gradients: dP_e, dP_h, dW_f,
+    dW_pair and (want_dh) dh."""
+    import torch
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    dev = h.device
+    N, B = dims.n_blocks, dims.B
+    r, rs = dims.d_proj, dims.d_pair
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dP_e": torch.empty((r, dims.d_embed), **f32), "dP_h": torch.empty((r, dims.d_hidden), **f32),
+           "dW_f": torch.empty((dims.d_z, 2 * r), **f32), "dW_pair": torch.empty((rs, 2 * dims.d_hidden), **f32)}
+    if want_dh:
+        out["dh"] = torch.empty((N, B, dims.d_hidden), **f32)
+    g = CRepGrads(out["dP_e"].data_ptr(), out["dP_h"].data_ptr(), out["dW_f"].data_ptr(), out["dW_pair"].data_ptr())
+    n = ctypes.c_size_t(0)
+    _check("dcoco_represent_backward",
+           lib.dcoco_represent_backward(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, None,
+                                        ctypes.byref(g), None, None, ctypes.byref(n), None))
+    ws = _workspace(n.value, dev, workspace)
+    n = ctypes.c_size_t(ws.numel())
+    _check("dcoco_represent_backward",
+           lib.dcoco_represent_backward(ctypes.byref(cd), ctypes.byref(cw), _ptr(h), _ptr(E), _ptr(cand_ids),
+                                        _ptr(dz), _ptr(ds) if B > 1 else None, ctypes.byref(g),
+                                        _ptr(out["dh"]) if want_dh else None, _ptr(ws), ctypes.byref(n),
+                                        _stream(stream)))
     return out
 
 

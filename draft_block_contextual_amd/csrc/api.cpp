@@ -349,11 +349,194 @@ hipError_t grad_product(GemmF32Args q, int a_dt, int b_dt, float* part, float* o
   return launch_sum_splits(part, splits, q.M, q.N, out, ldo, st);
 }
 
+// ---- representation backward (bf16 storage)
+
+int pad64(int x) { return (x + 63) / 64 * 64; }
+
+struct RepBwdLayout {
+  int split_h, split_e;    // forward recompute: split-K of P_h h and P_e E[c]
+  int s_f, s_e, s_h, s_dh; // splits of the gradient products
+  int Rp, RKp;             // row counts padded to 64 (reduction length)
+  float* Y;                // [split_h][R][r]: P_h h partials
+  float* U;                // [split_e][RK][r]: P_e E[c] partials
+  void* A1z;               // bf16 [RK, 2 d_z]: dz hi | lo
+  void* dzT;               // bf16 [2 d_z, RKp]: dz^T, hi rows then lo rows
+  void* WfT2;              // bf16 [2 r, 2 d_z]: W_f^T, twice along k
+  float* dBG;              // [RK, 2 r]: dz W_f (db | per-candidate part of dg)
+  void* bq;                // bf16 [RK, r]: b
+  void* gq;                // bf16 [R, r]: g
+  float* dxe;              // [RK, r]
+  void* BGT;               // bf16 [2 r, RKp]: b^T, then g^T repeated over k
+  void* dxeT;              // bf16 [2 r, RKp]: dx_e^T hi rows then lo rows
+  void* EcT;               // bf16 [d_embed, RKp]: the gathered E rows, transposed
+  float* Acat;             // [R, C]: dx_h | ds at the left slot | ds at the right slot
+  void* A1cat;             // bf16 [R, 2C]
+  void* AcatT;             // bf16 [2C, Rp]
+  void* hT;                // bf16 [d_hidden, Rp]
+  void* WcatT2;            // bf16 [d_hidden, 2C]: [P_h; W_L; W_R]^T, twice along k
+  float* part;             // split partial products
+};
+
+RepBwdLayout carve_rep_bwd(Carve& c, const dcoco_dims* d) {
+  RepBwdLayout L;
+  const int R = d->n_blocks * d->B;
+  const int RK = R * d->K;
+  const int r = d->d_proj, rz = d->d_z, rs = d->d_pair, dh = d->d_hidden, de = d->d_embed;
+  const int C = r + 2 * rs;
+  L.Rp = pad64(R);
+  L.RKp = pad64(RK);
+  L.split_h = gemm_pick_split(R, r, dh, kDtypeBf16, kDtypeBf16);
+  L.split_e = gemm_pick_split(RK, r, de, kDtypeBf16, kDtypeBf16);
+  L.s_f = gemm_pick_split_max(2 * rz, 2 * r, L.RKp, kMaxGradSplit);
+  L.s_e = gemm_pick_split_max(2 * r, de, L.RKp, kMaxGradSplit);
+  L.s_h = gemm_pick_split_max(2 * C, dh, L.Rp, kMaxGradSplit);
+  L.s_dh = gemm_pick_split_max(R, dh, 2 * C, 4);
+  const size_t bf = 2, f4 = 4;
+  const size_t RKs = RK, Rs = R, RKps = L.RKp, Rps = L.Rp;
+  L.Y = static_cast<float*>(c.take(f4 * L.split_h * Rs * r));
+  L.U = static_cast<float*>(c.take(f4 * L.split_e * RKs * r));
+  L.A1z = c.take(bf * RKs * 2 * rz);
+  L.dzT = c.take(bf * 2 * rz * RKps);
+  L.WfT2 = c.take(bf * 2 * r * 2 * rz);
+  L.dBG = static_cast<float*>(c.take(f4 * RKs * 2 * r));
+  L.bq = c.take(bf * RKs * r);
+  L.gq = c.take(bf * Rs * r);
+  L.dxe = static_cast<float*>(c.take(f4 * RKs * r));
+  L.BGT = c.take(bf * 2 * r * RKps);
+  L.dxeT = c.take(bf * 2 * r * RKps);
+  L.EcT = c.take(bf * de * RKps);
+  L.Acat = static_cast<float*>(c.take(f4 * Rs * C));
+  L.A1cat = c.take(bf * Rs * 2 * C);
+  L.AcatT = c.take(bf * 2 * C * Rps);
+  L.hT = c.take(bf * dh * Rps);
+  L.WcatT2 = c.take(bf * dh * 2 * C);
+  const size_t part = std::max({static_cast<size_t>(L.s_f) * 2 * rz * 2 * r, static_cast<size_t>(L.s_e) * 2 * r * de,
+                                static_cast<size_t>(L.s_h) * 2 * C * dh, static_cast<size_t>(L.s_dh) * Rs * dh});
+  L.part = static_cast<float*>(c.take(f4 * part));
+  return L;
+}
+
+// C [M, N] = A [M, Kd] W^T (W rows [N][Kd], both bf16, Kd % 64 == 0) into
+// fp32 split partials part [split][M][N]
+hipError_t bf16_product(int M, int N, int Kd, const void* A, long long lda, const void* W, long long ldw, int split,
+                        float* part, hipStream_t st) {
+  GemmProblem q{};
+  q.M = M; q.N = N; q.Kd = Kd;
+  q.A = A; q.lda = lda; q.a_dtype = kDtypeBf16;
+  q.w[0] = W; q.ldw[0] = ldw; q.col0[0] = 0;
+  q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = N;
+  q.w_dtype = kDtypeBf16;
+  q.split = split; q.out_f32 = part; q.ldo = N; q.out = nullptr;
+  return launch_gemm(q, st);
+}
+
+hipError_t run_rep_backward(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
+                            const int32_t* ids, const float* dz, const float* ds, const dcoco_rep_grads* g,
+                            float* dh_out, const RepBwdLayout& L, hipStream_t st) {
+  const int N = d->n_blocks, B = d->B, K = d->K;
+  const int R = N * B, RK = R * K;
+  const int r = d->d_proj, rz = d->d_z, rs = d->d_pair, dh = d->d_hidden, de = d->d_embed;
+  const int C = r + 2 * rs;
+  const int Rp = L.Rp, RKp = L.RKp;
+  const long long RKpl = RKp, Rpl = Rp;
+  hipError_t e = hipSuccess;
+  // forward recompute: x_h = P_h h, x_e = P_e E[c] (split-K partials)
+  {
+    GemmProblem q{};
+    q.M = R; q.N = r; q.Kd = dh;
+    q.A = h; q.lda = dh; q.a_dtype = kDtypeBf16;
+    q.w[0] = w->P_h; q.ldw[0] = dh; q.col0[0] = 0;
+    q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = r;
+    q.w_dtype = kDtypeBf16;
+    q.split = L.split_h; q.out_f32 = L.Y; q.ldo = r; q.out = nullptr;
+    e = launch_gemm(q, st);
+  }
+  if (e == hipSuccess) {
+    GemmProblem q{};
+    q.M = RK; q.N = r; q.Kd = de;
+    q.A = E; q.lda = de; q.a_rows = ids; q.a_rows_max = d->V - 1; q.a_dtype = kDtypeBf16;
+    q.w[0] = w->P_e; q.ldw[0] = de; q.col0[0] = 0;
+    q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = r;
+    q.w_dtype = kDtypeBf16;
+    q.split = L.split_e; q.out_f32 = L.U; q.ldo = r; q.out = nullptr;
+    e = launch_gemm(q, st);
+  }
+  // dBG = dz [W_fb | W_fg]: dz as two bf16 parts against W_f^T twice
+  if (e == hipSuccess)
+    e = launch_split_t_ex(dz, true, rz, RK, RKp, rz, RowMap{}, L.A1z, L.dzT, RKpl, 0, static_cast<long long>(rz) * RKpl,
+                          st);
+  if (e == hipSuccess)
+    e = launch_split_t_ex(w->W_f, false, 2ll * r, rz, rz, 2 * r, RowMap{}, nullptr, L.WfT2, 2ll * rz, 0, rz, st);
+  if (e == hipSuccess) e = bf16_product(RK, 2 * r, 2 * rz, L.A1z, 2ll * rz, L.WfT2, 2ll * rz, 1, L.dBG, st);
+  // LayerNorm forward (b, g) and backward (dx_e; dx_h into Acat), ds placed by slot
+  if (e == hipSuccess)
+    e = launch_ln_fwd_bwd(L.U, L.split_e, RK, r, 0, r, d->ln_eps, L.dBG, 2ll * r, 0, 1, L.bq, L.dxe, r, st);
+  if (e == hipSuccess)
+    e = launch_ln_fwd_bwd(L.Y, L.split_h, R, r, 0, r, d->ln_eps, L.dBG, 2ll * r, r, K, L.gq, L.Acat, C, st);
+  if (e == hipSuccess) e = launch_pack_ds(ds, N, B, rs, r, C, L.Acat, st);
+  // transposed operands of the weight-gradient products (reduction over rows)
+  if (e == hipSuccess) e = launch_split_t_ex(L.bq, false, r, RK, RKp, r, RowMap{}, nullptr, L.BGT, RKpl, 0, 0, st);
+  if (e == hipSuccess) {
+    RowMap rep;
+    rep.mode = 2;
+    rep.rep = K;
+    e = launch_split_t_ex(L.gq, false, r, RK, RKp, r, rep, nullptr, static_cast<char*>(L.BGT) + 2ll * r * RKpl,
+                          RKpl, 0, 0, st);
+  }
+  if (e == hipSuccess)
+    e = launch_split_t_ex(L.dxe, true, r, RK, RKp, r, RowMap{}, nullptr, L.dxeT, RKpl, 0, static_cast<long long>(r) * RKpl,
+                          st);
+  if (e == hipSuccess) {
+    RowMap gat;
+    gat.mode = 1;
+    gat.ids = ids;
+    gat.idmax = d->V - 1;
+    e = launch_split_t_ex(E, false, de, RK, RKp, de, gat, nullptr, L.EcT, RKpl, 0, 0, st);
+  }
+  if (e == hipSuccess)
+    e = launch_split_t_ex(L.Acat, true, C, R, Rp, C, RowMap{}, L.A1cat, L.AcatT, Rpl, 0, static_cast<long long>(C) * Rpl,
+                          st);
+  if (e == hipSuccess) e = launch_split_t_ex(h, false, dh, R, Rp, dh, RowMap{}, nullptr, L.hT, Rpl, 0, 0, st);
+  // dW_f = dz^T [b | g repeated]: hi and lo parts stacked along M, then added
+  if (e == hipSuccess) e = bf16_product(2 * rz, 2 * r, RKp, L.dzT, RKpl, L.BGT, RKpl, L.s_f, L.part, st);
+  if (e == hipSuccess)
+    e = launch_sum_splits_ex(L.part, 2 * L.s_f, static_cast<long long>(rz) * 2 * r, rz, 2 * r, 2ll * r, g->dW_f, 2ll * r,
+                             st);
+  // dP_e = dx_e^T E[c]
+  if (e == hipSuccess) e = bf16_product(2 * r, de, RKp, L.dxeT, RKpl, L.EcT, RKpl, L.s_e, L.part, st);
+  if (e == hipSuccess)
+    e = launch_sum_splits_ex(L.part, 2 * L.s_e, static_cast<long long>(r) * de, r, de, de, g->dP_e, de, st);
+  // [dP_h; dW_L; dW_R] = Acat^T h
+  if (e == hipSuccess) e = bf16_product(2 * C, dh, Rp, L.AcatT, Rpl, L.hT, Rpl, L.s_h, L.part, st);
+  const long long slice = static_cast<long long>(C) * dh;
+  if (e == hipSuccess) e = launch_sum_splits_ex(L.part, 2 * L.s_h, slice, r, dh, dh, g->dP_h, dh, st);
+  if (e == hipSuccess)
+    e = launch_sum_splits_ex(L.part + static_cast<long long>(r) * dh, 2 * L.s_h, slice, rs, dh, dh, g->dW_pair, 2ll * dh,
+                             st);
+  if (e == hipSuccess)
+    e = launch_sum_splits_ex(L.part + static_cast<long long>(r + rs) * dh, 2 * L.s_h, slice, rs, dh, dh,
+                             g->dW_pair + dh, 2ll * dh, st);
+  if (!dh_out || e != hipSuccess) return e;
+  // dh = Acat [P_h; W_L; W_R]: Acat as two bf16 parts against the weights twice
+  const long long ldc2 = 2ll * C;
+  e = launch_split_t_ex(w->P_h, false, dh, r, r, dh, RowMap{}, nullptr, L.WcatT2, ldc2, 0, C, st);
+  if (e == hipSuccess)
+    e = launch_split_t_ex(w->W_pair, false, 2ll * dh, rs, rs, dh, RowMap{}, nullptr, L.WcatT2, ldc2, r, C, st);
+  if (e == hipSuccess)
+    e = launch_split_t_ex(static_cast<const char*>(w->W_pair) + 2ll * dh, false, 2ll * dh, rs, rs, dh, RowMap{},
+                          nullptr, L.WcatT2, ldc2, r + rs, C, st);
+  if (e != hipSuccess) return e;
+  if (L.s_dh == 1) return bf16_product(R, dh, 2 * C, L.A1cat, ldc2, L.WcatT2, ldc2, 1, dh_out, st);
+  e = bf16_product(R, dh, 2 * C, L.A1cat, ldc2, L.WcatT2, ldc2, L.s_dh, L.part, st);
+  if (e == hipSuccess) e = launch_sum_splits(L.part, L.s_dh, R, dh, dh_out, dh, st);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 104; }
+int dcoco_abi_version(void) { return 105; }
 
 const char* dcoco_status_string(int status) {
   switch (status) {
@@ -583,6 +766,27 @@ int dcoco_score_backward(const dcoco_dims* d, const dcoco_weights* w, const void
     e = grad_product(q, kDtypeF32, dt, L.part, ds, rs, st);
   }
   return hip_status(e);
+}
+
+int dcoco_represent_backward(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
+                             const int32_t* cand_ids, const float* dz, const float* ds, const dcoco_rep_grads* g,
+                             float* dh, void* workspace, size_t* workspace_bytes, void* stream) {
+  int rc = check_dims(d, true);
+  if (rc != DCOCO_OK) return rc;
+  if (d->dtype != DCOCO_BF16) return DCOCO_ERR_UNSUPPORTED;
+  Carve c(nullptr);
+  carve_rep_bwd(c, d);
+  rc = check_ws(workspace, workspace_bytes, c.off);
+  if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
+  if ((rc = check_weights(w, true, false)) != DCOCO_OK) return rc;
+  if (!g || !ptr_ok(g->dP_e) || !ptr_ok(g->dP_h) || !ptr_ok(g->dW_f) || !ptr_ok(g->dW_pair) || !opt_ok(dh))
+    return DCOCO_ERR_INVALID_ARG;
+  if (!ptr_ok(h) || !ptr_ok(E) || !ptr_ok(cand_ids) || !ptr_ok(dz)) return DCOCO_ERR_INVALID_ARG;
+  if (d->B > 1 && !ptr_ok(ds)) return DCOCO_ERR_INVALID_ARG;
+  Carve cw(workspace);
+  const RepBwdLayout L = carve_rep_bwd(cw, d);
+  return hip_status(run_rep_backward(d, w, h, E, cand_ids, dz, d->B > 1 ? ds : nullptr, g, dh, L,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h,

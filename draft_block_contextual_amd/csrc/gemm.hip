@@ -786,6 +786,14 @@ int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype) {
   return pick_split(M, N, Kd, bk, dma);
 }
 
+int gemm_pick_split_max(int M, int N, int Kd, int max_split) {
+  const Tile t = pick_tile(M, N, Kd % 64 == 0);
+  const long long tiles = static_cast<long long>((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  int split = 1;
+  while (tiles * split < 256 && split < max_split && Kd / (split * 2) >= 256) split *= 2;
+  return split;
+}
+
 hipError_t launch_gemm(const GemmProblem& q, hipStream_t st) {
   if (q.a_dtype == kDtypeBf16 && q.w_dtype == kDtypeBf16) return launch_gemm_t<bf16, bf16, bf16>(q, st);
   if (q.a_dtype == kDtypeF32 && q.w_dtype == kDtypeF32) return launch_gemm_t<float, float, float>(q, st);

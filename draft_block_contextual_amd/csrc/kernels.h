@@ -45,6 +45,9 @@ struct GemmProblem {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
 // number of K-splits and partial-buffer bytes chosen for a problem size
 int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype);
+// bf16 products with a long reduction (weight gradients): splits (a power of
+// two up to max_split) for about 256 workgroups, each split >= 128 deep
+int gemm_pick_split_max(int M, int N, int Kd, int max_split);
 
 // ------------------------------------------------------ row LayerNorm
 // y[m, :] = LN(sum_s x[s][m][col0 : col0 + r]) (non-affine), stored as out_dtype.
@@ -148,9 +151,46 @@ int colsum_blocks(int rows);
 hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* tmp, float* out, hipStream_t st);
 // out[0] = sum of x[0..n); tmp holds n / 8192 + 1 partial sums
 hipError_t launch_sum(const float* x, long long n, float* tmp, float* out, hipStream_t st);
+// which source row an operand row m reads: m itself, a clamped id (gathered
+// rows) or m / rep (each source row repeated rep times)
+struct RowMap {
+  int mode = 0;                // 0 identity, 1 ids, 2 repeat
+  const int32_t* ids = nullptr;
+  int idmax = 0;
+  int rep = 1;
+  __device__ __forceinline__ long long row(int m) const {
+    if (mode == 1) {
+      const int id = ids[m];
+      return id < 0 ? 0 : (id > idmax ? idmax : id);
+    }
+    if (mode == 2) return m / rep;
+    return m;
+  }
+};
 // two-part bf16 split of X [M, C] fp32 (or a bf16 copy): A1 [M, 2C] = [hi | lo]
 // (optional), At [C, 2M] = its transpose with the parts side by side
 hipError_t launch_split_t(const void* X, bool split, int M, int C, void* A1, void* At, hipStream_t st);
+// the same with a row stride, a row map and a placement in a wider At:
+// At[j][col0 + m] = hi and At[j][col0 + lo_off + m] = lo (row stride ldt) for
+// m < Mpad, rows m >= M being zeros; with lo_off == 0 a bf16 input is stored
+// once (no second copy)
+hipError_t launch_split_t_ex(const void* X, bool split, long long ldx, int M, int Mpad, int C, RowMap map, void* A1,
+                             void* At, long long ldt, long long col0, long long lo_off, hipStream_t st);
+// out[r][c] (row stride ld_out) = sum over s of part[s * split_stride + r * ld_part + c]
+hipError_t launch_sum_splits_ex(const float* part, int splits, long long split_stride, int rows, int cols,
+                                long long ld_part, float* out, long long ld_out, hipStream_t st);
+// LayerNorm forward and backward of the rows of x = sum_s x[s][M][ldx]
+// (columns col0 .. col0 + r - 1): y = LN(x) stored as bf16 [M, r]; with the
+// upstream gradient dy(m) = sum over q < rep of dY[(m rep + q) * ld_dy + c]
+// (columns dy_col0 ..), dx = (dy - mean(dy) - y mean(dy y)) / sigma into dX
+// [M, ld_dx] fp32
+hipError_t launch_ln_fwd_bwd(const float* x, int split, int M, int ldx, int col0, int r, float eps, const float* dY,
+                             long long ld_dy, int dy_col0, int rep, void* y_bf, float* dX, long long ld_dx,
+                             hipStream_t st);
+// Acat [N B, C] fp32 columns r .. r + 2 rs: the pair-state gradients ds [N, B-1, rs]
+// placed at their left slot (columns r ..) and right slot (columns r + rs ..),
+// zeros where a slot has no such pair
+hipError_t launch_pack_ds(const float* ds, int N, int B, int rs, int r, int C, float* Acat, hipStream_t st);
 // W1t [rz, 4H] bf16 from W1 [H, ldw] bf16 (see train.hip)
 hipError_t launch_w1t(const void* W1, int H, int rz, long long ldw, void* W1t, hipStream_t st);
 hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st);

@@ -353,27 +353,35 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmF32Args g) {
   }
 }
 
-// out[r * ld_out + c] = sum over the splits s (in order) of part[s][r][c]
+// out[r * ld_out + c] = sum over the splits s (in order) of
+// part[s * split_stride + r * ld_part + c]
 __global__ void __launch_bounds__(kThreads) sum_splits_kernel(const float* __restrict__ part, int splits,
-                                                              int rows, int cols, float* __restrict__ out,
+                                                              long long split_stride, int rows, int cols,
+                                                              long long ld_part, float* __restrict__ out,
                                                               long long ld_out) {
   const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
-  const long long total = static_cast<long long>(rows) * cols;
-  if (idx >= total) return;
+  if (idx >= static_cast<long long>(rows) * cols) return;
+  const long long r = idx / cols;
+  const long long c = idx % cols;
+  const float* src = part + r * ld_part + c;
   float v = 0.f;
-  for (int s = 0; s < splits; ++s) v += part[s * total + idx];
-  out[(idx / cols) * ld_out + idx % cols] = v;
+  for (int s = 0; s < splits; ++s) v += src[s * split_stride];
+  out[r * ld_out + c] = v;
 }
 
-// Two-part bf16 split of an fp32 matrix X [M, C]:
-// X = hi + lo + e with hi = bf16(X), lo = bf16(X - hi), |e| <= 2^-17 |X|.
-// Writes A1 [M, 2C] = [hi | lo] (row-major, when A1 is not null) and the
-// transpose At [C, 2M] with At[j][q M + m] = part q of X[m][j].  A bf16 input
-// (SPLIT false) is copied into both halves of At unchanged.  64 x 64 tiles
-// through LDS so both stores are coalesced.
+// Two-part bf16 split of an fp32 matrix X [M, C] (row stride ldx, row m read
+// from source row map(m)): X = hi + lo + e with hi = bf16(X), lo =
+// bf16(X - hi), |e| <= 2^-17 |X|.  Writes A1 [M, 2C] = [hi | lo] (row-major,
+// when A1 is not null) and the transpose into At: At[j][col0 + m] = hi,
+// At[j][col0 + lo_off + m] = lo (row stride ldt) for m < Mpad, the rows
+// m >= M being zeros (padding of a reduction dimension).  A bf16 input
+// (SPLIT false) is copied unchanged: into both places, or once when lo_off is
+// 0.  64 x 64 tiles through LDS so both stores are coalesced.
 template <typename TI, bool SPLIT>
-__global__ void __launch_bounds__(kThreads) split_t_kernel(const TI* __restrict__ X, int M, int C,
-                                                           uint16_t* __restrict__ A1, uint16_t* __restrict__ At) {
+__global__ void __launch_bounds__(kThreads) split_t_kernel(const TI* __restrict__ X, long long ldx, int M, int Mpad,
+                                                           int C, RowMap map, uint16_t* __restrict__ A1,
+                                                           uint16_t* __restrict__ At, long long ldt, long long col0,
+                                                           long long lo_off) {
   __shared__ uint16_t sH[64][66];
   __shared__ uint16_t sL[64][66];
   const int m0 = blockIdx.y * 64;
@@ -385,14 +393,16 @@ __global__ void __launch_bounds__(kThreads) split_t_kernel(const TI* __restrict_
   for (int r = 0; r < 16; ++r) {
     const int lm = r * 4 + (tid >> 6);
     const int m = min(m0 + lm, M - 1);
+    const long long src = map.row(m);
     uint16_t hi, lo;
     if constexpr (SPLIT) {
-      const float x = X[static_cast<long long>(m) * C + j];
+      const float x = X[src * ldx + j];
       hi = f32_to_bf16(x);
       lo = f32_to_bf16(x - bf16_to_f32(hi));
     } else {
-      hi = lo = X[static_cast<long long>(m) * C + j].bits;
+      hi = lo = X[src * ldx + j].bits;
     }
+    if (m0 + lm >= M) hi = lo = 0;
     sH[lm][lj] = hi;
     sL[lm][lj] = lo;
     if (A1 && m0 + lm < M && j0 + lj < C) {
@@ -402,15 +412,89 @@ __global__ void __launch_bounds__(kThreads) split_t_kernel(const TI* __restrict_
   }
   __syncthreads();
   const int lm = tid & 63;
-  if (m0 + lm >= M) return;
+  if (m0 + lm >= Mpad) return;
+  const bool second = SPLIT || lo_off != 0;
 #pragma unroll 4
   for (int r = 0; r < 16; ++r) {
     const int jj = r * 4 + (tid >> 6);
     if (j0 + jj >= C) break;
-    const long long row = static_cast<long long>(j0 + jj) * 2 * M;
+    const long long row = static_cast<long long>(j0 + jj) * ldt + col0;
     At[row + m0 + lm] = sH[lm][jj];
-    At[row + M + m0 + lm] = sL[lm][jj];
+    if (second) At[row + lo_off + m0 + lm] = sL[lm][jj];
   }
+}
+
+// LayerNorm forward and backward per row, one wave per row (4 rows per
+// workgroup), VPL values per lane (column l + 64 i).  Forward as in the
+// representation stage: the split partials added in order, two-pass mean and
+// variance in fp32, y = (x - mean) / sqrt(var + eps).  Backward:
+// dx = (dy - mean(dy) - y mean(dy y)) / sqrt(var + eps), dy being the sum
+// (in order) of rep upstream rows.
+template <int VPL>
+__global__ void __launch_bounds__(kThreads)
+ln_fwd_bwd_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0, int r, float eps,
+                  const float* __restrict__ dY, long long ld_dy, int dy_col0, int rep, uint16_t* __restrict__ y_bf,
+                  float* __restrict__ dX, long long ld_dx) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= M) return;
+  const float inv_r = 1.0f / static_cast<float>(r);
+  float v[VPL], g[VPL];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = l + i * 64;
+    float a = 0.f, b = 0.f;
+    if (c < r) {
+      for (int s = 0; s < split; ++s) a += x[(static_cast<long long>(s) * M + row) * ldx + col0 + c];
+      for (int q = 0; q < rep; ++q) b += dY[(static_cast<long long>(row) * rep + q) * ld_dy + dy_col0 + c];
+    }
+    v[i] = a;
+    g[i] = b;
+    sum += a;
+  }
+  const float mean = wave_sum(sum) * inv_r;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    v[i] = (l + i * 64) < r ? v[i] - mean : 0.f;
+    sq += v[i] * v[i];
+  }
+  const float inv = 1.0f / sqrtf(wave_sum(sq) * inv_r + eps);
+  float sg = 0.f, sgy = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    v[i] *= inv;                       // y
+    sg += g[i];
+    sgy += g[i] * v[i];
+  }
+  const float mg = wave_sum(sg) * inv_r;
+  const float mgy = wave_sum(sgy) * inv_r;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = l + i * 64;
+    if (c < r) {
+      y_bf[static_cast<long long>(row) * r + c] = f32_to_bf16(v[i]);
+      dX[static_cast<long long>(row) * ld_dx + c] = (g[i] - mg - v[i] * mgy) * inv;
+    }
+  }
+}
+
+// Acat[i][r + c] = ds of the pair whose left slot is i, Acat[i][r + rs + c] =
+// ds of the pair whose right slot is i (zeros at the block ends)
+__global__ void __launch_bounds__(kThreads) pack_ds_kernel(const float* __restrict__ ds, int N, int B, int rs, int r,
+                                                           int C, float* __restrict__ Acat) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx >= static_cast<long long>(N) * B * 2 * rs) return;
+  const long long i = idx / (2 * rs);
+  const int c2 = static_cast<int>(idx % (2 * rs));
+  const int side = c2 / rs;              // 0: i is the left slot, 1: the right slot
+  const int c = c2 % rs;
+  const long long n = i / B;
+  const int j = static_cast<int>(i % B) - side;   // pair index within the block
+  float v = 0.f;
+  if (j >= 0 && j < B - 1) v = ds[(n * (B - 1) + j) * rs + c];
+  Acat[i * C + r + c2] = v;
 }
 
 // W1t [rz, 4H] bf16: W1t[c][q 2H + j] = W1[j][c] (j < H) or W1[j - H][rz + c],
@@ -441,13 +525,45 @@ hipError_t launch_loss(const float* S, const int32_t* cand_ids, const int32_t* t
 }
 
 hipError_t launch_split_t(const void* X, bool split, int M, int C, void* A1, void* At, hipStream_t st) {
-  const dim3 grid((C + 63) / 64, (M + 63) / 64);
+  return launch_split_t_ex(X, split, C, M, M, C, RowMap{}, A1, At, 2ll * M, 0, M, st);
+}
+
+hipError_t launch_split_t_ex(const void* X, bool split, long long ldx, int M, int Mpad, int C, RowMap map, void* A1,
+                             void* At, long long ldt, long long col0, long long lo_off, hipStream_t st) {
+  if (M <= 0 || C <= 0 || Mpad < M) return M <= 0 ? hipSuccess : hipErrorInvalidValue;
+  const dim3 grid((C + 63) / 64, (Mpad + 63) / 64);
   if (split)
-    hipLaunchKernelGGL((split_t_kernel<float, true>), grid, dim3(kThreads), 0, st, static_cast<const float*>(X), M,
-                       C, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At));
+    hipLaunchKernelGGL((split_t_kernel<float, true>), grid, dim3(kThreads), 0, st, static_cast<const float*>(X), ldx,
+                       M, Mpad, C, map, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At), ldt, col0, lo_off);
   else
-    hipLaunchKernelGGL((split_t_kernel<bf16, false>), grid, dim3(kThreads), 0, st, static_cast<const bf16*>(X), M,
-                       C, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At));
+    hipLaunchKernelGGL((split_t_kernel<bf16, false>), grid, dim3(kThreads), 0, st, static_cast<const bf16*>(X), ldx,
+                       M, Mpad, C, map, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At), ldt, col0, lo_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_fwd_bwd(const float* x, int split, int M, int ldx, int col0, int r, float eps, const float* dY,
+                             long long ld_dy, int dy_col0, int rep, void* y_bf, float* dX, long long ld_dx,
+                             hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const int vpl = (r + 63) / 64;
+  const dim3 grid((M + 3) / 4);
+  uint16_t* yb = static_cast<uint16_t*>(y_bf);
+#define DCOCO_LNB(V)                                                                                              \
+  hipLaunchKernelGGL((ln_fwd_bwd_kernel<V>), grid, dim3(kThreads), 0, st, x, split, M, ldx, col0, r, eps, dY, ld_dy, \
+                     dy_col0, rep, yb, dX, ld_dx)
+  if (vpl <= 4) DCOCO_LNB(4);
+  else if (vpl <= 8) DCOCO_LNB(8);
+  else if (vpl <= 16) DCOCO_LNB(16);
+  else if (vpl <= 32) DCOCO_LNB(32);
+  else return hipErrorInvalidValue;
+#undef DCOCO_LNB
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_ds(const float* ds, int N, int B, int rs, int r, int C, float* Acat, hipStream_t st) {
+  const long long n = static_cast<long long>(N) * B * 2 * rs;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_ds_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, st, ds, N, B, rs, r, C, Acat);
   return hipGetLastError();
 }
 
@@ -495,8 +611,15 @@ hipError_t launch_gemm_f32(const GemmF32Args& g, int a_dtype, int b_dtype, hipSt
 
 hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, float* out, long long ld_out,
                              hipStream_t st) {
-  hipLaunchKernelGGL(sum_splits_kernel, dim3(blocks_for(static_cast<long long>(rows) * cols)), dim3(kThreads), 0,
-                     st, part, splits, rows, cols, out, ld_out);
+  return launch_sum_splits_ex(part, splits, static_cast<long long>(rows) * cols, rows, cols, cols, out, ld_out, st);
+}
+
+hipError_t launch_sum_splits_ex(const float* part, int splits, long long split_stride, int rows, int cols,
+                                long long ld_part, float* out, long long ld_out, hipStream_t st) {
+  const long long n = static_cast<long long>(rows) * cols;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_splits_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, st, part, splits, split_stride,
+                     rows, cols, ld_part, out, ld_out);
   return hipGetLastError();
 }
 

@@ -241,6 +241,40 @@ int dcoco_score_backward(const dcoco_dims* dims, const dcoco_weights* w, const v
                          float* d_cand_logits, const dcoco_mlp_grads* grads,
                          void* workspace, size_t* workspace_bytes, void* stream);
 
+/* Gradients of the representation weights, fp32, overwritten. */
+typedef struct {
+  float* dP_e;     /* [d_proj, d_embed] */
+  float* dP_h;     /* [d_proj, d_hidden] */
+  float* dW_f;     /* [d_z, 2 d_proj], columns as W_f: [b | g] */
+  float* dW_pair;  /* [d_pair, 2 d_hidden], columns as W_pair: [h_p | h_{p+1}] */
+} dcoco_rep_grads;
+
+/* Backward of the representations ([P2] part 1, paper Sec. 3.2, with the
+ * forward of dcoco_represent): given dz = dL/dz and ds = dL/ds (e.g. from
+ * dcoco_score_backward), with x_e = P_e E[c], x_h = P_h h, b = LN(x_e),
+ * g = LN(x_h), sigma = sqrt(var + eps) per row:
+ *   dW_f = sum_{i,k} dz_{i,k} [b_{i,k}; g_i]^T,
+ *   db = W_fb^T dz,  dg_i = W_fg^T sum_k dz_{i,k},
+ *   dx = (dy - mean(dy) - y mean(dy y)) / sigma  (LN backward, y = LN(x)),
+ *   dP_e = sum dx_e E[c]^T,  dP_h = sum dx_h h^T,
+ *   dW_pair = sum_p ds_p [h_p; h_{p+1}]^T,
+ *   dh_i = P_h^T dx_{h,i} + W_L^T ds_i + W_R^T ds_{i-1}  (pairs that exist).
+ * E is frozen (no gradient).  x_e and x_h are recomputed; the bf16 roundings
+ * of b and g count as the identity, and dW_f takes the rounded b and g.
+ * bf16 storage only (fp32 storage: DCOCO_ERR_UNSUPPORTED).
+ *   h, E, cand_ids  as dcoco_represent
+ *   dz   [n_blocks, B, K, d_z] fp32
+ *   ds   [n_blocks, B-1, d_pair] fp32   (may be NULL when B == 1)
+ *   grads                               out (every pointer required)
+ *   dh   [n_blocks, B, d_hidden] fp32   out, may be NULL (not computed)
+ * The gradient products run on bf16 MFMA over a two-part bf16 split of the
+ * fp32 gradients (relative remainder <= 2^-17) with fp32 accumulation.
+ * Workspace queried as for the other entry points.  Deterministic. */
+int dcoco_represent_backward(const dcoco_dims* dims, const dcoco_weights* w, const void* h,
+                             const void* E, const int32_t* cand_ids, const float* dz,
+                             const float* ds, const dcoco_rep_grads* grads, float* dh,
+                             void* workspace, size_t* workspace_bytes, void* stream);
+
 /* The whole path for n_blocks draft blocks: top-K, representations, pair
  * states, transition scores and the greedy walk, on one stream.
  *   logits [n_blocks*B, V], h [n_blocks, B, d_hidden], E [V, d_embed]: dtype
@@ -286,7 +320,8 @@ const char* dcoco_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor): 101 adds the table
  * entry points, 102 dcoco_select_path, 103 dcoco_loss and
- * dcoco_score_backward, 104 dcoco_lm_head_topk. */
+ * dcoco_score_backward, 104 dcoco_lm_head_topk, 105
+ * dcoco_represent_backward. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import draft_block_contextual_amd as dc
-    assert lib.dcoco_abi_version() == 104
+    assert lib.dcoco_abi_version() == 105
     assert dc.status_string(0) == "ok"
     for code in (-1, -2, -3, -4):
         assert dc.status_string(code) not in ("ok", "unknown status")
@@ -195,3 +195,34 @@ def test_training_argument_checks(lib):
     small = ctypes.c_size_t(n.value - 256)
     assert lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), fake, fake, fake, fake, None, None,
                                     ctypes.byref(g), fake, ctypes.byref(small), None) == -3
+
+
+def test_represent_backward_argument_checks(lib):
+    import draft_block_contextual_amd as dc
+    fake = ctypes.c_void_p(1 << 20)
+    cw = dc.CWeights()
+    g = dc.CRepGrads()
+    n = ctypes.c_size_t(0)
+
+    def call(dims, h=None, E=None, ids=None, dz=None, ds=None, grads=g, ws=None, nb=n):
+        return lib.dcoco_represent_backward(ctypes.byref(dims.c()), ctypes.byref(cw), h, E, ids, dz, ds,
+                                            ctypes.byref(grads), None, ws, ctypes.byref(nb), None)
+
+    d = _dims(n_blocks=2)
+    assert call(d) == 0
+    # the gathered rows transposed, the dz split and the forward partials
+    RK = 2 * 16 * 16
+    assert n.value >= RK * 4096 * 2 + RK * 256 * 2 * 2
+    assert call(_dims(n_blocks=2, dtype="f32")) == -2          # bf16 storage only
+    assert call(_dims(n_blocks=2, d_proj=48)) == -2
+    # weights, gradient buffers and inputs are checked before any launch
+    need = n.value
+    nb = ctypes.c_size_t(need)
+    assert call(d, fake, fake, fake, fake, fake, ws=fake, nb=nb) == -1          # no weights
+    cw.P_e = cw.P_h = cw.W_f = cw.W_pair = 1 << 20
+    assert call(d, fake, fake, fake, fake, fake, ws=fake, nb=nb) == -1          # no gradient buffers
+    g.dP_e = g.dP_h = g.dW_f = g.dW_pair = 1 << 20
+    assert call(d, fake, fake, fake, fake, None, ws=fake, nb=nb) == -1          # B > 1 needs ds
+    assert call(d, None, fake, fake, fake, fake, ws=fake, nb=nb) == -1          # no h
+    small = ctypes.c_size_t(need - 256)
+    assert call(d, fake, fake, fake, fake, fake, ws=fake, nb=small) == -3

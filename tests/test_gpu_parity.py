@@ -723,6 +723,138 @@ def test_score_backward_full_q8b_32_sampled():
     _grad_check(_np(out["d_cand_logits"])[blocks], R["d_cand_vals"], "full:dcl")
 
 
+# ------------------------------------------------- representation backward
+
+def _ln64(x, eps):
+    mu = x.mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + eps)
+
+
+def _flip_size(y):
+    """How far the bf16 rounding of an LN output may move between the fp64
+    oracle and the kernel's fp32 evaluation: the rounding decision is taken
+    on values that agree to about 1e-7 of max(1, |y|), so an entry within
+    2^-17 of that scale of a rounding midpoint may round either way (by one
+    bf16 step); every other entry rounds alike (size 0)."""
+    w = 2.0 ** -17 * np.maximum(1.0, np.abs(y))
+    return np.abs(O.round_bf16(y + w) - O.round_bf16(y - w))
+
+
+def _rep_bwd_check(out, h, Er, f64, dz, ds, eps, blocks=None, tag=""):
+    R = O.represent_backward(h, Er, f64["P_e"], f64["P_h"], f64["W_f"], f64["W_pair"], dz, ds, eps, True)
+    for key in ("dP_e", "dP_h", "dW_pair"):
+        _grad_check(_np(out[key]), R[key], f"{tag}:{key}")
+    if "dh" in out:
+        dh = _np(out["dh"])
+        if blocks is not None:
+            others = np.setdiff1d(np.arange(dh.shape[0]), blocks)
+            assert np.all(dh[others] == 0), tag
+            dh = dh[blocks]
+        _grad_check(dh, R["dh"], f"{tag}:dh")
+    # dW_f multiplies the bf16-rounded b and g: besides the fp32 floor, each
+    # entry may move by the upstream gradient times a rounding step wherever
+    # the rounding decision is a near-tie
+    r = f64["P_e"].shape[0]
+    fb = _flip_size(_ln64(Er @ f64["P_e"].T, eps))              # [N, B, K, r]
+    fg = _flip_size(_ln64(h @ f64["P_h"].T, eps))               # [N, B, r]
+    slack = np.concatenate([np.einsum("nbkz,nbkr->zr", np.abs(dz), fb),
+                            np.einsum("nbz,nbr->zr", np.abs(dz.sum(axis=2)), fg)], axis=1)
+    got = _np(out["dW_f"]).astype(np.float64)
+    ref = R["dW_f"]
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref)
+    assert np.all(err <= 2e-4 * scale + slack), (tag, "dW_f", (err - slack).max(), scale)
+    assert got.shape == (f64["W_f"].shape[0], 2 * r)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "k64_small", "k32_small", "widez_bf16", "tall_bf16"])
+def test_represent_backward_matches_oracle(name):
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case represent_backward {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    ref = _oracle(name)
+    dims, w, _, h, E = device_inputs(inp)
+    ids = ref["cand_ids"].astype(np.int32)
+    g = np.random.default_rng(67)
+    dz = (g.standard_normal((D.n_blocks, D.B, D.K, D.r_z)) / D.n_blocks).astype(np.float32)
+    ds = (g.standard_normal((D.n_blocks, D.B - 1, D.r_s)) / D.n_blocks).astype(np.float32)
+    out = dc.represent_backward(dims, w, h, E, _dev_i32(ids), _dev_f32(dz), _dev_f32(ds))
+    torch.cuda.synchronize()
+    f64 = {k: O.to_f64(inp[k], "bf16") for k in ("P_e", "P_h", "W_f", "W_pair")}
+    h64 = O.to_f64(inp["h"], "bf16")
+    Er = O.to_f64(inp["E"], "bf16")[ids]
+    _rep_bwd_check(out, h64, Er, f64, dz.astype(np.float64), ds.astype(np.float64), D.ln_eps, tag=name)
+
+
+def test_represent_backward_single_slot_and_no_dh():
+    # B = 1: no pairs, so dW_pair is zero and dh is the LN path alone; a
+    # second call without dh leaves the weight gradients unchanged
+    import draft_block_contextual_amd as dc
+    import dataclasses
+    import torch
+    name = "small_bf16"
+    print(f"case represent_backward {name} B=1", flush=True)
+    inp = _inputs(name)
+    D1 = dataclasses.replace(inp["dims"], B=1)
+    ids = _oracle(name)["cand_ids"][:, :1].astype(np.int32)
+    dims, w, _, _, E = device_inputs(inp)
+    dims = dc.Dims.from_synth(D1)
+    h1 = np.ascontiguousarray(inp["h"][:, :1])
+    hd = to_dev(h1, "bf16", "cuda")
+    g = np.random.default_rng(68)
+    dz = g.standard_normal((D1.n_blocks, 1, D1.K, D1.r_z)).astype(np.float32)
+    out = dc.represent_backward(dims, w, hd, E, _dev_i32(ids), _dev_f32(dz), None)
+    out2 = dc.represent_backward(dims, w, hd, E, _dev_i32(ids), _dev_f32(dz), None, want_dh=False)
+    torch.cuda.synchronize()
+    assert np.all(_np(out["dW_pair"]) == 0)
+    for key in ("dP_e", "dP_h", "dW_f"):
+        assert np.array_equal(_np(out[key]), _np(out2[key])), key
+    f64 = {k: O.to_f64(inp[k], "bf16") for k in ("P_e", "P_h", "W_f", "W_pair")}
+    Er = O.to_f64(inp["E"], "bf16")[ids]
+    _rep_bwd_check(out, O.to_f64(h1, "bf16"), Er, f64, dz.astype(np.float64),
+                   np.zeros((D1.n_blocks, 0, D1.r_s)), D1.ln_eps, tag="B1")
+
+
+def test_represent_backward_full_q8b_32_sampled():
+    # the full 32-block launch with the upstream gradients nonzero in two
+    # blocks only: the weight gradients are then those two blocks' sums (the
+    # oracle computes them), and dh of every other block is exactly zero
+    import draft_block_contextual_amd as dc
+    import torch
+    D = synth.get_config("q8b_32").dims
+    N, B, K, d, e, r, rz, rs = D.n_blocks, D.B, D.K, D.d, D.e, D.r, D.r_z, D.r_s
+    print(f"case represent_backward q8b_32 N={N} B={B} K={K}", flush=True)
+    g = np.random.default_rng(69)
+
+    def bf(x):
+        return (np.asarray(x, np.float32).view(np.uint32) + 0x8000 >> 16 << 16).view(np.float32).astype(np.float64)
+
+    pool = np.sort(g.choice(D.V, 8192, replace=False))
+    rows = bf(g.standard_normal((len(pool), e)))
+    ids = pool[g.integers(0, len(pool), (N, B, K))].astype(np.int32)
+    h = bf(g.standard_normal((N, B, d)) * 30)
+    W = {"P_e": bf(g.standard_normal((r, e)) / np.sqrt(e)), "P_h": bf(g.standard_normal((r, d)) / np.sqrt(d)),
+         "W_f": bf(g.standard_normal((rz, 2 * r)) / np.sqrt(2 * r)),
+         "W_pair": bf(g.standard_normal((rs, 2 * d)) / np.sqrt(2 * d))}
+    blocks = [0, 17]
+    dz = np.zeros((N, B, K, rz), np.float32)
+    ds = np.zeros((N, B - 1, rs), np.float32)
+    dz[blocks] = g.standard_normal((2, B, K, rz)).astype(np.float32) / N
+    ds[blocks] = g.standard_normal((2, B - 1, rs)).astype(np.float32) / N
+    E = torch.zeros((D.V, e), dtype=torch.bfloat16, device="cuda")
+    E[torch.from_numpy(pool).cuda()] = _bf16_dev(rows)
+    dims = dc.Dims.from_synth(D)
+    w = dc.Weights(P_e=_bf16_dev(W["P_e"]), P_h=_bf16_dev(W["P_h"]), W_f=_bf16_dev(W["W_f"]),
+                   W_pair=_bf16_dev(W["W_pair"]), W1=None, b1=None, w2=None, b2=0.0)
+    out = dc.represent_backward(dims, w, _bf16_dev(h), E, _dev_i32(ids), _dev_f32(dz), _dev_f32(ds))
+    torch.cuda.synchronize()
+    lookup = np.searchsorted(pool, ids[blocks])
+    _rep_bwd_check(out, h[blocks], rows[lookup], W, dz[blocks].astype(np.float64), ds[blocks].astype(np.float64),
+                   D.ln_eps, blocks=blocks, tag="full")
+
+
 # ---------------------------------------------------------- drafter LM head
 
 def _lm_check(ids, vals, logits, K):
