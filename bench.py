@@ -70,6 +70,10 @@ def algorithmic_work(D):
         "weight_bytes": w_params * e,
         "mfma_flops": 2.0 * (RK * D.e * D.r + R * D.d * (D.r + 2 * D.r_s) + R * D.r * D.r_z
                              + RK * D.r * D.r_z + 2 * RK * D.r_z * D.H),
+        # representation backward: P_e E[c] and P_h h again, dz W_f, dW_f,
+        # dP_e, [dP_h; dW_pair] and dh (each product counted once)
+        "rep_bwd_flops": 2.0 * (2 * RK * D.e * D.r + R * D.d * D.r + 2 * RK * D.r_z * 2 * D.r
+                                + 2 * R * D.d * (D.r + 2 * D.r_s)),
         "grid_elems": P * D.K * D.K * D.H,
         "transitions": P * D.K * D.K,
     }
@@ -244,6 +248,13 @@ def main():
         "train_loss": lambda i: dc.loss(dims, S, ids, targets(), 4.0, stream=stream),
         "train_backward": lambda i: dc.score_backward(dims, w, z, s, S, stream=stream),
     }
+    if dt == "bf16":
+        # and on through the representations (P_e, P_h, W_f, W_pair and dh)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        dzr = torch.randn((N, B, K, D.r_z), generator=gen, device=dev) / N
+        dsr = torch.randn((N, max(B - 1, 1), D.r_s), generator=gen, device=dev) / N
+        stages["train_rep_backward"] = lambda i: dc.represent_backward(dims, w, dsets[i % len(dsets)][1], E, ids,
+                                                                       dzr, dsr, stream=stream)
     tgt_cache = []
 
     def targets():
@@ -372,6 +383,8 @@ def main():
         "mfma_frac_represent": round(work["mfma_flops"] / (stage_us["represent"] * 1e-6) / 1e12
                                      / MFMA_BF16_PEAK_TFLOPS, 4),
         "alu_frac_score": round(grid_rate / VALU_LANE_OPS, 4),
+        "mfma_frac_rep_backward": (round(work["rep_bwd_flops"] / (stage_us["train_rep_backward"] * 1e-6) / 1e12
+                                         / MFMA_BF16_PEAK_TFLOPS, 4) if "train_rep_backward" in stage_us else None),
         "roofline": roof,
         "cpu_baseline": cpu,
         "btable_path": btable,

@@ -293,23 +293,20 @@ int check_ws(void* ws, size_t* bytes, size_t need) {
 
 constexpr int kMaxGradSplit = 16;
 
-// bf16 storage with N*B*K a multiple of 32: the two large gradient products
-// run on bf16 MFMA over a two-part split of the fp32 gradients
-bool bwd_on_mfma(const dcoco_dims* d) {
-  return d->dtype == DCOCO_BF16 && (static_cast<long long>(d->n_blocks) * d->B * d->K) % 32 == 0;
-}
+// bf16 storage: the two large gradient products run on bf16 MFMA over a
+// two-part split of the fp32 gradients (the row-reduction kernel)
+bool bwd_on_mfma(const dcoco_dims* d) { return d->dtype == DCOCO_BF16; }
+
+size_t wgrad_part_floats(int M, int N, int Kd);
 
 struct BwdLayout {
   ScoreLayout SL;
   float* dAB;      // [N*B*K, 2H]
   float* dC;       // [P, H]
   float* dw2p;     // [P, H]
-  float* part;     // [kMaxGradSplit, max(H, P), max(d_z, d_pair)]
+  float* part;     // split partial products
+  size_t part_floats;
   float* red;      // partial sums of the reductions
-  void* A1;        // bf16 [N*B*K, 4H]: [dA | dB] hi, then lo
-  void* At;        // bf16 [2H, 2 N*B*K]: its transpose, parts side by side
-  void* Zt;        // bf16 [d_z, 2 N*B*K]: z transposed, twice
-  void* W1t;       // bf16 [d_z, 4H]
 };
 
 BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
@@ -321,16 +318,14 @@ BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
   L.dAB = static_cast<float*>(c.take(sizeof(float) * RK * 2 * H));
   L.dC = static_cast<float*>(c.take(sizeof(float) * P * H));
   L.dw2p = static_cast<float*>(c.take(sizeof(float) * P * H));
-  L.part = static_cast<float*>(
-      c.take(sizeof(float) * kMaxGradSplit * std::max(H, P) * std::max(d->d_z, d->d_pair)));
+  L.part_floats = kMaxGradSplit * std::max(H, P) * std::max(d->d_z, d->d_pair);
+  if (bwd_on_mfma(d))
+    L.part_floats = std::max({L.part_floats, wgrad_part_floats(static_cast<int>(RK), d->d_z, 2 * d->d_mlp),
+                              wgrad_part_floats(2 * d->d_mlp, d->d_z, static_cast<int>(RK))});
+  L.part = static_cast<float*>(c.take(sizeof(float) * L.part_floats));
   const size_t red = 2 * (static_cast<size_t>(colsum_blocks(static_cast<int>(P))) + 1) * H +
                      P * d->K * d->K / 8192 + 2;
   L.red = static_cast<float*>(c.take(sizeof(float) * red));
-  const bool mf = bwd_on_mfma(d);
-  L.A1 = c.take(mf ? 2 * RK * 4 * H : 0);
-  L.At = c.take(mf ? 2 * 2 * H * 2 * RK : 0);
-  L.Zt = c.take(mf ? 2 * static_cast<size_t>(d->d_z) * 2 * RK : 0);
-  L.W1t = c.take(mf ? 2 * static_cast<size_t>(d->d_z) * 4 * H : 0);
   return L;
 }
 
@@ -349,32 +344,61 @@ hipError_t grad_product(GemmF32Args q, int a_dt, int b_dt, float* part, float* o
   return launch_sum_splits(part, splits, q.M, q.N, out, ldo, st);
 }
 
-// ---- representation backward (bf16 storage)
+// ---- gradient products on the row-reduction kernel
 
-int pad64(int x) { return (x + 63) / 64 * 64; }
+// one destination of a product's output rows (consecutive segments)
+struct OutSeg {
+  float* c;
+  long long ld;
+  int rows;
+};
+
+// split-K choice for a product, never more than the partial buffer holds
+int wgrad_split_for(int M, int N, int Kd, size_t part_floats) {
+  int split = wgrad_pick_split(M, N, Kd);
+  while (split > 1 && static_cast<size_t>(split) * M * N > part_floats) split /= 2;
+  return split;
+}
+
+size_t wgrad_part_floats(int M, int N, int Kd) {
+  const int split = wgrad_pick_split(M, N, Kd);
+  return split > 1 ? static_cast<size_t>(split) * M * N : 0;
+}
+
+// runs the product p (A, B, M, N, Kd set) with its output rows going to
+// segs[0..nseg) in order; with a k split, through fp32 partials summed in order
+hipError_t wgrad_run(WgradArgs p, bool rr, const OutSeg* segs, int nseg, float* part, size_t part_floats,
+                     hipStream_t st) {
+  const int split = wgrad_split_for(p.M, p.N, p.Kd, part_floats);
+  if (split == 1) {
+    p.c0 = segs[0].c; p.ldc0 = segs[0].ld; p.cend0 = segs[0].rows;
+    if (nseg > 1) { p.c1 = segs[1].c; p.ldc1 = segs[1].ld; p.cend1 = segs[0].rows + segs[1].rows; }
+    if (nseg > 2) { p.c2 = segs[2].c; p.ldc2 = segs[2].ld; }
+    return launch_wgrad(p, rr, 1, st);
+  }
+  p.c0 = part; p.ldc0 = p.N; p.c_split = static_cast<long long>(p.M) * p.N;
+  hipError_t e = launch_wgrad(p, rr, split, st);
+  const int gz = wgrad_grid_splits(p.Kd, split);
+  long long row = 0;
+  for (int i = 0; i < nseg && e == hipSuccess; ++i) {
+    e = launch_sum_splits_ex(part + row * p.N, gz, p.c_split, segs[i].rows, p.N, p.N, segs[i].c, segs[i].ld, st);
+    row += segs[i].rows;
+  }
+  return e;
+}
+
+// ---- representation backward (bf16 storage)
 
 struct RepBwdLayout {
   int split_h, split_e;    // forward recompute: split-K of P_h h and P_e E[c]
-  int s_f, s_e, s_h, s_dh; // splits of the gradient products
-  int Rp, RKp;             // row counts padded to 64 (reduction length)
   float* Y;                // [split_h][R][r]: P_h h partials
   float* U;                // [split_e][RK][r]: P_e E[c] partials
-  void* A1z;               // bf16 [RK, 2 d_z]: dz hi | lo
-  void* dzT;               // bf16 [2 d_z, RKp]: dz^T, hi rows then lo rows
-  void* WfT2;              // bf16 [2 r, 2 d_z]: W_f^T, twice along k
   float* dBG;              // [RK, 2 r]: dz W_f (db | per-candidate part of dg)
-  void* bq;                // bf16 [RK, r]: b
-  void* gq;                // bf16 [R, r]: g
+  void* BG;                // bf16 [RK, 2 r]: b | g repeated over the slot's candidates
   float* dxe;              // [RK, r]
-  void* BGT;               // bf16 [2 r, RKp]: b^T, then g^T repeated over k
-  void* dxeT;              // bf16 [2 r, RKp]: dx_e^T hi rows then lo rows
-  void* EcT;               // bf16 [d_embed, RKp]: the gathered E rows, transposed
   float* Acat;             // [R, C]: dx_h | ds at the left slot | ds at the right slot
-  void* A1cat;             // bf16 [R, 2C]
-  void* AcatT;             // bf16 [2C, Rp]
-  void* hT;                // bf16 [d_hidden, Rp]
-  void* WcatT2;            // bf16 [d_hidden, 2C]: [P_h; W_L; W_R]^T, twice along k
   float* part;             // split partial products
+  size_t part_floats;
 };
 
 RepBwdLayout carve_rep_bwd(Carve& c, const dcoco_dims* d) {
@@ -383,51 +407,19 @@ RepBwdLayout carve_rep_bwd(Carve& c, const dcoco_dims* d) {
   const int RK = R * d->K;
   const int r = d->d_proj, rz = d->d_z, rs = d->d_pair, dh = d->d_hidden, de = d->d_embed;
   const int C = r + 2 * rs;
-  L.Rp = pad64(R);
-  L.RKp = pad64(RK);
   L.split_h = gemm_pick_split(R, r, dh, kDtypeBf16, kDtypeBf16);
   L.split_e = gemm_pick_split(RK, r, de, kDtypeBf16, kDtypeBf16);
-  L.s_f = gemm_pick_split_max(2 * rz, 2 * r, L.RKp, kMaxGradSplit);
-  L.s_e = gemm_pick_split_max(2 * r, de, L.RKp, kMaxGradSplit);
-  L.s_h = gemm_pick_split_max(2 * C, dh, L.Rp, kMaxGradSplit);
-  L.s_dh = gemm_pick_split_max(R, dh, 2 * C, 4);
-  const size_t bf = 2, f4 = 4;
-  const size_t RKs = RK, Rs = R, RKps = L.RKp, Rps = L.Rp;
-  L.Y = static_cast<float*>(c.take(f4 * L.split_h * Rs * r));
-  L.U = static_cast<float*>(c.take(f4 * L.split_e * RKs * r));
-  L.A1z = c.take(bf * RKs * 2 * rz);
-  L.dzT = c.take(bf * 2 * rz * RKps);
-  L.WfT2 = c.take(bf * 2 * r * 2 * rz);
-  L.dBG = static_cast<float*>(c.take(f4 * RKs * 2 * r));
-  L.bq = c.take(bf * RKs * r);
-  L.gq = c.take(bf * Rs * r);
-  L.dxe = static_cast<float*>(c.take(f4 * RKs * r));
-  L.BGT = c.take(bf * 2 * r * RKps);
-  L.dxeT = c.take(bf * 2 * r * RKps);
-  L.EcT = c.take(bf * de * RKps);
-  L.Acat = static_cast<float*>(c.take(f4 * Rs * C));
-  L.A1cat = c.take(bf * Rs * 2 * C);
-  L.AcatT = c.take(bf * 2 * C * Rps);
-  L.hT = c.take(bf * dh * Rps);
-  L.WcatT2 = c.take(bf * dh * 2 * C);
-  const size_t part = std::max({static_cast<size_t>(L.s_f) * 2 * rz * 2 * r, static_cast<size_t>(L.s_e) * 2 * r * de,
-                                static_cast<size_t>(L.s_h) * 2 * C * dh, static_cast<size_t>(L.s_dh) * Rs * dh});
-  L.part = static_cast<float*>(c.take(f4 * part));
+  const size_t RKs = RK, Rs = R;
+  L.Y = static_cast<float*>(c.take(4 * L.split_h * Rs * r));
+  L.U = static_cast<float*>(c.take(4 * L.split_e * RKs * r));
+  L.dBG = static_cast<float*>(c.take(4 * RKs * 2 * r));
+  L.BG = c.take(2 * RKs * 2 * r);
+  L.dxe = static_cast<float*>(c.take(4 * RKs * r));
+  L.Acat = static_cast<float*>(c.take(4 * Rs * C));
+  L.part_floats = std::max({wgrad_part_floats(RK, 2 * r, rz), wgrad_part_floats(rz, 2 * r, RK),
+                            wgrad_part_floats(r, de, RK), wgrad_part_floats(C, dh, R), wgrad_part_floats(R, dh, C)});
+  L.part = static_cast<float*>(c.take(4 * std::max<size_t>(L.part_floats, 1)));
   return L;
-}
-
-// C [M, N] = A [M, Kd] W^T (W rows [N][Kd], both bf16, Kd % 64 == 0) into
-// fp32 split partials part [split][M][N]
-hipError_t bf16_product(int M, int N, int Kd, const void* A, long long lda, const void* W, long long ldw, int split,
-                        float* part, hipStream_t st) {
-  GemmProblem q{};
-  q.M = M; q.N = N; q.Kd = Kd;
-  q.A = A; q.lda = lda; q.a_dtype = kDtypeBf16;
-  q.w[0] = W; q.ldw[0] = ldw; q.col0[0] = 0;
-  q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = N;
-  q.w_dtype = kDtypeBf16;
-  q.split = split; q.out_f32 = part; q.ldo = N; q.out = nullptr;
-  return launch_gemm(q, st);
 }
 
 hipError_t run_rep_backward(const dcoco_dims* d, const dcoco_weights* w, const void* h, const void* E,
@@ -437,8 +429,9 @@ hipError_t run_rep_backward(const dcoco_dims* d, const dcoco_weights* w, const v
   const int R = N * B, RK = R * K;
   const int r = d->d_proj, rz = d->d_z, rs = d->d_pair, dh = d->d_hidden, de = d->d_embed;
   const int C = r + 2 * rs;
-  const int Rp = L.Rp, RKp = L.RKp;
-  const long long RKpl = RKp, Rpl = Rp;
+  const uint16_t* Wf = static_cast<const uint16_t*>(w->W_f);
+  const uint16_t* Wp = static_cast<const uint16_t*>(w->W_pair);
+  uint16_t* BG = static_cast<uint16_t*>(L.BG);
   hipError_t e = hipSuccess;
   // forward recompute: x_h = P_h h, x_e = P_e E[c] (split-K partials)
   {
@@ -461,75 +454,61 @@ hipError_t run_rep_backward(const dcoco_dims* d, const dcoco_weights* w, const v
     q.split = L.split_e; q.out_f32 = L.U; q.ldo = r; q.out = nullptr;
     e = launch_gemm(q, st);
   }
-  // dBG = dz [W_fb | W_fg]: dz as two bf16 parts against W_f^T twice
+  // dBG = dz [W_fb | W_fg]
+  if (e == hipSuccess) {
+    WgradArgs p;
+    p.M = RK; p.N = 2 * r; p.Kd = rz;
+    p.A = dz; p.lda = rz;
+    p.b0 = Wf; p.ldb0 = 2ll * r;
+    const OutSeg o{L.dBG, 2ll * r, RK};
+    e = wgrad_run(p, false, &o, 1, L.part, L.part_floats, st);
+  }
+  // LayerNorm forward (b, and g once per candidate, into BG) and backward
+  // (dx_e; dx_h into Acat); ds placed by slot
   if (e == hipSuccess)
-    e = launch_split_t_ex(dz, true, rz, RK, RKp, rz, RowMap{}, L.A1z, L.dzT, RKpl, 0, static_cast<long long>(rz) * RKpl,
+    e = launch_ln_fwd_bwd(L.U, L.split_e, RK, r, 0, r, d->ln_eps, L.dBG, 2ll * r, 0, 1, BG, 2ll * r, 1, L.dxe, r, st);
+  if (e == hipSuccess)
+    e = launch_ln_fwd_bwd(L.Y, L.split_h, R, r, 0, r, d->ln_eps, L.dBG, 2ll * r, r, K, BG + r, 2ll * r, K, L.Acat, C,
                           st);
-  if (e == hipSuccess)
-    e = launch_split_t_ex(w->W_f, false, 2ll * r, rz, rz, 2 * r, RowMap{}, nullptr, L.WfT2, 2ll * rz, 0, rz, st);
-  if (e == hipSuccess) e = bf16_product(RK, 2 * r, 2 * rz, L.A1z, 2ll * rz, L.WfT2, 2ll * rz, 1, L.dBG, st);
-  // LayerNorm forward (b, g) and backward (dx_e; dx_h into Acat), ds placed by slot
-  if (e == hipSuccess)
-    e = launch_ln_fwd_bwd(L.U, L.split_e, RK, r, 0, r, d->ln_eps, L.dBG, 2ll * r, 0, 1, L.bq, L.dxe, r, st);
-  if (e == hipSuccess)
-    e = launch_ln_fwd_bwd(L.Y, L.split_h, R, r, 0, r, d->ln_eps, L.dBG, 2ll * r, r, K, L.gq, L.Acat, C, st);
   if (e == hipSuccess) e = launch_pack_ds(ds, N, B, rs, r, C, L.Acat, st);
-  // transposed operands of the weight-gradient products (reduction over rows)
-  if (e == hipSuccess) e = launch_split_t_ex(L.bq, false, r, RK, RKp, r, RowMap{}, nullptr, L.BGT, RKpl, 0, 0, st);
+  // dW_f = dz^T [b | g]
   if (e == hipSuccess) {
-    RowMap rep;
-    rep.mode = 2;
-    rep.rep = K;
-    e = launch_split_t_ex(L.gq, false, r, RK, RKp, r, rep, nullptr, static_cast<char*>(L.BGT) + 2ll * r * RKpl,
-                          RKpl, 0, 0, st);
+    WgradArgs p;
+    p.M = rz; p.N = 2 * r; p.Kd = RK;
+    p.A = dz; p.lda = rz;
+    p.b0 = BG; p.ldb0 = 2ll * r;
+    const OutSeg o{g->dW_f, 2ll * r, rz};
+    e = wgrad_run(p, true, &o, 1, L.part, L.part_floats, st);
   }
-  if (e == hipSuccess)
-    e = launch_split_t_ex(L.dxe, true, r, RK, RKp, r, RowMap{}, nullptr, L.dxeT, RKpl, 0, static_cast<long long>(r) * RKpl,
-                          st);
+  // dP_e = dx_e^T E[c] (E rows gathered by candidate id)
   if (e == hipSuccess) {
-    RowMap gat;
-    gat.mode = 1;
-    gat.ids = ids;
-    gat.idmax = d->V - 1;
-    e = launch_split_t_ex(E, false, de, RK, RKp, de, gat, nullptr, L.EcT, RKpl, 0, 0, st);
+    WgradArgs p;
+    p.M = r; p.N = de; p.Kd = RK;
+    p.A = L.dxe; p.lda = r;
+    p.b0 = static_cast<const uint16_t*>(E); p.ldb0 = de;
+    p.bmap.mode = 1; p.bmap.ids = ids; p.bmap.idmax = d->V - 1;
+    const OutSeg o{g->dP_e, de, r};
+    e = wgrad_run(p, true, &o, 1, L.part, L.part_floats, st);
   }
-  if (e == hipSuccess)
-    e = launch_split_t_ex(L.Acat, true, C, R, Rp, C, RowMap{}, L.A1cat, L.AcatT, Rpl, 0, static_cast<long long>(C) * Rpl,
-                          st);
-  if (e == hipSuccess) e = launch_split_t_ex(h, false, dh, R, Rp, dh, RowMap{}, nullptr, L.hT, Rpl, 0, 0, st);
-  // dW_f = dz^T [b | g repeated]: hi and lo parts stacked along M, then added
-  if (e == hipSuccess) e = bf16_product(2 * rz, 2 * r, RKp, L.dzT, RKpl, L.BGT, RKpl, L.s_f, L.part, st);
-  if (e == hipSuccess)
-    e = launch_sum_splits_ex(L.part, 2 * L.s_f, static_cast<long long>(rz) * 2 * r, rz, 2 * r, 2ll * r, g->dW_f, 2ll * r,
-                             st);
-  // dP_e = dx_e^T E[c]
-  if (e == hipSuccess) e = bf16_product(2 * r, de, RKp, L.dxeT, RKpl, L.EcT, RKpl, L.s_e, L.part, st);
-  if (e == hipSuccess)
-    e = launch_sum_splits_ex(L.part, 2 * L.s_e, static_cast<long long>(r) * de, r, de, de, g->dP_e, de, st);
   // [dP_h; dW_L; dW_R] = Acat^T h
-  if (e == hipSuccess) e = bf16_product(2 * C, dh, Rp, L.AcatT, Rpl, L.hT, Rpl, L.s_h, L.part, st);
-  const long long slice = static_cast<long long>(C) * dh;
-  if (e == hipSuccess) e = launch_sum_splits_ex(L.part, 2 * L.s_h, slice, r, dh, dh, g->dP_h, dh, st);
-  if (e == hipSuccess)
-    e = launch_sum_splits_ex(L.part + static_cast<long long>(r) * dh, 2 * L.s_h, slice, rs, dh, dh, g->dW_pair, 2ll * dh,
-                             st);
-  if (e == hipSuccess)
-    e = launch_sum_splits_ex(L.part + static_cast<long long>(r + rs) * dh, 2 * L.s_h, slice, rs, dh, dh,
-                             g->dW_pair + dh, 2ll * dh, st);
+  if (e == hipSuccess) {
+    WgradArgs p;
+    p.M = C; p.N = dh; p.Kd = R;
+    p.A = L.Acat; p.lda = C;
+    p.b0 = static_cast<const uint16_t*>(h); p.ldb0 = dh;
+    const OutSeg o[3] = {{g->dP_h, dh, r}, {g->dW_pair, 2ll * dh, rs}, {g->dW_pair + dh, 2ll * dh, rs}};
+    e = wgrad_run(p, true, o, 3, L.part, L.part_floats, st);
+  }
   if (!dh_out || e != hipSuccess) return e;
-  // dh = Acat [P_h; W_L; W_R]: Acat as two bf16 parts against the weights twice
-  const long long ldc2 = 2ll * C;
-  e = launch_split_t_ex(w->P_h, false, dh, r, r, dh, RowMap{}, nullptr, L.WcatT2, ldc2, 0, C, st);
-  if (e == hipSuccess)
-    e = launch_split_t_ex(w->W_pair, false, 2ll * dh, rs, rs, dh, RowMap{}, nullptr, L.WcatT2, ldc2, r, C, st);
-  if (e == hipSuccess)
-    e = launch_split_t_ex(static_cast<const char*>(w->W_pair) + 2ll * dh, false, 2ll * dh, rs, rs, dh, RowMap{},
-                          nullptr, L.WcatT2, ldc2, r + rs, C, st);
-  if (e != hipSuccess) return e;
-  if (L.s_dh == 1) return bf16_product(R, dh, 2 * C, L.A1cat, ldc2, L.WcatT2, ldc2, 1, dh_out, st);
-  e = bf16_product(R, dh, 2 * C, L.A1cat, ldc2, L.WcatT2, ldc2, L.s_dh, L.part, st);
-  if (e == hipSuccess) e = launch_sum_splits(L.part, L.s_dh, R, dh, dh_out, dh, st);
-  return e;
+  // dh = Acat [P_h; W_L; W_R]
+  WgradArgs p;
+  p.M = R; p.N = dh; p.Kd = C;
+  p.A = L.Acat; p.lda = C;
+  p.b0 = static_cast<const uint16_t*>(w->P_h); p.ldb0 = dh; p.bend0 = r;
+  p.b1 = Wp; p.ldb1 = 2ll * dh; p.bend1 = r + rs;
+  p.b2 = Wp + dh; p.ldb2 = 2ll * dh;
+  const OutSeg o{dh_out, dh, R};
+  return wgrad_run(p, false, &o, 1, L.part, L.part_floats, st);
 }
 
 }  // namespace
@@ -702,35 +681,26 @@ int dcoco_score_backward(const dcoco_dims* d, const dcoco_weights* w, const void
   if (e == hipSuccess) e = launch_sum(dS, static_cast<long long>(P) * d->K * d->K, red2, g->db2, st);
   if (e == hipSuccess && d_cand_logits) e = launch_dlogit(dS, d->n_blocks, d->B, d->K, d_cand_logits, st);
   if (bwd_on_mfma(d)) {
-    // [dA | dB] = hi + lo (two bf16 parts); z and W1 are bf16 already
-    if (e == hipSuccess) e = launch_split_t(L.dAB, true, RK, 2 * H, L.A1, L.At, st);
-    if (e == hipSuccess) e = launch_split_t(z, false, RK, rz, nullptr, L.Zt, st);
-    if (e == hipSuccess) e = launch_w1t(w->W1, H, rz, ldw1, L.W1t, st);
-    // dz = [dA | dB]_hi [W1a; W1b] + [dA | dB]_lo [W1a; W1b], one product over 4H
+    const uint16_t* W1u = static_cast<const uint16_t*>(w->W1);
+    // dz = dA W1a + dB W1b: one product over 2H, W1's two column blocks
+    // stacked along k
     if (e == hipSuccess) {
-      GemmProblem q{};
-      q.M = RK; q.N = rz; q.Kd = 4 * H;
-      q.A = L.A1; q.lda = 4ll * H; q.a_dtype = kDtypeBf16;
-      q.w[0] = L.W1t; q.ldw[0] = 4ll * H; q.col0[0] = 0;
-      q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = rz;
-      q.w_dtype = kDtypeBf16;
-      q.split = 1; q.out_f32 = dz; q.ldo = rz; q.out = nullptr;
-      e = launch_gemm(q, st);
+      WgradArgs p;
+      p.M = RK; p.N = rz; p.Kd = 2 * H;
+      p.A = L.dAB; p.lda = 2ll * H;
+      p.b0 = W1u; p.ldb0 = ldw1; p.bend0 = H;
+      p.b1 = W1u + rz; p.ldb1 = ldw1;
+      const OutSeg o{dz, rz, RK};
+      e = wgrad_run(p, false, &o, 1, L.part, L.part_floats, st);
     }
-    // dW1a, dW1b: (dA or dB)^T z over 2 N*B*K (both parts), split over k
-    for (int part = 0; part < 2 && e == hipSuccess; ++part) {
-      GemmProblem q{};
-      q.M = H; q.N = rz; q.Kd = 2 * RK;
-      q.A = static_cast<const char*>(L.At) + 2ll * part * H * 2 * RK; q.lda = 2ll * RK; q.a_dtype = kDtypeBf16;
-      q.w[0] = L.Zt; q.ldw[0] = 2ll * RK; q.col0[0] = 0;
-      q.seg_end[0] = q.seg_end[1] = q.seg_end[2] = rz;
-      q.w_dtype = kDtypeBf16;
-      int split = 1;
-      while (split < kMaxGradSplit && ((H + 63) / 64) * ((rz + 63) / 64) * split < 256 && q.Kd / (2 * split) >= 256)
-        split *= 2;
-      q.split = split; q.out_f32 = L.part; q.ldo = rz; q.out = nullptr;
-      e = launch_gemm(q, st);
-      if (e == hipSuccess) e = launch_sum_splits(L.part, split, H, rz, g->dW1 + part * rz, ldw1, st);
+    // [dW1a; dW1b] = [dA | dB]^T z, reduced over the N*B*K candidate rows
+    if (e == hipSuccess) {
+      WgradArgs p;
+      p.M = 2 * H; p.N = rz; p.Kd = RK;
+      p.A = L.dAB; p.lda = 2ll * H;
+      p.b0 = static_cast<const uint16_t*>(z); p.ldb0 = rz;
+      const OutSeg o[2] = {{g->dW1, ldw1, H}, {g->dW1 + rz, ldw1, H}};
+      e = wgrad_run(p, true, o, 2, L.part, L.part_floats, st);
     }
   } else {
     // fp32 products: dW1a, dW1b, then dz = dA W1a + dB W1b

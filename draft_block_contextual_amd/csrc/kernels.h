@@ -151,48 +151,66 @@ int colsum_blocks(int rows);
 hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* tmp, float* out, hipStream_t st);
 // out[0] = sum of x[0..n); tmp holds n / 8192 + 1 partial sums
 hipError_t launch_sum(const float* x, long long n, float* tmp, float* out, hipStream_t st);
-// which source row an operand row m reads: m itself, a clamped id (gathered
-// rows) or m / rep (each source row repeated rep times)
+// which source row an operand row m reads: m itself or a clamped id
+// (gathered rows)
 struct RowMap {
-  int mode = 0;                // 0 identity, 1 ids, 2 repeat
+  int mode = 0;                // 0 identity, 1 ids
   const int32_t* ids = nullptr;
   int idmax = 0;
-  int rep = 1;
   __device__ __forceinline__ long long row(int m) const {
     if (mode == 1) {
       const int id = ids[m];
       return id < 0 ? 0 : (id > idmax ? idmax : id);
     }
-    if (mode == 2) return m / rep;
     return m;
   }
 };
-// two-part bf16 split of X [M, C] fp32 (or a bf16 copy): A1 [M, 2C] = [hi | lo]
-// (optional), At [C, 2M] = its transpose with the parts side by side
-hipError_t launch_split_t(const void* X, bool split, int M, int C, void* A1, void* At, hipStream_t st);
-// the same with a row stride, a row map and a placement in a wider At:
-// At[j][col0 + m] = hi and At[j][col0 + lo_off + m] = lo (row stride ldt) for
-// m < Mpad, rows m >= M being zeros; with lo_off == 0 a bf16 input is stored
-// once (no second copy)
-hipError_t launch_split_t_ex(const void* X, bool split, long long ldx, int M, int Mpad, int C, RowMap map, void* A1,
-                             void* At, long long ldt, long long col0, long long lo_off, hipStream_t st);
+// Gradient products on bf16 MFMA (wgrad.hip): C[m, n] = sum_k A(m, k) B(k, n),
+// A fp32 split into two bf16 parts on chip, B bf16 stored [k][n].
+//   row reduction: A(m, k) = A[k * lda + m], else A[m * lda + k]
+//   B row k: k < bend0: b0 + bmap.row(k) * ldb0; k < bend1: b1 + (k - bend0) * ldb1;
+//            else b2 + (k - bend1) * ldb2 (b1, b2 may be null when unused)
+//   C row m: m < cend0: c0 + m * ldc0; m < cend1: c1 + (m - cend0) * ldc1;
+//            else c2 + (m - cend1) * ldc2; split z of k adds z * c_split
+// Needs N % 8 == 0, lda % 4 == 0, ldb % 8 == 0, 16-byte aligned A and B, and
+// M % 4 == 0 (row reduction) or Kd % 8 == 0.
+struct WgradArgs {
+  int M = 0, N = 0, Kd = 0, ksplit = 0;
+  const float* A = nullptr;
+  long long lda = 0;
+  const uint16_t* b0 = nullptr;
+  const uint16_t* b1 = nullptr;
+  const uint16_t* b2 = nullptr;
+  long long ldb0 = 0, ldb1 = 0, ldb2 = 0;
+  int bend0 = 0x7fffffff, bend1 = 0x7fffffff;
+  RowMap bmap;
+  float* c0 = nullptr;
+  float* c1 = nullptr;
+  float* c2 = nullptr;
+  long long ldc0 = 0, ldc1 = 0, ldc2 = 0;
+  int cend0 = 0x7fffffff, cend1 = 0x7fffffff;
+  long long c_split = 0;
+};
+// splits of k for about 256 workgroups (a power of two up to 16, each >= 128 deep)
+int wgrad_pick_split(int M, int N, int Kd);
+// number of k splits the launch actually runs (partials written) for `splits`
+int wgrad_grid_splits(int Kd, int splits);
+hipError_t launch_wgrad(WgradArgs p, bool row_reduction, int splits, hipStream_t st);
 // out[r][c] (row stride ld_out) = sum over s of part[s * split_stride + r * ld_part + c]
 hipError_t launch_sum_splits_ex(const float* part, int splits, long long split_stride, int rows, int cols,
                                 long long ld_part, float* out, long long ld_out, hipStream_t st);
 // LayerNorm forward and backward of the rows of x = sum_s x[s][M][ldx]
-// (columns col0 .. col0 + r - 1): y = LN(x) stored as bf16 [M, r]; with the
-// upstream gradient dy(m) = sum over q < rep of dY[(m rep + q) * ld_dy + c]
-// (columns dy_col0 ..), dx = (dy - mean(dy) - y mean(dy y)) / sigma into dX
-// [M, ld_dx] fp32
+// (columns col0 .. col0 + r - 1): y = LN(x) stored as bf16 into rows
+// m y_rep .. m y_rep + y_rep - 1 of y_bf (row stride ld_y); with the upstream
+// gradient dy(m) = sum over q < rep of dY[(m rep + q) * ld_dy + c] (columns
+// dy_col0 ..), dx = (dy - mean(dy) - y mean(dy y)) / sigma into dX [M, ld_dx] fp32
 hipError_t launch_ln_fwd_bwd(const float* x, int split, int M, int ldx, int col0, int r, float eps, const float* dY,
-                             long long ld_dy, int dy_col0, int rep, void* y_bf, float* dX, long long ld_dx,
-                             hipStream_t st);
+                             long long ld_dy, int dy_col0, int rep, void* y_bf, long long ld_y, int y_rep, float* dX,
+                             long long ld_dx, hipStream_t st);
 // Acat [N B, C] fp32 columns r .. r + 2 rs: the pair-state gradients ds [N, B-1, rs]
 // placed at their left slot (columns r ..) and right slot (columns r + rs ..),
 // zeros where a slot has no such pair
 hipError_t launch_pack_ds(const float* ds, int N, int B, int rs, int r, int C, float* Acat, hipStream_t st);
-// W1t [rz, 4H] bf16 from W1 [H, ldw] bf16 (see train.hip)
-hipError_t launch_w1t(const void* W1, int H, int rz, long long ldw, void* W1t, hipStream_t st);
 hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st);
 hipError_t launch_fill(float* x, long long n, float v, hipStream_t st);
 

@@ -369,72 +369,18 @@ __global__ void __launch_bounds__(kThreads) sum_splits_kernel(const float* __res
   out[r * ld_out + c] = v;
 }
 
-// Two-part bf16 split of an fp32 matrix X [M, C] (row stride ldx, row m read
-// from source row map(m)): X = hi + lo + e with hi = bf16(X), lo =
-// bf16(X - hi), |e| <= 2^-17 |X|.  Writes A1 [M, 2C] = [hi | lo] (row-major,
-// when A1 is not null) and the transpose into At: At[j][col0 + m] = hi,
-// At[j][col0 + lo_off + m] = lo (row stride ldt) for m < Mpad, the rows
-// m >= M being zeros (padding of a reduction dimension).  A bf16 input
-// (SPLIT false) is copied unchanged: into both places, or once when lo_off is
-// 0.  64 x 64 tiles through LDS so both stores are coalesced.
-template <typename TI, bool SPLIT>
-__global__ void __launch_bounds__(kThreads) split_t_kernel(const TI* __restrict__ X, long long ldx, int M, int Mpad,
-                                                           int C, RowMap map, uint16_t* __restrict__ A1,
-                                                           uint16_t* __restrict__ At, long long ldt, long long col0,
-                                                           long long lo_off) {
-  __shared__ uint16_t sH[64][66];
-  __shared__ uint16_t sL[64][66];
-  const int m0 = blockIdx.y * 64;
-  const int j0 = blockIdx.x * 64;
-  const int tid = threadIdx.x;
-  const int lj = tid & 63;
-  const int j = min(j0 + lj, C - 1);
-#pragma unroll 4
-  for (int r = 0; r < 16; ++r) {
-    const int lm = r * 4 + (tid >> 6);
-    const int m = min(m0 + lm, M - 1);
-    const long long src = map.row(m);
-    uint16_t hi, lo;
-    if constexpr (SPLIT) {
-      const float x = X[src * ldx + j];
-      hi = f32_to_bf16(x);
-      lo = f32_to_bf16(x - bf16_to_f32(hi));
-    } else {
-      hi = lo = X[src * ldx + j].bits;
-    }
-    if (m0 + lm >= M) hi = lo = 0;
-    sH[lm][lj] = hi;
-    sL[lm][lj] = lo;
-    if (A1 && m0 + lm < M && j0 + lj < C) {
-      A1[static_cast<long long>(m) * 2 * C + j] = hi;
-      A1[static_cast<long long>(m) * 2 * C + C + j] = lo;
-    }
-  }
-  __syncthreads();
-  const int lm = tid & 63;
-  if (m0 + lm >= Mpad) return;
-  const bool second = SPLIT || lo_off != 0;
-#pragma unroll 4
-  for (int r = 0; r < 16; ++r) {
-    const int jj = r * 4 + (tid >> 6);
-    if (j0 + jj >= C) break;
-    const long long row = static_cast<long long>(j0 + jj) * ldt + col0;
-    At[row + m0 + lm] = sH[lm][jj];
-    if (second) At[row + lo_off + m0 + lm] = sL[lm][jj];
-  }
-}
-
 // LayerNorm forward and backward per row, one wave per row (4 rows per
 // workgroup), VPL values per lane (column l + 64 i).  Forward as in the
 // representation stage: the split partials added in order, two-pass mean and
 // variance in fp32, y = (x - mean) / sqrt(var + eps).  Backward:
 // dx = (dy - mean(dy) - y mean(dy y)) / sqrt(var + eps), dy being the sum
-// (in order) of rep upstream rows.
+// (in order) of rep upstream rows.  The bf16 y of row m is stored into rows
+// m y_rep .. m y_rep + y_rep - 1 of y_bf (row stride ld_y).
 template <int VPL>
 __global__ void __launch_bounds__(kThreads)
 ln_fwd_bwd_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0, int r, float eps,
                   const float* __restrict__ dY, long long ld_dy, int dy_col0, int rep, uint16_t* __restrict__ y_bf,
-                  float* __restrict__ dX, long long ld_dx) {
+                  long long ld_y, int y_rep, float* __restrict__ dX, long long ld_dx) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (row >= M) return;
@@ -474,7 +420,8 @@ ln_fwd_bwd_kernel(const float* __restrict__ x, int split, int M, int ldx, int co
   for (int i = 0; i < VPL; ++i) {
     const int c = l + i * 64;
     if (c < r) {
-      y_bf[static_cast<long long>(row) * r + c] = f32_to_bf16(v[i]);
+      const uint16_t yb = f32_to_bf16(v[i]);
+      for (int q = 0; q < y_rep; ++q) y_bf[(static_cast<long long>(row) * y_rep + q) * ld_y + c] = yb;
       dX[static_cast<long long>(row) * ld_dx + c] = (g[i] - mg - v[i] * mgy) * inv;
     }
   }
@@ -497,18 +444,6 @@ __global__ void __launch_bounds__(kThreads) pack_ds_kernel(const float* __restri
   Acat[i * C + r + c2] = v;
 }
 
-// W1t [rz, 4H] bf16: W1t[c][q 2H + j] = W1[j][c] (j < H) or W1[j - H][rz + c],
-// for q = 0, 1 (the two halves meet the hi and lo parts of [dA | dB])
-__global__ void __launch_bounds__(kThreads) w1t_kernel(const uint16_t* __restrict__ W1, int H, int rz,
-                                                       long long ldw, uint16_t* __restrict__ W1t) {
-  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
-  if (idx >= static_cast<long long>(rz) * 4 * H) return;
-  const int c = static_cast<int>(idx / (4 * H));
-  const int k = static_cast<int>(idx % (4 * H));
-  const int j = k % (2 * H);
-  W1t[idx] = j < H ? W1[static_cast<long long>(j) * ldw + c] : W1[static_cast<long long>(j - H) * ldw + rz + c];
-}
-
 inline unsigned blocks_for(long long n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
 
 }  // namespace
@@ -524,33 +459,16 @@ hipError_t launch_loss(const float* S, const int32_t* cand_ids, const int32_t* t
   return hipGetLastError();
 }
 
-hipError_t launch_split_t(const void* X, bool split, int M, int C, void* A1, void* At, hipStream_t st) {
-  return launch_split_t_ex(X, split, C, M, M, C, RowMap{}, A1, At, 2ll * M, 0, M, st);
-}
-
-hipError_t launch_split_t_ex(const void* X, bool split, long long ldx, int M, int Mpad, int C, RowMap map, void* A1,
-                             void* At, long long ldt, long long col0, long long lo_off, hipStream_t st) {
-  if (M <= 0 || C <= 0 || Mpad < M) return M <= 0 ? hipSuccess : hipErrorInvalidValue;
-  const dim3 grid((C + 63) / 64, (Mpad + 63) / 64);
-  if (split)
-    hipLaunchKernelGGL((split_t_kernel<float, true>), grid, dim3(kThreads), 0, st, static_cast<const float*>(X), ldx,
-                       M, Mpad, C, map, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At), ldt, col0, lo_off);
-  else
-    hipLaunchKernelGGL((split_t_kernel<bf16, false>), grid, dim3(kThreads), 0, st, static_cast<const bf16*>(X), ldx,
-                       M, Mpad, C, map, static_cast<uint16_t*>(A1), static_cast<uint16_t*>(At), ldt, col0, lo_off);
-  return hipGetLastError();
-}
-
 hipError_t launch_ln_fwd_bwd(const float* x, int split, int M, int ldx, int col0, int r, float eps, const float* dY,
-                             long long ld_dy, int dy_col0, int rep, void* y_bf, float* dX, long long ld_dx,
-                             hipStream_t st) {
+                             long long ld_dy, int dy_col0, int rep, void* y_bf, long long ld_y, int y_rep, float* dX,
+                             long long ld_dx, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const int vpl = (r + 63) / 64;
   const dim3 grid((M + 3) / 4);
   uint16_t* yb = static_cast<uint16_t*>(y_bf);
 #define DCOCO_LNB(V)                                                                                              \
   hipLaunchKernelGGL((ln_fwd_bwd_kernel<V>), grid, dim3(kThreads), 0, st, x, split, M, ldx, col0, r, eps, dY, ld_dy, \
-                     dy_col0, rep, yb, dX, ld_dx)
+                     dy_col0, rep, yb, ld_y, y_rep, dX, ld_dx)
   if (vpl <= 4) DCOCO_LNB(4);
   else if (vpl <= 8) DCOCO_LNB(8);
   else if (vpl <= 16) DCOCO_LNB(16);
@@ -564,12 +482,6 @@ hipError_t launch_pack_ds(const float* ds, int N, int B, int rs, int r, int C, f
   const long long n = static_cast<long long>(N) * B * 2 * rs;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(pack_ds_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, st, ds, N, B, rs, r, C, Acat);
-  return hipGetLastError();
-}
-
-hipError_t launch_w1t(const void* W1, int H, int rz, long long ldw, void* W1t, hipStream_t st) {
-  hipLaunchKernelGGL(w1t_kernel, dim3(blocks_for(static_cast<long long>(rz) * 4 * H)), dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(W1), H, rz, ldw, static_cast<uint16_t*>(W1t));
   return hipGetLastError();
 }
 

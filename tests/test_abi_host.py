@@ -210,9 +210,9 @@ def test_represent_backward_argument_checks(lib):
 
     d = _dims(n_blocks=2)
     assert call(d) == 0
-    # the gathered rows transposed, the dz split and the forward partials
+    # per candidate row: dz W_f (2 r fp32), dx_e (r fp32), [b | g] (2 r bf16)
     RK = 2 * 16 * 16
-    assert n.value >= RK * 4096 * 2 + RK * 256 * 2 * 2
+    assert n.value >= RK * 256 * (8 + 4 + 4)
     assert call(_dims(n_blocks=2, dtype="f32")) == -2          # bf16 storage only
     assert call(_dims(n_blocks=2, d_proj=48)) == -2
     # weights, gradient buffers and inputs are checked before any launch
