@@ -378,13 +378,13 @@ hipError_t wgrad_run(WgradArgs p, bool rr, const OutSeg* segs, int nseg, float* 
   }
   p.c0 = part; p.ldc0 = p.N; p.c_split = static_cast<long long>(p.M) * p.N;
   hipError_t e = launch_wgrad(p, rr, split, st);
-  const int gz = wgrad_grid_splits(p.Kd, split);
-  long long row = 0;
-  for (int i = 0; i < nseg && e == hipSuccess; ++i) {
-    e = launch_sum_splits_ex(part + row * p.N, gz, p.c_split, segs[i].rows, p.N, p.N, segs[i].c, segs[i].ld, st);
-    row += segs[i].rows;
-  }
-  return e;
+  if (e != hipSuccess) return e;
+  SegOut o{};
+  o.out0 = segs[0].c; o.ld0 = segs[0].ld; o.end0 = segs[0].rows;
+  o.out1 = nseg > 1 ? segs[1].c : segs[0].c; o.ld1 = nseg > 1 ? segs[1].ld : segs[0].ld;
+  o.end1 = nseg > 1 ? segs[0].rows + segs[1].rows : p.M;
+  o.out2 = nseg > 2 ? segs[2].c : o.out1; o.ld2 = nseg > 2 ? segs[2].ld : o.ld1;
+  return launch_sum_splits_seg(part, wgrad_grid_splits(p.Kd, split), p.c_split, p.M, p.N, o, st);
 }
 
 // ---- representation backward (bf16 storage)

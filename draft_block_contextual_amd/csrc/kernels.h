@@ -196,6 +196,15 @@ int wgrad_pick_split(int M, int N, int Kd);
 // number of k splits the launch actually runs (partials written) for `splits`
 int wgrad_grid_splits(int Kd, int splits);
 hipError_t launch_wgrad(WgradArgs p, bool row_reduction, int splits, hipStream_t st);
+// row r of part [rows, cols] summed over its splits (split_stride apart) into
+// out0 (r < end0), out1 (r < end1) or out2, each with its own row stride
+struct SegOut {
+  float* out0; long long ld0; int end0;
+  float* out1; long long ld1; int end1;
+  float* out2; long long ld2;
+};
+hipError_t launch_sum_splits_seg(const float* part, int splits, long long split_stride, int rows, int cols,
+                                 const SegOut& o, hipStream_t st);
 // out[r][c] (row stride ld_out) = sum over s of part[s * split_stride + r * ld_part + c]
 hipError_t launch_sum_splits_ex(const float* part, int splits, long long split_stride, int rows, int cols,
                                 long long ld_part, float* out, long long ld_out, hipStream_t st);

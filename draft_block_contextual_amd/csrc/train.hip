@@ -386,18 +386,30 @@ ln_fwd_bwd_kernel(const float* __restrict__ x, int split, int M, int ldx, int co
   if (row >= M) return;
   const float inv_r = 1.0f / static_cast<float>(r);
   float v[VPL], g[VPL];
+  int cc[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    cc[i] = min(l + i * 64, r - 1);       // lanes past r re-read a valid column
+    v[i] = 0.f;
+    g[i] = 0.f;
+  }
+  // loads unconditional and several rows deep, sums in a fixed order
+  for (int s = 0; s < split; ++s) {
+    const float* xs = x + (static_cast<long long>(s) * M + row) * ldx + col0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] += xs[cc[i]];
+  }
+#pragma unroll 4
+  for (int q = 0; q < rep; ++q) {
+    const float* dq = dY + (static_cast<long long>(row) * rep + q) * ld_dy + dy_col0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) g[i] += dq[cc[i]];
+  }
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const int c = l + i * 64;
-    float a = 0.f, b = 0.f;
-    if (c < r) {
-      for (int s = 0; s < split; ++s) a += x[(static_cast<long long>(s) * M + row) * ldx + col0 + c];
-      for (int q = 0; q < rep; ++q) b += dY[(static_cast<long long>(row) * rep + q) * ld_dy + dy_col0 + c];
-    }
-    v[i] = a;
-    g[i] = b;
-    sum += a;
+    if (l + i * 64 >= r) v[i] = g[i] = 0.f;
+    sum += v[i];
   }
   const float mean = wave_sum(sum) * inv_r;
   float sq = 0.f;
@@ -419,6 +431,93 @@ ln_fwd_bwd_kernel(const float* __restrict__ x, int split, int M, int ldx, int co
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int c = l + i * 64;
+    if (c < r) {
+      const uint16_t yb = f32_to_bf16(v[i]);
+      for (int q = 0; q < y_rep; ++q) y_bf[(static_cast<long long>(row) * y_rep + q) * ld_y + c] = yb;
+      dX[static_cast<long long>(row) * ld_dx + c] = (g[i] - mg - v[i] * mgy) * inv;
+    }
+  }
+}
+
+// The same per row with one workgroup per row (thread t takes columns t,
+// t + 256, ...): for few rows with many upstream rows each, where one wave
+// per row leaves most of the chip idle.  Sums over the workgroup: each wave's
+// DPP sum, then the four added in wave order.
+template <int VPT>
+__global__ void __launch_bounds__(kThreads)
+ln_fwd_bwd_wg_kernel(const float* __restrict__ x, int split, int M, int ldx, int col0, int r, float eps,
+                     const float* __restrict__ dY, long long ld_dy, int dy_col0, int rep,
+                     uint16_t* __restrict__ y_bf, long long ld_y, int y_rep, float* __restrict__ dX,
+                     long long ld_dx) {
+  __shared__ float red[4][4];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6;
+  const float inv_r = 1.0f / static_cast<float>(r);
+  float v[VPT], g[VPT];
+  int cc[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    cc[i] = min(tid + i * kThreads, r - 1);
+    v[i] = 0.f;
+    g[i] = 0.f;
+  }
+  for (int s = 0; s < split; ++s) {
+    const float* xs = x + (static_cast<long long>(s) * M + row) * ldx + col0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) v[i] += xs[cc[i]];
+  }
+#pragma unroll 8
+  for (int q = 0; q < rep; ++q) {
+    const float* dq = dY + (static_cast<long long>(row) * rep + q) * ld_dy + dy_col0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) g[i] += dq[cc[i]];
+  }
+  // workgroup sum of up to two values, fixed order
+  auto wg_sum2 = [&](float a, float b, int slot, float& ra, float& rb) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if ((tid & 63) == 0) {
+      red[slot][wv] = a;
+      red[slot + 1][wv] = b;
+    }
+    __syncthreads();
+    ra = (red[slot][0] + red[slot][1]) + (red[slot][2] + red[slot][3]);
+    rb = (red[slot + 1][0] + red[slot + 1][1]) + (red[slot + 1][2] + red[slot + 1][3]);
+  };
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    if (tid + i * kThreads >= r) v[i] = g[i] = 0.f;
+    sum += v[i];
+  }
+  float tot, unused;
+  wg_sum2(sum, 0.f, 0, tot, unused);
+  const float mean = tot * inv_r;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    v[i] = (tid + i * kThreads) < r ? v[i] - mean : 0.f;
+    sq += v[i] * v[i];
+  }
+  float sqt;
+  wg_sum2(sq, 0.f, 2, sqt, unused);
+  const float inv = 1.0f / sqrtf(sqt * inv_r + eps);
+  float sg = 0.f, sgy = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    v[i] *= inv;
+    sg += g[i];
+    sgy += g[i] * v[i];
+  }
+  __syncthreads();                         // red[0..1] is reused
+  float tg, tgy;
+  wg_sum2(sg, sgy, 0, tg, tgy);
+  const float mg = tg * inv_r;
+  const float mgy = tgy * inv_r;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = tid + i * kThreads;
     if (c < r) {
       const uint16_t yb = f32_to_bf16(v[i]);
       for (int q = 0; q < y_rep; ++q) y_bf[(static_cast<long long>(row) * y_rep + q) * ld_y + c] = yb;
@@ -463,9 +562,22 @@ hipError_t launch_ln_fwd_bwd(const float* x, int split, int M, int ldx, int col0
                              long long ld_dy, int dy_col0, int rep, void* y_bf, long long ld_y, int y_rep, float* dX,
                              long long ld_dx, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  uint16_t* yb = static_cast<uint16_t*>(y_bf);
+  if (M < 4096 && r <= 2048) {
+    // few rows: a workgroup per row
+    const int vpt = (r + kThreads - 1) / kThreads;
+#define DCOCO_LNW(V)                                                                                              \
+  hipLaunchKernelGGL((ln_fwd_bwd_wg_kernel<V>), dim3(M), dim3(kThreads), 0, st, x, split, M, ldx, col0, r, eps, dY, \
+                     ld_dy, dy_col0, rep, yb, ld_y, y_rep, dX, ld_dx)
+    if (vpt <= 1) DCOCO_LNW(1);
+    else if (vpt <= 2) DCOCO_LNW(2);
+    else if (vpt <= 4) DCOCO_LNW(4);
+    else DCOCO_LNW(8);
+#undef DCOCO_LNW
+    return hipGetLastError();
+  }
   const int vpl = (r + 63) / 64;
   const dim3 grid((M + 3) / 4);
-  uint16_t* yb = static_cast<uint16_t*>(y_bf);
 #define DCOCO_LNB(V)                                                                                              \
   hipLaunchKernelGGL((ln_fwd_bwd_kernel<V>), grid, dim3(kThreads), 0, st, x, split, M, ldx, col0, r, eps, dY, ld_dy, \
                      dy_col0, rep, yb, ld_y, y_rep, dX, ld_dx)
@@ -524,6 +636,34 @@ hipError_t launch_gemm_f32(const GemmF32Args& g, int a_dtype, int b_dtype, hipSt
 hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, float* out, long long ld_out,
                              hipStream_t st) {
   return launch_sum_splits_ex(part, splits, static_cast<long long>(rows) * cols, rows, cols, cols, out, ld_out, st);
+}
+
+// rows of part [M, cols] (splits split_stride apart) into up to three
+// destinations: rows [0, end0) to out0, [end0, end1) to out1, the rest to out2
+__global__ void __launch_bounds__(kThreads) sum_splits_seg_kernel(const float* __restrict__ part, int splits,
+                                                                  long long split_stride, int rows, int cols,
+                                                                  SegOut o) {
+  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx >= static_cast<long long>(rows) * cols) return;
+  const int r = static_cast<int>(idx / cols);
+  const int c = static_cast<int>(idx % cols);
+  const float* src = part + idx;
+  float v = 0.f;
+  for (int s = 0; s < splits; ++s) v += src[s * split_stride];
+  float* dst;
+  if (r < o.end0) dst = o.out0 + static_cast<long long>(r) * o.ld0;
+  else if (r < o.end1) dst = o.out1 + static_cast<long long>(r - o.end0) * o.ld1;
+  else dst = o.out2 + static_cast<long long>(r - o.end1) * o.ld2;
+  dst[c] = v;
+}
+
+hipError_t launch_sum_splits_seg(const float* part, int splits, long long split_stride, int rows, int cols,
+                                 const SegOut& o, hipStream_t st) {
+  const long long n = static_cast<long long>(rows) * cols;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_splits_seg_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, st, part, splits, split_stride,
+                     rows, cols, o);
+  return hipGetLastError();
 }
 
 hipError_t launch_sum_splits_ex(const float* part, int splits, long long split_stride, int rows, int cols,
