@@ -207,10 +207,13 @@ __global__ void __launch_bounds__(kThreads) grid_bwd_kernel(GridBwdArgs g) {
 #pragma unroll
     for (int a = 0; a < KR; ++a) av[a] = Arow[static_cast<long long>(min(a, K - 1)) * ld];
   }
-  bool small = true;
+  // the pair term joins the B side: u = A(a) + (B(b) + c).  sigma(u) =
+  // 1 / (1 + e^-A e^-(B+c)) is exact in the factored form whenever e^-A is a
+  // normal number (|A| <= 80): a B-side factor of 0 or inf then still gives
+  // sigma = 1 or 0
 #pragma unroll
   for (int b = 0; b < KR; ++b) {
-    small = small && fabsf(bv[b]) <= 40.f;
+    bv[b] += c;
     eb[b] = expf(-bv[b]);
     db[b] = 0.f;
   }
@@ -226,10 +229,10 @@ __global__ void __launch_bounds__(kThreads) grid_bwd_kernel(GridBwdArgs g) {
     } else {
       ar = Arow[static_cast<long long>(a) * ld];
     }
-    const float ap = ar + c;
+    const float ap = ar;
     const float* ga = sG + a * K;
     float da = 0.f;
-    if (small && fabsf(ap) <= 40.f) {
+    if (fabsf(ap) <= 80.f) {
       const float ea = expf(-ap);
 #pragma unroll
       for (int b = 0; b < KR; ++b) {
@@ -248,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) grid_bwd_kernel(GridBwdArgs g) {
       for (int b = 0; b < KR; ++b) {
         if (b < K) {
           const float u = ap + bv[b];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-u));
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * u));
           const float gab = ga[b];
           const float du = gab * w2h * (sg * fmaf(u, 1.0f - sg, 1.0f));
           dw2 = fmaf(gab, u * sg, dw2);

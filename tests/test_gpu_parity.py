@@ -662,6 +662,32 @@ def test_score_backward_matches_oracle(name):
     assert abs(float(_np(out["db2"])[0]) - R["db2"]) <= 1e-5 * max(1.0, np.abs(G).sum())
 
 
+def test_score_backward_large_preactivations():
+    # W1 scaled by 2^6 (exact in bf16): many pre-activations leave the range
+    # where the kernel factors e^-u per side, so both of its paths run
+    import draft_block_contextual_amd as dc
+    import torch
+    name = "small_bf16"
+    print(f"case score_backward {name} W1*64", flush=True)
+    inp = _inputs(name)
+    ref = _oracle(name)
+    dims, w, _, _, _ = device_inputs(inp)
+    wt = {k: O.to_f64(inp[k], "bf16") for k in ("W1", "b1", "w2")}
+    W1 = wt["W1"] * 64.0
+    w.W1 = _bf16_dev(W1)
+    z = ref["z"]
+    s32 = ref["s"].astype(np.float32)
+    A = np.abs(z @ W1[:, :z.shape[-1]].T)
+    assert (A > 80).mean() > 0.05 and (A <= 80).mean() > 0.05      # both paths taken
+    G = np.random.default_rng(64).standard_normal(ref["S"].shape) / inp["dims"].n_blocks
+    out = dc.score_backward(dims, w, _bf16_dev(z), _dev_f32(s32), _dev_f32(G.astype(np.float32)))
+    torch.cuda.synchronize()
+    R = O.score_backward(z, s32.astype(np.float64), W1, wt["b1"], wt["w2"], G.astype(np.float32).astype(np.float64))
+    for key in ("dz", "ds", "dW1", "db1", "dw2", "d_cand_vals"):
+        got = _np(out["d_cand_logits" if key == "d_cand_vals" else key])
+        _grad_check(got, R[key], f"big:{key}")
+
+
 def test_training_step_end_to_end():
     # loss then backward on one config, as a training step would chain them
     import draft_block_contextual_amd as dc
