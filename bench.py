@@ -323,11 +323,11 @@ def main():
     # Dominant kernel: top-K, one launch per dcoco_topk call, so the events
     # around that call time exactly that kernel.  It is bound by reading the
     # logits once from HBM.
-    kname = "topk_bf16_row_kernel" if dt == "bf16" else "topk_partial_kernel+topk_merge_kernel"
+    kname = "topk_bf16_row_reg_kernel" if dt == "bf16" else "topk_partial_kernel+topk_merge_kernel"
     topk_us = stage_us["topk"]
     ach = work["logit_bytes"] / (topk_us * 1e-6) / 1e9
     digest = source_digest([f"draft_block_contextual_amd/csrc/{f}"
-                            for f in ("topk.hip", "common.h", "select.h", "dma.h", "wave.h")])
+                            for f in ("topk.hip", "common.h", "select.h", "wave.h")])
     traffic = stored_traffic(f"topk_{cfg.name}", digest)
     roof = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),

@@ -28,7 +28,6 @@
 #include <type_traits>
 
 #include "common.h"
-#include "dma.h"
 #include "kernels.h"
 #include "select.h"
 #include "wave.h"
@@ -489,29 +488,66 @@ __device__ __forceinline__ void row_finish(const uint16_t* rowp, int V, int K, i
   }
 }
 
+// Barrier for LDS traffic only: waits for this wave's LDS accesses, not for
+// its vector-memory loads still in flight (a __syncthreads would drain those
+// as well, and the register ring below keeps several segments in flight
+// across the barriers of the bound computation).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+template <int NV>
+__device__ __forceinline__ void row_load_regs(const uint16_t* rowp, int V, int seg0, int l, uint32_t (&kw)[NV * 4]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e0 = seg0 + (i * kWave + l) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(rowp + min(e0, V - 8));   // clamped inside the row
+    kw[4 * i] = v.x;
+    kw[4 * i + 1] = v.y;
+    kw[4 * i + 2] = v.z;
+    kw[4 * i + 3] = v.w;
+  }
+}
+
+// vectors past the row end become the padding pattern 0xffff
+template <int NV>
+__device__ __forceinline__ void row_pad(int seg0, int V, int l, uint32_t (&kw)[NV * 4]) {
+  if (seg0 + kWave * NV * 8 > V) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const bool in = seg0 + (i * kWave + l) * 8 < V;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kw[4 * i + q] = in ? kw[4 * i + q] : 0xffffffffu;
+    }
+  }
+}
+
+// vectors per lane and segment, and register sets in the ring
+#ifndef DCOCO_TOPK_NV
+#define DCOCO_TOPK_NV 3
+#endif
+#ifndef DCOCO_TOPK_D
+#define DCOCO_TOPK_D 4
+#endif
+constexpr int kRegNV = DCOCO_TOPK_NV;
+constexpr int kRegD = DCOCO_TOPK_D;
+
 // Rows whose length is a multiple of 8 and that start 16-byte aligned.  Each
-// wave streams its segments through a private ring of S LDS slots filled by
-// direct global->LDS loads: S - 1 segments are in flight while the wave
-// screens the current one, and the waits are a fixed vmcnt.  Loads are
-// unconditional; a vector past the row end reads a clamped address inside the
-// row and is replaced when the segment is read.  Padding is the pattern
-// 0xffff (a NaN whose packed key is 1, below every real key but the NaNs
-// that also sit below -inf): groups of padding never lift the bound, and
-// padding is never appended (its ids are >= V).
-template <int NV, int G, int S>
+// wave streams its segments through a ring of D register sets: D segments per
+// wave in flight, plain 16-byte vector loads (the compiler's waits follow the
+// issue order), LDS kept for the lists.  Loads are unconditional; a vector
+// past the row end reads a clamped address inside the row and is replaced by
+// padding, the pattern 0xffff (a NaN whose packed key is 1, below every real
+// key but the NaNs that also sit below -inf): groups of padding never lift
+// the bound, and padding is never appended (its ids are >= V).
+template <int NV, int G, int D>
 __global__ void __launch_bounds__(kRowWaves * kWave)
-topk_bf16_row_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
-                     float* __restrict__ vals) {
+topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
+                         float* __restrict__ vals) {
   constexpr int kSegLen = kWave * NV * 8;
-  constexpr int kSlot = NV * 1024;           // LDS bytes per segment
-  static_assert(S >= 2 && (S - 1) * NV < 64, "ring depth");
   const int row = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int l = lane_id();
   const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
 
-  __shared__ __align__(1024) char s_ring[kRowWaves * S * kSlot];
-  // the group maxima of the first segments live in the (still empty) lists
   static_assert(kRowWaves * G * kWave * 4 <= kRowWaves * kRowCap * 8, "group maxima fit the lists");
   __shared__ uint64_t s_cand[kRowWaves][kRowCap];
   __shared__ int32_t s_flag[kRowWaves][kFlagCap];
@@ -520,74 +556,45 @@ topk_bf16_row_kernel(const uint16_t* __restrict__ logits, int V, int K, int roun
   __shared__ int s_cnt[kRowWaves];
   uint32_t* s_gm = reinterpret_cast<uint32_t*>(&s_cand[0][0]);
 
-  char* ring = s_ring + w * S * kSlot;
-  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_offset(ring));
-  const uint16_t* lane_p = rowp + l * 8;
-  auto issue = [&](int rd) {
-    const int seg0 = (rd * kRowWaves + w) * kSegLen;
-    const uint32_t slot = ring_lds + static_cast<uint32_t>(rd % S) * kSlot;
-    if (seg0 + kSegLen <= V) {
+  uint32_t ring[D][NV * 4];
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
-        dma16(lane_p + seg0 + i * (kWave * 8), __builtin_amdgcn_readfirstlane(slot + i * 1024));
-    } else {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int e0 = seg0 + (i * kWave + l) * 8;
-        dma16(rowp + min(e0, V - 8), __builtin_amdgcn_readfirstlane(slot + i * 1024));
-      }
-    }
-  };
-  auto read = [&](int rd, uint32_t (&kw)[NV * 4]) {
-    const int seg0 = (rd * kRowWaves + w) * kSegLen;
-    const char* slot = ring + (rd % S) * kSlot;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(slot + i * 1024 + l * 16);
-      kw[4 * i] = v.x;
-      kw[4 * i + 1] = v.y;
-      kw[4 * i + 2] = v.z;
-      kw[4 * i + 3] = v.w;
-    }
-    if (seg0 + kSegLen > V) {
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const bool in = seg0 + (i * kWave + l) * 8 < V;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kw[4 * i + q] = in ? kw[4 * i + q] : 0xffffffffu;
-      }
-    }
-  };
-#pragma unroll
-  for (int r = 0; r < S - 1; ++r) issue(r);
+  for (int r = 0; r < D; ++r) row_load_regs<NV>(rowp, V, (r * kRowWaves + w) * kSegLen, l, ring[r]);
 
-  // row-wide bound from the first segments (all -inf for a wave past the end)
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"((S - 2) * NV) : "memory");
+  // row-wide bound from the first segments (all padding for a wave past the end)
   {
     uint32_t kw[NV * 4];
-    read(0, kw);
+#pragma unroll
+    for (int j = 0; j < NV * 4; ++j) kw[j] = ring[0][j];
+    row_pad<NV>(w * kSegLen, V, l, kw);
     uint32_t gmx[G];
     group_max<NV, G>(kw, gmx);
 #pragma unroll
     for (int g = 0; g < G; ++g) s_gm[(w * G + g) * kWave + l] = gmx[g];
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t t = row_bound<G>(s_gm, K, l);
-  __syncthreads();                          // the lists overwrite the maxima from here on
+  lds_barrier();                            // the lists overwrite the maxima from here on
 
   int nseg = 0;
   int nflag = 0;
-  for (int rd = 0; rd < rounds; ++rd) {
-    issue(rd + S - 1);
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"((S - 1) * NV) : "memory");
-    const int seg0 = (rd * kRowWaves + w) * kSegLen;
-    if (seg0 >= V) continue;
-    ++nseg;
-    uint32_t kw[NV * 4];
-    read(rd, kw);
-    row_screen<NV>(kw, seg0, V, l, t, nflag, s_flag[w]);
+  for (int rd0 = 0; rd0 < rounds; rd0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int rd = rd0 + j;
+      if (rd < rounds) {
+        const int seg0 = (rd * kRowWaves + w) * kSegLen;
+        uint32_t kw[NV * 4];
+#pragma unroll
+        for (int q = 0; q < NV * 4; ++q) kw[q] = ring[j][q];
+        if (rd + D < rounds) row_load_regs<NV>(rowp, V, ((rd + D) * kRowWaves + w) * kSegLen, l, ring[j]);
+        if (seg0 < V) {
+          ++nseg;
+          row_pad<NV>(seg0, V, l, kw);
+          row_screen<NV>(kw, seg0, V, l, t, nflag, s_flag[w]);
+        }
+      }
+    }
   }
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
   __builtin_amdgcn_wave_barrier();
   int cnt = 0;
   const bool exact = nflag > kFlagCap || !row_collect<true>(rowp, V, t, s_flag[w], nflag, l, s_cand[w], cnt);
@@ -711,14 +718,13 @@ hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* p
   if constexpr (std::is_same<T, bf16>::value) {
     const uint16_t* lb = reinterpret_cast<const uint16_t*>(logits);
     const int G = K <= 16 ? 1 : (K <= 32 ? 2 : 4);
-    // aligned rows: 3 vectors per lane and segment, a 2-slot ring per wave
-    // (48 KB of LDS: two workgroups fit a compute unit); other rows: 8
-    // vectors per lane, element loads
+    // aligned rows: kRegNV vectors per lane and segment, kRegD segments in
+    // flight per wave; other rows: 8 vectors per lane, element loads
     if (vec) {
-      const int rounds = (V + kRowWaves * kWave * 3 * 8 - 1) / (kRowWaves * kWave * 3 * 8);
+      const int rounds = (V + kRowWaves * kWave * kRegNV * 8 - 1) / (kRowWaves * kWave * kRegNV * 8);
 #define DCOCO_ROW(GG)                                                                                   \
-  hipLaunchKernelGGL((topk_bf16_row_kernel<3, GG, 2>), dim3(rows), dim3(kRowWaves * kWave), 0, st, lb, V, K, \
-                     rounds, ids, vals)
+  hipLaunchKernelGGL((topk_bf16_row_reg_kernel<kRegNV, GG, kRegD>), dim3(rows), dim3(kRowWaves * kWave), 0, st, lb, \
+                     V, K, rounds, ids, vals)
       if (G == 1) DCOCO_ROW(1);
       else if (G == 2) DCOCO_ROW(2);
       else DCOCO_ROW(4);
