@@ -146,6 +146,16 @@ CONFIGS = {
     "tall_bf16": Config("tall_bf16", _d(3, 15, 50, 6007, 256, 512, 256, 256, 64, 256, "bf16"),
                         30.0, "peaks", 50, 2008, "random",
                         "2250 candidate rows (ragged over 128-row tiles) with 256-wide projections"),
+    # degenerate and limit shapes: one slot (no transitions), one candidate,
+    # the widest projections the boundary accepts, the most rows it accepts
+    "b1_bf16": Config("b1_bf16", _d(3, 1, 8, 5003, 128, 128, 64, 64, 64, 64, "bf16"),
+                      30.0, "peaks", 8, 2009, "random", "B = 1: no pairs, the drafter's top-1 per slot"),
+    "k1_bf16": Config("k1_bf16", _d(3, 6, 1, 5003, 128, 128, 64, 64, 64, 64, "bf16"),
+                      30.0, "peaks", 1, 2010, "random", "K = 1: one candidate per slot"),
+    "wide_max": Config("wide_max", _d(2, 4, 4, 3001, 256, 256, 2048, 2048, 2048, 256, "bf16"),
+                       30.0, "peaks", 4, 2011, "random", "d_proj = d_z = d_pair = 2048 (the widest accepted)"),
+    "rows_max": Config("rows_max", _d(4095, 16, 4, 1024, 64, 64, 32, 32, 32, 64, "bf16"),
+                       30.0, "peaks", 4, 2012, "random", "65520 slot rows (the most accepted is 65535)"),
     # LM-head shapes (head tied to E, so d == e): ragged vocabulary tiles,
     # ragged row tiles, rows without planted peaks (bf16 ties at the K-th)
     "lmh_small": Config("lmh_small", _d(2, 8, 16, 5003, 256, 256, 64, 64, 64, 64, "bf16"),

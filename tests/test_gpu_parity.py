@@ -50,7 +50,7 @@ def _oracle(name, blocks=None):
 
 
 SMALL = ["tiny", "tiny_zero", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "mid_f32",
-         "k64_small", "k32_small", "widez_bf16", "tall_bf16"]
+         "k64_small", "k32_small", "widez_bf16", "tall_bf16", "b1_bf16", "k1_bf16", "wide_max"]
 
 
 def _run_block(name):
@@ -460,6 +460,37 @@ def test_full_large_sampled():
     _full_size("large", (0, 63))
 
 
+def test_full_rows_max_sampled():
+    # 4095 blocks of 16 slots: 65520 rows, near the 65535 the boundary accepts
+    _full_size("rows_max", (0, 2047, 4094))
+
+
+def test_degenerate_shapes_select_the_drafter():
+    # B = 1: no transitions, every slot keeps the drafter's top-1; K = 1: the
+    # only candidate is chosen whatever the scores
+    for name in ("b1_bf16", "k1_bf16"):
+        print(f"case degenerate {name}", flush=True)
+        inp, out = _run_block(name)
+        assert np.all(out["sel_idx"] == 0), name
+        np.testing.assert_array_equal(out["sel_tok"], out["cand_ids"][:, :, 0])
+        np.testing.assert_array_equal(out["cand_ids"], _oracle(name)["cand_ids"])
+
+
+def test_score_backward_single_slot_is_zero():
+    import draft_block_contextual_amd as dc
+    import torch
+    name = "b1_bf16"
+    print(f"case score_backward {name}", flush=True)
+    inp = _inputs(name)
+    D = inp["dims"]
+    dims, w, _, _, _ = device_inputs(inp)
+    z = _oracle(name)["z"]
+    out = dc.score_backward(dims, w, _bf16_dev(z), None, None)
+    torch.cuda.synchronize()
+    for key in ("dz", "dW1", "db1", "dw2", "db2", "d_cand_logits"):
+        assert np.all(_np(out[key]) == 0), key
+
+
 # --------------------------------- table of normalised candidate projections
 
 def _bf16_ulp(x):
@@ -637,7 +668,7 @@ def _grad_check(got, R, name, rel=2e-4):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "k32_small",
-                                  "k64_small", "widez_bf16"])
+                                  "k64_small", "widez_bf16", "wide_max"])
 def test_score_backward_matches_oracle(name):
     import draft_block_contextual_amd as dc
     import torch
@@ -793,7 +824,8 @@ def _rep_bwd_check(out, h, Er, f64, dz, ds, eps, blocks=None, tag=""):
     assert got.shape == (f64["W_f"].shape[0], 2 * r)
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "k64_small", "k32_small", "widez_bf16", "tall_bf16"])
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "k64_small", "k32_small", "widez_bf16", "tall_bf16",
+                                  "wide_max"])
 def test_represent_backward_matches_oracle(name):
     import draft_block_contextual_amd as dc
     import torch
