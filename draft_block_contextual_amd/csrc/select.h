@@ -15,15 +15,18 @@ __device__ __forceinline__ uint64_t make_comp(uint32_t key, uint32_t id) {
 
 // Exact top-K of the composites c[0..Q) held by the lanes of one wave (0 =
 // empty slot); KEYBITS is the width of the key half.  Marks the
-// min(K, #non-empty) largest in sel[].
+// min(K, #non-empty) largest in sel[].  idbits bounds the ids (id < 2^idbits),
+// so the inverted ids share their top 32 - idbits bits (all ones) and the
+// tie-break search starts below them.
 template <int Q, int KEYBITS>
-__device__ void select_topk(const uint64_t (&c)[Q], int K, bool (&sel)[Q]) {
+__device__ void select_topk(const uint64_t (&c)[Q], int K, bool (&sel)[Q], int idbits = 32) {
   uint32_t tk = 0;
   for (int bit = KEYBITS - 1; bit >= 0; --bit) {
     const uint32_t cand = tk | (1u << bit);
     int cnt = 0;
+    // an empty slot has key 0, below every candidate bound (cand >= 1)
 #pragma unroll
-    for (int q = 0; q < Q; ++q) cnt += __popcll(ballot(c[q] != 0 && comp_key(c[q]) >= cand));
+    for (int q = 0; q < Q; ++q) cnt += __popcll(ballot(comp_key(c[q]) >= cand));
     if (cnt >= K) tk = cand;
   }
   int ngt = 0, neq = 0;
@@ -34,9 +37,9 @@ __device__ void select_topk(const uint64_t (&c)[Q], int K, bool (&sel)[Q]) {
     neq += __popcll(ballot(v && comp_key(c[q]) == tk));
   }
   const int need = K - ngt;
-  uint32_t ti = 0;
+  uint32_t ti = idbits >= 32 ? 0u : (0xffffffffu << idbits);
   if (neq > need) {
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = min(idbits, 32) - 1; bit >= 0; --bit) {
       const uint32_t cand = ti | (1u << bit);
       int cnt = 0;
 #pragma unroll

@@ -387,8 +387,7 @@ __device__ __forceinline__ uint32_t row_bound(const uint32_t* s_gm, int K, int l
 // every number and is always flagged, and a NaN that is not flagged ranks
 // below at least K numbers of the row.
 template <int NV>
-__device__ __forceinline__ void row_screen(const uint32_t (&kw)[NV * 4], int seg0, int V, int l, uint32_t t,
-                                           int& nflag, int32_t* flags) {
+__device__ __forceinline__ uint32_t row_vflags(const uint32_t (&kw)[NV * 4], uint32_t t) {
   uint32_t vflag = 0u;
   if (t > 0x8000u) {
     const uint32_t thr = ((t ^ 0x8000u) - 1u) * 0x00010001u;   // raw pattern of t, minus one
@@ -407,6 +406,12 @@ __device__ __forceinline__ void row_screen(const uint32_t (&kw)[NV * 4], int seg
       vflag |= (any != 0u ? 1u : 0u) << i;
     }
   }
+  return vflag;
+}
+
+// Records the first element index of every flagged vector in the wave's list.
+template <int NV>
+__device__ __forceinline__ void row_append(uint32_t vflag, int seg0, int V, int l, int& nflag, int32_t* flags) {
   if (ballot(vflag != 0u) == 0ull) return;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -418,6 +423,12 @@ __device__ __forceinline__ void row_screen(const uint32_t (&kw)[NV * 4], int seg
     if (f && pos < kFlagCap) flags[pos] = e0;
     nflag += __popcll(m);
   }
+}
+
+template <int NV>
+__device__ __forceinline__ void row_screen(const uint32_t (&kw)[NV * 4], int seg0, int V, int l, uint32_t t,
+                                           int& nflag, int32_t* flags) {
+  row_append<NV>(row_vflags<NV>(kw, t), seg0, V, l, nflag, flags);
 }
 
 // Reads the flagged vectors again (each lane one vector per pass) and appends
@@ -530,16 +541,96 @@ __device__ __forceinline__ void row_pad(int seg0, int V, int l, uint32_t (&kw)[N
 constexpr int kRegNV = DCOCO_TOPK_NV;
 constexpr int kRegD = DCOCO_TOPK_D;
 
+// A wave's running top-K: one composite per lane (lanes < K, 0 = empty), and
+// once it holds K entries the smallest key among them (kmin).  An element
+// whose key is below kmin, or equal to it with a larger id than every entry,
+// cannot be in the wave's top-K; elements streamed later have larger ids than
+// every entry, so the screen may use kmin + 1.
+struct RunList {
+  uint64_t c = 0ull;
+  int n = 0;
+  uint32_t kmin = 0u;
+  bool bad = false;   // a NaN at or above the threshold: the bound may not hold
+};
+
+// Merges the 8 elements of one 16-byte vector per lane (raw bf16 words w4,
+// first element id e0, act false for an idle lane) into the running list:
+// elements with exact key >= max(t0, kmin) (NaN keys are 0) join the list's
+// composites, and the list becomes the top K of both.  s_tmp holds 64
+// composites of this wave's LDS for the compaction.
+__device__ __forceinline__ void list_merge(const uint32_t (&w4)[4], int e0, bool act, int V, int K, int l,
+                                           uint32_t t0, RunList& L, uint64_t* s_tmp) {
+  const uint32_t thr = L.n >= K ? max(t0, L.kmin) : t0;
+  uint64_t c[9];
+  bool any = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t kk = pack_keys(w4[q]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t raw = (kk >> (16 * h)) & 0xffffu;
+      const uint32_t k = canon_half(raw);
+      const int e = e0 + 2 * q + h;
+      const bool live = act && e < V;
+      const bool in = live && k >= thr;
+      L.bad |= live && raw >= thr && k != raw;
+      c[2 * q + h] = in ? make_comp(k, static_cast<uint32_t>(e)) : 0ull;
+      any |= in;
+    }
+  }
+  if (ballot(any) == 0ull) return;
+  c[8] = L.c;
+  bool sel[9];
+  select_topk<9, 16>(c, K, sel, 32 - __clz(static_cast<unsigned>(V)));   // ids < V
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < 9; ++q) {
+    const uint64_t m = ballot(sel[q]);
+    if (sel[q]) s_tmp[base + lanes_below(m)] = c[q];
+    base += __popcll(m);
+  }
+  // one wave: its LDS accesses complete in order; wait for the stores only
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+  L.c = l < base ? s_tmp[l] : 0ull;
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+  L.n = base;
+  if (base >= K) L.kmin = ~wave_max_u32_dpp(l < K ? ~comp_key(L.c) : 0u);
+}
+
+// Merges the flagged vectors (read again from the row) into the running list.
+__device__ __forceinline__ void list_flush(const uint16_t* rowp, int V, int K, int l, uint32_t t0,
+                                           const int32_t* flags, int& nflag, RunList& L, uint64_t* s_tmp) {
+  for (int b = 0; b < nflag; b += kWave) {
+    const bool act = b + l < nflag;
+    const int e0 = act ? flags[b + l] : 0;
+    const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);   // e0 + 8 <= V
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    list_merge(w4, e0, act, V, K, l, t0, L, s_tmp);
+  }
+  nflag = 0;
+}
+
 // Rows whose length is a multiple of 8 and that start 16-byte aligned.  Each
 // wave streams its segments through a ring of D register sets: D segments per
 // wave in flight, plain 16-byte vector loads (the compiler's waits follow the
-// issue order), LDS kept for the lists.  Loads are unconditional; a vector
-// past the row end reads a clamped address inside the row and is replaced by
-// padding, the pattern 0xffff (a NaN whose packed key is 1, below every real
-// key but the NaNs that also sit below -inf): groups of padding never lift
-// the bound, and padding is never appended (its ids are >= V).
+// issue order).  Loads are unconditional; a vector past the row end reads a
+// clamped address inside the row and is replaced by padding, the pattern
+// 0xffff (a NaN whose packed key is 1, below every real key but the NaNs that
+// also sit below -inf): groups of padding never lift the bound, and padding
+// never joins a list (its ids are >= V).
+//   Each wave keeps an exact running top-K.  A segment whose screen flags
+// more than kDense vectors (ties at the bound, rising rows) is merged into it
+// straight from registers, one vector per lane at a time; sparse flags are
+// recorded and merged in batches (when the list would overflow, and at the
+// end).  Every merge lifts the screen to one above the list's smallest key,
+// so a row of equal or ascending values costs a few merges per segment, not
+// a rescan.
+constexpr int kDense = 24;
+
 template <int NV, int G, int D>
-__global__ void __launch_bounds__(kRowWaves * kWave)
+__global__ void __launch_bounds__(kRowWaves * kWave, 4)   // two workgroups per CU
 topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
                          float* __restrict__ vals) {
   constexpr int kSegLen = kWave * NV * 8;
@@ -548,13 +639,13 @@ topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
   const int l = lane_id();
   const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
 
-  static_assert(kRowWaves * G * kWave * 4 <= kRowWaves * kRowCap * 8, "group maxima fit the lists");
-  __shared__ uint64_t s_cand[kRowWaves][kRowCap];
+  __shared__ uint32_t s_gm[kRowWaves * G * kWave];
   __shared__ int32_t s_flag[kRowWaves][kFlagCap];
+  __shared__ uint64_t s_tmp[kRowWaves][kWave];
+  __shared__ uint64_t s_cand[kRowWaves][kRowCap];
   __shared__ uint64_t s_best[kRowWaves * 64];
   __shared__ uint64_t s_fin[64];
   __shared__ int s_cnt[kRowWaves];
-  uint32_t* s_gm = reinterpret_cast<uint32_t*>(&s_cand[0][0]);
 
   uint32_t ring[D][NV * 4];
 #pragma unroll
@@ -572,34 +663,100 @@ topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
     for (int g = 0; g < G; ++g) s_gm[(w * G + g) * kWave + l] = gmx[g];
   }
   lds_barrier();
-  const uint32_t t = row_bound<G>(s_gm, K, l);
-  lds_barrier();                            // the lists overwrite the maxima from here on
+  const uint32_t t0 = row_bound<G>(s_gm, K, l);
 
-  int nseg = 0;
+  // Until a wave meets a dense segment or fills its flag list it only records
+  // flags (the common case); then it leaves the streaming loop for a loop
+  // that keeps the running list (the segments still in flight are read again).
+  RunList L;
   int nflag = 0;
-  for (int rd0 = 0; rd0 < rounds; rd0 += D) {
+  int rd_slow = rounds;                     // first round the slow loop takes
+  for (int rd0 = 0; rd0 < rounds && rd_slow == rounds; rd0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int rd = rd0 + j;
-      if (rd < rounds) {
+      if (rd < rounds && rd_slow == rounds) {
         const int seg0 = (rd * kRowWaves + w) * kSegLen;
         uint32_t kw[NV * 4];
 #pragma unroll
         for (int q = 0; q < NV * 4; ++q) kw[q] = ring[j][q];
         if (rd + D < rounds) row_load_regs<NV>(rowp, V, ((rd + D) * kRowWaves + w) * kSegLen, l, ring[j]);
         if (seg0 < V) {
-          ++nseg;
           row_pad<NV>(seg0, V, l, kw);
-          row_screen<NV>(kw, seg0, V, l, t, nflag, s_flag[w]);
+          const uint32_t vf = row_vflags<NV>(kw, t0);
+          if (ballot(vf != 0u) != 0ull) {
+            int nf = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+              nf += __popcll(ballot(((vf >> i) & 1u) && seg0 + (i * kWave + l) * 8 < V));
+            if (nf > kDense || nflag + nf > kFlagCap) rd_slow = rd;
+            else row_append<NV>(vf, seg0, V, l, nflag, s_flag[w]);
+          }
         }
       }
     }
   }
+  const bool refining = rd_slow < rounds;
+  if (refining) {
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // the ring's loads are not used
+    list_flush(rowp, V, K, l, t0, s_flag[w], nflag, L, s_tmp[w]);
+    uint32_t nxt[NV * 4];
+    row_load_regs<NV>(rowp, V, (rd_slow * kRowWaves + w) * kSegLen, l, nxt);
+    for (int rd = rd_slow; rd < rounds; ++rd) {
+      const int seg0 = (rd * kRowWaves + w) * kSegLen;
+      if (seg0 >= V) break;
+      uint32_t kw[NV * 4];
+#pragma unroll
+      for (int q = 0; q < NV * 4; ++q) kw[q] = nxt[q];
+      if (rd + 1 < rounds) row_load_regs<NV>(rowp, V, ((rd + 1) * kRowWaves + w) * kSegLen, l, nxt);
+      row_pad<NV>(seg0, V, l, kw);
+      const uint32_t ts = L.n >= K ? max(t0, L.kmin + 1u) : t0;
+      const uint32_t vf = ts > 0xffffu ? 0u : row_vflags<NV>(kw, ts);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (ballot((vf >> i) & 1u) == 0ull) continue;
+        const uint32_t w4[4] = {kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]};
+        list_merge(w4, seg0 + (i * kWave + l) * 8, true, V, K, l, t0, L, s_tmp[w]);
+      }
+    }
+  }
   __builtin_amdgcn_wave_barrier();
-  int cnt = 0;
-  const bool exact = nflag > kFlagCap || !row_collect<true>(rowp, V, t, s_flag[w], nflag, l, s_cand[w], cnt);
-  row_finish<NV>(rowp, V, K, rounds, w, l, nseg, exact, cnt, s_cand, s_best, s_fin, s_cnt,
-                 ids + static_cast<size_t>(row) * K, vals + static_cast<size_t>(row) * K);
+  bool exact = false;
+  if (refining) {
+    list_flush(rowp, V, K, l, t0, s_flag[w], nflag, L, s_tmp[w]);
+    exact = ballot(L.bad) != 0ull;
+    if (!exact && l < K) s_best[w * K + l] = L.c;
+  } else {
+    // the common case: the flagged vectors' elements at or above t0 become
+    // candidates and one small selection finishes (a NaN candidate, or more
+    // candidates than the list holds, takes the exact path)
+    int cnt = 0;
+    exact = !row_collect<true>(rowp, V, t0, s_flag[w], nflag, l, s_cand[w], cnt);
+    if (!exact) {
+      select_small<16>(s_cand[w], cnt, K, s_best + w * K);
+    } else if (cnt > kRowCap) {
+      // too many candidates for the list: merge the flagged vectors instead
+      list_flush(rowp, V, K, l, t0, s_flag[w], nflag, L, s_tmp[w]);
+      exact = ballot(L.bad) != 0ull;
+      if (!exact && l < K) s_best[w * K + l] = L.c;
+    }
+  }
+  if (exact) {
+    int segs = 0;
+    for (int rd = 0; rd < rounds; ++rd) segs += (rd * kRowWaves + w) * kSegLen < V ? 1 : 0;
+    exact_wave_bf16(rowp, V, K, w, kRowWaves, segs, NV, &s_cnt[w], s_best + w * K);
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int count = kRowWaves * K;
+    if (count <= 2 * kWave) finish_row<2, 16>(s_best, count, K, s_fin, rowp, V, ids + static_cast<size_t>(row) * K,
+                                              vals + static_cast<size_t>(row) * K);
+    else if (count <= 4 * kWave) finish_row<4, 16>(s_best, count, K, s_fin, rowp, V,
+                                                   ids + static_cast<size_t>(row) * K,
+                                                   vals + static_cast<size_t>(row) * K);
+    else finish_row<8, 16>(s_best, count, K, s_fin, rowp, V, ids + static_cast<size_t>(row) * K,
+                           vals + static_cast<size_t>(row) * K);
+  }
 }
 
 // Any other bf16 row: element loads, one segment at a time.
