@@ -50,6 +50,8 @@ def parse():
                     help="only run a plain 256 MiB device copy (for scaling HBM counters)")
     ap.add_argument("--no-btable", action="store_true", help="skip the table-path timing")
     ap.add_argument("--no-lm-head", action="store_true", help="skip the fused LM-head top-K timing")
+    ap.add_argument("--no-stress", action="store_true", help="skip the top-K stress-row timing")
+    ap.add_argument("--no-attainable", action="store_true", help="skip the copy / library-GEMM reference rates")
     ap.add_argument("--null-stream", action="store_true",
                     help="launch on the null stream instead of a stream of our own")
     return ap.parse_args()
@@ -191,6 +193,21 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})",
           file=sys.stderr, flush=True)
 
+    # ---- per-call latency: the same steps one at a time, an event pair each
+    # (outside the timed region above; the host waits between calls)
+    call_us = []
+    for i in range(min(args.steps, 100)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        b.synchronize()
+        call_us.append(a.elapsed_time(b) * 1e3)
+    call_us = np.asarray(call_us)
+    latency = {"p10": round(float(np.percentile(call_us, 10)), 2), "p50": round(float(np.median(call_us)), 2),
+               "p90": round(float(np.percentile(call_us, 90)), 2), "calls": int(call_us.size)}
+
     # ---- the table path (a next step beyond the per-call path): b_v = LN(P_e E_v)
     # built once for the weight set, outside the timed region, then the same
     # steps with b gathered from the table.  Reported beside `value`, not as it.
@@ -319,6 +336,70 @@ def main():
               file=sys.stderr, flush=True)
         del lg, hd
 
+    # ---- top-K on stress rows (not in the metric): no planted peaks, rising
+    # and falling ramps, constant rows; same shape as the timed logits
+    topk_stress = None
+    if dt == "bf16" and not args.no_stress:
+        R_, V_ = N * B, D.V
+        gen = torch.Generator(device=dev).manual_seed(11)
+        cases = {
+            "flat_normal_sd2": lambda: (torch.randn(R_, V_, generator=gen, device=dev) * 2).to(torch.bfloat16),
+            "ramp_up": lambda: torch.linspace(-12, 12, V_, device=dev).to(torch.bfloat16).repeat(R_, 1),
+            "ramp_down": lambda: torch.linspace(12, -12, V_, device=dev).to(torch.bfloat16).repeat(R_, 1),
+            "constant": lambda: torch.full((R_, V_), 1.5, device=dev, dtype=torch.bfloat16),
+        }
+        topk_stress = {}
+        for cname, make in cases.items():
+            lgs = make()
+            for _ in range(2):
+                dc.topk(dims, lgs, ids, cl, workspace=ws, stream=stream)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                dc.topk(dims, lgs, ids, cl, workspace=ws, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            topk_stress[cname] = round(a.elapsed_time(b) * 1e3 / 5, 1)
+            del lgs
+        topk_stress["unit"] = "us per dcoco_topk call"
+        print(f"# top-K stress rows: {topk_stress}", file=sys.stderr, flush=True)
+
+    # ---- attainable rates on this GPU, beside the spec-sheet peaks: a device
+    # copy (read + write bytes) and a large bf16 GEMM through the BLAS library
+    attain = None
+    if not args.no_attainable:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+                torch.matmul(ga, gb)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(10):
+                dst.copy_(src)
+            b.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(10):
+                torch.matmul(ga, gb)
+            b.record(stream)
+        torch.cuda.synchronize()
+        gemm_tf = 2.0 * 8192 ** 3 * 10 / (a.elapsed_time(b) * 1e-3) / 1e12
+        attain = {"copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tf, 1),
+                  "how": "256 MiB device copy (bytes read + written); 8192^3 bf16 matmul through torch"}
+        del src, dst, ga, gb
+        print(f"# attainable: {attain}", file=sys.stderr, flush=True)
+
     work = algorithmic_work(D)
     # Dominant kernel: top-K, one launch per dcoco_topk call, so the events
     # around that call time exactly that kernel.  It is bound by reading the
@@ -335,6 +416,9 @@ def main():
             "traffic_bytes_per_launch": traffic,
             "algorithmic_bytes_per_launch": work["logit_bytes"], "launch_us": round(topk_us, 2),
             "source_digest": digest}
+    if attain is not None:
+        # the same achieved rate against the device-copy rate measured above
+        roof["frac_of_copy"] = round(ach / attain["copy_GBps"], 4)
     # a grid element issues fma, rcp (quarter rate: 4 slots), add, fma
     grid_rate = work["grid_elems"] * 7 / (stage_us["score"] * 1e-6)
 
@@ -385,7 +469,10 @@ def main():
         "alu_frac_score": round(grid_rate / VALU_LANE_OPS, 4),
         "mfma_frac_rep_backward": (round(work["rep_bwd_flops"] / (stage_us["train_rep_backward"] * 1e-6) / 1e12
                                          / MFMA_BF16_PEAK_TFLOPS, 4) if "train_rep_backward" in stage_us else None),
+        "latency_us": latency,
         "roofline": roof,
+        "attainable": attain,
+        "topk_stress": topk_stress,
         "cpu_baseline": cpu,
         "btable_path": btable,
         "lm_head_topk": lm_head,

@@ -991,3 +991,30 @@ def test_full_q8b_32_lm_head_sampled():
     assert frac >= 0.75, frac
     # every row: the planted peaks are the top 16 (they stand 12+ above the background)
     np.testing.assert_array_equal(np.sort(_np(ids), axis=1), np.sort(L["planted"], axis=1))
+
+
+# ------------------------------------------------------ top-K stress rows
+
+@pytest.mark.parametrize("kind", ["ramp_up", "ramp_down", "constant", "ramp_up_noisy"])
+def test_topk_stress_rows(kind):
+    # rows that defeat a sampled threshold: every later element above it
+    # (rising), all elements tied (constant); the result must stay exact
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case topk stress {kind}", flush=True)
+    R, V, K = 24, 151936, 16
+    x = np.linspace(-12, 12, V)
+    if kind == "ramp_down":
+        x = x[::-1]
+    if kind == "constant":
+        x = np.full(V, 1.5)
+    rows = np.tile(x, (R, 1))
+    if kind == "ramp_up_noisy":
+        rows = rows + np.random.default_rng(70).standard_normal((R, V)) * 0.5
+    bits = synth.f32_to_bf16_bits(rows.astype(np.float32))
+    dims = dc.Dims(1, R, K, V, 32, 32, 32, 32, 32, 32, "bf16")
+    ids, vals = dc.topk(dims, to_dev(bits, "bf16"))
+    torch.cuda.synchronize()
+    ref_ids, ref_vals = O.top_k(O.to_f64(bits, "bf16"), K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_array_equal(vals.cpu().numpy().astype(np.float64), ref_vals)
