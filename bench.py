@@ -96,11 +96,16 @@ def copy_calibration():
 
 
 def source_digest(paths):
-    """Digest of kernel sources; a stored counter figure is used only while it matches."""
+    """Digest of kernel sources with comments and blank lines removed; a stored
+    counter figure is used only while it matches (comment edits keep it)."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            txt = f.read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", "", txt)
+        lines = [ln.rstrip() for ln in txt.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,7 +9,12 @@
 // (key << 32) | (0xffffffff - id); composites are unique, so "the K largest
 // composites" is exactly the wanted set, whatever the ties.
 //
-// Design (HBM-bound scan; each logit is read once):
+// bf16 rows (the drafter's logits) take one workgroup per row
+// (topk_bf16_row_reg_kernel, described where it is defined): a sampled bound,
+// a streamed screen, and an exact selection of the few survivors, with a
+// running-list fallback for rows that defeat the bound.
+//
+// fp32 rows (HBM-bound scan; each logit is read once):
 //   * a row is split into chunks of 4 wave segments; one workgroup (4 waves)
 //     per (row, chunk).  A wave segment is 64 lanes x 8 x 16-byte vectors, read
 //     with coalesced 16-byte loads and kept in registers as keys;
@@ -334,8 +339,10 @@ __device__ __attribute__((noinline)) void exact_wave_bf16(const uint16_t* rowp, 
 //      were just streamed) and their elements at or above T become
 //      candidates; each wave selects its top-K exactly and wave 0 merges the
 //      8 lists, sorts the K winners and writes ids and values.
-// A NaN among the candidates, or a list that overflows, sends the wave to the
-// exact path.
+// In the aligned kernel a wave whose flags would overflow, or that meets a
+// dense segment, keeps an exact running list instead (see list_merge); a NaN
+// at or above the bound sends the wave to the exact path (a rescan).  The
+// unaligned kernel sends every overflow there.
 constexpr int kRowWaves = 8;
 constexpr int kRowCap = 128;                // candidates per wave list
 constexpr int kFlagCap = 128;               // flagged vectors per wave list
