@@ -16,6 +16,7 @@
 // hi) (|a - hi - lo| <= 2^-17 |a|); both parts meet the same B fragment, so
 // the product is the fp32 one up to that remainder and fp32 accumulation.
 #include "common.h"
+#include "dma.h"
 #include "kernels.h"
 
 namespace dcoco {
@@ -302,7 +303,186 @@ __global__ void __launch_bounds__(kWgThreads, SETS == 2 ? 1 : 2) wgrad_kernel(Wg
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same products with the operands' raw tiles streamed into LDS by direct
+// global->LDS loads (global_load_lds_dwordx4: one wave instruction moves 64
+// lanes x 16 bytes), two tiles ahead, in a 2-slot ring; a transform pass then
+// reads each raw tile, splits / transposes it with the staging code above
+// into the MFMA layout, and the waves multiply.  No staging registers and no
+// compiler-counted loads in the loop: the waits are fixed vmcnt counts.
+// Raw layouts, one 1 KB instruction after another:
+//   row reduction A: 64 k-rows x 512 B (128 fp32 of m), chunk c of row r at
+//     position c ^ ((r >> 3) & 7), so the transform's column reads of 8 rows
+//     fall on different banks;
+//   column reduction A: 128 m-rows x 256 B (64 fp32 of k), natural order;
+//   B: 64 k-rows x 256 B (128 bf16 of n), chunk c of row r at c ^ ((r >> 3) & 7).
+// Gathered B rows take their ids from LDS (staged once per workgroup).
+constexpr int kRawA = kWgBK * kWgBM * 4;     // 32 KB
+constexpr int kRawB = kWgBK * kWgBN * 2;     // 16 KB
+constexpr int kRawBytes = kRawA + kRawB;
+constexpr int kDmaA = kRawA / 1024 / 4;      // A instructions per wave per tile (8)
+constexpr int kDmaB = kRawB / 1024 / 4;      // B instructions per wave per tile (4)
+constexpr int kIdsCap = 2048;                // gathered ids staged per workgroup
+
+__device__ __forceinline__ int raw_swz(int r) { return (r >> 3) & 7; }
+
+template <bool RR>
+__device__ __forceinline__ void wg_issue(const WgradArgs& p, const int32_t* s_ids, int kbeg, int m0, int n0, int k0,
+                                         int kend, uint32_t raw, int wv, int l) {
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int j = wv * kDmaA + i;
+    const float* src;
+    if constexpr (RR) {
+      const int r = 2 * j + (l >> 5);
+      const int c = (l & 31) ^ raw_swz(r);
+      const int k = min(k0 + r, kend - 1);
+      const int m = min(m0 + c * 4, p.M - 4);
+      src = p.A + static_cast<long long>(k) * p.lda + m;
+    } else {
+      const int r = 4 * j + (l >> 4);
+      const int m = min(m0 + r, p.M - 1);
+      const int k = min(k0 + (l & 15) * 4, kend - 4);
+      src = p.A + static_cast<long long>(m) * p.lda + k;
+    }
+    dma16(src, __builtin_amdgcn_readfirstlane(raw + j * 1024));
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int j = wv * kDmaB + i;
+    const int r = 4 * j + (l >> 4);
+    const int c = (l & 15) ^ raw_swz(r);
+    const int k = min(k0 + r, kend - 1);
+    const int n = min(n0 + c * 8, p.N - 8);
+    const uint16_t* row = p.bmap.mode == 1 ? p.b0 + static_cast<long long>(s_ids[k - kbeg]) * p.ldb0 : b_row(p, k);
+    dma16(row + n, __builtin_amdgcn_readfirstlane(raw + kRawA + j * 1024));
+  }
+}
+
+// one raw tile (LDS) into the staging registers, masked like wg_load
+template <bool RR>
+__device__ __forceinline__ void wg_from_raw(const WgradArgs& p, const char* raw, const WgTask& t, int m0, int n0,
+                                            int k0, int kend, float4 (&ra)[8], uint4 (&rb)[8]) {
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const uint4 zu = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (RR) {
+    const bool mok = m0 + 4 * t.mg < p.M;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int r = t.kg * 8 + kk;
+      const float4 v = *reinterpret_cast<const float4*>(raw + r * 512 + ((t.mg ^ raw_swz(r)) * 16));
+      ra[kk] = (mok && k0 + r < kend) ? v : z4;
+    }
+  } else {
+    const bool kok = k0 + t.kg * 8 < kend;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = t.mg + 32 * i;
+      const char* q = raw + m * 256 + t.kg * 32;
+      const float4 v0 = *reinterpret_cast<const float4*>(q);
+      const float4 v1 = *reinterpret_cast<const float4*>(q + 16);
+      const bool ok = kok && m0 + m < p.M;
+      ra[2 * i] = ok ? v0 : z4;
+      ra[2 * i + 1] = ok ? v1 : z4;
+    }
+  }
+  if (t.b_task) {
+    const bool nok = n0 + 8 * t.ng < p.N;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int r = t.kg * 8 + kk;
+      const uint4 v = *reinterpret_cast<const uint4*>(raw + kRawA + r * 256 + ((t.ng ^ raw_swz(r)) * 16));
+      rb[kk] = (nok && k0 + r < kend) ? v : zu;
+    }
+  }
+}
+
+__device__ __forceinline__ void lds_only_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+template <bool RR>
+__global__ void __launch_bounds__(kWgThreads, 1) wgrad_dma_kernel(WgradArgs p) {
+  __shared__ __align__(1024) char raw0[kRawBytes];
+  __shared__ __align__(1024) char raw1[kRawBytes];
+  __shared__ __align__(16) char sAh[kWgBM * kWgRow];
+  __shared__ __align__(16) char sAl[kWgBM * kWgRow];
+  __shared__ __align__(16) char sB[kWgBN * kWgRow];
+  __shared__ int32_t s_ids[kIdsCap];
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int wm = wv >> 1;
+  const int wn = wv & 1;
+  const int n0 = blockIdx.x * kWgBN;
+  const int m0 = blockIdx.y * kWgBM;
+  const int z = blockIdx.z;
+  const int kbeg = z * p.ksplit;
+  const int kend = min(p.Kd, kbeg + p.ksplit);
+  WgTask t;
+  t.kg = tid & 7;
+  t.mg = tid >> 3;
+  t.ng = tid >> 3;
+  t.b_task = tid < 128;
+  if (p.bmap.mode == 1) {
+    for (int i = tid; i < kend - kbeg; i += kWgThreads) {
+      const int id = p.bmap.ids[kbeg + i];
+      s_ids[i] = id < 0 ? 0 : (id > p.bmap.idmax ? p.bmap.idmax : id);
+    }
+  }
+  lds_only_barrier();
+  const uint32_t r0 = __builtin_amdgcn_readfirstlane(lds_offset(raw0));
+  const uint32_t r1 = __builtin_amdgcn_readfirstlane(lds_offset(raw1));
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (kbeg < kend) wg_issue<RR>(p, s_ids, kbeg, m0, n0, kbeg, kend, r0, wv, l);
+  if (kbeg + kWgBK < kend) wg_issue<RR>(p, s_ids, kbeg, m0, n0, kbeg + kWgBK, kend, r1, wv, l);
+  int par = 0;
+  for (int k0 = kbeg; k0 < kend; k0 += kWgBK, par ^= 1) {
+    // this tile's raw data has landed when at most the next tile's loads are
+    // still in flight; the barrier also ends every wave's reads of the
+    // previous MFMA tile
+    if (k0 + kWgBK < kend) wait_vmcnt_barrier<kDmaA + kDmaB>();
+    else wait_vmcnt_barrier<0>();
+    {
+      float4 ra[8];
+      uint4 rb[8];
+      wg_from_raw<RR>(p, par ? raw1 : raw0, t, m0, n0, k0, kend, ra, rb);
+      wg_stage<RR>(t, ra, rb, sAh, sAl, sB);
+    }
+    lds_only_barrier();                      // MFMA tile complete, this raw slot free
+    if (k0 + 2 * kWgBK < kend) wg_issue<RR>(p, s_ids, kbeg, m0, n0, k0 + 2 * kWgBK, kend, par ? r1 : r0, wv, l);
+    wg_compute(sAh, sAl, sB, wm, wn, l, acc);
+  }
+
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + wm * 64 + a * 16 + (l >> 4) * 4 + v;
+      if (m >= p.M) continue;
+      float* row;
+      if (m < p.cend0) row = p.c0 + static_cast<long long>(m) * p.ldc0;
+      else if (m < p.cend1) row = p.c1 + static_cast<long long>(m - p.cend0) * p.ldc1;
+      else row = p.c2 + static_cast<long long>(m - p.cend1) * p.ldc2;
+      row += z * p.c_split;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = n0 + wn * 64 + b * 16 + (l & 15);
+        if (n < p.N) row[n] = acc[a][b][v];
+      }
+    }
+}
+
 }  // namespace
+
+#ifndef DCOCO_WGRAD_DMA
+#define DCOCO_WGRAD_DMA 1
+#endif
+constexpr bool kWgradUseDma = DCOCO_WGRAD_DMA != 0;
 
 int wgrad_pick_split(int M, int N, int Kd) {
   const long long tiles = static_cast<long long>((M + kWgBM - 1) / kWgBM) * ((N + kWgBN - 1) / kWgBN);
@@ -329,8 +509,20 @@ hipError_t launch_wgrad(WgradArgs p, bool row_reduction, int splits, hipStream_t
   p.ksplit = ks;
   const int gz = p.Kd > 0 ? (p.Kd + ks - 1) / ks : 1;
   const dim3 grid((p.N + kWgBN - 1) / kWgBN, (p.M + kWgBM - 1) / kWgBM, gz);
-  // row reductions run at two waves per SIMD; column reductions (short k
-  // per workgroup, A rows read whole) gain more from the deeper pipeline
+  // the DMA ring takes a whole CU per workgroup (its LDS), so it pays when the
+  // grid fits one workgroup per CU; larger grids run two register-staged
+  // workgroups per CU, whose transforms and MFMAs then overlap
+  const long long wgs = static_cast<long long>(grid.x) * grid.y * grid.z;
+  const bool dma = kWgradUseDma && wgs <= 256 && (p.bmap.mode != 1 || ks <= kIdsCap);
+  if (dma) {
+    if (row_reduction)
+      hipLaunchKernelGGL((wgrad_dma_kernel<true>), grid, dim3(kWgThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((wgrad_dma_kernel<false>), grid, dim3(kWgThreads), 0, st, p);
+    return hipGetLastError();
+  }
+  // register staging: row reductions at two waves per SIMD; column reductions
+  // (short k per workgroup, A rows read whole) gain more from two sets
   if (row_reduction)
     hipLaunchKernelGGL((wgrad_kernel<true, 1>), grid, dim3(kWgThreads), 0, st, p);
   else
