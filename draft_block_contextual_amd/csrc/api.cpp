@@ -323,8 +323,8 @@ BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
     L.part_floats = std::max({L.part_floats, wgrad_part_floats(static_cast<int>(RK), d->d_z, 2 * d->d_mlp),
                               wgrad_part_floats(2 * d->d_mlp, d->d_z, static_cast<int>(RK))});
   L.part = static_cast<float*>(c.take(sizeof(float) * L.part_floats));
-  const size_t red = 2 * (static_cast<size_t>(colsum_blocks(static_cast<int>(P))) + 1) * H +
-                     P * d->K * d->K / 8192 + 2;
+  const size_t red = static_cast<size_t>(mlp_reduce_floats(static_cast<int>(P), static_cast<int>(H), d->n_blocks,
+                                                            d->B, d->K));
   L.red = static_cast<float*>(c.take(sizeof(float) * red));
   return L;
 }
@@ -675,11 +675,9 @@ int dcoco_score_backward(const dcoco_dims* d, const dcoco_weights* w, const void
     a.dAB = L.dAB; a.dC = L.dC; a.dw2p = L.dw2p;
     e = launch_grid_bwd(a, dt, st);
   }
-  float* red2 = L.red + 2 * (colsum_blocks(P) + 1) * static_cast<long long>(H);
-  if (e == hipSuccess) e = launch_colsum(L.dw2p, P, H, H, L.red, g->dw2, st);
-  if (e == hipSuccess) e = launch_colsum(L.dC, P, H, H, L.red, g->db1, st);
-  if (e == hipSuccess) e = launch_sum(dS, static_cast<long long>(P) * d->K * d->K, red2, g->db2, st);
-  if (e == hipSuccess && d_cand_logits) e = launch_dlogit(dS, d->n_blocks, d->B, d->K, d_cand_logits, st);
+  if (e == hipSuccess)
+    e = launch_mlp_reduce(L.dw2p, L.dC, P, H, dS, d->n_blocks, d->B, d->K, L.red, g->dw2, g->db1, g->db2,
+                          d_cand_logits, st);
   if (bwd_on_mfma(d)) {
     const uint16_t* W1u = static_cast<const uint16_t*>(w->W1);
     // dz = dA W1a + dB W1b: one product over 2H, W1's two column blocks

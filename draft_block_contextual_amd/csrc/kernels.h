@@ -145,12 +145,6 @@ struct GemmF32Args {
 hipError_t launch_gemm_f32(const GemmF32Args& g, int a_dtype, int b_dtype, hipStream_t st);
 hipError_t launch_sum_splits(const float* part, int splits, int rows, int cols, float* out, long long ld_out,
                              hipStream_t st);
-// column sums of x [rows, cols] (row stride ld) into out [cols]; tmp holds
-// the partial rows (colsum_tmp_floats of them)
-int colsum_blocks(int rows);
-hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* tmp, float* out, hipStream_t st);
-// out[0] = sum of x[0..n); tmp holds n / 8192 + 1 partial sums
-hipError_t launch_sum(const float* x, long long n, float* tmp, float* out, hipStream_t st);
 // which source row an operand row m reads: m itself or a clamped id
 // (gathered rows)
 struct RowMap {
@@ -220,7 +214,12 @@ hipError_t launch_ln_fwd_bwd(const float* x, int split, int M, int ldx, int col0
 // placed at their left slot (columns r ..) and right slot (columns r + rs ..),
 // zeros where a slot has no such pair
 hipError_t launch_pack_ds(const float* ds, int N, int B, int rs, int r, int C, float* Acat, hipStream_t st);
-hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st);
+// the scoring backward's reductions in two launches: dw2 and db1 (column sums
+// of dw2p and dC [P, H]), d l (into dcl_out, or tmp when null) and db2 = sum
+// of d l; tmp holds mlp_reduce_floats(...) floats
+int mlp_reduce_floats(int P, int H, int N, int B, int K);
+hipError_t launch_mlp_reduce(const float* dw2p, const float* dC, int P, int H, const float* dS, int N, int B, int K,
+                             float* tmp, float* dw2, float* db1, float* db2, float* dcl_out, hipStream_t st);
 hipError_t launch_fill(float* x, long long n, float v, hipStream_t st);
 
 }  // namespace dcoco

@@ -116,18 +116,22 @@ __global__ void __launch_bounds__(kThreads) sum_kernel(const float* __restrict__
   if (threadIdx.x == 0) out[blockIdx.x] = v;
 }
 
-// Column sums in a fixed order.  Workgroup (bx, by) takes 64 columns of the
-// rows [by * kColRows, +kColRows): four row groups of eight rows, loads all in
-// flight, combined through LDS into out[by * cols + c] (one partial row per
-// row block; a second launch with rows = number of blocks adds those).
+// Column sums in a fixed order work on blocks of 64 columns x kColRows rows:
+// four row groups of eight rows, loads all in flight, combined through LDS.
 constexpr int kColRows = 32;
-__global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restrict__ x, int rows, int cols,
-                                                          long long ld, float* __restrict__ out) {
-  __shared__ float red[kThreads];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
+
+// The reductions after the grid backward in two launches.  First: the
+// 32-row partial column sums of dw2p and dC (colsum_block, one block per
+// (64 columns, 32 rows) of each) and d l (one thread per entry, the sum over a
+// in order), side by side.
+// Second: the partial rows added in order into dw2 and db1, and db2 as the
+// sum of d l (every dS element enters d l exactly once, slot 0 holds zeros).
+__device__ __forceinline__ void colsum_block(const float* __restrict__ x, int rows, int cols, long long ld, int bx,
+                                             int by, float* red, float* __restrict__ out) {
+  const int c = bx * 64 + (threadIdx.x & 63);
   const int g = threadIdx.x >> 6;
   const int cc = min(c, cols - 1);
-  const int r0 = blockIdx.y * kColRows + g * (kColRows / 4);
+  const int r0 = by * kColRows + g * (kColRows / 4);
   float t[kColRows / 4];
 #pragma unroll
   for (int j = 0; j < kColRows / 4; ++j) t[j] = x[static_cast<long long>(min(r0 + j, rows - 1)) * ld + cc];
@@ -137,26 +141,77 @@ __global__ void __launch_bounds__(kThreads) colsum_kernel(const float* __restric
   red[threadIdx.x] = v;
   __syncthreads();
   if (g == 0 && c < cols)
-    out[static_cast<long long>(blockIdx.y) * cols + c] =
+    out[static_cast<long long>(by) * cols + c] =
         (red[threadIdx.x] + red[threadIdx.x + 64]) + (red[threadIdx.x + 128] + red[threadIdx.x + 192]);
 }
 
-// d l_i(b) = sum_a dS_{i-1}(a, b) for slots i >= 1, 0 for slot 0; one thread
-// per (n, i, b)
-__global__ void __launch_bounds__(kThreads) dlogit_kernel(const float* __restrict__ dS, int N, int B, int K,
-                                                          float* __restrict__ dcl) {
-  const long long idx = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
-  if (idx >= static_cast<long long>(N) * B * K) return;
-  const int b = static_cast<int>(idx % K);
-  const long long ni = idx / K;
-  const int i = static_cast<int>(ni % B);
-  const long long n = ni / B;
-  float v = 0.f;
-  if (i > 0) {
-    const float* g = dS + ((n * (B - 1) + i - 1) * K) * K + b;
-    for (int a = 0; a < K; ++a) v += g[static_cast<long long>(a) * K];
+__global__ void __launch_bounds__(kThreads) mlp_reduce1_kernel(const float* __restrict__ dw2p,
+                                                               const float* __restrict__ dC, int P, int H,
+                                                               const float* __restrict__ dS, int N, int B, int K,
+                                                               float* __restrict__ part_w, float* __restrict__ part_c,
+                                                               float* __restrict__ dcl) {
+  __shared__ float red[kThreads];
+  const int cb = (H + 63) / 64;
+  const int rb = (P + kColRows - 1) / kColRows;
+  const int nb = cb * rb;
+  const int blk = blockIdx.x;
+  if (blk < nb) {
+    colsum_block(dw2p, P, H, H, blk % cb, blk / cb, red, part_w);
+  } else if (blk < 2 * nb) {
+    colsum_block(dC, P, H, H, (blk - nb) % cb, (blk - nb) / cb, red, part_c);
+  } else {
+    const long long idx = static_cast<long long>(blk - 2 * nb) * kThreads + threadIdx.x;
+    if (idx >= static_cast<long long>(N) * B * K) return;
+    const int b = static_cast<int>(idx % K);
+    const long long ni = idx / K;
+    const int i = static_cast<int>(ni % B);
+    const long long n = ni / B;
+    float v = 0.f;
+    if (i > 0) {
+      const float* g = dS + ((n * (B - 1) + i - 1) * K) * K + b;
+      for (int a = 0; a < K; ++a) v += g[static_cast<long long>(a) * K];
+    }
+    dcl[idx] = v;
   }
-  dcl[idx] = v;
+}
+
+__global__ void __launch_bounds__(kThreads) mlp_reduce2_kernel(const float* __restrict__ part_w,
+                                                               const float* __restrict__ part_c, int P, int H,
+                                                               const float* __restrict__ dcl, long long ncl,
+                                                               float* __restrict__ dw2, float* __restrict__ db1,
+                                                               float* __restrict__ db2) {
+  __shared__ float red[kThreads];
+  const int cb = (H + 63) / 64;
+  const int rb = (P + kColRows - 1) / kColRows;
+  const int blk = blockIdx.x;
+  if (blk < 2 * cb) {
+    const float* part = blk < cb ? part_w : part_c;
+    float* out = blk < cb ? dw2 : db1;
+    const int bx = blk % cb;
+    if (rb <= kColRows) {
+      colsum_block(part, rb, H, H, bx, 0, red, out);
+    } else {
+      // many row blocks: one thread per column adds them in order
+      const int c = bx * 64 + static_cast<int>(threadIdx.x);
+      if (threadIdx.x < 64 && c < H) {
+        float v = 0.f;
+        for (int r = 0; r < rb; ++r) v += part[static_cast<long long>(r) * H + c];
+        out[c] = v;
+      }
+    }
+    return;
+  }
+  // db2: fixed-order sum of d l over one workgroup
+  float v = 0.f;
+  for (long long i = threadIdx.x; i < ncl; i += kThreads) v += dcl[i];
+  red[threadIdx.x] = v;
+  __syncthreads();
+#pragma unroll
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (static_cast<int>(threadIdx.x) < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) db2[0] = red[0];
 }
 
 __global__ void __launch_bounds__(kThreads) fill_kernel(float* __restrict__ x, long long n, float v) {
@@ -678,33 +733,24 @@ hipError_t launch_sum_splits_ex(const float* part, int splits, long long split_s
   return hipGetLastError();
 }
 
-int colsum_blocks(int rows) { return (rows + kColRows - 1) / kColRows; }
-
-hipError_t launch_colsum(const float* x, int rows, int cols, long long ld, float* tmp, float* out, hipStream_t st) {
-  const int rb = colsum_blocks(rows);
-  if (rb == 1) {
-    hipLaunchKernelGGL(colsum_kernel, dim3((cols + 63) / 64, 1), dim3(kThreads), 0, st, x, rows, cols, ld, out);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(colsum_kernel, dim3((cols + 63) / 64, rb), dim3(kThreads), 0, st, x, rows, cols, ld, tmp);
-  return launch_colsum(tmp, rb, cols, cols, tmp + static_cast<long long>(rb) * cols, out, st);
+int mlp_reduce_floats(int P, int H, int N, int B, int K) {
+  const int rb = (P + kColRows - 1) / kColRows;
+  return 2 * rb * H + N * B * K;
 }
 
-hipError_t launch_sum(const float* x, long long n, float* tmp, float* out, hipStream_t st) {
-  const long long chunk = 8192;
-  const long long nb = (n + chunk - 1) / chunk;
-  if (nb <= 1) {
-    hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, x, n, n, out);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(sum_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, x, n, chunk, tmp);
-  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(kThreads), 0, st, tmp, nb, nb, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_dlogit(const float* dS, int N, int B, int K, float* dcl, hipStream_t st) {
-  hipLaunchKernelGGL(dlogit_kernel, dim3(blocks_for(static_cast<long long>(N) * B * K)), dim3(kThreads), 0, st,
-                     dS, N, B, K, dcl);
+hipError_t launch_mlp_reduce(const float* dw2p, const float* dC, int P, int H, const float* dS, int N, int B, int K,
+                             float* tmp, float* dw2, float* db1, float* db2, float* dcl_out, hipStream_t st) {
+  const int cb = (H + 63) / 64;
+  const int rb = (P + kColRows - 1) / kColRows;
+  float* part_w = tmp;
+  float* part_c = tmp + static_cast<long long>(rb) * H;
+  float* dcl = dcl_out ? dcl_out : tmp + 2ll * rb * H;
+  const long long ncl = static_cast<long long>(N) * B * K;
+  const unsigned nb1 = static_cast<unsigned>(2 * cb * rb) + blocks_for(ncl);
+  hipLaunchKernelGGL(mlp_reduce1_kernel, dim3(nb1), dim3(kThreads), 0, st, dw2p, dC, P, H, dS, N, B, K, part_w,
+                     part_c, dcl);
+  hipLaunchKernelGGL(mlp_reduce2_kernel, dim3(2 * cb + 1), dim3(kThreads), 0, st, part_w, part_c, P, H, dcl, ncl,
+                     dw2, db1, db2);
   return hipGetLastError();
 }
 
