@@ -619,6 +619,131 @@ __device__ __forceinline__ void list_flush(const uint16_t* rowp, int V, int K, i
   nflag = 0;
 }
 
+// ---- on-chip finish of a row (register-ring kernel) --------------------
+// A wave reading LDS that its own lanes just wrote: the wave's LDS accesses
+// complete in order, so waiting for its stores and stopping the compiler from
+// moving accesses across is enough.
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The r-th largest of src[0..n) (unique composites, 0 = empty) goes to dst[r]
+// for r < K, dst[#non-empty..K) is cleared.  Each lane ranks Q entries by
+// counting the larger ones over broadcast LDS reads, so the list comes out
+// sorted (value desc, id asc) without ballot chains.  n <= 64 Q; src and dst
+// must not overlap.
+template <int Q>
+__device__ __forceinline__ void rank_top(const uint64_t* src, int n, int K, uint64_t* dst, int l) {
+  uint64_t c[Q];
+  int r[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int i = q * kWave + l;
+    c[q] = i < n ? src[i] : 0ull;
+    r[q] = 0;
+  }
+#pragma unroll 4
+  for (int j = 0; j < n; ++j) {
+    const uint64_t v = src[j];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) r[q] += v > c[q] ? 1 : 0;
+  }
+  int nz = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    nz += __popcll(ballot(c[q] != 0ull));
+    if (c[q] != 0ull && r[q] < K) dst[r[q]] = c[q];
+  }
+  for (int i = nz + l; i < K; i += kWave) dst[i] = 0ull;
+}
+
+// row_append that also keeps each flagged vector's four words in vecs[], so
+// the candidates can later be collected from LDS instead of memory.
+template <int NV>
+__device__ __forceinline__ void row_append_keep(uint32_t vflag, const uint32_t (&kw)[NV * 4], int seg0, int V, int l,
+                                                int& nflag, int32_t* flags, uint4* vecs) {
+  if (ballot(vflag != 0u) == 0ull) return;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e0 = seg0 + (i * kWave + l) * 8;
+    const bool f = ((vflag >> i) & 1u) && e0 < V;
+    const uint64_t m = ballot(f);
+    if (m == 0ull) continue;
+    const int pos = nflag + lanes_below(m);
+    if (f && pos < kFlagCap) {
+      flags[pos] = e0;
+      vecs[pos] = make_uint4(kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]);
+    }
+    nflag += __popcll(m);
+  }
+}
+
+// row_collect over the kept vectors (nflag <= kFlagCap): the elements at or
+// above t become candidates; false if one of them is a NaN pattern or the
+// list overflows (the caller then takes another path).
+__device__ __forceinline__ bool row_collect_kept(const int32_t* flags, const uint4* vecs, int nflag, int V, uint32_t t,
+                                                 int l, uint64_t* cand, int& cnt) {
+  bool bad = false;
+  for (int b = 0; b < nflag; b += kWave) {
+    const bool act = b + l < nflag;
+    const int e0 = act ? flags[b + l] : 0;
+    const uint4 v = vecs[act ? b + l : 0];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t kk = pack_keys(w4[q]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t k = (kk >> (16 * h)) & 0xffffu;
+        const int e = e0 + 2 * q + h;
+        const bool c = act && k >= t && e < V;
+        bad |= c && (k > 0xff80u || k < 0x0080u);
+        const uint64_t m = ballot(c);
+        const int pos = cnt + lanes_below(m);
+        if (c && pos < kRowCap) cand[pos] = make_comp(k, static_cast<uint32_t>(e));
+        cnt += __popcll(m);
+      }
+    }
+  }
+  return ballot(bad) == 0ull && cnt <= kRowCap;
+}
+
+// All waves at once, after each has written its sorted list of K to
+// lists[w K ..]: an entry's rank in the row is its position in its own list
+// plus, for every other list, the number of that list's entries above it
+// (counted with independent LDS reads, which pipeline, rather than a binary
+// search, whose reads depend on each other).  With KP = K rounded up to a
+// power of two, the 64 / KP lanes of one entry split the other lists between
+// them and add their counts.  Entries of rank < K go to out[rank].
+__device__ __forceinline__ void merge_sorted_lists(const uint64_t* lists, int K, int w, int l, uint64_t* out) {
+  int KP = 1;
+  while (KP < K) KP <<= 1;                   // K <= 64
+  const int G = kWave / KP;                  // lanes per entry
+  const int c = l % KP;
+  const int g = l / KP;
+  const uint64_t x = c < K ? lists[w * K + c] : 0ull;
+  int rank = 0;
+  for (int j = g; j < kRowWaves; j += G) {
+    if (j == w) {
+      rank += c;
+      continue;
+    }
+    const uint64_t* lst = lists + j * K;
+#pragma unroll 8
+    for (int i = 0; i < K; ++i) rank += lst[i] > x ? 1 : 0;
+  }
+  for (int off = KP; off < kWave; off <<= 1) rank += __shfl_xor(rank, off, kWave);
+  if (g == 0 && x != 0ull && rank < K) out[rank] = x;
+}
+
+// The bf16 pattern of an order key (the inverse of pack_keys on one half);
+// 0x8000 stands for both zeros and 0 for a NaN, so those two read the row.
+__device__ __forceinline__ bool key_is_exact_bf16(uint32_t k) { return k != 0u && k != 0x8000u; }
+__device__ __forceinline__ uint32_t key_to_bf16(uint32_t k) {
+  return k >= 0x8000u ? (k ^ 0x8000u) : ((0x10000u - k) & 0xffffu);
+}
+
 // Rows whose length is a multiple of 8 and that start 16-byte aligned.  Each
 // wave streams its segments through a ring of D register sets: D segments per
 // wave in flight, plain 16-byte vector loads (the compiler's waits follow the
@@ -634,6 +759,11 @@ __device__ __forceinline__ void list_flush(const uint16_t* rowp, int V, int K, i
 // end).  Every merge lifts the screen to one above the list's smallest key,
 // so a row of equal or ascending values costs a few merges per segment, not
 // a rescan.
+//   The finish stays on chip.  A flagged vector's 16 bytes are kept in LDS
+// when it is flagged, so the candidates are collected without reading the row
+// again; each wave ranks its candidates into a sorted list of K; all waves
+// then rank their own entries across the eight lists, and the values are
+// decoded from the keys (only a zero or NaN key reads the row).
 constexpr int kDense = 24;
 
 template <int NV, int G, int D>
@@ -648,6 +778,7 @@ topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
 
   __shared__ uint32_t s_gm[kRowWaves * G * kWave];
   __shared__ int32_t s_flag[kRowWaves][kFlagCap];
+  __shared__ uint4 s_vec[kRowWaves][kFlagCap];
   __shared__ uint64_t s_tmp[kRowWaves][kWave];
   __shared__ uint64_t s_cand[kRowWaves][kRowCap];
   __shared__ uint64_t s_best[kRowWaves * 64];
@@ -697,7 +828,7 @@ topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
             for (int i = 0; i < NV; ++i)
               nf += __popcll(ballot(((vf >> i) & 1u) && seg0 + (i * kWave + l) * 8 < V));
             if (nf > kDense || nflag + nf > kFlagCap) rd_slow = rd;
-            else row_append<NV>(vf, seg0, V, l, nflag, s_flag[w]);
+            else row_append_keep<NV>(vf, kw, seg0, V, l, nflag, s_flag[w], s_vec[w]);
           }
         }
       }
@@ -728,41 +859,57 @@ topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
     }
   }
   __builtin_amdgcn_wave_barrier();
+  // Each wave leaves its K best, sorted, in s_best[w K ..]; then all waves
+  // rank their entries across the lists and wave 0 writes the row.  Nothing
+  // here reads memory except the exact path and values whose key stands for
+  // two patterns (zeros) or none (NaN).
+  uint64_t* mine = s_best + w * K;
   bool exact = false;
+  bool listed = false;                       // the running list holds the wave's K best
   if (refining) {
     list_flush(rowp, V, K, l, t0, s_flag[w], nflag, L, s_tmp[w]);
     exact = ballot(L.bad) != 0ull;
-    if (!exact && l < K) s_best[w * K + l] = L.c;
+    listed = !exact;
   } else {
-    // the common case: the flagged vectors' elements at or above t0 become
-    // candidates and one small selection finishes (a NaN candidate, or more
-    // candidates than the list holds, takes the exact path)
+    // the common case: the kept vectors' elements at or above t0 become
+    // candidates (a NaN candidate takes the exact path; more candidates than
+    // the list holds, the running list)
     int cnt = 0;
-    exact = !row_collect<true>(rowp, V, t0, s_flag[w], nflag, l, s_cand[w], cnt);
+    exact = !row_collect_kept(s_flag[w], s_vec[w], nflag, V, t0, l, s_cand[w], cnt);
     if (!exact) {
-      select_small<16>(s_cand[w], cnt, K, s_best + w * K);
+      wave_lds_fence();
+      if (cnt <= kWave) rank_top<1>(s_cand[w], cnt, K, mine, l);
+      else rank_top<kRowCap / kWave>(s_cand[w], cnt, K, mine, l);
     } else if (cnt > kRowCap) {
-      // too many candidates for the list: merge the flagged vectors instead
       list_flush(rowp, V, K, l, t0, s_flag[w], nflag, L, s_tmp[w]);
       exact = ballot(L.bad) != 0ull;
-      if (!exact && l < K) s_best[w * K + l] = L.c;
+      listed = !exact;
     }
+  }
+  if (listed) {
+    if (l < K) s_tmp[w][l] = L.c;
+    wave_lds_fence();
+    rank_top<1>(s_tmp[w], K, K, mine, l);
   }
   if (exact) {
     int segs = 0;
     for (int rd = 0; rd < rounds; ++rd) segs += (rd * kRowWaves + w) * kSegLen < V ? 1 : 0;
-    exact_wave_bf16(rowp, V, K, w, kRowWaves, segs, NV, &s_cnt[w], s_best + w * K);
+    exact_wave_bf16(rowp, V, K, w, kRowWaves, segs, NV, &s_cnt[w], s_tmp[w]);
+    wave_lds_fence();
+    rank_top<1>(s_tmp[w], K, K, mine, l);
   }
-  __syncthreads();
-  if (w == 0) {
-    const int count = kRowWaves * K;
-    if (count <= 2 * kWave) finish_row<2, 16>(s_best, count, K, s_fin, rowp, V, ids + static_cast<size_t>(row) * K,
-                                              vals + static_cast<size_t>(row) * K);
-    else if (count <= 4 * kWave) finish_row<4, 16>(s_best, count, K, s_fin, rowp, V,
-                                                   ids + static_cast<size_t>(row) * K,
-                                                   vals + static_cast<size_t>(row) * K);
-    else finish_row<8, 16>(s_best, count, K, s_fin, rowp, V, ids + static_cast<size_t>(row) * K,
-                           vals + static_cast<size_t>(row) * K);
+  if (w == 0 && l < K) s_fin[l] = 0ull;
+  lds_barrier();
+  merge_sorted_lists(s_best, K, w, l, s_fin);
+  lds_barrier();
+  if (w == 0 && l < K) {
+    const uint64_t x = s_fin[l];
+    const uint32_t id = 0xffffffffu - comp_inv(x);
+    const uint32_t k = comp_key(x);
+    const uint32_t rid = id < static_cast<uint32_t>(V) ? id : 0u;
+    const uint32_t bits = key_is_exact_bf16(k) ? key_to_bf16(k) : static_cast<uint32_t>(rowp[rid]);
+    ids[static_cast<size_t>(row) * K + l] = static_cast<int32_t>(id);
+    vals[static_cast<size_t>(row) * K + l] = bf16_to_f32(static_cast<uint16_t>(bits));
   }
 }
 
