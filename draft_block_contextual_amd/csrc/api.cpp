@@ -257,7 +257,7 @@ hipError_t ab_gemm(const dcoco_dims* d, const dcoco_weights* w, const void* z, c
 
 // AB, then the grid (needs the pair term)
 hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* cl, float* S,
-                      const ScoreLayout& L, hipStream_t st) {
+                      const ScoreLayout& L, hipStream_t st, int32_t* best = nullptr) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int P = d->n_blocks * (d->B - 1);
   if (P == 0) return hipSuccess;
@@ -267,8 +267,17 @@ hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z
   GridProblem g{};
   g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.H = H; g.dtype = dt;
   g.AB = L.AB; g.C = L.C; g.nq = dt == kDtypeBf16 ? 3 : 1; g.b1 = w->b1; g.w2 = w->w2; g.b2 = w->b2;
-  g.cand_logits = cl; g.S = S;
+  g.cand_logits = cl; g.S = S; g.best = best;
   return launch_grid(g, st);
+}
+
+// The greedy walk after the grid: from the grid's argmax table when the block
+// fits the table walk, else from S.
+hipError_t walk_after_grid(const float* S, const int32_t* best, const float* cl, const int32_t* ids,
+                           const dcoco_dims* d, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st) {
+  if (best != nullptr)
+    return launch_walk_table(best, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
+  return launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
 }
 
 hipError_t run_score(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* s,
@@ -769,7 +778,7 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   const size_t RK = static_cast<size_t>(R) * d->K;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
   auto layout = [&](Carve& c, void** topk_ws, int32_t** ids, float** cl, RepLayout* L, void** z,
-                    float** s, float** S, ScoreLayout* SL) {
+                    float** s, float** S, ScoreLayout* SL, int32_t** best) {
     *topk_ws = c.take(topk_workspace_bytes(dt, R, d->V, d->K));
     *ids = static_cast<int32_t*>(c.take(sizeof(int32_t) * RK));
     *cl = static_cast<float*>(c.take(sizeof(float) * RK));
@@ -778,11 +787,14 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
     *s = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_pair));
     *S = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->K * d->K));
     *SL = carve_score(c, d);
+    *best = walk_table_supported(d->B, d->K) && P > 0
+                ? static_cast<int32_t*>(c.take(sizeof(int32_t) * P * d->K)) : nullptr;
   };
   void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* S; ScoreLayout SL;
+  int32_t* best;
   {
     Carve c(nullptr);
-    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
+    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL, &best);
     rc = check_ws(workspace, workspace_bytes, c.off);
     if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
   }
@@ -791,7 +803,7 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (!opt_ok(sel_idx) || !opt_ok(S_out) || !opt_ok(cand_ids_out) || !opt_ok(cand_logits_out))
     return DCOCO_ERR_INVALID_ARG;
   Carve cw(workspace);
-  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
+  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL, &best);
   if (cand_ids_out) ids = cand_ids_out;
   if (cand_logits_out) cl = cand_logits_out;
   if (S_out) S = S_out;
@@ -803,8 +815,8 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
   if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
-  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st);
-  if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
+  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best);
+  if (e == hipSuccess) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
   return hip_status(e);
 }
 
@@ -855,7 +867,7 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
   const size_t RK = static_cast<size_t>(R) * d->K;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
   auto layout = [&](Carve& c, void** topk_ws, int32_t** ids, float** cl, RepLayout* L, void** z,
-                    float** s, float** S, ScoreLayout* SL) {
+                    float** s, float** S, ScoreLayout* SL, int32_t** best) {
     *topk_ws = c.take(topk_workspace_bytes(dt, R, d->V, d->K));
     *ids = static_cast<int32_t*>(c.take(sizeof(int32_t) * RK));
     *cl = static_cast<float*>(c.take(sizeof(float) * RK));
@@ -864,11 +876,14 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
     *s = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->d_pair));
     *S = static_cast<float*>(c.take(sizeof(float) * (P ? P : 1) * d->K * d->K));
     *SL = carve_score(c, d);
+    *best = walk_table_supported(d->B, d->K) && P > 0
+                ? static_cast<int32_t*>(c.take(sizeof(int32_t) * P * d->K)) : nullptr;
   };
   void* topk_ws; int32_t* ids; float* cl; RepLayout L; void* z; float* s; float* S; ScoreLayout SL;
+  int32_t* best;
   {
     Carve c(nullptr);
-    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
+    layout(c, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL, &best);
     rc = check_ws(workspace, workspace_bytes, c.off);
     if (rc != DCOCO_OK) return rc > 0 ? DCOCO_OK : rc;
   }
@@ -878,7 +893,7 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
   if (!opt_ok(sel_idx) || !opt_ok(S_out) || !opt_ok(cand_ids_out) || !opt_ok(cand_logits_out))
     return DCOCO_ERR_INVALID_ARG;
   Carve cw(workspace);
-  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL);
+  layout(cw, &topk_ws, &ids, &cl, &L, &z, &s, &S, &SL, &best);
   if (cand_ids_out) ids = cand_ids_out;
   if (cand_logits_out) cl = cand_logits_out;
   if (S_out) S = S_out;
@@ -890,8 +905,8 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
   if (e == hipSuccess)
     e = launch_gather_gemm(btable, ids, d->V - 1, static_cast<int>(RK), r, w->W_f, 2ll * r, 0, d->d_z, z, L.gf,
                            d->K, st);
-  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st);
-  if (e == hipSuccess) e = launch_walk(S, cl, ids, d->n_blocks, d->B, d->K, sel_idx, sel_tok, st);
+  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best);
+  if (e == hipSuccess) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
   return hip_status(e);
 }
 

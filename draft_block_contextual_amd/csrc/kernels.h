@@ -90,6 +90,7 @@ struct GridProblem {
   float b2;
   const float* cand_logits;    // [N, B, K]
   float* S;                    // [N, B-1, K, K]
+  int32_t* best;               // [N, B-1, K] or null: argmax_b S_p(a, b) per row a
 };
 hipError_t launch_grid(const GridProblem& p, hipStream_t st);
 
@@ -98,6 +99,11 @@ hipError_t launch_split3(const float* s, long long n, void* s3, hipStream_t st);
 
 hipError_t launch_walk(const float* S, const float* cand_logits, const int32_t* cand_ids, int N,
                        int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
+// The same walk from the grid's per-row argmax table best [N, B-1, K]; false
+// from walk_table_supported means the block does not fit (use launch_walk).
+bool walk_table_supported(int B, int K);
+hipError_t launch_walk_table(const int32_t* best, const float* cand_logits, const int32_t* cand_ids, int N,
+                             int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st);
 
 // Whole-path rules: maximise sum_j lam^j sigma_j over all K^B paths (slot j
 // 0-based; sigma_0 = l_0(k_0), sigma_j = S_{j-1}(k_{j-1}, k_j)).

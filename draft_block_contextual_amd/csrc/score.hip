@@ -45,6 +45,7 @@ struct GridDev {
   float b2;
   const float* cand_logits;
   float* S;
+  int32_t* best;
 };
 
 // s -> three bf16 rows per pair (hi, mid, lo with s = hi + mid + lo exactly
@@ -296,13 +297,59 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
   __syncthreads();
   const float* lnext = g.cand_logits + (static_cast<long long>(n) * g.B + p + 1) * K;
   float* Sp = g.S + static_cast<long long>(np) * K * K;
-  for (int idx = tid; idx < K * K; idx += 256) {
-    const int a = idx / K;
-    const int b = idx - a * K;
-    const int o = a * KR + b;
-    float sum = red[o];
-    for (int sl = 1; sl < 4 * UPS; ++sl) sum += red[sl * KR * KR + o];
-    Sp[idx] = lnext[b] + (sum + g.b2);
+  constexpr int kPerT = (KR * KR + 255) / 256;
+  float sv[kPerT];
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < K * K) {
+      const int a = idx / K;
+      const int b = idx - a * K;
+      const int o = a * KR + b;
+      float sum = red[o];
+      for (int sl = 1; sl < 4 * UPS; ++sl) sum += red[sl * KR * KR + o];
+      sv[i] = lnext[b] + (sum + g.b2);
+      Sp[idx] = sv[i];
+    }
+  }
+  if (g.best == nullptr) return;
+  // the walk's step from each row a: argmax_b S_p(a, b) under the walk's rule
+  // (largest order key, the lowest b among equal keys; NaN never wins)
+  if constexpr (KR * KR <= 256) {
+    if (K == KR) {
+      // thread a K + b holds S_p(a, b) and each row fills an aligned group of
+      // KR lanes: a max over (key, KR - 1 - b) within the group decides
+      const int b = tid % KR;
+      const bool valid = tid < K * K;
+      uint64_t c = valid ? (static_cast<uint64_t>(order_key(sv[0])) << 32) | static_cast<uint32_t>(KR - 1 - b) : 0ull;
+#pragma unroll
+      for (int off = KR / 2; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(c, off, kWave);
+        c = o > c ? o : c;
+      }
+      if (valid && b == 0) g.best[static_cast<long long>(np) * K + tid / KR] = KR - 1 - static_cast<int>(c & 0xffu);
+      return;
+    }
+  }
+  __syncthreads();                     // every thread is done reading red
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < K * K) smem[idx] = sv[i];
+  }
+  __syncthreads();
+  if (tid < K) {
+    const float* row = smem + tid * K;
+    uint32_t bk = order_key(row[0]);
+    int bb = 0;
+    for (int b = 1; b < K; ++b) {
+      const uint32_t k = order_key(row[b]);
+      if (k > bk) {
+        bk = k;
+        bb = b;
+      }
+    }
+    g.best[static_cast<long long>(np) * K + tid] = bb;
   }
 }
 
@@ -411,6 +458,51 @@ walk_kernel(const float* __restrict__ S, const float* __restrict__ cl, const int
       }
     }
     if (p0 + batch >= Bm1) break;
+  }
+}
+
+// The walk from the grid's argmax table: k_1 = argmax of the first slot's
+// logits, then k_{p+1} = best_p(k_p).  One wave per block: the block's table is
+// staged in LDS with its loads all in flight, one lane follows the chain
+// (one LDS read per step), and the chosen ids are fetched in parallel.
+constexpr int kWalkTab = 8192;    // table entries staged: (B - 1) K
+constexpr int kWalkMaxB = 2048;   // slots per block
+
+__global__ void __launch_bounds__(kWave)
+walk_table_kernel(const int32_t* __restrict__ best, const float* __restrict__ cl, const int32_t* __restrict__ ids,
+                  int B, int K, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_tok) {
+  __shared__ int32_t sB[kWalkTab];
+  __shared__ int32_t sK[kWalkMaxB];
+  const int n = blockIdx.x;
+  const int l = lane_id();
+  const int nt = (B - 1) * K;
+  const int32_t* bn = best + static_cast<long long>(n) * nt;
+  for (int base = 0; base < nt; base += 8 * kWave) {
+    int32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = bn[min(base + j * kWave + l, nt - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (base + j * kWave + l < nt) sB[base + j * kWave + l] = v[j];
+  }
+  const float c0 = cl[static_cast<long long>(n) * B * K + (l < K ? l : 0)];
+  int k = wave_argmax(c0, l < K);
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+  if (l == 0) {
+    sK[0] = k;
+    for (int p = 0; p + 1 < B; ++p) {
+      k = min(max(sB[p * K + k], 0), K - 1);   // in range by construction; kept so
+      sK[p + 1] = k;                            // no table value can index outside
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+  for (int j = l; j < B; j += kWave) {
+    const int kj = sK[j];
+    const long long o = static_cast<long long>(n) * B + j;
+    if (sel_idx) sel_idx[o] = kj;
+    sel_tok[o] = ids[o * K + kj];
   }
 }
 
@@ -537,7 +629,7 @@ hipError_t launch_grid_t(const GridProblem& q, hipStream_t st) {
   GridDev g;
   g.N = q.N; g.B = q.B; g.K = q.K; g.H = q.H; g.P = q.N * (q.B - 1); g.nq = q.nq;
   g.AB = q.AB; g.C = q.C; g.b1 = q.b1; g.w2 = q.w2; g.b2 = q.b2;
-  g.cand_logits = q.cand_logits; g.S = q.S;
+  g.cand_logits = q.cand_logits; g.S = q.S; g.best = q.best;
   const int blocks = q.N * (q.B - 1);
   if (blocks <= 0) return hipSuccess;
 #define DCOCO_GRID(KRV, TAV) hipLaunchKernelGGL((grid_kernel<T, GridShape<KRV, TAV>>), dim3(blocks), dim3(256), 0, st, g)
@@ -579,6 +671,19 @@ hipError_t launch_split3(const float* s, long long n, void* s3, hipStream_t st) 
 hipError_t launch_walk(const float* S, const float* cand_logits, const int32_t* cand_ids, int N,
                        int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st) {
   hipLaunchKernelGGL(walk_kernel, dim3(N), dim3(256), 0, st, S, cand_logits, cand_ids, B, K, sel_idx,
+                     sel_tok);
+  return hipGetLastError();
+}
+
+bool walk_table_supported(int B, int K) {
+  return B >= 1 && K >= 1 && K <= kWave && B <= kWalkMaxB && static_cast<long long>(B - 1) * K <= kWalkTab;
+}
+
+hipError_t launch_walk_table(const int32_t* best, const float* cand_logits, const int32_t* cand_ids, int N,
+                             int B, int K, int32_t* sel_idx, int32_t* sel_tok, hipStream_t st) {
+  if (!walk_table_supported(B, K)) return hipErrorInvalidValue;
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(walk_table_kernel, dim3(N), dim3(kWave), 0, st, best, cand_logits, cand_ids, B, K, sel_idx,
                      sel_tok);
   return hipGetLastError();
 }

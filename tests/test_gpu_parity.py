@@ -465,6 +465,41 @@ def test_full_rows_max_sampled():
     _full_size("rows_max", (0, 2047, 4094))
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "widez_bf16", "k64_small", "small_f32", "mid_f32"])
+def test_correct_block_walk_ties(name):
+    # w2 = 0 and logits on a coarse grid: every row of S_p is l_{p+1}(b) + b2,
+    # with many equal values, so each step's argmax is decided by the lowest
+    # index among ties.  The walk inside dcoco_correct_block must equal the
+    # oracle's walk on the returned S, and dcoco_select's walk on the same S.
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case correct_block walk ties {name}", flush=True)
+    inp = dict(_inputs(name))
+    D = inp["dims"]
+    zero = np.zeros_like(np.asarray(inp["w2"]))
+    inp["w2"] = zero
+    lg = O.to_f64(inp["logits"], D.dtype)
+    coarse = np.round(lg)                       # few distinct values per row
+    inp["logits"] = synth.f32_to_bf16_bits(coarse.astype(np.float32)) if D.dtype == "bf16" else coarse.astype(np.float32)
+    dims, w, logits, h, E = device_inputs(inp)
+    out = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    torch.cuda.synchronize()
+    out = {k: _np(v) for k, v in out.items()}
+    N, B, K = out["cand_ids"].shape
+    ri, rt, _ = O.greedy_walk(out["S"].astype(np.float64), out["cand_logits"].astype(np.float64), out["cand_ids"])
+    np.testing.assert_array_equal(out["sel_idx"], ri)
+    np.testing.assert_array_equal(out["sel_tok"], rt)
+    S = torch.from_numpy(out["S"]).cuda()
+    cl = torch.from_numpy(out["cand_logits"]).cuda()
+    ids = torch.from_numpy(out["cand_ids"]).cuda()
+    si, st = dc.select(dims, S, cl, ids)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(si), out["sel_idx"])
+    # candidates are sorted, so index 0 is always among a row's maxima and the
+    # lowest index among equal maxima is 0 at every step
+    assert np.all(out["sel_idx"] == 0)
+
+
 def test_degenerate_shapes_select_the_drafter():
     # B = 1: no transitions, every slot keeps the drafter's top-1; K = 1: the
     # only candidate is chosen whatever the scores
@@ -995,14 +1030,16 @@ def test_full_q8b_32_lm_head_sampled():
 
 # ------------------------------------------------------ top-K stress rows
 
-@pytest.mark.parametrize("kind", ["ramp_up", "ramp_down", "constant", "ramp_up_noisy"])
-def test_topk_stress_rows(kind):
+@pytest.mark.parametrize("kind,K", [("ramp_up", 16), ("ramp_down", 16), ("constant", 16), ("ramp_up_noisy", 16),
+                                    ("normal", 16), ("normal", 64), ("normal", 1)])
+def test_topk_stress_rows(kind, K):
     # rows that defeat a sampled threshold: every later element above it
-    # (rising), all elements tied (constant); the result must stay exact
+    # (rising), all elements tied (constant); plain N(0, 2^2) rows, whose K-th
+    # largest bf16 value is usually tied with others; the result must stay exact
     import draft_block_contextual_amd as dc
     import torch
-    print(f"case topk stress {kind}", flush=True)
-    R, V, K = 24, 151936, 16
+    print(f"case topk stress {kind} K={K}", flush=True)
+    R, V = 24, 151936
     x = np.linspace(-12, 12, V)
     if kind == "ramp_down":
         x = x[::-1]
@@ -1011,6 +1048,8 @@ def test_topk_stress_rows(kind):
     rows = np.tile(x, (R, 1))
     if kind == "ramp_up_noisy":
         rows = rows + np.random.default_rng(70).standard_normal((R, V)) * 0.5
+    if kind == "normal":
+        rows = np.random.default_rng(71 + K).standard_normal((R, V)) * 2.0
     bits = synth.f32_to_bf16_bits(rows.astype(np.float32))
     dims = dc.Dims(1, R, K, V, 32, 32, 32, 32, 32, 32, "bf16")
     ids, vals = dc.topk(dims, to_dev(bits, "bf16"))
