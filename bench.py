@@ -128,7 +128,7 @@ def stored_traffic(kernel, digest):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(blocks are independent; sharding would split the streams).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
