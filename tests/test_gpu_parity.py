@@ -500,6 +500,26 @@ def test_correct_block_walk_ties(name):
     assert np.all(out["sel_idx"] == 0)
 
 
+@pytest.mark.parametrize("B,K", [(2100, 2), (300, 32)])
+def test_correct_block_walk_fallback_shapes(B, K):
+    # blocks too large for the walk over the grid's argmax table (more than
+    # 2048 slots, or more than 8192 table entries) take the walk over S; the
+    # result must still be the oracle's walk on the returned scores
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case correct_block walk fallback B={B} K={K}", flush=True)
+    cfg = synth.Config(f"fallback_{B}_{K}", synth._d(1, B, K, 3001, 64, 64, 32, 32, 32, 64, "bf16"),
+                       30.0, "peaks", K, 2100 + K, "random")
+    inp = synth.make_inputs(cfg)
+    dims, w, logits, h, E = device_inputs(inp)
+    out = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    torch.cuda.synchronize()
+    out = {k: _np(v) for k, v in out.items()}
+    ri, rt, _ = O.greedy_walk(out["S"].astype(np.float64), out["cand_logits"].astype(np.float64), out["cand_ids"])
+    np.testing.assert_array_equal(out["sel_idx"], ri)
+    np.testing.assert_array_equal(out["sel_tok"], rt)
+
+
 def test_degenerate_shapes_select_the_drafter():
     # B = 1: no transitions, every slot keeps the drafter's top-1; K = 1: the
     # only candidate is chosen whatever the scores
