@@ -124,6 +124,9 @@ def test_topk_ties_and_special_values(dtype, V, K):
     got = vals.cpu().numpy().astype(np.float64)
     np.testing.assert_array_equal(np.isnan(got), np.isnan(ref_vals))
     np.testing.assert_array_equal(got[~np.isnan(got)], ref_vals[~np.isnan(ref_vals)])
+    # the values are the logits themselves: a -0 stays -0 (equal keys, so the
+    # id decides the order, but the value written must keep its sign)
+    np.testing.assert_array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(ref_vals[~np.isnan(ref_vals)]))
 
 
 # ------------------------------------------------------------------- walk
