@@ -509,7 +509,9 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
   p.A = static_cast<const char*>(q.A);
   p.lda = q.lda;
   p.a_rows = q.a_rows;
-  p.a_rows_max = q.a_rows_max > 0 ? q.a_rows_max : 0x7fffffff;
+  // gathered rows are always clamped into [0, a_rows_max] (0 is a valid
+  // maximum: a one-row table); without a gather the clamp is never read
+  p.a_rows_max = q.a_rows ? (q.a_rows_max > 0 ? q.a_rows_max : 0) : 0x7fffffff;
   p.w0 = static_cast<const char*>(q.w[0]);
   p.w1 = static_cast<const char*>(q.w[1] ? q.w[1] : q.w[0]);
   p.w2 = static_cast<const char*>(q.w[2] ? q.w[2] : q.w[0]);

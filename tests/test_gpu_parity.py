@@ -337,6 +337,44 @@ def test_represent_matches_oracle(name):
         np.testing.assert_allclose(s, ref["s"], rtol=1e-4, atol=1e-3)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_represent_clamps_ids_of_a_one_row_table(dtype):
+    # V = 1: every id is clamped to the table's only row, so ids past either
+    # end give exactly the result of id 0 (forward, and the backward's
+    # recomputed forward and gathered rows)
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case represent V=1 {dtype}", flush=True)
+    N, B, K, d, r = 2, 3, 1, 64, 32
+    dims = dc.Dims(N, B, K, 1, d, d, r, r, r, 32, dtype)
+    g = np.random.default_rng(80)
+
+    def mat(*shape, scale=0.1):
+        x = (g.standard_normal(shape) * scale).astype(np.float32)
+        return to_dev(synth.f32_to_bf16_bits(x) if dtype == "bf16" else x, dtype)
+
+    w = dc.Weights(P_e=mat(r, d), P_h=mat(r, d), W_f=mat(r, 2 * r), W_pair=mat(r, 2 * d), W1=None, b1=None,
+                   w2=None, b2=0.0)
+    h = mat(N, B, d, scale=30.0)
+    E = mat(1, d, scale=0.02)
+    zero = torch.zeros((N, B, K), dtype=torch.int32, device="cuda")
+    bad = torch.tensor([[[5], [-3], [1]], [[1 << 20], [-(1 << 30)], [0]]], dtype=torch.int32, device="cuda")
+    z0, s0 = dc.represent(dims, w, h, E, zero)
+    z1, s1 = dc.represent(dims, w, h, E, bad)
+    torch.cuda.synchronize()
+    assert torch.equal(z0.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       z1.view(torch.int16 if dtype == "bf16" else torch.int32))
+    assert torch.equal(s0, s1)
+    if dtype == "bf16":
+        dz = torch.randn((N, B, K, r), device="cuda")
+        ds = torch.randn((N, B - 1, r), device="cuda")
+        a = dc.represent_backward(dims, w, h, E, zero, dz, ds)
+        b = dc.represent_backward(dims, w, h, E, bad, dz, ds)
+        torch.cuda.synchronize()
+        for k in a:
+            assert torch.equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("name", ["tiny_bias", "small_bf16", "small_f32", "mid_bf16", "k64_small"])
 def test_score_matches_oracle(name):
     import draft_block_contextual_amd as dc
