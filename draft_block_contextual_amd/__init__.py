@@ -143,11 +143,22 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _resolve(stream):
+    """The torch stream a call runs on: the one given, else the current one."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream(stream):
+    return ctypes.c_void_p(_resolve(stream).cuda_stream)
+
+
+def _on(stream):
+    """Allocate under the stream the kernels run on, so that the caching
+    allocator hands a freed block to other work only after that stream's work
+    (the outputs and workspaces made here are used on that stream only)."""
+    import torch
+    return torch.cuda.stream(_resolve(stream))
 
 
 def _check(fn: str, rc: int):
@@ -160,20 +171,35 @@ def _torch_dtype(dtype: str):
     return torch.bfloat16 if dtype == "bf16" else torch.float32
 
 
+# One cached workspace per (device, stream), allocated on that stream: a
+# replaced buffer is released to the caching allocator on the stream that
+# used it, so it is reused only after that stream's queued work.
 _ws_cache: dict = {}
+_WS_STREAMS = 8
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _workspace(nbytes: int, device, workspace=None, stream=None):
     import torch
     if workspace is not None:
         return workspace
-    key = (str(device), nbytes)
+    st = _resolve(stream)
+    key = (str(device), st.cuda_stream)
     ws = _ws_cache.get(key)
-    if ws is None:
-        _ws_cache.clear()
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws is None or ws.numel() < nbytes:
+        _ws_cache.pop(key, None)
+        if len(_ws_cache) >= _WS_STREAMS:
+            _ws_cache.pop(next(iter(_ws_cache)))
+        with torch.cuda.stream(st):
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
+
+
+def _empty(stream, *shape_args, **kw):
+    """torch.empty allocated under the call's stream (see _on)."""
+    import torch
+    with _on(stream):
+        return torch.empty(*shape_args, **kw)
 
 
 def _query(fn, *args) -> int:
@@ -190,11 +216,11 @@ def topk(dims: Dims, logits, cand_ids=None, cand_logits=None, workspace=None, st
     R = dims.n_blocks * dims.B
     dev = logits.device
     if cand_ids is None:
-        cand_ids = torch.empty((R, dims.K), dtype=torch.int32, device=dev)
+        cand_ids = _empty(stream, (R, dims.K), dtype=torch.int32, device=dev)
     if cand_logits is None:
-        cand_logits = torch.empty((R, dims.K), dtype=torch.float32, device=dev)
+        cand_logits = _empty(stream, (R, dims.K), dtype=torch.float32, device=dev)
     need = _query(lib.dcoco_topk, ctypes.byref(cd), _ptr(logits), _ptr(cand_ids), _ptr(cand_logits))
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_topk", lib.dcoco_topk(ctypes.byref(cd), _ptr(logits), _ptr(cand_ids), _ptr(cand_logits),
                                         _ptr(ws), ctypes.byref(n), _stream(stream)))
@@ -208,12 +234,12 @@ def represent(dims: Dims, w: Weights, h, E, cand_ids, z=None, s=None, workspace=
     cd, cw = dims.c(), w.c()
     dev = h.device
     if z is None:
-        z = torch.empty((dims.n_blocks, dims.B, dims.K, dims.d_z), dtype=_torch_dtype(dims.dtype), device=dev)
+        z = _empty(stream, (dims.n_blocks, dims.B, dims.K, dims.d_z), dtype=_torch_dtype(dims.dtype), device=dev)
     if s is None:
-        s = torch.empty((dims.n_blocks, max(dims.B - 1, 1), dims.d_pair), dtype=torch.float32, device=dev)
+        s = _empty(stream, (dims.n_blocks, max(dims.B - 1, 1), dims.d_pair), dtype=torch.float32, device=dev)
     args = (ctypes.byref(cd), ctypes.byref(cw), _ptr(h), _ptr(E), _ptr(cand_ids), _ptr(z), _ptr(s))
     need = _query(lib.dcoco_represent, *args)
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_represent", lib.dcoco_represent(*args, _ptr(ws), ctypes.byref(n), _stream(stream)))
     return z, s[:, :dims.B - 1]
@@ -226,10 +252,10 @@ def score(dims: Dims, w: Weights, z, s, cand_logits, S=None, workspace=None, str
     cd, cw = dims.c(), w.c()
     dev = z.device
     if S is None:
-        S = torch.empty((dims.n_blocks, max(dims.B - 1, 1), dims.K, dims.K), dtype=torch.float32, device=dev)
+        S = _empty(stream, (dims.n_blocks, max(dims.B - 1, 1), dims.K, dims.K), dtype=torch.float32, device=dev)
     args = (ctypes.byref(cd), ctypes.byref(cw), _ptr(z), _ptr(s), _ptr(cand_logits), _ptr(S))
     need = _query(lib.dcoco_score, *args)
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_score", lib.dcoco_score(*args, _ptr(ws), ctypes.byref(n), _stream(stream)))
     return S[:, :dims.B - 1]
@@ -242,9 +268,9 @@ def select(dims: Dims, S, cand_logits, cand_ids, sel_idx=None, sel_tok=None, str
     cd = dims.c()
     dev = cand_logits.device
     if sel_idx is None:
-        sel_idx = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+        sel_idx = _empty(stream, (dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
     if sel_tok is None:
-        sel_tok = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+        sel_tok = _empty(stream, (dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
     _check("dcoco_select", lib.dcoco_select(ctypes.byref(cd), _ptr(S), _ptr(cand_logits), _ptr(cand_ids),
                                             _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
     return sel_idx, sel_tok
@@ -262,9 +288,9 @@ def select_path(dims: Dims, S, cand_logits, cand_ids, rule: str = "greedy", lam:
     cd = dims.c()
     dev = cand_logits.device
     if sel_idx is None:
-        sel_idx = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+        sel_idx = _empty(stream, (dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
     if sel_tok is None:
-        sel_tok = torch.empty((dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
+        sel_tok = _empty(stream, (dims.n_blocks, dims.B), dtype=torch.int32, device=dev)
     _check("dcoco_select_path", lib.dcoco_select_path(ctypes.byref(cd), _ptr(S), _ptr(cand_logits),
                                                       _ptr(cand_ids), PATH_RULES[rule], float(lam),
                                                       _ptr(sel_idx), _ptr(sel_tok), _stream(stream)))
@@ -279,13 +305,13 @@ def lm_head_topk(dims: Dims, hd, W_lm, cand_ids=None, cand_logits=None, workspac
     dev = hd.device
     R = dims.n_blocks * dims.B
     if cand_ids is None:
-        cand_ids = torch.empty((R, dims.K), dtype=torch.int32, device=dev)
+        cand_ids = _empty(stream, (R, dims.K), dtype=torch.int32, device=dev)
     if cand_logits is None:
-        cand_logits = torch.empty((R, dims.K), dtype=torch.float32, device=dev)
+        cand_logits = _empty(stream, (R, dims.K), dtype=torch.float32, device=dev)
     n = ctypes.c_size_t(0)
     _check("dcoco_lm_head_topk", lib.dcoco_lm_head_topk(ctypes.byref(cd), None, None, None, None, None,
                                                         ctypes.byref(n), None))
-    ws = _workspace(n.value, dev, workspace)
+    ws = _workspace(n.value, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_lm_head_topk", lib.dcoco_lm_head_topk(ctypes.byref(cd), _ptr(hd), _ptr(W_lm), _ptr(cand_ids),
                                                         _ptr(cand_logits), _ptr(ws), ctypes.byref(n),
@@ -300,9 +326,9 @@ def loss(dims: Dims, S, cand_ids, target_tok, rho: float = 4.0, stream=None):
     cd = dims.c()
     dev = cand_ids.device
     Bm1 = max(dims.B - 1, 1)
-    out = torch.empty(4, dtype=torch.float32, device=dev)   # a 16-byte slot for the scalar
-    pair = torch.empty((dims.n_blocks, Bm1), dtype=torch.float32, device=dev)
-    dS = torch.empty((dims.n_blocks, Bm1, dims.K, dims.K), dtype=torch.float32, device=dev)
+    out = _empty(stream, 4, dtype=torch.float32, device=dev)   # a 16-byte slot for the scalar
+    pair = _empty(stream, (dims.n_blocks, Bm1), dtype=torch.float32, device=dev)
+    dS = _empty(stream, (dims.n_blocks, Bm1, dims.K, dims.K), dtype=torch.float32, device=dev)
     _check("dcoco_loss", lib.dcoco_loss(ctypes.byref(cd), _ptr(S), _ptr(cand_ids), _ptr(target_tok),
                                         float(rho), _ptr(out), _ptr(pair), _ptr(dS), _stream(stream)))
     return out[:1], pair[:, :dims.B - 1], dS[:, :dims.B - 1]
@@ -318,15 +344,15 @@ def score_backward(dims: Dims, w: Weights, z, s, dS, workspace=None, stream=None
     N, B, K = dims.n_blocks, dims.B, dims.K
     H, rz, rs = dims.d_mlp, dims.d_z, dims.d_pair
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"dz": torch.empty((N, B, K, rz), **f32), "ds": torch.empty((N, max(B - 1, 1), rs), **f32),
-           "d_cand_logits": torch.empty((N, B, K), **f32), "dW1": torch.empty((H, 2 * rz + rs), **f32),
-           "db1": torch.empty(H, **f32), "dw2": torch.empty(H, **f32), "db2": torch.empty(4, **f32)}
+    out = {"dz": _empty(stream, (N, B, K, rz), **f32), "ds": _empty(stream, (N, max(B - 1, 1), rs), **f32),
+           "d_cand_logits": _empty(stream, (N, B, K), **f32), "dW1": _empty(stream, (H, 2 * rz + rs), **f32),
+           "db1": _empty(stream, H, **f32), "dw2": _empty(stream, H, **f32), "db2": _empty(stream, 4, **f32)}
     g = CMlpGrads(out["dW1"].data_ptr(), out["db1"].data_ptr(), out["dw2"].data_ptr(), out["db2"].data_ptr())
     n = ctypes.c_size_t(0)
     _check("dcoco_score_backward", lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), None, None, None,
                                                             None, None, None, ctypes.byref(g), None,
                                                             ctypes.byref(n), None))
-    ws = _workspace(n.value, dev, workspace)
+    ws = _workspace(n.value, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_score_backward",
            lib.dcoco_score_backward(ctypes.byref(cd), ctypes.byref(cw), _ptr(z), _ptr(s), _ptr(dS),
@@ -349,16 +375,16 @@ def represent_backward(dims: Dims, w: Weights, h, E, cand_ids, dz, ds, want_dh: 
     N, B = dims.n_blocks, dims.B
     r, rs = dims.d_proj, dims.d_pair
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"dP_e": torch.empty((r, dims.d_embed), **f32), "dP_h": torch.empty((r, dims.d_hidden), **f32),
-           "dW_f": torch.empty((dims.d_z, 2 * r), **f32), "dW_pair": torch.empty((rs, 2 * dims.d_hidden), **f32)}
+    out = {"dP_e": _empty(stream, (r, dims.d_embed), **f32), "dP_h": _empty(stream, (r, dims.d_hidden), **f32),
+           "dW_f": _empty(stream, (dims.d_z, 2 * r), **f32), "dW_pair": _empty(stream, (rs, 2 * dims.d_hidden), **f32)}
     if want_dh:
-        out["dh"] = torch.empty((N, B, dims.d_hidden), **f32)
+        out["dh"] = _empty(stream, (N, B, dims.d_hidden), **f32)
     g = CRepGrads(out["dP_e"].data_ptr(), out["dP_h"].data_ptr(), out["dW_f"].data_ptr(), out["dW_pair"].data_ptr())
     n = ctypes.c_size_t(0)
     _check("dcoco_represent_backward",
            lib.dcoco_represent_backward(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, None,
                                         ctypes.byref(g), None, None, ctypes.byref(n), None))
-    ws = _workspace(n.value, dev, workspace)
+    ws = _workspace(n.value, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_represent_backward",
            lib.dcoco_represent_backward(ctypes.byref(cd), ctypes.byref(cw), _ptr(h), _ptr(E), _ptr(cand_ids),
@@ -385,10 +411,10 @@ def build_btable(dims: Dims, w: Weights, E, table=None, workspace=None, stream=N
     cd, cw = dims.c(), w.c()
     dev = E.device
     if table is None:
-        table = torch.empty((dims.V, dims.d_proj), dtype=torch.bfloat16, device=dev)
+        table = _empty(stream, (dims.V, dims.d_proj), dtype=torch.bfloat16, device=dev)
     args = (ctypes.byref(cd), ctypes.byref(cw), _ptr(E), _ptr(table))
     need = _query(lib.dcoco_build_btable, *args)
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     _check("dcoco_build_btable", lib.dcoco_build_btable(*args, _ptr(ws), ctypes.byref(n), _stream(stream)))
     return table
@@ -406,18 +432,18 @@ def correct_block(dims: Dims, w: Weights, logits, h, E, sel_tok=None, sel_idx=No
     dev = logits.device
     N, B, K = dims.n_blocks, dims.B, dims.K
     if sel_tok is None:
-        sel_tok = torch.empty((N, B), dtype=torch.int32, device=dev)
+        sel_tok = _empty(stream, (N, B), dtype=torch.int32, device=dev)
     if want_all:
         if sel_idx is None:
-            sel_idx = torch.empty((N, B), dtype=torch.int32, device=dev)
+            sel_idx = _empty(stream, (N, B), dtype=torch.int32, device=dev)
         if S is None:
-            S = torch.empty((N, max(B - 1, 1), K, K), dtype=torch.float32, device=dev)
+            S = _empty(stream, (N, max(B - 1, 1), K, K), dtype=torch.float32, device=dev)
         if cand_ids is None:
-            cand_ids = torch.empty((N, B, K), dtype=torch.int32, device=dev)
+            cand_ids = _empty(stream, (N, B, K), dtype=torch.int32, device=dev)
         if cand_logits is None:
-            cand_logits = torch.empty((N, B, K), dtype=torch.float32, device=dev)
+            cand_logits = _empty(stream, (N, B, K), dtype=torch.float32, device=dev)
     need = correct_block_workspace_bytes(dims, w, btable is not None)
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, stream)
     n = ctypes.c_size_t(ws.numel())
     fn = lib.dcoco_correct_block if btable is None else lib.dcoco_correct_block_btable
     src = E if btable is None else btable

@@ -83,7 +83,10 @@ typedef struct {
 } dcoco_dims;
 
 /* Corrector parameters, shared by every slot and transition ([P2] part 1,
- * paper Sec. 3.2).  Storage type = dims.dtype; b2 is passed by value.
+ * paper Sec. 3.2).  Storage type = dims.dtype; b2 is passed by value.  The
+ * MLP's activation is SiLU, the only one supported: the pages do not name
+ * the activation and SiLU is the reading taken, so no field selects it.
+ * Layout:
  *   P_e    [d_proj, d_embed]        candidate embedding projection
  *   P_h    [d_proj, d_hidden]       slot hidden-state projection
  *   W_f    [d_z, 2*d_proj]          fusion f; columns [b | g]
@@ -275,8 +278,16 @@ int dcoco_represent_backward(const dcoco_dims* dims, const dcoco_weights* w, con
                              const float* ds, const dcoco_rep_grads* grads, float* dh,
                              void* workspace, size_t* workspace_bytes, void* stream);
 
-/* The whole path for n_blocks draft blocks: top-K, representations, pair
- * states, transition scores and the greedy walk, on one stream.
+/* The whole corrector for n_blocks draft blocks, on one stream: top-K
+ * ([P1] "Keep the leading candidates"), representations and pair states
+ * ([P1] "Score neighboring candidates in parallel"; [P2] part 1, paper
+ * Sec. 3.2), transition scores (same passages) and the prefix-first greedy
+ * walk ([P1] "Select using the realized token identities"; [P2] part 2,
+ * paper Sec. 3.3).  It reads only what one drafter pass leaves behind (its
+ * logits and hidden states) plus the frozen embedding table and the
+ * corrector's own parameters, and returns the corrected block y_1..y_B
+ * ([P2] part 1: no extra drafter pass).  Each step is exactly the entry
+ * point of the same name above; the intermediates live in the workspace.
  *   logits [n_blocks*B, V], h [n_blocks, B, d_hidden], E [V, d_embed]: dtype
  *   sel_tok         [n_blocks, B] int32           out: the corrected block
  *   sel_idx         [n_blocks, B] int32           out, may be NULL
