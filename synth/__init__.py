@@ -156,6 +156,12 @@ CONFIGS = {
                        30.0, "peaks", 4, 2011, "random", "d_proj = d_z = d_pair = 2048 (the widest accepted)"),
     "rows_max": Config("rows_max", _d(4095, 16, 4, 1024, 64, 64, 32, 32, 32, 64, "bf16"),
                        30.0, "peaks", 4, 2012, "random", "65520 slot rows (the most accepted is 65535)"),
+    # several hidden-unit slabs per pair in the scoring grid: K = 32 in fp32,
+    # and K = 16 with H = 512 as in the Qwen3-8B-shaped workload
+    "k32_f32": Config("k32_f32", _d(2, 5, 32, 9000, 256, 256, 128, 128, 128, 320, "f32"),
+                      30.0, "peaks", 32, 2013, "random", "K = 32, H = 320 in fp32"),
+    "h512_bf16": Config("h512_bf16", _d(3, 6, 16, 7001, 256, 256, 128, 128, 128, 512, "bf16"),
+                        30.0, "peaks", 16, 2014, "random", "K = 16 with H = 512 on a small shape"),
     # LM-head shapes (head tied to E, so d == e): ragged vocabulary tiles,
     # ragged row tiles, rows without planted peaks (bf16 ties at the K-th)
     "lmh_small": Config("lmh_small", _d(2, 8, 16, 5003, 256, 256, 64, 64, 64, 64, "bf16"),
@@ -388,3 +394,63 @@ def to_float(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(a)
     return np.asarray(a, np.float32)
+
+
+def make_inputs_device(cfg: Config | str, seed: int | None = None, sets: int = 1, device="cuda:0") -> dict:
+    """The same recipe as ``make_inputs``, drawn on the GPU with torch's
+    seeded generator (Philox), for throughput runs at shapes whose host-side
+    draw would take minutes (the 4.3 GB embedding table of the d = 8192
+    workload).  The values follow the same distributions but are not the
+    numpy draws, so nothing is compared against the oracle with them.
+
+    Returns torch tensors on ``device`` (bf16 or fp32 per the config): E,
+    P_e, P_h, W_f, W_pair, W1, b1, w2, b2 (float), and ``sets`` independent
+    (logits [N*B, V], h [N, B, d]) pairs under "sets".
+    """
+    import torch
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    seed = cfg.seed if seed is None else seed
+    D = cfg.dims
+    dt = torch.bfloat16 if D.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device).manual_seed(seed)
+
+    def normal(shape, std):
+        return (torch.randn(shape, generator=gen, device=device) * std).to(dt)
+
+    def xavier(shape):
+        return normal(shape, float(np.sqrt(2.0 / (shape[0] + shape[1]))))
+
+    out = {"dims": D, "cfg": cfg}
+    E = torch.empty((D.V, D.e), dtype=dt, device=device)
+    step = max(1, (1 << 26) // D.e)
+    for r0 in range(0, D.V, step):
+        r1 = min(D.V, r0 + step)
+        E[r0:r1] = normal((r1 - r0, D.e), 0.02)
+    out["E"] = E
+    out["P_e"] = xavier((D.r, D.e))
+    out["P_h"] = xavier((D.r, D.d))
+    out["W_f"] = xavier((D.r_z, 2 * D.r))
+    out["W_pair"] = xavier((D.r_s, 2 * D.d))
+    out["W1"] = xavier((D.H, 2 * D.r_z + D.r_s))
+    out["b1"] = torch.zeros(D.H, dtype=dt, device=device)
+    out["w2"] = xavier((1, D.H))[0].contiguous()
+    out["b2"] = 0.0
+    R = D.n_blocks * D.B
+    P = cfg.n_peaks
+    peak_vals = 20.0 + 0.5 * torch.arange(P, device=device, dtype=torch.float32)
+    out["sets"] = []
+    for _ in range(sets):
+        h = normal((D.n_blocks, D.B, D.d), cfg.h_scale)
+        lg = torch.empty((R, D.V), dtype=dt, device=device)
+        for r0 in range(0, R, 64):
+            r1 = min(R, r0 + 64)
+            x = (torch.randn((r1 - r0, D.V), generator=gen, device=device) * 2.0).clamp_(-12.0, 12.0)
+            if P:
+                # P distinct random ids per row, given the planted values in a random order
+                pos = torch.rand((r1 - r0, D.V), generator=gen, device=device).topk(P, dim=1).indices
+                order = torch.rand((r1 - r0, P), generator=gen, device=device).argsort(dim=1)
+                x.scatter_(1, pos, peak_vals[order])
+            lg[r0:r1] = x.to(dt)
+        out["sets"].append((lg, h))
+    return out
