@@ -93,21 +93,30 @@ struct GridShape {
   static constexpr int STR = HS + 4;             // LDS row stride (floats)
   static constexpr int ARR = KR * STR;
   static constexpr int NLD = KR * HS / 4 / 256;  // float4 per thread per operand and slab
-  static constexpr int kRed = 4 * UPS * KR * KR;
-  static constexpr int kSmem = (4 * ARR > kRed ? 4 * ARR : kRed) + 4 * HS;
+  static constexpr int kRed = 4 * UPS * KR * KR;  // partial sums to add at the end
+  // LDS floats with partial sums of ACC_BYTES each (the reduction reuses the
+  // slab arrays and the per-unit terms once the last slab is done)
+  template <int ACC_BYTES>
+  static constexpr int smem_floats() {
+    return (4 * ARR > kRed * ACC_BYTES / 4 ? 4 * ARR : kRed * ACC_BYTES / 4) + 4 * HS;
+  }
   static_assert(LPU * UPS == kWave && NLD * 1024 == KR * HS, "grid shape");
-  static_assert(kRed <= kSmem, "reduction fits");
 };
 
+// The fp32 path adds its terms in fp64: a pair's terms can be hundreds of
+// times larger than the score they sum to (large pre-activations of opposite
+// signs), and fp32 running sums would then lose the score's low digits.  Each
+// term is still formed in fp32.
 template <typename T, typename GS>
 __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
+  using Acc = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
   constexpr int KR = GS::KR;
   constexpr int TA = GS::TA;
   constexpr int HS = GS::HS;
   constexpr int STR = GS::STR;
   constexpr int NLD = GS::NLD;
   constexpr int UPS = GS::UPS;
-  __shared__ __align__(16) float smem[GS::kSmem];
+  __shared__ __align__(16) float smem[GS::template smem_floats<sizeof(Acc)>()];
   __shared__ int s_slow[2];
   float* arr0 = smem;                 // 2^A'  (or A')
   float* arr1 = smem + GS::ARR;       // w'A'
@@ -171,11 +180,11 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
     }
   };
 
-  float acc[TA][TA];
+  Acc acc[TA][TA];
 #pragma unroll
   for (int i = 0; i < TA; ++i)
 #pragma unroll
-    for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < TA; ++j) acc[i][j] = 0;
 
   stage_c(0, 0);
   fetch(0);
@@ -261,7 +270,10 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
             for (int j = 0; j < TA; ++j) {
               const float den = fmaf(ea[i][c], eb[j][c], 1.0f);
               const float r = __builtin_amdgcn_rcpf(den);
-              acc[i][j] = fmaf(wa[i][c] + wb[j][c], r, acc[i][j]);
+              if constexpr (std::is_same<Acc, float>::value)
+                acc[i][j] = fmaf(wa[i][c] + wb[j][c], r, acc[i][j]);
+              else
+                acc[i][j] += static_cast<Acc>((wa[i][c] + wb[j][c]) * r);
             }
       }
     } else {
@@ -281,14 +293,17 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
             for (int j = 0; j < TA; ++j) {
               const float t = av[i][c] + bv[j][c];
               const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-              acc[i][j] = fmaf(wq[c], t * r, acc[i][j]);
+              if constexpr (std::is_same<Acc, float>::value)
+                acc[i][j] = fmaf(wq[c], t * r, acc[i][j]);
+              else
+                acc[i][j] += static_cast<Acc>(wq[c] * (t * r));
             }
       }
     }
     __syncthreads();
   }
   // ---- add the 4 UPS partial sums per output in a fixed order
-  float* red = smem;
+  Acc* red = reinterpret_cast<Acc*>(smem);
   const int slot = wv * UPS + grp;
 #pragma unroll
   for (int i = 0; i < TA; ++i)
@@ -306,9 +321,9 @@ __global__ void __launch_bounds__(256) grid_kernel(GridDev g) {
       const int a = idx / K;
       const int b = idx - a * K;
       const int o = a * KR + b;
-      float sum = red[o];
+      Acc sum = red[o];
       for (int sl = 1; sl < 4 * UPS; ++sl) sum += red[sl * KR * KR + o];
-      sv[i] = lnext[b] + (sum + g.b2);
+      sv[i] = lnext[b] + static_cast<float>(sum + static_cast<Acc>(g.b2));
       Sp[idx] = sv[i];
     }
   }

@@ -67,6 +67,45 @@ def s_tolerance_ok(S_gpu: np.ndarray, S_ref: np.ndarray, dtype: str):
     return not bad.any(), float(np.nanmax(diff)) if diff.size else 0.0, int(bad.sum())
 
 
+def score_magnitude(z, s, cand_vals, W1, b1, w2, b2):
+    """M[n, p, a, b]: the size of what an evaluation of S_p(a, b) adds up,
+    |l| + |b2| + sum_h |w2_h| (|SiLU(u_h)| + |SiLU'(u_h)| sum_j |W1[h, j] x_j|)
+    with x = [z_{p,a}; z_{p+1,b}; s_p] and u = W1 x + b1 (float64).  A first-
+    order rounding analysis of any fp32 evaluation bounds its error by
+    n 2^-24 M, n = 2 r_z + r_s + H (the lengths of the two sums)."""
+    z = np.asarray(z, np.float64)
+    N, B, K, rz = z.shape
+    W1 = np.asarray(W1, np.float64)
+    Wa, Wb, Ws = W1[:, :rz], W1[:, rz:2 * rz], W1[:, 2 * rz:]
+    M = np.empty((N, B - 1, K, K))
+    for n in range(N):
+        for p in range(B - 1):
+            A, Bv, C = z[n, p] @ Wa.T, z[n, p + 1] @ Wb.T, s[n, p] @ Ws.T + b1
+            aA, aB, aC = np.abs(z[n, p]) @ np.abs(Wa).T, np.abs(z[n, p + 1]) @ np.abs(Wb).T, np.abs(s[n, p]) @ np.abs(Ws).T
+            u = A[:, None, :] + Bv[None, :, :] + C
+            with np.errstate(over="ignore"):
+                sig = 1.0 / (1.0 + np.exp(-u))
+            dsilu = sig * (1.0 + u * (1.0 - sig))
+            absx = aA[:, None, :] + aB[None, :, :] + aC
+            M[n, p] = (np.abs(cand_vals[n, p + 1])[None, :] + abs(b2)
+                       + (np.abs(w2) * (np.abs(u * sig) + np.abs(dsilu) * absx)).sum(-1))
+    return M
+
+
+def s_tolerance_cancelling(S_gpu, S_ref, M, n_terms, frac=0.99):
+    """fp32 scores whose terms cancel far below their magnitude M: every
+    element within max(1e-4 max(1, |S|), n_terms 2^-24 M), and at least `frac`
+    of them within 1e-4 max(1, |S|).  Returns (ok, worst, count outside the
+    relative bar, count outside both)."""
+    diff = np.abs(S_gpu.astype(np.float64) - S_ref)
+    rel = S_REL_F32 * np.maximum(1.0, np.abs(S_ref))
+    cond = n_terms * 2.0 ** -24 * M
+    out_rel = ~(diff <= rel)
+    out_all = ~(diff <= np.maximum(rel, cond))
+    ok = (not out_all.any()) and out_rel.mean() <= 1.0 - frac
+    return ok, float(np.nanmax(diff)), int(out_rel.sum()), int(out_all.sum())
+
+
 def lockstep_path_check(S_gpu, S_ref, cand_vals, sel_gpu, sel_ref):
     """Walk the GPU and oracle paths in lockstep.  At each step where both
     paths share the predecessor, the chosen successor must agree whenever the
