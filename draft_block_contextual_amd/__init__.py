@@ -24,8 +24,8 @@ DTYPE_CODE = {"f32": 0, "bf16": 1}
 # every entry point include/dcoco.h declares
 EXPORTS = ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
            "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_represent_backward",
-           "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable",
-           "dcoco_status_string", "dcoco_abi_version"]
+           "dcoco_correct_block", "dcoco_correct_block_static", "dcoco_build_btable",
+           "dcoco_correct_block_btable", "dcoco_static_scratch_bytes", "dcoco_status_string", "dcoco_abi_version"]
 
 
 class DcocoError(RuntimeError):
@@ -81,11 +81,15 @@ def load() -> ctypes.CDLL:
     lib.dcoco_score_backward.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, ctypes.POINTER(CMlpGrads), vp, sz, vp]
     lib.dcoco_represent_backward.argtypes = [pd, pw, vp, vp, vp, vp, vp, ctypes.POINTER(CRepGrads), vp, vp, sz, vp]
     lib.dcoco_correct_block.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
+    lib.dcoco_correct_block_static.argtypes = [pd, pw, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dcoco_static_scratch_bytes.argtypes = []
+    lib.dcoco_static_scratch_bytes.restype = ctypes.c_size_t
     lib.dcoco_build_btable.argtypes = [pd, pw, vp, vp, vp, sz, vp]
     lib.dcoco_correct_block_btable.argtypes = [pd, pw, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp]
     for f in ["dcoco_topk", "dcoco_represent", "dcoco_score", "dcoco_select", "dcoco_select_path",
               "dcoco_lm_head_topk", "dcoco_loss", "dcoco_score_backward", "dcoco_represent_backward",
-              "dcoco_correct_block", "dcoco_build_btable", "dcoco_correct_block_btable"]:
+              "dcoco_correct_block", "dcoco_correct_block_static", "dcoco_build_btable",
+              "dcoco_correct_block_btable"]:
         getattr(lib, f).restype = ctypes.c_int
     lib.dcoco_status_string.argtypes = [ctypes.c_int]
     lib.dcoco_status_string.restype = ctypes.c_char_p
@@ -460,3 +464,21 @@ def correct_block(dims: Dims, w: Weights, logits, h, E, sel_tok=None, sel_idx=No
     if cand_logits is not None:
         out["cand_logits"] = cand_logits
     return out
+
+
+def static_scratch_bytes() -> int:
+    """Size of the library's static per-GPU scratch buffer (dcoco_correct_block_static)."""
+    return int(load().dcoco_static_scratch_bytes())
+
+
+def correct_block_static(dims: Dims, w: Weights, logits, h, E, sel_tok, sel_idx=None, S=None, cand_ids=None,
+                         cand_logits=None, stream=None):
+    """dcoco_correct_block_static: the whole path with the intermediates in the
+    library's static scratch buffer.  Allocates nothing: every output is the
+    caller's (sel_tok required; the others may be None).  Calls that overlap
+    on one GPU race on the shared buffer."""
+    lib = load()
+    cd, cw = dims.c(), w.c()
+    _check("dcoco_correct_block_static", lib.dcoco_correct_block_static(
+        ctypes.byref(cd), ctypes.byref(cw), _ptr(logits), _ptr(h), _ptr(E), _ptr(sel_tok), _ptr(sel_idx), _ptr(S),
+        _ptr(cand_ids), _ptr(cand_logits), _stream(stream)))

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -520,11 +521,39 @@ hipError_t run_rep_backward(const dcoco_dims* d, const dcoco_weights* w, const v
   return wgrad_run(p, false, &o, 1, L.part, L.part_floats, st);
 }
 
+// ---- the static scratch buffer of dcoco_correct_block_static
+
+// One buffer per GPU, in the library's code object (each device that loads the
+// library holds its own copy until the process ends).  Host code never uses
+// this name as an address: the device address comes from hipGetSymbolAddress.
+__device__ __align__(256) char scratch[DCOCO_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch`, looked up once per device
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DCOCO_ERR_HIP;
+  if (dev >= kMaxDevices) return DCOCO_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DCOCO_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DCOCO_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 105; }
+int dcoco_abi_version(void) { return 106; }
+
+size_t dcoco_static_scratch_bytes(void) { return DCOCO_STATIC_SCRATCH_BYTES; }
 
 const char* dcoco_status_string(int status) {
   switch (status) {
@@ -818,6 +847,22 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best);
   if (e == hipSuccess) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
   return hip_status(e);
+}
+
+int dcoco_correct_block_static(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h,
+                               const void* E, int32_t* sel_tok, int32_t* sel_idx, float* S_out,
+                               int32_t* cand_ids_out, float* cand_logits_out, void* stream) {
+  // the size this call needs (a pure query: nothing is launched)
+  size_t need = 0;
+  int rc = dcoco_correct_block(d, w, nullptr, nullptr, nullptr, nullptr, &need, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, stream);
+  if (rc != DCOCO_OK) return rc;
+  if (need > DCOCO_STATIC_SCRATCH_BYTES) return DCOCO_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if ((rc = static_scratch(&ws)) != DCOCO_OK) return rc;
+  size_t have = DCOCO_STATIC_SCRATCH_BYTES;
+  return dcoco_correct_block(d, w, logits, h, E, ws, &have, sel_tok, sel_idx, S_out, cand_ids_out,
+                             cand_logits_out, stream);
 }
 
 int dcoco_build_btable(const dcoco_dims* d, const dcoco_weights* w, const void* E, void* table,

@@ -301,6 +301,29 @@ int dcoco_correct_block(const dcoco_dims* dims, const dcoco_weights* w,
                         int32_t* cand_ids_out, float* cand_logits_out,
                         void* stream);
 
+/* dcoco_correct_block with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The intermediates live in a static
+ * buffer of DCOCO_STATIC_SCRATCH_BYTES (96 MiB) inside the library, one per
+ * GPU, held from the library's load until the process ends; the call
+ * allocates nothing.  Arguments, outputs, ordering and results are those of
+ * dcoco_correct_block (the same kernels run).  A problem whose workspace
+ * (dcoco_correct_block's size query) exceeds the buffer returns
+ * DCOCO_ERR_UNSUPPORTED before anything is launched; the 32-stream
+ * B = 16, K = 16, d = 4096, V = 151936 workload fits.  Every call on one GPU
+ * uses that GPU's single buffer: calls that overlap in time on one GPU (two
+ * streams, two threads) race and corrupt each other's results; serialise
+ * them.  No part of the buffer needs to start at any value, so what an
+ * earlier call left there does not matter.  dcoco_static_scratch_bytes()
+ * returns the buffer's size. */
+#define DCOCO_STATIC_SCRATCH_BYTES (96u << 20)
+int dcoco_correct_block_static(const dcoco_dims* dims, const dcoco_weights* w,
+                               const void* logits, const void* h, const void* E,
+                               int32_t* sel_tok, int32_t* sel_idx, float* S_out,
+                               int32_t* cand_ids_out, float* cand_logits_out,
+                               void* stream);
+size_t dcoco_static_scratch_bytes(void);
+
 /* Table of normalised candidate projections, a re-association of step a2
  * beyond the per-call path: E is frozen and P_e fixed at inference ([P1]
  * "Score neighboring candidates in parallel"; [P2] part 1), so
@@ -332,7 +355,7 @@ const char* dcoco_status_string(int status);
 /* ABI version of this header (major * 100 + minor): 101 adds the table
  * entry points, 102 dcoco_select_path, 103 dcoco_loss and
  * dcoco_score_backward, 104 dcoco_lm_head_topk, 105
- * dcoco_represent_backward. */
+ * dcoco_represent_backward, 106 dcoco_correct_block_static. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus
