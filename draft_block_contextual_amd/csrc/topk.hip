@@ -158,7 +158,7 @@ topk_partial_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
           const int e = seg0 + (i * kWave + l) * kVec + j;
           if (key[i][j] > tk && e < V) {
             const int pos = atomicAdd(&s_cnt[w], 1);
-            wave_out[pos] = make_comp(key[i][j], static_cast<uint32_t>(e));
+            if (pos < K) wave_out[pos] = make_comp(key[i][j], static_cast<uint32_t>(e));
           }
         }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -296,8 +296,11 @@ __device__ __attribute__((noinline)) void exact_wave_bf16(const uint16_t* rowp, 
         const int e = seg0 + (i * kWave + l) * 8 + j;
         const int k = key_at(e);
         if (k > static_cast<int>(tk)) {
+          // fewer than K keys exceed tk when both passes read the same row;
+          // the guard keeps a row that changes under the call (a caller's
+          // race) from writing past the list
           const int pos = atomicAdd(cnt_slot, 1);
-          out[pos] = make_comp(static_cast<uint32_t>(k), static_cast<uint32_t>(e));
+          if (pos < K) out[pos] = make_comp(static_cast<uint32_t>(k), static_cast<uint32_t>(e));
         }
       }
   }
@@ -448,10 +451,12 @@ __device__ __forceinline__ bool row_collect(const uint16_t* rowp, int V, uint32_
   bool bad = false;
   for (int b = 0; b < nflag; b += kWave) {
     const bool act = b + l < nflag;
-    const int e0 = act ? flags[b + l] : 0;
+    // flags hold vector starts e0 < V (e0 + 8 <= V on the vector path); the
+    // clamp keeps every read inside the row whatever the list holds
+    const int e0 = act ? min(max(flags[b + l], 0), kVec ? V - 8 : V - 1) : 0;
     uint32_t w4[4];
     if constexpr (kVec) {
-      const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);   // e0 + 8 <= V
+      const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);
       w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
     } else {
 #pragma unroll
@@ -611,8 +616,10 @@ __device__ __forceinline__ void list_flush(const uint16_t* rowp, int V, int K, i
                                            const int32_t* flags, int& nflag, RunList& L, uint64_t* s_tmp) {
   for (int b = 0; b < nflag; b += kWave) {
     const bool act = b + l < nflag;
-    const int e0 = act ? flags[b + l] : 0;
-    const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);   // e0 + 8 <= V
+    // flagged vector starts satisfy e0 + 8 <= V; clamped so that every read
+    // stays inside the row whatever the list holds
+    const int e0 = act ? min(max(flags[b + l], 0), V - 8) : 0;
+    const uint4 v = *reinterpret_cast<const uint4*>(rowp + e0);
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
     list_merge(w4, e0, act, V, K, l, t0, L, s_tmp);
   }

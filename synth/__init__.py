@@ -453,4 +453,7 @@ def make_inputs_device(cfg: Config | str, seed: int | None = None, sets: int = 1
                 x.scatter_(1, pos, peak_vals[order])
             lg[r0:r1] = x.to(dt)
         out["sets"].append((lg, h))
+    # the draws ran on torch's current stream; finish them so that a caller
+    # reading these tensors on another stream sees the values
+    torch.cuda.synchronize(device)
     return out
