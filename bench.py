@@ -33,6 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 # fp32 vector issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-ops/s
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# a grid element costs 7 lane-op slots: fma, rcp (quarter rate: 4 slots), add, fma
+GRID_ELEM_PEAK = VALU_LANE_OPS / 7
 
 
 def parse():
@@ -45,7 +47,8 @@ def parse():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=64)
-    ap.add_argument("--sweep", action="store_true", help="also time 4/8/16 streams")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (1/4/8/16 streams, K = 64, d = 8192)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling HBM counters)")
     ap.add_argument("--no-btable", action="store_true", help="skip the table-path timing")
@@ -58,20 +61,27 @@ def parse():
 
 
 def algorithmic_work(D):
-    """Bytes and flops the method itself must move / compute per call."""
+    """Bytes and flops the method itself must move / compute per call, by
+    stage (weights read once per call)."""
     e = 2 if D.dtype == "bf16" else 4
     R = D.n_blocks * D.B
     RK = R * D.K
     P = D.n_blocks * (D.B - 1)
     w_params = (D.r * D.e + D.r * D.d + D.r_z * 2 * D.r + D.r_s * 2 * D.d
                 + D.H * (2 * D.r_z + D.r_s) + 2 * D.H)
-    return {
+    w = {
         "logit_bytes": R * D.V * e,
         "gather_bytes": RK * D.e * e,
         "h_bytes": R * D.d * e,
         "weight_bytes": w_params * e,
-        "mfma_flops": 2.0 * (RK * D.e * D.r + R * D.d * (D.r + 2 * D.r_s) + R * D.r * D.r_z
-                             + RK * D.r * D.r_z + 2 * RK * D.r_z * D.H),
+        # representation stage: P_e E[c], [P_h; W_L; W_R] h, and the fusion
+        # W_f [b; g] (its g half once per slot, its b half once per candidate)
+        "cand_flops": 2.0 * RK * D.e * D.r,
+        "slot_flops": 2.0 * R * D.d * (D.r + 2 * D.r_s),
+        "fuse_flops": 2.0 * (R * D.r * D.r_z + RK * D.r * D.r_z),
+        # scoring stage: W1a z and W1b z per candidate, W1s s_p per pair
+        "ab_flops": 2.0 * RK * D.r_z * 2 * D.H,
+        "pair_flops": 2.0 * P * D.r_s * D.H,
         # representation backward: P_e E[c] and P_h h again, dz W_f, dW_f,
         # dP_e, [dP_h; dW_pair] and dh (each product counted once)
         "rep_bwd_flops": 2.0 * (2 * RK * D.e * D.r + R * D.d * D.r + 2 * RK * D.r_z * 2 * D.r
@@ -79,6 +89,10 @@ def algorithmic_work(D):
         "grid_elems": P * D.K * D.K * D.H,
         "transitions": P * D.K * D.K,
     }
+    w["represent_flops"] = w["cand_flops"] + w["slot_flops"] + w["fuse_flops"]
+    w["score_mfma_flops"] = w["ab_flops"] + w["pair_flops"]
+    w["total_bytes"] = w["logit_bytes"] + w["gather_bytes"] + w["h_bytes"] + w["weight_bytes"]
+    return w
 
 
 def copy_calibration():
@@ -123,6 +137,128 @@ def stored_traffic(kernel, digest):
     if vals.get("source_digest") != digest or "hbm_bytes_per_launch" not in vals:
         return None
     return float(vals["hbm_bytes_per_launch"])
+
+
+KERNEL_SOURCES = ["topk.hip", "gemm.hip", "rep.hip", "score.hip", "api.cpp", "common.h", "dma.h", "kernels.h",
+                  "ln_tile.h", "select.h", "wave.h"]
+
+
+def stored_kernel_figures(name, digest):
+    """Per-kernel figures from a committed rocprofv3 summary
+    (profiles/<name>.md: lines '- <kernel>.<field>: <value>'), or None when the
+    file is missing or was taken from other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
+    if not os.path.exists(path):
+        return None
+    vals, figs = {}, {}
+    for line in open(path):
+        m = re.match(r"^- ([\w.]+): (\S+)$", line.strip())
+        if not m:
+            continue
+        key, v = m.group(1), m.group(2)
+        if "." in key:
+            k, f = key.split(".", 1)
+            figs.setdefault(k, {})[f] = float(v)
+        else:
+            vals[key] = v
+    if vals.get("source_digest") != digest:
+        return None
+    return figs
+
+
+def kernel_rooflines(figs, work):
+    """Each profiled kernel against the bound of its own work: algorithmic
+    bytes or flops per launch over its profiled duration, and the counters'
+    HBM bytes against the algorithmic ones where they were taken."""
+    bounds = {
+        # kernel key: (bound, algorithmic work per launch, unit)
+        "topk": ("hbm", work["logit_bytes"]),
+        "cand_gemm": ("mfma", work["cand_flops"]),
+        "slot_gemm": ("mfma", work["slot_flops"]),
+        "ab_gemm": ("mfma", work["ab_flops"]),
+        "pair_term": ("mfma", work["pair_flops"]),
+        "grid": ("alu", work["grid_elems"]),
+    }
+    out = {}
+    for k, f in figs.items():
+        us = f.get("us")
+        if us is None:
+            continue
+        e = {"us": us}
+        if k in bounds:
+            bound, amount = bounds[k]
+            rate = amount / (us * 1e-6)
+            if bound == "hbm":
+                e.update(bound="hbm", achieved_GBps=round(rate / 1e9, 1), frac=round(rate / 1e9 / HBM_PEAK_GBS, 4))
+            elif bound == "mfma":
+                e.update(bound="mfma", achieved_TFLOPs=round(rate / 1e12, 1),
+                         frac=round(rate / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+            else:
+                e.update(bound="alu", elems_per_s=round(rate, 1), frac=round(rate / GRID_ELEM_PEAK, 4))
+        if "hbm_bytes" in f:
+            e["hbm_bytes_per_launch"] = f["hbm_bytes"]
+            e["hbm_GBps"] = round(f["hbm_bytes"] / (us * 1e-6) / 1e9, 1)
+            if "algo_bytes" in f:
+                e["traffic_over_algorithmic"] = round(f["hbm_bytes"] / f["algo_bytes"], 3)
+        if "mfma_busy" in f:
+            e["mfma_busy_frac"] = f["mfma_busy"]
+        out[k] = e
+    return out
+
+
+def time_workload(dc, torch, dims, w, E, dsets, stream, desc, steps=20, reps=10):
+    """Whole-path and per-stage times of one workload on rotating input sets;
+    each figure is one event pair around calls queued back to back."""
+    N, B, K = dims.n_blocks, dims.B, dims.K
+    dev = E.device
+    dt = dims.dtype
+    ws = torch.empty(dc.correct_block_workspace_bytes(dims, w), dtype=torch.uint8, device=dev)
+    sel = torch.empty((N, B), dtype=torch.int32, device=dev)
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    us = timed(lambda i: dc.correct_block(dims, w, dsets[i % len(dsets)][0], dsets[i % len(dsets)][1], E,
+                                          sel_tok=sel, workspace=ws, stream=stream), steps)
+    R = N * B
+    ids = torch.empty((R, K), dtype=torch.int32, device=dev)
+    cl = torch.empty((R, K), dtype=torch.float32, device=dev)
+    z = torch.empty((N, B, K, dims.d_z), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=dev)
+    s = torch.empty((N, max(B - 1, 1), dims.d_pair), dtype=torch.float32, device=dev)
+    S = torch.empty((N, max(B - 1, 1), K, K), dtype=torch.float32, device=dev)
+    si = torch.empty((N, B), dtype=torch.int32, device=dev)
+    st = {
+        "topk": timed(lambda i: dc.topk(dims, dsets[i % len(dsets)][0], ids, cl, workspace=ws, stream=stream), reps),
+        "represent": timed(lambda i: dc.represent(dims, w, dsets[i % len(dsets)][1], E, ids, z, s, workspace=ws,
+                                                  stream=stream), reps),
+        "score": timed(lambda i: dc.score(dims, w, z, s, cl, S, workspace=ws, stream=stream), reps),
+        "select": timed(lambda i: dc.select(dims, S, cl, ids, si, sel, stream=stream), reps),
+    }
+
+    class _D:
+        pass
+    Dw = _D()
+    Dw.n_blocks, Dw.B, Dw.K, Dw.V = N, B, K, dims.V
+    Dw.d, Dw.e, Dw.r, Dw.r_z, Dw.r_s, Dw.H, Dw.dtype = (dims.d_hidden, dims.d_embed, dims.d_proj, dims.d_z,
+                                                        dims.d_pair, dims.d_mlp, dt)
+    wk = algorithmic_work(Dw)
+    del ws, ids, cl, z, s, S, si, sel
+    return {"workload": desc, "us_per_call": round(us, 2), "blocks_per_s": round(N / (us * 1e-6), 1),
+            "transitions_per_s": round(wk["transitions"] / (us * 1e-6), 1),
+            "stage_us": {k: round(v, 2) for k, v in st.items()},
+            "hbm_frac_topk": round(wk["logit_bytes"] / (st["topk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac_represent": round(wk["represent_flops"] / (st["represent"] * 1e-6) / 1e12
+                                         / MFMA_BF16_PEAK_TFLOPS, 4),
+            "alu_frac_score": round(wk["grid_elems"] / (st["score"] * 1e-6) / GRID_ELEM_PEAK, 4)}
 
 
 def main():
@@ -275,6 +411,7 @@ def main():
         gen = torch.Generator(device=dev).manual_seed(7)
         dzr = torch.randn((N, B, K, D.r_z), generator=gen, device=dev) / N
         dsr = torch.randn((N, max(B - 1, 1), D.r_s), generator=gen, device=dev) / N
+        torch.cuda.synchronize()     # made on torch's stream, read on the bench stream
         stages["train_rep_backward"] = lambda i: dc.represent_backward(dims, w, dsets[i % len(dsets)][1], E, ids,
                                                                        dzr, dsr, stream=stream)
     tgt_cache = []
@@ -283,7 +420,8 @@ def main():
         # one of each slot's candidates, drawn once (seeded) after top-K has run
         if not tgt_cache:
             pick = torch.from_numpy(np.random.default_rng(5).integers(0, K, (N, B, 1))).to(dev)
-            tgt_cache.append(torch.gather(ids.view(N, B, K), 2, pick).view(N, B).to(torch.int32).contiguous())
+            with torch.cuda.stream(stream):     # ids were written on this stream
+                tgt_cache.append(torch.gather(ids.view(N, B, K), 2, pick).view(N, B).to(torch.int32).contiguous())
         return tgt_cache[0]
     stage_us = {}
     for name, fn in stages.items():
@@ -355,7 +493,8 @@ def main():
         }
         topk_stress = {}
         for cname, make in cases.items():
-            lgs = make()
+            with torch.cuda.stream(stream):     # made on the stream that reads them
+                lgs = make()
             for _ in range(2):
                 dc.topk(dims, lgs, ids, cl, workspace=ws, stream=stream)
             torch.cuda.synchronize()
@@ -379,6 +518,7 @@ def main():
         dst = torch.empty_like(src)
         ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
         gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        torch.cuda.synchronize()     # made on torch's stream, read on the bench stream
         with torch.cuda.stream(stream):
             for _ in range(3):
                 dst.copy_(src)
@@ -424,33 +564,51 @@ def main():
     if attain is not None:
         # the same achieved rate against the device-copy rate measured above
         roof["frac_of_copy"] = round(ach / attain["copy_GBps"], 4)
-    # a grid element issues fma, rcp (quarter rate: 4 slots), add, fma
-    grid_rate = work["grid_elems"] * 7 / (stage_us["score"] * 1e-6)
-
-    # ---- CPU oracle on a bounded sample of the same workload
+    # ---- CPU oracle on a bounded sample of the same workload, its BLAS on
+    # every core of this process's affinity mask; then single-threaded on the
+    # tiny workload and on one block of this workload (the one-stream shape)
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import dcoco_oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:
-            threads = len(os.sched_getaffinity(0))
-        # whole input sets first, then a part of the next one
+        from threadpoolctl import threadpool_limits
+        cores = len(os.sched_getaffinity(0))
         nb = max(1, min(args.cpu_blocks, N * len(sets)))
-        t = time.perf_counter()
-        done = 0
-        for j, sj in enumerate(sets):
-            take = min(N, nb - done)
-            if take <= 0:
-                break
-            O.correct_block({**base, "logits": sj["logits"], "h": sj["h"]}, blocks=list(range(take)))
-            done += take
-        el = time.perf_counter() - t
-        cpu = {"value": round(nb / el, 4), "unit": "blocks/s", "cores": threads, "kind": "oracle",
+        with threadpool_limits(cores):
+            t = time.perf_counter()
+            done = 0
+            for j, sj in enumerate(sets):
+                take = min(N, nb - done)
+                if take <= 0:
+                    break
+                O.correct_block({**base, "logits": sj["logits"], "h": sj["h"]}, blocks=list(range(take)))
+                done += take
+            el = time.perf_counter() - t
+        single = {}
+        with threadpool_limits(1):
+            tiny = synth.make_inputs("tiny")
+            t = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t < 1.0:
+                O.correct_block(tiny)
+                reps += 1
+            single["tiny"] = round(reps / (time.perf_counter() - t), 2)
+            t = time.perf_counter()
+            O.correct_block(base, blocks=[0])
+            single[f"one_block_of_{cfg.name}"] = round(1.0 / (time.perf_counter() - t), 3)
+        cpu = {"value": round(nb / el, 4), "unit": "blocks/s", "cores": cores, "kind": "oracle",
                "sample": f"{nb} blocks ({nb // N} whole input sets of {N} blocks"
                          f"{f' + {nb % N} blocks' if nb % N else ''}, same shapes as the timed steps), "
-                         f"NumPy float64, {el:.1f} s"}
+                         f"NumPy float64 with BLAS on {cores} threads, {el:.1f} s",
+               "single_thread_blocks_per_s": single}
+
+    # ---- every kernel of the step against its own bound, from the committed
+    # rocprofv3 summaries of this command (durations, HBM counters, MFMA busy
+    # cycles), used only while the kernel sources match the ones profiled
+    kdig = source_digest([f"draft_block_contextual_amd/csrc/{f}" for f in KERNEL_SOURCES])
+    figs = stored_kernel_figures(f"kernels_{cfg.name}", kdig)
+    kernels = {"source_digest": kdig, "from": f"profiles/kernels_{cfg.name}.md" if figs else None}
+    if figs:
+        kernels.update(kernel_rooflines(figs, work))
 
     out = {
         "metric": "corrected draft blocks/sec @B=16,K=16,d=4096,32 streams; % HBM/MFMA peak",
@@ -469,39 +627,50 @@ def main():
                    "V": D.V, "embed": D.e, "proj": D.r, "mlp_hidden": D.H},
         "transitions_per_s": round(work["transitions"] * args.steps / (gpu_ms / 1e3), 1),
         "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "mfma_frac_represent": round(work["mfma_flops"] / (stage_us["represent"] * 1e-6) / 1e12
+        # each stage against its own work, timed live (the stage's entry point
+        # alone, between events on the stream it runs on)
+        "mfma_frac_represent": round(work["represent_flops"] / (stage_us["represent"] * 1e-6) / 1e12
                                      / MFMA_BF16_PEAK_TFLOPS, 4),
-        "alu_frac_score": round(grid_rate / VALU_LANE_OPS, 4),
+        "mfma_frac_score": round(work["score_mfma_flops"] / (stage_us["score"] * 1e-6) / 1e12
+                                 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "alu_frac_score": round(work["grid_elems"] / (stage_us["score"] * 1e-6) / GRID_ELEM_PEAK, 4),
         "mfma_frac_rep_backward": (round(work["rep_bwd_flops"] / (stage_us["train_rep_backward"] * 1e-6) / 1e12
                                          / MFMA_BF16_PEAK_TFLOPS, 4) if "train_rep_backward" in stage_us else None),
         "latency_us": latency,
         "roofline": roof,
+        "kernels": kernels,
         "attainable": attain,
         "topk_stress": topk_stress,
         "cpu_baseline": cpu,
         "btable_path": btable,
         "lm_head_topk": lm_head,
     }
-    if args.sweep:
-        sweep = {}
-        for n in (4, 8, 16):
+    # ---- the other workloads: one stream, the 4/8/16-stream sweep (the
+    # first n blocks of the same rotating input sets), the K = 64 stress shape
+    # and the d = 8192 shape (drawn on the GPU: see synth.make_inputs_device)
+    if not args.no_configs:
+        other = {}
+        for n in (1, 4, 8, 16):
             dn = dc.Dims.from_synth(D)
             dn.n_blocks = n
-            lg_n = dsets[0][0][: n * B]
-            h_n = dsets[0][1][:n]
-            st_n = torch.empty((n, B), dtype=torch.int32, device=dev)
-            for i in range(5):
-                dc.correct_block(dn, w, lg_n, h_n, E, sel_tok=st_n, workspace=ws, stream=stream)
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for i in range(20):
-                dc.correct_block(dn, w, lg_n, h_n, E, sel_tok=st_n, workspace=ws, stream=stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / 20
-            sweep[str(n)] = {"us_per_call": round(us, 2), "blocks_per_s": round(n / (us * 1e-6), 1)}
-        out["stream_sweep"] = sweep
+            sub = [(lg[: n * B], h[:n]) for lg, h in dsets]
+            other[f"q8b_{n}" if cfg.name == "q8b_32" else f"{cfg.name}@{n}"] = time_workload(
+                dc, torch, dn, w, E, sub, stream, f"{n} streams of the {cfg.name} shapes")
+        if dt == "bf16" and cfg.name == "q8b_32":
+            for name in ("kstress", "large"):
+                xc = synth.get_config(name)
+                print(f"# drawing {name} on the GPU: {xc.desc}", file=sys.stderr, flush=True)
+                g = synth.make_inputs_device(xc, sets=args.sets, device=dev)
+                torch.cuda.synchronize()     # drawn on torch's stream, read on the bench stream
+                wx = dc.Weights(P_e=g["P_e"], P_h=g["P_h"], W_f=g["W_f"], W_pair=g["W_pair"], W1=g["W1"],
+                                b1=g["b1"], w2=g["w2"], b2=g["b2"])
+                other[name] = time_workload(dc, torch, dc.Dims.from_synth(xc.dims), wx, g["E"], g["sets"], stream,
+                                            xc.desc)
+                del g, wx
+                torch.cuda.empty_cache()
+        out["workloads"] = other
+        print(f"# other workloads: { {k: v['us_per_call'] for k, v in other.items()} }", file=sys.stderr,
+              flush=True)
     print(json.dumps(out))
 
 
