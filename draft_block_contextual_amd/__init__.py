@@ -200,9 +200,12 @@ def _workspace(nbytes: int, device, workspace=None, stream=None):
 
 
 def _empty(stream, *shape_args, **kw):
-    """torch.empty allocated under the call's stream (see _on)."""
+    """torch.empty allocated under the call's stream (see _on); with no stream
+    given the call runs on the current stream, where torch allocates anyway."""
     import torch
-    with _on(stream):
+    if stream is None:
+        return torch.empty(*shape_args, **kw)
+    with torch.cuda.stream(stream):
         return torch.empty(*shape_args, **kw)
 
 
@@ -330,9 +333,13 @@ def loss(dims: Dims, S, cand_ids, target_tok, rho: float = 4.0, stream=None):
     cd = dims.c()
     dev = cand_ids.device
     Bm1 = max(dims.B - 1, 1)
-    out = _empty(stream, 4, dtype=torch.float32, device=dev)   # a 16-byte slot for the scalar
-    pair = _empty(stream, (dims.n_blocks, Bm1), dtype=torch.float32, device=dev)
-    dS = _empty(stream, (dims.n_blocks, Bm1, dims.K, dims.K), dtype=torch.float32, device=dev)
+    # one buffer for the scalar (a 16-byte slot), the pair terms and dS
+    n_pair = dims.n_blocks * Bm1
+    off = 4 + (n_pair + 3) // 4 * 4          # dS starts 16-byte aligned
+    buf = _empty(stream, off + n_pair * dims.K * dims.K, dtype=torch.float32, device=dev)
+    out = buf[:4]
+    pair = buf[4:4 + n_pair].view(dims.n_blocks, Bm1)
+    dS = buf[off:].view(dims.n_blocks, Bm1, dims.K, dims.K)
     _check("dcoco_loss", lib.dcoco_loss(ctypes.byref(cd), _ptr(S), _ptr(cand_ids), _ptr(target_tok),
                                         float(rho), _ptr(out), _ptr(pair), _ptr(dS), _stream(stream)))
     return out[:1], pair[:, :dims.B - 1], dS[:, :dims.B - 1]
