@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libdcoco.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["topk.hip", "gemm.hip", "rep.hip", "score.hip", "train.hip", "wgrad.hip", "api.cpp"]
+SOURCES = ["topk.hip", "gemm.hip", "rep.hip", "score.hip", "score_slab.hip", "train.hip", "wgrad.hip", "api.cpp"]
 ARCH = os.environ.get("DCOCO_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

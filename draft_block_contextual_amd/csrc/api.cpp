@@ -197,21 +197,32 @@ hipError_t run_represent(const dcoco_dims* d, const dcoco_weights* w, const void
   return cand_finish(d, w, z, L, st);
 }
 
+// the scores come from the on-chip slab kernels (no A, B buffer)
+bool use_slab(const dcoco_dims* d) {
+  return score_slab_preferred(d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32, d->n_blocks, d->B, d->K, d->d_z,
+                              d->d_mlp);
+}
+
 // scoring stage buffers
 struct ScoreLayout {
   void* s3;       // bf16 [3, P, rs] (bf16 path only)
   float* C;       // fp32 [nq, P, H]
-  float* AB;      // fp32 [N*B*K, 2H]
+  float* AB;      // fp32 [N*B*K, 2H] (A, B through memory), else null
+  float* part;    // fp32 [nslab, P, K, K] (slab kernels), else null
 };
 
-ScoreLayout carve_score(Carve& c, const dcoco_dims* d) {
+// with_ab: the A, B buffer even where the slab kernels score (training needs it)
+ScoreLayout carve_score(Carve& c, const dcoco_dims* d, bool with_ab = false) {
   ScoreLayout L;
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
   const size_t RK = static_cast<size_t>(d->n_blocks) * d->B * d->K;
   const int nq = d->dtype == DCOCO_BF16 ? 3 : 1;
+  const bool slab = use_slab(d);
   L.s3 = c.take(d->dtype == DCOCO_BF16 ? 3 * P * d->d_pair * 2 : 0);
   L.C = static_cast<float*>(c.take(sizeof(float) * nq * P * d->d_mlp));
-  L.AB = static_cast<float*>(c.take(sizeof(float) * RK * 2 * d->d_mlp));
+  L.AB = (with_ab || !slab) ? static_cast<float*>(c.take(sizeof(float) * RK * 2 * d->d_mlp)) : nullptr;
+  L.part = slab ? static_cast<float*>(c.take(score_slab_part_bytes(d->n_blocks, d->B, d->K, d->d_mlp)))
+                : nullptr;
   return L;
 }
 
@@ -256,7 +267,7 @@ hipError_t ab_gemm(const dcoco_dims* d, const dcoco_weights* w, const void* z, c
   return launch_gemm(q, st);
 }
 
-// AB, then the grid (needs the pair term)
+// the scores (need the pair term): the slab kernels, else A, B through memory and the grid
 hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* cl, float* S,
                       const ScoreLayout& L, hipStream_t st, int32_t* best = nullptr) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
@@ -264,6 +275,14 @@ hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z
   if (P == 0) return hipSuccess;
   const int H = d->d_mlp;
   hipError_t e;
+  if (L.part != nullptr) {
+    ScoreSlabProblem q{};
+    q.N = d->n_blocks; q.B = d->B; q.K = d->K; q.H = H; q.rz = d->d_z;
+    q.z = z; q.W1 = w->W1; q.ldw1 = 2ll * d->d_z + d->d_pair;
+    q.C = L.C; q.nq = dt == kDtypeBf16 ? 3 : 1; q.b1 = w->b1; q.w2 = w->w2; q.b2 = w->b2;
+    q.cand_logits = cl; q.part = L.part; q.S = S; q.best = best;
+    return launch_score_slab(q, st);
+  }
   if ((e = ab_gemm(d, w, z, L, st)) != hipSuccess) return e;
   GridProblem g{};
   g.N = d->n_blocks; g.B = d->B; g.K = d->K; g.H = H; g.dtype = dt;
@@ -324,7 +343,7 @@ BwdLayout carve_bwd(Carve& c, const dcoco_dims* d) {
   const size_t P = static_cast<size_t>(d->n_blocks) * (d->B - 1);
   const size_t RK = static_cast<size_t>(d->n_blocks) * d->B * d->K;
   const size_t H = d->d_mlp;
-  L.SL = carve_score(c, d);
+  L.SL = carve_score(c, d, true);  // the backward reads A and B
   L.dAB = static_cast<float*>(c.take(sizeof(float) * RK * 2 * H));
   L.dC = static_cast<float*>(c.take(sizeof(float) * P * H));
   L.dw2p = static_cast<float*>(c.take(sizeof(float) * P * H));

@@ -94,6 +94,32 @@ struct GridProblem {
 };
 hipError_t launch_grid(const GridProblem& p, hipStream_t st);
 
+// The same scores with A = W1a z and B = W1b z formed on chip (bf16 only):
+// one workgroup per (block, 64-unit slab, chunk of pairs) stores each slab's
+// sum per pair in part [nslab, N*(B-1), K, K]; a second launch adds the slabs,
+// l_{p+1}(b) and b2 into S and fills best.
+struct ScoreSlabProblem {
+  int N, B, K, H, rz;
+  const void* z;               // [N*B*K, rz] bf16
+  const void* W1;              // [H, ldw1] bf16: columns [z_a | z_b | s]
+  long long ldw1;
+  const float* C;              // [nq, N*(B-1), H] fp32: parts of W1s s_p (summed)
+  int nq;
+  const void* b1;              // [H] bf16 or null
+  const void* w2;              // [H] bf16
+  float b2;
+  const float* cand_logits;    // [N, B, K]
+  float* part;                 // [nslab, N*(B-1), K, K] fp32 scratch
+  float* S;                    // [N, B-1, K, K]
+  int32_t* best;               // [N, B-1, K] or null
+};
+bool score_slab_supported(int dtype, int K, int rz, int H);
+int score_slab_count(int H);
+bool score_slab_preferred(int dtype, int N, int B, int K, int rz, int H);
+size_t score_slab_part_bytes(int N, int B, int K, int H);
+int score_slab_pairs_per_chunk(int N, int B, int K, int H);
+hipError_t launch_score_slab(const ScoreSlabProblem& p, hipStream_t st);
+
 // s3 = three bf16 rows per value of s (hi, mid, lo), s3[q * n + i]
 hipError_t launch_split3(const float* s, long long n, void* s3, hipStream_t st);
 

@@ -1,0 +1,448 @@
+// Transition scoring with the per-candidate products formed on chip (bf16
+// storage; review of arXiv 2610.12570, "Contextual Correction of Parallel
+// Drafts for Speculative Decoding", part 1 of "New approach: DCOCO", paper
+// Sec. 3.2; Two Delta, "Two Delta makes NVIDIA Nemotron 3.5 Super even faster
+// with DCOCO", "Score neighboring candidates in parallel"):
+//   S_p(a,b) = l_{p+1}(b) + b2 + sum_h w2_h SiLU(A_{p,a,h} + B_{p,b,h} + C_{p,h}),
+//   A_{p,a} = W1a z_{p,a},  B_{p,b} = W1b z_{p+1,b},  C_p = W1s s_p + b1.
+// The sum over hidden units is cut into slabs of 64 and a draft block's pairs
+// into chunks.  A workgroup takes one (block, slab, chunk): each of its four
+// waves keeps the W1a and W1b rows of 16 units of the slab in registers and
+// walks the chunk's slots in order.  Slot t's candidate rows z_t are copied
+// into LDS one slot ahead (direct global->LDS loads); A_t = W1a z_t and
+// B_t = W1b z_t are formed on v_mfma_f32_16x16x32_bf16; B_t completes pair
+// t-1, whose K x K grid over the wave's units is evaluated at once, and A_t
+// is kept for pair t.  A and B never reach memory.  With A' = -log2(e) A,
+// B' = -log2(e) (B + C_p) and w' = -ln(2) w2 a term is
+// w2 SiLU(u) = w' (A' + B') / (1 + 2^A' 2^B'); a wave with some |A'| > 64 in
+// a pair stages A', B' instead and evaluates 2^(A'+B') per element.  Each
+// pair's sum over the slab (the four waves added in a fixed order once the
+// chunk is done) is stored per slab;
+// pair_finish_kernel adds the slabs in order, adds l_{p+1}(b) + b2 and takes
+// each row's argmax for the walk.
+#include <algorithm>
+
+#include "common.h"
+#include "dma.h"
+#include "kernels.h"
+
+namespace dcoco {
+
+namespace {
+
+constexpr float kNegLog2e = -1.4426950408889634f;
+constexpr float kNegLn2 = -0.6931471805599453f;
+constexpr int kUW = 16;                  // units per wave per slab
+constexpr int kUS = 4 * kUW;             // units per slab
+constexpr int kMaxKs = 8;                // 32-deep k steps of z (W1 fragments in registers): r_z <= 256
+
+struct SlabDev {
+  int N, B, K, H, P, rz, nq, nslab, pc, nchunk;
+  const uint16_t* z;       // [N*B*K, rz]
+  const uint16_t* W1;      // [H, ldw1]: columns [z_a | z_b | s]
+  long long ldw1;
+  const float* C;          // [nq, P, H]: parts of W1s s_p (summed)
+  const uint16_t* b1;      // [H] or null
+  const uint16_t* w2;      // [H]
+  float* part;             // [nslab, P, K, K]: each slab's sum
+};
+
+// KR candidates padded to whole 16-row MFMA tiles; a lane owns a TA x TA
+// block of (a, b) outputs (TA = KR / 8, so the wave's 64 lanes cover the
+// whole K x K grid) over all 16 of the wave's units: a lane's sums are the
+// wave's, and no lane reduction is needed.  Each wave keeps its sum of every
+// pair of the chunk in LDS; the four waves are added at the end.
+template <int KRV, int NKSV>
+struct SlabShape {
+  static constexpr int KR = KRV;
+  static constexpr int NKS = NKSV;                 // 32-deep k steps: r_z = 32 NKS
+  static constexpr int TA = KR / 8;
+  static constexpr int RT = KR / 16;
+  static constexpr int STR = kUW + 4;              // LDS floats per staged candidate row
+  static constexpr int ARR = KR * STR;             // floats per staged array
+  static constexpr int WREG = 4 * ARR + kUW;       // a wave's region: 4 arrays + w' per unit
+  static constexpr int STAGE = 4 * WREG;           // floats of the four waves' regions
+  static constexpr int ZBUF = KR * NKS * 32 * 2;   // bytes of one slot's z rows
+  static constexpr int MAXPC = KR == 16 ? 4 : 1;     // pairs per chunk
+  static constexpr int SUMS = 4 * MAXPC * KR * KR;   // [wave][pair][KR * KR] sums
+  static_assert((KR / TA) * (KR / TA) == kWave, "one output block per lane");
+  static_assert(NKS >= 2 && NKS <= kMaxKs, "r_z");
+  // K <= 16: three workgroups per CU
+  static_assert(2 * ZBUF + (STAGE + SUMS) * 4 <= (KR == 16 ? 53 : 160) * 1024, "LDS");
+};
+
+// the 16-byte chunk c of z row r sits at chunk position c ^ (r & 7) of its
+// LDS row, so the 16 rows of one fragment read spread over the banks
+__device__ __forceinline__ int zswz(int r, int c) { return c ^ (r & 7); }
+
+// staged arrays: row r's float4 group g (units 4g .. 4g+3) sits at group
+// g ^ ((r >> 3) & 1), so the eight rows one grid read touches fall on
+// distinct banks
+__device__ __forceinline__ int sidx(int r, int h) { return r * (kUW + 4) + (((h >> 2) ^ ((r >> 3) & 1)) << 2) + (h & 3); }
+
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename SS>
+__global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(SlabDev g) {
+  constexpr int KR = SS::KR, TA = SS::TA, RT = SS::RT, ARR = SS::ARR, MAXPC = SS::MAXPC, NKS = SS::NKS;
+  __shared__ __align__(1024) char zb0[SS::ZBUF];
+  __shared__ __align__(1024) char zb1[SS::ZBUF];
+  __shared__ __align__(16) float smem[SS::STAGE];
+  __shared__ __align__(16) float sums[SS::SUMS];   // [wave][pair of the chunk][KR * KR]
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = tid >> 6;
+  const int K = g.K;
+  const int H = g.H;
+  constexpr int rz = NKS * 32;
+  const int B = g.B;
+  const int Bm1 = B - 1;
+  int bid = blockIdx.x;
+  const int chunk = bid % g.nchunk;
+  bid /= g.nchunk;
+  const int slab = bid % g.nslab;
+  const int n = bid / g.nslab;
+  const int t0 = chunk * g.pc;                   // first slot: pair t0 is the chunk's first
+  const int t1 = min(t0 + g.pc, Bm1);            // last slot: pair t1 - 1 is the chunk's last
+  constexpr int rowb = rz * 2;                   // bytes of one z row
+
+  // grid layout of this lane: outputs (la TA + i, lb TA + j)
+  const int la = l / (KR / TA);
+  const int lb = l % (KR / TA);
+  // MFMA layout: unit fr of the wave's 16, candidate rows 4 fq + v of each
+  // 16-row tile; fragment row fr, k chunk fq
+  const int fr = l & 15;
+  const int fq = l >> 4;
+
+  float* wreg = smem + wv * SS::WREG;
+  float* sEA = wreg;                 // 2^A' (or A')
+  float* sWA = wreg + ARR;           // w'A'
+  float* sEB = wreg + 2 * ARR;       // 2^B' (or B')
+  float* sWB = wreg + 3 * ARR;       // w'B'
+  float* sWq = wreg + 4 * ARR;       // w' per unit (per-element form)
+
+  // ---- this lane's unit: W1a and W1b fragments for every k step, per-unit terms
+  const int u = slab * kUS + wv * kUW + fr;
+  const int uc = min(u, H - 1);
+  const bool uin = u < H;
+  bf16x8_t wa[NKS], wb[NKS];
+  {
+    const uint16_t* src = g.W1 + static_cast<long long>(uc) * g.ldw1 + fq * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      wa[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + ks * 32));
+      wb[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + rz + ks * 32));
+    }
+  }
+  const float wq = uin ? kNegLn2 * bf16_to_f32(g.w2[uc]) : 0.f;
+  const float bb = g.b1 ? bf16_to_f32(g.b1[uc]) : 0.f;
+  if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
+
+  // ---- z rows of slot t into zb[t & 1] (KR rows; rows past K repeat row K-1)
+  const long long zrow0 = static_cast<long long>(n) * B * K;
+  const int ninst = KR * rowb / 1024;            // 1 KB direct loads per slot
+  auto issue_z = [&](int t) {
+    char* dst = (t & 1) ? zb1 : zb0;
+    for (int j = wv; j < ninst; j += 4) {
+      const int byte = j * 1024 + l * 16;
+      const int r = byte / rowb;
+      const int pc = (byte - r * rowb) >> 4;
+      const int c = zswz(r, pc);
+      const long long srow = zrow0 + static_cast<long long>(t) * K + min(r, K - 1);
+      dma16(g.z + srow * rz + c * 8, __builtin_amdgcn_readfirstlane(lds_offset(dst) + j * 1024));
+    }
+  };
+
+  // C_p + b1 of this lane's unit, pair p of the block (0 <= p < B - 1)
+  auto load_c = [&](int p) -> float {
+    const long long np = static_cast<long long>(n) * Bm1 + p;
+    float c = g.C[np * H + uc];
+    if (g.nq > 1) c += g.C[(static_cast<long long>(g.P) + np) * H + uc];
+    if (g.nq > 2) c += g.C[(2ll * g.P + np) * H + uc];
+    return c + bb;
+  };
+
+  issue_z(t0);
+  float c_prev = load_c(t0);         // C of the pair completed at the next step
+  bool slow_prev = false;            // that pair takes the per-element form (wave-uniform)
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  __syncthreads();                   // slot t0's rows and the w' table are in LDS
+
+  for (int t = t0; t <= t1; ++t) {
+    const char* zt = (t & 1) ? zb1 : zb0;
+    if (t < t1) issue_z(t + 1);      // the other buffer was last read at step t - 1
+    const float cq = kNegLog2e * c_prev;                 // pair t - 1 (when t > t0)
+    if (t > t0 && t < t1) c_prev = load_c(t);            // pair t, used at step t + 1
+
+    // ---- A_t = W1a z_t, B_t = W1b z_t for the wave's 16 units
+    f32x4_t accA[RT], accB[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      accA[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accB[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = rt * 16 + fr;
+        const bf16x8_t x = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(zt + r * rowb + zswz(r, ks * 4 + fq) * 16));
+        accA[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, wa[ks], accA[rt], 0, 0, 0);
+        accB[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, wb[ks], accB[rt], 0, 0, 0);
+      }
+    }
+
+    // ---- pair t - 1: its successor side from B_t, then its grid
+    if (t > t0) {
+      const int p = t - 1;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float bp = fmaf(kNegLog2e, accB[rt][v], cq);
+          const int o = sidx(rt * 16 + fq * 4 + v, fr);
+          const float e = __builtin_amdgcn_exp2f(bp);
+          sEB[o] = slow_prev ? bp : e;
+          sWB[o] = wq * bp;
+        }
+      wave_lds_sync();
+      float acc[TA][TA];
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
+      if (!slow_prev) {
+        for (int h = 0; h < kUW; h += 4) {
+          float4 ea[TA], wa4[TA], eb[TA], wb4[TA];
+#pragma unroll
+          for (int i = 0; i < TA; ++i) {
+            ea[i] = *reinterpret_cast<const float4*>(sEA + sidx(la * TA + i, h));
+            wa4[i] = *reinterpret_cast<const float4*>(sWA + sidx(la * TA + i, h));
+            eb[i] = *reinterpret_cast<const float4*>(sEB + sidx(lb * TA + i, h));
+            wb4[i] = *reinterpret_cast<const float4*>(sWB + sidx(lb * TA + i, h));
+          }
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+            for (int i = 0; i < TA; ++i)
+#pragma unroll
+              for (int j = 0; j < TA; ++j) {
+                const float den = fmaf(ea[i][c4], eb[j][c4], 1.0f);
+                const float r = __builtin_amdgcn_rcpf(den);
+                acc[i][j] = fmaf(wa4[i][c4] + wb4[j][c4], r, acc[i][j]);
+              }
+        }
+      } else {
+        for (int h = 0; h < kUW; h += 4) {
+          float4 av[TA], bv[TA];
+#pragma unroll
+          for (int i = 0; i < TA; ++i) {
+            av[i] = *reinterpret_cast<const float4*>(sEA + sidx(la * TA + i, h));
+            bv[i] = *reinterpret_cast<const float4*>(sEB + sidx(lb * TA + i, h));
+          }
+          const float4 w4 = *reinterpret_cast<const float4*>(sWq + h);
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+            for (int i = 0; i < TA; ++i)
+#pragma unroll
+              for (int j = 0; j < TA; ++j) {
+                const float tt = av[i][c4] + bv[j][c4];
+                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(tt));
+                acc[i][j] = fmaf(w4[c4], tt * r, acc[i][j]);
+              }
+        }
+      }
+      // the wave's sum for pair p (its 16 units), kept until the chunk is done
+      float* ws = sums + (wv * MAXPC + (p - t0)) * KR * KR;
+#pragma unroll
+      for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int j = 0; j < TA; ++j) ws[(la * TA + i) * KR + lb * TA + j] = acc[i][j];
+    }
+
+    // ---- pair t: its predecessor side from A_t
+    if (t < t1) {
+      float ap[RT][4];
+      bool big = false;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          ap[rt][v] = kNegLog2e * accA[rt][v];
+          big |= fabsf(ap[rt][v]) > 64.f;
+        }
+      slow_prev = __builtin_amdgcn_ballot_w64(big) != 0;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int o = sidx(rt * 16 + fq * 4 + v, fr);
+          const float e = __builtin_amdgcn_exp2f(ap[rt][v]);
+          sEA[o] = slow_prev ? ap[rt][v] : e;
+          sWA[o] = wq * ap[rt][v];
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t + 1's rows (this wave's share)
+    __syncthreads();                                       // ... and every other wave's
+  }
+  // the slab's sum per pair: the four waves added in order.  The chunk's
+  // pairs are consecutive in the pair index, so this is one contiguous run
+  // of (t1 - t0) K^2 sums.
+  float* dst = g.part + (static_cast<long long>(slab) * g.P + static_cast<long long>(n) * Bm1 + t0) * K * K;
+  const int kk = K * K;
+  const int total = (t1 - t0) * kk;
+  for (int i = tid; i < total; i += 256) {
+    const int q = i / kk;
+    const int idx = i - q * kk;
+    const int a = idx / K;
+    const int o = q * KR * KR + a * KR + (idx - a * K);
+    float sum = sums[o];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum += sums[w * MAXPC * KR * KR + o];
+    dst[i] = sum;
+  }
+}
+
+// S_p(a, b) = l_{p+1}(b) + (sum of the slabs' partial sums, in slab order) + b2,
+// and best_p(a) = argmax_b S_p(a, b) (largest order key, the lowest b among
+// equal keys; NaN never wins).  One workgroup per pair.
+template <int KR>
+__global__ void __launch_bounds__(256)
+pair_finish_kernel(const float* __restrict__ part, int nslab, int P, int B, int K, float b2,
+                   const float* __restrict__ cand_logits, float* __restrict__ S, int32_t* __restrict__ best) {
+  constexpr int kPerT = (KR * KR + 255) / 256;
+  __shared__ float sS[KR * KR];
+  const int np = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int Bm1 = B - 1;
+  const int n = np / Bm1;
+  const int p = np - n * Bm1;
+  const int kk = K * K;
+  const float* lnext = cand_logits + (static_cast<long long>(n) * B + p + 1) * K;
+  float sum[kPerT];
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) sum[i] = 0.f;
+  // four slabs' loads in flight at once (slab and index clamped, masked after)
+  for (int s0 = 0; s0 < nslab; s0 += 4) {
+    float v[4][kPerT];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        const int idx = min(tid + 256 * i, kk - 1);
+        v[q][i] = part[(static_cast<long long>(min(s0 + q, nslab - 1)) * P + np) * kk + idx];
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i)
+        if (s0 + q < nslab) sum[i] = (s0 + q == 0) ? v[q][i] : sum[i] + v[q][i];
+  }
+  float* Sp = S + static_cast<long long>(np) * kk;
+#pragma unroll
+  for (int i = 0; i < kPerT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < kk) {
+      const int a = idx / K;
+      const int b = idx - a * K;
+      const float sv = lnext[b] + (sum[i] + b2);
+      Sp[idx] = sv;
+      sS[a * KR + b] = sv;
+    }
+  }
+  if (best == nullptr) return;
+  __syncthreads();
+  if (tid < K) {
+    const float* row = sS + tid * KR;
+    uint32_t bk = order_key(row[0]);
+    int bi = 0;
+    for (int b = 1; b < K; ++b) {
+      const uint32_t k2 = order_key(row[b]);
+      if (k2 > bk) {
+        bk = k2;
+        bi = b;
+      }
+    }
+    best[static_cast<long long>(np) * K + tid] = bi;
+  }
+}
+
+}  // namespace
+
+bool score_slab_supported(int dtype, int K, int rz, int H) {
+  return dtype == kDtypeBf16 && K >= 1 && K <= 32 && (rz == 64 || rz == 128 || rz == 256) && H >= 16 &&
+         H % 16 == 0;
+}
+
+int score_slab_count(int H) { return (H + kUS - 1) / kUS; }
+
+// Up to about 40M grid elements (P K^2 H) the slab kernels finish first: their
+// time is set by each workgroup's walk over its chunk.  Beyond that the grid
+// kernel after the A, B GEMM evaluates the elements at a higher rate and wins
+// (at 32 blocks of B = 16, K = 16, H = 512 the two take about the same time).
+bool score_slab_preferred(int dtype, int N, int B, int K, int rz, int H) {
+  const double elems = static_cast<double>(N) * (B - 1) * K * K * H;
+  return score_slab_supported(dtype, K, rz, H) && elems <= 40.0e6;
+}
+
+size_t score_slab_part_bytes(int N, int B, int K, int H) {
+  const long long P = static_cast<long long>(N) * (B - 1);
+  return sizeof(float) * static_cast<size_t>(score_slab_count(H)) * static_cast<size_t>(P > 0 ? P : 0) *
+         static_cast<size_t>(K) * static_cast<size_t>(K);
+}
+
+// pairs per chunk: about two workgroups per CU, every chunk at least one
+// pair and no more than the workgroup keeps in LDS (4 for K <= 16, else 1)
+int score_slab_pairs_per_chunk(int N, int B, int K, int H) {
+  const int Bm1 = B - 1;
+  if (Bm1 < 1) return 1;
+  const long long wg = static_cast<long long>(N) * score_slab_count(H);
+  long long chunks = (512 + wg - 1) / wg;
+  if (chunks > Bm1) chunks = Bm1;
+  if (chunks < 1) chunks = 1;
+  const int pc = static_cast<int>((Bm1 + chunks - 1) / chunks);
+  return std::min(pc, K <= 16 ? 4 : 1);
+}
+
+hipError_t launch_score_slab(const ScoreSlabProblem& q, hipStream_t st) {
+  const int Bm1 = q.B - 1;
+  const int P = q.N * Bm1;
+  if (P <= 0) return hipSuccess;
+  if (!score_slab_supported(kDtypeBf16, q.K, q.rz, q.H)) return hipErrorInvalidValue;
+  SlabDev d;
+  d.N = q.N; d.B = q.B; d.K = q.K; d.H = q.H; d.P = P; d.rz = q.rz; d.nq = q.nq;
+  d.nslab = score_slab_count(q.H);
+  d.pc = score_slab_pairs_per_chunk(q.N, q.B, q.K, q.H);
+  d.nchunk = (Bm1 + d.pc - 1) / d.pc;
+  d.z = static_cast<const uint16_t*>(q.z);
+  d.W1 = static_cast<const uint16_t*>(q.W1);
+  d.ldw1 = q.ldw1;
+  d.C = q.C;
+  d.b1 = static_cast<const uint16_t*>(q.b1);
+  d.w2 = static_cast<const uint16_t*>(q.w2);
+  d.part = q.part;
+  const dim3 grid(static_cast<unsigned>(q.N) * d.nslab * d.nchunk);
+#define DCOCO_SLAB(KRV)                                                                                   \
+  if (q.rz == 64) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 2>>), grid, dim3(256), 0, st, d);       \
+  else if (q.rz == 128) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 4>>), grid, dim3(256), 0, st, d); \
+  else hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 8>>), grid, dim3(256), 0, st, d)
+  if (q.K <= 16) {
+    DCOCO_SLAB(16);
+    hipLaunchKernelGGL((pair_finish_kernel<16>), dim3(P), dim3(256), 0, st, q.part, d.nslab, P, q.B, q.K, q.b2,
+                       q.cand_logits, q.S, q.best);
+  } else {
+    DCOCO_SLAB(32);
+    hipLaunchKernelGGL((pair_finish_kernel<32>), dim3(P), dim3(256), 0, st, q.part, d.nslab, P, q.B, q.K, q.b2,
+                       q.cand_logits, q.S, q.best);
+  }
+#undef DCOCO_SLAB
+  return hipGetLastError();
+}
+
+}  // namespace dcoco

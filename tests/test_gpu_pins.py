@@ -1,10 +1,12 @@
 """Special cases of the pages checked on the HIP path (through the C ABI).
 
 * Large pre-activations: the scoring grid evaluates w2 SiLU(u) through
-  per-candidate factors 2^A', 2^B' while every |A'| of a slab of hidden units
-  stays within 64, and through 2^(A'+B') per element otherwise.  Scores with
-  W1 rows scaled by 2^6 (exact in bf16 and fp32) must still match the oracle,
-  with both forms taken in the same launch.
+  per-candidate factors 2^A', 2^B' while every |A'| of a group of hidden
+  units stays within 64, and through 2^(A'+B') per element otherwise (a group
+  is one wave's 16 units where A and B are formed on chip, a slab of
+  4096 / KR units where they go through memory).  Scores with W1 rows scaled
+  by 2^6 (exact in bf16 and fp32) must still match the oracle, with both
+  forms taken in the same launch.
 * The walk reads one row per pair (review of arXiv 2610.12570, "Contextual
   Correction of Parallel Drafts for Speculative Decoding", part 2 of "New
   approach: DCOCO", paper Sec. 3.3: O(BK) on top of the scoring): poisoning
@@ -68,13 +70,28 @@ def _slab(K):
     return 4096 // KR
 
 
-def _slab_counts(z, W1, K, H):
-    """(slabs certainly above, slabs certainly below) the |A'| = 64 switch, where
-    A' = -log2(e) W1a z_{p,a} over a pair's K predecessor rows and one slab of
-    hidden units (values within 0.1% of 64 count as neither)."""
+def _on_chip(D):
+    """The library forms A and B on chip for bf16 with K <= 32, r_z of 64, 128
+    or 256, and at most 40M grid elements N (B-1) K^2 H; otherwise they go
+    through memory to the grid kernel."""
+    return (D.dtype == "bf16" and D.K <= 32 and D.r_z in (64, 128, 256) and D.H % 16 == 0
+            and D.n_blocks * (D.B - 1) * D.K * D.K * D.H <= 40e6)
+
+
+def _group(D):
+    """Hidden units that take one form together: one wave's 16 where A and B
+    are formed on chip, else the grid's slab of 4096 / KR units."""
+    return 16 if _on_chip(D) else _slab(D.K)
+
+
+def _slab_counts(z, W1, D):
+    """(groups certainly above, groups certainly below) the |A'| = 64 switch,
+    where A' = -log2(e) W1a z_{p,a} over a pair's K predecessor rows and one
+    group of hidden units (values within 0.1% of 64 count as neither)."""
     N, B, _, rz = z.shape
+    H = D.H
     A = np.abs(z[:, :-1] @ W1[:, :rz].T) * LOG2E          # [N, B-1, K, H]
-    hs = _slab(K)
+    hs = _group(D)
     hi = lo = 0
     for h0 in range(0, H, hs):
         m = A[..., h0:h0 + hs].max(axis=(-1, -2))         # [N, B-1]
@@ -112,18 +129,23 @@ def _check_scores(got, Sref, D, z, s, cand_vals, W1, inp):
     assert ok, (worst, n_rel, n_all)
 
 
-@pytest.mark.parametrize("name,mode", [("k32_small", "units"), ("k64_small", "units"), ("h512_bf16", "units"),
-                                       ("mid_bf16", "slots"), ("k32_f32", "units"), ("mid_f32", "slots"),
-                                       ("small_f32", "slots")])
-def test_score_large_preactivations(name, mode):
+@pytest.mark.parametrize("name,mode,tile", [("k32_small", "units", 1), ("k64_small", "units", 1),
+                                            ("h512_bf16", "units", 1), ("mid_bf16", "slots", 1),
+                                            ("h512_bf16", "units", 21), ("mid_bf16", "slots", 11),
+                                            ("k32_f32", "units", 1), ("mid_f32", "slots", 1),
+                                            ("small_f32", "slots", 1)])
+def test_score_large_preactivations(name, mode, tile):
     # "units": the W1 rows of the first slab of hidden units scaled by 2^6, so
     # that slab of every pair takes the per-element form and the later slabs
     # the factored one.  "slots": z of every even slot scaled by 2^6, so pairs
     # whose predecessor slot is even take the per-element form and the others
     # the factored one (with large B' values on their successor side).
+    # tile > 1 repeats the blocks that many times, past the size where the
+    # library scores through the A, B buffer and the grid kernel.
+    import dataclasses
     import draft_block_contextual_amd as dc
     import torch
-    print(f"case score large pre-activations {name} {mode}", flush=True)
+    print(f"case score large pre-activations {name} {mode} x{tile}", flush=True)
     inp = _inputs(name)
     D = inp["dims"]
     ref = O.correct_block(inp)
@@ -137,24 +159,30 @@ def test_score_large_preactivations(name, mode):
         w.W1 = to_dev(_store(W1, D.dtype), D.dtype)
     else:
         z[:, 0::2] *= 64.0
-    hi, lo = _slab_counts(z, W1, D.K, D.H)
-    print(f"  slabs above the switch: {hi}, below: {lo}", flush=True)
-    assert hi > 0 and lo > 0
     s32 = ref["s"].astype(np.float32)
-    cl = ref["cand_vals"].astype(np.float32)
+    Sref = O.transition_scores(z, s32.astype(np.float64), ref["cand_vals"], W1, O.to_f64(inp["b1"], D.dtype),
+                               O.to_f64(inp["w2"], D.dtype), inp["b2"])
+    vals, ids = ref["cand_vals"], ref["cand_ids"]
+    if tile > 1:
+        z, s32, vals, ids, Sref = (np.concatenate([x] * tile) for x in (z, s32, vals, ids, Sref))
+        D = dataclasses.replace(D, n_blocks=D.n_blocks * tile)
+        dims = dc.Dims.from_synth(D)
+    hi, lo = _slab_counts(z, W1, D)
+    print(f"  {'on chip' if _on_chip(D) else 'through memory'}; groups above the switch: {hi}, below: {lo}",
+          flush=True)
+    assert hi > 0 and lo > 0
+    assert _on_chip(D) == (tile == 1 and D.dtype == "bf16" and D.K <= 32)
+    cl = vals.astype(np.float32)
     S = dc.score(dims, w, to_dev(_store(z, D.dtype), D.dtype), torch.from_numpy(s32).cuda(),
                  torch.from_numpy(cl).cuda())
     torch.cuda.synchronize()
-    Sref = O.transition_scores(z, s32.astype(np.float64), ref["cand_vals"], W1, O.to_f64(inp["b1"], D.dtype),
-                               O.to_f64(inp["w2"], D.dtype), inp["b2"])
     got = _np(S)
-    _check_scores(got, Sref, D, z, s32.astype(np.float64), ref["cand_vals"], W1, inp)
+    _check_scores(got, Sref, D, z, s32.astype(np.float64), vals, W1, inp)
     # and the walk over those scores is the oracle's wherever the margin decides
-    ri, _, _ = O.greedy_walk(Sref, ref["cand_vals"], ref["cand_ids"])
-    si, _ = dc.select(dims, S, torch.from_numpy(cl).cuda(),
-                      torch.from_numpy(ref["cand_ids"].astype(np.int32)).cuda())
+    ri, _, _ = O.greedy_walk(Sref, vals, ids)
+    si, _ = dc.select(dims, S, torch.from_numpy(cl).cuda(), torch.from_numpy(ids.astype(np.int32)).cuda())
     torch.cuda.synchronize()
-    ok, cmp, tot, fail = lockstep_path_check(got, Sref, ref["cand_vals"], _np(si), ri)
+    ok, cmp, tot, fail = lockstep_path_check(got, Sref, vals, _np(si), ri)
     assert ok, f"path differs at a step with margin > {PATH_MARGIN}: {fail}"
 
 
@@ -168,8 +196,8 @@ def test_correct_block_large_preactivations(name):
     W1 = _scaled_w1(inp, _slab(D.K))
     inp["W1"] = _store(W1, D.dtype)
     ref = O.correct_block(inp)
-    hi, lo = _slab_counts(ref["z"], W1, D.K, D.H)
-    print(f"  slabs above the switch: {hi}, below: {lo}", flush=True)
+    hi, lo = _slab_counts(ref["z"], W1, D)
+    print(f"  groups above the switch: {hi}, below: {lo}", flush=True)
     assert hi > 0 and lo > 0
     dims, w, logits, h, E = device_inputs(inp)
     out = dc.correct_block(dims, w, logits, h, E, want_all=True)
