@@ -543,15 +543,12 @@ __device__ __forceinline__ void row_pad(int seg0, int V, int l, uint32_t (&kw)[N
   }
 }
 
-// vectors per lane and segment, and register sets in the ring
-#ifndef DCOCO_TOPK_NV
-#define DCOCO_TOPK_NV 3
-#endif
-#ifndef DCOCO_TOPK_D
-#define DCOCO_TOPK_D 4
-#endif
-constexpr int kRegNV = DCOCO_TOPK_NV;
-constexpr int kRegD = DCOCO_TOPK_D;
+// vectors per lane and segment (3: 3 KB per wave and segment), and register
+// sets in the ring (4 segments in flight per wave).  Measured on the 32-stream
+// workload: 4 vectors or 6 to 8 register sets were no faster, and more sets
+// cost occupancy.
+constexpr int kRegNV = 3;
+constexpr int kRegD = 4;
 
 // A wave's running top-K: one composite per lane (lanes < K, 0 = empty), and
 // once it holds K entries the smallest key among them (kmin).  An element

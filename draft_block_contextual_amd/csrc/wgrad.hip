@@ -479,10 +479,8 @@ __global__ void __launch_bounds__(kWgThreads, 1) wgrad_dma_kernel(WgradArgs p) {
 
 }  // namespace
 
-#ifndef DCOCO_WGRAD_DMA
-#define DCOCO_WGRAD_DMA 1
-#endif
-constexpr bool kWgradUseDma = DCOCO_WGRAD_DMA != 0;
+// weight gradients with bf16 operands take the direct global->LDS kernel
+constexpr bool kWgradUseDma = true;
 
 int wgrad_pick_split(int M, int N, int Kd) {
   const long long tiles = static_cast<long long>((M + kWgBM - 1) / kWgBM) * ((N + kWgBN - 1) / kWgBN);
