@@ -570,7 +570,7 @@ int static_scratch(void** out) {
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 106; }
+int dcoco_abi_version(void) { return 107; }
 
 size_t dcoco_static_scratch_bytes(void) { return DCOCO_STATIC_SCRATCH_BYTES; }
 
@@ -888,7 +888,7 @@ int dcoco_build_btable(const dcoco_dims* d, const dcoco_weights* w, const void* 
                        void* workspace, size_t* workspace_bytes, void* stream) {
   int rc = check_dims(d, true);
   if (rc != DCOCO_OK) return rc;
-  if (d->dtype != DCOCO_BF16 || !gather_gemm_supported(d->d_proj)) return DCOCO_ERR_UNSUPPORTED;
+  if (d->dtype != DCOCO_BF16) return DCOCO_ERR_UNSUPPORTED;
   const int dt = kDtypeBf16;
   const int r = d->d_proj;
   const int chunk = d->V < kTableChunk ? d->V : kTableChunk;
@@ -924,7 +924,7 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
                                void* stream) {
   int rc = check_dims(d, true);
   if (rc != DCOCO_OK) return rc;
-  if (d->dtype != DCOCO_BF16 || !gather_gemm_supported(d->d_proj)) return DCOCO_ERR_UNSUPPORTED;
+  if (d->dtype != DCOCO_BF16) return DCOCO_ERR_UNSUPPORTED;
   const int dt = kDtypeBf16;
   if (!topk_supported(dt, d->V, d->K)) return DCOCO_ERR_UNSUPPORTED;
   const int R = d->n_blocks * d->B;
@@ -966,9 +966,24 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
   hipError_t e = slot_part(d, w, h, s, SL.s3, L, st);
   if (e == hipSuccess) e = pair_term(d, w, s, SL, true, st);
   if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
-  if (e == hipSuccess)
-    e = launch_gather_gemm(btable, ids, d->V - 1, static_cast<int>(RK), r, w->W_f, 2ll * r, 0, d->d_z, z, L.gf,
-                           d->K, st);
+  if (e == hipSuccess) {
+    if (gather_gemm_supported(r)) {
+      // table rows gathered into the LDS operand tile, W_fb slice resident in LDS
+      e = launch_gather_gemm(btable, ids, d->V - 1, static_cast<int>(RK), r, w->W_f, 2ll * r, 0, d->d_z, z, L.gf,
+                             d->K, st);
+    } else {
+      // wider rows: the GEMM gathers table rows by id, z = W_fb b[c] + gf[slot]
+      GemmProblem q{};
+      q.M = static_cast<int>(RK); q.N = d->d_z; q.Kd = r;
+      q.A = btable; q.lda = r; q.a_rows = ids; q.a_rows_max = d->V - 1; q.a_dtype = dt;
+      q.w[0] = w->W_f; q.ldw[0] = 2ll * r; q.col0[0] = 0; q.seg_end[0] = d->d_z;
+      q.w[1] = q.w[2] = nullptr; q.seg_end[1] = q.seg_end[2] = d->d_z;
+      q.w_dtype = dt;
+      q.split = 1; q.out = z; q.out_dtype = dt; q.ldo = d->d_z;
+      q.row_bias = L.gf; q.row_bias_div = d->K; q.col_bias = nullptr;
+      e = launch_gemm(q, st);
+    }
+  }
   if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best);
   if (e == hipSuccess) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
   return hip_status(e);

@@ -328,8 +328,9 @@ size_t dcoco_static_scratch_bytes(void);
  * beyond the per-call path: E is frozen and P_e fixed at inference ([P1]
  * "Score neighboring candidates in parallel"; [P2] part 1), so
  * b_v = LN(P_e E_v) can be formed once for every token v and gathered per
- * call instead of gathering E rows and projecting them.  bf16 only, d_proj
- * <= 256 (otherwise DCOCO_ERR_UNSUPPORTED).
+ * call instead of gathering E rows and projecting them.  bf16 only (fp32
+ * storage returns DCOCO_ERR_UNSUPPORTED); any d_proj the other entry points
+ * accept.
  *   E     [V, d_embed] bf16
  *   table [V, d_proj] bf16   out: b_v rounded to bf16 (the per-call rounding
  *                            point of b); uses only w->P_e.
@@ -341,7 +342,8 @@ int dcoco_build_btable(const dcoco_dims* dims, const dcoco_weights* w, const voi
 /* dcoco_correct_block with b_{i,k} read from a table made by
  * dcoco_build_btable (table [V, d_proj] bf16) instead of projecting gathered
  * E rows; w->P_e is not used.  Same outputs, ordering and errors; the result
- * equals the per-call path up to the fp32 summation order of P_e E_v. */
+ * equals the per-call path up to the fp32 summation order of P_e E_v.  bf16
+ * only. */
 int dcoco_correct_block_btable(const dcoco_dims* dims, const dcoco_weights* w,
                                const void* logits, const void* h, const void* btable,
                                void* workspace, size_t* workspace_bytes,
@@ -355,7 +357,8 @@ const char* dcoco_status_string(int status);
 /* ABI version of this header (major * 100 + minor): 101 adds the table
  * entry points, 102 dcoco_select_path, 103 dcoco_loss and
  * dcoco_score_backward, 104 dcoco_lm_head_topk, 105
- * dcoco_represent_backward, 106 dcoco_correct_block_static. */
+ * dcoco_represent_backward, 106 dcoco_correct_block_static, 107 the table
+ * entry points for any d_proj. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

@@ -162,6 +162,9 @@ CONFIGS = {
                       30.0, "peaks", 32, 2013, "random", "K = 32, H = 320 in fp32"),
     "h512_bf16": Config("h512_bf16", _d(3, 6, 16, 7001, 256, 256, 128, 128, 128, 512, "bf16"),
                         30.0, "peaks", 16, 2014, "random", "K = 16 with H = 512 on a small shape"),
+    # d_proj = 512, as in the d = 8192 workload: the table path's GEMM gathers the rows
+    "r512_bf16": Config("r512_bf16", _d(2, 6, 16, 6007, 512, 512, 512, 256, 128, 256, "bf16"),
+                        30.0, "peaks", 16, 2015, "random", "d_proj = 512 on a small shape"),
     # LM-head shapes (head tied to E, so d == e): ragged vocabulary tiles,
     # ragged row tiles, rows without planted peaks (bf16 ties at the K-th)
     "lmh_small": Config("lmh_small", _d(2, 8, 16, 5003, 256, 256, 64, 64, 64, 64, "bf16"),

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import draft_block_contextual_amd as dc
-    assert lib.dcoco_abi_version() == 106
+    assert lib.dcoco_abi_version() == 107
     assert dc.status_string(0) == "ok"
     for code in (-1, -2, -3, -4):
         assert dc.status_string(code) not in ("ok", "unknown status")
@@ -144,11 +144,19 @@ def test_btable_queries(lib):
                                           ctypes.byref(n2), None, None, None, None, None, None) == 0
     rc, n_full = _query_block(lib, d)
     assert rc == 0 and 0 < n2.value < n_full          # no buffers for the gathered projection
-    # fp32 storage and wide projections have no table path
-    for kw in (dict(dtype="f32"), dict(d_proj=512)):
-        cdx = _dims(**kw).c()
+    # fp32 storage has no table path; wide projections do (the GEMM gathers the table rows)
+    cdx = _dims(dtype="f32").c()
+    assert lib.dcoco_build_btable(ctypes.byref(cdx), ctypes.byref(cw), None, None, None,
+                                  ctypes.byref(n), None) == -2
+    assert lib.dcoco_correct_block_btable(ctypes.byref(cdx), ctypes.byref(cw), None, None, None, None,
+                                          ctypes.byref(n2), None, None, None, None, None, None) == -2
+    for r in (512, 2048):
+        cdx = _dims(d_proj=r).c()
         assert lib.dcoco_build_btable(ctypes.byref(cdx), ctypes.byref(cw), None, None, None,
-                                      ctypes.byref(n), None) == -2
+                                      ctypes.byref(n), None) == 0
+        assert n.value >= 4 * 8192 * r * 4
+        assert lib.dcoco_correct_block_btable(ctypes.byref(cdx), ctypes.byref(cw), None, None, None, None,
+                                              ctypes.byref(n2), None, None, None, None, None, None) == 0
 
 
 def test_select_path_argument_checks(lib):

@@ -616,7 +616,7 @@ def _bf16_ulp(x):
     return np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))).astype(int) - 7)
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "tall_bf16", "q8b_1"])
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "tall_bf16", "q8b_1", "r512_bf16", "wide_max"])
 def test_btable_rows_match_oracle(name):
     import draft_block_contextual_amd as dc
     import torch
@@ -652,7 +652,8 @@ def _check_block(inp, out, ref, sl=None):
     return worst
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "k64_small", "k32_small", "widez_bf16", "tall_bf16"])
+@pytest.mark.parametrize("name", ["small_bf16", "mid_bf16", "k64_small", "k32_small", "widez_bf16", "tall_bf16",
+                                  "r512_bf16", "wide_max"])
 def test_correct_block_btable_matches_oracle(name):
     import draft_block_contextual_amd as dc
     import torch
