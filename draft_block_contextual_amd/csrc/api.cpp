@@ -570,7 +570,7 @@ int static_scratch(void** out) {
 
 extern "C" {
 
-int dcoco_abi_version(void) { return 107; }
+int dcoco_abi_version(void) { return 108; }
 
 size_t dcoco_static_scratch_bytes(void) { return DCOCO_STATIC_SCRATCH_BYTES; }
 

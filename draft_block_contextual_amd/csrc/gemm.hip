@@ -569,18 +569,21 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
 // all groups are merged by lm_head_merge_kernel.
 constexpr int kLmBM = 128;
 constexpr int kLmBN = 256;
-constexpr int kLmMaxK = 16;
+constexpr int kLmMaxK = 64;
 using LmTile = DmaTile<kLmBM, kLmBN, 2, 4, 2>;
 
 __device__ __forceinline__ uint32_t key16_of(float x) { return order_key(bf16{f32_to_bf16(x)}); }
 
+// KMAX (16 or 64) bounds K: the rows' lists take 128 KMAX composites of LDS
+// beside the two ring slots (96 KB), all 160 KB at KMAX = 64.
+template <int KMAX>
 __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int tiles_m, int tiles_n, int groups,
                                                            int xcd_map, uint64_t* __restrict__ part) {
   constexpr int TM = LmTile::TM, TN = LmTile::TN, MW = LmTile::MW, NWB = LmTile::NWB;
+  static_assert(2 * LmTile::kStage + kLmBM * KMAX * 8 <= 160 * 1024, "LDS");
   __shared__ __align__(1024) char sm0[LmTile::kStage];
   __shared__ __align__(1024) char sm1[LmTile::kStage];
-  __shared__ uint64_t s_top[kLmBM][kLmMaxK];
-  __shared__ uint64_t s_kth[kLmBM];
+  __shared__ uint64_t s_top[kLmBM][KMAX];   // per row, sorted; entry K - 1 is 0 until K are held
   constexpr int kRowBytes = kLmBN * 2;                   // staged keys of one row
   constexpr int kRows0 = LmTile::kStage / kRowBytes;     // rows that fit in sm0
   static_assert(kLmBM - kRows0 <= LmTile::kStage / kRowBytes, "keys fit the ring");
@@ -605,8 +608,7 @@ __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int
   auto keyrow = [&](int r) -> uint16_t* {
     return reinterpret_cast<uint16_t*>(r < kRows0 ? sm0 + r * kRowBytes : sm1 + (r - kRows0) * kRowBytes);
   };
-  for (int i = tid; i < kLmBM * kLmMaxK; i += 512) (&s_top[0][0])[i] = 0ull;
-  for (int i = tid; i < kLmBM; i += 512) s_kth[i] = 0ull;
+  for (int i = tid; i < kLmBM * KMAX; i += 512) (&s_top[0][0])[i] = 0ull;
 
   for (int tn = g; tn < tiles_n; tn += groups) {
     const int n0 = tn * kLmBN;
@@ -626,7 +628,7 @@ __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int
     __syncthreads();
     for (int i = 0; i < kLmBM / 8; ++i) {
       const int r = wv + 8 * i;
-      const uint64_t thr = s_kth[r];
+      const uint64_t thr = s_top[r][K - 1];   // the row's K-th best so far (0 while not full)
       const uint16_t* kr = keyrow(r);
       uint64_t c[5];
       c[0] = l < K ? s_top[r][l] : 0ull;     // the current list, sorted
@@ -680,8 +682,6 @@ __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int
         }
       }
       if (l < K) s_top[r][l] = cur;
-      const uint64_t last = __shfl(cur, K - 1, kWave);
-      if (l == 0) s_kth[r] = last;           // 0 while the list is not full
     }
     __syncthreads();                         // the next tile's loads reuse the ring
   }
@@ -744,7 +744,7 @@ int lm_head_groups(int M, int V, int K) {
   const int tiles_m = (M + kLmBM - 1) / kLmBM;
   const int tiles_n = (V + kLmBN - 1) / kLmBN;
   int groups = std::max(1, 256 / tiles_m);
-  groups = std::min(groups, 1024 / K);         // the merge holds 1024 composites per row
+  groups = std::min(groups, 2048 / K);         // the merge holds 2048 composites per row
   groups = std::min(groups, tiles_n);
   if (groups >= 8) groups -= groups % 8;
   return groups;
@@ -769,15 +769,20 @@ hipError_t launch_lm_head_topk(const void* hd, const void* W_lm, int M, int V, i
   const int groups = lm_head_groups(M, V, K);
   const int xcd_map = groups % 8 == 0 ? 1 : 0;
   uint64_t* part = static_cast<uint64_t*>(workspace);
-  hipLaunchKernelGGL(lm_head_topk_kernel, dim3(tiles_m * groups), dim3(512), 0, st, p, K, tiles_m, tiles_n, groups,
-                     xcd_map, part);
+  if (K <= 16)
+    hipLaunchKernelGGL(lm_head_topk_kernel<16>, dim3(tiles_m * groups), dim3(512), 0, st, p, K, tiles_m, tiles_n,
+                       groups, xcd_map, part);
+  else
+    hipLaunchKernelGGL(lm_head_topk_kernel<64>, dim3(tiles_m * groups), dim3(512), 0, st, p, K, tiles_m, tiles_n,
+                       groups, xcd_map, part);
   const int count = groups * K;
 #define DCOCO_LMM(QV) \
   hipLaunchKernelGGL((lm_head_merge_kernel<QV>), dim3(M), dim3(64), 0, st, part, groups, M, K, ids, vals)
   if (count <= 64) DCOCO_LMM(1);
   else if (count <= 256) DCOCO_LMM(4);
   else if (count <= 512) DCOCO_LMM(8);
-  else DCOCO_LMM(16);
+  else if (count <= 1024) DCOCO_LMM(16);
+  else DCOCO_LMM(32);
 #undef DCOCO_LMM
   return hipGetLastError();
 }

@@ -185,7 +185,7 @@ int dcoco_select_path(const dcoco_dims* dims, const float* S, const float* cand_
  *   W_lm        [V, d_hidden] bf16            LM head (rows = vocabulary)
  *   cand_ids    [n_blocks*B, K] int32         out
  *   cand_logits [n_blocks*B, K] fp32          out: the bf16 logits, widened
- * bf16 storage only; K <= 16 and d_hidden a multiple of 64, else
+ * bf16 storage only; K <= 64 and d_hidden a multiple of 64, else
  * DCOCO_ERR_UNSUPPORTED.  Workspace: query with workspace == NULL (a few MB:
  * per-workgroup candidate lists).  Deterministic. */
 int dcoco_lm_head_topk(const dcoco_dims* dims, const void* hd, const void* W_lm,
@@ -358,7 +358,7 @@ const char* dcoco_status_string(int status);
  * entry points, 102 dcoco_select_path, 103 dcoco_loss and
  * dcoco_score_backward, 104 dcoco_lm_head_topk, 105
  * dcoco_represent_backward, 106 dcoco_correct_block_static, 107 the table
- * entry points for any d_proj. */
+ * entry points for any d_proj, 108 dcoco_lm_head_topk for K up to 64. */
 int dcoco_abi_version(void);
 
 #ifdef __cplusplus

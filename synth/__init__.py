@@ -175,6 +175,10 @@ CONFIGS = {
                        30.0, "peaks", 0, 2103, "random", "LM head: background only, K = 12, V = 20011"),
     "lmh_k1": Config("lmh_k1", _d(2, 4, 1, 3001, 128, 128, 64, 64, 64, 64, "bf16"),
                      30.0, "peaks", 1, 2104, "random", "LM head: K = 1"),
+    "lmh_k32": Config("lmh_k32", _d(3, 8, 32, 12007, 256, 256, 64, 64, 64, 64, "bf16"),
+                      30.0, "peaks", 0, 2105, "random", "LM head: K = 32, background only (ties at the K-th)"),
+    "lmh_k64": Config("lmh_k64", _d(5, 8, 64, 9001, 320, 320, 64, 64, 64, 64, "bf16"),
+                      30.0, "peaks", 64, 2106, "random", "LM head: K = 64, 40 rows"),
 }
 
 # tensor roles, in the fixed order their seeds are spawned

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     import draft_block_contextual_amd as dc
-    assert lib.dcoco_abi_version() == 107
+    assert lib.dcoco_abi_version() == 108
     assert dc.status_string(0) == "ok"
     for code in (-1, -2, -3, -4):
         assert dc.status_string(code) not in ("ok", "unknown status")

@@ -1059,7 +1059,7 @@ def _lm_check(ids, vals, logits, K):
     return exact / R
 
 
-@pytest.mark.parametrize("name", ["lmh_small", "lmh_rows", "lmh_flat", "lmh_k1"])
+@pytest.mark.parametrize("name", ["lmh_small", "lmh_rows", "lmh_flat", "lmh_k1", "lmh_k32", "lmh_k64"])
 def test_lm_head_topk_matches_oracle(name):
     import draft_block_contextual_amd as dc
     import torch
