@@ -267,11 +267,23 @@ hipError_t ab_gemm(const dcoco_dims* d, const dcoco_weights* w, const void* z, c
   return launch_gemm(q, st);
 }
 
-// the scores (need the pair term): the slab kernels, else A, B through memory and the grid
+// The walk's outputs, when the scoring launches may also walk.
+struct WalkOut {
+  const int32_t* ids;
+  int32_t* sel_idx;
+  int32_t* sel_tok;
+};
+
+// the scores (need the pair term): the slab kernels, else A, B through memory
+// and the grid.  With best, the walk's table.  With wk on the slab path (and a
+// block that fits), the finishing launch walks each block itself and
+// *walked is set; the caller then launches no walk.
 hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z, const float* cl, float* S,
-                      const ScoreLayout& L, hipStream_t st, int32_t* best = nullptr) {
+                      const ScoreLayout& L, hipStream_t st, int32_t* best = nullptr, const WalkOut* wk = nullptr,
+                      bool* walked = nullptr) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int P = d->n_blocks * (d->B - 1);
+  if (walked) *walked = false;
   if (P == 0) return hipSuccess;
   const int H = d->d_mlp;
   hipError_t e;
@@ -281,7 +293,13 @@ hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z
     q.z = z; q.W1 = w->W1; q.ldw1 = 2ll * d->d_z + d->d_pair;
     q.C = L.C; q.nq = dt == kDtypeBf16 ? 3 : 1; q.b1 = w->b1; q.w2 = w->w2; q.b2 = w->b2;
     q.cand_logits = cl; q.part = L.part; q.S = S; q.best = best;
-    return launch_score_slab(q, st);
+    const bool walk = wk != nullptr && block_finish_walk_fits(d->B, d->K, d->d_mlp);
+    if (walk) {
+      q.cand_ids = wk->ids; q.sel_idx = wk->sel_idx; q.sel_tok = wk->sel_tok;
+    }
+    e = launch_score_slab(q, st);
+    if (e == hipSuccess && walked) *walked = walk;
+    return e;
   }
   if ((e = ab_gemm(d, w, z, L, st)) != hipSuccess) return e;
   GridProblem g{};
@@ -863,8 +881,10 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
   if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
-  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best);
-  if (e == hipSuccess) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
+  const WalkOut wk{ids, sel_idx, sel_tok};
+  bool walked = false;
+  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best, &wk, &walked);
+  if (e == hipSuccess && !walked) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
   return hip_status(e);
 }
 
@@ -984,8 +1004,10 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
       e = launch_gemm(q, st);
     }
   }
-  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best);
-  if (e == hipSuccess) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
+  const WalkOut wk{ids, sel_idx, sel_tok};
+  bool walked = false;
+  if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best, &wk, &walked);
+  if (e == hipSuccess && !walked) e = walk_after_grid(S, best, cl, ids, d, sel_idx, sel_tok, st);
   return hip_status(e);
 }
 

@@ -112,8 +112,15 @@ struct ScoreSlabProblem {
   float* part;                 // [nslab, N*(B-1), K, K] fp32 scratch
   float* S;                    // [N, B-1, K, K]
   int32_t* best;               // [N, B-1, K] or null
+  // with sel_tok (and block_finish_walk_fits), one launch per block finishes
+  // the scores and walks: sel_idx (may be null) and sel_tok from cand_ids;
+  // best is then not written
+  const int32_t* cand_ids;
+  int32_t* sel_idx;
+  int32_t* sel_tok;
 };
 bool score_slab_supported(int dtype, int K, int rz, int H);
+bool block_finish_walk_fits(int B, int K, int H);
 int score_slab_count(int H);
 bool score_slab_preferred(int dtype, int N, int B, int K, int rz, int H);
 size_t score_slab_part_bytes(int N, int B, int K, int H);

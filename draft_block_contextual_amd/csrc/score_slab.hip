@@ -373,6 +373,117 @@ pair_finish_kernel(const float* __restrict__ part, int nslab, int P, int B, int 
   }
 }
 
+// One workgroup per block: the finish of all its pairs, then the walk
+// (review of arXiv 2610.12570, "Contextual Correction of Parallel Drafts for
+// Speculative Decoding", part 2 of "New approach: DCOCO", paper Sec. 3.3),
+// in one launch and without any workgroup waiting for another.  The threads
+// take the block's outputs o = p K^2 + a K + b in groups of VEC (VEC = 4 when
+// K^2 is a multiple of 4, so every group is one aligned 16-byte load per
+// slab): S_p(a, b) = l_{p+1}(b) + (the slabs' sums in slab order) + b2 is
+// stored and kept in LDS; then best_p(a) = argmax_b S_p(a, b) for every
+// (p, a) (largest order key, lowest b among equal keys); then wave 0 follows
+// k_0 = argmax_a l_0(a), k_{p+1} = best_p(k_p) and the chosen ids are written.
+// The sums are the same, in the same order, as the per-pair finish above.
+constexpr int kBlkThreads = 1024;
+constexpr int kBlkSlabs = 8;         // slab loads in flight per group
+constexpr int kBlkScores = 16384;    // scores of one block staged in LDS: (B - 1) K^2
+constexpr int kBlkTab = 2048;        // walk table entries: (B - 1) K
+constexpr int kBlkMaxB = 512;        // slots per block
+constexpr long long kBlkPartBytes = 256 * 1024;   // partial sums one workgroup reads
+
+template <int VEC>
+__device__ __forceinline__ void blk_load(const float* p, float (&v)[VEC]) {
+  if constexpr (VEC == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+    v[0] = *p;
+  }
+}
+
+template <int VEC>
+__global__ void __launch_bounds__(kBlkThreads)
+block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B, int K, float b2,
+                         const float* __restrict__ cand_logits, const int32_t* __restrict__ cand_ids,
+                         float* __restrict__ S, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_tok) {
+  __shared__ float sS[kBlkScores];
+  __shared__ int32_t sT[kBlkTab];
+  __shared__ int32_t sK[kBlkMaxB];
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int Bm1 = B - 1;
+  const int kk = K * K;
+  const int tot = Bm1 * kk;   // this block's scores, a multiple of VEC
+  const int ng = tot / VEC;
+  const long long np0 = static_cast<long long>(n) * Bm1;
+  const long long slab_stride = static_cast<long long>(P) * kk;
+  const float* pb = part + np0 * kk;
+  for (int g = tid; g < ng; g += kBlkThreads) {
+    float sum[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) sum[i] = 0.f;
+    for (int s0 = 0; s0 < nslab; s0 += kBlkSlabs) {
+      float v[kBlkSlabs][VEC];
+#pragma unroll
+      for (int q = 0; q < kBlkSlabs; ++q)   // slab clamped, its value masked below
+        blk_load<VEC>(pb + min(s0 + q, nslab - 1) * slab_stride + static_cast<long long>(g) * VEC, v[q]);
+#pragma unroll
+      for (int q = 0; q < kBlkSlabs; ++q)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+          if (s0 + q < nslab) sum[i] = (s0 + q == 0) ? v[q][i] : sum[i] + v[q][i];
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const int o = g * VEC + i;
+      const int p = o / kk;
+      const int b = o % K;
+      const float sv = cand_logits[(static_cast<long long>(n) * B + p + 1) * K + b] + (sum[i] + b2);
+      S[np0 * kk + o] = sv;
+      sS[o] = sv;
+    }
+  }
+  __syncthreads();
+  // the walk's table: best_p(a) for every (p, a) of the block
+  for (int r = tid; r < Bm1 * K; r += kBlkThreads) {
+    const float* row = sS + r * K;
+    uint32_t bk = order_key(row[0]);
+    int bi = 0;
+    for (int b = 1; b < K; ++b) {
+      const uint32_t k2 = order_key(row[b]);
+      if (k2 > bk) {
+        bk = k2;
+        bi = b;
+      }
+    }
+    sT[r] = bi;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int l = tid;
+    const float c0 = cand_logits[static_cast<long long>(n) * B * K + (l < K ? l : 0)];
+    const uint32_t key = l < K ? order_key(c0) : 0u;   // lanes >= K carry the NaN key
+    uint32_t m = key;
+    for (int off = kWave / 2; off > 0; off >>= 1)
+      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, kWave)));
+    int k = __builtin_ctzll(ballot(key == m));   // lowest index among the largest keys
+    if (l == 0) {
+      sK[0] = k;
+      for (int p = 0; p < Bm1; ++p) {
+        k = min(max(sT[p * K + k], 0), K - 1);
+        sK[p + 1] = k;
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < B; j += kBlkThreads) {
+    const int kj = sK[j];
+    const long long o = static_cast<long long>(n) * B + j;
+    if (sel_idx) sel_idx[o] = kj;
+    sel_tok[o] = cand_ids[o * K + kj];
+  }
+}
+
 }  // namespace
 
 bool score_slab_supported(int dtype, int K, int rz, int H) {
@@ -381,6 +492,16 @@ bool score_slab_supported(int dtype, int K, int rz, int H) {
 }
 
 int score_slab_count(int H) { return (H + kUS - 1) / kUS; }
+
+// One workgroup holds a block's scores and table in LDS, and reads no more
+// than kBlkPartBytes of partial sums: beyond that the per-pair finish, spread
+// over every pair, and the separate walk finish first.
+bool block_finish_walk_fits(int B, int K, int H) {
+  const long long tot = static_cast<long long>(B - 1) * K * K;
+  return B >= 2 && K >= 1 && K <= kWave && B <= kBlkMaxB && tot <= kBlkScores &&
+         static_cast<long long>(B - 1) * K <= kBlkTab &&
+         tot * score_slab_count(H) * static_cast<long long>(sizeof(float)) <= kBlkPartBytes;
+}
 
 // Up to about 40M grid elements (P K^2 H) the slab kernels finish first: their
 // time is set by each workgroup's walk over its chunk.  Beyond that the grid
@@ -432,16 +553,25 @@ hipError_t launch_score_slab(const ScoreSlabProblem& q, hipStream_t st) {
   if (q.rz == 64) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 2>>), grid, dim3(256), 0, st, d);       \
   else if (q.rz == 128) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 4>>), grid, dim3(256), 0, st, d); \
   else hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 8>>), grid, dim3(256), 0, st, d)
-  if (q.K <= 16) {
-    DCOCO_SLAB(16);
+  if (q.K <= 16) DCOCO_SLAB(16);
+  else DCOCO_SLAB(32);
+#undef DCOCO_SLAB
+  if (q.sel_tok != nullptr) {
+    // the finish of a whole block and its walk in one workgroup
+    if (q.cand_ids == nullptr || !block_finish_walk_fits(q.B, q.K, q.H)) return hipErrorInvalidValue;
+    if ((q.K * q.K) % 4 == 0)
+      hipLaunchKernelGGL((block_finish_walk_kernel<4>), dim3(q.N), dim3(kBlkThreads), 0, st, q.part, d.nslab, P,
+                         q.B, q.K, q.b2, q.cand_logits, q.cand_ids, q.S, q.sel_idx, q.sel_tok);
+    else
+      hipLaunchKernelGGL((block_finish_walk_kernel<1>), dim3(q.N), dim3(kBlkThreads), 0, st, q.part, d.nslab, P,
+                         q.B, q.K, q.b2, q.cand_logits, q.cand_ids, q.S, q.sel_idx, q.sel_tok);
+  } else if (q.K <= 16) {
     hipLaunchKernelGGL((pair_finish_kernel<16>), dim3(P), dim3(256), 0, st, q.part, d.nslab, P, q.B, q.K, q.b2,
                        q.cand_logits, q.S, q.best);
   } else {
-    DCOCO_SLAB(32);
     hipLaunchKernelGGL((pair_finish_kernel<32>), dim3(P), dim3(256), 0, st, q.part, d.nslab, P, q.B, q.K, q.b2,
                        q.cand_logits, q.S, q.best);
   }
-#undef DCOCO_SLAB
   return hipGetLastError();
 }
 

@@ -584,6 +584,39 @@ def test_correct_block_walk_fallback_shapes(B, K):
     np.testing.assert_array_equal(out["sel_tok"], rt)
 
 
+@pytest.mark.parametrize("name", ["mid_bf16", "h512_bf16", "k32_small", "k1_bf16", "odd_k_slab", "b30_k7_slab"])
+def test_correct_block_equals_separate_calls(name):
+    # On these shapes the whole-path call scores with the on-chip slab kernels
+    # and one workgroup per block finishes the sums and walks the block (K^2 a
+    # multiple of 4 or not); dcoco_score finishes pair by pair and dcoco_select
+    # walks separately.  The sums are added in the same order, so S is
+    # bit-identical and so is the walk.
+    import draft_block_contextual_amd as dc
+    import torch
+    print(f"case correct_block vs separate calls {name}", flush=True)
+    extra = {
+        "odd_k_slab": synth.Config("odd_k_slab", synth._d(3, 9, 7, 3001, 128, 128, 64, 64, 64, 96, "bf16"),
+                                   30.0, "peaks", 7, 2201, "random"),
+        "b30_k7_slab": synth.Config("b30_k7_slab", synth._d(2, 30, 7, 2003, 128, 96, 64, 128, 64, 160, "bf16"),
+                                    30.0, "peaks", 7, 2202, "random"),
+    }
+    inp = synth.make_inputs(extra[name]) if name in extra else _inputs(name)
+    dims, w, logits, h, E = device_inputs(inp)
+    out = dc.correct_block(dims, w, logits, h, E, want_all=True)
+    ids, cl = out["cand_ids"], out["cand_logits"]
+    z, s = dc.represent(dims, w, h, E, ids)
+    S = dc.score(dims, w, z, s, cl)
+    si, st = dc.select(dims, S, cl, ids)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(out["S"]), _np(S))
+    np.testing.assert_array_equal(_np(out["sel_idx"]), _np(si))
+    np.testing.assert_array_equal(_np(out["sel_tok"]), _np(st))
+    o = {k: _np(v) for k, v in out.items()}
+    ri, rt, _ = O.greedy_walk(o["S"].astype(np.float64), o["cand_logits"].astype(np.float64), o["cand_ids"])
+    np.testing.assert_array_equal(o["sel_idx"], ri)
+    np.testing.assert_array_equal(o["sel_tok"], rt)
+
+
 def test_degenerate_shapes_select_the_drafter():
     # B = 1: no transitions, every slot keeps the drafter's top-1; K = 1: the
     # only candidate is chosen whatever the scores
