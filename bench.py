@@ -178,6 +178,7 @@ def kernel_rooflines(figs, work):
         "ab_gemm": ("mfma", work["ab_flops"]),
         "pair_term": ("mfma", work["pair_flops"]),
         "grid": ("alu", work["grid_elems"]),
+        "slab": ("alu", work["grid_elems"]),
     }
     out = {}
     for k, f in figs.items():

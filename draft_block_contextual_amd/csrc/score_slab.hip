@@ -16,10 +16,10 @@
 // B' = -log2(e) (B + C_p) and w' = -ln(2) w2 a term is
 // w2 SiLU(u) = w' (A' + B') / (1 + 2^A' 2^B'); a wave with some |A'| > 64 in
 // a pair stages A', B' instead and evaluates 2^(A'+B') per element.  Each
-// pair's sum over the slab (the four waves added in a fixed order once the
-// chunk is done) is stored per slab;
-// pair_finish_kernel adds the slabs in order, adds l_{p+1}(b) + b2 and takes
-// each row's argmax for the walk.
+// pair's sum over the slab (the four waves added in a fixed order) is stored
+// per slab; pair_finish_kernel, or block_finish_walk_kernel for a whole block,
+// adds the slabs in order, adds l_{p+1}(b) + b2 and takes each row's argmax
+// for the walk.
 #include <algorithm>
 
 #include "common.h"
@@ -50,8 +50,11 @@ struct SlabDev {
 // KR candidates padded to whole 16-row MFMA tiles; a lane owns a TA x TA
 // block of (a, b) outputs (TA = KR / 8, so the wave's 64 lanes cover the
 // whole K x K grid) over all 16 of the wave's units: a lane's sums are the
-// wave's, and no lane reduction is needed.  Each wave keeps its sum of every
-// pair of the chunk in LDS; the four waves are added at the end.
+// wave's, and no lane reduction is needed.  Each wave puts its sum of a pair
+// in LDS; after the step's barrier the workgroup adds the four waves in order
+// and stores the pair's slab sum.  For KR = 16 the sums are double-buffered
+// (the pair finished at one step is added up at the next), so a chunk may hold
+// any number of pairs; for KR = 32 a chunk is one pair.
 template <int KRV, int NKSV>
 struct SlabShape {
   static constexpr int KR = KRV;
@@ -63,8 +66,8 @@ struct SlabShape {
   static constexpr int WREG = 4 * ARR + kUW;       // a wave's region: 4 arrays + w' per unit
   static constexpr int STAGE = 4 * WREG;           // floats of the four waves' regions
   static constexpr int ZBUF = KR * NKS * 32 * 2;   // bytes of one slot's z rows
-  static constexpr int MAXPC = KR == 16 ? 4 : 1;     // pairs per chunk
-  static constexpr int SUMS = 4 * MAXPC * KR * KR;   // [wave][pair][KR * KR] sums
+  static constexpr int NBUF = KR == 16 ? 2 : 1;      // pair-sum buffers (1: one pair per chunk)
+  static constexpr int SUMS = NBUF * 4 * KR * KR;     // [buffer][wave][KR * KR] sums
   static_assert((KR / TA) * (KR / TA) == kWave, "one output block per lane");
   static_assert(NKS >= 2 && NKS <= kMaxKs, "r_z");
   // K <= 16: three workgroups per CU
@@ -87,11 +90,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <typename SS>
 __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(SlabDev g) {
-  constexpr int KR = SS::KR, TA = SS::TA, RT = SS::RT, ARR = SS::ARR, MAXPC = SS::MAXPC, NKS = SS::NKS;
+  constexpr int KR = SS::KR, TA = SS::TA, RT = SS::RT, ARR = SS::ARR, NBUF = SS::NBUF, NKS = SS::NKS;
   __shared__ __align__(1024) char zb0[SS::ZBUF];
   __shared__ __align__(1024) char zb1[SS::ZBUF];
   __shared__ __align__(16) float smem[SS::STAGE];
-  __shared__ __align__(16) float sums[SS::SUMS];   // [wave][pair of the chunk][KR * KR]
+  __shared__ __align__(16) float sums[SS::SUMS];   // [pair p % NBUF][wave][KR * KR]
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -125,22 +128,10 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   float* sWB = wreg + 3 * ARR;       // w'B'
   float* sWq = wreg + 4 * ARR;       // w' per unit (per-element form)
 
-  // ---- this lane's unit: W1a and W1b fragments for every k step, per-unit terms
+  // ---- this lane's unit
   const int u = slab * kUS + wv * kUW + fr;
   const int uc = min(u, H - 1);
   const bool uin = u < H;
-  bf16x8_t wa[NKS], wb[NKS];
-  {
-    const uint16_t* src = g.W1 + static_cast<long long>(uc) * g.ldw1 + fq * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      wa[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + ks * 32));
-      wb[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + rz + ks * 32));
-    }
-  }
-  const float wq = uin ? kNegLn2 * bf16_to_f32(g.w2[uc]) : 0.f;
-  const float bb = g.b1 ? bf16_to_f32(g.b1[uc]) : 0.f;
-  if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
 
   // ---- z rows of slot t into zb[t & 1] (KR rows; rows past K repeat row K-1)
   const long long zrow0 = static_cast<long long>(n) * B * K;
@@ -157,26 +148,84 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
     }
   };
 
-  // C_p + b1 of this lane's unit, pair p of the block (0 <= p < B - 1)
-  auto load_c = [&](int p) -> float {
+  // the parts of C_p for this lane's unit, pair p of the block (0 <= p < B - 1):
+  // loaded unconditionally (part indices clamped to the parts there are) and
+  // added only after the step's explicit wait, so no load is waited on early
+  float cr[3];
+  auto load_c = [&](int p) {
     const long long np = static_cast<long long>(n) * Bm1 + p;
-    float c = g.C[np * H + uc];
-    if (g.nq > 1) c += g.C[(static_cast<long long>(g.P) + np) * H + uc];
-    if (g.nq > 2) c += g.C[(2ll * g.P + np) * H + uc];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) cr[q] = g.C[(min(q, g.nq - 1) * static_cast<long long>(g.P) + np) * H + uc];
+  };
+  // C_p + b1, parts added in order (the loads have landed)
+  auto sum_c = [&](float bb) -> float {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) asm volatile("" : "+v"(cr[q]));
+    float c = cr[0];
+    if (g.nq > 1) c += cr[1];
+    if (g.nq > 2) c += cr[2];
     return c + bb;
   };
 
+  // every load of the prologue in flight at once: slot t0's rows, C of pair
+  // t0, the W1a and W1b fragments of every k step, w2 and b1
   issue_z(t0);
-  float c_prev = load_c(t0);         // C of the pair completed at the next step
-  bool slow_prev = false;            // that pair takes the per-element form (wave-uniform)
+  load_c(t0);
+  bf16x8_t wa[NKS], wb[NKS];
+  {
+    const uint16_t* src = g.W1 + static_cast<long long>(uc) * g.ldw1 + fq * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      wa[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + ks * 32));
+      wb[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + rz + ks * 32));
+    }
+  }
+  uint32_t w2b = g.w2[uc];
+  uint32_t b1b = (g.b1 ? g.b1 : g.w2)[uc];
   asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  // the compiler does not see the wait above: passing every loaded register
+  // through an empty asm ends its tracking of these loads here, so it never
+  // waits on them again inside the loop (where that wait would also cover
+  // the loads issued there)
+  asm volatile("" : "+v"(w2b), "+v"(b1b));
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+    u32x4 x = __builtin_bit_cast(u32x4, wa[ks]);
+    u32x4 y = __builtin_bit_cast(u32x4, wb[ks]);
+    asm volatile("" : "+v"(x), "+v"(y));
+    wa[ks] = __builtin_bit_cast(bf16x8_t, x);
+    wb[ks] = __builtin_bit_cast(bf16x8_t, y);
+  }
+  const float wq = uin ? kNegLn2 * bf16_to_f32(static_cast<uint16_t>(w2b)) : 0.f;
+  const float bb = g.b1 ? bf16_to_f32(static_cast<uint16_t>(b1b)) : 0.f;
+  if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
+  float c_prev = sum_c(bb);          // C of the pair completed at the next step
+  bool slow_prev = false;            // that pair takes the per-element form (wave-uniform)
   __syncthreads();                   // slot t0's rows and the w' table are in LDS
+
+  // the slab's sum of pair p: the four waves added in order
+  const int kk = K * K;
+  auto store_pair = [&](int p) {
+    const float* sb = sums + (p % NBUF) * 4 * KR * KR;
+    float* dst = g.part + (static_cast<long long>(slab) * g.P + static_cast<long long>(n) * Bm1 + p) * kk;
+    for (int i = tid; i < kk; i += 256) {
+      const int a = i / K;
+      const int o = a * KR + (i - a * K);
+      float sum = sb[o];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) sum += sb[w * KR * KR + o];
+      dst[i] = sum;
+    }
+  };
 
   for (int t = t0; t <= t1; ++t) {
     const char* zt = (t & 1) ? zb1 : zb0;
     if (t < t1) issue_z(t + 1);      // the other buffer was last read at step t - 1
+    // pair t - 2 was finished at step t - 1; its buffer is next written at step t + 1
+    if (NBUF == 2 && t >= t0 + 2) store_pair(t - 2);
     const float cq = kNegLog2e * c_prev;                 // pair t - 1 (when t > t0)
-    if (t > t0 && t < t1) c_prev = load_c(t);            // pair t, used at step t + 1
+    if (t > t0 && t < t1) load_c(t);                     // pair t, used at step t + 1
 
     // ---- A_t = W1a z_t, B_t = W1b z_t for the wave's 16 units
     f32x4_t accA[RT], accB[RT];
@@ -258,8 +307,8 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
               }
         }
       }
-      // the wave's sum for pair p (its 16 units), kept until the chunk is done
-      float* ws = sums + (wv * MAXPC + (p - t0)) * KR * KR;
+      // the wave's sum for pair p (its 16 units), added up after the barrier
+      float* ws = sums + ((p % NBUF) * 4 + wv) * KR * KR;
 #pragma unroll
       for (int i = 0; i < TA; ++i)
 #pragma unroll
@@ -289,24 +338,11 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t + 1's rows (this wave's share)
+    if (t > t0 && t < t1) c_prev = sum_c(bb);
     __syncthreads();                                       // ... and every other wave's
   }
-  // the slab's sum per pair: the four waves added in order.  The chunk's
-  // pairs are consecutive in the pair index, so this is one contiguous run
-  // of (t1 - t0) K^2 sums.
-  float* dst = g.part + (static_cast<long long>(slab) * g.P + static_cast<long long>(n) * Bm1 + t0) * K * K;
-  const int kk = K * K;
-  const int total = (t1 - t0) * kk;
-  for (int i = tid; i < total; i += 256) {
-    const int q = i / kk;
-    const int idx = i - q * kk;
-    const int a = idx / K;
-    const int o = q * KR * KR + a * KR + (idx - a * K);
-    float sum = sums[o];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) sum += sums[w * MAXPC * KR * KR + o];
-    dst[i] = sum;
-  }
+  // the last pair (and, with one buffer, the only one)
+  if (t1 > t0) store_pair(t1 - 1);
 }
 
 // S_p(a, b) = l_{p+1}(b) + (sum of the slabs' partial sums, in slab order) + b2,
@@ -389,6 +425,8 @@ constexpr int kBlkSlabs = 8;         // slab loads in flight per group
 constexpr int kBlkScores = 16384;    // scores of one block staged in LDS: (B - 1) K^2
 constexpr int kBlkTab = 2048;        // walk table entries: (B - 1) K
 constexpr int kBlkMaxB = 512;        // slots per block
+constexpr int kBlkIds = kBlkTab + kWave;   // candidate ids of a block: B K <= (B - 1) K + K
+constexpr int kBlkIdsPerT = (kBlkIds + kBlkThreads - 1) / kBlkThreads;
 constexpr long long kBlkPartBytes = 256 * 1024;   // partial sums one workgroup reads
 
 template <int VEC>
@@ -409,6 +447,8 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
   __shared__ float sS[kBlkScores];
   __shared__ int32_t sT[kBlkTab];
   __shared__ int32_t sK[kBlkMaxB];
+  __shared__ int32_t sId[kBlkIds];
+  __shared__ float sC0[kWave];
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int Bm1 = B - 1;
@@ -418,7 +458,21 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
   const long long np0 = static_cast<long long>(n) * Bm1;
   const long long slab_stride = static_cast<long long>(P) * kk;
   const float* pb = part + np0 * kk;
+  // the block's candidate ids and slot 0's logits are loaded now, with the
+  // sums, and put in LDS once the sums are done (indices clamped)
+  const int nid = B * K;
+  const int32_t* idn = cand_ids + static_cast<long long>(n) * nid;
+  int32_t idv[kBlkIdsPerT];
+#pragma unroll
+  for (int i = 0; i < kBlkIdsPerT; ++i) idv[i] = idn[min(tid + i * kBlkThreads, nid - 1)];
+  const float c0v = cand_logits[static_cast<long long>(n) * nid + min(tid, K - 1)];
   for (int g = tid; g < ng; g += kBlkThreads) {
+    float ln[VEC];   // l_{p+1}(b) of the group's outputs, loaded before the sums
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const int o = g * VEC + i;
+      ln[i] = cand_logits[(static_cast<long long>(n) * B + o / kk + 1) * K + o % K];
+    }
     float sum[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) sum[i] = 0.f;
@@ -436,13 +490,15 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       const int o = g * VEC + i;
-      const int p = o / kk;
-      const int b = o % K;
-      const float sv = cand_logits[(static_cast<long long>(n) * B + p + 1) * K + b] + (sum[i] + b2);
+      const float sv = ln[i] + (sum[i] + b2);
       S[np0 * kk + o] = sv;
       sS[o] = sv;
     }
   }
+#pragma unroll
+  for (int i = 0; i < kBlkIdsPerT; ++i)
+    if (tid + i * kBlkThreads < nid) sId[tid + i * kBlkThreads] = idv[i];
+  if (tid < K) sC0[tid] = c0v;
   __syncthreads();
   // the walk's table: best_p(a) for every (p, a) of the block
   for (int r = tid; r < Bm1 * K; r += kBlkThreads) {
@@ -461,8 +517,7 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
   __syncthreads();
   if (tid < kWave) {
     const int l = tid;
-    const float c0 = cand_logits[static_cast<long long>(n) * B * K + (l < K ? l : 0)];
-    const uint32_t key = l < K ? order_key(c0) : 0u;   // lanes >= K carry the NaN key
+    const uint32_t key = l < K ? order_key(sC0[l]) : 0u;   // lanes >= K carry the NaN key
     uint32_t m = key;
     for (int off = kWave / 2; off > 0; off >>= 1)
       m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, kWave)));
@@ -480,11 +535,13 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
     const int kj = sK[j];
     const long long o = static_cast<long long>(n) * B + j;
     if (sel_idx) sel_idx[o] = kj;
-    sel_tok[o] = cand_ids[o * K + kj];
+    sel_tok[o] = sId[j * K + kj];
   }
 }
 
 }  // namespace
+
+constexpr long long kSlabSlots = 3 * 256;   // resident K <= 16 slab workgroups: three on each of 256 CUs
 
 bool score_slab_supported(int dtype, int K, int rz, int H) {
   return dtype == kDtypeBf16 && K >= 1 && K <= 32 && (rz == 64 || rz == 128 || rz == 256) && H >= 16 &&
@@ -503,13 +560,18 @@ bool block_finish_walk_fits(int B, int K, int H) {
          tot * score_slab_count(H) * static_cast<long long>(sizeof(float)) <= kBlkPartBytes;
 }
 
-// Up to about 40M grid elements (P K^2 H) the slab kernels finish first: their
-// time is set by each workgroup's walk over its chunk.  Beyond that the grid
-// kernel after the A, B GEMM evaluates the elements at a higher rate and wins
-// (at 32 blocks of B = 16, K = 16, H = 512 the two take about the same time).
+// For K <= 16 the slab kernels scored faster than the A, B GEMM and the grid
+// kernel at every block count measured (16 to 96 blocks of B = 16, K = 16,
+// H = 512, r_z = 256: 130 against 133 us per call at 32 blocks, 326 against
+// 352 at 96); they are taken while one chunk per block keeps the launch within
+// one resident round (blocks x slabs <= 768), the largest count measured.
+// For K > 16 (one pair per workgroup) up to about 40M grid elements
+// (P K^2 H), as measured for the earlier K <= 16 form.
 bool score_slab_preferred(int dtype, int N, int B, int K, int rz, int H) {
+  if (!score_slab_supported(dtype, K, rz, H)) return false;
+  if (K <= 16) return static_cast<long long>(N) * score_slab_count(H) <= kSlabSlots;
   const double elems = static_cast<double>(N) * (B - 1) * K * K * H;
-  return score_slab_supported(dtype, K, rz, H) && elems <= 40.0e6;
+  return elems <= 40.0e6;
 }
 
 size_t score_slab_part_bytes(int N, int B, int K, int H) {
@@ -518,17 +580,17 @@ size_t score_slab_part_bytes(int N, int B, int K, int H) {
          static_cast<size_t>(K) * static_cast<size_t>(K);
 }
 
-// pairs per chunk: about two workgroups per CU, every chunk at least one
-// pair and no more than the workgroup keeps in LDS (4 for K <= 16, else 1)
+// pairs per chunk: for K <= 16 as many chunks as keep every resident
+// workgroup slot busy for one round (three workgroups per CU), each at least
+// one pair; for K > 16 one pair per chunk (one pair-sum buffer)
 int score_slab_pairs_per_chunk(int N, int B, int K, int H) {
   const int Bm1 = B - 1;
-  if (Bm1 < 1) return 1;
+  if (Bm1 < 1 || K > 16) return 1;
   const long long wg = static_cast<long long>(N) * score_slab_count(H);
-  long long chunks = (512 + wg - 1) / wg;
+  long long chunks = kSlabSlots / wg;
   if (chunks > Bm1) chunks = Bm1;
   if (chunks < 1) chunks = 1;
-  const int pc = static_cast<int>((Bm1 + chunks - 1) / chunks);
-  return std::min(pc, K <= 16 ? 4 : 1);
+  return static_cast<int>((Bm1 + chunks - 1) / chunks);
 }
 
 hipError_t launch_score_slab(const ScoreSlabProblem& q, hipStream_t st) {

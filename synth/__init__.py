@@ -165,6 +165,12 @@ CONFIGS = {
     # d_proj = 512, as in the d = 8192 workload: the table path's GEMM gathers the rows
     "r512_bf16": Config("r512_bf16", _d(2, 6, 16, 6007, 512, 512, 512, 256, 128, 256, "bf16"),
                         30.0, "peaks", 16, 2015, "random", "d_proj = 512 on a small shape"),
+    # many blocks, so that on-chip scoring gives each workgroup a run of
+    # three pairs (a whole and a ragged slab count)
+    "chunks_bf16": Config("chunks_bf16", _d(128, 16, 16, 3001, 64, 64, 64, 64, 64, 64, "bf16"),
+                          30.0, "peaks", 16, 2016, "random", "128 blocks of B = 16, K = 16, H = 64"),
+    "chunks_ragged": Config("chunks_ragged", _d(64, 16, 12, 3001, 64, 64, 64, 128, 64, 96, "bf16"),
+                            30.0, "peaks", 12, 2017, "random", "64 blocks of B = 16, K = 12, H = 96"),
     # LM-head shapes (head tied to E, so d == e): ragged vocabulary tiles,
     # ragged row tiles, rows without planted peaks (bf16 ties at the K-th)
     "lmh_small": Config("lmh_small", _d(2, 8, 16, 5003, 256, 256, 64, 64, 64, 64, "bf16"),

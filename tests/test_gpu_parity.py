@@ -50,7 +50,8 @@ def _oracle(name, blocks=None):
 
 
 SMALL = ["tiny", "tiny_zero", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "mid_f32",
-         "k64_small", "k32_small", "widez_bf16", "tall_bf16", "b1_bf16", "k1_bf16", "wide_max"]
+         "k64_small", "k32_small", "widez_bf16", "tall_bf16", "b1_bf16", "k1_bf16", "wide_max",
+         "chunks_bf16", "chunks_ragged"]
 
 
 def _run_block(name):
@@ -584,7 +585,8 @@ def test_correct_block_walk_fallback_shapes(B, K):
     np.testing.assert_array_equal(out["sel_tok"], rt)
 
 
-@pytest.mark.parametrize("name", ["mid_bf16", "h512_bf16", "k32_small", "k1_bf16", "odd_k_slab", "b30_k7_slab"])
+@pytest.mark.parametrize("name", ["mid_bf16", "h512_bf16", "k32_small", "k1_bf16", "odd_k_slab", "b30_k7_slab",
+                                  "chunks_bf16", "chunks_ragged"])
 def test_correct_block_equals_separate_calls(name):
     # On these shapes the whole-path call scores with the on-chip slab kernels
     # and one workgroup per block finishes the sums and walks the block (K^2 a

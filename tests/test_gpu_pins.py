@@ -72,10 +72,14 @@ def _slab(K):
 
 def _on_chip(D):
     """The library forms A and B on chip for bf16 with K <= 32, r_z of 64, 128
-    or 256, and at most 40M grid elements N (B-1) K^2 H; otherwise they go
-    through memory to the grid kernel."""
-    return (D.dtype == "bf16" and D.K <= 32 and D.r_z in (64, 128, 256) and D.H % 16 == 0
-            and D.n_blocks * (D.B - 1) * D.K * D.K * D.H <= 40e6)
+    or 256 and H a multiple of 16: for K <= 16 while blocks x slabs of 64
+    units stay within 768, for K > 16 up to 40M grid elements N (B-1) K^2 H;
+    otherwise they go through memory to the grid kernel."""
+    if not (D.dtype == "bf16" and D.K <= 32 and D.r_z in (64, 128, 256) and D.H % 16 == 0):
+        return False
+    if D.K <= 16:
+        return D.n_blocks * ((D.H + 63) // 64) <= 768
+    return D.n_blocks * (D.B - 1) * D.K * D.K * D.H <= 40e6
 
 
 def _group(D):
@@ -131,7 +135,7 @@ def _check_scores(got, Sref, D, z, s, cand_vals, W1, inp):
 
 @pytest.mark.parametrize("name,mode,tile", [("k32_small", "units", 1), ("k64_small", "units", 1),
                                             ("h512_bf16", "units", 1), ("mid_bf16", "slots", 1),
-                                            ("h512_bf16", "units", 21), ("mid_bf16", "slots", 11),
+                                            ("h512_bf16", "units", 33), ("mid_bf16", "slots", 49),
                                             ("k32_f32", "units", 1), ("mid_f32", "slots", 1),
                                             ("small_f32", "slots", 1)])
 def test_score_large_preactivations(name, mode, tile):
