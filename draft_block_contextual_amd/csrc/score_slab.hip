@@ -21,6 +21,7 @@
 // adds the slabs in order, adds l_{p+1}(b) + b2 and takes each row's argmax
 // for the walk.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "dma.h"
@@ -171,32 +172,46 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   // t0, the W1a and W1b fragments of every k step, w2 and b1
   issue_z(t0);
   load_c(t0);
-  bf16x8_t wa[NKS], wb[NKS];
-  {
-    const uint16_t* src = g.W1 + static_cast<long long>(uc) * g.ldw1 + fq * 8;
+  // W1a and W1b rows of the wave's 16 units, loaded with the four 16-byte
+  // quarters of a unit's 64-byte slice of each k step in adjacent lanes
+  // (lane 4 v + q: unit v, quarter q), so each group of four lanes reads one
+  // contiguous segment; the fragments are moved into the MFMA layout below.
+  // (Whole 128-byte lines per eight lanes measured slower.)  W1b is first
+  // needed at step t0 + 1, so its loads are issued last and waited on at the
+  // end of step t0.
+  using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+  u32x4 ra[NKS], rb[NKS];
+  const uint16_t* wsrc = g.W1 + static_cast<long long>(min(slab * kUS + wv * kUW + (l >> 2), H - 1)) * g.ldw1 +
+                         (l & 3) * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      wa[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + ks * 32));
-      wb[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + rz + ks * 32));
-    }
-  }
+  for (int ks = 0; ks < NKS; ++ks) ra[ks] = *reinterpret_cast<const u32x4*>(wsrc + ks * 32);
   uint32_t w2b = g.w2[uc];
   uint32_t b1b = (g.b1 ? g.b1 : g.w2)[uc];
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-  // the compiler does not see the wait above: passing every loaded register
-  // through an empty asm ends its tracking of these loads here, so it never
-  // waits on them again inside the loop (where that wait would also cover
-  // the loads issued there)
-  asm volatile("" : "+v"(w2b), "+v"(b1b));
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
-    u32x4 x = __builtin_bit_cast(u32x4, wa[ks]);
-    u32x4 y = __builtin_bit_cast(u32x4, wb[ks]);
-    asm volatile("" : "+v"(x), "+v"(y));
-    wa[ks] = __builtin_bit_cast(bf16x8_t, x);
-    wb[ks] = __builtin_bit_cast(bf16x8_t, y);
-  }
+  for (int ks = 0; ks < NKS; ++ks) rb[ks] = *reinterpret_cast<const u32x4*>(wsrc + rz + ks * 32);
+  // every load but the W1b ones has landed (loads complete in issue order)
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NKS) : "memory");
+  // the compiler does not see the wait above: passing a loaded register
+  // through an empty asm ends its tracking of that load there, so it never
+  // waits on it again inside the loop (where that wait would also cover the
+  // loads issued there)
+  asm volatile("" : "+v"(w2b), "+v"(b1b));
+  // MFMA B fragments: lane l holds unit l & 15, k chunk l >> 4 of each k
+  // step, which lane 4 (l & 15) + (l >> 4) loaded
+  bf16x8_t wa[NKS], wb[NKS];
+  auto gather = [&](u32x4 (&r)[NKS], bf16x8_t (&w)[NKS]) {
+    const int from = 4 * (4 * fr + fq);   // byte index of the source lane
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      asm volatile("" : "+v"(r[ks]));
+      u32x4 x;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        x[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(r[ks][d])));
+      w[ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  };
+  gather(ra, wa);
   const float wq = uin ? kNegLn2 * bf16_to_f32(static_cast<uint16_t>(w2b)) : 0.f;
   const float bb = g.b1 ? bf16_to_f32(static_cast<uint16_t>(b1b)) : 0.f;
   if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
@@ -219,16 +234,9 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
     }
   };
 
-  for (int t = t0; t <= t1; ++t) {
-    const char* zt = (t & 1) ? zb1 : zb0;
-    if (t < t1) issue_z(t + 1);      // the other buffer was last read at step t - 1
-    // pair t - 2 was finished at step t - 1; its buffer is next written at step t + 1
-    if (NBUF == 2 && t >= t0 + 2) store_pair(t - 2);
-    const float cq = kNegLog2e * c_prev;                 // pair t - 1 (when t > t0)
-    if (t > t0 && t < t1) load_c(t);                     // pair t, used at step t + 1
-
-    // ---- A_t = W1a z_t, B_t = W1b z_t for the wave's 16 units
-    f32x4_t accA[RT], accB[RT];
+  // A_t = W1a z_t and / or B_t = W1b z_t for the wave's 16 units
+  auto form = [&](auto DA, auto DB, const char* zt, f32x4_t (&accA)[RT], f32x4_t (&accB)[RT]) {
+    constexpr bool kA = decltype(DA)::value, kB = decltype(DB)::value;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       accA[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -241,108 +249,144 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
         const int r = rt * 16 + fr;
         const bf16x8_t x = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const uint4*>(zt + r * rowb + zswz(r, ks * 4 + fq) * 16));
-        accA[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, wa[ks], accA[rt], 0, 0, 0);
-        accB[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, wb[ks], accB[rt], 0, 0, 0);
+        if constexpr (kA) accA[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, wa[ks], accA[rt], 0, 0, 0);
+        if constexpr (kB) accB[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, wb[ks], accB[rt], 0, 0, 0);
       }
     }
+  };
 
-    // ---- pair t - 1: its successor side from B_t, then its grid
-    if (t > t0) {
-      const int p = t - 1;
+  // pair p: its successor side from B_{p+1} (cq = -log2(e) (C_p + b1)), then
+  // its grid; the wave's sum is left in LDS for the workgroup to add up
+  auto finish_pair = [&](int p, float cq, const f32x4_t (&accB)[RT]) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float bp = fmaf(kNegLog2e, accB[rt][v], cq);
-          const int o = sidx(rt * 16 + fq * 4 + v, fr);
-          const float e = __builtin_amdgcn_exp2f(bp);
-          sEB[o] = slow_prev ? bp : e;
-          sWB[o] = wq * bp;
-        }
-      wave_lds_sync();
-      float acc[TA][TA];
-#pragma unroll
-      for (int i = 0; i < TA; ++i)
-#pragma unroll
-        for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
-      if (!slow_prev) {
-        for (int h = 0; h < kUW; h += 4) {
-          float4 ea[TA], wa4[TA], eb[TA], wb4[TA];
-#pragma unroll
-          for (int i = 0; i < TA; ++i) {
-            ea[i] = *reinterpret_cast<const float4*>(sEA + sidx(la * TA + i, h));
-            wa4[i] = *reinterpret_cast<const float4*>(sWA + sidx(la * TA + i, h));
-            eb[i] = *reinterpret_cast<const float4*>(sEB + sidx(lb * TA + i, h));
-            wb4[i] = *reinterpret_cast<const float4*>(sWB + sidx(lb * TA + i, h));
-          }
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-            for (int i = 0; i < TA; ++i)
-#pragma unroll
-              for (int j = 0; j < TA; ++j) {
-                const float den = fmaf(ea[i][c4], eb[j][c4], 1.0f);
-                const float r = __builtin_amdgcn_rcpf(den);
-                acc[i][j] = fmaf(wa4[i][c4] + wb4[j][c4], r, acc[i][j]);
-              }
-        }
-      } else {
-        for (int h = 0; h < kUW; h += 4) {
-          float4 av[TA], bv[TA];
-#pragma unroll
-          for (int i = 0; i < TA; ++i) {
-            av[i] = *reinterpret_cast<const float4*>(sEA + sidx(la * TA + i, h));
-            bv[i] = *reinterpret_cast<const float4*>(sEB + sidx(lb * TA + i, h));
-          }
-          const float4 w4 = *reinterpret_cast<const float4*>(sWq + h);
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-            for (int i = 0; i < TA; ++i)
-#pragma unroll
-              for (int j = 0; j < TA; ++j) {
-                const float tt = av[i][c4] + bv[j][c4];
-                const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(tt));
-                acc[i][j] = fmaf(w4[c4], tt * r, acc[i][j]);
-              }
-        }
+      for (int v = 0; v < 4; ++v) {
+        const float bp = fmaf(kNegLog2e, accB[rt][v], cq);
+        const int o = sidx(rt * 16 + fq * 4 + v, fr);
+        const float e = __builtin_amdgcn_exp2f(bp);
+        sEB[o] = slow_prev ? bp : e;
+        sWB[o] = wq * bp;
       }
-      // the wave's sum for pair p (its 16 units), added up after the barrier
-      float* ws = sums + ((p % NBUF) * 4 + wv) * KR * KR;
+    wave_lds_sync();
+    float acc[TA][TA];
 #pragma unroll
-      for (int i = 0; i < TA; ++i)
+    for (int i = 0; i < TA; ++i)
 #pragma unroll
-        for (int j = 0; j < TA; ++j) ws[(la * TA + i) * KR + lb * TA + j] = acc[i][j];
+      for (int j = 0; j < TA; ++j) acc[i][j] = 0.f;
+    if (!slow_prev) {
+      for (int h = 0; h < kUW; h += 4) {
+        float4 ea[TA], wa4[TA], eb[TA], wb4[TA];
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+          ea[i] = *reinterpret_cast<const float4*>(sEA + sidx(la * TA + i, h));
+          wa4[i] = *reinterpret_cast<const float4*>(sWA + sidx(la * TA + i, h));
+          eb[i] = *reinterpret_cast<const float4*>(sEB + sidx(lb * TA + i, h));
+          wb4[i] = *reinterpret_cast<const float4*>(sWB + sidx(lb * TA + i, h));
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+          for (int i = 0; i < TA; ++i)
+#pragma unroll
+            for (int j = 0; j < TA; ++j) {
+              const float den = fmaf(ea[i][c4], eb[j][c4], 1.0f);
+              const float r = __builtin_amdgcn_rcpf(den);
+              acc[i][j] = fmaf(wa4[i][c4] + wb4[j][c4], r, acc[i][j]);
+            }
+      }
+    } else {
+      for (int h = 0; h < kUW; h += 4) {
+        float4 av[TA], bv[TA];
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+          av[i] = *reinterpret_cast<const float4*>(sEA + sidx(la * TA + i, h));
+          bv[i] = *reinterpret_cast<const float4*>(sEB + sidx(lb * TA + i, h));
+        }
+        const float4 w4 = *reinterpret_cast<const float4*>(sWq + h);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+          for (int i = 0; i < TA; ++i)
+#pragma unroll
+            for (int j = 0; j < TA; ++j) {
+              const float tt = av[i][c4] + bv[j][c4];
+              const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(tt));
+              acc[i][j] = fmaf(w4[c4], tt * r, acc[i][j]);
+            }
+      }
     }
+    float* ws = sums + ((p % NBUF) * 4 + wv) * KR * KR;
+#pragma unroll
+    for (int i = 0; i < TA; ++i)
+#pragma unroll
+      for (int j = 0; j < TA; ++j) ws[(la * TA + i) * KR + lb * TA + j] = acc[i][j];
+  };
 
-    // ---- pair t: its predecessor side from A_t
-    if (t < t1) {
-      float ap[RT][4];
-      bool big = false;
+  // pair t: its predecessor side from A_t (and whether it takes the
+  // per-element form)
+  auto start_pair = [&](const f32x4_t (&accA)[RT]) {
+    float ap[RT][4];
+    bool big = false;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          ap[rt][v] = kNegLog2e * accA[rt][v];
-          big |= fabsf(ap[rt][v]) > 64.f;
-        }
-      slow_prev = __builtin_amdgcn_ballot_w64(big) != 0;
+      for (int v = 0; v < 4; ++v) {
+        ap[rt][v] = kNegLog2e * accA[rt][v];
+        big |= fabsf(ap[rt][v]) > 64.f;
+      }
+    slow_prev = __builtin_amdgcn_ballot_w64(big) != 0;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int o = sidx(rt * 16 + fq * 4 + v, fr);
-          const float e = __builtin_amdgcn_exp2f(ap[rt][v]);
-          sEA[o] = slow_prev ? ap[rt][v] : e;
-          sWA[o] = wq * ap[rt][v];
-        }
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int o = sidx(rt * 16 + fq * 4 + v, fr);
+        const float e = __builtin_amdgcn_exp2f(ap[rt][v]);
+        sEA[o] = slow_prev ? ap[rt][v] : e;
+        sWA[o] = wq * ap[rt][v];
+      }
+  };
+
+  using kYes = std::true_type;
+  using kNo = std::false_type;
+  // ---- step t0: A_t0 only (B_t0 would complete a pair outside the chunk);
+  // every chunk has a pair, so slot t0 + 1 exists
+  {
+    issue_z(t0 + 1);
+    f32x4_t accA[RT], accB[RT];
+    form(kYes{}, kNo{}, (t0 & 1) ? zb1 : zb0, accA, accB);
+    start_pair(accA);
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t0 + 1's rows, the W1b rows
+    gather(rb, wb);
+    __syncthreads();
+  }
+  // ---- steps t0 + 1 .. t1 - 1: B_t completes pair t - 1, A_t starts pair t
+  for (int t = t0 + 1; t < t1; ++t) {
+    const char* zt = (t & 1) ? zb1 : zb0;
+    issue_z(t + 1);                  // the other buffer was last read at step t - 1
+    // pair t - 2 was finished at step t - 1; its buffer is next written at step t + 1
+    if (NBUF == 2 && t >= t0 + 2) store_pair(t - 2);
+    const float cq = kNegLog2e * c_prev;   // pair t - 1
+    load_c(t);                             // pair t, used at step t + 1
+    f32x4_t accA[RT], accB[RT];
+    form(kYes{}, kYes{}, zt, accA, accB);
+    finish_pair(t - 1, cq, accB);
+    start_pair(accA);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t + 1's rows (this wave's share)
-    if (t > t0 && t < t1) c_prev = sum_c(bb);
+    c_prev = sum_c(bb);
     __syncthreads();                                       // ... and every other wave's
   }
+  // ---- step t1: B_t1 only (A_t1 would start a pair outside the chunk)
+  {
+    if (NBUF == 2 && t1 >= t0 + 2) store_pair(t1 - 2);
+    const float cq = kNegLog2e * c_prev;   // pair t1 - 1
+    f32x4_t accA[RT], accB[RT];
+    form(kNo{}, kYes{}, (t1 & 1) ? zb1 : zb0, accA, accB);
+    finish_pair(t1 - 1, cq, accB);
+    __syncthreads();                 // every wave's sum of pair t1 - 1 is in LDS
+  }
   // the last pair (and, with one buffer, the only one)
-  if (t1 > t0) store_pair(t1 - 1);
+  store_pair(t1 - 1);
 }
 
 // S_p(a, b) = l_{p+1}(b) + (sum of the slabs' partial sums, in slab order) + b2,
