@@ -26,6 +26,7 @@
 #include "common.h"
 #include "dma.h"
 #include "kernels.h"
+#include "wave.h"
 
 namespace dcoco {
 
@@ -468,6 +469,9 @@ constexpr int kBlkThreads = 1024;
 constexpr int kBlkSlabs = 8;         // slab loads in flight per group
 constexpr int kBlkScores = 16384;    // scores of one block staged in LDS: (B - 1) K^2
 constexpr int kBlkTab = 2048;        // walk table entries: (B - 1) K
+// the staged rows are (K | 1) apart: at most (B - 1) K and B - 1 more entries
+constexpr int kBlkScoresPad = kBlkScores + kBlkTab;
+constexpr int kBlkTabPad = kBlkTab + 512;
 constexpr int kBlkMaxB = 512;        // slots per block
 constexpr int kBlkIds = kBlkTab + kWave;   // candidate ids of a block: B K <= (B - 1) K + K
 constexpr int kBlkIdsPerT = (kBlkIds + kBlkThreads - 1) / kBlkThreads;
@@ -488,8 +492,8 @@ __global__ void __launch_bounds__(kBlkThreads)
 block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B, int K, float b2,
                          const float* __restrict__ cand_logits, const int32_t* __restrict__ cand_ids,
                          float* __restrict__ S, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_tok) {
-  __shared__ float sS[kBlkScores];
-  __shared__ int32_t sT[kBlkTab];
+  __shared__ float sS[kBlkScoresPad];
+  __shared__ int32_t sT[kBlkTabPad];
   __shared__ int32_t sK[kBlkMaxB];
   __shared__ int32_t sId[kBlkIds];
   __shared__ float sC0[kWave];
@@ -498,6 +502,7 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
   const int Bm1 = B - 1;
   const int kk = K * K;
   const int tot = Bm1 * kk;   // this block's scores, a multiple of VEC
+  const int srow = K | 1;     // LDS stride of a score row and a table row: odd
   const int ng = tot / VEC;
   const long long np0 = static_cast<long long>(n) * Bm1;
   const long long slab_stride = static_cast<long long>(P) * kk;
@@ -536,7 +541,7 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
       const int o = g * VEC + i;
       const float sv = ln[i] + (sum[i] + b2);
       S[np0 * kk + o] = sv;
-      sS[o] = sv;
+      sS[(o / K) * srow + o % K] = sv;
     }
   }
 #pragma unroll
@@ -544,9 +549,10 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
     if (tid + i * kBlkThreads < nid) sId[tid + i * kBlkThreads] = idv[i];
   if (tid < K) sC0[tid] = c0v;
   __syncthreads();
-  // the walk's table: best_p(a) for every (p, a) of the block
+  // the walk's table: best_p(a) for every (p, a) of the block, one thread
+  // per row (the odd row stride keeps the threads' reads on distinct banks)
   for (int r = tid; r < Bm1 * K; r += kBlkThreads) {
-    const float* row = sS + r * K;
+    const float* row = sS + r * srow;
     uint32_t bk = order_key(row[0]);
     int bi = 0;
     for (int b = 1; b < K; ++b) {
@@ -556,20 +562,17 @@ block_finish_walk_kernel(const float* __restrict__ part, int nslab, int P, int B
         bi = b;
       }
     }
-    sT[r] = bi;
+    sT[(r / K) * srow + r % K] = bi;
   }
   __syncthreads();
   if (tid < kWave) {
     const int l = tid;
     const uint32_t key = l < K ? order_key(sC0[l]) : 0u;   // lanes >= K carry the NaN key
-    uint32_t m = key;
-    for (int off = kWave / 2; off > 0; off >>= 1)
-      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, kWave)));
-    int k = __builtin_ctzll(ballot(key == m));   // lowest index among the largest keys
+    int k = __builtin_ctzll(ballot(key == wave_max_u32_dpp(key)));   // lowest index among the largest keys
     if (l == 0) {
       sK[0] = k;
       for (int p = 0; p < Bm1; ++p) {
-        k = min(max(sT[p * K + k], 0), K - 1);
+        k = min(max(sT[p * srow + k], 0), K - 1);
         sK[p + 1] = k;
       }
     }
