@@ -139,7 +139,7 @@ def stored_traffic(kernel, digest):
     return float(vals["hbm_bytes_per_launch"])
 
 
-KERNEL_SOURCES = ["topk.hip", "gemm.hip", "rep.hip", "score.hip", "score_slab.hip", "api.cpp", "common.h", "dma.h", "kernels.h",
+KERNEL_SOURCES = ["topk.hip", "gemm.hip", "rep.hip", "score.hip", "score_slab.hip", "api.cpp", "common.h", "dma.h", "gemm_tile.h", "kernels.h",
                   "ln_tile.h", "select.h", "wave.h"]
 
 

@@ -113,33 +113,42 @@ int hip_status(hipError_t e) { return e == hipSuccess ? DCOCO_OK : DCOCO_ERR_HIP
 
 // slot side: [P_h; W_L; W_R] h (split-K partials), s_p (+ its bf16 split when
 // s3 is given), gf = W_fg LN(P_h h)
-hipError_t slot_part(const dcoco_dims* d, const dcoco_weights* w, const void* h, float* s, void* s3,
-                     const RepLayout& L, hipStream_t st) {
+// slot side, first half: [P_h; W_pair halves] h as fp32 partials (split k ranges)
+GemmProblem slot_gemm_problem(const dcoco_dims* d, const dcoco_weights* w, const void* h, const RepLayout& L,
+                              int split) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int R = d->n_blocks * d->B;
-  const int r = d->d_proj, rs = d->d_pair, rz = d->d_z, dh = d->d_hidden;
+  const int r = d->d_proj, rs = d->d_pair, dh = d->d_hidden;
+  const int ns = r + 2 * rs;
+  GemmProblem q{};
+  q.M = R; q.N = ns; q.Kd = dh;
+  q.A = h; q.lda = dh; q.a_rows = nullptr; q.a_dtype = dt;
+  q.w[0] = w->P_h; q.ldw[0] = dh; q.col0[0] = 0; q.seg_end[0] = r;
+  q.w[1] = w->W_pair; q.ldw[1] = 2ll * dh; q.col0[1] = 0; q.seg_end[1] = r + rs;
+  q.w[2] = w->W_pair; q.ldw[2] = 2ll * dh; q.col0[2] = dh; q.seg_end[2] = ns;
+  q.w_dtype = dt;
+  q.split = split; q.out_f32 = L.Y; q.ldo = ns; q.out = nullptr;
+  return q;
+}
+
+// slot side, second half: gf = W_fg LN(P_h h) and the pair states (and their
+// bf16 split into s3 when given) from `split` partials
+hipError_t slot_finish(const dcoco_dims* d, const dcoco_weights* w, float* s, void* s3, const RepLayout& L,
+                       int split, hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int R = d->n_blocks * d->B;
+  const int r = d->d_proj, rs = d->d_pair, rz = d->d_z;
   const int ns = r + 2 * rs;
   hipError_t e;
-  {
-    GemmProblem q{};
-    q.M = R; q.N = ns; q.Kd = dh;
-    q.A = h; q.lda = dh; q.a_rows = nullptr; q.a_dtype = dt;
-    q.w[0] = w->P_h; q.ldw[0] = dh; q.col0[0] = 0; q.seg_end[0] = r;
-    q.w[1] = w->W_pair; q.ldw[1] = 2ll * dh; q.col0[1] = 0; q.seg_end[1] = r + rs;
-    q.w[2] = w->W_pair; q.ldw[2] = 2ll * dh; q.col0[2] = dh; q.seg_end[2] = ns;
-    q.w_dtype = dt;
-    q.split = L.split_slot; q.out_f32 = L.Y; q.ldo = ns; q.out = nullptr;
-    if ((e = launch_gemm(q, st)) != hipSuccess) return e;
-  }
   if (dt == kDtypeBf16 && ln_gemm_pair_supported(r, rs))
-    return launch_ln_gemm_pair(L.Y, L.split_slot, R, ns, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, d->B, r,
+    return launch_ln_gemm_pair(L.Y, split, R, ns, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, d->B, r,
                                r + rs, rs, s, s3, st);
-  if ((e = launch_pair_state(L.Y, L.split_slot, d->n_blocks, d->B, ns, r, r + rs, rs, s, s3, st)) != hipSuccess)
+  if ((e = launch_pair_state(L.Y, split, d->n_blocks, d->B, ns, r, r + rs, rs, s, s3, st)) != hipSuccess)
     return e;
   if (dt == kDtypeBf16)
-    return launch_ln_gemm(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, nullptr,
+    return launch_ln_gemm(L.Y, split, R, ns, 0, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, nullptr,
                           nullptr, 1, st);
-  if ((e = launch_ln_rows(L.Y, L.split_slot, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
+  if ((e = launch_ln_rows(L.Y, split, R, ns, 0, r, d->ln_eps, L.g, dt, st)) != hipSuccess) return e;
   GemmProblem q{};
   q.M = R; q.N = rz; q.Kd = r;
   q.A = L.g; q.lda = r; q.a_dtype = dt;
@@ -148,6 +157,37 @@ hipError_t slot_part(const dcoco_dims* d, const dcoco_weights* w, const void* h,
   q.w_dtype = dt;
   q.split = 1; q.out_f32 = L.gf; q.ldo = rz; q.out = nullptr;
   return launch_gemm(q, st);
+}
+
+hipError_t slot_part(const dcoco_dims* d, const dcoco_weights* w, const void* h, float* s, void* s3,
+                     const RepLayout& L, hipStream_t st) {
+  hipError_t e;
+  if ((e = launch_gemm(slot_gemm_problem(d, w, h, L, L.split_slot), st)) != hipSuccess) return e;
+  return slot_finish(d, w, s, s3, L, L.split_slot, st);
+}
+
+constexpr int kTopkGemmSlots = 3 * 256;   // resident workgroups of the joint launch: three per CU
+
+// top-K of the logits and the slot side.  Where the rows and the slot GEMM
+// can share one launch (bf16, aligned rows, K <= 16), the GEMM's k split is
+// cut until its tiles and the rows fit the resident workgroup slots once;
+// otherwise the slot side and top-K run one after the other.
+hipError_t topk_and_slot(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h, float* s,
+                         void* s3, const RepLayout& L, void* topk_ws, int32_t* ids, float* cl, hipStream_t st) {
+  const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
+  const int R = d->n_blocks * d->B;
+  if (dt == kDtypeBf16) {
+    GemmProblem q = slot_gemm_problem(d, w, h, L, L.split_slot);
+    while (q.split > 1 && topk_gemm_workgroups(q) + R > kTopkGemmSlots) q.split /= 2;
+    if (topk_gemm_supported(d->V, d->K, logits, q)) {
+      hipError_t e = launch_topk_gemm(logits, R, d->V, d->K, ids, cl, q, st);
+      if (e != hipSuccess) return e;
+      return slot_finish(d, w, s, s3, L, q.split, st);
+    }
+  }
+  hipError_t e = slot_part(d, w, h, s, s3, L, st);
+  if (e != hipSuccess) return e;
+  return launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
 }
 
 // candidate side, first half: P_e E[c] over gathered rows (split-K partials)
@@ -876,9 +916,8 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = dt == kDtypeBf16;
   // the pair-state kernel also writes the bf16 split of s that the pair term reads
-  hipError_t e = slot_part(d, w, h, s, bf ? SL.s3 : nullptr, L, st);
+  hipError_t e = topk_and_slot(d, w, logits, h, s, bf ? SL.s3 : nullptr, L, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = pair_term(d, w, s, SL, bf, st);
-  if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
   if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
   const WalkOut wk{ids, sel_idx, sel_tok};
@@ -983,9 +1022,8 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int r = d->d_proj;
-  hipError_t e = slot_part(d, w, h, s, SL.s3, L, st);
+  hipError_t e = topk_and_slot(d, w, logits, h, s, SL.s3, L, topk_ws, ids, cl, st);
   if (e == hipSuccess) e = pair_term(d, w, s, SL, true, st);
-  if (e == hipSuccess) e = launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
   if (e == hipSuccess) {
     if (gather_gemm_supported(r)) {
       // table rows gathered into the LDS operand tile, W_fb slice resident in LDS

@@ -45,6 +45,14 @@ struct GemmProblem {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t st);
 // number of K-splits and partial-buffer bytes chosen for a problem size
 int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype);
+
+// bf16 top-K of `rows` rows (aligned rows, K <= 16) and a bf16 GEMM q with
+// fp32 partials (no gather) in one launch: the GEMM's 64 x 64 tiles (times
+// q.split) and the rows share the CUs, three workgroups per CU.
+bool topk_gemm_supported(int V, int K, const void* logits, const GemmProblem& q);
+int topk_gemm_workgroups(const GemmProblem& q);
+hipError_t launch_topk_gemm(const void* logits, int rows, int V, int K, int32_t* ids, float* vals,
+                            const GemmProblem& q, hipStream_t st);
 // bf16 products with a long reduction (weight gradients): splits (a power of
 // two up to max_split) for about 256 workgroups, each split >= 128 deep
 int gemm_pick_split_max(int M, int N, int Kd, int max_split);

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_tile.h"
 #include "kernels.h"
 #include "select.h"
 #include "wave.h"
@@ -770,24 +771,65 @@ __device__ __forceinline__ uint32_t key_to_bf16(uint32_t k) {
 // decoded from the keys (only a zero or NaN key reads the row).
 constexpr int kDense = 24;
 
+// The LDS of one row's workgroup: the row kernel below declares the arrays;
+// the launch that runs rows beside GEMM tiles carves them from one buffer.
+template <int G>
+struct RowLds {
+  uint32_t* s_gm;                 // [kRowWaves * G * kWave]
+  int32_t (*s_flag)[kFlagCap];    // [kRowWaves][kFlagCap]
+  uint4 (*s_vec)[kFlagCap];       // [kRowWaves][kFlagCap]
+  uint64_t (*s_tmp)[kWave];       // [kRowWaves][kWave]
+  uint64_t (*s_cand)[kRowCap];    // [kRowWaves][kRowCap]
+  uint64_t* s_best;               // [kRowWaves * 64]
+  uint64_t* s_fin;                // [64]
+  int* s_cnt;                     // [kRowWaves]
+
+  // parts in decreasing alignment; bytes of the whole
+  static constexpr size_t kVec = sizeof(uint4) * kRowWaves * kFlagCap;
+  static constexpr size_t kTmp = sizeof(uint64_t) * kRowWaves * kWave;
+  static constexpr size_t kCand = sizeof(uint64_t) * kRowWaves * kRowCap;
+  static constexpr size_t kBest = sizeof(uint64_t) * kRowWaves * 64;
+  static constexpr size_t kFin = sizeof(uint64_t) * 64;
+  static constexpr size_t kGm = sizeof(uint32_t) * kRowWaves * G * kWave;
+  static constexpr size_t kFlag = sizeof(int32_t) * kRowWaves * kFlagCap;
+  static constexpr size_t kCnt = sizeof(int) * kRowWaves;
+  static constexpr size_t kBytes = kVec + kTmp + kCand + kBest + kFin + kGm + kFlag + kCnt;
+  static_assert(kVec % 16 == 0 && kTmp % 16 == 0 && kCand % 16 == 0 && kBest % 16 == 0 && kFin % 16 == 0 &&
+                kGm % 16 == 0 && kFlag % 16 == 0, "16-byte aligned parts");
+
+  // base 16-byte aligned
+  __device__ static RowLds carve(char* base) {
+    RowLds S;
+    char* p = base;
+    S.s_vec = reinterpret_cast<uint4 (*)[kFlagCap]>(p); p += kVec;
+    S.s_tmp = reinterpret_cast<uint64_t (*)[kWave]>(p); p += kTmp;
+    S.s_cand = reinterpret_cast<uint64_t (*)[kRowCap]>(p); p += kCand;
+    S.s_best = reinterpret_cast<uint64_t*>(p); p += kBest;
+    S.s_fin = reinterpret_cast<uint64_t*>(p); p += kFin;
+    S.s_gm = reinterpret_cast<uint32_t*>(p); p += kGm;
+    S.s_flag = reinterpret_cast<int32_t (*)[kFlagCap]>(p); p += kFlag;
+    S.s_cnt = reinterpret_cast<int*>(p);
+    return S;
+  }
+};
+
+// top-K of one row by one workgroup of kRowWaves waves (threadIdx.x < 512)
 template <int NV, int G, int D>
-__global__ void __launch_bounds__(kRowWaves * kWave, 4)   // two workgroups per CU
-topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
-                         float* __restrict__ vals) {
+__device__ __forceinline__ void topk_row_reg(const uint16_t* __restrict__ logits, int V, int K, int rounds,
+                                             int32_t* __restrict__ ids, float* __restrict__ vals, int row,
+                                             const RowLds<G>& S) {
   constexpr int kSegLen = kWave * NV * 8;
-  const int row = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int l = lane_id();
   const uint16_t* rowp = logits + static_cast<size_t>(row) * V;
-
-  __shared__ uint32_t s_gm[kRowWaves * G * kWave];
-  __shared__ int32_t s_flag[kRowWaves][kFlagCap];
-  __shared__ uint4 s_vec[kRowWaves][kFlagCap];
-  __shared__ uint64_t s_tmp[kRowWaves][kWave];
-  __shared__ uint64_t s_cand[kRowWaves][kRowCap];
-  __shared__ uint64_t s_best[kRowWaves * 64];
-  __shared__ uint64_t s_fin[64];
-  __shared__ int s_cnt[kRowWaves];
+  uint32_t* const s_gm = S.s_gm;
+  int32_t (*const s_flag)[kFlagCap] = S.s_flag;
+  uint4 (*const s_vec)[kFlagCap] = S.s_vec;
+  uint64_t (*const s_tmp)[kWave] = S.s_tmp;
+  uint64_t (*const s_cand)[kRowCap] = S.s_cand;
+  uint64_t* const s_best = S.s_best;
+  uint64_t* const s_fin = S.s_fin;
+  int* const s_cnt = S.s_cnt;
 
   uint32_t ring[D][NV * 4];
 #pragma unroll
@@ -915,6 +957,74 @@ topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int 
     ids[static_cast<size_t>(row) * K + l] = static_cast<int32_t>(id);
     vals[static_cast<size_t>(row) * K + l] = bf16_to_f32(static_cast<uint16_t>(bits));
   }
+}
+
+template <int NV, int G, int D>
+__global__ void __launch_bounds__(kRowWaves * kWave, 4)   // two workgroups per CU
+topk_bf16_row_reg_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
+                         float* __restrict__ vals) {
+  __shared__ uint32_t s_gm[kRowWaves * G * kWave];
+  __shared__ int32_t s_flag[kRowWaves][kFlagCap];
+  __shared__ uint4 s_vec[kRowWaves][kFlagCap];
+  __shared__ uint64_t s_tmp[kRowWaves][kWave];
+  __shared__ uint64_t s_cand[kRowWaves][kRowCap];
+  __shared__ uint64_t s_best[kRowWaves * 64];
+  __shared__ uint64_t s_fin[64];
+  __shared__ int s_cnt[kRowWaves];
+  const RowLds<G> S{s_gm, s_flag, s_vec, s_tmp, s_cand, s_best, s_fin, s_cnt};
+  topk_row_reg<NV, G, D>(logits, V, K, rounds, ids, vals, blockIdx.x, S);
+}
+
+// Top-K rows and the tiles of one small GEMM (fp32 split-K partials, no
+// gather) in one launch, the GEMM's workgroups first: the rows stream the
+// logits at the HBM rate while the GEMM, held back by its loads' latency, runs
+// on the workgroup slots the rows leave (three workgroups per CU).  Each GEMM
+// workgroup takes one 64 x 64 tile of one k range with eight waves.
+constexpr int kFuseStages = 3;
+using FuseTile = DmaTile<64, 64, 2, 4, kFuseStages>;
+constexpr size_t kFuseLds = RowLds<1>::kBytes > static_cast<size_t>(FuseTile::kStage) * kFuseStages
+                                ? RowLds<1>::kBytes
+                                : static_cast<size_t>(FuseTile::kStage) * kFuseStages;
+
+template <int NV, int D>
+__global__ void __launch_bounds__(kRowWaves * kWave, 6)   // three workgroups per CU
+topk_gemm_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
+                 float* __restrict__ vals, GemmDev p, int tiles_m, int tiles_n, int n_gemm) {
+  __shared__ __align__(1024) char arena[kFuseLds];
+  const int bid = blockIdx.x;
+  if (bid < n_gemm) {
+    constexpr int MW = FuseTile::MW, NWB = FuseTile::NWB, TM = FuseTile::TM, TN = FuseTile::TN;
+    constexpr int kStage = FuseTile::kStage;
+    int b = bid;
+    const int tn = b % tiles_n;
+    b /= tiles_n;
+    const int tm = b % tiles_m;
+    const int zs = b / tiles_m;
+    const int n0 = tn * 64;
+    const int m0 = tm * 64;
+    const int kbeg = zs * p.ksplit;
+    const int kend = min(p.Kd, kbeg + p.ksplit);
+    f32x4_t acc[TM][TN];
+    dma_tile_mainloop<64, 64, 2, 4, kFuseStages>(p, m0, n0, kbeg, kend, arena, arena + kStage, arena + 2 * kStage,
+                                                  arena, acc);
+    const int l = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int wm = wv / 4;
+    const int wn = wv % 4;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int c = 0; c < TN; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + wm * MW + a * 16 + (l >> 4) * 4 + v;
+          const int n = n0 + wn * NWB + c * 16 + (l & 15);
+          if (m < p.M && n < p.N) p.out_f32[(static_cast<long long>(zs) * p.M + m) * p.ldo + n] = acc[a][c][v];
+        }
+    return;
+  }
+  const RowLds<1> S = RowLds<1>::carve(arena);
+  topk_row_reg<NV, 1, D>(logits, V, K, rounds, ids, vals, bid - n_gemm, S);
 }
 
 // Any other bf16 row: element loads, one segment at a time.
@@ -1077,6 +1187,31 @@ hipError_t launch_topk_t(const void* logits, int rows, int V, int K, uint64_t* p
 }
 
 }  // namespace
+
+bool topk_gemm_supported(int V, int K, const void* logits, const GemmProblem& q) {
+  const bool vec = (static_cast<size_t>(V) * sizeof(uint16_t)) % 16 == 0 &&
+                   (reinterpret_cast<uintptr_t>(logits) % 16) == 0;
+  return vec && K >= 1 && K <= 16 && q.a_dtype == kDtypeBf16 && q.w_dtype == kDtypeBf16 && q.a_rows == nullptr &&
+         q.out == nullptr && q.out_f32 != nullptr && q.Kd % 64 == 0 && q.M >= 1 && q.N >= 1 && q.split >= 1;
+}
+
+int topk_gemm_workgroups(const GemmProblem& q) {
+  return ((q.M + 63) / 64) * ((q.N + 63) / 64) * q.split;
+}
+
+hipError_t launch_topk_gemm(const void* logits, int rows, int V, int K, int32_t* ids, float* vals,
+                            const GemmProblem& q, hipStream_t st) {
+  if (!topk_gemm_supported(V, K, logits, q)) return hipErrorInvalidValue;
+  if (rows <= 0) return hipSuccess;
+  const GemmDev p = gemm_dev(q, 64);
+  const int tiles_m = (q.M + 63) / 64;
+  const int tiles_n = (q.N + 63) / 64;
+  const int n_gemm = tiles_m * tiles_n * q.split;
+  const int rounds = (V + kRowWaves * kWave * kRegNV * 8 - 1) / (kRowWaves * kWave * kRegNV * 8);
+  hipLaunchKernelGGL((topk_gemm_kernel<kRegNV, kRegD>), dim3(n_gemm + rows), dim3(kRowWaves * kWave), 0, st,
+                     static_cast<const uint16_t*>(logits), V, K, rounds, ids, vals, p, tiles_m, tiles_n, n_gemm);
+  return hipGetLastError();
+}
 
 size_t topk_workspace_bytes(int dtype, int rows, int V, int K) {
   if (dtype == kDtypeBf16) return 0;   // one workgroup per row, no partials
