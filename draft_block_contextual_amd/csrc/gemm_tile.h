@@ -140,26 +140,31 @@ __device__ __forceinline__ void dma_tile_mainloop(
   const int frow = l & 15;
   auto compute = [&](const char* sa) {
     const char* sw = sa + kABytes;
+    // every fragment of the stage (both 32-deep halves) is read first, so the
+    // MFMAs issue back to back behind the reads instead of waiting on each
+    bf16x8_t fa[2][TM], fw[2][TN];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = ks * 4 + (l >> 4);
-      bf16x8_t fa[TM], fw[TN];
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
         const int row = wm * MW + a * 16 + frow;
-        fa[a] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + row * kDmaRow + dma_swz(row, c) * 16));
+        fa[ks][a] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + row * kDmaRow + dma_swz(row, c) * 16));
       }
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const int row = wn * NWB + b * 16 + frow;
-        fw[b] = as_bf16x8(*reinterpret_cast<const uint4*>(sw + row * kDmaRow + dma_swz(row, c) * 16));
+        fw[ks][b] = as_bf16x8(*reinterpret_cast<const uint4*>(sw + row * kDmaRow + dma_swz(row, c) * 16));
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fw[b], acc[a][b], 0, 0, 0);
-    }
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][a], fw[ks][b], acc[a][b], 0, 0, 0);
   };
   // one pipeline step on ring slot S: wait for its loads, barrier, refill the
   // slot consumed in the previous step, then compute on slot S
