@@ -73,6 +73,7 @@ def algorithmic_work(D):
         "logit_bytes": R * D.V * e,
         "gather_bytes": RK * D.e * e,
         "h_bytes": R * D.d * e,
+        "slot_weight_bytes": (D.r + 2 * D.r_s) * D.d * e,
         "weight_bytes": w_params * e,
         # representation stage: P_e E[c], [P_h; W_L; W_R] h, and the fusion
         # W_f [b; g] (its g half once per slot, its b half once per candidate)
@@ -179,6 +180,9 @@ def kernel_rooflines(figs, work):
         "pair_term": ("mfma", work["pair_flops"]),
         "grid": ("alu", work["grid_elems"]),
         "slab": ("alu", work["grid_elems"]),
+        # top-K rows and the slot GEMM in one launch: the logits, h and the
+        # slot weights read once
+        "topk_gemm": ("hbm", work["logit_bytes"] + work["h_bytes"] + work["slot_weight_bytes"]),
     }
     out = {}
     for k, f in figs.items():
@@ -554,7 +558,8 @@ def main():
     topk_us = stage_us["topk"]
     ach = work["logit_bytes"] / (topk_us * 1e-6) / 1e9
     digest = source_digest([f"draft_block_contextual_amd/csrc/{f}"
-                            for f in ("topk.hip", "common.h", "select.h", "wave.h")])
+                            for f in ("topk.hip", "common.h", "dma.h", "gemm_tile.h", "kernels.h", "select.h",
+                                      "wave.h")])
     traffic = stored_traffic(f"topk_{cfg.name}", digest)
     roof = {"bound": "hbm", "kernel": kname, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),

@@ -106,11 +106,17 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   constexpr int rz = NKS * 32;
   const int B = g.B;
   const int Bm1 = B - 1;
-  int bid = blockIdx.x;
-  const int chunk = bid % g.nchunk;
-  bid /= g.nchunk;
-  const int slab = bid % g.nslab;
-  const int n = bid / g.nslab;
+  // workgroups are dealt to the 8 XCDs in turn (blockIdx % 8); when the
+  // grid divides evenly, XCD x takes a contiguous run of the work items
+  // (block, chunk, slab), slab fastest, so the slabs of one chunk share that
+  // XCD's L2 copy of the chunk's z rows
+  const int G = static_cast<int>(gridDim.x);
+  int li = static_cast<int>(blockIdx.x);
+  if (G % 8 == 0) li = (li % 8) * (G / 8) + li / 8;
+  const int slab = li % g.nslab;
+  li /= g.nslab;
+  const int chunk = li % g.nchunk;
+  const int n = li / g.nchunk;
   const int t0 = chunk * g.pc;                   // first slot: pair t0 is the chunk's first
   const int t1 = min(t0 + g.pc, Bm1);            // last slot: pair t1 - 1 is the chunk's last
   constexpr int rowb = rz * 2;                   // bytes of one z row

@@ -523,11 +523,15 @@ __device__ __forceinline__ void row_load_regs(const uint16_t* rowp, int V, int s
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e0 = seg0 + (i * kWave + l) * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(rowp + min(e0, V - 8));   // clamped inside the row
-    kw[4 * i] = v.x;
-    kw[4 * i + 1] = v.y;
-    kw[4 * i + 2] = v.z;
-    kw[4 * i + 3] = v.w;
+    // clamped inside the row; non-temporal: the logits are read once, so they
+    // should not push what other work keeps in L2 (the launch that also runs
+    // the slot GEMM's tiles re-reads its weights from there)
+    using u32x4 = __attribute__((ext_vector_type(4))) uint32_t;
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + min(e0, V - 8)));
+    kw[4 * i] = v[0];
+    kw[4 * i + 1] = v[1];
+    kw[4 * i + 2] = v[2];
+    kw[4 * i + 3] = v[3];
   }
 }
 
@@ -995,7 +999,11 @@ topk_gemm_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, 
   if (bid < n_gemm) {
     constexpr int MW = FuseTile::MW, NWB = FuseTile::NWB, TM = FuseTile::TM, TN = FuseTile::TN;
     constexpr int kStage = FuseTile::kStage;
+    // workgroups are dealt to the 8 XCDs in turn: when the tiles divide
+    // evenly, XCD x takes a contiguous run of (split, tm, tn), so it reads
+    // only its own rows of A from HBM rather than all of them
     int b = bid;
+    if (n_gemm % 8 == 0) b = (bid % 8) * (n_gemm / 8) + bid / 8;
     const int tn = b % tiles_n;
     b /= tiles_n;
     const int tm = b % tiles_m;
