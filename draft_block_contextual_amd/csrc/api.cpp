@@ -246,9 +246,10 @@ bool use_slab(const dcoco_dims* d) {
 // scoring stage buffers
 struct ScoreLayout {
   void* s3;       // bf16 [3, P, rs] (bf16 path only)
-  float* C;       // fp32 [nq, P, H]
+  float* C;       // fp32 [nq, P, H]; null when the slab launch forms the pair term
   float* AB;      // fp32 [N*B*K, 2H] (A, B through memory), else null
   float* part;    // fp32 [nslab, P, K, K] (slab kernels), else null
+  bool c_chip;    // the slab launch forms W1s s_p from s3 (no C buffer, no pair-term GEMM)
 };
 
 // with_ab: the A, B buffer even where the slab kernels score (training needs it)
@@ -258,8 +259,10 @@ ScoreLayout carve_score(Carve& c, const dcoco_dims* d, bool with_ab = false) {
   const size_t RK = static_cast<size_t>(d->n_blocks) * d->B * d->K;
   const int nq = d->dtype == DCOCO_BF16 ? 3 : 1;
   const bool slab = use_slab(d);
+  L.c_chip = slab && !with_ab && d->dtype == DCOCO_BF16 &&
+             score_slab_c_on_chip(d->n_blocks, d->B, d->K, d->d_mlp, d->d_pair);
   L.s3 = c.take(d->dtype == DCOCO_BF16 ? 3 * P * d->d_pair * 2 : 0);
-  L.C = static_cast<float*>(c.take(sizeof(float) * nq * P * d->d_mlp));
+  L.C = L.c_chip ? nullptr : static_cast<float*>(c.take(sizeof(float) * nq * P * d->d_mlp));
   L.AB = (with_ab || !slab) ? static_cast<float*>(c.take(sizeof(float) * RK * 2 * d->d_mlp)) : nullptr;
   L.part = slab ? static_cast<float*>(c.take(score_slab_part_bytes(d->n_blocks, d->B, d->K, d->d_mlp)))
                 : nullptr;
@@ -267,7 +270,8 @@ ScoreLayout carve_score(Carve& c, const dcoco_dims* d, bool with_ab = false) {
 }
 
 // pair term: C_p parts = W1s s_p (bf16 path: s split into hi/mid/lo rows; the
-// split is made here unless s3_ready)
+// split is made here unless s3_ready).  Where the slab launch forms the
+// product itself, only the split is made.
 hipError_t pair_term(const dcoco_dims* d, const dcoco_weights* w, const float* s, const ScoreLayout& L,
                      bool s3_ready, hipStream_t st) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
@@ -279,6 +283,7 @@ hipError_t pair_term(const dcoco_dims* d, const dcoco_weights* w, const float* s
   if (dt == kDtypeBf16 && !s3_ready &&
       (e = launch_split3(s, static_cast<long long>(P) * rs, L.s3, st)) != hipSuccess)
     return e;
+  if (L.c_chip) return hipSuccess;
   GemmProblem q{};
   q.M = nq * P; q.N = H; q.Kd = rs;
   q.A = dt == kDtypeBf16 ? L.s3 : static_cast<const void*>(s); q.lda = rs; q.a_dtype = dt;
@@ -332,6 +337,7 @@ hipError_t score_tail(const dcoco_dims* d, const dcoco_weights* w, const void* z
     q.N = d->n_blocks; q.B = d->B; q.K = d->K; q.H = H; q.rz = d->d_z;
     q.z = z; q.W1 = w->W1; q.ldw1 = 2ll * d->d_z + d->d_pair;
     q.C = L.C; q.nq = dt == kDtypeBf16 ? 3 : 1; q.b1 = w->b1; q.w2 = w->w2; q.b2 = w->b2;
+    q.s3 = L.c_chip ? L.s3 : nullptr; q.rs = d->d_pair;
     q.cand_logits = cl; q.part = L.part; q.S = S; q.best = best;
     const bool walk = wk != nullptr && block_finish_walk_fits(d->B, d->K, d->d_mlp);
     if (walk) {

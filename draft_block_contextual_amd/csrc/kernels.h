@@ -111,8 +111,12 @@ struct ScoreSlabProblem {
   const void* z;               // [N*B*K, rz] bf16
   const void* W1;              // [H, ldw1] bf16: columns [z_a | z_b | s]
   long long ldw1;
-  const float* C;              // [nq, N*(B-1), H] fp32: parts of W1s s_p (summed)
+  const float* C;              // [nq, N*(B-1), H] fp32: parts of W1s s_p (summed), when s3 is null
   int nq;
+  // with s3 (bf16 [3, N*(B-1), rs]: the parts of s_p), the launch forms
+  // W1s s_p itself and C is not read; needs score_slab_c_on_chip
+  const void* s3;
+  int rs;
   const void* b1;              // [H] bf16 or null
   const void* w2;              // [H] bf16
   float b2;
@@ -129,6 +133,7 @@ struct ScoreSlabProblem {
 };
 bool score_slab_supported(int dtype, int K, int rz, int H);
 bool block_finish_walk_fits(int B, int K, int H);
+bool score_slab_c_on_chip(int N, int B, int K, int H, int rs);
 int score_slab_count(int H);
 bool score_slab_preferred(int dtype, int N, int B, int K, int rz, int H);
 size_t score_slab_part_bytes(int N, int B, int K, int H);

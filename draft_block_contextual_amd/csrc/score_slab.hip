@@ -5,6 +5,11 @@
 // with DCOCO", "Score neighboring candidates in parallel"):
 //   S_p(a,b) = l_{p+1}(b) + b2 + sum_h w2_h SiLU(A_{p,a,h} + B_{p,b,h} + C_{p,h}),
 //   A_{p,a} = W1a z_{p,a},  B_{p,b} = W1b z_{p+1,b},  C_p = W1s s_p + b1.
+// W1s s_p comes either from memory (three parts, one per bf16 part of s_p)
+// or, for chunks of at most five pairs, from the launch itself: the
+// workgroup forms the parts of its chunk's pairs over its slab's units on
+// MFMA in the prologue, exactly as the separate product would (same operand
+// fragments, same k order), and adds them in the same order.
 // The sum over hidden units is cut into slabs of 64 and a draft block's pairs
 // into chunks.  A workgroup takes one (block, slab, chunk): each of its four
 // waves keeps the W1a and W1b rows of 16 units of the slab in registers and
@@ -37,13 +42,17 @@ constexpr float kNegLn2 = -0.6931471805599453f;
 constexpr int kUW = 16;                  // units per wave per slab
 constexpr int kUS = 4 * kUW;             // units per slab
 constexpr int kMaxKs = 8;                // 32-deep k steps of z (W1 fragments in registers): r_z <= 256
+constexpr int kChipPairs = 5;            // pairs per chunk with the pair term formed on chip: 3 parts x 5 <= 16 rows
 
 struct SlabDev {
   int N, B, K, H, P, rz, nq, nslab, pc, nchunk;
   const uint16_t* z;       // [N*B*K, rz]
   const uint16_t* W1;      // [H, ldw1]: columns [z_a | z_b | s]
   long long ldw1;
-  const float* C;          // [nq, P, H]: parts of W1s s_p (summed)
+  const float* C;          // [nq, P, H]: parts of W1s s_p (summed); null when formed on chip
+  const uint16_t* s3;      // [3, P, rs]: bf16 parts of s_p (on-chip pair term), else null
+  long long s3_part;       // P rs
+  int rs;
   const uint16_t* b1;      // [H] or null
   const uint16_t* w2;      // [H]
   float* part;             // [nslab, P, K, K]: each slab's sum
@@ -72,8 +81,10 @@ struct SlabShape {
   static constexpr int SUMS = NBUF * 4 * KR * KR;     // [buffer][wave][KR * KR] sums
   static_assert((KR / TA) * (KR / TA) == kWave, "one output block per lane");
   static_assert(NKS >= 2 && NKS <= kMaxKs, "r_z");
+  static constexpr int CSUM = 4 * kChipPairs * kUW;  // on-chip pair term: [wave][pair][unit]
   // K <= 16: three workgroups per CU
-  static_assert(2 * ZBUF + (STAGE + SUMS) * 4 <= (KR == 16 ? 53 : 160) * 1024, "LDS");
+  static_assert(2 * ZBUF + (STAGE + SUMS + CSUM) * 4 <= (KR == 16 ? 53 : 160) * 1024, "LDS");
+  static_assert(KR * KR >= 16 * kUW, "a wave's pair-sum buffer holds one 16 x 16 product tile");
 };
 
 // the 16-byte chunk c of z row r sits at chunk position c ^ (r & 7) of its
@@ -90,13 +101,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <typename SS>
+template <typename SS, bool CHIP>
 __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(SlabDev g) {
   constexpr int KR = SS::KR, TA = SS::TA, RT = SS::RT, ARR = SS::ARR, NBUF = SS::NBUF, NKS = SS::NKS;
   __shared__ __align__(1024) char zb0[SS::ZBUF];
   __shared__ __align__(1024) char zb1[SS::ZBUF];
   __shared__ __align__(16) float smem[SS::STAGE];
   __shared__ __align__(16) float sums[SS::SUMS];   // [pair p % NBUF][wave][KR * KR]
+  __shared__ __align__(16) float csum[CHIP ? SS::CSUM : 4];   // [wave][pair - t0][unit]: W1s s_p summed
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -178,7 +190,7 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   // every load of the prologue in flight at once: slot t0's rows, C of pair
   // t0, the W1a and W1b fragments of every k step, w2 and b1
   issue_z(t0);
-  load_c(t0);
+  if constexpr (!CHIP) load_c(t0);
   // W1a and W1b rows of the wave's 16 units, loaded with the four 16-byte
   // quarters of a unit's 64-byte slice of each k step in adjacent lanes
   // (lane 4 v + q: unit v, quarter q), so each group of four lanes reads one
@@ -192,6 +204,25 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
                          (l & 3) * 8;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) ra[ks] = *reinterpret_cast<const u32x4*>(wsrc + ks * 32);
+  // on chip: the W1s rows of the wave's units (as W1a, k steps past r_s
+  // repeat the last) and the MFMA A fragments of the chunk's s_p parts,
+  // operand row fr = (part q, pair t0 + i) at q np + i; rows from 3 np on
+  // repeat row 0 and are never read
+  const int np = t1 - t0;
+  const int nks_s = g.rs >> 5;
+  u32x4 rw[CHIP ? kMaxKs : 1], rsf[CHIP ? kMaxKs : 1];
+  if constexpr (CHIP) {
+    const int rrow = fr < 3 * np ? fr : 0;
+    const int q = rrow / np;
+    const uint16_t* ssrc = g.s3 + q * g.s3_part +
+                           (static_cast<long long>(n) * Bm1 + t0 + (rrow - q * np)) * g.rs + fq * 8;
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) {
+      const int kc = min(ks, nks_s - 1);
+      rw[ks] = *reinterpret_cast<const u32x4*>(wsrc + 2 * rz + kc * 32);
+      rsf[ks] = *reinterpret_cast<const u32x4*>(ssrc + kc * 32);
+    }
+  }
   uint32_t w2b = g.w2[uc];
   uint32_t b1b = (g.b1 ? g.b1 : g.w2)[uc];
 #pragma unroll
@@ -203,6 +234,10 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   // waits on it again inside the loop (where that wait would also cover the
   // loads issued there)
   asm volatile("" : "+v"(w2b), "+v"(b1b));
+  if constexpr (CHIP) {
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) asm volatile("" : "+v"(rw[ks]), "+v"(rsf[ks]));
+  }
   // MFMA B fragments: lane l holds unit l & 15, k chunk l >> 4 of each k
   // step, which lane 4 (l & 15) + (l >> 4) loaded
   bf16x8_t wa[NKS], wb[NKS];
@@ -222,7 +257,40 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   const float wq = uin ? kNegLn2 * bf16_to_f32(static_cast<uint16_t>(w2b)) : 0.f;
   const float bb = g.b1 ? bf16_to_f32(static_cast<uint16_t>(b1b)) : 0.f;
   if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
-  float c_prev = sum_c(bb);          // C of the pair completed at the next step
+  float* cs = csum + wv * kChipPairs * kUW;
+  if constexpr (CHIP) {
+    // the parts of W1s s_p: one 16 x 16 tile (rows: part and pair; columns:
+    // the wave's units), staged in the wave's first pair-sum buffer (not
+    // written before the first pair's grid), then added per pair and unit
+    // in part order
+    f32x4_t accC = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int from = 4 * (4 * fr + fq);
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) {
+      if (ks < nks_s) {
+        u32x4 x;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          x[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(rw[ks][d])));
+        accC = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rsf[ks]),
+                                                       __builtin_bit_cast(bf16x8_t, x), accC, 0, 0, 0);
+      }
+    }
+    float* tc = sums + wv * KR * KR;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) tc[(4 * fq + v) * kUW + fr] = accC[v];
+    wave_lds_sync();
+    for (int e = l; e < np * kUW; e += kWave) {
+      const int i = e / kUW, uu = e % kUW;
+      float c = tc[i * kUW + uu];
+      c += tc[(np + i) * kUW + uu];
+      c += tc[(2 * np + i) * kUW + uu];
+      cs[e] = c;
+    }
+    wave_lds_sync();
+  }
+  // C of the pair completed at the next step
+  float c_prev = CHIP ? cs[fr] + bb : sum_c(bb);
   bool slow_prev = false;            // that pair takes the per-element form (wave-uniform)
   __syncthreads();                   // slot t0's rows and the w' table are in LDS
 
@@ -374,13 +442,13 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
     // pair t - 2 was finished at step t - 1; its buffer is next written at step t + 1
     if (NBUF == 2 && t >= t0 + 2) store_pair(t - 2);
     const float cq = kNegLog2e * c_prev;   // pair t - 1
-    load_c(t);                             // pair t, used at step t + 1
+    if constexpr (!CHIP) load_c(t);        // pair t, used at step t + 1
     f32x4_t accA[RT], accB[RT];
     form(kYes{}, kYes{}, zt, accA, accB);
     finish_pair(t - 1, cq, accB);
     start_pair(accA);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t + 1's rows (this wave's share)
-    c_prev = sum_c(bb);
+    c_prev = CHIP ? cs[(t - t0) * kUW + fr] + bb : sum_c(bb);
     __syncthreads();                                       // ... and every other wave's
   }
   // ---- step t1: B_t1 only (A_t1 would start a pair outside the chunk)
@@ -646,11 +714,21 @@ int score_slab_pairs_per_chunk(int N, int B, int K, int H) {
   return static_cast<int>((Bm1 + chunks - 1) / chunks);
 }
 
+// The pair term is formed inside the slab launch when every chunk has at
+// most five pairs (its three bf16 parts per pair fill at most one 16-row
+// MFMA tile) and r_s is a whole number of 32-deep k steps, at most 256.
+bool score_slab_c_on_chip(int N, int B, int K, int H, int rs) {
+  return B >= 2 && rs >= 32 && rs <= 32 * kMaxKs && rs % 32 == 0 &&
+         score_slab_pairs_per_chunk(N, B, K, H) <= kChipPairs;
+}
+
 hipError_t launch_score_slab(const ScoreSlabProblem& q, hipStream_t st) {
   const int Bm1 = q.B - 1;
   const int P = q.N * Bm1;
   if (P <= 0) return hipSuccess;
   if (!score_slab_supported(kDtypeBf16, q.K, q.rz, q.H)) return hipErrorInvalidValue;
+  const bool chip = q.s3 != nullptr;
+  if (chip ? !score_slab_c_on_chip(q.N, q.B, q.K, q.H, q.rs) : q.C == nullptr) return hipErrorInvalidValue;
   SlabDev d;
   d.N = q.N; d.B = q.B; d.K = q.K; d.H = q.H; d.P = P; d.rz = q.rz; d.nq = q.nq;
   d.nslab = score_slab_count(q.H);
@@ -659,18 +737,25 @@ hipError_t launch_score_slab(const ScoreSlabProblem& q, hipStream_t st) {
   d.z = static_cast<const uint16_t*>(q.z);
   d.W1 = static_cast<const uint16_t*>(q.W1);
   d.ldw1 = q.ldw1;
-  d.C = q.C;
+  d.C = chip ? nullptr : q.C;
+  d.s3 = static_cast<const uint16_t*>(q.s3);
+  d.s3_part = static_cast<long long>(P) * q.rs;
+  d.rs = q.rs;
   d.b1 = static_cast<const uint16_t*>(q.b1);
   d.w2 = static_cast<const uint16_t*>(q.w2);
   d.part = q.part;
   const dim3 grid(static_cast<unsigned>(q.N) * d.nslab * d.nchunk);
-#define DCOCO_SLAB(KRV)                                                                                   \
-  if (q.rz == 64) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 2>>), grid, dim3(256), 0, st, d);       \
-  else if (q.rz == 128) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 4>>), grid, dim3(256), 0, st, d); \
-  else hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, 8>>), grid, dim3(256), 0, st, d)
-  if (q.K <= 16) DCOCO_SLAB(16);
-  else DCOCO_SLAB(32);
+#define DCOCO_SLAB_C(KRV, NKSV)                                                                         \
+  if (chip) hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, NKSV>, true>), grid, dim3(256), 0, st, d); \
+  else hipLaunchKernelGGL((score_slab_kernel<SlabShape<KRV, NKSV>, false>), grid, dim3(256), 0, st, d)
+#define DCOCO_SLAB(KRV)                        \
+  if (q.rz == 64) { DCOCO_SLAB_C(KRV, 2); }     \
+  else if (q.rz == 128) { DCOCO_SLAB_C(KRV, 4); } \
+  else { DCOCO_SLAB_C(KRV, 8); }
+  if (q.K <= 16) { DCOCO_SLAB(16) }
+  else { DCOCO_SLAB(32) }
 #undef DCOCO_SLAB
+#undef DCOCO_SLAB_C
   if (q.sel_tok != nullptr) {
     // the finish of a whole block and its walk in one workgroup
     if (q.cand_ids == nullptr || !block_finish_walk_fits(q.B, q.K, q.H)) return hipErrorInvalidValue;

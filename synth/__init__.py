@@ -171,6 +171,13 @@ CONFIGS = {
                           30.0, "peaks", 16, 2016, "random", "128 blocks of B = 16, K = 16, H = 64"),
     "chunks_ragged": Config("chunks_ragged", _d(64, 16, 12, 3001, 64, 64, 64, 128, 64, 96, "bf16"),
                             30.0, "peaks", 12, 2017, "random", "64 blocks of B = 16, K = 12, H = 96"),
+    # on-chip scoring with the pair term formed in the scoring launch at its
+    # limit (five pairs, fifteen operand rows per workgroup), and with runs
+    # of six pairs, where the pair term comes from its own product
+    "chunks_five": Config("chunks_five", _d(256, 16, 4, 3001, 64, 64, 64, 64, 64, 64, "bf16"),
+                          30.0, "peaks", 4, 2018, "random", "256 blocks of B = 16, K = 4, H = 64"),
+    "chunks_long": Config("chunks_long", _d(8, 64, 8, 3001, 64, 64, 64, 64, 64, 512, "bf16"),
+                          30.0, "peaks", 8, 2019, "random", "8 blocks of B = 64, K = 8, H = 512"),
     # LM-head shapes (head tied to E, so d == e): ragged vocabulary tiles,
     # ragged row tiles, rows without planted peaks (bf16 ties at the K-th)
     "lmh_small": Config("lmh_small", _d(2, 8, 16, 5003, 256, 256, 64, 64, 64, 64, "bf16"),

@@ -234,3 +234,35 @@ def test_represent_backward_argument_checks(lib):
     assert call(d, None, fake, fake, fake, fake, ws=fake, nb=nb) == -1          # no h
     small = ctypes.c_size_t(need - 256)
     assert call(d, fake, fake, fake, fake, fake, ws=fake, nb=small) == -3
+
+
+def _query_score(lib, dims):
+    import draft_block_contextual_amd as dc
+    cd = dims.c()
+    cw = dc.CWeights()
+    n = ctypes.c_size_t(0)
+    rc = lib.dcoco_score(ctypes.byref(cd), ctypes.byref(cw), None, None, None, None, None, ctypes.byref(n), None)
+    return rc, n.value
+
+
+@pytest.mark.parametrize("n_blocks,B,K,H,on_chip", [
+    (256, 16, 4, 64, True),      # five pairs per scoring workgroup: the pair term formed in the scoring launch
+    (32, 16, 16, 512, True),     # the 32-stream shape (five pairs per workgroup)
+    (8, 64, 8, 512, False),      # six pairs per workgroup: the pair term from its own product
+    (2, 5, 32, 320, True),       # K > 16: one pair per workgroup
+])
+def test_score_workspace_drops_the_pair_term_buffer_when_formed_on_chip(lib, n_blocks, B, K, H, on_chip):
+    # bf16 scoring on the slab path needs the bf16 split of s and the per-slab
+    # pair sums, plus the fp32 pair term [3, P, H] only when the scoring launch
+    # does not form it (each piece rounded up to 256 bytes)
+    def up(x):
+        return (x + 255) // 256 * 256
+    d = _dims(n_blocks=n_blocks, B=B, K=K, d_mlp=H, d_z=64, d_pair=64, d_proj=64, d_hidden=64, d_embed=64, V=3001)
+    rc, n = _query_score(lib, d)
+    assert rc == 0
+    P = n_blocks * (B - 1)
+    nslab = (H + 63) // 64
+    need = up(3 * P * 64 * 2) + up(4 * nslab * P * K * K)
+    if not on_chip:
+        need += up(4 * 3 * P * H)
+    assert n == need

@@ -51,7 +51,7 @@ def _oracle(name, blocks=None):
 
 SMALL = ["tiny", "tiny_zero", "tiny_bias", "small_bf16", "small_f32", "mid_bf16", "mid_f32",
          "k64_small", "k32_small", "widez_bf16", "tall_bf16", "b1_bf16", "k1_bf16", "wide_max",
-         "chunks_bf16", "chunks_ragged"]
+         "chunks_bf16", "chunks_ragged", "chunks_five", "chunks_long"]
 
 
 def _run_block(name):
@@ -586,7 +586,7 @@ def test_correct_block_walk_fallback_shapes(B, K):
 
 
 @pytest.mark.parametrize("name", ["mid_bf16", "h512_bf16", "k32_small", "k1_bf16", "odd_k_slab", "b30_k7_slab",
-                                  "chunks_bf16", "chunks_ragged"])
+                                  "chunks_bf16", "chunks_ragged", "chunks_five", "chunks_long"])
 def test_correct_block_equals_separate_calls(name):
     # On these shapes the whole-path call scores with the on-chip slab kernels
     # and one workgroup per block finishes the sums and walks the block (K^2 a
