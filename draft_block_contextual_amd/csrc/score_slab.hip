@@ -84,7 +84,7 @@ struct SlabShape {
   static constexpr int CSUM = 4 * kChipPairs * kUW;  // on-chip pair term: [wave][pair][unit]
   // K <= 16: three workgroups per CU
   static_assert(2 * ZBUF + (STAGE + SUMS + CSUM) * 4 <= (KR == 16 ? 53 : 160) * 1024, "LDS");
-  static_assert(KR * KR >= 16 * kUW, "a wave's pair-sum buffer holds one 16 x 16 product tile");
+  static_assert(2 * ARR >= 16 * kUW, "a wave's B-side arrays hold one 16 x 16 product tile");
 };
 
 // the 16-byte chunk c of z row r sits at chunk position c ^ (r & 7) of its
@@ -147,6 +147,7 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   float* sEB = wreg + 2 * ARR;       // 2^B' (or B')
   float* sWB = wreg + 3 * ARR;       // w'B'
   float* sWq = wreg + 4 * ARR;       // w' per unit (per-element form)
+  float* cs = csum + wv * kChipPairs * kUW;   // on-chip pair term, summed: [pair - t0][unit]
 
   // ---- this lane's unit
   const int u = slab * kUS + wv * kUW + fr;
@@ -204,10 +205,14 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
                          (l & 3) * 8;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) ra[ks] = *reinterpret_cast<const u32x4*>(wsrc + ks * 32);
-  // on chip: the W1s rows of the wave's units (as W1a, k steps past r_s
-  // repeat the last) and the MFMA A fragments of the chunk's s_p parts,
-  // operand row fr = (part q, pair t0 + i) at q np + i; rows from 3 np on
-  // repeat row 0 and are never read
+  uint32_t w2b = g.w2[uc];
+  uint32_t b1b = (g.b1 ? g.b1 : g.w2)[uc];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) rb[ks] = *reinterpret_cast<const u32x4*>(wsrc + rz + ks * 32);
+  // on chip, issued after W1b and used at the end of step t0: the W1s rows
+  // of the wave's units (as W1a; k steps past r_s repeat the last) and the
+  // MFMA A fragments of the chunk's s_p parts, operand row fr = (part q,
+  // pair t0 + i) at q np + i (rows from 3 np on repeat row 0, never read)
   const int np = t1 - t0;
   const int nks_s = g.rs >> 5;
   u32x4 rw[CHIP ? kMaxKs : 1], rsf[CHIP ? kMaxKs : 1];
@@ -223,21 +228,14 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
       rsf[ks] = *reinterpret_cast<const u32x4*>(ssrc + kc * 32);
     }
   }
-  uint32_t w2b = g.w2[uc];
-  uint32_t b1b = (g.b1 ? g.b1 : g.w2)[uc];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) rb[ks] = *reinterpret_cast<const u32x4*>(wsrc + rz + ks * 32);
-  // every load but the W1b ones has landed (loads complete in issue order)
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NKS) : "memory");
+  // every load but the W1b ones (and the on-chip pair term's) has landed
+  // (loads complete in issue order)
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(CHIP ? NKS + 2 * kMaxKs : NKS) : "memory");
   // the compiler does not see the wait above: passing a loaded register
   // through an empty asm ends its tracking of that load there, so it never
   // waits on it again inside the loop (where that wait would also cover the
   // loads issued there)
   asm volatile("" : "+v"(w2b), "+v"(b1b));
-  if constexpr (CHIP) {
-#pragma unroll
-    for (int ks = 0; ks < kMaxKs; ++ks) asm volatile("" : "+v"(rw[ks]), "+v"(rsf[ks]));
-  }
   // MFMA B fragments: lane l holds unit l & 15, k chunk l >> 4 of each k
   // step, which lane 4 (l & 15) + (l >> 4) loaded
   bf16x8_t wa[NKS], wb[NKS];
@@ -257,40 +255,8 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   const float wq = uin ? kNegLn2 * bf16_to_f32(static_cast<uint16_t>(w2b)) : 0.f;
   const float bb = g.b1 ? bf16_to_f32(static_cast<uint16_t>(b1b)) : 0.f;
   if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
-  float* cs = csum + wv * kChipPairs * kUW;
-  if constexpr (CHIP) {
-    // the parts of W1s s_p: one 16 x 16 tile (rows: part and pair; columns:
-    // the wave's units), staged in the wave's first pair-sum buffer (not
-    // written before the first pair's grid), then added per pair and unit
-    // in part order
-    f32x4_t accC = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int from = 4 * (4 * fr + fq);
-#pragma unroll
-    for (int ks = 0; ks < kMaxKs; ++ks) {
-      if (ks < nks_s) {
-        u32x4 x;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          x[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(rw[ks][d])));
-        accC = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rsf[ks]),
-                                                       __builtin_bit_cast(bf16x8_t, x), accC, 0, 0, 0);
-      }
-    }
-    float* tc = sums + wv * KR * KR;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) tc[(4 * fq + v) * kUW + fr] = accC[v];
-    wave_lds_sync();
-    for (int e = l; e < np * kUW; e += kWave) {
-      const int i = e / kUW, uu = e % kUW;
-      float c = tc[i * kUW + uu];
-      c += tc[(np + i) * kUW + uu];
-      c += tc[(2 * np + i) * kUW + uu];
-      cs[e] = c;
-    }
-    wave_lds_sync();
-  }
-  // C of the pair completed at the next step
-  float c_prev = CHIP ? cs[fr] + bb : sum_c(bb);
+  // C of the pair completed at the next step (on chip: formed at step t0)
+  float c_prev = CHIP ? 0.f : sum_c(bb);
   bool slow_prev = false;            // that pair takes the per-element form (wave-uniform)
   __syncthreads();                   // slot t0's rows and the w' table are in LDS
 
@@ -433,6 +399,40 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
     start_pair(accA);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t0 + 1's rows, the W1b rows
     gather(rb, wb);
+    if constexpr (CHIP) {
+      // the parts of W1s s_p: one 16 x 16 tile (rows: part and pair;
+      // columns: the wave's units), staged in the wave's B-side arrays (next
+      // written by this wave's first grid), then added per pair and unit in
+      // part order
+#pragma unroll
+      for (int ks = 0; ks < kMaxKs; ++ks) asm volatile("" : "+v"(rw[ks]), "+v"(rsf[ks]));
+      f32x4_t accC = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int from = 4 * (4 * fr + fq);
+#pragma unroll
+      for (int ks = 0; ks < kMaxKs; ++ks) {
+        if (ks < nks_s) {
+          u32x4 x;
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            x[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(rw[ks][d])));
+          accC = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rsf[ks]),
+                                                         __builtin_bit_cast(bf16x8_t, x), accC, 0, 0, 0);
+        }
+      }
+      float* tc = sEB;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tc[(4 * fq + v) * kUW + fr] = accC[v];
+      wave_lds_sync();
+      for (int e = l; e < np * kUW; e += kWave) {
+        const int i = e / kUW, uu = e % kUW;
+        float c = tc[i * kUW + uu];
+        c += tc[(np + i) * kUW + uu];
+        c += tc[(2 * np + i) * kUW + uu];
+        cs[e] = c;
+      }
+      wave_lds_sync();
+      c_prev = cs[fr] + bb;
+    }
     __syncthreads();
   }
   // ---- steps t0 + 1 .. t1 - 1: B_t completes pair t - 1, A_t starts pair t
