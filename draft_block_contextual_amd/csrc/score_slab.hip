@@ -85,6 +85,7 @@ struct SlabShape {
   // K <= 16: three workgroups per CU
   static_assert(2 * ZBUF + (STAGE + SUMS + CSUM) * 4 <= (KR == 16 ? 53 : 160) * 1024, "LDS");
   static_assert(2 * ARR >= 16 * kUW, "a wave's B-side arrays hold one 16 x 16 product tile");
+  static_assert(SUMS * 4 >= 16 * 32 * kMaxKs * 2, "the pair-sum buffers hold 16 rows of s_p parts");
 };
 
 // the 16-byte chunk c of z row r sits at chunk position c ^ (r & 7) of its
@@ -192,6 +193,26 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   // t0, the W1a and W1b fragments of every k step, w2 and b1
   issue_z(t0);
   if constexpr (!CHIP) load_c(t0);
+  // on chip: the chunk's bf16 parts of s_p, operand row r = (part q, pair
+  // t0 + i) at q np + i (rows from 3 np on repeat row 0 and are never read),
+  // copied once into the pair-sum buffers (first written at step t0 + 1);
+  // 16-byte chunk c of row r at position c ^ (r & 7) when rows hold a
+  // multiple of eight chunks
+  const int np = t1 - t0;
+  const int nks_s = g.rs >> 5;
+  const int rowb_s = g.rs * 2;
+  const int smask = (g.rs & 63) == 0 ? 7 : 0;
+  if constexpr (CHIP) {
+    for (int j = wv; j < nks_s; j += 4) {          // 16 rows x rs x 2 bytes = rs / 32 KB
+      const int byte = j * 1024 + l * 16;
+      const int r = byte / rowb_s;
+      const int c = ((byte - r * rowb_s) >> 4) ^ (r & smask);
+      const int rr = r < 3 * np ? r : 0;
+      const int q = rr / np;
+      const uint16_t* src = g.s3 + q * g.s3_part + (static_cast<long long>(n) * Bm1 + t0 + (rr - q * np)) * g.rs;
+      dma16(src + c * 8, __builtin_amdgcn_readfirstlane(lds_offset(sums) + j * 1024));
+    }
+  }
   // W1a and W1b rows of the wave's 16 units, loaded with the four 16-byte
   // quarters of a unit's 64-byte slice of each k step in adjacent lanes
   // (lane 4 v + q: unit v, quarter q), so each group of four lanes reads one
@@ -207,35 +228,26 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   for (int ks = 0; ks < NKS; ++ks) ra[ks] = *reinterpret_cast<const u32x4*>(wsrc + ks * 32);
   uint32_t w2b = g.w2[uc];
   uint32_t b1b = (g.b1 ? g.b1 : g.w2)[uc];
+  // on chip: the W1s rows of the wave's units, as W1a (k steps past r_s
+  // repeat the last)
+  u32x4 rw[CHIP ? kMaxKs : 1];
+  if constexpr (CHIP) {
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) rw[ks] = *reinterpret_cast<const u32x4*>(wsrc + 2 * rz + min(ks, nks_s - 1) * 32);
+  }
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) rb[ks] = *reinterpret_cast<const u32x4*>(wsrc + rz + ks * 32);
-  // on chip, issued after W1b and used at the end of step t0: the W1s rows
-  // of the wave's units (as W1a; k steps past r_s repeat the last) and the
-  // MFMA A fragments of the chunk's s_p parts, operand row fr = (part q,
-  // pair t0 + i) at q np + i (rows from 3 np on repeat row 0, never read)
-  const int np = t1 - t0;
-  const int nks_s = g.rs >> 5;
-  u32x4 rw[CHIP ? kMaxKs : 1], rsf[CHIP ? kMaxKs : 1];
-  if constexpr (CHIP) {
-    const int rrow = fr < 3 * np ? fr : 0;
-    const int q = rrow / np;
-    const uint16_t* ssrc = g.s3 + q * g.s3_part +
-                           (static_cast<long long>(n) * Bm1 + t0 + (rrow - q * np)) * g.rs + fq * 8;
-#pragma unroll
-    for (int ks = 0; ks < kMaxKs; ++ks) {
-      const int kc = min(ks, nks_s - 1);
-      rw[ks] = *reinterpret_cast<const u32x4*>(wsrc + 2 * rz + kc * 32);
-      rsf[ks] = *reinterpret_cast<const u32x4*>(ssrc + kc * 32);
-    }
-  }
-  // every load but the W1b ones (and the on-chip pair term's) has landed
-  // (loads complete in issue order)
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(CHIP ? NKS + 2 * kMaxKs : NKS) : "memory");
+  // every load but the W1b ones has landed (loads complete in issue order)
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(NKS) : "memory");
   // the compiler does not see the wait above: passing a loaded register
   // through an empty asm ends its tracking of that load there, so it never
   // waits on it again inside the loop (where that wait would also cover the
   // loads issued there)
   asm volatile("" : "+v"(w2b), "+v"(b1b));
+  if constexpr (CHIP) {
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) asm volatile("" : "+v"(rw[ks]));
+  }
   // MFMA B fragments: lane l holds unit l & 15, k chunk l >> 4 of each k
   // step, which lane 4 (l & 15) + (l >> 4) loaded
   bf16x8_t wa[NKS], wb[NKS];
@@ -255,10 +267,44 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
   const float wq = uin ? kNegLn2 * bf16_to_f32(static_cast<uint16_t>(w2b)) : 0.f;
   const float bb = g.b1 ? bf16_to_f32(static_cast<uint16_t>(b1b)) : 0.f;
   if (l < kUW) sWq[l] = wq;          // lane l < 16 holds unit l of the wave's 16
-  // C of the pair completed at the next step (on chip: formed at step t0)
+  // C of the pair completed at the next step
   float c_prev = CHIP ? 0.f : sum_c(bb);
   bool slow_prev = false;            // that pair takes the per-element form (wave-uniform)
-  __syncthreads();                   // slot t0's rows and the w' table are in LDS
+  __syncthreads();                   // slot t0's rows, the w' table (and the s_p parts) are in LDS
+  if constexpr (CHIP) {
+    // the parts of W1s s_p: one 16 x 16 tile (rows: part and pair; columns:
+    // the wave's units) on MFMA, staged in the wave's B-side arrays (next
+    // written by this wave's first grid), then added per pair and unit in
+    // part order
+    const char* sp = reinterpret_cast<const char*>(sums);
+    f32x4_t accC = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int from = 4 * (4 * fr + fq);
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) {
+      if (ks < nks_s) {
+        u32x4 x;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          x[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(rw[ks][d])));
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(sp + fr * rowb_s + (((ks * 4 + fq) ^ (fr & smask)) << 4)));
+        accC = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, x), accC, 0, 0, 0);
+      }
+    }
+    float* tc = sEB;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) tc[(4 * fq + v) * kUW + fr] = accC[v];
+    wave_lds_sync();
+    for (int e = l; e < np * kUW; e += kWave) {
+      const int i = e / kUW, uu = e % kUW;
+      float c = tc[i * kUW + uu];
+      c += tc[(np + i) * kUW + uu];
+      c += tc[(2 * np + i) * kUW + uu];
+      cs[e] = c;
+    }
+    wave_lds_sync();
+    c_prev = cs[fr] + bb;
+  }
 
   // the slab's sum of pair p: the four waves added in order
   const int kk = K * K;
@@ -399,40 +445,6 @@ __global__ void __launch_bounds__(256, SS::KR == 16 ? 3 : 1) score_slab_kernel(S
     start_pair(accA);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // slot t0 + 1's rows, the W1b rows
     gather(rb, wb);
-    if constexpr (CHIP) {
-      // the parts of W1s s_p: one 16 x 16 tile (rows: part and pair;
-      // columns: the wave's units), staged in the wave's B-side arrays (next
-      // written by this wave's first grid), then added per pair and unit in
-      // part order
-#pragma unroll
-      for (int ks = 0; ks < kMaxKs; ++ks) asm volatile("" : "+v"(rw[ks]), "+v"(rsf[ks]));
-      f32x4_t accC = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int from = 4 * (4 * fr + fq);
-#pragma unroll
-      for (int ks = 0; ks < kMaxKs; ++ks) {
-        if (ks < nks_s) {
-          u32x4 x;
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-            x[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(from, static_cast<int>(rw[ks][d])));
-          accC = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rsf[ks]),
-                                                         __builtin_bit_cast(bf16x8_t, x), accC, 0, 0, 0);
-        }
-      }
-      float* tc = sEB;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) tc[(4 * fq + v) * kUW + fr] = accC[v];
-      wave_lds_sync();
-      for (int e = l; e < np * kUW; e += kWave) {
-        const int i = e / kUW, uu = e % kUW;
-        float c = tc[i * kUW + uu];
-        c += tc[(np + i) * kUW + uu];
-        c += tc[(2 * np + i) * kUW + uu];
-        cs[e] = c;
-      }
-      wave_lds_sync();
-      c_prev = cs[fr] + bb;
-    }
     __syncthreads();
   }
   // ---- steps t0 + 1 .. t1 - 1: B_t completes pair t - 1, A_t starts pair t
