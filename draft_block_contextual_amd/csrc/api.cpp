@@ -132,14 +132,19 @@ GemmProblem slot_gemm_problem(const dcoco_dims* d, const dcoco_weights* w, const
 }
 
 // slot side, second half: gf = W_fg LN(P_h h) and the pair states (and their
-// bf16 split into s3 when given) from `split` partials
+// bf16 split into s3 when given) from `split` partials; without pairs the
+// pair states are left to the z launch (bf16 path)
 hipError_t slot_finish(const dcoco_dims* d, const dcoco_weights* w, float* s, void* s3, const RepLayout& L,
-                       int split, hipStream_t st) {
+                       int split, hipStream_t st, bool pairs = true) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int R = d->n_blocks * d->B;
   const int r = d->d_proj, rs = d->d_pair, rz = d->d_z;
   const int ns = r + 2 * rs;
   hipError_t e;
+  if (!pairs) {
+    if (dt != kDtypeBf16) return hipErrorInvalidValue;
+    return launch_ln_gemm_gf(L.Y, split, R, ns, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, st);
+  }
   if (dt == kDtypeBf16 && ln_gemm_pair_supported(r, rs))
     return launch_ln_gemm_pair(L.Y, split, R, ns, r, d->ln_eps, w->W_f, 2ll * r, r, rz, L.gf, d->B, r,
                                r + rs, rs, s, s3, st);
@@ -171,9 +176,12 @@ constexpr int kTopkGemmSlots = 3 * 256;   // resident workgroups of the joint la
 // top-K of the logits and the slot side.  Where the rows and the slot GEMM
 // can share one launch (bf16, aligned rows, K <= 16), the GEMM's k split is
 // cut until its tiles and the rows fit the resident workgroup slots once;
-// otherwise the slot side and top-K run one after the other.
+// otherwise the slot side and top-K run one after the other.  With pairs
+// false the pair states are left to the z launch; *split gets the k split
+// of the slot partial sums.
 hipError_t topk_and_slot(const dcoco_dims* d, const dcoco_weights* w, const void* logits, const void* h, float* s,
-                         void* s3, const RepLayout& L, void* topk_ws, int32_t* ids, float* cl, hipStream_t st) {
+                         void* s3, const RepLayout& L, void* topk_ws, int32_t* ids, float* cl, hipStream_t st,
+                         bool pairs = true, int* split = nullptr) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int R = d->n_blocks * d->B;
   if (dt == kDtypeBf16) {
@@ -182,12 +190,30 @@ hipError_t topk_and_slot(const dcoco_dims* d, const dcoco_weights* w, const void
     if (topk_gemm_supported(d->V, d->K, logits, q)) {
       hipError_t e = launch_topk_gemm(logits, R, d->V, d->K, ids, cl, q, st);
       if (e != hipSuccess) return e;
-      return slot_finish(d, w, s, s3, L, q.split, st);
+      if (split) *split = q.split;
+      return slot_finish(d, w, s, s3, L, q.split, st, pairs);
     }
   }
-  hipError_t e = slot_part(d, w, h, s, s3, L, st);
+  if (split) *split = L.split_slot;
+  hipError_t e = launch_gemm(slot_gemm_problem(d, w, h, L, L.split_slot), st);
+  if (e == hipSuccess) e = slot_finish(d, w, s, s3, L, L.split_slot, st, pairs);
   if (e != hipSuccess) return e;
   return launch_topk(dt, logits, R, d->V, d->K, topk_ws, ids, cl, st);
+}
+
+// The pair states can ride on the z launch (bf16, r <= 256): the arguments
+// for it, from the slot partial sums of k split `split`.
+bool z_pairs(const dcoco_dims* d, const RepLayout& L, int split, float* s, void* s3, PairStateArgs* ps) {
+  const long long RK = static_cast<long long>(d->n_blocks) * d->B * d->K;
+  const int P = d->n_blocks * (d->B - 1);
+  const int r = d->d_proj, rs = d->d_pair;
+  if (d->dtype != DCOCO_BF16 || r > 256 || P <= 0 || RK > (1ll << 30) || split > 4 ||
+      !ln_gemm_pair_supported(r, rs) || !ln_gemm_pairs_fit(static_cast<int>(RK), P, rs))
+    return false;
+  if (ps == nullptr) return true;
+  ps->Y = L.Y; ps->split = split; ps->ldy = r + 2 * rs; ps->B = d->B; ps->cl = r; ps->cr = r + rs; ps->rs = rs;
+  ps->P = P; ps->s = s; ps->s3 = s3;
+  return true;
 }
 
 // candidate side, first half: P_e E[c] over gathered rows (split-K partials)
@@ -207,14 +233,16 @@ hipError_t cand_gemm(const dcoco_dims* d, const dcoco_weights* w, const void* E,
 }
 
 // candidate side, second half (needs gf): z = W_fb LN(P_e E[c]) + gf[slot]
+// (bf16: with ps, the pair states in the same launch)
 hipError_t cand_finish(const dcoco_dims* d, const dcoco_weights* w, void* z, const RepLayout& L,
-                       hipStream_t st) {
+                       hipStream_t st, const PairStateArgs* ps = nullptr) {
   const int dt = d->dtype == DCOCO_BF16 ? kDtypeBf16 : kDtypeF32;
   const int RK = d->n_blocks * d->B * d->K;
   const int r = d->d_proj, rz = d->d_z;
   if (dt == kDtypeBf16)
     return launch_ln_gemm(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, w->W_f, 2ll * r, 0, rz, nullptr, z, L.gf,
-                          d->K, st);
+                          d->K, st, ps);
+  if (ps) return hipErrorInvalidValue;
   hipError_t e;
   if ((e = launch_ln_rows(L.U, L.split_cand, RK, r, 0, r, d->ln_eps, L.b, dt, st)) != hipSuccess) return e;
   GemmProblem q{};
@@ -921,11 +949,17 @@ int dcoco_correct_block(const dcoco_dims* d, const dcoco_weights* w, const void*
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = dt == kDtypeBf16;
-  // the pair-state kernel also writes the bf16 split of s that the pair term reads
-  hipError_t e = topk_and_slot(d, w, logits, h, s, bf ? SL.s3 : nullptr, L, topk_ws, ids, cl, st);
-  if (e == hipSuccess) e = pair_term(d, w, s, SL, bf, st);
+  // the launch that makes the pair states also writes the bf16 split of s
+  // that the pair term reads: the z launch where it can carry them, else
+  // the gf launch
+  const bool zp = bf && z_pairs(d, L, L.split_slot, s, SL.s3, nullptr);
+  int split = 0;
+  hipError_t e = topk_and_slot(d, w, logits, h, s, bf ? SL.s3 : nullptr, L, topk_ws, ids, cl, st, !zp, &split);
+  PairStateArgs ps{};
+  if (zp && !z_pairs(d, L, split, s, SL.s3, &ps)) e = hipErrorInvalidValue;
   if (e == hipSuccess) e = cand_gemm(d, w, E, ids, L, st);
-  if (e == hipSuccess) e = cand_finish(d, w, z, L, st);
+  if (e == hipSuccess) e = cand_finish(d, w, z, L, st, zp ? &ps : nullptr);
+  if (e == hipSuccess) e = pair_term(d, w, s, SL, bf, st);
   const WalkOut wk{ids, sel_idx, sel_tok};
   bool walked = false;
   if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best, &wk, &walked);
@@ -1028,13 +1062,17 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
   if (S_out) S = S_out;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int r = d->d_proj;
-  hipError_t e = topk_and_slot(d, w, logits, h, s, SL.s3, L, topk_ws, ids, cl, st);
-  if (e == hipSuccess) e = pair_term(d, w, s, SL, true, st);
+  // the pair states ride on the gathered z launch where it can carry them
+  const bool zp = gather_gemm_supported(r) && z_pairs(d, L, L.split_slot, s, SL.s3, nullptr);
+  int split = 0;
+  hipError_t e = topk_and_slot(d, w, logits, h, s, SL.s3, L, topk_ws, ids, cl, st, !zp, &split);
+  PairStateArgs ps{};
+  if (zp && !z_pairs(d, L, split, s, SL.s3, &ps)) e = hipErrorInvalidValue;
   if (e == hipSuccess) {
     if (gather_gemm_supported(r)) {
       // table rows gathered into the LDS operand tile, W_fb slice resident in LDS
       e = launch_gather_gemm(btable, ids, d->V - 1, static_cast<int>(RK), r, w->W_f, 2ll * r, 0, d->d_z, z, L.gf,
-                             d->K, st);
+                             d->K, st, zp ? &ps : nullptr);
     } else {
       // wider rows: the GEMM gathers table rows by id, z = W_fb b[c] + gf[slot]
       GemmProblem q{};
@@ -1048,6 +1086,7 @@ int dcoco_correct_block_btable(const dcoco_dims* d, const dcoco_weights* w, cons
       e = launch_gemm(q, st);
     }
   }
+  if (e == hipSuccess) e = pair_term(d, w, s, SL, true, st);
   const WalkOut wk{ids, sel_idx, sel_tok};
   bool walked = false;
   if (e == hipSuccess) e = score_tail(d, w, z, cl, S, SL, st, best, &wk, &walked);

@@ -62,12 +62,25 @@ int gemm_pick_split_max(int M, int N, int Kd, int max_split);
 hipError_t launch_ln_rows(const float* x, int split, int M, int ldx, int col0, int r, float eps,
                           void* y, int out_dtype, hipStream_t st);
 
+// Pair states made by a z launch beside its rows: pair p = n (B - 1) + i
+// gets s_p = sum_s Y[s][n B + i][cl : cl + rs] + sum_s Y[s][n B + i + 1][cr : cr + rs]
+// (splits added in order) and, with s3, its three bf16 parts (s3[q P rs + p rs + j]).
+struct PairStateArgs {
+  const float* Y;
+  int split, ldy, B, cl, cr, rs, P;
+  float* s;
+  void* s3;
+};
+// the z launch over M rows can carry the P pair states of width rs
+bool ln_gemm_pairs_fit(int M, int P, int rs);
+
 // bf16 only: out[m, :] = W[:, wcol0 : wcol0 + r] LN(sum_s x[s][m][col0 : col0 + r]) with the
 // LN output rounded to bf16; fp32 out (out_bf == nullptr) or bf16 out with
-// + row_bias[m / row_div][n] (out_bf != nullptr).
+// + row_bias[m / row_div][n] (out_bf != nullptr; then, with ps, the pair
+// states too: r <= 256 and ln_gemm_pairs_fit).
 hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, int r, float eps,
                           const void* W, long long ldw, int wcol0, int N, float* out_f32, void* out_bf,
-                          const float* row_bias, int row_div, hipStream_t st);
+                          const float* row_bias, int row_div, hipStream_t st, const PairStateArgs* ps = nullptr);
 
 // s[n, p, :] = sum_s Y[s][n*B+p][cl : cl+rs] + sum_s Y[s][n*B+p+1][cr : cr+rs]
 // s3 (optional): the same values as three bf16 rows hi, mid, lo (s3[q * n + i])
@@ -77,12 +90,15 @@ bool ln_gemm_pair_supported(int r, int rs);
 hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r, float eps, const void* W,
                                long long ldw, int wcol0, int N, float* gf, int B, int cl, int cr, int rs, float* s,
                                void* s3, hipStream_t st);
+// the same gf launch without the pair states (r <= 256)
+hipError_t launch_ln_gemm_gf(const float* Y, int split, int M, int ldy, int r, float eps, const void* W,
+                             long long ldw, int wcol0, int N, float* gf, hipStream_t st);
 // z rows from a table of normalised projections (bf16): out = W[:, wcol0 .. +r]
 // tab[ids[m]] + row_bias[m / row_div], bf16 out [M][N]
 bool gather_gemm_supported(int r);
 hipError_t launch_gather_gemm(const void* tab, const int32_t* ids, int idmax, int M, int r, const void* W,
                               long long ldw, int wcol0, int N, void* out_bf, const float* row_bias, int row_div,
-                              hipStream_t st);
+                              hipStream_t st, const PairStateArgs* ps = nullptr);
 hipError_t launch_pair_state(const float* Y, int split, int N, int B, int ldy, int cl, int cr,
                              int rs, float* s, void* s3, hipStream_t st);
 

@@ -254,15 +254,43 @@ ln_gemm_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, flo
 constexpr int kLgCols = 256;                 // W rows (output columns) per LDS chunk
 constexpr int kLgRowBytes = 512;             // LDS bytes per W row (k <= 256)
 
-// Pair states assembled by the same launch (gf mode): for the workgroup's
-// slot rows m = n B + i with i < B - 1, s_p = Y_L[m] + Y_R[m + 1] (split
-// partials added in order) and its exact three-way bf16 split.
+// Pair states assembled by the same launch: s_p = Y_L[m] + Y_R[m + 1] for
+// slot row m = n B + i of pair p = n (B - 1) + i (split partials added in
+// order) and its exact three-way bf16 split.  By rows (gf mode): the pairs
+// of the workgroup's slot rows, from the operand x.  By workgroup (z mode):
+// workgroup x takes pairs x ppw .. x ppw + ppw - 1, one float4 item of 4
+// columns per thread, from y.
 struct PairArgs {
   int B, cl, cr, rs;
   float* s;
   uint16_t* s3;
   long long total;      // N (B - 1) rs
+  const float* y;       // z mode: slot partial sums [split][N B][ldy]
+  int split, ldy, ppw, P;
 };
+
+// s_p's four columns at t = p rs + j and their bf16 split
+__device__ __forceinline__ void store_pair_state(const PairArgs& pa, long long t, float4 sum) {
+  *reinterpret_cast<float4*>(pa.s + t) = sum;
+  if (pa.s3 == nullptr) return;
+  const float v4[4] = {sum.x, sum.y, sum.z, sum.w};
+  uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    hi[c] = f32_to_bf16(v4[c]);
+    const float r1 = v4[c] - bf16_to_f32(hi[c]);
+    mid[c] = f32_to_bf16(r1);
+    lo[c] = f32_to_bf16(r1 - bf16_to_f32(mid[c]));
+  }
+  auto pack4 = [](const uint16_t (&h)[4]) {
+    return make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
+  };
+  *reinterpret_cast<uint2*>(pa.s3 + t) = pack4(hi);
+  *reinterpret_cast<uint2*>(pa.s3 + pa.total + t) = pack4(mid);
+  *reinterpret_cast<uint2*>(pa.s3 + 2 * pa.total + t) = pack4(lo);
+}
+
+constexpr int kPairMaxSplit = 4;
 
 // Rows taken from a bf16 table instead of normalised here (GATHER mode): row
 // m of the operand is table row ids[m] (clamped into [0, idmax]), r values.
@@ -278,7 +306,8 @@ struct GatherArgs {
 // gridDim.y == 1 and ncols_wg == N.  With several column groups each one
 // normalises the same rows (cheap next to the loads), and in gf mode
 // assembles its share of the pair-state columns.
-template <int BM, int SPLIT, int MODE, bool PAIR, bool GATHER = false, int NCOL = kLgCols>
+// PAIR: 0 no pair states, 1 by rows (gf mode), 2 by workgroup (z mode).
+template <int BM, int SPLIT, int MODE, int PAIR, bool GATHER = false, int NCOL = kLgCols>
 __global__ void __launch_bounds__(256)
 ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, float eps,
                  const bf16* __restrict__ W, long long ldw, int wcol0, int N, float* __restrict__ out_f32,
@@ -335,6 +364,32 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
   };
   if constexpr (MODE == 1) load_bias(nb);
 
+  // z mode pair states: this thread's item loaded now (every split, the
+  // split index clamped so all loads issue unconditionally), added and
+  // stored after the operand rows are normalised
+  float4 pya[kPairMaxSplit], pyb[kPairMaxSplit];
+  bool pok = false;
+  long long pt = 0;
+  if constexpr (PAIR == 2) {
+    const int q4 = pa.rs >> 2;
+    const int item = tid;
+    const int p = static_cast<int>(blockIdx.x) * pa.ppw + item / q4;
+    const int j = (item % q4) * 4;
+    pok = item < pa.ppw * q4 && p < pa.P;
+    const long long pp = pok ? p : 0;
+    const long long nblk = pp / (pa.B - 1);
+    const long long ml = nblk * pa.B + (pp - nblk * (pa.B - 1));   // left slot row; the right one is ml + 1
+    const int jj = pok ? j : 0;
+    const long long rows = static_cast<long long>(pa.P / (pa.B - 1)) * pa.B;
+#pragma unroll
+    for (int s2 = 0; s2 < kPairMaxSplit; ++s2) {
+      const long long so = static_cast<long long>(min(s2, pa.split - 1)) * rows;
+      pya[s2] = *reinterpret_cast<const float4*>(pa.y + (so + ml) * pa.ldy + pa.cl + jj);
+      pyb[s2] = *reinterpret_cast<const float4*>(pa.y + (so + ml + 1) * pa.ldy + pa.cr + jj);
+    }
+    pt = pp * pa.rs + jj;
+  }
+
   if constexpr (GATHER) {
     // ---- table rows of this wave's RPW operand rows: lanes 0-31 and 32-63
     // take two rows per load round, one 16-byte chunk each; every load is
@@ -364,9 +419,23 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
     ln_rows_tile<RPW, SPLIT>(x, M, ldx, col0, r, eps, m0 + wv * RPW, tile + wv * RPW * kStr, kStr, l);
   }
 
+  if constexpr (PAIR == 2) {
+    if (pok) {
+      float4 a = pya[0], b = pyb[0];
+#pragma unroll
+      for (int s2 = 1; s2 < kPairMaxSplit; ++s2) {
+        if (s2 < pa.split) {
+          a.x += pya[s2].x; a.y += pya[s2].y; a.z += pya[s2].z; a.w += pya[s2].w;
+          b.x += pyb[s2].x; b.y += pyb[s2].y; b.z += pyb[s2].z; b.w += pyb[s2].w;
+        }
+      }
+      store_pair_state(pa, pt, make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w));
+    }
+  }
+
   // ---- pair states of this workgroup's rows (loads in flight with the
   // weight copy; float4 items of (row, 4 columns), 1024 per batch)
-  if constexpr (PAIR) {
+  if constexpr (PAIR == 1) {
     // this column group's share of the pair-state columns (all of them when
     // the share would not be whole float4 items)
     const int groups = gridDim.y;
@@ -403,26 +472,8 @@ ln_gemm_w_kernel(const float* __restrict__ x, int M, int ldx, int col0, int r, f
         t[k] = (static_cast<long long>(m / pa.B) * (pa.B - 1) + i) * pa.rs + j;
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (!ok[k]) continue;
-        *reinterpret_cast<float4*>(pa.s + t[k]) = sum[k];
-        if (pa.s3 == nullptr) continue;
-        const float v4[4] = {sum[k].x, sum[k].y, sum[k].z, sum[k].w};
-        uint16_t hi[4], mid[4], lo[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          hi[c] = f32_to_bf16(v4[c]);
-          const float r1 = v4[c] - bf16_to_f32(hi[c]);
-          mid[c] = f32_to_bf16(r1);
-          lo[c] = f32_to_bf16(r1 - bf16_to_f32(mid[c]));
-        }
-        auto pack4 = [](const uint16_t (&h)[4]) {
-          return make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
-        };
-        *reinterpret_cast<uint2*>(pa.s3 + t[k]) = pack4(hi);
-        *reinterpret_cast<uint2*>(pa.s3 + pa.total + t[k]) = pack4(mid);
-        *reinterpret_cast<uint2*>(pa.s3 + 2 * pa.total + t[k]) = pack4(lo);
-      }
+      for (int k = 0; k < 4; ++k)
+        if (ok[k]) store_pair_state(pa, t[k], sum[k]);
     }
   }
 
@@ -515,13 +566,45 @@ hipError_t launch_ln_rows(const float* x, int split, int M, int ldx, int col0, i
   return launch_ln_t<float>(x, split, M, ldx, col0, r, eps, y, st);
 }
 
+namespace {
+
+int ln_gemm_w_rows(int M) { return M >= 4096 ? 32 : 16; }
+
+// the z-mode pair-state arguments, or false where the launch cannot carry them
+bool z_pair_args(const PairStateArgs* ps, int M, PairArgs* pa) {
+  if (ps == nullptr || ps->B < 2 || ps->P <= 0 || !ln_gemm_pairs_fit(M, ps->P, ps->rs) || ps->split < 1 ||
+      ps->split > kPairMaxSplit)
+    return false;
+  const int grid = (M + ln_gemm_w_rows(M) - 1) / ln_gemm_w_rows(M);
+  pa->B = ps->B; pa->cl = ps->cl; pa->cr = ps->cr; pa->rs = ps->rs;
+  pa->s = ps->s; pa->s3 = static_cast<uint16_t*>(ps->s3);
+  pa->total = static_cast<long long>(ps->P) * ps->rs;
+  pa->y = ps->Y; pa->split = ps->split; pa->ldy = ps->ldy;
+  pa->ppw = (ps->P + grid - 1) / grid; pa->P = ps->P;
+  return true;
+}
+
+}  // namespace
+
+// The z launch (one workgroup per ln_gemm_w_rows(M) rows) takes ceil(P /
+// workgroups) pairs per workgroup, one float4 item per thread.
+bool ln_gemm_pairs_fit(int M, int P, int rs) {
+  if (M <= 0 || P <= 0 || rs <= 0 || rs % 4 != 0) return false;
+  const long long grid = (M + ln_gemm_w_rows(M) - 1) / ln_gemm_w_rows(M);
+  const long long ppw = (P + grid - 1) / grid;
+  return ppw * (rs / 4) <= 256;
+}
+
 hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, int r, float eps,
                           const void* W, long long ldw, int wcol0, int N, float* out_f32, void* out_bf,
-                          const float* row_bias, int row_div, hipStream_t st) {
+                          const float* row_bias, int row_div, hipStream_t st, const PairStateArgs* ps) {
   const bf16* Wb = static_cast<const bf16*>(W);
   bf16* ob = static_cast<bf16*>(out_bf);
   const bool bias = out_bf != nullptr;
   if (split != 1 && split != 2 && split != 4) return hipErrorInvalidValue;
+  PairArgs pa{};
+  const bool pairs = ps != nullptr;
+  if (pairs && (!bias || r > 256 || !z_pair_args(ps, M, &pa))) return hipErrorInvalidValue;
   // tile rows: enough workgroups to cover the chip, LN width in registers
 #define DCOCO_LNG(BMV, RM, SP, MD)                                                                      \
   hipLaunchKernelGGL((ln_gemm_kernel<BMV, RM, SP, MD>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, M, \
@@ -530,19 +613,21 @@ hipError_t launch_ln_gemm(const float* x, int split, int M, int ldx, int col0, i
   if (split == 1) DCOCO_LNG(BMV, RM, 1, MD);         \
   else if (split == 2) DCOCO_LNG(BMV, RM, 2, MD);    \
   else DCOCO_LNG(BMV, RM, 4, MD)
-#define DCOCO_LNW(BMV, SP, MD)                                                                      \
-  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD, false>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, \
-                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div, PairArgs{},      \
+#define DCOCO_LNW(BMV, SP, MD, PR)                                                                      \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, SP, MD, PR>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, x, \
+                     M, ldx, col0, r, eps, Wb, ldw, wcol0, N, out_f32, ob, row_bias, row_div, pa,          \
                      GatherArgs{}, N)
-#define DCOCO_LNW_SPLIT(BMV, MD)                 \
-  if (split == 1) DCOCO_LNW(BMV, 1, MD);         \
-  else if (split == 2) DCOCO_LNW(BMV, 2, MD);    \
-  else DCOCO_LNW(BMV, 4, MD)
+#define DCOCO_LNW_SPLIT(BMV, MD, PR)                 \
+  if (split == 1) DCOCO_LNW(BMV, 1, MD, PR);         \
+  else if (split == 2) DCOCO_LNW(BMV, 2, MD, PR);    \
+  else DCOCO_LNW(BMV, 4, MD, PR)
   if (r <= 256) {
     if (M >= 4096) {
-      if (bias) { DCOCO_LNW_SPLIT(32, 1); } else { DCOCO_LNW_SPLIT(32, 0); }
+      if (pairs) { DCOCO_LNW_SPLIT(32, 1, 2); }
+      else if (bias) { DCOCO_LNW_SPLIT(32, 1, 0); } else { DCOCO_LNW_SPLIT(32, 0, 0); }
     } else {
-      if (bias) { DCOCO_LNW_SPLIT(16, 1); } else { DCOCO_LNW_SPLIT(16, 0); }
+      if (pairs) { DCOCO_LNW_SPLIT(16, 1, 2); }
+      else if (bias) { DCOCO_LNW_SPLIT(16, 1, 0); } else { DCOCO_LNW_SPLIT(16, 0, 0); }
     }
   } else if (r <= 512) {
     if (bias) { DCOCO_LNG_SPLIT(16, 512, 1); } else { DCOCO_LNG_SPLIT(16, 512, 0); }
@@ -569,7 +654,7 @@ hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r,
   const bf16* Wb = static_cast<const bf16*>(W);
   // few rows: the output columns are spread over four workgroups of 64
 #define DCOCO_LNP(SP)                                                                                             \
-  hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, true, false, 64>), dim3((M + 15) / 16, (N + 63) / 64), dim3(256), \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, 1, false, 64>), dim3((M + 15) / 16, (N + 63) / 64), dim3(256), \
                      0, st, Y, M, ldy, 0, r, eps, Wb, ldw, wcol0, N, gf, static_cast<bf16*>(nullptr),               \
                      static_cast<const float*>(nullptr), 1, pa, GatherArgs{}, 64)
   if (split == 1) DCOCO_LNP(1);
@@ -579,24 +664,43 @@ hipError_t launch_ln_gemm_pair(const float* Y, int split, int M, int ldy, int r,
   return hipGetLastError();
 }
 
+hipError_t launch_ln_gemm_gf(const float* Y, int split, int M, int ldy, int r, float eps, const void* W,
+                             long long ldw, int wcol0, int N, float* gf, hipStream_t st) {
+  if (r > 256 || (split != 1 && split != 2 && split != 4)) return hipErrorInvalidValue;
+  const bf16* Wb = static_cast<const bf16*>(W);
+  // as launch_ln_gemm_pair, without the pair states
+#define DCOCO_LNF(SP)                                                                                            \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<16, SP, 0, 0, false, 64>), dim3((M + 15) / 16, (N + 63) / 64), dim3(256), \
+                     0, st, Y, M, ldy, 0, r, eps, Wb, ldw, wcol0, N, gf, static_cast<bf16*>(nullptr),              \
+                     static_cast<const float*>(nullptr), 1, PairArgs{}, GatherArgs{}, 64)
+  if (split == 1) DCOCO_LNF(1);
+  else if (split == 2) DCOCO_LNF(2);
+  else DCOCO_LNF(4);
+#undef DCOCO_LNF
+  return hipGetLastError();
+}
+
 bool gather_gemm_supported(int r) { return r <= 256 && r % 8 == 0; }
 
 hipError_t launch_gather_gemm(const void* tab, const int32_t* ids, int idmax, int M, int r, const void* W,
                               long long ldw, int wcol0, int N, void* out_bf, const float* row_bias, int row_div,
-                              hipStream_t st) {
+                              hipStream_t st, const PairStateArgs* ps) {
   if (!gather_gemm_supported(r)) return hipErrorInvalidValue;
+  PairArgs pa{};
+  const bool pairs = ps != nullptr;
+  if (pairs && !z_pair_args(ps, M, &pa)) return hipErrorInvalidValue;
   GatherArgs ga;
   ga.tab = static_cast<const uint16_t*>(tab);
   ga.ids = ids;
   ga.idmax = idmax;
   const bf16* Wb = static_cast<const bf16*>(W);
   bf16* ob = static_cast<bf16*>(out_bf);
-#define DCOCO_LNG_G(BMV)                                                                                  \
-  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, 1, 1, false, true>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st, \
+#define DCOCO_LNG_G(BMV, PR)                                                                                  \
+  hipLaunchKernelGGL((ln_gemm_w_kernel<BMV, 1, 1, PR, true>), dim3((M + BMV - 1) / BMV), dim3(256), 0, st,   \
                      static_cast<const float*>(nullptr), M, r, 0, r, 1.0f, Wb, ldw, wcol0, N,                \
-                     static_cast<float*>(nullptr), ob, row_bias, row_div, PairArgs{}, ga, N)
-  if (M >= 4096) DCOCO_LNG_G(32);
-  else DCOCO_LNG_G(16);
+                     static_cast<float*>(nullptr), ob, row_bias, row_div, pa, ga, N)
+  if (M >= 4096) { if (pairs) { DCOCO_LNG_G(32, 2); } else { DCOCO_LNG_G(32, 0); } }
+  else { if (pairs) { DCOCO_LNG_G(16, 2); } else { DCOCO_LNG_G(16, 0); } }
 #undef DCOCO_LNG_G
   return hipGetLastError();
 }
