@@ -993,21 +993,34 @@ constexpr size_t kFuseLds = RowLds<1>::kBytes > static_cast<size_t>(FuseTile::kS
 template <int NV, int D>
 __global__ void __launch_bounds__(kRowWaves * kWave, 6)   // three workgroups per CU
 topk_gemm_kernel(const uint16_t* __restrict__ logits, int V, int K, int rounds, int32_t* __restrict__ ids,
-                 float* __restrict__ vals, GemmDev p, int tiles_m, int tiles_n, int n_gemm) {
+                 float* __restrict__ vals, GemmDev p, int tiles_m, int tiles_n, int n_gemm, int cm, int cn) {
   __shared__ __align__(1024) char arena[kFuseLds];
   const int bid = blockIdx.x;
   if (bid < n_gemm) {
     constexpr int MW = FuseTile::MW, NWB = FuseTile::NWB, TM = FuseTile::TM, TN = FuseTile::TN;
     constexpr int kStage = FuseTile::kStage;
-    // workgroups are dealt to the 8 XCDs in turn: when the tiles divide
-    // evenly, XCD x takes a contiguous run of (split, tm, tn), so it reads
-    // only its own rows of A from HBM rather than all of them
-    int b = bid;
-    if (n_gemm % 8 == 0) b = (bid % 8) * (n_gemm / 8) + bid / 8;
-    const int tn = b % tiles_n;
-    b /= tiles_n;
-    const int tm = b % tiles_m;
-    const int zs = b / tiles_m;
+    // workgroups are dealt to the 8 XCDs in turn (blockIdx % 8).  With a
+    // block shape (cm, cn), the cm cn XCDs of one k split each take a
+    // (tiles_m / cm) x (tiles_n / cn) block of tiles, so the rows of A and of
+    // W an XCD reads stay few next to the logits streaming through its L2;
+    // otherwise, when the tiles divide evenly, XCD x takes a contiguous run
+    // of (split, tm, tn)
+    int tn, tm, zs;
+    if (cm > 0) {
+      const int x = bid % 8, j = bid / 8;
+      const int bm = tiles_m / cm, bn = tiles_n / cn;
+      const int q = x % (cm * cn);
+      zs = x / (cm * cn);
+      tm = (q / cn) * bm + j / bn;
+      tn = (q % cn) * bn + j % bn;
+    } else {
+      int b = bid;
+      if (n_gemm % 8 == 0) b = (bid % 8) * (n_gemm / 8) + bid / 8;
+      tn = b % tiles_n;
+      b /= tiles_n;
+      tm = b % tiles_m;
+      zs = b / tiles_m;
+    }
     const int n0 = tn * 64;
     const int m0 = tm * 64;
     const int kbeg = zs * p.ksplit;
@@ -1216,8 +1229,21 @@ hipError_t launch_topk_gemm(const void* logits, int rows, int V, int K, int32_t*
   const int tiles_n = (q.N + 63) / 64;
   const int n_gemm = tiles_m * tiles_n * q.split;
   const int rounds = (V + kRowWaves * kWave * kRegNV * 8 - 1) / (kRowWaves * kWave * kRegNV * 8);
+  // the block shape with the fewest A and W rows per XCD: the 8 / split XCDs
+  // of a k split factored as cm x cn, dividing the tile grid evenly
+  int cm = 0, cn = 0;
+  if (8 % q.split == 0) {
+    const int c = 8 / q.split;
+    int best = 1 << 30;
+    for (int f = 1; f <= c; ++f) {
+      if (c % f || tiles_m % f || tiles_n % (c / f)) continue;
+      const int rows_x = tiles_m / f + tiles_n / (c / f);
+      if (rows_x < best) { best = rows_x; cm = f; cn = c / f; }
+    }
+  }
   hipLaunchKernelGGL((topk_gemm_kernel<kRegNV, kRegD>), dim3(n_gemm + rows), dim3(kRowWaves * kWave), 0, st,
-                     static_cast<const uint16_t*>(logits), V, K, rounds, ids, vals, p, tiles_m, tiles_n, n_gemm);
+                     static_cast<const uint16_t*>(logits), V, K, rounds, ids, vals, p, tiles_m, tiles_n, n_gemm, cm,
+                     cn);
   return hipGetLastError();
 }
 
