@@ -373,26 +373,34 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
 // are merged into its sorted list (a few per tile: inserted one by one; many,
 // as on the first tile: an exact selection over list + tile).  The lists of
 // all groups are merged by lm_head_merge_kernel.
-constexpr int kLmBM = 128;
 constexpr int kLmBN = 256;
 constexpr int kLmMaxK = 64;
-using LmTile = DmaTile<kLmBM, kLmBN, 2, 4, 2>;
+// row tile: 256 rows (16 waves) where the lists are short (K <= 16), else
+// 128 (8 waves); each wave owns 64 x 64 outputs
+constexpr int lm_rows(int K) { return K <= 16 ? 256 : 128; }
+template <int BM>
+using LmTile = DmaTile<BM, kLmBN, BM / 64, 4, 2>;
 
 __device__ __forceinline__ uint32_t key16_of(float x) { return order_key(bf16{f32_to_bf16(x)}); }
 
-// KMAX (16 or 64) bounds K: the rows' lists take 128 KMAX composites of LDS
-// beside the two ring slots (96 KB), all 160 KB at KMAX = 64.
-template <int KMAX>
-__global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int tiles_m, int tiles_n, int groups,
-                                                           int xcd_map, uint64_t* __restrict__ part) {
-  constexpr int TM = LmTile::TM, TN = LmTile::TN, MW = LmTile::MW, NWB = LmTile::NWB;
-  static_assert(2 * LmTile::kStage + kLmBM * KMAX * 8 <= 160 * 1024, "LDS");
-  __shared__ __align__(1024) char sm0[LmTile::kStage];
-  __shared__ __align__(1024) char sm1[LmTile::kStage];
+// KMAX (16 or 64) bounds K: the rows' lists take BM KMAX composites of LDS
+// beside the two ring slots: 128 + 32 KB for 256-row tiles at KMAX = 16,
+// 96 + 64 KB for 128-row tiles at KMAX = 64.
+template <int KMAX, int BM>
+__global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, int tiles_m, int tiles_n, int groups,
+                                                             int xcd_map, uint64_t* __restrict__ part) {
+  using LT = LmTile<BM>;
+  constexpr int NWV = LT::NW;          // waves
+  constexpr int NT = NWV * 64;         // threads
+  constexpr int kLmBM = BM;
+  constexpr int TM = LT::TM, TN = LT::TN, MW = LT::MW, NWB = LT::NWB;
+  static_assert(2 * LT::kStage + kLmBM * KMAX * 8 <= 160 * 1024, "LDS");
+  __shared__ __align__(1024) char sm0[LT::kStage];
+  __shared__ __align__(1024) char sm1[LT::kStage];
   __shared__ uint64_t s_top[kLmBM][KMAX];   // per row, sorted; entry K - 1 is 0 until K are held
   constexpr int kRowBytes = kLmBN * 2;                   // staged keys of one row
-  constexpr int kRows0 = LmTile::kStage / kRowBytes;     // rows that fit in sm0
-  static_assert(kLmBM - kRows0 <= LmTile::kStage / kRowBytes, "keys fit the ring");
+  constexpr int kRows0 = LT::kStage / kRowBytes;         // rows that fit in sm0
+  static_assert(kLmBM - kRows0 <= LT::kStage / kRowBytes, "keys fit the ring");
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -414,12 +422,12 @@ __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int
   auto keyrow = [&](int r) -> uint16_t* {
     return reinterpret_cast<uint16_t*>(r < kRows0 ? sm0 + r * kRowBytes : sm1 + (r - kRows0) * kRowBytes);
   };
-  for (int i = tid; i < kLmBM * KMAX; i += 512) (&s_top[0][0])[i] = 0ull;
+  for (int i = tid; i < kLmBM * KMAX; i += NT) (&s_top[0][0])[i] = 0ull;
 
   for (int tn = g; tn < tiles_n; tn += groups) {
     const int n0 = tn * kLmBN;
     f32x4_t acc[TM][TN];
-    dma_tile_mainloop<kLmBM, kLmBN, 2, 4, 2>(p, m0, n0, 0, p.Kd, sm0, sm1, sm0, sm0, acc);
+    dma_tile_mainloop<kLmBM, kLmBN, kLmBM / 64, 4, 2>(p, m0, n0, 0, p.Kd, sm0, sm1, sm0, sm0, acc);
     __syncthreads();                         // every wave is done with the ring
 #pragma unroll
     for (int a = 0; a < TM; ++a)
@@ -432,8 +440,8 @@ __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int
           keyrow(r)[c] = n0 + c < p.N ? static_cast<uint16_t>(key16_of(acc[a][bb][v])) : 0;
         }
     __syncthreads();
-    for (int i = 0; i < kLmBM / 8; ++i) {
-      const int r = wv + 8 * i;
+    for (int i = 0; i < kLmBM / NWV; ++i) {
+      const int r = wv + NWV * i;
       const uint64_t thr = s_top[r][K - 1];   // the row's K-th best so far (0 while not full)
       const uint16_t* kr = keyrow(r);
       uint64_t c[5];
@@ -491,7 +499,7 @@ __global__ void __launch_bounds__(512) lm_head_topk_kernel(GemmDev p, int K, int
     }
     __syncthreads();                         // the next tile's loads reuse the ring
   }
-  for (int i = tid; i < kLmBM * K; i += 512) {
+  for (int i = tid; i < kLmBM * K; i += NT) {
     const int r = i / K;
     const int j = i - r * K;
     if (m0 + r < p.M) part[(static_cast<long long>(g) * p.M + m0 + r) * K + j] = s_top[r][j];
@@ -571,7 +579,7 @@ bool lm_head_topk_supported(int M, int V, int d, int K) {
 }
 
 int lm_head_groups(int M, int V, int K) {
-  const int tiles_m = (M + kLmBM - 1) / kLmBM;
+  const int tiles_m = (M + lm_rows(K) - 1) / lm_rows(K);
   const int tiles_n = (V + kLmBN - 1) / kLmBN;
   int groups = std::max(1, 256 / tiles_m);
   groups = std::min(groups, 2048 / K);         // the merge holds 2048 composites per row
@@ -594,17 +602,17 @@ hipError_t launch_lm_head_topk(const void* hd, const void* W_lm, int M, int V, i
   p.ldw0 = p.ldw1 = p.ldw2 = d;
   p.end0 = p.end1 = V;
   p.row_bias_div = 1;
-  const int tiles_m = (M + kLmBM - 1) / kLmBM;
+  const int tiles_m = (M + lm_rows(K) - 1) / lm_rows(K);
   const int tiles_n = (V + kLmBN - 1) / kLmBN;
   const int groups = lm_head_groups(M, V, K);
   const int xcd_map = groups % 8 == 0 ? 1 : 0;
   uint64_t* part = static_cast<uint64_t*>(workspace);
   if (K <= 16)
-    hipLaunchKernelGGL(lm_head_topk_kernel<16>, dim3(tiles_m * groups), dim3(512), 0, st, p, K, tiles_m, tiles_n,
-                       groups, xcd_map, part);
+    hipLaunchKernelGGL((lm_head_topk_kernel<16, lm_rows(16)>), dim3(tiles_m * groups), dim3(lm_rows(16) * 4), 0,
+                       st, p, K, tiles_m, tiles_n, groups, xcd_map, part);
   else
-    hipLaunchKernelGGL(lm_head_topk_kernel<64>, dim3(tiles_m * groups), dim3(512), 0, st, p, K, tiles_m, tiles_n,
-                       groups, xcd_map, part);
+    hipLaunchKernelGGL((lm_head_topk_kernel<64, lm_rows(64)>), dim3(tiles_m * groups), dim3(lm_rows(64) * 4), 0,
+                       st, p, K, tiles_m, tiles_n, groups, xcd_map, part);
   const int count = groups * K;
 #define DCOCO_LMM(QV) \
   hipLaunchKernelGGL((lm_head_merge_kernel<QV>), dim3(M), dim3(64), 0, st, part, groups, M, K, ids, vals)

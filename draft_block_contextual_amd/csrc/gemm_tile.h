@@ -138,33 +138,39 @@ __device__ __forceinline__ void dma_tile_mainloop(
     else return sm3;
   };
   const int frow = l & 15;
+  // fragments of both 32-deep halves of a stage are read first (so the MFMAs
+  // issue back to back behind the reads) unless the wave tile is large or
+  // the workgroup has more than 8 waves (fewer registers per wave), where
+  // each half is read in turn
+  constexpr int KH = (NW <= 8 && (TM + TN) * 2 <= 16) ? 2 : 1;
   auto compute = [&](const char* sa) {
     const char* sw = sa + kABytes;
-    // every fragment of the stage (both 32-deep halves) is read first, so the
-    // MFMAs issue back to back behind the reads instead of waiting on each
-    bf16x8_t fa[2][TM], fw[2][TN];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ks * 4 + (l >> 4);
+    for (int k0 = 0; k0 < 2; k0 += KH) {
+      bf16x8_t fa[KH][TM], fw[KH][TN];
 #pragma unroll
-      for (int a = 0; a < TM; ++a) {
-        const int row = wm * MW + a * 16 + frow;
-        fa[ks][a] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + row * kDmaRow + dma_swz(row, c) * 16));
+      for (int kh = 0; kh < KH; ++kh) {
+        const int c = (k0 + kh) * 4 + (l >> 4);
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+          const int row = wm * MW + a * 16 + frow;
+          fa[kh][a] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + row * kDmaRow + dma_swz(row, c) * 16));
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int row = wn * NWB + b * 16 + frow;
+          fw[kh][b] = as_bf16x8(*reinterpret_cast<const uint4*>(sw + row * kDmaRow + dma_swz(row, c) * 16));
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
 #pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int row = wn * NWB + b * 16 + frow;
-        fw[ks][b] = as_bf16x8(*reinterpret_cast<const uint4*>(sw + row * kDmaRow + dma_swz(row, c) * 16));
-      }
+      for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kh][a], fw[kh][b], acc[a][b], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][a], fw[ks][b], acc[a][b], 0, 0, 0);
   };
   // one pipeline step on ring slot S: wait for its loads, barrier, refill the
   // slot consumed in the previous step, then compute on slot S
