@@ -376,7 +376,7 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
 constexpr int kLmBN = 256;
 constexpr int kLmMaxK = 64;
 // row tile: 256 rows (16 waves) where the lists are short (K <= 16), else
-// 128 (8 waves); each wave owns 64 x 64 outputs
+// 128 (8 waves); each wave owns 64 x 64 outputs; two ring slots
 constexpr int lm_rows(int K) { return K <= 16 ? 256 : 128; }
 template <int BM>
 using LmTile = DmaTile<BM, kLmBN, BM / 64, 4, 2>;
@@ -390,17 +390,18 @@ template <int KMAX, int BM>
 __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, int tiles_m, int tiles_n, int groups,
                                                              int xcd_map, uint64_t* __restrict__ part) {
   using LT = LmTile<BM>;
+  constexpr int kSlots = 2;
   constexpr int NWV = LT::NW;          // waves
   constexpr int NT = NWV * 64;         // threads
   constexpr int kLmBM = BM;
   constexpr int TM = LT::TM, TN = LT::TN, MW = LT::MW, NWB = LT::NWB;
-  static_assert(2 * LT::kStage + kLmBM * KMAX * 8 <= 160 * 1024, "LDS");
+  static_assert(kSlots * LT::kStage + kLmBM * KMAX * 8 <= 160 * 1024, "LDS");
   __shared__ __align__(1024) char sm0[LT::kStage];
   __shared__ __align__(1024) char sm1[LT::kStage];
   __shared__ uint64_t s_top[kLmBM][KMAX];   // per row, sorted; entry K - 1 is 0 until K are held
   constexpr int kRowBytes = kLmBN * 2;                   // staged keys of one row
-  constexpr int kRows0 = LT::kStage / kRowBytes;         // rows that fit in sm0
-  static_assert(kLmBM - kRows0 <= LT::kStage / kRowBytes, "keys fit the ring");
+  constexpr int kRowsSlot = LT::kStage / kRowBytes;      // rows of keys one ring slot holds
+  static_assert(kLmBM <= kSlots * kRowsSlot, "keys fit the ring");
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -420,7 +421,7 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
   }
   const int m0 = tm * kLmBM;
   auto keyrow = [&](int r) -> uint16_t* {
-    return reinterpret_cast<uint16_t*>(r < kRows0 ? sm0 + r * kRowBytes : sm1 + (r - kRows0) * kRowBytes);
+    return reinterpret_cast<uint16_t*>(r < kRowsSlot ? sm0 + r * kRowBytes : sm1 + (r - kRowsSlot) * kRowBytes);
   };
   for (int i = tid; i < kLmBM * KMAX; i += NT) (&s_top[0][0])[i] = 0ull;
 
@@ -456,8 +457,27 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
         n += __popcll(ballot(c[q + 1] != 0ull));
       }
       if (n == 0) continue;
+      if (n > 32) {
+        // many newcomers (as on a row's first tile): only keys at or above
+        // the K-th largest of the lanes' largest keys can make the list
+        // (at least K newcomers reach it)
+        uint32_t mk = 0;
+#pragma unroll
+        for (int q = 1; q < 5; ++q) mk = max(mk, comp_key(c[q]));
+        uint32_t tk = 0;
+        for (int bit = 15; bit >= 0; --bit) {
+          const uint32_t cand = tk | (1u << bit);
+          if (__popcll(ballot(mk >= cand)) >= K) tk = cand;
+        }
+        n = 0;
+#pragma unroll
+        for (int q = 1; q < 5; ++q) {
+          c[q] = comp_key(c[q]) >= tk ? c[q] : 0ull;
+          n += __popcll(ballot(c[q] != 0ull));
+        }
+      }
       uint64_t cur = c[0];
-      if (n <= 8 && thr != 0ull) {
+      if (n <= 32) {
         // insert each newcomer into the sorted list (lanes 0..K-1)
 #pragma unroll
         for (int q = 1; q < 5; ++q) {
