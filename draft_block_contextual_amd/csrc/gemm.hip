@@ -23,6 +23,7 @@
 #include "gemm_tile.h"
 #include "kernels.h"
 #include "select.h"
+#include "wave.h"
 
 namespace dcoco {
 
@@ -383,6 +384,13 @@ using LmTile = DmaTile<BM, kLmBN, BM / 64, 4, 2>;
 
 __device__ __forceinline__ uint32_t key16_of(float x) { return order_key(bf16{f32_to_bf16(x)}); }
 
+// v from a wave-uniform lane, through the scalar unit (no LDS permute)
+__device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane) {
+  const uint32_t lo = read_lane_u32(static_cast<uint32_t>(v), lane);
+  const uint32_t hi = read_lane_u32(static_cast<uint32_t>(v >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // KMAX (16 or 64) bounds K: the rows' lists take BM KMAX composites of LDS
 // beside the two ring slots: 128 + 32 KB for 256-row tiles at KMAX = 16,
 // 96 + 64 KB for 128-row tiles at KMAX = 64.
@@ -485,7 +493,7 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
           while (m) {
             const int src = __builtin_ctzll(m);
             m &= m - 1;
-            const uint64_t x = __shfl(c[q], src, kWave);
+            const uint64_t x = read_lane_u64(c[q], src);
             const int pos = __popcll(ballot(l < K && cur > x));
             const uint64_t up = __shfl_up(cur, 1, kWave);
             cur = l < pos ? cur : (l == pos ? x : up);
@@ -507,11 +515,11 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
         __builtin_amdgcn_wave_barrier();
         const uint64_t mine = l < base ? scratch[l] : 0ull;
         int rank = 0;
-        for (int j = 0; j < base; ++j) rank += __shfl(mine, j, kWave) > mine ? 1 : 0;
+        for (int j = 0; j < base; ++j) rank += read_lane_u64(mine, j) > mine ? 1 : 0;
         cur = 0ull;
         for (int j = 0; j < base; ++j) {
-          const uint64_t xj = __shfl(mine, j, kWave);
-          const int rj = __shfl(rank, j, kWave);
+          const uint64_t xj = read_lane_u64(mine, j);
+          const int rj = static_cast<int>(read_lane_u32(static_cast<uint32_t>(rank), j));
           cur = l == rj ? xj : cur;
         }
       }
