@@ -384,6 +384,14 @@ using LmTile = DmaTile<BM, kLmBN, BM / 64, 4, 2>;
 
 __device__ __forceinline__ uint32_t key16_of(float x) { return order_key(bf16{f32_to_bf16(x)}); }
 
+// lane l gets lane l - 1's v (lane 0 gets 0): a DPP wave shift, no LDS permute
+__device__ __forceinline__ uint64_t shift_up_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), 0x138, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), 0x138, 0xf, 0xf,
+                                             false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
 // v from a wave-uniform lane, through the scalar unit (no LDS permute)
 __device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane) {
   const uint32_t lo = read_lane_u32(static_cast<uint32_t>(v), lane);
@@ -495,7 +503,7 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
             m &= m - 1;
             const uint64_t x = read_lane_u64(c[q], src);
             const int pos = __popcll(ballot(l < K && cur > x));
-            const uint64_t up = __shfl_up(cur, 1, kWave);
+            const uint64_t up = shift_up_u64(cur);
             cur = l < pos ? cur : (l == pos ? x : up);
           }
         }
