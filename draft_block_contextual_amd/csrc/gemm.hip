@@ -368,12 +368,18 @@ hipError_t launch_gemm_t(const GemmProblem& q, hipStream_t st) {
 // tile by tile on MFMA, rounded to bf16 (the drafter's stored logit), and
 // each workgroup keeps, per row, the top K of every vocabulary tile it has
 // seen; the logits never reach memory.  Workgroup (tm, g) takes rows
-// [128 tm, +128) and vocabulary tiles g, g + groups, ...  Per tile, after the
-// k loop, the 128 x 256 keys are staged in the (now idle) LDS ring; each wave
-// then takes 16 rows: the tile's composites above the row's current K-th best
-// are merged into its sorted list (a few per tile: inserted one by one; many,
-// as on the first tile: an exact selection over list + tile).  The lists of
-// all groups are merged by lm_head_merge_kernel.
+// [BM tm, +BM) and vocabulary tiles g, g + groups, ...  Per tile, after the
+// k loop, the BM x 256 keys are staged in the (now idle) LDS ring.  With K <= 16
+// each row is then merged by one lane (all of the workgroup's rows at once, one
+// per lane of the first BM / 64 waves): the lane marks its row's keys above the
+// list's K-th best (or, while the list is not full, at or above a bound that K
+// of the tile's keys reach: the K-th largest of the 64 per-lane maxima of the
+// row, found by one wave beforehand), then pushes each marked composite through
+// a fixed insertion network over its 16 list entries (a composite below the
+// K-th best leaves the list as it is).  With K <= 64 one wave merges each row:
+// the tile's composites above the row's K-th best go into its sorted list (a
+// few: inserted one by one; many: an exact selection over list + tile).  The
+// lists of all groups are merged by lm_head_merge_kernel.
 constexpr int kLmBN = 256;
 constexpr int kLmMaxK = 64;
 // row tile: 256 rows (16 waves) where the lists are short (K <= 16), else
@@ -391,6 +397,10 @@ __device__ __forceinline__ uint64_t shift_up_u64(uint64_t v) {
                                              false);
   return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
 }
+
+// the larger / smaller of two composites
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 // v from a wave-uniform lane, through the scalar unit (no LDS permute)
 __device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane) {
@@ -415,6 +425,8 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
   __shared__ __align__(1024) char sm0[LT::kStage];
   __shared__ __align__(1024) char sm1[LT::kStage];
   __shared__ uint64_t s_top[kLmBM][KMAX];   // per row, sorted; entry K - 1 is 0 until K are held
+  // entry j of row r sits at j ^ (r & 15) for KMAX = 16, so the lanes that each
+  // read their own row's entry j fall on different banks
   constexpr int kRowBytes = kLmBN * 2;                   // staged keys of one row
   constexpr int kRowsSlot = LT::kStage / kRowBytes;      // rows of keys one ring slot holds
   static_assert(kLmBM <= kSlots * kRowsSlot, "keys fit the ring");
@@ -439,6 +451,7 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
   auto keyrow = [&](int r) -> uint16_t* {
     return reinterpret_cast<uint16_t*>(r < kRowsSlot ? sm0 + r * kRowBytes : sm1 + (r - kRowsSlot) * kRowBytes);
   };
+  auto tp = [](int r, int j) { return KMAX == 16 ? (j ^ (r & 15)) : j; };
   for (int i = tid; i < kLmBM * KMAX; i += NT) (&s_top[0][0])[i] = 0ull;
 
   for (int tn = g; tn < tiles_n; tn += groups) {
@@ -459,10 +472,29 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
     __syncthreads();
     for (int i = 0; i < kLmBM / NWV; ++i) {
       const int r = wv + NWV * i;
-      const uint64_t thr = s_top[r][K - 1];   // the row's K-th best so far (0 while not full)
+      const uint64_t thr = s_top[r][tp(r, K - 1)];   // the row's K-th best so far (0 while not full)
       const uint16_t* kr = keyrow(r);
+      if constexpr (KMAX == 16) {
+        // a list not full yet: the K-th largest of the lanes' maxima over keys
+        // 4 l .. 4 l + 3 (K of the tile's keys reach it), left in the list's
+        // empty entry K - 1 with bit 63 set (no composite has it) for the
+        // row's lane
+        if (thr == 0ull) {
+          const uint64_t v = *reinterpret_cast<const uint64_t*>(kr + 4 * l);
+          const uint32_t m0 = max(static_cast<uint32_t>(v) & 0xffffu, static_cast<uint32_t>(v >> 16) & 0xffffu);
+          const uint32_t m1 = max(static_cast<uint32_t>(v >> 32) & 0xffffu, static_cast<uint32_t>(v >> 48));
+          const uint32_t mx = max(m0, m1);
+          uint32_t tb = 0;
+          for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t cand = tb | (1u << bit);
+            if (__popcll(ballot(mx >= cand)) >= K) tb = cand;
+          }
+          if (l == 0) s_top[r][tp(r, K - 1)] = (1ull << 63) | tb;
+        }
+        continue;
+      }
       uint64_t c[5];
-      c[0] = l < K ? s_top[r][l] : 0ull;     // the current list, sorted
+      c[0] = l < K ? s_top[r][tp(r, l)] : 0ull;     // the current list, sorted
       int n = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -531,14 +563,80 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
           cur = l == rj ? xj : cur;
         }
       }
-      if (l < K) s_top[r][l] = cur;
+      if (l < K) s_top[r][tp(r, l)] = cur;
+    }
+    if constexpr (KMAX == 16) {
+      __syncthreads();                       // the bounds of the rows not full yet
+      if (tid < kLmBM) {
+        // one lane per row: bit w of mw marks the row's 8-byte word (w + r) mod
+        // 64 (the lanes start at different words, so their reads fall on
+        // different banks) when one of its four keys beats the K-th best (full
+        // list) or reaches the bound (list not full)
+        const int r = tid;
+        const uint64_t T = s_top[r][tp(r, K - 1)];
+        const bool bound = (T >> 63) != 0ull;
+        const int tk = bound ? static_cast<int>(static_cast<uint32_t>(T)) - 1 : static_cast<int>(comp_key(T));
+        const uint16_t* kr = keyrow(r);
+        auto word = [&](int w) { return *reinterpret_cast<const uint64_t*>(kr + 4 * ((w + r) & 63)); };
+        auto key_of = [](uint64_t v, int j) { return static_cast<int>(static_cast<uint32_t>(v >> (16 * j)) & 0xffffu); };
+        uint64_t mw = 0ull;
+#pragma unroll 1
+        for (int w8 = 0; w8 < 64; w8 += 8) {
+          uint32_t m8 = 0u;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const uint64_t v = word(w8 + w);
+            const int mx = max(max(key_of(v, 0), key_of(v, 1)), max(key_of(v, 2), key_of(v, 3)));
+            m8 |= (mx > tk ? 1u : 0u) << w;
+          }
+          mw |= static_cast<uint64_t>(m8) << w8;
+        }
+        uint64_t L[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint64_t e = s_top[r][j ^ (r & 15)];
+          L[j] = (bound && j == K - 1) ? 0ull : e;   // the bound's entry was empty
+        }
+        // one marked key per lane and round, until no lane has any left (a
+        // marked word holds at least one)
+        uint64_t cur = 0ull;   // the current word's keys
+        uint32_t ks = 0u;      // its marked keys not yet taken
+        int wc = 0;            // its word index
+        const bool any = mw != 0ull;
+        while (ballot(mw != 0ull || ks != 0u) != 0ull) {
+          if (ks == 0u && mw != 0ull) {
+            wc = __builtin_ctzll(mw);
+            mw &= mw - 1;
+            cur = word(wc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ks |= (key_of(cur, j) > tk ? 1u : 0u) << j;
+          }
+          uint64_t x = 0ull;
+          if (ks != 0u) {
+            const int j = __builtin_ctz(ks);
+            ks &= ks - 1;
+            const int col = (((wc + r) & 63) << 2) | j;
+            const uint32_t key = static_cast<uint32_t>(key_of(cur, j));   // 0: a pad column or NaN
+            x = key ? make_comp(key, static_cast<uint32_t>(n0 + col)) : 0ull;
+          }
+          // sorted insertion of x into L[0..15], the smallest falling out; the
+          // first K entries depend only on the first K and x
+#pragma unroll
+          for (int j = 15; j >= 1; --j) L[j] = max_u64(L[j], min_u64(L[j - 1], x));
+          L[0] = max_u64(L[0], x);
+        }
+        if (any || bound) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) s_top[r][j ^ (r & 15)] = L[j];
+        }
+      }
     }
     __syncthreads();                         // the next tile's loads reuse the ring
   }
   for (int i = tid; i < kLmBM * K; i += NT) {
     const int r = i / K;
     const int j = i - r * K;
-    if (m0 + r < p.M) part[(static_cast<long long>(g) * p.M + m0 + r) * K + j] = s_top[r][j];
+    if (m0 + r < p.M) part[(static_cast<long long>(g) * p.M + m0 + r) * K + j] = s_top[r][tp(r, j)];
   }
 }
 
