@@ -390,6 +390,23 @@ using LmTile = DmaTile<BM, kLmBN, BM / 64, 4, 2>;
 
 __device__ __forceinline__ uint32_t key16_of(float x) { return order_key(bf16{f32_to_bf16(x)}); }
 
+// The order keys of the bf16 roundings (to nearest, ties to even) of x0 and
+// x1 in the low and high half: the packed conversion instruction rounds both,
+// then per half a negative h maps to 0x8000 - (h & 0x7fff) (its two's
+// complement) and a non-negative one to h + 0x8000; NaN maps to 0.  The same
+// keys as key16_of.
+__device__ __forceinline__ uint32_t key16x2(float x0, float x1) {
+  const uint32_t h = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x0))) |
+                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(x1))) << 16);
+  const uint32_t sgn = ((h >> 15) & 0x00010001u) * 0xffffu;       // 0xffff in each negative half
+  const uint32_t neg = (~h & 0x7fff7fffu) + 0x00010001u;          // per half 0x8000 - (h & 0x7fff)
+  const uint32_t pos = h | 0x80008000u;
+  uint32_t k = (neg & sgn) | (pos & ~sgn);
+  if (x0 != x0) k &= 0xffff0000u;
+  if (x1 != x1) k &= 0x0000ffffu;
+  return k;
+}
+
 // lane l gets lane l - 1's v (lane 0 gets 0): a DPP wave shift, no LDS permute
 __device__ __forceinline__ uint64_t shift_up_u64(uint64_t v) {
   const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), 0x138, 0xf, 0xf, false);
@@ -397,10 +414,6 @@ __device__ __forceinline__ uint64_t shift_up_u64(uint64_t v) {
                                              false);
   return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
 }
-
-// the larger / smaller of two composites
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 // v from a wave-uniform lane, through the scalar unit (no LDS permute)
 __device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane) {
@@ -410,7 +423,7 @@ __device__ __forceinline__ uint64_t read_lane_u64(uint64_t v, int lane) {
 }
 
 // KMAX (16 or 64) bounds K: the rows' lists take BM KMAX composites of LDS
-// beside the two ring slots: 128 + 32 KB for 256-row tiles at KMAX = 16,
+// beside the two ring slots: 128 + 16 KB for 256-row tiles at KMAX = 16,
 // 96 + 64 KB for 128-row tiles at KMAX = 64.
 template <int KMAX, int BM>
 __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, int tiles_m, int tiles_n, int groups,
@@ -421,10 +434,14 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
   constexpr int NT = NWV * 64;         // threads
   constexpr int kLmBM = BM;
   constexpr int TM = LT::TM, TN = LT::TN, MW = LT::MW, NWB = LT::NWB;
-  static_assert(kSlots * LT::kStage + kLmBM * KMAX * 8 <= 160 * 1024, "LDS");
+  // K <= 16: a list entry is (key << 16) | (0xffff - the column's index within
+  // the group: 256 x the group's tiles before it + column), 0 = empty; the
+  // group holds at most 256 tiles.  K <= 64: the 64-bit composite.
+  using TopT = std::conditional_t<KMAX == 16, uint32_t, uint64_t>;
+  static_assert(kSlots * LT::kStage + kLmBM * KMAX * sizeof(TopT) <= 160 * 1024, "LDS");
   __shared__ __align__(1024) char sm0[LT::kStage];
   __shared__ __align__(1024) char sm1[LT::kStage];
-  __shared__ uint64_t s_top[kLmBM][KMAX];   // per row, sorted; entry K - 1 is 0 until K are held
+  __shared__ TopT s_top[kLmBM][KMAX];   // per row, sorted; entry K - 1 is 0 until K are held
   // entry j of row r sits at j ^ (r & 15) for KMAX = 16, so the lanes that each
   // read their own row's entry j fall on different banks
   constexpr int kRowBytes = kLmBN * 2;                   // staged keys of one row
@@ -452,9 +469,10 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
     return reinterpret_cast<uint16_t*>(r < kRowsSlot ? sm0 + r * kRowBytes : sm1 + (r - kRowsSlot) * kRowBytes);
   };
   auto tp = [](int r, int j) { return KMAX == 16 ? (j ^ (r & 15)) : j; };
-  for (int i = tid; i < kLmBM * KMAX; i += NT) (&s_top[0][0])[i] = 0ull;
+  for (int i = tid; i < kLmBM * KMAX; i += NT) (&s_top[0][0])[i] = 0;
 
-  for (int tn = g; tn < tiles_n; tn += groups) {
+  int ord = 0;   // the group's tiles before this one
+  for (int tn = g; tn < tiles_n; tn += groups, ++ord) {
     const int n0 = tn * kLmBN;
     f32x4_t acc[TM][TN];
     dma_tile_mainloop<kLmBM, kLmBN, kLmBM / 64, 4, 2>(p, m0, n0, 0, p.Kd, sm0, sm1, sm0, sm0, acc);
@@ -462,24 +480,27 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
-      for (int bb = 0; bb < TN; ++bb)
+      for (int bb = 0; bb < TN; ++bb) {
+        const int c = wn * NWB + bb * 16 + (l & 15);
+        const bool live = n0 + c < p.N;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < 4; v += 2) {
           const int r = wm * MW + a * 16 + (l >> 4) * 4 + v;
-          const int c = wn * NWB + bb * 16 + (l & 15);
-          keyrow(r)[c] = n0 + c < p.N ? static_cast<uint16_t>(key16_of(acc[a][bb][v])) : 0;
+          const uint32_t k2 = live ? key16x2(acc[a][bb][v], acc[a][bb][v + 1]) : 0u;
+          keyrow(r)[c] = static_cast<uint16_t>(k2);
+          keyrow(r + 1)[c] = static_cast<uint16_t>(k2 >> 16);
         }
+      }
     __syncthreads();
     for (int i = 0; i < kLmBM / NWV; ++i) {
       const int r = wv + NWV * i;
-      const uint64_t thr = s_top[r][tp(r, K - 1)];   // the row's K-th best so far (0 while not full)
       const uint16_t* kr = keyrow(r);
       if constexpr (KMAX == 16) {
         // a list not full yet: the K-th largest of the lanes' maxima over keys
         // 4 l .. 4 l + 3 (K of the tile's keys reach it), left in the list's
-        // empty entry K - 1 with bit 63 set (no composite has it) for the
+        // empty entry K - 1 as (1 << 16) | bound (no entry has key 1) for the
         // row's lane
-        if (thr == 0ull) {
+        if (s_top[r][tp(r, K - 1)] == 0u) {
           const uint64_t v = *reinterpret_cast<const uint64_t*>(kr + 4 * l);
           const uint32_t m0 = max(static_cast<uint32_t>(v) & 0xffffu, static_cast<uint32_t>(v >> 16) & 0xffffu);
           const uint32_t m1 = max(static_cast<uint32_t>(v >> 32) & 0xffffu, static_cast<uint32_t>(v >> 48));
@@ -489,12 +510,12 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
             const uint32_t cand = tb | (1u << bit);
             if (__popcll(ballot(mx >= cand)) >= K) tb = cand;
           }
-          if (l == 0) s_top[r][tp(r, K - 1)] = (1ull << 63) | tb;
+          if (l == 0) s_top[r][tp(r, K - 1)] = (1u << 16) | tb;
         }
-        continue;
-      }
+      } else {
+      const uint64_t thr = s_top[r][K - 1];   // the row's K-th best so far (0 while not full)
       uint64_t c[5];
-      c[0] = l < K ? s_top[r][tp(r, l)] : 0ull;     // the current list, sorted
+      c[0] = l < K ? s_top[r][l] : 0ull;     // the current list, sorted
       int n = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -563,7 +584,8 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
           cur = l == rj ? xj : cur;
         }
       }
-      if (l < K) s_top[r][tp(r, l)] = cur;
+      if (l < K) s_top[r][l] = cur;
+      }
     }
     if constexpr (KMAX == 16) {
       __syncthreads();                       // the bounds of the rows not full yet
@@ -573,9 +595,9 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
         // different banks) when one of its four keys beats the K-th best (full
         // list) or reaches the bound (list not full)
         const int r = tid;
-        const uint64_t T = s_top[r][tp(r, K - 1)];
-        const bool bound = (T >> 63) != 0ull;
-        const int tk = bound ? static_cast<int>(static_cast<uint32_t>(T)) - 1 : static_cast<int>(comp_key(T));
+        const uint32_t T = s_top[r][tp(r, K - 1)];
+        const bool bound = (T >> 16) == 1u;
+        const int tk = bound ? static_cast<int>(T & 0xffffu) - 1 : static_cast<int>(T >> 16);
         const uint16_t* kr = keyrow(r);
         auto word = [&](int w) { return *reinterpret_cast<const uint64_t*>(kr + 4 * ((w + r) & 63)); };
         auto key_of = [](uint64_t v, int j) { return static_cast<int>(static_cast<uint32_t>(v >> (16 * j)) & 0xffffu); };
@@ -591,11 +613,11 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
           }
           mw |= static_cast<uint64_t>(m8) << w8;
         }
-        uint64_t L[16];
+        uint32_t L[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const uint64_t e = s_top[r][j ^ (r & 15)];
-          L[j] = (bound && j == K - 1) ? 0ull : e;   // the bound's entry was empty
+          const uint32_t e = s_top[r][j ^ (r & 15)];
+          L[j] = (bound && j == K - 1) ? 0u : e;   // the bound's entry was empty
         }
         // one marked key per lane and round, until no lane has any left (a
         // marked word holds at least one)
@@ -611,19 +633,19 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) ks |= (key_of(cur, j) > tk ? 1u : 0u) << j;
           }
-          uint64_t x = 0ull;
+          uint32_t x = 0u;
           if (ks != 0u) {
             const int j = __builtin_ctz(ks);
             ks &= ks - 1;
             const int col = (((wc + r) & 63) << 2) | j;
             const uint32_t key = static_cast<uint32_t>(key_of(cur, j));   // 0: a pad column or NaN
-            x = key ? make_comp(key, static_cast<uint32_t>(n0 + col)) : 0ull;
+            x = key ? (key << 16) | (0xffffu - static_cast<uint32_t>(ord * kLmBN + col)) : 0u;
           }
           // sorted insertion of x into L[0..15], the smallest falling out; the
           // first K entries depend only on the first K and x
 #pragma unroll
-          for (int j = 15; j >= 1; --j) L[j] = max_u64(L[j], min_u64(L[j - 1], x));
-          L[0] = max_u64(L[0], x);
+          for (int j = 15; j >= 1; --j) L[j] = max(L[j], min(L[j - 1], x));
+          L[0] = max(L[0], x);
         }
         if (any || bound) {
 #pragma unroll
@@ -636,7 +658,19 @@ __global__ void __launch_bounds__(BM * 4) lm_head_topk_kernel(GemmDev p, int K, 
   for (int i = tid; i < kLmBM * K; i += NT) {
     const int r = i / K;
     const int j = i - r * K;
-    if (m0 + r < p.M) part[(static_cast<long long>(g) * p.M + m0 + r) * K + j] = s_top[r][tp(r, j)];
+    uint64_t c;
+    if constexpr (KMAX == 16) {
+      // back to the global composite: column index 256 o + col of the group
+      // is vocabulary id 256 (g + o groups) + col
+      const uint32_t e = s_top[r][tp(r, j)];
+      const uint32_t li = 0xffffu - (e & 0xffffu);
+      c = e ? make_comp(e >> 16, static_cast<uint32_t>((g + static_cast<int>(li >> 8) * groups) * kLmBN +
+                                                       static_cast<int>(li & 255u)))
+            : 0ull;
+    } else {
+      c = s_top[r][j];
+    }
+    if (m0 + r < p.M) part[(static_cast<long long>(g) * p.M + m0 + r) * K + j] = c;
   }
 }
 
@@ -712,8 +746,11 @@ bool lm_head_topk_supported(int M, int V, int d, int K) {
   return M >= 1 && V >= K && K >= 1 && K <= kLmMaxK && d >= 64 && d % 64 == 0;
 }
 
-int lm_head_groups(int M, int V, int K) {
-  const int tiles_m = (M + lm_rows(K) - 1) / lm_rows(K);
+namespace {
+
+// vocabulary groups for row tiles of `rows` rows
+int lm_groups_for(int M, int V, int K, int rows) {
+  const int tiles_m = (M + rows - 1) / rows;
   const int tiles_n = (V + kLmBN - 1) / kLmBN;
   int groups = std::max(1, 256 / tiles_m);
   groups = std::min(groups, 2048 / K);         // the merge holds 2048 composites per row
@@ -721,6 +758,21 @@ int lm_head_groups(int M, int V, int K) {
   if (groups >= 8) groups -= groups % 8;
   return groups;
 }
+
+// K <= 16 takes the 256-row kernel with 32-bit list entries while no group
+// holds more than 256 vocabulary tiles; otherwise the 128-row kernel
+bool lm_short_lists(int M, int V, int K) {
+  if (K > 16) return false;
+  const int tiles_n = (V + kLmBN - 1) / kLmBN;
+  const int groups = lm_groups_for(M, V, K, lm_rows(16));
+  return (tiles_n + groups - 1) / groups <= 256;
+}
+
+int lm_rows_for(int M, int V, int K) { return lm_short_lists(M, V, K) ? lm_rows(16) : lm_rows(64); }
+
+}  // namespace
+
+int lm_head_groups(int M, int V, int K) { return lm_groups_for(M, V, K, lm_rows_for(M, V, K)); }
 
 size_t lm_head_workspace_bytes(int M, int V, int K) {
   return sizeof(uint64_t) * static_cast<size_t>(lm_head_groups(M, V, K)) * M * K;
@@ -736,12 +788,13 @@ hipError_t launch_lm_head_topk(const void* hd, const void* W_lm, int M, int V, i
   p.ldw0 = p.ldw1 = p.ldw2 = d;
   p.end0 = p.end1 = V;
   p.row_bias_div = 1;
-  const int tiles_m = (M + lm_rows(K) - 1) / lm_rows(K);
+  const int rows = lm_rows_for(M, V, K);
+  const int tiles_m = (M + rows - 1) / rows;
   const int tiles_n = (V + kLmBN - 1) / kLmBN;
   const int groups = lm_head_groups(M, V, K);
   const int xcd_map = groups % 8 == 0 ? 1 : 0;
   uint64_t* part = static_cast<uint64_t*>(workspace);
-  if (K <= 16)
+  if (lm_short_lists(M, V, K))
     hipLaunchKernelGGL((lm_head_topk_kernel<16, lm_rows(16)>), dim3(tiles_m * groups), dim3(lm_rows(16) * 4), 0,
                        st, p, K, tiles_m, tiles_n, groups, xcd_map, part);
   else
