@@ -681,7 +681,11 @@ __device__ __forceinline__ float value_of_key16(uint32_t k) {
 }
 
 // One wave per row: the top K of the groups' lists, sorted (value desc, id
-// asc), ids and bf16 values out.
+// asc), ids and bf16 values out.  Each list is sorted, so the K-th largest key
+// among the groups' first entries bounds the answer from below (K entries
+// reach it); the entries at or above it (a few more than K for the drafter's
+// logits) are ranked directly.  Beyond 64 of them an exact selection over all
+// entries runs instead.
 template <int Q>
 __global__ void __launch_bounds__(64) lm_head_merge_kernel(const uint64_t* __restrict__ part, int groups, int M,
                                                            int K, int32_t* __restrict__ ids, float* __restrict__ vals) {
@@ -696,8 +700,46 @@ __global__ void __launch_bounds__(64) lm_head_merge_kernel(const uint64_t* __res
     const int gq = i / K;
     c[q] = gq < groups ? part[(static_cast<long long>(gq) * M + row) * K + (i - gq * K)] : 0ull;
   }
-  select_topk<Q, 16>(c, K, sel);
+  // the groups' first entries, one group per lane and round (groups <= 64 Q)
+  uint32_t kf[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int gq = q * kWave + l;
+    kf[q] = (q * kWave < groups && gq < groups)
+                ? comp_key(part[(static_cast<long long>(gq) * M + row) * K]) : 0u;
+  }
+  uint32_t kb = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t cand = kb | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (q * kWave < groups) cnt += __popcll(ballot(kf[q] >= cand));
+    if (cnt >= K) kb = cand;
+  }
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) n += __popcll(ballot(c[q] != 0ull && comp_key(c[q]) >= kb));
   int base = 0;
+  if (n <= kWave) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const bool in = c[q] != 0ull && comp_key(c[q]) >= kb;
+      const uint64_t m = ballot(in);
+      if (in) s_fin[base + lanes_below(m)] = c[q];
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mine = l < base ? s_fin[l] : 0ull;
+    int rank = 0;
+    for (int j = 0; j < base; ++j) rank += s_fin[j] > mine ? 1 : 0;
+    if (l < base && rank < K) {
+      ids[static_cast<long long>(row) * K + rank] = static_cast<int32_t>(0xffffffffu - comp_inv(mine));
+      vals[static_cast<long long>(row) * K + rank] = value_of_key16(comp_key(mine));
+    }
+    return;
+  }
+  select_topk<Q, 16>(c, K, sel);
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     const uint64_t m = ballot(sel[q]);
