@@ -186,9 +186,10 @@ hipError_t topk_and_slot(const dcoco_dims* d, const dcoco_weights* w, const void
   const int R = d->n_blocks * d->B;
   if (dt == kDtypeBf16) {
     GemmProblem q = slot_gemm_problem(d, w, h, L, L.split_slot);
-    while (q.split > 1 && topk_gemm_workgroups(q) + R > kTopkGemmSlots) q.split /= 2;
+    const int row_wgs = topk_gemm_row_workgroups(R, d->V);
+    while (q.split > 1 && topk_gemm_workgroups(q) + row_wgs > kTopkGemmSlots) q.split /= 2;
     if (topk_gemm_supported(d->V, d->K, logits, q)) {
-      hipError_t e = launch_topk_gemm(logits, R, d->V, d->K, ids, cl, q, st);
+      hipError_t e = launch_topk_gemm(logits, R, d->V, d->K, ids, cl, q, topk_ws, st);
       if (e != hipSuccess) return e;
       if (split) *split = q.split;
       return slot_finish(d, w, s, s3, L, q.split, st, pairs);

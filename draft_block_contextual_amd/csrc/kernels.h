@@ -50,9 +50,13 @@ int gemm_pick_split(int M, int N, int Kd, int a_dtype, int w_dtype);
 // fp32 partials (no gather) in one launch: the GEMM's 64 x 64 tiles (times
 // q.split) and the rows share the CUs, three workgroups per CU.
 bool topk_gemm_supported(int V, int K, const void* logits, const GemmProblem& q);
+// With few rows each row is cut into segments (topk_gemm_row_workgroups
+// counts the row workgroups) whose composites go to `partial`
+// (topk_workspace_bytes of the rows) and a merge launch follows.
 int topk_gemm_workgroups(const GemmProblem& q);
+int topk_gemm_row_workgroups(int rows, int V);
 hipError_t launch_topk_gemm(const void* logits, int rows, int V, int K, int32_t* ids, float* vals,
-                            const GemmProblem& q, hipStream_t st);
+                            const GemmProblem& q, void* partial, hipStream_t st);
 // bf16 products with a long reduction (weight gradients): splits (a power of
 // two up to max_split) for about 256 workgroups, each split >= 128 deep
 int gemm_pick_split_max(int M, int N, int Kd, int max_split);

@@ -106,7 +106,10 @@ typedef struct {
  *   cand_ids    [n_blocks*B, K] int32    out: c_{i,k}
  *   cand_logits [n_blocks*B, K] fp32     out: l_i(k), the logit value widened
  * Each row's K largest logits, sorted by value descending; equal values go to
- * the lower id; -0 equals +0; NaN ranks below every number. */
+ * the lower id; -0 equals +0; NaN ranks below every number.
+ * Workspace: none, except for bf16 calls of at most 32 rows, whose rows are
+ * cut into column segments: it then holds each segment's K results
+ * (rows * segments * K * 8 bytes, at most 256 KB) until a merge ranks them. */
 int dcoco_topk(const dcoco_dims* dims, const void* logits, int32_t* cand_ids,
                float* cand_logits, void* workspace, size_t* workspace_bytes,
                void* stream);

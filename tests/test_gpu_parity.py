@@ -130,6 +130,38 @@ def test_topk_ties_and_special_values(dtype, V, K):
     np.testing.assert_array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(ref_vals[~np.isnan(ref_vals)]))
 
 
+@pytest.mark.parametrize("R", [1, 3, 16, 32, 100])
+def test_topk_rows_cut_into_segments(R):
+    """Few rows (at most 32) are cut into column segments and merged; more
+    rows stay whole.  The K best must not depend on where the cuts fall.  Rows of a tied top value spread over the
+    whole row (lower ids win across segments), the K best packed into one
+    narrow band, and the K best one per segment at the cut points' sides."""
+    import draft_block_contextual_amd as dc
+    import torch
+    V, K = 151936, 16
+    print(f"case topk segments R={R}", flush=True)
+    g = np.random.default_rng(1000 + R)
+    rows = np.round(g.standard_normal((R, V)) * 4) / 4
+    for i in range(R):
+        kind = i % 3
+        if kind == 0:       # 40 equal maxima spread evenly: the 16 lowest ids win
+            rows[i, np.linspace(0, V - 1, 40).astype(np.int64)] = 30.0
+        elif kind == 1:     # the K best in one band of 64 columns
+            c = int(g.integers(0, V - 64))
+            rows[i, c:c + 64:4] = 20.0 + np.arange(16) * 0.5
+        else:               # equal maxima just below and above every multiple of 512
+            cols = np.arange(512, V, 512)
+            rows[i, cols[g.integers(0, cols.size, 12)] - 1] = 25.0
+            rows[i, cols[g.integers(0, cols.size, 12)]] = 25.0
+    bits = synth.f32_to_bf16_bits(rows.astype(np.float32))
+    dims = dc.Dims(R, 1, K, V, 32, 32, 32, 32, 32, 32, "bf16")
+    ids, vals = dc.topk(dims, to_dev(bits, "bf16"))
+    torch.cuda.synchronize()
+    ref_ids, ref_vals = O.top_k(O.to_f64(bits, "bf16"), K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_array_equal(vals.cpu().numpy().astype(np.float64), ref_vals)
+
+
 # ------------------------------------------------------------------- walk
 
 def _select(S, vals, ids):
