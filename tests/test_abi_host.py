@@ -121,6 +121,24 @@ def test_workspace_and_pointer_checks(lib):
     assert lib.dcoco_select(ctypes.byref(cd), fake, fake, fake, None, None, None) == -1
 
 
+@pytest.mark.parametrize("n_blocks,K,V,segments", [
+    (1, 16, 151936, 16), (1, 64, 151936, 16), (2, 16, 151936, 8), (1, 16, 40000, 9),
+    (1, 16, 5000, 1), (4, 16, 151936, 1), (32, 16, 151936, 1)])
+def test_topk_workspace_holds_the_row_segments(lib, n_blocks, K, V, segments):
+    # bf16 calls of at most 32 rows cut each row into column segments (about
+    # 256 workgroups in all, at most 16 per row, each segment at least 4096
+    # columns) and keep each segment's K composites (8 bytes) for the merge;
+    # more rows, or rows too short to cut, need no workspace beyond the minimum
+    rows = n_blocks * 16
+    rc, n = _query_topk(lib, _dims(n_blocks=n_blocks, K=K, V=V))
+    assert rc == 0
+    if segments > 1:
+        assert n >= rows * segments * K * 8
+        assert n < rows * segments * K * 8 + 4096
+    else:
+        assert n <= 4096
+
+
 def test_vocab_limits_for_topk(lib):
     # bf16 rows: one workgroup per row, any vocabulary up to 2^30
     rc, n = _query_topk(lib, _dims(K=64, V=600000))
