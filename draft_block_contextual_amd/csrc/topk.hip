@@ -1181,16 +1181,17 @@ topk_merge_kernel(const T* __restrict__ logits, int V, int K, int nchunks,
 
 // At most 32 rows (one or two draft blocks of 16 slots) leave most of the
 // chip idle with a workgroup per row, each streaming its whole row: rows are
-// then cut into segments so that about 256 workgroups stream (at most 16
-// segments, each at least 4096 columns, so every segment holds more than K
-// columns), and a merge launch ranks each row's segment results.  Measured
-// at 16 rows of 151936: 11.8 us against 15.7 us per call.  From 64 rows on,
-// the extra launch and the segments' finishing work cost more than the
-// shorter streams save (a whole-path call at 64 to 256 rows was 2.4 to
-// 4.6 us slower with segments), so those rows stay whole.
+// then cut into up to 8 column segments (at most 256 workgroups in all; each
+// segment at least 4096 columns, so it holds more than K), and a merge launch
+// ranks each row's segment results.  Measured at 16 rows of 151936, the
+// whole-path call took 43.0 us with 8 segments against 43.5 with 4, 44.3
+// with 16 and 46.8 with whole rows.  From 64 rows on, the extra launch and
+// the segments' finishing work cost more than the shorter streams save (a
+// whole-path call at 64 to 256 rows was 2.4 to 4.6 us slower with segments),
+// so those rows stay whole.
 int topk_row_segments(int rows, int V) {
   if (rows <= 0 || rows > 32) return 1;
-  const int s = std::min(std::min((256 + rows - 1) / rows, 16), V / 4096);
+  const int s = std::min(std::min((256 + rows - 1) / rows, 8), V / 4096);
   return std::max(s, 1);
 }
 

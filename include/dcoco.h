@@ -109,7 +109,7 @@ typedef struct {
  * the lower id; -0 equals +0; NaN ranks below every number.
  * Workspace: none, except for bf16 calls of at most 32 rows, whose rows are
  * cut into column segments: it then holds each segment's K results
- * (rows * segments * K * 8 bytes, at most 256 KB) until a merge ranks them. */
+ * (rows * segments * K * 8 bytes, at most 128 KB) until a merge ranks them. */
 int dcoco_topk(const dcoco_dims* dims, const void* logits, int32_t* cand_ids,
                float* cand_logits, void* workspace, size_t* workspace_bytes,
                void* stream);

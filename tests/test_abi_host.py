@@ -122,12 +122,12 @@ def test_workspace_and_pointer_checks(lib):
 
 
 @pytest.mark.parametrize("n_blocks,K,V,segments", [
-    (1, 16, 151936, 16), (1, 64, 151936, 16), (2, 16, 151936, 8), (1, 16, 40000, 9),
+    (1, 16, 151936, 8), (1, 64, 151936, 8), (2, 16, 151936, 8), (1, 16, 40000, 8), (1, 16, 20000, 4),
     (1, 16, 5000, 1), (4, 16, 151936, 1), (32, 16, 151936, 1)])
 def test_topk_workspace_holds_the_row_segments(lib, n_blocks, K, V, segments):
-    # bf16 calls of at most 32 rows cut each row into column segments (about
-    # 256 workgroups in all, at most 16 per row, each segment at least 4096
-    # columns) and keep each segment's K composites (8 bytes) for the merge;
+    # bf16 calls of at most 32 rows cut each row into column segments (at
+    # most 256 workgroups in all, at most 8 per row, each segment at least
+    # 4096 columns) and keep each segment's K composites (8 bytes) for the merge;
     # more rows, or rows too short to cut, need no workspace beyond the minimum
     rows = n_blocks * 16
     rc, n = _query_topk(lib, _dims(n_blocks=n_blocks, K=K, V=V))
